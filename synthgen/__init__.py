@@ -1,0 +1,217 @@
+"""Seeded synthetic inputs for one SparsePR attention call.
+
+This module only draws random numbers and lays them out; it holds none of
+the method's arithmetic (no grouping, routing, attention or fitting).  It is
+the single source of inputs shared by the CPU oracle and the GPU path.
+
+Workloads.  The pages evaluate video diffusion transformers whose attention
+calls see 720p latents (45 x 80 spatial tokens) over 21 or 33 latent frames,
+and a 480p CogVideoX-like latent (30 x 45 over 13 frames).  Real activations
+and model weights are not available, so each call is replaced by a Gaussian
+mixture with the same token counts, head counts and head dimensions:
+
+* every token n carries one mixture label c_n, drawn uniformly;
+* q_n = mu^Q[c_n] + 0.5 * eps_q + 0.3 * pos(n),
+  k_n = mu^K[c_n] + 0.5 * eps_k + 0.3 * pos(n),  v_n ~ N(0, I);
+* component means mu^Q, mu^K ~ N(0, 1.5^2 I), drawn independently for Q and
+  K (variant ``near_exact`` uses mu^K = mu^Q, which makes the routed cells
+  hold nearly all attention mass);
+* pos(n) is a 3-D sinusoidal position code of the token's (t, y, x) cell.
+
+The query partition is the mixture label.  The key/value partition is the
+label too, or, with ``kv_split = s``, label c is cut into s consecutive runs
+of its tokens (in ascending token order), giving group s*c + j.
+
+Per head h the draws come from numpy ``PCG64(SeedSequence([seed, h]))`` in
+the order: labels, mu^Q, mu^K, Q noise, K noise, V.  bf16 workloads are
+rounded from float32 to bfloat16 with round-to-nearest-even.
+"""
+from __future__ import annotations
+
+import dataclasses
+from fractions import Fraction
+from typing import Optional
+
+import numpy as np
+
+__all__ = [
+    "Workload",
+    "WORKLOADS",
+    "workload",
+    "small_workload",
+    "make_head",
+    "make_call",
+    "position_code",
+    "f32_to_bf16_bits",
+    "bf16_bits_to_f32",
+]
+
+
+@dataclasses.dataclass(frozen=True)
+class Workload:
+    name: str
+    heads: int
+    n: int                 # N_q = N_k tokens (self-attention)
+    head_dim: int
+    dtype: str             # "bf16" or "f32"
+    components: int        # mixture components = query groups C_q
+    kv_split: int          # K/V groups per component (C_k = components * kv_split)
+    grid: Optional[tuple]  # (T, Y, X) latent grid, or None for no position code
+    rho: str               # executed-pair density target, decimal string
+    m: int = 64            # probe rows per head
+    r: int = 16            # output-subspace rank
+    lam: float = 0.1       # ridge strength
+    seed: int = 0
+    mean_std: float = 1.5
+    spread: float = 0.5
+    pos_scale: float = 0.3
+
+    @property
+    def c_q(self) -> int:
+        return self.components
+
+    @property
+    def c_k(self) -> int:
+        return self.components * self.kv_split
+
+    @property
+    def rho_fraction(self) -> Fraction:
+        return Fraction(self.rho)
+
+
+WORKLOADS = {
+    # single fp32 head, 32 x 32 cells, no position code
+    "tiny_fp32": Workload("tiny_fp32", heads=1, n=4096, head_dim=64, dtype="f32",
+                          components=32, kv_split=1, grid=None, rho="0.26", seed=0),
+    # CogVideoX-like 480p latent, 13 x 30 x 45 tokens
+    "cogvideox": Workload("cogvideox", heads=8, n=17550, head_dim=64, dtype="bf16",
+                          components=64, kv_split=1, grid=(13, 30, 45), rho="0.26", seed=1),
+    # Wan2.2-like 720p, 81 frames -> 21 x 45 x 80 tokens
+    "wan": Workload("wan", heads=40, n=75600, head_dim=128, dtype="bf16",
+                    components=256, kv_split=4, grid=(21, 45, 80), rho="0.22", seed=2),
+    # HunyuanVideo-like 720p, 129 frames -> 33 x 45 x 80 tokens
+    "hunyuan": Workload("hunyuan", heads=24, n=118800, head_dim=128, dtype="bf16",
+                        components=256, kv_split=4, grid=(33, 45, 80), rho="0.26", seed=3),
+}
+
+
+def workload(name: str) -> Workload:
+    return WORKLOADS[name]
+
+
+def small_workload(name="small", heads=2, n=700, head_dim=64, dtype="bf16", components=8,
+                   kv_split=1, grid=None, rho="0.3", m=64, r=16, lam=0.1, seed=11,
+                   **kw) -> Workload:
+    """A reduced workload with the same generator (test sizes)."""
+    return Workload(name, heads=heads, n=n, head_dim=head_dim, dtype=dtype,
+                    components=components, kv_split=kv_split, grid=grid, rho=rho,
+                    m=m, r=r, lam=lam, seed=seed, **kw)
+
+
+# ----------------------------------------------------------------------------
+# bfloat16 bit helpers (input encoding only)
+# ----------------------------------------------------------------------------
+
+def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Round float32 to bfloat16 (nearest, ties to even); returns uint16 bits."""
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
+    rounding = ((u >> 16) & 1) + np.uint32(0x7FFF)
+    out = ((u + rounding) >> 16).astype(np.uint16)
+    nan = np.isnan(x)
+    if nan.any():
+        out[nan] = np.uint16(0x7FC0)
+    return out
+
+
+def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
+    return (np.asarray(b, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
+
+
+# ----------------------------------------------------------------------------
+# position code
+# ----------------------------------------------------------------------------
+
+def position_code(grid, d: int) -> np.ndarray:
+    """3-D sinusoidal code, float32 [T*Y*X, d].
+
+    Token n = (t*Y + y)*X + x.  Channels split as [t | y | x] with
+    d_y = d_x = 2*floor(d/6) and d_t = d - d_y - d_x.  An axis chunk of 2m
+    channels holds sin(p*w_j) for j < m followed by cos(p*w_j), with
+    w_j = 10000^(-j/m).
+    """
+    T, Y, X = grid
+    dy = dx = 2 * (d // 6)
+    dt = d - dy - dx
+    t = np.repeat(np.arange(T), Y * X)
+    y = np.tile(np.repeat(np.arange(Y), X), T)
+    x = np.tile(np.arange(X), T * Y)
+
+    def axis(p, width):
+        m = width // 2
+        w = 10000.0 ** (-np.arange(m) / m)
+        ang = p[:, None].astype(np.float64) * w[None, :]
+        return np.concatenate([np.sin(ang), np.cos(ang)], axis=1)
+
+    return np.concatenate([axis(t, dt), axis(y, dy), axis(x, dx)], axis=1).astype(np.float32)
+
+
+# ----------------------------------------------------------------------------
+# per-head draw
+# ----------------------------------------------------------------------------
+
+def _kv_labels(labels: np.ndarray, components: int, split: int) -> np.ndarray:
+    if split == 1:
+        return labels.copy()
+    out = np.empty_like(labels)
+    for c in range(components):
+        idx = np.nonzero(labels == c)[0]          # ascending token order
+        n = idx.size
+        bounds = [(j * n) // split for j in range(split + 1)]
+        for j in range(split):
+            out[idx[bounds[j]:bounds[j + 1]]] = split * c + j
+    return out
+
+
+def make_head(w: Workload, h: int, variant: str = "default", pos: Optional[np.ndarray] = None):
+    """Draw head h.  Returns dict with float32 q, k, v [N, d] (bf16-exact for
+    bf16 workloads), uint16 bits (bf16 only) and int32 labels_q, labels_kv."""
+    if variant not in ("default", "near_exact"):
+        raise ValueError(variant)
+    rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([w.seed, h])))
+    n, d, C = w.n, w.head_dim, w.components
+    labels = rng.integers(0, C, size=n).astype(np.int32)
+    mu_q = (rng.standard_normal((C, d), dtype=np.float32) * np.float32(w.mean_std))
+    mu_k = (rng.standard_normal((C, d), dtype=np.float32) * np.float32(w.mean_std))
+    if variant == "near_exact":
+        mu_k = mu_q
+    q = rng.standard_normal((n, d), dtype=np.float32)
+    q *= np.float32(w.spread)
+    q += mu_q[labels]
+    k = rng.standard_normal((n, d), dtype=np.float32)
+    k *= np.float32(w.spread)
+    k += mu_k[labels]
+    v = rng.standard_normal((n, d), dtype=np.float32)
+    if w.grid is not None:
+        if pos is None:
+            pos = position_code(w.grid, d)
+        ps = pos * np.float32(w.pos_scale)
+        q += ps
+        k += ps
+    out = {"labels_q": labels, "labels_kv": _kv_labels(labels, C, w.kv_split).astype(np.int32)}
+    if w.dtype == "bf16":
+        for name, arr in (("q", q), ("k", k), ("v", v)):
+            bits = f32_to_bf16_bits(arr)
+            out[name + "_bits"] = bits
+            out[name] = bf16_bits_to_f32(bits)
+    elif w.dtype == "f32":
+        out["q"], out["k"], out["v"] = q, k, v
+    else:
+        raise ValueError(w.dtype)
+    return out
+
+
+def make_call(w: Workload, variant: str = "default", heads=None):
+    """Draw every head (or the listed ones).  Returns a list of per-head dicts."""
+    pos = position_code(w.grid, w.head_dim) if w.grid is not None else None
+    hs = range(w.heads) if heads is None else heads
+    return [make_head(w, h, variant, pos) for h in hs]
