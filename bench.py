@@ -1,0 +1,241 @@
+"""Benchmark of one SparsePR attention call on one MI355X.
+
+python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload wan]
+
+A step is one whole attention call (layout, routing, sparse attention,
+probes + fit on a side stream, correction) over all heads of the workload,
+inputs resident in HBM.  Prints one JSON line.  Only one GPU is used; the
+path shards by head (see the design notes), and --gpus above 1 is refused.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+F32_PEAK_TFLOPS = 157.3        # MI355X fp32 (matrix and vector)
+HBM_PEAK_GBS = 8000.0
+METRIC = "ms per sparse-attention call (all heads) + executed-pair TFLOPS, % bf16 peak"
+PROFILE_PMC = os.path.join(ROOT, "profiles", "attn_bf16_kernel_wan_pmc.txt")
+KERNEL_SRC = os.path.join(ROOT, "free_block_sparse_major_amd", "csrc", "attn.hip")
+
+
+def _src_hash(path):
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def _traffic_from_profile(workload_name):
+    """HBM bytes per attention launch from the committed PMC summary, or None
+    if there is none or the kernel source changed since it was taken."""
+    if not os.path.exists(PROFILE_PMC):
+        return None
+    txt = open(PROFILE_PMC).read()
+    m_hash = re.search(r"attn_src_sha256_16\s*=\s*([0-9a-f]+)", txt)
+    m_wl = re.search(r"workload\s*=\s*(\S+)", txt)
+    m_b = re.search(r"hbm_bytes_per_launch\s*=\s*([0-9.eE+]+)", txt)
+    if not (m_hash and m_b and m_wl) or m_hash.group(1) != _src_hash(KERNEL_SRC):
+        return None
+    if m_wl.group(1) != workload_name:
+        return None
+    return float(m_b.group(1))
+
+
+def cpu_baseline(w, arrays, budget_seconds=20.0):
+    """The oracle, as it is, on the host cores: head 0 in full except the
+    sparse attention, which runs on whole query groups until ~budget_seconds;
+    scaled to ms per call over all heads and all rows."""
+    import numpy as np
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        cores = os.cpu_count() or 1
+    h = 0
+    if w.dtype == "bf16":
+        f32 = lambda a: (a.astype(np.uint32) << 16).view(np.float32)
+    else:
+        f32 = lambda a: a
+    q, k, v = f32(arrays["q"][h]), f32(arrays["k"][h]), f32(arrays["v"][h])
+    lq, lk = arrays["labels_q"][h], arrays["labels_kv"][h]
+    t0 = time.time()
+    r = oracle.run_head(q, k, v, lq, lk, w.c_q, w.c_k, w.rho, m=w.m, rank=w.r, lam=w.lam,
+                        query_rows=np.zeros(0, np.int64))
+    t_fixed = time.time() - t0
+    # sparse attention + correction on whole query groups, largest first
+    sizes = np.diff(r["offsets_q"])
+    rows_done, t_rows = 0, 0.0
+    for a in np.argsort(-sizes, kind="stable"):
+        if t_rows > budget_seconds or sizes[a] == 0:
+            break
+        rows = r["perm_q"][r["offsets_q"][a]:r["offsets_q"][a + 1]]
+        t1 = time.time()
+        o, _ = oracle.sparse_attention_rows(q[rows], lq[rows], k, v, lk, r["z"], r["scale"])
+        oracle.apply_correction(o, r["fit"])
+        t_rows += time.time() - t1
+        rows_done += rows.size
+    per_head = t_fixed + t_rows * (w.n / max(rows_done, 1))
+    ms_call = per_head * w.heads * 1e3
+    return {"value": ms_call, "unit": "ms/call", "cores": int(cores), "kind": "oracle",
+            "sample": (f"head 0: routing/probes/fit in full ({t_fixed:.1f} s), sparse attention "
+                       f"+ correction on {rows_done} of {w.n} query rows ({t_rows:.1f} s); "
+                       f"scaled to {w.heads} heads x {w.n} rows, fp64 numpy")}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="wan")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-dense", action="store_true")
+    ap.add_argument("--rho", default=None, help="override the executed-density target")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the SparsePR call shards by head with no "
+              "communication, so a multi-GPU figure is not produced by this build.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import dataclasses
+
+    import numpy as np
+    import torch
+
+    import free_block_sparse_major_amd as fb
+    import synthgen as sg
+
+    w = sg.workload(args.workload)
+    if args.rho:
+        w = dataclasses.replace(w, rho=args.rho)
+    t0 = time.time()
+    arr = sg.make_call_arrays(w)
+    gen_s = time.time() - t0
+    dev = torch.device("cuda")
+    if w.dtype == "bf16":
+        up = lambda a: torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
+    else:
+        up = lambda a: torch.from_numpy(a).to(dev)
+    q, k, v = up(arr["q"]), up(arr["k"]), up(arr["v"])
+    lq = torch.from_numpy(arr["labels_q"]).to(dev)
+    lk = torch.from_numpy(arr["labels_kv"]).to(dev)
+    dtype = fb.BF16 if w.dtype == "bf16" else fb.F32
+    call = fb.SparsePRCall(w.heads, w.n, w.n, w.head_dim, dtype, w.c_q, w.c_k, m=w.m, rank=w.r,
+                           lam=w.lam, rho=w.rho, out_dtype=fb.BF16 if w.dtype == "bf16" else fb.F32)
+
+    # attention launches are bracketed with events on the stream they run on
+    attn_events = []
+    orig_attend = call.attend
+
+    def timed_attend(stream=None):
+        s = torch.cuda.current_stream() if stream is None else stream
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(s)
+        orig_attend(stream)
+        e1.record(s)
+        attn_events.append((e0, e1))
+
+    for _ in range(args.warmup):
+        call(lq, lk, q, k, v)
+    torch.cuda.synchronize()
+    call.attend = timed_attend
+    attn_events.clear()
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    e_start, e_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e_start.record()
+    for _ in range(args.steps):
+        call(lq, lk, q, k, v)
+    e_end.record()
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t_start) * 1e3 / args.steps
+    ms_call = e_start.elapsed_time(e_end) / args.steps
+    attn_ms = sum(a.elapsed_time(b) for a, b in attn_events) / len(attn_events)
+    call.attend = orig_attend
+
+    routed = int(call.routed_pairs.sum().item())
+    H, n, d, m_eff = w.heads, w.n, w.head_dim, min(w.m, w.n)
+    attn_flop = 4.0 * d * routed
+    exec_flop = 4.0 * d * (routed + H * m_eff * n)
+    peak = BF16_PEAK_TFLOPS if w.dtype == "bf16" else F32_PEAK_TFLOPS
+    attn_tflops = attn_flop / (attn_ms * 1e-3) / 1e12
+    call_tflops = exec_flop / (ms_call * 1e-3) / 1e12
+    rho_route = routed / (H * n * n)
+    rho_exec = rho_route + m_eff / n
+
+    out = {
+        "metric": METRIC,
+        "value": round(ms_call, 4),
+        "unit": "ms/call",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_call, 4),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if w.dtype == "bf16" else "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": (f"{w.name}: {H} heads x {n} tokens, d={d}, {w.dtype}, "
+                         f"C_q={w.c_q}, C_k={w.c_k}, rho*={w.rho}, M={w.m}, r={w.r}, "
+                         f"lambda={w.lam}, seed={w.seed}"),
+            "heads": H, "tokens": n, "head_dim": d, "c_q": w.c_q, "c_k": w.c_k,
+            "rho_target": w.rho, "m": w.m, "r": w.r, "lambda": w.lam,
+            "parallelism": "single GPU",
+        },
+        "executed_pair_tflops": round(call_tflops, 2),
+        "pct_bf16_peak": round(100 * call_tflops / BF16_PEAK_TFLOPS, 2),
+        "attn_ms": round(attn_ms, 4),
+        "attn_tflops": round(attn_tflops, 2),
+        "attn_pct_peak": round(100 * attn_tflops / peak, 2),
+        "routed_pairs": routed,
+        "rho_route": round(rho_route, 6),
+        "rho_exec": round(rho_exec, 6),
+        "wall_ms_per_call": round(wall_ms, 4),
+        "input_generation_s": round(gen_s, 1),
+    }
+    traffic = _traffic_from_profile(w.name)
+    out["roofline"] = {
+        "bound": "mfma" if w.dtype == "bf16" else "alu",
+        "kernel": "attn_bf16_kernel<%d>" % d if w.dtype == "bf16" else "attn_f32_kernel<%d>" % d,
+        "achieved": round(attn_tflops, 2),
+        "peak": peak,
+        "unit": "TFLOP/s",
+        "frac": round(attn_tflops / peak, 4),
+        "traffic": traffic,
+    }
+    if not args.no_dense:
+        qq, kk, vv = q.unsqueeze(0), k.unsqueeze(0), v.unsqueeze(0)
+        for _ in range(2):
+            torch.nn.functional.scaled_dot_product_attention(qq, kk, vv)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(3):
+            torch.nn.functional.scaled_dot_product_attention(qq, kk, vv)
+        e1.record()
+        torch.cuda.synchronize()
+        dense_ms = e0.elapsed_time(e1) / 3
+        out["dense_sdpa_ms"] = round(dense_ms, 3)
+        out["speedup_vs_dense_sdpa"] = round(dense_ms / ms_call, 3)
+        del qq, kk, vv
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(w, arr)
+        out["cpu_baseline"]["value"] = round(out["cpu_baseline"]["value"], 1)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,280 @@
+"""MI355X-native SparsePR attention call: thin Python binding of libsparsepr.
+
+The five ABI calls keep their C names and only marshal arguments (torch
+tensors -> device pointers, current HIP stream); every step of the path runs
+in the HIP kernels of libsparsepr.so.  There is no CPU fallback: importing
+works without a GPU, but every call raises if the library is missing.
+
+`SparsePRCall` allocates the per-call buffers once (torch device memory) and
+chains the five calls; probe fitting runs on a side stream concurrently with
+the sparse attention, joined before the correction.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from fractions import Fraction
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libsparsepr.so")
+
+OK, ERR_INVALID, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = range(5)
+BF16, F32 = 0, 1
+CALL_PARTITION_LAYOUT, CALL_ROUTE_CELLS, CALL_SPARSE_ATTN, CALL_PROBE_FIT, CALL_CORRECT = range(5)
+EXPORTED = (
+    "sparsepr_partition_layout", "sparsepr_route_cells", "sparsepr_sparse_attn",
+    "sparsepr_probe_fit", "sparsepr_correct", "sparsepr_workspace_bytes",
+    "sparsepr_status_string", "sparsepr_version",
+)
+
+
+class Dims(ctypes.Structure):
+    _fields_ = [
+        ("heads", ctypes.c_int32), ("n_q", ctypes.c_int32), ("n_k", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32), ("dtype", ctypes.c_int32), ("c_q", ctypes.c_int32),
+        ("c_k", ctypes.c_int32), ("reserved", ctypes.c_int32),
+        ("q_stride_head", ctypes.c_int64), ("q_stride_tok", ctypes.c_int64),
+        ("kv_stride_head", ctypes.c_int64), ("kv_stride_tok", ctypes.c_int64),
+    ]
+
+
+class SparsePRError(RuntimeError):
+    pass
+
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH):
+    """Loads libsparsepr.so (raises if it was not built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise SparsePRError(f"{path} is missing: build it with `python -m "
+                            "free_block_sparse_major_amd.build` (there is no CPU fallback)")
+    lib = ctypes.CDLL(path)
+    P, I32, I64, SZ, D = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t, ctypes.c_double
+    DP = ctypes.POINTER(Dims)
+    lib.sparsepr_workspace_bytes.argtypes = [I32, DP, I32, I32]
+    lib.sparsepr_workspace_bytes.restype = SZ
+    lib.sparsepr_status_string.argtypes = [I32]
+    lib.sparsepr_status_string.restype = ctypes.c_char_p
+    lib.sparsepr_version.argtypes = []
+    lib.sparsepr_version.restype = I32
+    lib.sparsepr_partition_layout.argtypes = [DP] + [P] * 14 + [P, SZ, P]
+    lib.sparsepr_partition_layout.restype = I32
+    lib.sparsepr_route_cells.argtypes = [DP, P, P, P, P, I64, P, P, P, P, SZ, P]
+    lib.sparsepr_route_cells.restype = I32
+    lib.sparsepr_sparse_attn.argtypes = [DP, P, P, P, P, P, P, P, ctypes.c_float, P, P, P, SZ, P]
+    lib.sparsepr_sparse_attn.restype = I32
+    lib.sparsepr_probe_fit.argtypes = ([DP, I32, I32, D] + [P] * 9 + [ctypes.c_float] + [P] * 7
+                                       + [P, SZ, P])
+    lib.sparsepr_probe_fit.restype = I32
+    lib.sparsepr_correct.argtypes = [DP, I32, I32] + [P] * 8 + [I32, I64, I64, P, SZ, P]
+    lib.sparsepr_correct.restype = I32
+    _lib = lib
+    return lib
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream=None):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _check(status, name):
+    if status != OK:
+        msg = load_library().sparsepr_status_string(status).decode()
+        raise SparsePRError(f"{name}: {msg} (status {status})")
+
+
+def make_dims(heads, n_q, n_k, head_dim, dtype, c_q, c_k, q_strides=None, kv_strides=None):
+    """q_strides / kv_strides: (stride_head, stride_tok) in elements; default [H][N][d]."""
+    qs = q_strides or (n_q * head_dim, head_dim)
+    ks = kv_strides or (n_k * head_dim, head_dim)
+    return Dims(heads, n_q, n_k, head_dim, dtype, c_q, c_k, 0, qs[0], qs[1], ks[0], ks[1])
+
+
+def workspace_bytes(which, dims, m=64, rank=16):
+    return int(load_library().sparsepr_workspace_bytes(which, ctypes.byref(dims), m, rank))
+
+
+def sparsepr_version():
+    return int(load_library().sparsepr_version())
+
+
+# ----------------------------------------------------------------------------
+# the five ABI calls (argument marshalling only)
+# ----------------------------------------------------------------------------
+
+def sparsepr_partition_layout(dims, labels_q, labels_kv, q, k, v, perm_q, offsets_q, perm_kv,
+                              offsets_kv, q_g, k_g, v_g, centroid_q, centroid_k, ws, stream=None):
+    st = load_library().sparsepr_partition_layout(
+        ctypes.byref(dims), _ptr(labels_q), _ptr(labels_kv), _ptr(q), _ptr(k), _ptr(v),
+        _ptr(perm_q), _ptr(offsets_q), _ptr(perm_kv), _ptr(offsets_kv), _ptr(q_g), _ptr(k_g),
+        _ptr(v_g), _ptr(centroid_q), _ptr(centroid_k), _ptr(ws),
+        ws.numel() * ws.element_size() if ws is not None else 0, _stream(stream))
+    _check(st, "sparsepr_partition_layout")
+
+
+def sparsepr_route_cells(dims, offsets_q, offsets_kv, centroid_q, centroid_k, budget, cell_rowptr,
+                         cell_col, routed_pairs, ws, stream=None):
+    st = load_library().sparsepr_route_cells(
+        ctypes.byref(dims), _ptr(offsets_q), _ptr(offsets_kv), _ptr(centroid_q), _ptr(centroid_k),
+        int(budget), _ptr(cell_rowptr), _ptr(cell_col), _ptr(routed_pairs), _ptr(ws),
+        ws.numel() * ws.element_size() if ws is not None else 0, _stream(stream))
+    _check(st, "sparsepr_route_cells")
+
+
+def sparsepr_sparse_attn(dims, offsets_q, offsets_kv, cell_rowptr, cell_col, q_g, k_g, v_g,
+                         softmax_scale, o_sp, lse, ws, stream=None):
+    st = load_library().sparsepr_sparse_attn(
+        ctypes.byref(dims), _ptr(offsets_q), _ptr(offsets_kv), _ptr(cell_rowptr), _ptr(cell_col),
+        _ptr(q_g), _ptr(k_g), _ptr(v_g), ctypes.c_float(softmax_scale), _ptr(o_sp), _ptr(lse),
+        _ptr(ws), ws.numel() * ws.element_size() if ws is not None else 0, _stream(stream))
+    _check(st, "sparsepr_sparse_attn")
+
+
+def sparsepr_probe_fit(dims, m, rank, lam, offsets_q, offsets_kv, perm_q, cell_rowptr, cell_col,
+                       centroid_q, q_g, k_g, v_g, softmax_scale, probe_rows, probe_tokens,
+                       o_probe_dense, o_probe_sparse, corr_a, corr_psi_t, corr_c, ws, stream=None):
+    st = load_library().sparsepr_probe_fit(
+        ctypes.byref(dims), int(m), int(rank), float(lam), _ptr(offsets_q), _ptr(offsets_kv),
+        _ptr(perm_q), _ptr(cell_rowptr), _ptr(cell_col), _ptr(centroid_q), _ptr(q_g), _ptr(k_g),
+        _ptr(v_g), ctypes.c_float(softmax_scale), _ptr(probe_rows), _ptr(probe_tokens),
+        _ptr(o_probe_dense), _ptr(o_probe_sparse), _ptr(corr_a), _ptr(corr_psi_t), _ptr(corr_c),
+        _ptr(ws), ws.numel() * ws.element_size() if ws is not None else 0, _stream(stream))
+    _check(st, "sparsepr_probe_fit")
+
+
+def sparsepr_correct(dims, m, rank, perm_q, o_sp, probe_tokens, o_probe_dense, corr_a, corr_psi_t,
+                     corr_c, out, out_dtype, out_stride_head, out_stride_tok, stream=None):
+    st = load_library().sparsepr_correct(
+        ctypes.byref(dims), int(m), int(rank), _ptr(perm_q), _ptr(o_sp), _ptr(probe_tokens),
+        _ptr(o_probe_dense), _ptr(corr_a), _ptr(corr_psi_t), _ptr(corr_c), _ptr(out),
+        int(out_dtype), int(out_stride_head), int(out_stride_tok), None, 0, _stream(stream))
+    _check(st, "sparsepr_correct")
+
+
+# ----------------------------------------------------------------------------
+# budget (host, exact rational) and the chained call
+# ----------------------------------------------------------------------------
+
+def routed_pair_budget(rho, n_q, n_k, m):
+    """ceil((rho*N_q - M_eff)*N_k), clamped at 0 (probe cost reserved)."""
+    m_eff = min(m, n_q)
+    return max(0, math.ceil((Fraction(rho) * n_q - m_eff) * n_k))
+
+
+class SparsePRCall:
+    """Device buffers and stream plumbing for repeated calls of one shape.
+
+    Inputs are torch tensors on the GPU: q [H][N_q][d], k, v [H][N_k][d]
+    (bf16 or f32, or any layout with contiguous last dim given via strides),
+    labels int32 [H][N].  Outputs stay resident on the device."""
+
+    def __init__(self, heads, n_q, n_k, head_dim, dtype, c_q, c_k, m=64, rank=16, lam=0.1,
+                 rho="0.26", budget=None, out_dtype=F32, device="cuda", q_strides=None,
+                 kv_strides=None, overlap=True):
+        load_library()
+        self.dims = make_dims(heads, n_q, n_k, head_dim, dtype, c_q, c_k, q_strides, kv_strides)
+        self.m, self.rank, self.lam = m, rank, lam
+        self.budget = routed_pair_budget(rho, n_q, n_k, m) if budget is None else int(budget)
+        self.scale = 1.0 / math.sqrt(head_dim)
+        self.out_dtype = out_dtype
+        self.overlap = overlap
+        H, d = heads, head_dim
+        dev = torch.device(device)
+        tdt = torch.bfloat16 if dtype == BF16 else torch.float32
+        i32 = dict(dtype=torch.int32, device=dev)
+        self.perm_q = torch.empty(H, n_q, **i32)
+        self.perm_kv = torch.empty(H, n_k, **i32)
+        self.offsets_q = torch.empty(H, c_q + 1, **i32)
+        self.offsets_kv = torch.empty(H, c_k + 1, **i32)
+        self.q_g = torch.empty(H, n_q, d, dtype=tdt, device=dev)
+        self.k_g = torch.empty(H, n_k, d, dtype=tdt, device=dev)
+        self.v_g = torch.empty(H, n_k, d, dtype=tdt, device=dev)
+        self.centroid_q = torch.empty(H, c_q, d, dtype=torch.float64, device=dev)
+        self.centroid_k = torch.empty(H, c_k, d, dtype=torch.float64, device=dev)
+        self.cell_rowptr = torch.empty(H, c_q + 1, **i32)
+        self.cell_col = torch.empty(H, c_q * c_k, **i32)
+        self.routed_pairs = torch.empty(H, dtype=torch.int64, device=dev)
+        self.o_sp = torch.empty(H, n_q, d, dtype=torch.float32, device=dev)
+        self.lse = torch.empty(H, n_q, dtype=torch.float32, device=dev)
+        self.probe_rows = torch.empty(H, m, **i32)
+        self.probe_tokens = torch.empty(H, m, **i32)
+        self.o_probe_dense = torch.empty(H, m, d, dtype=torch.float32, device=dev)
+        self.o_probe_sparse = torch.empty(H, m, d, dtype=torch.float32, device=dev)
+        self.corr_a = torch.empty(H, d, max(rank, 1), dtype=torch.float32, device=dev)
+        self.corr_psi_t = torch.empty(H, max(rank, 1), d, dtype=torch.float32, device=dev)
+        self.corr_c = torch.empty(H, d, dtype=torch.float32, device=dev)
+        odt = torch.bfloat16 if out_dtype == BF16 else torch.float32
+        self.out = torch.empty(H, n_q, d, dtype=odt, device=dev)
+
+        def ws(which):
+            nb = workspace_bytes(which, self.dims, m, rank)
+            return torch.empty(max(nb, 256), dtype=torch.uint8, device=dev)
+
+        self.ws_layout = ws(CALL_PARTITION_LAYOUT)
+        self.ws_route = ws(CALL_ROUTE_CELLS)
+        self.ws_attn = ws(CALL_SPARSE_ATTN)
+        self.ws_probe = ws(CALL_PROBE_FIT)
+        self.side = torch.cuda.Stream(device=dev) if overlap else None
+        self.ev_routed = torch.cuda.Event()
+        self.ev_fit = torch.cuda.Event()
+
+    # individual stages -------------------------------------------------------
+    def layout(self, labels_q, labels_kv, q, k, v, stream=None):
+        sparsepr_partition_layout(self.dims, labels_q, labels_kv, q, k, v, self.perm_q,
+                                  self.offsets_q, self.perm_kv, self.offsets_kv, self.q_g,
+                                  self.k_g, self.v_g, self.centroid_q, self.centroid_k,
+                                  self.ws_layout, stream)
+
+    def route(self, stream=None):
+        sparsepr_route_cells(self.dims, self.offsets_q, self.offsets_kv, self.centroid_q,
+                             self.centroid_k, self.budget, self.cell_rowptr, self.cell_col,
+                             self.routed_pairs, self.ws_route, stream)
+
+    def attend(self, stream=None):
+        sparsepr_sparse_attn(self.dims, self.offsets_q, self.offsets_kv, self.cell_rowptr,
+                             self.cell_col, self.q_g, self.k_g, self.v_g, self.scale, self.o_sp,
+                             self.lse, self.ws_attn, stream)
+
+    def probe_fit(self, stream=None):
+        sparsepr_probe_fit(self.dims, self.m, self.rank, self.lam, self.offsets_q,
+                           self.offsets_kv, self.perm_q, self.cell_rowptr, self.cell_col,
+                           self.centroid_q, self.q_g, self.k_g, self.v_g, self.scale,
+                           self.probe_rows, self.probe_tokens, self.o_probe_dense,
+                           self.o_probe_sparse, self.corr_a, self.corr_psi_t, self.corr_c,
+                           self.ws_probe, stream)
+
+    def correct(self, stream=None):
+        sparsepr_correct(self.dims, self.m, self.rank, self.perm_q, self.o_sp, self.probe_tokens,
+                         self.o_probe_dense, self.corr_a, self.corr_psi_t, self.corr_c, self.out,
+                         self.out_dtype, self.out.stride(0), self.out.stride(1), stream)
+
+    def __call__(self, labels_q, labels_kv, q, k, v):
+        """One whole attention call on the current stream (probe fit on the
+        side stream when overlap is on).  Returns the output tensor."""
+        main = torch.cuda.current_stream()
+        self.layout(labels_q, labels_kv, q, k, v)
+        self.route()
+        if self.side is not None:
+            self.ev_routed.record(main)
+            self.side.wait_event(self.ev_routed)
+            self.probe_fit(self.side)
+            self.ev_fit.record(self.side)
+            self.attend()
+            main.wait_event(self.ev_fit)
+        else:
+            self.attend()
+            self.probe_fit()
+        self.correct()
+        return self.out

@@ -1,0 +1,295 @@
+// S1-S3: group-major layout of Q, K, V.
+//
+// SparsePR paper, §3 problem setup: queries and keys are partitioned into
+// groups, each value follows its key.  The review of the paper (method
+// summary, step (3)) permutes Q, K, V to a group-major layout before the
+// variable-length block-sparse kernel.  Inside a group tokens keep their
+// ascending token order, so the layout is a stable counting sort of the labels.
+//
+// Kernels (per tensor kind, per head):
+//   hist     per 1024-token tile: label histogram            -> counts[c][tile]
+//   scan     exclusive scan of counts in (label, tile) order  -> bases, offsets
+//   scatter  per tile: bitonic sort of (label, index), rank   -> perm
+//   gather   row copy q_g[j] = q[perm[j]] with 16-byte accesses (HBM bound)
+//   centroid fp64 sum of each group's rows / group size
+
+#include "common.h"
+
+namespace spr {
+namespace {
+
+constexpr int kTile = 1024;       // tokens per histogram / scatter tile
+constexpr int kThreads = 256;
+
+struct KindArgs {
+  const int32_t* labels;  // [H][N]
+  int32_t* perm;          // [H][N]
+  int32_t* offsets;       // [H][C+1]
+  int32_t* counts;        // [H][C][ntiles] (workspace)
+  int n, c, ntiles;
+};
+
+__global__ __launch_bounds__(kThreads) void hist_kernel(KindArgs qa, KindArgs ka) {
+  const KindArgs& A = blockIdx.z == 0 ? qa : ka;
+  const int tile = blockIdx.x, h = blockIdx.y;
+  if (tile >= A.ntiles) return;
+  __shared__ int32_t hist[SPARSEPR_MAX_GROUPS];
+  for (int i = threadIdx.x; i < A.c; i += kThreads) hist[i] = 0;
+  __syncthreads();
+  const int32_t* lab = A.labels + int64_t(h) * A.n;
+  const int t0 = tile * kTile;
+  for (int i = threadIdx.x; i < kTile; i += kThreads) {
+    int t = t0 + i;
+    if (t < A.n) atomicAdd(&hist[lab[t]], 1);
+  }
+  __syncthreads();
+  int32_t* cnt = A.counts + int64_t(h) * A.c * A.ntiles;
+  for (int c = threadIdx.x; c < A.c; c += kThreads) cnt[int64_t(c) * A.ntiles + tile] = hist[c];
+}
+
+// One block per (head, kind): exclusive scan of counts[c][tile] in (c, tile)
+// order, in place.  offsets[c] = base of (c, tile 0), offsets[C] = N.
+__global__ __launch_bounds__(1024) void scan_kernel(KindArgs qa, KindArgs ka) {
+  const KindArgs& A = blockIdx.y == 0 ? qa : ka;
+  const int h = blockIdx.x;
+  __shared__ long long red[16];
+  int32_t* cnt = A.counts + int64_t(h) * A.c * A.ntiles;
+  const long long len = int64_t(A.c) * A.ntiles;
+  const long long per = (len + blockDim.x - 1) / blockDim.x;
+  const long long lo = per * threadIdx.x;
+  const long long hi = lo + per < len ? lo + per : len;
+  long long s = 0;
+  for (long long i = lo; i < hi; ++i) s += cnt[i];
+  long long total;
+  long long run = block_exclusive_scan(s, red, &total);
+  for (long long i = lo; i < hi; ++i) {
+    int32_t v = cnt[i];
+    cnt[i] = int32_t(run);
+    run += v;
+  }
+  __syncthreads();
+  int32_t* off = A.offsets + int64_t(h) * (A.c + 1);
+  for (int c = threadIdx.x; c < A.c; c += blockDim.x) off[c] = cnt[int64_t(c) * A.ntiles];
+  if (threadIdx.x == 0) off[A.c] = A.n;
+}
+
+// Per tile: sort the tile's (label, local index) keys with a bitonic network,
+// then the sorted position minus the tile-local start of the label is the
+// token's rank among earlier same-label tokens of the tile.
+__global__ __launch_bounds__(kThreads) void scatter_kernel(KindArgs qa, KindArgs ka) {
+  const KindArgs& A = blockIdx.z == 0 ? qa : ka;
+  const int tile = blockIdx.x, h = blockIdx.y;
+  if (tile >= A.ntiles) return;
+  __shared__ uint32_t keys[kTile];
+  __shared__ int32_t hist[SPARSEPR_MAX_GROUPS];
+  __shared__ long long red[kThreads / 64];
+  const int32_t* lab = A.labels + int64_t(h) * A.n;
+  const int t0 = tile * kTile;
+  for (int i = threadIdx.x; i < A.c; i += kThreads) hist[i] = 0;
+  __syncthreads();
+  for (int i = threadIdx.x; i < kTile; i += kThreads) {
+    int t = t0 + i;
+    uint32_t key = 0xffffffffu;  // padding sorts last
+    if (t < A.n) {
+      int l = lab[t];
+      key = (uint32_t(l) << 10) | uint32_t(i);
+      atomicAdd(&hist[l], 1);
+    }
+    keys[i] = key;
+  }
+  __syncthreads();
+  // exclusive scan of the tile histogram (C <= 1024 entries, 4 per thread)
+  {
+    int base = threadIdx.x * 4;
+    long long s = 0;
+    int v[4];
+    for (int j = 0; j < 4; ++j) {
+      v[j] = base + j < A.c ? hist[base + j] : 0;
+      s += v[j];
+    }
+    long long tot;
+    long long run = block_exclusive_scan(s, red, &tot);
+    __syncthreads();
+    for (int j = 0; j < 4; ++j) {
+      if (base + j < A.c) hist[base + j] = int32_t(run);
+      run += v[j];
+    }
+  }
+  __syncthreads();
+  // bitonic sort, ascending, 1024 keys, 2 compare-exchanges per thread per stage
+  for (int size = 2; size <= kTile; size <<= 1) {
+    for (int stride = size >> 1; stride > 0; stride >>= 1) {
+      for (int p = threadIdx.x; p < kTile / 2; p += kThreads) {
+        int i = 2 * p - (p & (stride - 1));
+        int j = i + stride;
+        bool up = (i & size) == 0;
+        uint32_t a = keys[i], b = keys[j];
+        if ((a > b) == up) {
+          keys[i] = b;
+          keys[j] = a;
+        }
+      }
+      __syncthreads();
+    }
+  }
+  const int32_t* cnt = A.counts + int64_t(h) * A.c * A.ntiles;
+  int32_t* perm = A.perm + int64_t(h) * A.n;
+  for (int s = threadIdx.x; s < kTile; s += kThreads) {
+    uint32_t key = keys[s];
+    if (key == 0xffffffffu) continue;
+    int l = int(key >> 10), i = int(key & 1023u);
+    int rank = s - hist[l];
+    int dest = cnt[int64_t(l) * A.ntiles + tile] + rank;
+    perm[dest] = t0 + i;
+  }
+}
+
+// Row gather with 16-byte accesses.  grid.z: 0 = q, 1 = k, 2 = v.
+struct GatherArgs {
+  const char* src[3];
+  char* dst[3];
+  const int32_t* perm[3];
+  int64_t stride_head[3], stride_tok[3];  // elements
+  int n[3];
+  int row_bytes;   // d * element size (multiple of 16)
+  int esize;
+};
+
+constexpr int kGatherRows = 64;
+
+__global__ __launch_bounds__(kThreads) void gather_kernel(GatherArgs g) {
+  const int kind = blockIdx.z, h = blockIdx.y;
+  const int n = g.n[kind];
+  const int r0 = blockIdx.x * kGatherRows;
+  if (r0 >= n) return;
+  const int chunks = g.row_bytes >> 4;
+  const int rows = min(kGatherRows, n - r0);
+  const int32_t* perm = g.perm[kind] + int64_t(h) * n;
+  const char* src = g.src[kind] + int64_t(h) * g.stride_head[kind] * g.esize;
+  char* dst = g.dst[kind] + (int64_t(h) * n + r0) * g.row_bytes;
+  const int64_t st = g.stride_tok[kind] * g.esize;
+  for (int i = threadIdx.x; i < rows * chunks; i += kThreads) {
+    int r = i / chunks, c = i - r * chunks;
+    int tok = perm[r0 + r];
+    uint4 v = *reinterpret_cast<const uint4*>(src + tok * st + c * 16);
+    *reinterpret_cast<uint4*>(dst + int64_t(r) * g.row_bytes + c * 16) = v;
+  }
+}
+
+// fp64 centroid of each group of the gathered q (kind 0) and k (kind 1).
+// Columns are split over threads, rows over `phases`; phase partials are
+// combined in a fixed order, so the result is deterministic.
+template <typename T>
+SPR_DEV double load_as_f64(const T* p);
+template <>
+SPR_DEV double load_as_f64<uint16_t>(const uint16_t* p) { return double(bf16_to_f32(*p)); }
+template <>
+SPR_DEV double load_as_f64<float>(const float* p) { return double(*p); }
+
+template <typename T>
+__global__ __launch_bounds__(kThreads) void centroid_kernel(const T* q_g, const T* k_g,
+                                                            const int32_t* off_q, const int32_t* off_k,
+                                                            double* cen_q, double* cen_k, int n_q,
+                                                            int n_k, int c_q, int c_k, int d) {
+  const int kind = blockIdx.z, h = blockIdx.y, a = blockIdx.x;
+  const int C = kind == 0 ? c_q : c_k;
+  if (a >= C) return;
+  const int N = kind == 0 ? n_q : n_k;
+  const int32_t* off = (kind == 0 ? off_q : off_k) + int64_t(h) * (C + 1);
+  const T* x = (kind == 0 ? q_g : k_g) + int64_t(h) * N * d;
+  double* cen = (kind == 0 ? cen_q : cen_k) + (int64_t(h) * C + a) * d;
+  __shared__ double part[kThreads];
+  const int phases = kThreads / d;
+  const int j = threadIdx.x % d, ph = threadIdx.x / d;
+  const int lo = off[a], hi = off[a + 1];
+  double s = 0.0;
+  for (int r = lo + ph; r < hi; r += phases) s += load_as_f64(x + int64_t(r) * d + j);
+  part[threadIdx.x] = s;
+  __syncthreads();
+  if (ph == 0) {
+    double t = 0.0;
+    for (int p = 0; p < phases; ++p) t += part[p * d + j];
+    cen[j] = hi > lo ? t / double(hi - lo) : 0.0;
+  }
+}
+
+}  // namespace
+
+size_t layout_ws_bytes(const sparsepr_dims* d) {
+  Carver cv(nullptr);
+  int tq = (d->n_q + kTile - 1) / kTile, tk = (d->n_k + kTile - 1) / kTile;
+  cv.take<int32_t>(size_t(d->heads) * d->c_q * tq);
+  cv.take<int32_t>(size_t(d->heads) * d->c_k * tk);
+  return cv.used;
+}
+
+}  // namespace spr
+
+using namespace spr;
+
+extern "C" int32_t sparsepr_partition_layout(const sparsepr_dims* dims, const int32_t* labels_q,
+                                             const int32_t* labels_kv, const void* q, const void* k,
+                                             const void* v, int32_t* perm_q, int32_t* offsets_q,
+                                             int32_t* perm_kv, int32_t* offsets_kv, void* q_g,
+                                             void* k_g, void* v_g, double* centroid_q,
+                                             double* centroid_k, void* ws, size_t ws_bytes,
+                                             hipStream_t stream) {
+  int32_t st = check_dims(dims);
+  if (st != SPARSEPR_OK) return st;
+  if (!labels_q || !labels_kv || !q || !k || !v || !perm_q || !offsets_q || !perm_kv ||
+      !offsets_kv || !q_g || !k_g || !v_g || !centroid_q || !centroid_k)
+    return SPARSEPR_ERR_INVALID;
+  const size_t need = layout_ws_bytes(dims);
+  if (need > 0 && (!ws || ws_bytes < need)) return SPARSEPR_ERR_WORKSPACE;
+  const int H = dims->heads, d = dims->head_dim;
+  Carver cv(ws);
+  KindArgs qa{labels_q, perm_q, offsets_q, nullptr, dims->n_q, dims->c_q,
+              (dims->n_q + kTile - 1) / kTile};
+  KindArgs ka{labels_kv, perm_kv, offsets_kv, nullptr, dims->n_k, dims->c_k,
+              (dims->n_k + kTile - 1) / kTile};
+  qa.counts = cv.take<int32_t>(size_t(H) * qa.c * qa.ntiles);
+  ka.counts = cv.take<int32_t>(size_t(H) * ka.c * ka.ntiles);
+  const int maxt = qa.ntiles > ka.ntiles ? qa.ntiles : ka.ntiles;
+
+  hist_kernel<<<dim3(maxt, H, 2), kThreads, 0, stream>>>(qa, ka);
+  SPR_LAUNCH_CHECK();
+  scan_kernel<<<dim3(H, 2), 1024, 0, stream>>>(qa, ka);
+  SPR_LAUNCH_CHECK();
+  scatter_kernel<<<dim3(maxt, H, 2), kThreads, 0, stream>>>(qa, ka);
+  SPR_LAUNCH_CHECK();
+
+  const int es = int(elem_bytes(dims->dtype));
+  GatherArgs g;
+  g.src[0] = static_cast<const char*>(q);
+  g.src[1] = static_cast<const char*>(k);
+  g.src[2] = static_cast<const char*>(v);
+  g.dst[0] = static_cast<char*>(q_g);
+  g.dst[1] = static_cast<char*>(k_g);
+  g.dst[2] = static_cast<char*>(v_g);
+  g.perm[0] = perm_q;
+  g.perm[1] = perm_kv;
+  g.perm[2] = perm_kv;
+  g.stride_head[0] = dims->q_stride_head;
+  g.stride_tok[0] = dims->q_stride_tok;
+  g.stride_head[1] = g.stride_head[2] = dims->kv_stride_head;
+  g.stride_tok[1] = g.stride_tok[2] = dims->kv_stride_tok;
+  g.n[0] = dims->n_q;
+  g.n[1] = g.n[2] = dims->n_k;
+  g.row_bytes = d * es;
+  g.esize = es;
+  const int maxn = dims->n_q > dims->n_k ? dims->n_q : dims->n_k;
+  gather_kernel<<<dim3((maxn + kGatherRows - 1) / kGatherRows, H, 3), kThreads, 0, stream>>>(g);
+  SPR_LAUNCH_CHECK();
+
+  const int maxc = dims->c_q > dims->c_k ? dims->c_q : dims->c_k;
+  if (dims->dtype == SPARSEPR_BF16)
+    centroid_kernel<uint16_t><<<dim3(maxc, H, 2), kThreads, 0, stream>>>(
+        static_cast<const uint16_t*>(q_g), static_cast<const uint16_t*>(k_g), offsets_q,
+        offsets_kv, centroid_q, centroid_k, dims->n_q, dims->n_k, dims->c_q, dims->c_k, d);
+  else
+    centroid_kernel<float><<<dim3(maxc, H, 2), kThreads, 0, stream>>>(
+        static_cast<const float*>(q_g), static_cast<const float*>(k_g), offsets_q, offsets_kv,
+        centroid_q, centroid_k, dims->n_q, dims->n_k, dims->c_q, dims->c_k, d);
+  SPR_LAUNCH_CHECK();
+  return SPARSEPR_OK;
+}

@@ -1,0 +1,776 @@
+// S6-S8: probe selection, exact probe rows and the correction fit.
+//
+// SparsePR paper, Appendix A.2 (Algorithm A.1): per non-empty query group,
+// rows are ranked by distance to the group centroid (ties by token index);
+// groups are ordered by decreasing size (ties by group id); traversal t
+// takes the t-th row of every group that still has one, until M probes.
+// Because groups are ordered by size, the groups still holding a t-th row
+// are exactly the first G(t) groups of that order, so the probe taken from
+// group a in traversal t sits at position S(t) + rank(a), where
+// S(t) = sum_a min(n_a, t).  Every group therefore finds its probe slots
+// without a sequential walk.
+//
+// Appendix A.1: with the retained (S) and omitted (U) key sets of the probe's
+// group, Z_S, N_S, Z_U, N_U are the softmax partition sums and value
+// numerators; O_sp = N_S/Z_S, O_dense = (N_S+N_U)/(Z_S+Z_U), and the residual
+// R = O_dense - O_sp = w_U (Z_S N_U - Z_U N_S) / (Z Z_S) is formed without
+// cancelling the retained part.  The probe kernel accumulates the four sums
+// (separate running maxima for S and U) over key chunks; a merge kernel
+// combines the chunks in fp64.
+//
+// Appendix A.2 / D.3 fit, per head in fp64: coverage weights |G_a|/m_a (the
+// review's step (4)), unit-sum weights for the means and the feature scale
+// sqrt(var + 1e-6), unit-mean weights for the ridge; the ridge is solved in
+// its dual (M x M) form B = Xw^T (Xw Xw^T + lam I)^-1 Rw with Xw = W~^1/2
+// Xbar, Rw = W~^1/2 Rbar; the right singular vectors of Rw come from a
+// cyclic Jacobi eigensolve of Rw Rw^T; finally B is folded with the
+// projection into A = diag(1/s) B Psi and c = mu_R - (mu_x A) Psi^T.
+
+#include "common.h"
+
+namespace spr {
+namespace {
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr int kChunks = 64;        // key chunks per head in the probe-row kernel
+constexpr int kMaxM = SPARSEPR_MAX_PROBES;
+
+// ---------------------------------------------------------------------------
+// plan: group ranks, per-group probe counts, S(t) table, default outputs
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(1024) void plan_kernel(const int32_t* __restrict__ off_q, int c_q,
+                                                   int n_q, int m, int32_t* __restrict__ m_a,
+                                                   int32_t* __restrict__ rank_out,
+                                                   int32_t* __restrict__ s_tab,
+                                                   int32_t* __restrict__ probe_rows,
+                                                   int32_t* __restrict__ probe_tokens,
+                                                   int32_t* __restrict__ probe_group) {
+  const int h = blockIdx.x, tid = threadIdx.x;
+  __shared__ int32_t na[SPARSEPR_MAX_GROUPS];
+  __shared__ int32_t cnt[kMaxM + 2];
+  __shared__ int32_t S[kMaxM + 2];
+  __shared__ int32_t sh_T;
+  const int32_t* o = off_q + (long long)h * (c_q + 1);
+  for (int a = tid; a < c_q; a += blockDim.x) na[a] = o[a + 1] - o[a];
+  for (int i = tid; i < kMaxM + 2; i += blockDim.x) cnt[i] = 0;
+  const int me = m < n_q ? m : n_q;
+  for (int i = tid; i < m; i += blockDim.x) {
+    probe_rows[(long long)h * m + i] = -1;
+    probe_tokens[(long long)h * m + i] = -1;
+    probe_group[(long long)h * m + i] = -1;
+  }
+  __syncthreads();
+  // histogram of min(n_a, M+1): G(j) = #{a : n_a >= j}
+  for (int a = tid; a < c_q; a += blockDim.x) {
+    int v = na[a] < kMaxM + 1 ? na[a] : kMaxM + 1;
+    if (v > 0) atomicAdd(&cnt[v], 1);
+  }
+  __syncthreads();
+  if (tid == 0) {
+    int ge = 0;  // #{a : n_a >= j}, built from the top
+    int Gj[kMaxM + 2];
+    for (int j = kMaxM + 1; j >= 1; --j) {
+      ge += cnt[j];
+      Gj[j] = ge;
+    }
+    S[0] = 0;
+    int T = 0;
+    for (int t = 1; t <= kMaxM + 1; ++t) {
+      S[t] = S[t - 1] + Gj[t];
+      if (T == 0 && S[t] >= me) T = t;
+    }
+    sh_T = T;
+  }
+  __syncthreads();
+  const int T = sh_T;
+  const int F = T - 1;
+  const int rem = me - S[F];
+  for (int a = tid; a < c_q; a += blockDim.x) {
+    int r = -1, ma = 0;
+    if (na[a] > 0) {
+      r = 0;
+      for (int b = 0; b < c_q; ++b)
+        if (na[b] > na[a] || (na[b] == na[a] && b < a)) ++r;
+      ma = na[a] < F ? na[a] : F;
+      if (na[a] > F && r < rem) ++ma;
+    }
+    m_a[(long long)h * c_q + a] = ma;
+    rank_out[(long long)h * c_q + a] = r;
+  }
+  for (int t = tid; t <= kMaxM + 1; t += blockDim.x) s_tab[(long long)h * (kMaxM + 2) + t] = S[t];
+}
+
+// ---------------------------------------------------------------------------
+// select: the m_a nearest rows of each probed group, in (distance, row) order
+// ---------------------------------------------------------------------------
+template <typename T>
+SPR_DEV float to_f32(T x);
+template <>
+SPR_DEV float to_f32<uint16_t>(uint16_t x) { return bf16_to_f32(x); }
+template <>
+SPR_DEV float to_f32<float>(float x) { return x; }
+
+template <typename T>
+__global__ __launch_bounds__(256) void select_kernel(
+    const T* __restrict__ q_g, const double* __restrict__ cen, const int32_t* __restrict__ off_q,
+    const int32_t* __restrict__ perm_q, const int32_t* __restrict__ m_a,
+    const int32_t* __restrict__ rank, const int32_t* __restrict__ s_tab, int n_q, int c_q, int d,
+    int m, double* __restrict__ dist, int32_t* __restrict__ probe_rows,
+    int32_t* __restrict__ probe_tokens, int32_t* __restrict__ probe_group) {
+  const int a = blockIdx.x, h = blockIdx.y, tid = threadIdx.x;
+  const int ma = m_a[(long long)h * c_q + a];
+  if (ma == 0) return;
+  __shared__ double cs[128];
+  __shared__ double rd[4];
+  __shared__ int32_t ri[4];
+  const int32_t* o = off_q + (long long)h * (c_q + 1);
+  const int lo = o[a], hi = o[a + 1];
+  const double* c = cen + ((long long)h * c_q + a) * d;
+  for (int j = tid; j < d; j += 256) cs[j] = c[j];
+  __syncthreads();
+  double* dh = dist + (long long)h * n_q;
+  for (int r = lo + tid; r < hi; r += 256) {
+    const T* x = q_g + ((long long)h * n_q + r) * d;
+    double s = 0.0;
+    for (int j = 0; j < d; ++j) {
+      double t = double(to_f32(x[j])) - cs[j];
+      s = fma(t, t, s);
+    }
+    dh[r] = sqrt(s);
+  }
+  __syncthreads();
+  const int rk = rank[(long long)h * c_q + a];
+  double pd = -1.0;
+  int pr = -1;
+  for (int t = 0; t < ma; ++t) {
+    double bd = __builtin_huge_val();
+    int br = 0x7fffffff;
+    for (int r = lo + tid; r < hi; r += 256) {
+      double v = dh[r];
+      bool after = v > pd || (v == pd && r > pr);
+      if (after && (v < bd || (v == bd && r < br))) { bd = v; br = r; }
+    }
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) {
+      double v2 = __shfl_xor(bd, off);
+      int r2 = __shfl_xor(br, off);
+      if (v2 < bd || (v2 == bd && r2 < br)) { bd = v2; br = r2; }
+    }
+    __syncthreads();
+    if ((tid & 63) == 0) { rd[tid >> 6] = bd; ri[tid >> 6] = br; }
+    __syncthreads();
+    bd = rd[0];
+    br = ri[0];
+    for (int w = 1; w < 4; ++w)
+      if (rd[w] < bd || (rd[w] == bd && ri[w] < br)) { bd = rd[w]; br = ri[w]; }
+    if (tid == 0) {
+      const int pos = s_tab[(long long)h * (kMaxM + 2) + t] + rk;
+      probe_rows[(long long)h * m + pos] = br;
+      probe_tokens[(long long)h * m + pos] = perm_q[(long long)h * n_q + br];
+      probe_group[(long long)h * m + pos] = a;
+    }
+    pd = bd;
+    pr = br;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// exact probe rows: retained / omitted partial sums per key chunk (VALU)
+// ---------------------------------------------------------------------------
+// Thread layout: probe p = tid / 4 (64 probes), dim slice sl = tid % 4 of
+// D/4 dims.  Partial record per (head, chunk, probe): [mS, mU, ZS, ZU] and
+// NS[D], NU[D].
+template <typename T, int D>
+__global__ __launch_bounds__(256) void probe_rows_kernel(
+    const T* __restrict__ q_g, const T* __restrict__ k_g, const T* __restrict__ v_g,
+    const int32_t* __restrict__ off_k, const int32_t* __restrict__ rowptr,
+    const int32_t* __restrict__ col, const int32_t* __restrict__ probe_rows,
+    const int32_t* __restrict__ probe_group, int n_q, int n_k, int c_q, int c_k, int m,
+    float scale_log2, float* __restrict__ part_s, float* __restrict__ part_n) {
+  constexpr int DPL = D / 4;
+  constexpr int TK = 32;
+  const int chunk = blockIdx.x, h = blockIdx.y, tid = threadIdx.x;
+  const int p = tid >> 2, sl = tid & 3;
+  __shared__ uint32_t mask[kMaxM][32];
+  __shared__ float ks[TK][D + 4];
+  __shared__ float vs[TK][D + 4];
+  __shared__ int32_t kgrp[TK];
+  __shared__ int32_t okl[SPARSEPR_MAX_GROUPS + 1];
+  for (int i = tid; i < kMaxM * 32; i += 256) (&mask[0][0])[i] = 0u;
+  const int32_t* ok = off_k + (long long)h * (c_k + 1);
+  for (int i = tid; i <= c_k; i += 256) okl[i] = ok[i];
+  __syncthreads();
+  const bool pvalid = p < m && probe_rows[(long long)h * m + p] >= 0;
+  const int grp = pvalid ? probe_group[(long long)h * m + p] : 0;
+  if (pvalid) {
+    const int32_t* rp = rowptr + (long long)h * (c_q + 1);
+    const int32_t* cl = col + (long long)h * c_q * c_k;
+    for (int i = rp[grp] + sl; i < rp[grp + 1]; i += 4) {
+      const int b = cl[i];
+      atomicOr(&mask[p][b >> 5], 1u << (b & 31));
+    }
+  }
+  float q[DPL];
+  {
+    const int row = pvalid ? probe_rows[(long long)h * m + p] : 0;
+    const T* qr = q_g + ((long long)h * n_q + row) * D + sl * DPL;
+#pragma unroll
+    for (int i = 0; i < DPL; ++i) q[i] = pvalid ? to_f32(qr[i]) : 0.f;
+  }
+  float ns[DPL], nu[DPL];
+#pragma unroll
+  for (int i = 0; i < DPL; ++i) ns[i] = nu[i] = 0.f;
+  const float NEG = -__builtin_huge_valf();
+  float mS = NEG, mU = NEG, zS = 0.f, zU = 0.f;
+  const int per = (n_k + kChunks - 1) / kChunks;
+  const int k0 = chunk * per, k1 = min(n_k, k0 + per);
+  const T* Kh = k_g + (long long)h * n_k * D;
+  const T* Vh = v_g + (long long)h * n_k * D;
+  for (int t0 = k0; t0 < k1; t0 += TK) {
+    __syncthreads();
+    for (int e = tid; e < TK * D; e += 256) {
+      const int r = e / D, j = e % D;
+      const int row = t0 + r;
+      float kv = 0.f, vv = 0.f;
+      if (row < k1) {
+        kv = to_f32(Kh[(long long)row * D + j]);
+        vv = to_f32(Vh[(long long)row * D + j]);
+      }
+      ks[r][j] = kv;
+      vs[r][j] = vv;
+    }
+    if (tid < TK) {
+      const int row = t0 + tid;
+      int g = -1;
+      if (row < k1) {
+        int lo = 0, hi = c_k - 1;  // largest b with okl[b] <= row
+        while (lo < hi) {
+          int mid = (lo + hi + 1) >> 1;
+          if (okl[mid] <= row) lo = mid;
+          else hi = mid - 1;
+        }
+        g = lo;
+      }
+      kgrp[tid] = g;
+    }
+    __syncthreads();
+    float s[TK];
+    bool in[TK];
+    float tS = NEG, tU = NEG;
+#pragma unroll
+    for (int j = 0; j < TK; ++j) {
+      float acc = 0.f;
+#pragma unroll
+      for (int i = 0; i < DPL; ++i) acc = fmaf(q[i], ks[j][sl * DPL + i], acc);
+      acc += __shfl_xor(acc, 1);
+      acc += __shfl_xor(acc, 2);
+      const int g = kgrp[j];
+      const bool ok_key = g >= 0;
+      in[j] = ok_key && ((mask[p][g >> 5] >> (g & 31)) & 1u);
+      s[j] = ok_key ? acc * scale_log2 : NEG;
+      if (ok_key) {
+        if (in[j]) tS = fmaxf(tS, s[j]);
+        else tU = fmaxf(tU, s[j]);
+      }
+    }
+    const float nS = fmaxf(mS, tS), nU = fmaxf(mU, tU);
+    const float aS = nS == NEG ? 1.f : exp2f(mS - nS);
+    const float aU = nU == NEG ? 1.f : exp2f(mU - nU);
+    mS = nS;
+    mU = nU;
+    zS *= aS;
+    zU *= aU;
+#pragma unroll
+    for (int i = 0; i < DPL; ++i) {
+      ns[i] *= aS;
+      nu[i] *= aU;
+    }
+#pragma unroll
+    for (int j = 0; j < TK; ++j) {
+      const float e = s[j] == NEG ? 0.f : exp2f(s[j] - (in[j] ? mS : mU));
+      const float eS = in[j] ? e : 0.f, eU = in[j] ? 0.f : e;
+      zS += eS;
+      zU += eU;
+#pragma unroll
+      for (int i = 0; i < DPL; ++i) {
+        const float v = vs[j][sl * DPL + i];
+        ns[i] = fmaf(eS, v, ns[i]);
+        nu[i] = fmaf(eU, v, nu[i]);
+      }
+    }
+  }
+  if (p >= m) return;
+  const long long rec = ((long long)h * kChunks + chunk) * m + p;
+  if (sl == 0) {
+    float* ps = part_s + rec * 4;
+    ps[0] = mS;
+    ps[1] = mU;
+    ps[2] = zS;
+    ps[3] = zU;
+  }
+  float* pn = part_n + rec * 2 * D;
+#pragma unroll
+  for (int i = 0; i < DPL; ++i) {
+    pn[sl * DPL + i] = ns[i];
+    pn[D + sl * DPL + i] = nu[i];
+  }
+}
+
+// ---------------------------------------------------------------------------
+// merge chunks (fp64): O_dense, O_sp and R at every probe
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void merge_kernel(const float* __restrict__ part_s,
+                                                   const float* __restrict__ part_n, int m,
+                                                   int me, int d, float* __restrict__ o_dense,
+                                                   float* __restrict__ o_sparse,
+                                                   double* __restrict__ xp,
+                                                   double* __restrict__ rp) {
+  const int h = blockIdx.x;
+  for (int e = threadIdx.x; e < me * d; e += 256) {
+    const int p = e / d, j = e % d;
+    double MS = -__builtin_huge_val(), MU = -__builtin_huge_val();
+    for (int c = 0; c < kChunks; ++c) {
+      const float* ps = part_s + (((long long)h * kChunks + c) * m + p) * 4;
+      MS = fmax(MS, double(ps[0]));
+      MU = fmax(MU, double(ps[1]));
+    }
+    double zS = 0, zU = 0, nS = 0, nU = 0;
+    for (int c = 0; c < kChunks; ++c) {
+      const long long rec = ((long long)h * kChunks + c) * m + p;
+      const float* ps = part_s + rec * 4;
+      const float* pn = part_n + rec * 2 * d;
+      const double fS = ps[0] == -__builtin_huge_valf() ? 0.0 : exp2(double(ps[0]) - MS);
+      const double fU = ps[1] == -__builtin_huge_valf() ? 0.0 : exp2(double(ps[1]) - MU);
+      zS += fS * ps[2];
+      zU += fU * ps[3];
+      nS += fS * pn[j];
+      nU += fU * pn[d + j];
+    }
+    // common max for the dense row
+    const double M = fmax(MS, MU);
+    const double wS = MS == -__builtin_huge_val() ? 0.0 : exp2(MS - M);
+    const double wU = MU == -__builtin_huge_val() ? 0.0 : exp2(MU - M);
+    const double Z = zS * wS + zU * wU;
+    const double x = nS / zS;
+    const double od = (nS * wS + nU * wU) / Z;
+    const double r = wU * (zS * nU - zU * nS) / (Z * zS);
+    const long long o = ((long long)h * m + p) * d + j;
+    o_dense[o] = float(od);
+    if (o_sparse) o_sparse[o] = float(x);
+    xp[o] = x;
+    rp[o] = r;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// fit (fp64, one block per head)
+// ---------------------------------------------------------------------------
+struct FitArgs {
+  const int32_t* off_q;
+  const int32_t* m_a;
+  const int32_t* probe_group;
+  const double* xp;   // [H][m][d]
+  const double* rp;   // [H][m][d]
+  double* xw;         // [H][m][d] scratch
+  double* rw;         // [H][m][d] scratch
+  double* zbuf;       // [H][64][64] scratch
+  double* abuf;       // [H][d][64] scratch (A, fp64)
+  double* pbuf;       // [H][d][64] scratch (Psi, fp64)
+  float* corr_a;
+  float* corr_psi_t;
+  float* corr_c;
+  int c_q, m, me, d, rank;
+  double lambda;
+};
+
+constexpr int kLd = kMaxM + 1;
+
+__global__ __launch_bounds__(256) void fit_kernel(FitArgs f) {
+  const int h = blockIdx.x, tid = threadIdx.x;
+  const int me = f.me, d = f.d;
+  __shared__ double w[kMaxM], wt[kMaxM];
+  __shared__ double mux[128], mur[128], sc[128];
+  __shared__ double G[kMaxM * kLd];   // Cholesky factor (lower)
+  __shared__ double E[kMaxM * kLd];   // Rw Rw^T, diagonalised in place
+  __shared__ double U[kMaxM * kLd];   // eigenvectors (columns)
+  __shared__ double rc[kMaxM / 2], rs[kMaxM / 2];
+  __shared__ int32_t order[kMaxM];
+  __shared__ double red[4];
+  __shared__ double tcol[kMaxM];
+  __shared__ int32_t sh_k;
+  __shared__ int32_t sh_stop;
+
+  const double* X = f.xp + (long long)h * f.m * d;
+  const double* R = f.rp + (long long)h * f.m * d;
+  double* Xw = f.xw + (long long)h * f.m * d;
+  double* Rw = f.rw + (long long)h * f.m * d;
+
+  // 1. coverage weights |G_a| / m_a
+  const int32_t* oq = f.off_q + (long long)h * (f.c_q + 1);
+  if (tid < me) {
+    const int a = f.probe_group[(long long)h * f.m + tid];
+    w[tid] = double(oq[a + 1] - oq[a]) / double(f.m_a[(long long)h * f.c_q + a]);
+  }
+  __syncthreads();
+  double sw = 0.0;
+  for (int p = 0; p < me; ++p) sw += w[p];
+  if (tid < me) wt[tid] = double(me) * w[tid] / sw;
+  // 2. weighted means and feature scale (unit-sum weights)
+  if (tid < d) {
+    double mx = 0, mr = 0;
+    for (int p = 0; p < me; ++p) {
+      const double wh = w[p] / sw;
+      mx += wh * X[p * d + tid];
+      mr += wh * R[p * d + tid];
+    }
+    double var = 0;
+    for (int p = 0; p < me; ++p) {
+      const double t = X[p * d + tid] - mx;
+      var += (w[p] / sw) * t * t;
+    }
+    mux[tid] = mx;
+    mur[tid] = mr;
+    sc[tid] = sqrt(var + 1e-6);
+  }
+  __syncthreads();
+  // 3. weighted, standardised features and centred residuals
+  for (int e = tid; e < me * d; e += 256) {
+    const int p = e / d, j = e % d;
+    const double sq = sqrt(wt[p]);
+    Xw[e] = sq * (X[e] - mux[j]) / sc[j];
+    Rw[e] = sq * (R[e] - mur[j]);
+  }
+  __syncthreads();
+  // 4. Gram matrices
+  for (int e = tid; e < me * me; e += 256) {
+    const int p = e / me, qq = e % me;
+    if (qq > p) continue;
+    double gx = 0, gr = 0;
+    for (int j = 0; j < d; ++j) {
+      gx = fma(Xw[p * d + j], Xw[qq * d + j], gx);
+      gr = fma(Rw[p * d + j], Rw[qq * d + j], gr);
+    }
+    if (p == qq) gx += f.lambda;
+    G[p * kLd + qq] = gx;
+    G[qq * kLd + p] = gx;
+    E[p * kLd + qq] = gr;
+    E[qq * kLd + p] = gr;
+    U[p * kLd + qq] = p == qq ? 1.0 : 0.0;
+    U[qq * kLd + p] = p == qq ? 1.0 : 0.0;
+  }
+  __syncthreads();
+  // 5. Cholesky G = L L^T (right-looking, lower triangle)
+  for (int k = 0; k < me; ++k) {
+    if (tid == 0) G[k * kLd + k] = sqrt(G[k * kLd + k]);
+    __syncthreads();
+    const double piv = G[k * kLd + k];
+    for (int i = k + 1 + tid; i < me; i += 256) G[i * kLd + k] /= piv;
+    __syncthreads();
+    const int rem = me - k - 1;
+    for (int e = tid; e < rem * rem; e += 256) {
+      const int i = k + 1 + e / rem, j = k + 1 + e % rem;
+      if (j <= i) G[i * kLd + j] -= G[i * kLd + k] * G[j * kLd + k];
+    }
+    __syncthreads();
+  }
+  // 6. cyclic Jacobi on E (round-robin pairs, disjoint rotations per round)
+  const int mp = (me + 1) & ~1;   // even player count; player me is a dummy if me is odd
+  const int npair = mp / 2;
+  for (int sweep = 0; sweep < 40; ++sweep) {
+    for (int rnd = 0; rnd < mp - 1; ++rnd) {
+      if (tid < npair) {
+        int pp, qq;
+        if (tid == 0) { pp = mp - 1; qq = rnd; }
+        else { pp = (rnd + tid) % (mp - 1); qq = (rnd - tid + (mp - 1)) % (mp - 1); }
+        double c = 1.0, s = 0.0;
+        if (pp < me && qq < me) {
+          const double apq = E[pp * kLd + qq];
+          if (apq != 0.0) {
+            const double app = E[pp * kLd + pp], aqq = E[qq * kLd + qq];
+            const double tau = (aqq - app) / (2.0 * apq);
+            const double t = (tau >= 0 ? 1.0 : -1.0) / (fabs(tau) + sqrt(1.0 + tau * tau));
+            c = 1.0 / sqrt(1.0 + t * t);
+            s = t * c;
+          }
+        }
+        rc[tid] = c;
+        rs[tid] = s;
+      }
+      __syncthreads();
+      // rows: E <- J^T E
+      for (int e = tid; e < npair * me; e += 256) {
+        const int i = e / me, j = e % me;
+        int pp, qq;
+        if (i == 0) { pp = mp - 1; qq = rnd; }
+        else { pp = (rnd + i) % (mp - 1); qq = (rnd - i + (mp - 1)) % (mp - 1); }
+        if (pp >= me || qq >= me) continue;
+        const double c = rc[i], s = rs[i];
+        const double xp_ = E[pp * kLd + j], xq = E[qq * kLd + j];
+        E[pp * kLd + j] = c * xp_ - s * xq;
+        E[qq * kLd + j] = s * xp_ + c * xq;
+      }
+      __syncthreads();
+      // columns: E <- E J, U <- U J
+      for (int e = tid; e < npair * me; e += 256) {
+        const int i = e / me, j = e % me;
+        int pp, qq;
+        if (i == 0) { pp = mp - 1; qq = rnd; }
+        else { pp = (rnd + i) % (mp - 1); qq = (rnd - i + (mp - 1)) % (mp - 1); }
+        if (pp >= me || qq >= me) continue;
+        const double c = rc[i], s = rs[i];
+        const double xp_ = E[j * kLd + pp], xq = E[j * kLd + qq];
+        E[j * kLd + pp] = c * xp_ - s * xq;
+        E[j * kLd + qq] = s * xp_ + c * xq;
+        const double up = U[j * kLd + pp], uq = U[j * kLd + qq];
+        U[j * kLd + pp] = c * up - s * uq;
+        U[j * kLd + qq] = s * up + c * uq;
+      }
+      __syncthreads();
+    }
+    // convergence: off-diagonal mass relative to the diagonal
+    double off = 0.0, dg = 0.0;
+    for (int e = tid; e < me * me; e += 256) {
+      const int i = e / me, j = e % me;
+      const double v = E[i * kLd + j];
+      if (i == j) dg += v * v;
+      else off += v * v;
+    }
+    const double OFF = block_sum(off, red);
+    const double DG = block_sum(dg, red);
+    if (tid == 0) sh_stop = (OFF <= 1e-30 * DG) || DG == 0.0;
+    __syncthreads();
+    if (sh_stop) break;
+  }
+  // 7. order eigenvalues (descending, ties by index), decide kept directions
+  if (tid < me) {
+    const double li = E[tid * kLd + tid];
+    int r = 0;
+    for (int j = 0; j < me; ++j) {
+      const double lj = E[j * kLd + j];
+      if (lj > li || (lj == li && j < tid)) ++r;
+    }
+    order[r] = tid;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    const double l1 = E[order[0] * kLd + order[0]];
+    const double s1 = l1 > 0 ? sqrt(l1) : 0.0;
+    int k = 0;
+    if (s1 > 0) {
+      const double floor_l = 64.0 * 2.220446049250313e-16 * l1;  // resolution of the Gram route
+      for (int i = 0; i < me; ++i) {
+        const double li = E[order[i] * kLd + order[i]];
+        if (li > floor_l && sqrt(li) > 1e-10 * s1) ++k;
+        else break;
+      }
+    }
+    int cap = f.rank < me ? f.rank : me;
+    cap = cap < d ? cap : d;
+    sh_k = k < cap ? k : cap;
+  }
+  __syncthreads();
+  const int k = sh_k;
+  double* Z = f.zbuf + (long long)h * kMaxM * kMaxM;
+  // 8. z_c = G^-1 (u_c sigma_c): forward then backward substitution, one thread per c
+  if (tid < k) {
+    const int ii = order[tid];
+    const double sig = sqrt(E[ii * kLd + ii]);
+    double* z = Z + tid * kMaxM;
+    for (int i = 0; i < me; ++i) {
+      double s = U[i * kLd + ii] * sig;
+      for (int j = 0; j < i; ++j) s -= G[i * kLd + j] * z[j];
+      z[i] = s / G[i * kLd + i];
+    }
+    for (int i = me - 1; i >= 0; --i) {
+      double s = z[i];
+      for (int j = i + 1; j < me; ++j) s -= G[j * kLd + i] * z[j];
+      z[i] = s / G[i * kLd + i];
+    }
+  }
+  __syncthreads();
+  double* Ab = f.abuf + (long long)h * d * kMaxM;
+  double* Pb = f.pbuf + (long long)h * d * kMaxM;
+  for (int e = tid; e < d * k; e += 256) {
+    const int j = e / k, c = e % k;
+    const int ii = order[c];
+    const double sig = sqrt(E[ii * kLd + ii]);
+    const double* z = Z + c * kMaxM;
+    double bpsi = 0.0, psi = 0.0;
+    for (int p = 0; p < me; ++p) {
+      bpsi = fma(Xw[p * d + j], z[p], bpsi);
+      psi = fma(Rw[p * d + j], U[p * kLd + ii], psi);
+    }
+    Ab[j * kMaxM + c] = bpsi / sc[j];
+    Pb[j * kMaxM + c] = psi / sig;
+  }
+  __syncthreads();
+  // 9. c = mu_R - (mu_x A) Psi^T
+  if (tid < k) {
+    double t = 0.0;
+    for (int j = 0; j < d; ++j) t = fma(mux[j], Ab[j * kMaxM + tid], t);
+    tcol[tid] = t;
+  }
+  __syncthreads();
+  float* oa = f.corr_a + (long long)h * d * f.rank;
+  float* op = f.corr_psi_t + (long long)h * f.rank * d;
+  float* ocv = f.corr_c + (long long)h * d;
+  for (int e = tid; e < d * f.rank; e += 256) {
+    const int j = e / f.rank, c = e % f.rank;
+    oa[e] = c < k ? float(Ab[j * kMaxM + c]) : 0.f;
+  }
+  for (int e = tid; e < f.rank * d; e += 256) {
+    const int c = e / d, j = e % d;
+    op[e] = c < k ? float(Pb[j * kMaxM + c]) : 0.f;
+  }
+  for (int j = tid; j < d; j += 256) {
+    double v = mur[j];
+    for (int c = 0; c < k; ++c) v -= tcol[c] * Pb[j * kMaxM + c];
+    ocv[j] = float(v);
+  }
+}
+
+struct ProbeWs {
+  int32_t *m_a, *rank, *s_tab, *group;
+  double* dist;
+  float *part_s, *part_n;
+  double *xp, *rp, *xw, *rw, *z, *a, *psi;
+};
+
+ProbeWs carve_probe(void* base, const sparsepr_dims* d, int m) {
+  Carver cv(base);
+  const size_t H = d->heads;
+  ProbeWs w;
+  w.m_a = cv.take<int32_t>(H * d->c_q);
+  w.rank = cv.take<int32_t>(H * d->c_q);
+  w.s_tab = cv.take<int32_t>(H * (kMaxM + 2));
+  w.group = cv.take<int32_t>(H * m);
+  w.dist = cv.take<double>(H * d->n_q);
+  w.part_s = cv.take<float>(H * kChunks * m * 4);
+  w.part_n = cv.take<float>(H * kChunks * m * 2 * d->head_dim);
+  w.xp = cv.take<double>(H * m * d->head_dim);
+  w.rp = cv.take<double>(H * m * d->head_dim);
+  w.xw = cv.take<double>(H * m * d->head_dim);
+  w.rw = cv.take<double>(H * m * d->head_dim);
+  w.z = cv.take<double>(H * kMaxM * kMaxM);
+  w.a = cv.take<double>(H * d->head_dim * kMaxM);
+  w.psi = cv.take<double>(H * d->head_dim * kMaxM);
+  // record the size in the last pointer slot via a dummy take
+  return w;
+}
+
+}  // namespace
+
+size_t probe_ws_bytes(const sparsepr_dims* d, int32_t m, int32_t rank) {
+  (void)rank;
+  Carver cv(nullptr);
+  const size_t H = d->heads;
+  cv.take<int32_t>(H * d->c_q);
+  cv.take<int32_t>(H * d->c_q);
+  cv.take<int32_t>(H * (kMaxM + 2));
+  cv.take<int32_t>(H * m);
+  cv.take<double>(H * d->n_q);
+  cv.take<float>(H * kChunks * m * 4);
+  cv.take<float>(H * kChunks * m * 2 * d->head_dim);
+  cv.take<double>(H * m * d->head_dim);
+  cv.take<double>(H * m * d->head_dim);
+  cv.take<double>(H * m * d->head_dim);
+  cv.take<double>(H * m * d->head_dim);
+  cv.take<double>(H * kMaxM * kMaxM);
+  cv.take<double>(H * d->head_dim * kMaxM);
+  cv.take<double>(H * d->head_dim * kMaxM);
+  return cv.used;
+}
+
+}  // namespace spr
+
+using namespace spr;
+
+extern "C" int32_t sparsepr_probe_fit(const sparsepr_dims* dims, int32_t m, int32_t rank,
+                                      double lambda, const int32_t* offsets_q,
+                                      const int32_t* offsets_kv, const int32_t* perm_q,
+                                      const int32_t* cell_rowptr, const int32_t* cell_col,
+                                      const double* centroid_q, const void* q_g, const void* k_g,
+                                      const void* v_g, float softmax_scale, int32_t* probe_rows,
+                                      int32_t* probe_tokens, float* o_probe_dense,
+                                      float* o_probe_sparse, float* corr_a, float* corr_psi_t,
+                                      float* corr_c, void* ws, size_t ws_bytes,
+                                      hipStream_t stream) {
+  int32_t st = check_dims(dims);
+  if (st != SPARSEPR_OK) return st;
+  if (m < 1 || m > SPARSEPR_MAX_PROBES || rank < 0 || rank > SPARSEPR_MAX_RANK || !(lambda >= 0.0))
+    return SPARSEPR_ERR_INVALID;
+  if (!offsets_q || !offsets_kv || !perm_q || !cell_rowptr || !cell_col || !centroid_q || !q_g ||
+      !k_g || !v_g || !probe_rows || !probe_tokens || !o_probe_dense || !corr_a || !corr_psi_t ||
+      !corr_c)
+    return SPARSEPR_ERR_INVALID;
+  if (rank > 0 && lambda == 0.0) return SPARSEPR_ERR_INVALID;  // dual solve needs lam > 0
+  const size_t need = probe_ws_bytes(dims, m, rank);
+  if (!ws || ws_bytes < need) return SPARSEPR_ERR_WORKSPACE;
+  ProbeWs w = carve_probe(ws, dims, m);
+  const int H = dims->heads, d = dims->head_dim;
+  const int me = m < dims->n_q ? m : dims->n_q;
+  plan_kernel<<<H, 1024, 0, stream>>>(offsets_q, dims->c_q, dims->n_q, m, w.m_a, w.rank, w.s_tab,
+                                      probe_rows, probe_tokens, w.group);
+  SPR_LAUNCH_CHECK();
+  const float sl2 = softmax_scale * kLog2e;
+  if (dims->dtype == SPARSEPR_BF16) {
+    select_kernel<uint16_t><<<dim3(dims->c_q, H), 256, 0, stream>>>(
+        static_cast<const uint16_t*>(q_g), centroid_q, offsets_q, perm_q, w.m_a, w.rank, w.s_tab,
+        dims->n_q, dims->c_q, d, m, w.dist, probe_rows, probe_tokens, w.group);
+    SPR_LAUNCH_CHECK();
+    auto* qq = static_cast<const uint16_t*>(q_g);
+    auto* kk = static_cast<const uint16_t*>(k_g);
+    auto* vv = static_cast<const uint16_t*>(v_g);
+    if (d == 128)
+      probe_rows_kernel<uint16_t, 128><<<dim3(kChunks, H), 256, 0, stream>>>(
+          qq, kk, vv, offsets_kv, cell_rowptr, cell_col, probe_rows, w.group, dims->n_q,
+          dims->n_k, dims->c_q, dims->c_k, m, sl2, w.part_s, w.part_n);
+    else
+      probe_rows_kernel<uint16_t, 64><<<dim3(kChunks, H), 256, 0, stream>>>(
+          qq, kk, vv, offsets_kv, cell_rowptr, cell_col, probe_rows, w.group, dims->n_q,
+          dims->n_k, dims->c_q, dims->c_k, m, sl2, w.part_s, w.part_n);
+  } else {
+    select_kernel<float><<<dim3(dims->c_q, H), 256, 0, stream>>>(
+        static_cast<const float*>(q_g), centroid_q, offsets_q, perm_q, w.m_a, w.rank, w.s_tab,
+        dims->n_q, dims->c_q, d, m, w.dist, probe_rows, probe_tokens, w.group);
+    SPR_LAUNCH_CHECK();
+    auto* qq = static_cast<const float*>(q_g);
+    auto* kk = static_cast<const float*>(k_g);
+    auto* vv = static_cast<const float*>(v_g);
+    if (d == 128)
+      probe_rows_kernel<float, 128><<<dim3(kChunks, H), 256, 0, stream>>>(
+          qq, kk, vv, offsets_kv, cell_rowptr, cell_col, probe_rows, w.group, dims->n_q,
+          dims->n_k, dims->c_q, dims->c_k, m, sl2, w.part_s, w.part_n);
+    else
+      probe_rows_kernel<float, 64><<<dim3(kChunks, H), 256, 0, stream>>>(
+          qq, kk, vv, offsets_kv, cell_rowptr, cell_col, probe_rows, w.group, dims->n_q,
+          dims->n_k, dims->c_q, dims->c_k, m, sl2, w.part_s, w.part_n);
+  }
+  SPR_LAUNCH_CHECK();
+  merge_kernel<<<H, 256, 0, stream>>>(w.part_s, w.part_n, m, me, d, o_probe_dense, o_probe_sparse,
+                                      w.xp, w.rp);
+  SPR_LAUNCH_CHECK();
+  FitArgs fa;
+  fa.off_q = offsets_q;
+  fa.m_a = w.m_a;
+  fa.probe_group = w.group;
+  fa.xp = w.xp;
+  fa.rp = w.rp;
+  fa.xw = w.xw;
+  fa.rw = w.rw;
+  fa.zbuf = w.z;
+  fa.abuf = w.a;
+  fa.pbuf = w.psi;
+  fa.corr_a = corr_a;
+  fa.corr_psi_t = corr_psi_t;
+  fa.corr_c = corr_c;
+  fa.c_q = dims->c_q;
+  fa.m = m;
+  fa.me = me;
+  fa.d = d;
+  fa.rank = rank;
+  fa.lambda = lambda;
+  fit_kernel<<<H, 256, 0, stream>>>(fa);
+  SPR_LAUNCH_CHECK();
+  return SPARSEPR_OK;
+}

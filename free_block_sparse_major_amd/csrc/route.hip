@@ -1,0 +1,345 @@
+// S3-S4: cell routing under a routed pair budget.
+//
+// SparsePR paper §4.3: every selected cell G_a x G_b costs |G_a||G_b| exact
+// interactions and the router keeps the shortest prefix of ranked cells that
+// reaches the pair budget (probe cost reserved by the caller).  The score is
+// the centroid logit s_ab = qbar_a . kbar_b / sqrt(d) (the value-aware score
+// the paper uses is not printed on its pages); every non-empty query group
+// first keeps its best cell, then cells follow in (s desc, a asc, b asc)
+// order.
+//
+// The greedy walk is equivalent to: find the crossing cell e* -- the first
+// cell (in that order) at which forced pairs + running pairs reach the
+// budget -- and select every candidate ordered at or before e*.  e* is found
+// without sorting: a 4096-bucket weighted histogram over the score range
+// narrows the search to one bucket, repeated until at most kCap candidates
+// remain, which are ranked by brute force in LDS.  Pair counts are int64.
+
+#include "common.h"
+
+namespace spr {
+namespace {
+
+constexpr int kSelThreads = 1024;
+constexpr int kBuckets = 4096;
+constexpr int kCap = 2048;
+
+// scores[h][a][b] = dot(cq[h][a], ck[h][b]) / sqrt_d, fp64; tile 16 x 64.
+__global__ __launch_bounds__(256) void score_kernel(const double* __restrict__ cq,
+                                                   const double* __restrict__ ck,
+                                                   double* __restrict__ scores, int c_q, int c_k,
+                                                   int d, double sqrt_d) {
+  const int a0 = blockIdx.x * 16, b0 = blockIdx.y * 64, h = blockIdx.z;
+  __shared__ double As[16][33];
+  __shared__ double Bs[64][33];
+  const int ta = threadIdx.x >> 4, tb = threadIdx.x & 15;
+  const double* Q = cq + int64_t(h) * c_q * d;
+  const double* K = ck + int64_t(h) * c_k * d;
+  double acc[4] = {0.0, 0.0, 0.0, 0.0};
+  for (int d0 = 0; d0 < d; d0 += 32) {
+    for (int i = threadIdx.x; i < 16 * 32; i += 256) {
+      int r = i >> 5, c = i & 31;
+      As[r][c] = a0 + r < c_q ? Q[int64_t(a0 + r) * d + d0 + c] : 0.0;
+    }
+    for (int i = threadIdx.x; i < 64 * 32; i += 256) {
+      int r = i >> 5, c = i & 31;
+      Bs[r][c] = b0 + r < c_k ? K[int64_t(b0 + r) * d + d0 + c] : 0.0;
+    }
+    __syncthreads();
+#pragma unroll 8
+    for (int j = 0; j < 32; ++j) {
+      double av = As[ta][j];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc[i] = fma(av, Bs[tb + 16 * i][j], acc[i]);
+    }
+    __syncthreads();
+  }
+  const int a = a0 + ta;
+  if (a >= c_q) return;
+  double* S = scores + (int64_t(h) * c_q + a) * c_k;
+  for (int i = 0; i < 4; ++i) {
+    int b = b0 + tb + 16 * i;
+    if (b < c_k) S[b] = acc[i] / sqrt_d;
+  }
+}
+
+enum { kModeNone = 0, kModeAll = 1, kModeThresh = 2 };
+
+__global__ __launch_bounds__(kSelThreads) void select_kernel(
+    const double* __restrict__ scores, const int32_t* __restrict__ off_q,
+    const int32_t* __restrict__ off_k, int c_q, int c_k, long long budget,
+    int32_t* __restrict__ rowptr, int32_t* __restrict__ col, long long* __restrict__ routed) {
+  const int h = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int nw = kSelThreads / 64;
+  __shared__ int32_t na[SPARSEPR_MAX_GROUPS], mb[SPARSEPR_MAX_GROUPS];
+  __shared__ int32_t forced[SPARSEPR_MAX_GROUPS], rc[SPARSEPR_MAX_GROUPS];
+  __shared__ long long hist[kBuckets];
+  __shared__ double cand_s[kCap];
+  __shared__ int32_t cand_i[kCap];
+  __shared__ long long red[kSelThreads / 64];
+  __shared__ double redd[kSelThreads / 64];
+  __shared__ int32_t slot;
+  __shared__ long long sh_tp;
+  __shared__ int32_t sh_j;
+  __shared__ double sh_es;
+  __shared__ int32_t sh_ei;
+
+  const int32_t* oq = off_q + int64_t(h) * (c_q + 1);
+  const int32_t* ok = off_k + int64_t(h) * (c_k + 1);
+  for (int i = tid; i < c_q; i += kSelThreads) na[i] = oq[i + 1] - oq[i];
+  for (int i = tid; i < c_k; i += kSelThreads) mb[i] = ok[i + 1] - ok[i];
+  __syncthreads();
+  if (tid == 0) { sh_es = 0.0; sh_ei = -1; }
+  const double* S = scores + int64_t(h) * c_q * c_k;
+  const int cells = c_q * c_k;
+
+  // forced cell of every non-empty query group: best score, ties -> smaller b
+  for (int a = wid; a < c_q; a += nw) {
+    double best = 0.0;
+    int bb = -1;
+    if (na[a] > 0) {
+      for (int b = lane; b < c_k; b += 64) {
+        if (mb[b] == 0) continue;
+        double s = S[int64_t(a) * c_k + b];
+        if (bb < 0 || s > best) { best = s; bb = b; }
+      }
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+      double s2 = __shfl_xor(best, o);
+      int b2 = __shfl_xor(bb, o);
+      bool take = b2 >= 0 && (bb < 0 || s2 > best || (s2 == best && b2 < bb));
+      if (take) { best = s2; bb = b2; }
+    }
+    if (lane == 0) forced[a] = bb;
+  }
+  __syncthreads();
+  long long fpart = 0;
+  for (int a = tid; a < c_q; a += kSelThreads)
+    if (forced[a] >= 0) fpart += (long long)na[a] * mb[forced[a]];
+  const long long F = block_sum(fpart, red);
+
+  auto is_cand = [&](int idx) -> bool {
+    int a = idx / c_k, b = idx - a * c_k;
+    return na[a] > 0 && mb[b] > 0 && b != forced[a];
+  };
+  auto weight = [&](int idx) -> long long {
+    int a = idx / c_k, b = idx - a * c_k;
+    return (long long)na[a] * mb[b];
+  };
+
+  int mode = kModeNone;
+  double es = 0.0;
+  int ei = -1;
+  long long T = budget - F;
+  if (T > 0) {
+    long long wpart = 0;
+    for (int idx = tid; idx < cells; idx += kSelThreads)
+      if (is_cand(idx)) wpart += weight(idx);
+    const long long W = block_sum(wpart, red);
+    if (W <= T) {
+      mode = kModeAll;
+    } else {
+      mode = kModeThresh;
+      // initial score interval over all candidates
+      double lmin = __builtin_huge_val(), lmax = -__builtin_huge_val();
+      for (int idx = tid; idx < cells; idx += kSelThreads)
+        if (is_cand(idx)) {
+          double s = S[idx];
+          lmin = s < lmin ? s : lmin;
+          lmax = s > lmax ? s : lmax;
+        }
+      double lo = block_min(lmin, redd);
+      double hi = block_max(lmax, redd);
+      long long Tp = T;  // target inside [lo, hi]; weight above hi already taken
+      for (int iter = 0; iter < 200; ++iter) {
+        if (lo == hi) {
+          // all remaining candidates tie on the score: order by cell index
+          const int per = (cells + kSelThreads - 1) / kSelThreads;
+          const int i0 = tid * per, i1 = min(cells, i0 + per);
+          long long part = 0;
+          for (int idx = i0; idx < i1; ++idx)
+            if (is_cand(idx) && S[idx] == lo) part += weight(idx);
+          long long tot;
+          long long run = block_exclusive_scan(part, red, &tot);
+          for (int idx = i0; idx < i1; ++idx)
+            if (is_cand(idx) && S[idx] == lo) {
+              long long w = weight(idx);
+              if (run < Tp && Tp <= run + w) { sh_es = lo; sh_ei = idx; }
+              run += w;
+            }
+          __syncthreads();
+          es = sh_es;
+          ei = sh_ei;
+          break;
+        }
+        long long cpart = 0;
+        for (int idx = tid; idx < cells; idx += kSelThreads)
+          if (is_cand(idx)) {
+            double s = S[idx];
+            if (s >= lo && s <= hi) ++cpart;
+          }
+        const long long cnt = block_sum(cpart, red);
+        if (cnt <= kCap) {
+          if (tid == 0) slot = 0;
+          __syncthreads();
+          for (int idx = tid; idx < cells; idx += kSelThreads)
+            if (is_cand(idx)) {
+              double s = S[idx];
+              if (s >= lo && s <= hi) {
+                int p = atomicAdd(&slot, 1);
+                cand_s[p] = s;
+                cand_i[p] = idx;
+              }
+            }
+          __syncthreads();
+          const int n = slot;
+          for (int i = tid; i < n; i += kSelThreads) {
+            const double si = cand_s[i];
+            const int ii = cand_i[i];
+            long long pre = 0;
+            for (int j = 0; j < n; ++j) {
+              double sj = cand_s[j];
+              if (sj > si || (sj == si && cand_i[j] < ii)) pre += weight(cand_i[j]);
+            }
+            long long w = weight(ii);
+            if (pre < Tp && Tp <= pre + w) { sh_es = si; sh_ei = ii; }
+          }
+          __syncthreads();
+          es = sh_es;
+          ei = sh_ei;
+          break;
+        }
+        // weighted histogram over [lo, hi]
+        for (int i = tid; i < kBuckets; i += kSelThreads) hist[i] = 0;
+        __syncthreads();
+        const double span = hi - lo;
+        auto bucket = [&](double s) -> int {
+          double f = (s - lo) / span * double(kBuckets);
+          int bk = int(f);
+          return bk < kBuckets ? bk : kBuckets - 1;
+        };
+        for (int idx = tid; idx < cells; idx += kSelThreads)
+          if (is_cand(idx)) {
+            double s = S[idx];
+            if (s >= lo && s <= hi) atomicAdd((unsigned long long*)&hist[bucket(s)],
+                                              (unsigned long long)weight(idx));
+          }
+        __syncthreads();
+        if (tid == 0) {
+          long long acc = 0;
+          int j = kBuckets - 1;
+          for (; j > 0; --j) {
+            if (acc + hist[j] >= Tp) break;
+            acc += hist[j];
+          }
+          sh_j = j;
+          sh_tp = Tp - acc;
+        }
+        __syncthreads();
+        const int jb = sh_j;
+        Tp = sh_tp;
+        double bmin = __builtin_huge_val(), bmax = -__builtin_huge_val();
+        for (int idx = tid; idx < cells; idx += kSelThreads)
+          if (is_cand(idx)) {
+            double s = S[idx];
+            if (s >= lo && s <= hi && bucket(s) == jb) {
+              bmin = s < bmin ? s : bmin;
+              bmax = s > bmax ? s : bmax;
+            }
+          }
+        const double nlo = block_min(bmin, redd);
+        const double nhi = block_max(bmax, redd);
+        lo = nlo;
+        hi = nhi;
+      }
+    }
+  }
+
+  // final selection -> per-row counts -> CSR
+  auto selected = [&](int a, int b) -> bool {
+    if (na[a] == 0 || mb[b] == 0) return false;
+    if (b == forced[a]) return true;
+    if (mode == kModeAll) return true;
+    if (mode == kModeNone) return false;
+    double s = S[int64_t(a) * c_k + b];
+    int idx = a * c_k + b;
+    return s > es || (s == es && idx <= ei);
+  };
+  for (int a = wid; a < c_q; a += nw) {
+    int cnt = 0;
+    for (int b0 = 0; b0 < c_k; b0 += 64) {
+      int b = b0 + lane;
+      bool f = b < c_k && selected(a, b);
+      cnt += __popcll(__ballot(f));
+    }
+    if (lane == 0) rc[a] = cnt;
+  }
+  __syncthreads();
+  long long mine = tid < c_q ? rc[tid] : 0;
+  long long tot;
+  long long pre = block_exclusive_scan(mine, red, &tot);
+  int32_t* rp = rowptr + int64_t(h) * (c_q + 1);
+  if (tid < c_q) rp[tid] = int32_t(pre);
+  if (tid == 0) rp[c_q] = int32_t(tot);
+  __syncthreads();
+  if (tid < c_q) rc[tid] = int32_t(pre);  // reuse as row start
+  __syncthreads();
+  int32_t* cl = col + int64_t(h) * c_q * c_k;
+  long long ppart = 0;
+  for (int a = wid; a < c_q; a += nw) {
+    int pos = rc[a];
+    for (int b0 = 0; b0 < c_k; b0 += 64) {
+      int b = b0 + lane;
+      bool f = b < c_k && selected(a, b);
+      unsigned long long m = __ballot(f);
+      if (f) {
+        int p = __popcll(m & ((1ull << lane) - 1ull));
+        cl[pos + p] = b;
+        ppart += (long long)na[a] * mb[b];
+      }
+      pos += __popcll(m);
+    }
+  }
+  const long long P = block_sum(ppart, red);
+  if (tid == 0) routed[h] = P;
+}
+
+}  // namespace
+
+size_t route_ws_bytes(const sparsepr_dims* d) {
+  Carver cv(nullptr);
+  cv.take<double>(size_t(d->heads) * d->c_q * d->c_k);
+  return cv.used;
+}
+
+}  // namespace spr
+
+using namespace spr;
+
+extern "C" int32_t sparsepr_route_cells(const sparsepr_dims* dims, const int32_t* offsets_q,
+                                        const int32_t* offsets_kv, const double* centroid_q,
+                                        const double* centroid_k, int64_t routed_pair_budget,
+                                        int32_t* cell_rowptr, int32_t* cell_col,
+                                        int64_t* routed_pairs, void* ws, size_t ws_bytes,
+                                        hipStream_t stream) {
+  int32_t st = check_dims(dims);
+  if (st != SPARSEPR_OK) return st;
+  if (!offsets_q || !offsets_kv || !centroid_q || !centroid_k || !cell_rowptr || !cell_col ||
+      !routed_pairs)
+    return SPARSEPR_ERR_INVALID;
+  const size_t need = route_ws_bytes(dims);
+  if (!ws || ws_bytes < need) return SPARSEPR_ERR_WORKSPACE;
+  Carver cv(ws);
+  double* scores = cv.take<double>(size_t(dims->heads) * dims->c_q * dims->c_k);
+  const int H = dims->heads, d = dims->head_dim;
+  dim3 g1((dims->c_q + 15) / 16, (dims->c_k + 63) / 64, H);
+  score_kernel<<<g1, 256, 0, stream>>>(centroid_q, centroid_k, scores, dims->c_q, dims->c_k, d,
+                                       __builtin_sqrt(double(d)));
+  SPR_LAUNCH_CHECK();
+  select_kernel<<<H, kSelThreads, 0, stream>>>(scores, offsets_q, offsets_kv, dims->c_q,
+                                               dims->c_k, (long long)routed_pair_budget,
+                                               cell_rowptr, cell_col, (long long*)routed_pairs);
+  SPR_LAUNCH_CHECK();
+  return SPARSEPR_OK;
+}

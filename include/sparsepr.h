@@ -1,0 +1,229 @@
+/*
+ * sparsepr.h -- C ABI of the MI355X (gfx950) SparsePR attention-call library.
+ *
+ * One SparsePR attention call ("Partition the Support, Reconstruct the
+ * Residual: Training-Free Sparse Attention for Video Generation and World
+ * Models", the SparsePR paper) runs five library calls in this order:
+ *
+ *   sparsepr_partition_layout  group-major permutation + gather + centroids
+ *   sparsepr_route_cells       centroid-logit routing under a pair budget
+ *   sparsepr_sparse_attn       renormalised hard-drop attention on the cells
+ *   sparsepr_probe_fit         Algorithm A.1 probes, exact probe rows, ridge
+ *                              fit and residual-subspace projection
+ *   sparsepr_correct           corrected output in original token order
+ *
+ * probe_fit does not read the sparse-attention output, so it may run on a
+ * second stream concurrently with sparse_attn (both only read what
+ * partition_layout and route_cells wrote).
+ *
+ * Conventions shared by every call
+ *   - Every pointer argument is a DEVICE pointer unless marked (host).
+ *     Every buffer is allocated, owned and freed by the caller; the library
+ *     keeps no pointer after a call returns and holds no mutable global
+ *     state.  Calls are thread-safe.
+ *   - Calls are asynchronous on `stream` and never synchronise the device;
+ *     inputs must stay valid until the stream reaches the call.
+ *   - Scratch memory is the caller's `ws` of `ws_bytes` bytes, at least
+ *     sparsepr_workspace_bytes(call, dims, m, rank) (256-byte aligned).
+ *     A workspace may be reused by the next call on the same stream.
+ *   - Tensors listed as [H][N][d] are dense, row-major, head-major.
+ *   - Data errors (labels outside [0, C), NaN inputs) are the caller's
+ *     contract and are not detected: NaN/Inf propagate into the outputs,
+ *     and out-of-range labels give undefined results.
+ *   - Return value: SPARSEPR_OK, or an error code; on error nothing was
+ *     launched.
+ */
+#ifndef SPARSEPR_H
+#define SPARSEPR_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+  SPARSEPR_OK = 0,
+  SPARSEPR_ERR_INVALID = 1,      /* null pointer, bad size, m < 1, rank < 0, ... */
+  SPARSEPR_ERR_UNSUPPORTED = 2,  /* head_dim not 64/128, dtype, C_q or C_k > 1024 */
+  SPARSEPR_ERR_WORKSPACE = 3,    /* ws_bytes smaller than required */
+  SPARSEPR_ERR_HIP = 4           /* a kernel launch failed */
+};
+
+enum { SPARSEPR_BF16 = 0, SPARSEPR_F32 = 1 };
+
+enum {
+  SPARSEPR_CALL_PARTITION_LAYOUT = 0,
+  SPARSEPR_CALL_ROUTE_CELLS = 1,
+  SPARSEPR_CALL_SPARSE_ATTN = 2,
+  SPARSEPR_CALL_PROBE_FIT = 3,
+  SPARSEPR_CALL_CORRECT = 4
+};
+
+#define SPARSEPR_MAX_GROUPS 1024
+#define SPARSEPR_MAX_PROBES 64
+#define SPARSEPR_MAX_RANK 64
+
+/*
+ * Shape of one attention call (self-attention with N_q queries and N_k
+ * paired key/value tokens per head, head dimension d; SparsePR paper §3
+ * problem setup).  Strides describe the caller's q/k/v inputs in ELEMENTS,
+ * so both [H][N][d] (stride_head = N*d, stride_tok = d) and [N][H][d]
+ * (stride_head = d, stride_tok = H*d) model layouts are accepted; the last
+ * dimension must be contiguous.  k and v share kv strides.
+ */
+typedef struct sparsepr_dims {
+  int32_t heads;       /* H >= 1 */
+  int32_t n_q;         /* N_q >= 1 */
+  int32_t n_k;         /* N_k >= 1 */
+  int32_t head_dim;    /* d: 64 or 128 */
+  int32_t dtype;       /* SPARSEPR_BF16 or SPARSEPR_F32 (q, k, v and gathered copies) */
+  int32_t c_q;         /* query groups, 1..1024 */
+  int32_t c_k;         /* key/value groups, 1..1024 */
+  int32_t reserved;    /* must be 0 */
+  int64_t q_stride_head, q_stride_tok;
+  int64_t kv_stride_head, kv_stride_tok;
+} sparsepr_dims;
+
+/* Workspace bytes needed by one call (0 if it needs none).  m and rank are
+ * only used by SPARSEPR_CALL_PROBE_FIT.  Returns 0 for invalid dims too;
+ * the call itself reports the error. */
+size_t sparsepr_workspace_bytes(int32_t which_call, const sparsepr_dims* dims /* host */,
+                                int32_t m, int32_t rank);
+
+/* Human-readable text of a status code (static storage). */
+const char* sparsepr_status_string(int32_t status);
+
+/* ABI version: major*10000 + minor*100 + patch. */
+int32_t sparsepr_version(void);
+
+/*
+ * S1-S3. Group-major layout.  (SparsePR paper §3: queries and keys are
+ * partitioned into groups, each value follows its key; the review's step
+ * (3): Q, K, V are permuted into group-major order before the varlen
+ * block-sparse kernel.)
+ *   labels_q [H][N_q], labels_kv [H][N_k]: int32 group ids in [0, C).
+ *   q [.. per q strides], k, v [.. per kv strides]: dims.dtype.
+ * Outputs
+ *   perm_q [H][N_q], perm_kv [H][N_k]: int32 token index of each group-major
+ *     row.  Groups in ascending id, tokens ascending inside a group (stable).
+ *   offsets_q [H][C_q+1], offsets_kv [H][C_k+1]: int32 first row of each
+ *     group; an empty group has offsets[a] == offsets[a+1].
+ *   q_g [H][N_q][d], k_g, v_g [H][N_k][d]: dims.dtype, bit-exact copies.
+ *   centroid_q [H][C_q][d], centroid_k [H][C_k][d]: fp64 group means of q
+ *     and k (exact fp64 sums of the inputs, divided by the group size);
+ *     rows of empty groups are 0.
+ */
+int32_t sparsepr_partition_layout(const sparsepr_dims* dims /* host */,
+                                  const int32_t* labels_q, const int32_t* labels_kv,
+                                  const void* q, const void* k, const void* v,
+                                  int32_t* perm_q, int32_t* offsets_q,
+                                  int32_t* perm_kv, int32_t* offsets_kv,
+                                  void* q_g, void* k_g, void* v_g,
+                                  double* centroid_q, double* centroid_k,
+                                  void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * S4. Cell routing under a routed pair budget.  (SparsePR paper §4.3: each
+ * cell G_a x G_b costs |G_a||G_b| interactions; the router keeps the
+ * shortest prefix that reaches the budget; probe cost M/N_q is reserved, so
+ * the caller passes budget = ceil((rho*N_q - M) * N_k).)
+ * Score s_ab = centroid_q[a] . centroid_k[b] / sqrt(d) in fp64.  Every
+ * non-empty query group first keeps its best non-empty cell (ties -> smaller
+ * b); then the other non-empty cells are taken in (s desc, a asc, b asc)
+ * order while the running pair count is below `routed_pair_budget`.  Empty
+ * groups are never selected.
+ * Outputs
+ *   cell_rowptr [H][C_q+1]: int32, per-head CSR row pointers (start at 0).
+ *   cell_col [H][C_q*C_k]: int32, selected b of query group a in
+ *     cell_col[h][rowptr[a] .. rowptr[a+1]), ascending; slots past
+ *     rowptr[C_q] are left untouched.
+ *   routed_pairs [H]: int64, sum of |G_a||G_b| over selected cells.
+ */
+int32_t sparsepr_route_cells(const sparsepr_dims* dims /* host */,
+                             const int32_t* offsets_q, const int32_t* offsets_kv,
+                             const double* centroid_q, const double* centroid_k,
+                             int64_t routed_pair_budget,
+                             int32_t* cell_rowptr, int32_t* cell_col, int64_t* routed_pairs,
+                             void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * S5. Renormalised hard-drop attention.  (SparsePR paper §3: a query of
+ * group a attends only to keys of the groups selected for a, with the
+ * softmax normalised over those keys.)
+ *   q_g, k_g, v_g: group-major [H][N][d] in dims.dtype.
+ *   softmax_scale: logits are (q . k) * softmax_scale (1/sqrt(d) normally).
+ * Outputs (group-major row order)
+ *   o_sp [H][N_q][d]: fp32 sparse output.
+ *   lse [H][N_q]: fp32 natural-log sum of exp of the scaled logits (may be NULL).
+ * Every non-empty query group has at least one selected cell after
+ * route_cells, so every row is written.
+ */
+int32_t sparsepr_sparse_attn(const sparsepr_dims* dims /* host */,
+                             const int32_t* offsets_q, const int32_t* offsets_kv,
+                             const int32_t* cell_rowptr, const int32_t* cell_col,
+                             const void* q_g, const void* k_g, const void* v_g,
+                             float softmax_scale, float* o_sp, float* lse,
+                             void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * S6-S8. Probes and correction fit.  (SparsePR paper App. A.2, Algorithm
+ * A.1: probe rows are taken per query group by increasing distance to the
+ * group centroid, groups by decreasing size, round-robin, until
+ * min(m, N_q) probes; exact rows against all keys give O_dense and the
+ * residual R_p = O_dense - O_sp at the probes; coverage weights |G_a|/m_a;
+ * weighted standardisation with sqrt(var + 1e-6); ridge with `lambda`;
+ * projection on the top `rank` right singular vectors of the weighted
+ * centred residuals (singular values <= 1e-10 * largest dropped).)
+ * The distance uses the raw queries (features of the given partition) and
+ * the fp64 centroids of partition_layout.  O_sp at a probe row is formed
+ * here from the same pass that forms the dense row (retained and omitted
+ * partial sums, SparsePR paper App. A.1), so this call does not read the
+ * output of sparse_attn.
+ *   m: 1..64 probes per head; rank: 0..64 (capped at min(m, d) columns).
+ * Outputs
+ *   probe_rows [H][m], probe_tokens [H][m]: int32 group-major row and token
+ *     index of each probe in selection order; entries past min(m, N_q) = -1.
+ *   o_probe_dense [H][m][d]: fp32 dense output of each probe row.
+ *   o_probe_sparse [H][m][d]: fp32 hard-drop output at each probe (may be NULL).
+ *   corr_a [H][d][rank], corr_psi_t [H][rank][d], corr_c [H][d]: fp32 folded
+ *     correction  out = o + (o . A) Psi^T + c  with A = diag(1/s) B Psi and
+ *     c = mu_R - (mu_x . A) Psi^T; dropped directions are zero columns.
+ */
+int32_t sparsepr_probe_fit(const sparsepr_dims* dims /* host */, int32_t m, int32_t rank,
+                           double lambda,
+                           const int32_t* offsets_q, const int32_t* offsets_kv,
+                           const int32_t* perm_q,
+                           const int32_t* cell_rowptr, const int32_t* cell_col,
+                           const double* centroid_q,
+                           const void* q_g, const void* k_g, const void* v_g,
+                           float softmax_scale,
+                           int32_t* probe_rows, int32_t* probe_tokens,
+                           float* o_probe_dense, float* o_probe_sparse,
+                           float* corr_a, float* corr_psi_t, float* corr_c,
+                           void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * S9. Correction and restore.  (Review step (5): unprobed rows get their
+ * sparse output plus the predicted residual, probe rows their dense
+ * output; the result returns to the original token order.)
+ *   o_sp [H][N_q][d] fp32 group-major (sparse_attn output).
+ *   out: [H][N_q][d]-shaped in ORIGINAL token order with element strides
+ *     out_stride_head, out_stride_tok; out_dtype SPARSEPR_BF16 (nearest-even
+ *     rounding) or SPARSEPR_F32.
+ */
+int32_t sparsepr_correct(const sparsepr_dims* dims /* host */, int32_t m, int32_t rank,
+                         const int32_t* perm_q, const float* o_sp,
+                         const int32_t* probe_tokens, const float* o_probe_dense,
+                         const float* corr_a, const float* corr_psi_t, const float* corr_c,
+                         void* out, int32_t out_dtype,
+                         int64_t out_stride_head, int64_t out_stride_tok,
+                         void* ws, size_t ws_bytes, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPARSEPR_H */

@@ -41,6 +41,7 @@ __all__ = [
     "small_workload",
     "make_head",
     "make_call",
+    "make_call_arrays",
     "position_code",
     "f32_to_bf16_bits",
     "bf16_bits_to_f32",
@@ -172,41 +173,86 @@ def _kv_labels(labels: np.ndarray, components: int, split: int) -> np.ndarray:
     return out
 
 
-def make_head(w: Workload, h: int, variant: str = "default", pos: Optional[np.ndarray] = None):
-    """Draw head h.  Returns dict with float32 q, k, v [N, d] (bf16-exact for
-    bf16 workloads), uint16 bits (bf16 only) and int32 labels_q, labels_kv."""
+class _Scratch:
+    """Per-shape scratch buffers reused across heads (fresh allocations are
+    avoided: first-touch page faults dominate generation time otherwise)."""
+
+    def __init__(self, n, d):
+        self.f = np.empty((n, d), np.float32)
+        self.g = np.empty((n, d), np.float32)
+        self.u = np.empty((n, d), np.uint32)
+
+
+def _encode_into(src: np.ndarray, dst: np.ndarray, scratch: _Scratch, bf16: bool):
+    """src float32 [n, d] -> dst (uint16 bf16 bits, nearest-even, or float32)."""
+    if not bf16:
+        np.copyto(dst, src)
+        return
+    u = src.view(np.uint32)
+    t = scratch.u
+    np.right_shift(u, np.uint32(16), out=t)
+    np.bitwise_and(t, np.uint32(1), out=t)
+    np.add(t, np.uint32(0x7FFF), out=t)
+    np.add(u, t, out=t)
+    np.right_shift(t, np.uint32(16), out=t)
+    np.copyto(dst, t, casting="unsafe")
+    nan = np.isnan(src)
+    if nan.any():
+        dst[nan] = np.uint16(0x7FC0)
+
+
+def _draw_head_into(w: Workload, h: int, variant: str, pos_scaled, qo, ko, vo, scratch):
+    """Draws head h and writes the encoded q, k, v into qo, ko, vo ([n, d]
+    uint16 bf16 bits or float32).  Returns (labels_q, labels_kv)."""
     if variant not in ("default", "near_exact"):
         raise ValueError(variant)
     rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([w.seed, h])))
     n, d, C = w.n, w.head_dim, w.components
+    bf16 = w.dtype == "bf16"
+    if w.dtype not in ("bf16", "f32"):
+        raise ValueError(w.dtype)
     labels = rng.integers(0, C, size=n).astype(np.int32)
     mu_q = (rng.standard_normal((C, d), dtype=np.float32) * np.float32(w.mean_std))
     mu_k = (rng.standard_normal((C, d), dtype=np.float32) * np.float32(w.mean_std))
     if variant == "near_exact":
         mu_k = mu_q
-    q = rng.standard_normal((n, d), dtype=np.float32)
-    q *= np.float32(w.spread)
-    q += mu_q[labels]
-    k = rng.standard_normal((n, d), dtype=np.float32)
-    k *= np.float32(w.spread)
-    k += mu_k[labels]
-    v = rng.standard_normal((n, d), dtype=np.float32)
-    if w.grid is not None:
-        if pos is None:
-            pos = position_code(w.grid, d)
-        ps = pos * np.float32(w.pos_scale)
-        q += ps
-        k += ps
-    out = {"labels_q": labels, "labels_kv": _kv_labels(labels, C, w.kv_split).astype(np.int32)}
-    if w.dtype == "bf16":
-        for name, arr in (("q", q), ("k", k), ("v", v)):
-            bits = f32_to_bf16_bits(arr)
-            out[name + "_bits"] = bits
-            out[name] = bf16_bits_to_f32(bits)
-    elif w.dtype == "f32":
-        out["q"], out["k"], out["v"] = q, k, v
+    f, g = scratch.f, scratch.g
+    for mu, out in ((mu_q, qo), (mu_k, ko)):
+        rng.standard_normal(dtype=np.float32, out=f)
+        f *= np.float32(w.spread)
+        np.take(mu, labels, axis=0, out=g, mode="clip")  # unbuffered gather
+        f += g
+        if pos_scaled is not None:
+            f += pos_scaled
+        _encode_into(f, out, scratch, bf16)
+    rng.standard_normal(dtype=np.float32, out=f)
+    _encode_into(f, vo, scratch, bf16)
+    return labels, _kv_labels(labels, C, w.kv_split).astype(np.int32)
+
+
+def _pos_scaled(w: Workload, pos=None):
+    if w.grid is None:
+        return None
+    if pos is None:
+        pos = position_code(w.grid, w.head_dim)
+    return pos * np.float32(w.pos_scale)
+
+
+def make_head(w: Workload, h: int, variant: str = "default", pos: Optional[np.ndarray] = None):
+    """Draw head h.  Returns dict with float32 q, k, v [N, d] (bf16-exact for
+    bf16 workloads), uint16 bits (bf16 only) and int32 labels_q, labels_kv."""
+    n, d = w.n, w.head_dim
+    bf16 = w.dtype == "bf16"
+    et = np.uint16 if bf16 else np.float32
+    qo, ko, vo = (np.empty((n, d), et) for _ in range(3))
+    lq, lk = _draw_head_into(w, h, variant, _pos_scaled(w, pos), qo, ko, vo, _Scratch(n, d))
+    out = {"labels_q": lq, "labels_kv": lk}
+    if bf16:
+        for name, arr in (("q", qo), ("k", ko), ("v", vo)):
+            out[name + "_bits"] = arr
+            out[name] = bf16_bits_to_f32(arr)
     else:
-        raise ValueError(w.dtype)
+        out["q"], out["k"], out["v"] = qo, ko, vo
     return out
 
 
@@ -215,3 +261,28 @@ def make_call(w: Workload, variant: str = "default", heads=None):
     pos = position_code(w.grid, w.head_dim) if w.grid is not None else None
     hs = range(w.heads) if heads is None else heads
     return [make_head(w, h, variant, pos) for h in hs]
+
+
+def make_call_arrays(w: Workload, variant: str = "default", threads: Optional[int] = None):
+    """All heads packed for upload: q, k, v [H, N, d] (uint16 bf16 bits or
+    float32) and labels_q, labels_kv int32 [H, N].  Same values as make_head.
+    Heads are drawn in parallel threads (independent generators per head)."""
+    import concurrent.futures as cf
+    import os
+
+    n, d, H = w.n, w.head_dim, w.heads
+    et = np.uint16 if w.dtype == "bf16" else np.float32
+    q, k, v = (np.empty((H, n, d), et) for _ in range(3))
+    lq = np.empty((H, n), np.int32)
+    lk = np.empty((H, n), np.int32)
+    ps = _pos_scaled(w)
+    nt = threads or max(1, min(8, os.cpu_count() or 1, H))
+
+    def work(tid):
+        scratch = _Scratch(n, d)
+        for h in range(tid, H, nt):
+            lq[h], lk[h] = _draw_head_into(w, h, variant, ps, q[h], k[h], v[h], scratch)
+
+    with cf.ThreadPoolExecutor(nt) as ex:
+        list(ex.map(work, range(nt)))
+    return {"q": q, "k": k, "v": v, "labels_q": lq, "labels_kv": lk}

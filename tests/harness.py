@@ -1,0 +1,169 @@
+"""Shared helpers of the GPU parity tests: draw inputs, run the HIP path
+through the C ABI, run the oracle on the same inputs, compare."""
+from __future__ import annotations
+
+import math
+import sys
+
+import numpy as np
+
+import oracle
+import synthgen as sg
+
+
+def say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def rel_fro(a, b):
+    a = np.asarray(a, np.float64)
+    b = np.asarray(b, np.float64)
+    den = np.linalg.norm(b)
+    return float(np.linalg.norm(a - b) / (den if den > 0 else 1.0))
+
+
+def tol_for(w):
+    return 1e-5 if w.dtype == "f32" else 2e-3
+
+
+def upload(w, heads_data, layout="hnd"):
+    """Device tensors q, k, v (bf16 or f32) and int32 labels for all heads.
+    layout 'hnd' -> [H][N][d]; 'nhd' -> [N][H][d] (strided model layout)."""
+    import torch
+    H = len(heads_data)
+    if w.dtype == "bf16":
+        def stack(name):
+            bits = np.stack([hd[name + "_bits"] for hd in heads_data])
+            t = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16)
+            return t
+    else:
+        def stack(name):
+            return torch.from_numpy(np.stack([hd[name] for hd in heads_data]))
+    q, k, v = (stack(n) for n in ("q", "k", "v"))
+    if layout == "nhd":
+        q, k, v = (t.transpose(0, 1).contiguous() for t in (q, k, v))
+    lq = torch.from_numpy(np.stack([hd["labels_q"] for hd in heads_data]))
+    lk = torch.from_numpy(np.stack([hd["labels_kv"] for hd in heads_data]))
+    dev = torch.device("cuda")
+    return (q.to(dev), k.to(dev), v.to(dev), lq.to(dev), lk.to(dev))
+
+
+def run_gpu(w, heads_data, budget=None, rank=None, m=None, layout="hnd", out_dtype="f32",
+            overlap=True):
+    import torch
+    import free_block_sparse_major_amd as fb
+    H = len(heads_data)
+    q, k, v, lq, lk = upload(w, heads_data, layout)
+    d = w.head_dim
+    strides = None
+    if layout == "nhd":
+        strides = (d, H * d)
+    call = fb.SparsePRCall(H, w.n, w.n, d, fb.BF16 if w.dtype == "bf16" else fb.F32, w.c_q, w.c_k,
+                           m=w.m if m is None else m, rank=w.r if rank is None else rank,
+                           lam=w.lam, rho=w.rho, budget=budget,
+                           out_dtype=fb.F32 if out_dtype == "f32" else fb.BF16,
+                           q_strides=strides, kv_strides=strides, overlap=overlap)
+    call(lq, lk, q, k, v)
+    torch.cuda.synchronize()
+    g = {name: getattr(call, name) for name in (
+        "perm_q", "perm_kv", "offsets_q", "offsets_kv", "centroid_q", "centroid_k",
+        "cell_rowptr", "cell_col", "routed_pairs", "o_sp", "lse", "probe_rows", "probe_tokens",
+        "o_probe_dense", "o_probe_sparse", "corr_a", "corr_psi_t", "corr_c", "out")}
+    out = {}
+    for key, t in g.items():
+        if t.dtype == torch.bfloat16:
+            t = t.float()
+        out[key] = t.cpu().numpy()
+    out["q_g"] = call.q_g.float().cpu().numpy() if w.dtype == "bf16" else call.q_g.cpu().numpy()
+    out["budget"] = call.budget
+    out["call"] = call
+    return out
+
+
+def oracle_head(w, hd, budget=None, rank=None, m=None, rows=None):
+    return oracle.run_head(hd["q"], hd["k"], hd["v"], hd["labels_q"], hd["labels_kv"], w.c_q,
+                           w.c_k, w.rho, m=w.m if m is None else m,
+                           rank=w.r if rank is None else rank, lam=w.lam, budget=budget,
+                           query_rows=rows)
+
+
+def cells_from_csr(rowptr, col, c_q, c_k):
+    z = np.zeros((c_q, c_k), bool)
+    for a in range(c_q):
+        z[a, col[rowptr[a]:rowptr[a + 1]]] = True
+    return z
+
+
+def score_gap(scores, z):
+    """Smallest |s| distance between a selected and an unselected candidate
+    cell score (diagnostic for near-ties at the routing boundary)."""
+    sel = scores[z & np.isfinite(scores)]
+    uns = scores[~z & np.isfinite(scores)]
+    if sel.size == 0 or uns.size == 0:
+        return math.inf
+    return float(sel.min() - uns.max()) if sel.min() > uns.max() else 0.0
+
+
+def compare_head(w, g, h, r, rows_orig=None, check_rows=True):
+    """Asserts parity of head h of GPU results `g` with oracle results `r`.
+    Returns a dict of measured errors."""
+    n, c_q, c_k, d = w.n, w.c_q, w.c_k, w.head_dim
+    tol = tol_for(w)
+    errs = {}
+    # layout: bit-exact
+    assert np.array_equal(g["perm_q"][h], r["perm_q"]), "perm_q"
+    assert np.array_equal(g["perm_kv"][h], r["perm_kv"]), "perm_kv"
+    assert np.array_equal(g["offsets_q"][h], r["offsets_q"]), "offsets_q"
+    assert np.array_equal(g["offsets_kv"][h], r["offsets_kv"]), "offsets_kv"
+    # centroids (fp64 means of the same values; summation order may differ)
+    ne = np.diff(r["offsets_q"]) > 0
+    cq = g["centroid_q"][h][ne]
+    assert np.allclose(cq, r["qbar"][ne], rtol=0, atol=1e-12 * max(1.0, np.abs(cq).max()))
+    # routing: bit-exact
+    z = cells_from_csr(g["cell_rowptr"][h], g["cell_col"][h], c_q, c_k)
+    errs["score_gap"] = score_gap(r["scores"], r["z"])
+    assert np.array_equal(z, r["z"]), f"cells differ (boundary score gap {errs['score_gap']:.3e})"
+    for a in range(c_q):
+        cols = g["cell_col"][h][g["cell_rowptr"][h][a]:g["cell_rowptr"][h][a + 1]]
+        assert np.all(np.diff(cols) > 0)
+    assert int(g["routed_pairs"][h]) == r["routed_pairs"]
+    # probes: bit-exact (selection order)
+    me = min(w.m, n) if "m_override" not in r else r["m_override"]
+    probes_tok = g["probe_tokens"][h][:len(r["probes"])]
+    assert np.array_equal(probes_tok, r["probes"]), "probe tokens"
+    inv = np.empty(n, np.int64)
+    inv[r["perm_q"]] = np.arange(n)
+    assert np.array_equal(g["probe_rows"][h][:len(r["probes"])], inv[r["probes"]])
+    assert np.all(g["probe_tokens"][h][len(r["probes"]):] == -1)
+    np_ = len(r["probes"])
+    errs["dense_p"] = rel_fro(g["o_probe_dense"][h][:np_], r["dense_p"])
+    errs["x_p"] = rel_fro(g["o_probe_sparse"][h][:np_], r["x_p"])
+    assert errs["dense_p"] <= tol, errs
+    assert errs["x_p"] <= tol, errs
+    # fit: compare the unique d x d operator A Psi^T and c
+    k = w.r
+    T_gpu = g["corr_a"][h][:, :k] @ g["corr_psi_t"][h][:k, :] if k > 0 else np.zeros((d, d))
+    errs["T"] = rel_fro(T_gpu, r["T"]) if np.linalg.norm(r["T"]) > 0 else float(np.abs(T_gpu).max())
+    errs["c"] = rel_fro(g["corr_c"][h], r["c"])
+    # sparse output rows and final output
+    if check_rows:
+        rows = r["rows"]
+        o_sp_g = g["o_sp"][h][inv[rows]]
+        errs["o_sp"] = rel_fro(o_sp_g, r["o_sp"])
+        errs["lse"] = float(np.abs(g["lse"][h][inv[rows]] - r["lse"]).max())
+        out_g = g["out"][h][rows]
+        errs["out"] = rel_fro(out_g, r["out"])
+        corr_g = out_g - o_sp_g
+        corr_r = r["out"] - r["o_sp"]
+        unprobed = ~np.isin(rows, r["probes"])
+        errs["correction"] = rel_fro(corr_g[unprobed], corr_r[unprobed])
+        assert errs["o_sp"] <= tol, errs
+        assert errs["out"] <= tol, errs
+        probed = np.isin(rows, r["probes"])
+        if probed.any():
+            dense_rows = {int(t): i for i, t in enumerate(r["probes"])}
+            for j in np.nonzero(probed)[0]:
+                assert np.array_equal(g["out"][h][rows[j]],
+                                      g["o_probe_dense"][h][dense_rows[int(rows[j])]])
+    return errs

@@ -1,0 +1,108 @@
+"""Host-side checks of the C ABI (no kernel launches): the library loads,
+exports every symbol the header declares, validates arguments and sizes its
+workspaces.  Runs without a GPU."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import free_block_sparse_major_amd as fb
+import synthgen as sg
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "sparsepr.h")
+
+
+def _declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(sparsepr_[a-z_]+)\s*\(", src)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(fb.LIB_PATH):
+        from free_block_sparse_major_amd.build import build
+        build()
+    return fb.load_library()
+
+
+def test_exports_every_declared_symbol(lib):
+    names = _declared()
+    assert set(names) == set(fb.EXPORTED)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_version_and_status_strings(lib):
+    assert fb.sparsepr_version() == 10000
+    for s, text in [(0, b"ok"), (1, b"invalid argument"), (2, b"unsupported shape or dtype"),
+                    (3, b"workspace too small"), (4, b"HIP launch error")]:
+        assert lib.sparsepr_status_string(s) == text
+    assert lib.sparsepr_status_string(99) == b"unknown status"
+
+
+def test_dims_struct_layout():
+    assert ctypes.sizeof(fb.Dims) == 8 * 4 + 4 * 8
+
+
+def test_workspace_sizes(lib):
+    for name in ("tiny_fp32", "cogvideox", "wan", "hunyuan"):
+        w = sg.workload(name)
+        dims = fb.make_dims(w.heads, w.n, w.n, w.head_dim, fb.BF16 if w.dtype == "bf16" else fb.F32,
+                            w.c_q, w.c_k)
+        for which in range(4):
+            nb = fb.workspace_bytes(which, dims, w.m, w.r)
+            assert nb > 0
+        assert fb.workspace_bytes(fb.CALL_CORRECT, dims) == 0
+        # route scratch holds one fp64 score per cell
+        assert fb.workspace_bytes(fb.CALL_ROUTE_CELLS, dims) >= 8 * w.heads * w.c_q * w.c_k
+    bad = fb.make_dims(1, 100, 100, 96, fb.BF16, 4, 4)
+    assert fb.workspace_bytes(fb.CALL_ROUTE_CELLS, bad) == 0
+    ok = fb.make_dims(1, 100, 100, 64, fb.BF16, 4, 4)
+    assert fb.workspace_bytes(fb.CALL_PROBE_FIT, ok, m=65) == 0
+    assert fb.workspace_bytes(fb.CALL_PROBE_FIT, ok, m=64, rank=65) == 0
+
+
+def _layout_status(lib, dims, null=False, ws_bytes=1 << 30):
+    p = ctypes.c_void_p(0 if null else 4096)
+    args = [p] * 14
+    return lib.sparsepr_partition_layout(ctypes.byref(dims), *args, ctypes.c_void_p(4096),
+                                         ws_bytes, None)
+
+
+def test_argument_validation_before_launch(lib):
+    """Every rejected call returns before touching the device."""
+    good = fb.make_dims(2, 300, 300, 64, fb.BF16, 8, 8)
+    assert _layout_status(lib, fb.make_dims(2, 300, 300, 96, fb.BF16, 8, 8)) == fb.ERR_UNSUPPORTED
+    assert _layout_status(lib, fb.make_dims(2, 300, 300, 64, 7, 8, 8)) == fb.ERR_UNSUPPORTED
+    assert _layout_status(lib, fb.make_dims(2, 300, 300, 64, fb.BF16, 2000, 8)) == fb.ERR_UNSUPPORTED
+    assert _layout_status(lib, fb.make_dims(0, 300, 300, 64, fb.BF16, 8, 8)) == fb.ERR_INVALID
+    assert _layout_status(lib, fb.make_dims(2, 0, 300, 64, fb.BF16, 8, 8)) == fb.ERR_INVALID
+    assert _layout_status(lib, fb.make_dims(2, 300, 300, 64, fb.BF16, 8, 8,
+                                            q_strides=(300 * 64, 60))) == fb.ERR_INVALID
+    assert _layout_status(lib, good, null=True) == fb.ERR_INVALID
+    assert _layout_status(lib, good, ws_bytes=16) == fb.ERR_WORKSPACE
+    P = ctypes.c_void_p(4096)
+    # probe_fit: m out of range, rank out of range, lambda 0 with rank > 0
+    for m, rank, lam in [(0, 16, 0.1), (65, 16, 0.1), (64, -1, 0.1), (64, 65, 0.1), (64, 16, 0.0),
+                         (64, 16, float("nan"))]:
+        st = lib.sparsepr_probe_fit(ctypes.byref(good), m, rank, lam, *([P] * 9),
+                                    ctypes.c_float(0.125), *([P] * 7), P, 1 << 30, None)
+        assert st == fb.ERR_INVALID, (m, rank, lam)
+    # correct: unsupported output dtype, misaligned output stride
+    st = lib.sparsepr_correct(ctypes.byref(good), 64, 16, *([P] * 8), 5, 300 * 64, 64, None, 0, None)
+    assert st == fb.ERR_UNSUPPORTED
+    st = lib.sparsepr_correct(ctypes.byref(good), 64, 16, *([P] * 8), fb.F32, 300 * 64, 65, None, 0,
+                              None)
+    assert st == fb.ERR_INVALID
+    # route: workspace too small
+    st = lib.sparsepr_route_cells(ctypes.byref(good), P, P, P, P, 100, P, P, P, P, 8, None)
+    assert st == fb.ERR_WORKSPACE
+
+
+def test_budget_matches_oracle_closed_form():
+    import oracle
+    for rho, n, m in [("0.26", 4096, 64), ("0.22", 75600, 64), ("0.26", 118800, 64), ("0.3", 50, 64)]:
+        assert fb.routed_pair_budget(rho, n, n, m) == oracle.routed_pair_budget(rho, n, n, m)
