@@ -65,13 +65,13 @@ def load_library(path: str = LIB_PATH):
     lib.sparsepr_status_string.restype = ctypes.c_char_p
     lib.sparsepr_version.argtypes = []
     lib.sparsepr_version.restype = I32
-    lib.sparsepr_partition_layout.argtypes = [DP] + [P] * 14 + [P, SZ, P]
+    lib.sparsepr_partition_layout.argtypes = [DP] + [P] * 15 + [P, SZ, P]
     lib.sparsepr_partition_layout.restype = I32
     lib.sparsepr_route_cells.argtypes = [DP, P, P, P, P, I64, P, P, P, P, SZ, P]
     lib.sparsepr_route_cells.restype = I32
-    lib.sparsepr_sparse_attn.argtypes = [DP, P, P, P, P, P, P, P, ctypes.c_float, P, P, P, SZ, P]
+    lib.sparsepr_sparse_attn.argtypes = [DP, P, P, P, P, P, P, P, P, ctypes.c_float, P, P, P, SZ, P]
     lib.sparsepr_sparse_attn.restype = I32
-    lib.sparsepr_probe_fit.argtypes = ([DP, I32, I32, D] + [P] * 9 + [ctypes.c_float] + [P] * 7
+    lib.sparsepr_probe_fit.argtypes = ([DP, I32, I32, D] + [P] * 10 + [ctypes.c_float] + [P] * 7
                                        + [P, SZ, P])
     lib.sparsepr_probe_fit.restype = I32
     lib.sparsepr_correct.argtypes = [DP, I32, I32] + [P] * 8 + [I32, I64, I64, P, SZ, P]
@@ -115,11 +115,12 @@ def sparsepr_version():
 # ----------------------------------------------------------------------------
 
 def sparsepr_partition_layout(dims, labels_q, labels_kv, q, k, v, perm_q, offsets_q, perm_kv,
-                              offsets_kv, q_g, k_g, v_g, centroid_q, centroid_k, ws, stream=None):
+                              offsets_kv, q_g, k_g, v_g, v_shift, centroid_q, centroid_k, ws,
+                              stream=None):
     st = load_library().sparsepr_partition_layout(
         ctypes.byref(dims), _ptr(labels_q), _ptr(labels_kv), _ptr(q), _ptr(k), _ptr(v),
         _ptr(perm_q), _ptr(offsets_q), _ptr(perm_kv), _ptr(offsets_kv), _ptr(q_g), _ptr(k_g),
-        _ptr(v_g), _ptr(centroid_q), _ptr(centroid_k), _ptr(ws),
+        _ptr(v_g), _ptr(v_shift), _ptr(centroid_q), _ptr(centroid_k), _ptr(ws),
         ws.numel() * ws.element_size() if ws is not None else 0, _stream(stream))
     _check(st, "sparsepr_partition_layout")
 
@@ -134,21 +135,21 @@ def sparsepr_route_cells(dims, offsets_q, offsets_kv, centroid_q, centroid_k, bu
 
 
 def sparsepr_sparse_attn(dims, offsets_q, offsets_kv, cell_rowptr, cell_col, q_g, k_g, v_g,
-                         softmax_scale, o_sp, lse, ws, stream=None):
+                         v_shift, softmax_scale, o_sp, lse, ws, stream=None):
     st = load_library().sparsepr_sparse_attn(
         ctypes.byref(dims), _ptr(offsets_q), _ptr(offsets_kv), _ptr(cell_rowptr), _ptr(cell_col),
-        _ptr(q_g), _ptr(k_g), _ptr(v_g), ctypes.c_float(softmax_scale), _ptr(o_sp), _ptr(lse),
+        _ptr(q_g), _ptr(k_g), _ptr(v_g), _ptr(v_shift), ctypes.c_float(softmax_scale), _ptr(o_sp), _ptr(lse),
         _ptr(ws), ws.numel() * ws.element_size() if ws is not None else 0, _stream(stream))
     _check(st, "sparsepr_sparse_attn")
 
 
 def sparsepr_probe_fit(dims, m, rank, lam, offsets_q, offsets_kv, perm_q, cell_rowptr, cell_col,
-                       centroid_q, q_g, k_g, v_g, softmax_scale, probe_rows, probe_tokens,
+                       centroid_q, q_g, k_g, v_g, v_shift, softmax_scale, probe_rows, probe_tokens,
                        o_probe_dense, o_probe_sparse, corr_a, corr_psi_t, corr_c, ws, stream=None):
     st = load_library().sparsepr_probe_fit(
         ctypes.byref(dims), int(m), int(rank), float(lam), _ptr(offsets_q), _ptr(offsets_kv),
         _ptr(perm_q), _ptr(cell_rowptr), _ptr(cell_col), _ptr(centroid_q), _ptr(q_g), _ptr(k_g),
-        _ptr(v_g), ctypes.c_float(softmax_scale), _ptr(probe_rows), _ptr(probe_tokens),
+        _ptr(v_g), _ptr(v_shift), ctypes.c_float(softmax_scale), _ptr(probe_rows), _ptr(probe_tokens),
         _ptr(o_probe_dense), _ptr(o_probe_sparse), _ptr(corr_a), _ptr(corr_psi_t), _ptr(corr_c),
         _ptr(ws), ws.numel() * ws.element_size() if ws is not None else 0, _stream(stream))
     _check(st, "sparsepr_probe_fit")
@@ -200,7 +201,9 @@ class SparsePRCall:
         self.offsets_kv = torch.empty(H, c_k + 1, **i32)
         self.q_g = torch.empty(H, n_q, d, dtype=tdt, device=dev)
         self.k_g = torch.empty(H, n_k, d, dtype=tdt, device=dev)
-        self.v_g = torch.empty(H, n_k, d, dtype=tdt, device=dev)
+        vdt = torch.float16 if dtype == BF16 else torch.float32
+        self.v_g = torch.empty(H, n_k, d, dtype=vdt, device=dev)
+        self.v_shift = torch.empty(H, dtype=torch.int32, device=dev)
         self.centroid_q = torch.empty(H, c_q, d, dtype=torch.float64, device=dev)
         self.centroid_k = torch.empty(H, c_k, d, dtype=torch.float64, device=dev)
         self.cell_rowptr = torch.empty(H, c_q + 1, **i32)
@@ -234,7 +237,8 @@ class SparsePRCall:
     def layout(self, labels_q, labels_kv, q, k, v, stream=None):
         sparsepr_partition_layout(self.dims, labels_q, labels_kv, q, k, v, self.perm_q,
                                   self.offsets_q, self.perm_kv, self.offsets_kv, self.q_g,
-                                  self.k_g, self.v_g, self.centroid_q, self.centroid_k,
+                                  self.k_g, self.v_g, self.v_shift, self.centroid_q,
+                                  self.centroid_k,
                                   self.ws_layout, stream)
 
     def route(self, stream=None):
@@ -244,13 +248,15 @@ class SparsePRCall:
 
     def attend(self, stream=None):
         sparsepr_sparse_attn(self.dims, self.offsets_q, self.offsets_kv, self.cell_rowptr,
-                             self.cell_col, self.q_g, self.k_g, self.v_g, self.scale, self.o_sp,
+                             self.cell_col, self.q_g, self.k_g, self.v_g, self.v_shift,
+                             self.scale, self.o_sp,
                              self.lse, self.ws_attn, stream)
 
     def probe_fit(self, stream=None):
         sparsepr_probe_fit(self.dims, self.m, self.rank, self.lam, self.offsets_q,
                            self.offsets_kv, self.perm_q, self.cell_rowptr, self.cell_col,
-                           self.centroid_q, self.q_g, self.k_g, self.v_g, self.scale,
+                           self.centroid_q, self.q_g, self.k_g, self.v_g, self.v_shift,
+                           self.scale,
                            self.probe_rows, self.probe_tokens, self.o_probe_dense,
                            self.o_probe_sparse, self.corr_a, self.corr_psi_t, self.corr_c,
                            self.ws_probe, stream)

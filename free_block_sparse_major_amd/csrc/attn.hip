@@ -15,15 +15,15 @@
 // wave.  Scores are formed transposed, S^T = K Q^T, so each lane owns one
 // query and 32 of the tile's 64 keys; the row max/sum need a single exchange
 // with the partner lane (lane ^ 32).  O^T = V^T P^T is accumulated likewise
-// (one query per lane).  K is staged in LDS row-major with an XOR swizzle of
-// 16-byte chunks; V is transposed into LDS (d rows) with keys reordered so
-// the 8 keys a lane's P fragment holds are contiguous.  K/V tiles are double
-// buffered in LDS and prefetched through registers one tile ahead.
-// PV runs on fp16 MFMA: P (in [0, 1]) is rounded to fp16 and V is converted
-// to fp16 after an exact power-of-two scale per head (chosen from the head's
-// largest |v| so every normal bf16 value converts without rounding); O is
-// scaled back at the end.  Rounding P to bf16 instead costs ~1.5e-3 relative
-// error on O, which the fitted correction then amplifies past 2e-3.
+// (one query per lane).  K and V tiles are double buffered in LDS and loaded
+// one tile ahead directly from global memory; V^T fragments come from
+// hardware transposing LDS reads, so V stays row-major.
+// PV runs on fp16 MFMA: P (in [0, 1]) is rounded to fp16 and V arrives as
+// fp16 after an exact power-of-two scale per head (the layout call chooses
+// it from the head's largest |v|, so every normal bf16 value converts without
+// rounding); O is scaled back at the end.  Rounding P to bf16 instead costs
+// ~1.5e-3 relative error on O, which the fitted correction then amplifies
+// past 2e-3.
 
 #include "common.h"
 
@@ -48,7 +48,7 @@ struct AttnArgs {
   float* o;
   float* lse;
   const int32_t* tiles;  // [H*c_q + 1] exclusive prefix of per-group tile counts
-  const uint32_t* vmax;  // [H] largest |v| bit pattern of the head (bf16 path)
+  const int32_t* v_shift;  // [H] v_g holds fp16(v * 2^-v_shift) (bf16 path)
   int H, n_q, n_k, c_q, c_k;
   float scale_log2;      // softmax_scale * log2(e)
   int grid_blocks;       // launched blocks (multiple of 8)
@@ -57,10 +57,8 @@ struct AttnArgs {
 // tiles[h*c_q + a] = sum over earlier (h, a) of ceil(n_a / tq); tiles[H*c_q] = total.
 __global__ __launch_bounds__(1024) void tile_table_kernel(const int32_t* __restrict__ off_q, int H,
                                                          int c_q, int tq,
-                                                         int32_t* __restrict__ tiles,
-                                                         uint32_t* __restrict__ vmax) {
+                                                         int32_t* __restrict__ tiles) {
   __shared__ long long red[16];
-  for (int i = threadIdx.x; i < H; i += blockDim.x) vmax[i] = 0u;
   const long long len = (long long)H * c_q;
   const long long per = (len + blockDim.x - 1) / blockDim.x;
   const long long lo = per * threadIdx.x, hi = lo + per < len ? lo + per : len;
@@ -81,37 +79,17 @@ __global__ __launch_bounds__(1024) void tile_table_kernel(const int32_t* __restr
   if (threadIdx.x == 0) tiles[len] = int32_t(tot);
 }
 
-// Largest |v| of every head as a bf16 bit pattern (sign cleared); positive
-// bf16 patterns order like their values.
-constexpr int kVmaxRows = 1024;
-__global__ __launch_bounds__(256) void vmax_kernel(const uint16_t* __restrict__ v, int n_k, int d,
-                                                  uint32_t* __restrict__ vmax) {
-  const int h = blockIdx.y;
-  const long long r0 = (long long)blockIdx.x * kVmaxRows;
-  const long long r1 = r0 + kVmaxRows < n_k ? r0 + kVmaxRows : n_k;
-  const uint4* src = reinterpret_cast<const uint4*>(v + ((long long)h * n_k) * d);
-  const long long c0 = r0 * d / 8, c1 = r1 * d / 8;
-  uint32_t mx = 0;
-  for (long long c = c0 + threadIdx.x; c < c1; c += 256) {
-    const uint4 w = src[c];
-    const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      mx = max(mx, ws[j] & 0x7fffu);
-      mx = max(mx, (ws[j] >> 16) & 0x7fffu);
-    }
-  }
-  mx = wave_max(mx);
-  if ((threadIdx.x & 63) == 0) atomicMax(&vmax[h], mx);
-}
-
 // Maps a launched block to (h, a, tile-in-group).  Blocks are dealt to the 8
-// XCDs round-robin by id; the remap gives each XCD a contiguous range of
-// work items so tiles of one query group (same K/V stream) share an L2.
+// XCDs round-robin by id.  The remap hands each XCD runs of kXcdRun
+// consecutive work items (tiles of one query group, same K/V stream, share
+// that XCD's L2) while the 8 XCDs interleave run by run, so the blocks in
+// flight across the GPU cover about one head: its K/V (tens of MB) stays in
+// the last-level cache instead of eight heads competing for it.
+constexpr int kXcdRun = 8;
 SPR_DEV bool locate_item(const AttnArgs& p, int& h, int& a, int& kt) {
   const int bid = blockIdx.x;
-  const int per_xcd = p.grid_blocks >> 3;
-  const int lid = (bid & 7) * per_xcd + (bid >> 3);
+  const int x = bid & 7, j = bid >> 3;
+  const int lid = (j / kXcdRun) * (8 * kXcdRun) + x * kXcdRun + (j % kXcdRun);
   const int total = p.tiles[p.H * p.c_q];
   if (lid >= total) return false;
   int lo = 0, hi = p.H * p.c_q - 1;
@@ -176,29 +154,96 @@ SPR_DEV int find_cell(const int32_t* cpos, int nc, int pos) {
 // ---------------------------------------------------------------------------
 // bf16 MFMA kernel
 // ---------------------------------------------------------------------------
+// LDS tiles (per stage): K as 64 rows x D bf16, V as 64 rows x D fp16, both
+// row-major in 16-byte chunks.  Tiles arrive straight from global memory
+// (global_load_lds, 16 bytes per lane): lane l of a wave writes LDS bytes
+// base + 16 l, so the XOR swizzle is applied by choosing which source chunk
+// each lane fetches.
+//   K chunk swizzle: physical = logical ^ (row & (CPR-1)); the QK^T A-operand
+//   read (32 rows, one chunk) then hits distinct banks.
+//   V chunk swizzle: physical = logical ^ swzV(row), a 64-byte-window rotation
+//   that spreads the 8 rows touched by one transposed read over the banks.
+// The PV A operand (V^T, 32 d x 16 keys) is read with ds_read_b64_tr_b16:
+// inside each 16-lane group, source lane r points at 4 values
+// V[k0 + r/4][d0 + 4(r%4) ..+3]; lane i then receives V[k0 + j][d0 + i] for
+// j = 0..3, i.e. 4 consecutive keys of its own column.
 template <int D>
-struct SmemBf16 {
-  uint16_t k[2][64 * D];
-  uint16_t vt[2][D * 64];
+struct SmemCells {
   int32_t cstart[SPARSEPR_MAX_GROUPS];
   int32_t cpos[SPARSEPR_MAX_GROUPS + 1];
   long long red[4];
 };
 
-// key position inside a 64-key tile of V^T: quads 1 and 2 of every 16 keys swap
-SPR_DEV int vt_key_pos(int kq) {
-  const int q4 = kq & 3;
-  const int pq = q4 == 1 ? 2 : (q4 == 2 ? 1 : q4);
-  return 16 * (kq >> 2) + 4 * pq;
+template <int B>
+struct Stage {
+  static constexpr int value = B;
+};
+
+typedef short v4i16_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4i16_t lds_v4i16_t;
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+template <int D>
+SPR_DEV int swz_v(int row) {
+  return D == 128 ? 4 * (row & 3) : 4 * ((row >> 1) & 1);
 }
+
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+
+typedef int v4i32_t __attribute__((ext_vector_type(4)));
+
+// Raw buffer resource over one head's rows (byte offsets at or past `bytes`
+// read as 0): base address, stride 0, num_records = bytes, raw dword format.
+SPR_DEV v4i32_t head_rsrc(const void* base, uint32_t bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  v4i32_t r;
+  r[0] = __builtin_amdgcn_readfirstlane(int(uint32_t(a)));
+  r[1] = __builtin_amdgcn_readfirstlane(int(uint32_t(a >> 32) & 0xffffu));
+  r[2] = __builtin_amdgcn_readfirstlane(int(bytes));
+  r[3] = 0x00020000;
+  return r;
+}
+
+// 16 bytes per lane from buffer offset `voff` straight into LDS at
+// lds_addr + 16 * lane.  Issued in asm so the compiler's wait insertion does
+// not pair it with later LDS reads of the other stage; completion is awaited
+// explicitly (vmcnt) before the barrier that publishes the stage.  M0 (the
+// LDS base) is read at issue and restored afterwards.
+SPR_DEV void lds_dma16(const v4i32_t& rsrc, uint32_t lds_addr, uint32_t voff) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %2, %3, 0 offen lds\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(lds_addr), "v"(voff), "s"(rsrc)
+      : "memory");
+}
+
+SPR_DEV uint32_t lds_addr_of(const void* p) {
+  return uint32_t(reinterpret_cast<size_t>(
+      (const __attribute__((address_space(3))) void*)(p)));
+}
+
+// log2-domain growth of the running max tolerated before O and l are rescaled
+// (P then stays below 2^8, well inside fp16)
+constexpr float kRescaleSlack = 8.f;
 
 template <int D>
 __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs p) {
-  constexpr int DCH = D / 8;          // 16-byte chunks per row
-  constexpr int NBLK = 16 * DCH;      // (key quad, dim chunk) load blocks per tile
-  constexpr int NS = D / 16;          // k-steps of the QK^T product
+  constexpr int CPR = D / 8;          // 16-byte chunks per row
+  constexpr int RPI = 64 / CPR;       // rows per 1 KB wave load
+  constexpr int NI = 16 / RPI;        // wave loads per tensor per tile (each wave: 16 rows)
+  constexpr int NS = D / 16;          // k-steps of QK^T
   constexpr int NDB = D / 32;         // 32-wide d blocks of the output
-  __shared__ SmemBf16<D> sm;
+  constexpr int RB = D * 2;           // row bytes (bf16 K, fp16 V)
+  // separate objects per stage: lets the compiler see that loads into one
+  // stage never alias reads of the other (no blanket wait before LDS reads)
+  __shared__ uint4 k_s0[8 * D], k_s1[8 * D];   // 64 rows x D bf16
+  __shared__ uint4 v_s0[8 * D], v_s1[8 * D];   // 64 rows x D fp16
+  __shared__ SmemCells<D> sm;
 
   int h, a, kt;
   if (!locate_item(p, h, a, kt)) return;
@@ -206,21 +251,20 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs p) {
   const int32_t* oq = p.off_q + (long long)h * (p.c_q + 1);
   const int r0 = oq[a] + kt * 128;
   const int nrows = min(128, oq[a + 1] - r0);
+  const int L = load_cells(p, h, a, sm.cstart, sm.cpos, sm.red);
+  const int ntiles = (L + 63) / 64;
+  // cell table -> (next boundary, row delta): row(pos) = pos + delta of its cell
   const int nc = p.rowptr[(long long)h * (p.c_q + 1) + a + 1] -
                  p.rowptr[(long long)h * (p.c_q + 1) + a];
-  const int L = load_cells(p, h, a, sm.cstart, sm.cpos, sm.red);
+  for (int i = tid; i < nc; i += 256) sm.cstart[i] -= sm.cpos[i];
+  __syncthreads();
 
-  const uint16_t* Kh = static_cast<const uint16_t*>(p.k) + (long long)h * p.n_k * D;
-  const uint16_t* Vh = static_cast<const uint16_t*>(p.v) + (long long)h * p.n_k * D;
-  // V scale 2^-sv puts the head's largest |v| in [2^14, 2^15): fp16 keeps
-  // every bf16 mantissa exactly down to 2^-28 of that maximum
-  int sv;
-  {
-    const int E = int((p.vmax[h] >> 7) & 0xffu);
-    sv = (E == 0 ? -127 : E - 127) - 14;
-    sv = sv < -100 ? -100 : (sv > 100 ? 100 : sv);
-  }
-  const float vscale = __builtin_ldexpf(1.f, -sv);
+  const uint32_t head_bytes = uint32_t(p.n_k) * RB;
+  const v4i32_t krs =
+      head_rsrc(static_cast<const char*>(p.k) + (long long)h * p.n_k * RB, head_bytes);
+  const v4i32_t vrs =
+      head_rsrc(static_cast<const char*>(p.v) + (long long)h * p.n_k * RB, head_bytes);
+  const int sv = p.v_shift[h];
 
   // query fragments: lane holds row n, dims 16s + 8g .. +8
   const int qloc = wid * 32 + n;
@@ -237,65 +281,41 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs p) {
       qf[s] = __builtin_bit_cast(bf16x8_t, w);
     }
   }
+  // Q fragments complete here (vmcnt(0)); otherwise the first use inside the
+  // loop would wait on the whole vector-memory queue, tile prefetch included
+  __builtin_amdgcn_s_waitcnt(0x0F70);
 
-  // loader role: key quad kq (keys 4kq..4kq+3 of the tile), dim chunk dc
-  const bool loader = tid < NBLK;
-  const int kq = tid / DCH, dc = tid % DCH;
-  uint4 kreg[4], vreg[4];
-  auto load_tile = [&](int t) {
-    if (!loader) return;
-    const int p0 = t * 64 + 4 * kq;
-    int c = p0 < L ? find_cell(sm.cpos, nc, p0) : 0;
+  // loader: wave w fills tile rows 16w .. 16w+15; load i covers RPI rows.
+  // Per load a cursor (cell index, its end position, its row delta).
+  int cur_c[NI], cur_end[NI], cur_dl[NI];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int pos = p0 + i;
-      if (pos < L) {
-        while (sm.cpos[c + 1] <= pos) ++c;
-        const long long row = sm.cstart[c] + (pos - sm.cpos[c]);
-        kreg[i] = *reinterpret_cast<const uint4*>(Kh + row * D + 8 * dc);
-        vreg[i] = *reinterpret_cast<const uint4*>(Vh + row * D + 8 * dc);
-      } else {
-        kreg[i] = make_uint4(0, 0, 0, 0);
-        vreg[i] = make_uint4(0, 0, 0, 0);
+  for (int i = 0; i < NI; ++i) {
+    cur_c[i] = 0;
+    cur_end[i] = sm.cpos[1];
+    cur_dl[i] = sm.cstart[0];
+  }
+  const int lrow = lane / CPR, lpc = lane % CPR;
+  auto issue_tile = [&](auto stage, int t) {
+    constexpr int B = decltype(stage)::value;
+    uint4* kbase = B == 0 ? k_s0 : k_s1;
+    uint4* vbase = B == 0 ? v_s0 : v_s1;
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const int row = 16 * wid + i * RPI + lrow;          // tile row of this lane
+      int pos = t * 64 + row;
+      pos = pos < L ? pos : L - 1;                        // tail rows: any valid row
+      while (pos >= cur_end[i]) {
+        ++cur_c[i];
+        cur_end[i] = sm.cpos[cur_c[i] + 1];
+        cur_dl[i] = sm.cstart[cur_c[i]];
       }
-    }
-  };
-  auto store_tile = [&](int buf) {
-    if (!loader) return;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r = 4 * kq + i;
-      const int pc = dc ^ (r & (DCH - 1));
-      *reinterpret_cast<uint4*>(&sm.k[buf][r * D + pc * 8]) = kreg[i];
-    }
-    const int kpos = vt_key_pos(kq);
-    const int chunk = kpos >> 3, half = (kpos >> 2) & 1;
-    uint32_t hv[4][4];  // [key][dim pair] fp16 pairs
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const uint32_t w[4] = {vreg[i].x, vreg[i].y, vreg[i].z, vreg[i].w};
-#pragma unroll
-      for (int m2 = 0; m2 < 4; ++m2) {
-        const _Float16 lo16 = static_cast<_Float16>(__uint_as_float(w[m2] << 16) * vscale);
-        const _Float16 hi16 = static_cast<_Float16>(__uint_as_float(w[m2] & 0xffff0000u) * vscale);
-        hv[i][m2] = uint32_t(__builtin_bit_cast(uint16_t, lo16)) |
-                    (uint32_t(__builtin_bit_cast(uint16_t, hi16)) << 16);
-      }
-    }
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int m = j >> 1;
-      uint32_t lo, hi;
-      if ((j & 1) == 0) {
-        lo = (hv[0][m] & 0xffffu) | (hv[1][m] << 16);
-        hi = (hv[2][m] & 0xffffu) | (hv[3][m] << 16);
-      } else {
-        lo = (hv[0][m] >> 16) | (hv[1][m] & 0xffff0000u);
-        hi = (hv[2][m] >> 16) | (hv[3][m] & 0xffff0000u);
-      }
-      const int d = 8 * dc + j;
-      const int pc = chunk ^ ((d >> 1) & 7);
-      *reinterpret_cast<uint2*>(&sm.vt[buf][d * 64 + pc * 8 + half * 4]) = make_uint2(lo, hi);
+      const uint32_t roff = uint32_t(pos + cur_dl[i]) * RB;
+      const int kc = lpc ^ (row & (CPR - 1));
+      const int vc = lpc ^ swz_v<D>(row);
+      uint4* kdst = kbase + (16 * wid + i * RPI) * CPR;
+      uint4* vdst = vbase + (16 * wid + i * RPI) * CPR;
+      lds_dma16(krs, __builtin_amdgcn_readfirstlane(lds_addr_of(kdst)), roff + kc * 16);
+      lds_dma16(vrs, __builtin_amdgcn_readfirstlane(lds_addr_of(vdst)), roff + vc * 16);
     }
   };
 
@@ -303,78 +323,112 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs p) {
 #pragma unroll
   for (int i = 0; i < NDB; ++i) oacc[i] = f32x16_t{};
   float m_run = -__builtin_huge_valf(), l_run = 0.f;
-  const float sl2 = p.scale_log2;
+  const float c2 = p.scale_log2;
+  const float slack = kRescaleSlack / c2;   // in raw score units
+  const f16x2_t ones = {static_cast<_Float16>(1.f), static_cast<_Float16>(1.f)};
 
-  auto compute = [&](int t, int buf) {
-    f32x16_t sacc[2];
+  // transposed-read addressing (fixed per lane): group G, index i in group
+  const int G = lane >> 4, gi = lane & 15, gg = G >> 1;
+  auto compute = [&](auto stage, int t) {
+    constexpr int B = decltype(stage)::value;
+    const uint4* kb_ = B == 0 ? k_s0 : k_s1;
+    const uint4* vb = B == 0 ? v_s0 : v_s1;
+    // S^T = K Q^T for the two 32-key blocks, fragments read one step ahead
+    f32x16_t sacc0 = f32x16_t{}, sacc1 = f32x16_t{};
+    const int r_a = n, r_b = 32 + n;
+    bf16x8_t a0 = __builtin_bit_cast(bf16x8_t, kb_[r_a * CPR + ((g) ^ (r_a & (CPR - 1)))]);
+    bf16x8_t a1 = __builtin_bit_cast(bf16x8_t, kb_[r_b * CPR + ((g) ^ (r_b & (CPR - 1)))]);
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      sacc[kb] = f32x16_t{};
-      const int r = 32 * kb + n;
+    for (int s = 0; s < NS; ++s) {
+      bf16x8_t n0 = a0, n1 = a1;
+      if (s + 1 < NS) {
+        n0 = __builtin_bit_cast(bf16x8_t, kb_[r_a * CPR + ((2 * s + 2 + g) ^ (r_a & (CPR - 1)))]);
+        n1 = __builtin_bit_cast(bf16x8_t, kb_[r_b * CPR + ((2 * s + 2 + g) ^ (r_b & (CPR - 1)))]);
+      }
+      sacc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qf[s], sacc0, 0, 0, 0);
+      sacc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qf[s], sacc1, 0, 0, 0);
+      a0 = n0;
+      a1 = n1;
+    }
+    // next tile's loads go out while the QK^T MFMAs drain
+    if (t + 1 < ntiles) issue_tile(Stage<1 - B>{}, t + 1);
+    const int tail = L - t * 64;   // valid keys in this tile (may exceed 64)
+    if (tail < 64) {
 #pragma unroll
-      for (int s = 0; s < NS; ++s) {
-        const int pc = (2 * s + g) ^ (r & (DCH - 1));
-        const bf16x8_t af = *reinterpret_cast<const bf16x8_t*>(&sm.k[buf][r * D + pc * 8]);
-        sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, qf[s], sacc[kb], 0, 0, 0);
+      for (int i = 0; i < 16; ++i) {
+        const int kk = 8 * (i >> 2) + 4 * g + (i & 3);
+        if (kk >= tail) sacc0[i] = -__builtin_huge_valf();
+        if (kk + 32 >= tail) sacc1[i] = -__builtin_huge_valf();
       }
     }
-    const int tail = L - t * 64;   // valid keys in this tile (may exceed 64)
     float mloc = -__builtin_huge_valf();
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int kk = 32 * kb + 8 * (i >> 2) + 4 * g + (i & 3);
-        float x = kk < tail ? sacc[kb][i] * sl2 : -__builtin_huge_valf();
-        sacc[kb][i] = x;
-        mloc = fmaxf(mloc, x);
-      }
+    for (int i = 0; i < 16; ++i) mloc = fmaxf(mloc, fmaxf(sacc0[i], sacc1[i]));
     mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
-    const float m_new = fmaxf(m_run, mloc);
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-    m_run = m_new;
-    float lsum = 0.f;
+    // lazy rescale: keep the old reference max unless the tile exceeds it by
+    // more than the slack (exact either way: O and l share the reference)
+    if (__ballot(mloc > m_run + slack)) {
+      const float m_new = fmaxf(m_run, mloc);
+      const float alpha = __builtin_amdgcn_exp2f((m_run - m_new) * c2);
+      m_run = m_new;
+      l_run *= alpha;
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const float e = __builtin_amdgcn_exp2f(sacc[kb][i] - m_new);
-        sacc[kb][i] = e;
-        lsum += e;
-      }
-    l_run = l_run * alpha + lsum;
-#pragma unroll
-    for (int db = 0; db < NDB; ++db) oacc[db] *= alpha;
+      for (int db = 0; db < NDB; ++db) oacc[db] *= alpha;
+    }
+    const float mc = m_run * c2;
     f16x8_t pf[4];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int kb = u >> 1, base = 8 * (u & 1);
-#pragma unroll
-      for (int j = 0; j < 8; ++j) pf[u][j] = static_cast<_Float16>(sacc[kb][base + j]);
+    for (int i = 0; i < 16; ++i) {
+      pf[i >> 3][i & 7] = static_cast<_Float16>(
+          __builtin_amdgcn_exp2f(__builtin_fmaf(sacc0[i], c2, -mc)));
+      pf[2 + (i >> 3)][i & 7] = static_cast<_Float16>(
+          __builtin_amdgcn_exp2f(__builtin_fmaf(sacc1[i], c2, -mc)));
     }
+    // row sum of the rounded P (the values the PV product uses)
+    float lsum = 0.f;
 #pragma unroll
-    for (int db = 0; db < NDB; ++db) {
-      const int d = 32 * db + n;
+    for (int u = 0; u < 4; ++u)
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int pc = (2 * u + g) ^ ((d >> 1) & 7);
-        const f16x8_t af = *reinterpret_cast<const f16x8_t*>(&sm.vt[buf][d * 64 + pc * 8]);
+      for (int j = 0; j < 8; j += 2)
+        lsum = __builtin_amdgcn_fdot2(f16x2_t{pf[u][j], pf[u][j + 1]}, ones, lsum, false);
+    l_run += lsum;
+    // u outer, d blocks inner: NDB independent accumulation chains interleave
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) {
+        // keys 16u + 4gg + gi/4 (first 4 slots) and +8 (last 4 slots); d chunk
+        const int row1 = 16 * u + 4 * gg + (gi >> 2);
+        const int row2 = row1 + 8;
+        const int ch = 4 * db + 2 * (G & 1) + ((gi & 3) >> 1);
+        const int hb = (gi & 1) * 8;
+        const char* b1 = reinterpret_cast<const char*>(vb + row1 * CPR + (ch ^ swz_v<D>(row1))) + hb;
+        const char* b2 = reinterpret_cast<const char*>(vb + row2 * CPR + (ch ^ swz_v<D>(row2))) + hb;
+        const v4i16_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)b1);
+        const v4i16_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)b2);
+        const f16x8_t af = __builtin_bit_cast(
+            f16x8_t, (short __attribute__((ext_vector_type(8)))){lo[0], lo[1], lo[2], lo[3],
+                                                                  hi[0], hi[1], hi[2], hi[3]});
         oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af, pf[u], oacc[db], 0, 0, 0);
       }
     }
   };
 
-  const int ntiles = (L + 63) / 64;
-  load_tile(0);
-  store_tile(0);
-  if (ntiles > 1) load_tile(1);
-  __syncthreads();
-  for (int t = 0; t < ntiles; ++t) {
-    const int buf = t & 1;
-    if (wave_active) compute(t, buf);
-    if (t + 1 < ntiles) store_tile(buf ^ 1);
-    if (t + 2 < ntiles) load_tile(t + 2);
-    __syncthreads();
+  // Two-stage pipeline with one barrier per tile: after the barrier of step
+  // t every wave has finished tile t-1, so the stage it used is refilled with
+  // tile t+1 (issued from inside compute, behind the QK^T MFMAs) while tile t
+  // is computed.  Raw s_barrier: __syncthreads() would
+  // also drain the loads in flight.
+  auto step = [&](auto stage, int t) {
+    constexpr int B = decltype(stage)::value;
+    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    if (wave_active) compute(stage, t);
+    else if (t + 1 < ntiles) issue_tile(Stage<1 - B>{}, t + 1);
+  };
+  if (ntiles > 0) issue_tile(Stage<0>{}, 0);
+  for (int t = 0; t < ntiles; t += 2) {
+    step(Stage<0>{}, t);
+    if (t + 1 < ntiles) step(Stage<1>{}, t + 1);
   }
 
   if (!row_valid) return;
@@ -389,7 +443,8 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs p) {
                              oacc[db][4 * i4 + 2] * inv, oacc[db][4 * i4 + 3] * inv);
       *reinterpret_cast<float4*>(orow + 32 * db + 8 * i4 + 4 * g) = v;
     }
-  if (g == 0 && p.lse) p.lse[(long long)h * p.n_q + r0 + qloc] = (m_run + __log2f(l_tot)) * kLn2;
+  if (g == 0 && p.lse)
+    p.lse[(long long)h * p.n_q + r0 + qloc] = (m_run * c2 + __log2f(l_tot)) * kLn2;
 }
 
 // ---------------------------------------------------------------------------
@@ -495,7 +550,6 @@ int rows_per_item(const sparsepr_dims* d) {
 size_t attn_ws_bytes(const sparsepr_dims* d) {
   Carver cv(nullptr);
   cv.take<int32_t>(size_t(d->heads) * d->c_q + 1);
-  cv.take<uint32_t>(size_t(d->heads));
   return cv.used;
 }
 
@@ -506,30 +560,25 @@ using namespace spr;
 extern "C" int32_t sparsepr_sparse_attn(const sparsepr_dims* dims, const int32_t* offsets_q,
                                         const int32_t* offsets_kv, const int32_t* cell_rowptr,
                                         const int32_t* cell_col, const void* q_g, const void* k_g,
-                                        const void* v_g, float softmax_scale, float* o_sp,
+                                        const void* v_g, const int32_t* v_shift,
+                                        float softmax_scale, float* o_sp,
                                         float* lse, void* ws, size_t ws_bytes,
                                         hipStream_t stream) {
   int32_t st = check_dims(dims);
   if (st != SPARSEPR_OK) return st;
-  if (!offsets_q || !offsets_kv || !cell_rowptr || !cell_col || !q_g || !k_g || !v_g || !o_sp)
+  if (!offsets_q || !offsets_kv || !cell_rowptr || !cell_col || !q_g || !k_g || !v_g ||
+      !v_shift || !o_sp)
     return SPARSEPR_ERR_INVALID;
   const size_t need = attn_ws_bytes(dims);
   if (!ws || ws_bytes < need) return SPARSEPR_ERR_WORKSPACE;
   Carver cv(ws);
   int32_t* tiles = cv.take<int32_t>(size_t(dims->heads) * dims->c_q + 1);
-  uint32_t* vmax = cv.take<uint32_t>(size_t(dims->heads));
   const int tq = rows_per_item(dims);
-  tile_table_kernel<<<1, 1024, 0, stream>>>(offsets_q, dims->heads, dims->c_q, tq, tiles, vmax);
+  tile_table_kernel<<<1, 1024, 0, stream>>>(offsets_q, dims->heads, dims->c_q, tq, tiles);
   SPR_LAUNCH_CHECK();
-  if (dims->dtype == SPARSEPR_BF16) {
-    dim3 g((dims->n_k + kVmaxRows - 1) / kVmaxRows, dims->heads);
-    vmax_kernel<<<g, 256, 0, stream>>>(static_cast<const uint16_t*>(v_g), dims->n_k,
-                                       dims->head_dim, vmax);
-    SPR_LAUNCH_CHECK();
-  }
   // upper bound of work items: sum_a ceil(n_a / tq) <= N_q / tq + C_q per head
   long long bound = (long long)dims->heads * ((dims->n_q + tq - 1) / tq + dims->c_q);
-  bound = (bound + 7) & ~7LL;
+  bound = (bound + 8 * kXcdRun - 1) / (8 * kXcdRun) * (8 * kXcdRun);
   if (bound > 0x7fffffffLL) return SPARSEPR_ERR_UNSUPPORTED;
   AttnArgs a;
   a.off_q = offsets_q;
@@ -542,7 +591,7 @@ extern "C" int32_t sparsepr_sparse_attn(const sparsepr_dims* dims, const int32_t
   a.o = o_sp;
   a.lse = lse;
   a.tiles = tiles;
-  a.vmax = vmax;
+  a.v_shift = v_shift;
   a.H = dims->heads;
   a.n_q = dims->n_q;
   a.n_k = dims->n_k;

@@ -29,9 +29,12 @@ struct KindArgs {
   int n, c, ntiles;
 };
 
-__global__ __launch_bounds__(kThreads) void hist_kernel(KindArgs qa, KindArgs ka) {
+__global__ __launch_bounds__(kThreads) void hist_kernel(KindArgs qa, KindArgs ka, uint32_t* vmax,
+                                                       int heads) {
   const KindArgs& A = blockIdx.z == 0 ? qa : ka;
   const int tile = blockIdx.x, h = blockIdx.y;
+  if (vmax && tile == 0 && h == 0 && blockIdx.z == 0)
+    for (int i = threadIdx.x; i < heads; i += kThreads) vmax[i] = 0u;
   if (tile >= A.ntiles) return;
   __shared__ int32_t hist[SPARSEPR_MAX_GROUPS];
   for (int i = threadIdx.x; i < A.c; i += kThreads) hist[i] = 0;
@@ -153,7 +156,17 @@ struct GatherArgs {
   int n[3];
   int row_bytes;   // d * element size (multiple of 16)
   int esize;
+  const uint32_t* vmax;  // bf16 inputs: per-head largest |v| bit pattern (else null)
+  int32_t* v_shift;      // [H] output: v_g = fp16(v * 2^-v_shift)
 };
+
+// Exponent shift that puts a head's largest |v| in [2^14, 2^15): every bf16
+// value down to 2^-28 of that maximum converts to fp16 without rounding.
+SPR_DEV int v_shift_of(uint32_t vmax_bits) {
+  const int E = int((vmax_bits >> 7) & 0xffu);
+  int s = (E == 0 ? -127 : E - 127) - 14;
+  return s < -100 ? -100 : (s > 100 ? 100 : s);
+}
 
 constexpr int kGatherRows = 64;
 
@@ -168,12 +181,58 @@ __global__ __launch_bounds__(kThreads) void gather_kernel(GatherArgs g) {
   const char* src = g.src[kind] + int64_t(h) * g.stride_head[kind] * g.esize;
   char* dst = g.dst[kind] + (int64_t(h) * n + r0) * g.row_bytes;
   const int64_t st = g.stride_tok[kind] * g.esize;
+  if (kind == 2 && g.vmax) {
+    // values: bf16 -> fp16 after the exact per-head power-of-two scale
+    const int sh = v_shift_of(g.vmax[h]);
+    const float sc = __builtin_ldexpf(1.f, -sh);
+    if (blockIdx.x == 0 && threadIdx.x == 0) g.v_shift[h] = sh;
+    for (int i = threadIdx.x; i < rows * chunks; i += kThreads) {
+      int r = i / chunks, c = i - r * chunks;
+      int tok = perm[r0 + r];
+      uint4 v = *reinterpret_cast<const uint4*>(src + tok * st + c * 16);
+      uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const _Float16 lo = static_cast<_Float16>(__uint_as_float(w[j] << 16) * sc);
+        const _Float16 hi = static_cast<_Float16>(__uint_as_float(w[j] & 0xffff0000u) * sc);
+        w[j] = uint32_t(__builtin_bit_cast(uint16_t, lo)) |
+               (uint32_t(__builtin_bit_cast(uint16_t, hi)) << 16);
+      }
+      *reinterpret_cast<uint4*>(dst + int64_t(r) * g.row_bytes + c * 16) =
+          make_uint4(w[0], w[1], w[2], w[3]);
+    }
+    return;
+  }
+  if (kind == 2 && blockIdx.x == 0 && threadIdx.x == 0 && g.v_shift) g.v_shift[h] = 0;
   for (int i = threadIdx.x; i < rows * chunks; i += kThreads) {
     int r = i / chunks, c = i - r * chunks;
     int tok = perm[r0 + r];
     uint4 v = *reinterpret_cast<const uint4*>(src + tok * st + c * 16);
     *reinterpret_cast<uint4*>(dst + int64_t(r) * g.row_bytes + c * 16) = v;
   }
+}
+
+// Largest |v| of every head of the caller's bf16 values (sign cleared; positive
+// bf16 bit patterns order like their values).  vmax must be zero on entry.
+__global__ __launch_bounds__(kThreads) void vmax_kernel(const uint16_t* __restrict__ v, int n,
+                                                       int d, int64_t stride_head,
+                                                       int64_t stride_tok,
+                                                       uint32_t* __restrict__ vmax) {
+  const int h = blockIdx.y;
+  const int r0 = blockIdx.x * kGatherRows;
+  if (r0 >= n) return;
+  const int rows = min(kGatherRows, n - r0);
+  const int chunks = d / 8;
+  uint32_t mx = 0;
+  for (int i = threadIdx.x; i < rows * chunks; i += kThreads) {
+    const int r = i / chunks, c = i - r * chunks;
+    const uint4 w = *reinterpret_cast<const uint4*>(v + h * stride_head + (r0 + r) * stride_tok + c * 8);
+    const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) mx = max(mx, max(ws[j] & 0x7fffu, (ws[j] >> 16) & 0x7fffu));
+  }
+  mx = wave_max(mx);
+  if ((threadIdx.x & 63) == 0) atomicMax(&vmax[h], mx);
 }
 
 // fp64 centroid of each group of the gathered q (kind 0) and k (kind 1).
@@ -220,6 +279,7 @@ size_t layout_ws_bytes(const sparsepr_dims* d) {
   int tq = (d->n_q + kTile - 1) / kTile, tk = (d->n_k + kTile - 1) / kTile;
   cv.take<int32_t>(size_t(d->heads) * d->c_q * tq);
   cv.take<int32_t>(size_t(d->heads) * d->c_k * tk);
+  cv.take<uint32_t>(size_t(d->heads));
   return cv.used;
 }
 
@@ -231,13 +291,13 @@ extern "C" int32_t sparsepr_partition_layout(const sparsepr_dims* dims, const in
                                              const int32_t* labels_kv, const void* q, const void* k,
                                              const void* v, int32_t* perm_q, int32_t* offsets_q,
                                              int32_t* perm_kv, int32_t* offsets_kv, void* q_g,
-                                             void* k_g, void* v_g, double* centroid_q,
-                                             double* centroid_k, void* ws, size_t ws_bytes,
-                                             hipStream_t stream) {
+                                             void* k_g, void* v_g, int32_t* v_shift,
+                                             double* centroid_q, double* centroid_k, void* ws,
+                                             size_t ws_bytes, hipStream_t stream) {
   int32_t st = check_dims(dims);
   if (st != SPARSEPR_OK) return st;
   if (!labels_q || !labels_kv || !q || !k || !v || !perm_q || !offsets_q || !perm_kv ||
-      !offsets_kv || !q_g || !k_g || !v_g || !centroid_q || !centroid_k)
+      !offsets_kv || !q_g || !k_g || !v_g || !v_shift || !centroid_q || !centroid_k)
     return SPARSEPR_ERR_INVALID;
   const size_t need = layout_ws_bytes(dims);
   if (need > 0 && (!ws || ws_bytes < need)) return SPARSEPR_ERR_WORKSPACE;
@@ -249,9 +309,11 @@ extern "C" int32_t sparsepr_partition_layout(const sparsepr_dims* dims, const in
               (dims->n_k + kTile - 1) / kTile};
   qa.counts = cv.take<int32_t>(size_t(H) * qa.c * qa.ntiles);
   ka.counts = cv.take<int32_t>(size_t(H) * ka.c * ka.ntiles);
+  uint32_t* vmax = cv.take<uint32_t>(size_t(H));
+  const bool bf16 = dims->dtype == SPARSEPR_BF16;
   const int maxt = qa.ntiles > ka.ntiles ? qa.ntiles : ka.ntiles;
 
-  hist_kernel<<<dim3(maxt, H, 2), kThreads, 0, stream>>>(qa, ka);
+  hist_kernel<<<dim3(maxt, H, 2), kThreads, 0, stream>>>(qa, ka, bf16 ? vmax : nullptr, H);
   SPR_LAUNCH_CHECK();
   scan_kernel<<<dim3(H, 2), 1024, 0, stream>>>(qa, ka);
   SPR_LAUNCH_CHECK();
@@ -277,7 +339,15 @@ extern "C" int32_t sparsepr_partition_layout(const sparsepr_dims* dims, const in
   g.n[1] = g.n[2] = dims->n_k;
   g.row_bytes = d * es;
   g.esize = es;
+  g.vmax = bf16 ? vmax : nullptr;
+  g.v_shift = v_shift;
   const int maxn = dims->n_q > dims->n_k ? dims->n_q : dims->n_k;
+  if (bf16) {
+    vmax_kernel<<<dim3((dims->n_k + kGatherRows - 1) / kGatherRows, H), kThreads, 0, stream>>>(
+        static_cast<const uint16_t*>(v), dims->n_k, d, dims->kv_stride_head, dims->kv_stride_tok,
+        vmax);
+    SPR_LAUNCH_CHECK();
+  }
   gather_kernel<<<dim3((maxn + kGatherRows - 1) / kGatherRows, H, 3), kThreads, 0, stream>>>(g);
   SPR_LAUNCH_CHECK();
 

@@ -180,9 +180,20 @@ __global__ __launch_bounds__(256) void select_kernel(
 // Thread layout: probe p = tid / 4 (64 probes), dim slice sl = tid % 4 of
 // D/4 dims.  Partial record per (head, chunk, probe): [mS, mU, ZS, ZU] and
 // NS[D], NU[D].
+// values: bf16 inputs arrive as fp16(v * 2^-v_shift) from the layout call
+template <typename T>
+SPR_DEV float v_to_f32(T x, float scale);
+template <>
+SPR_DEV float v_to_f32<uint16_t>(uint16_t x, float scale) {
+  return float(__builtin_bit_cast(_Float16, x)) * scale;
+}
+template <>
+SPR_DEV float v_to_f32<float>(float x, float scale) { return x; }
+
 template <typename T, int D>
 __global__ __launch_bounds__(256) void probe_rows_kernel(
     const T* __restrict__ q_g, const T* __restrict__ k_g, const T* __restrict__ v_g,
+    const int32_t* __restrict__ v_shift,
     const int32_t* __restrict__ off_k, const int32_t* __restrict__ rowptr,
     const int32_t* __restrict__ col, const int32_t* __restrict__ probe_rows,
     const int32_t* __restrict__ probe_group, int n_q, int n_k, int c_q, int c_k, int m,
@@ -226,6 +237,7 @@ __global__ __launch_bounds__(256) void probe_rows_kernel(
   const int k0 = chunk * per, k1 = min(n_k, k0 + per);
   const T* Kh = k_g + (long long)h * n_k * D;
   const T* Vh = v_g + (long long)h * n_k * D;
+  const float vscale = __builtin_ldexpf(1.f, v_shift[h]);
   for (int t0 = k0; t0 < k1; t0 += TK) {
     __syncthreads();
     for (int e = tid; e < TK * D; e += 256) {
@@ -234,7 +246,7 @@ __global__ __launch_bounds__(256) void probe_rows_kernel(
       float kv = 0.f, vv = 0.f;
       if (row < k1) {
         kv = to_f32(Kh[(long long)row * D + j]);
-        vv = to_f32(Vh[(long long)row * D + j]);
+        vv = v_to_f32(Vh[(long long)row * D + j], vscale);
       }
       ks[r][j] = kv;
       vs[r][j] = vv;
@@ -690,7 +702,8 @@ extern "C" int32_t sparsepr_probe_fit(const sparsepr_dims* dims, int32_t m, int3
                                       const int32_t* offsets_kv, const int32_t* perm_q,
                                       const int32_t* cell_rowptr, const int32_t* cell_col,
                                       const double* centroid_q, const void* q_g, const void* k_g,
-                                      const void* v_g, float softmax_scale, int32_t* probe_rows,
+                                      const void* v_g, const int32_t* v_shift,
+                                      float softmax_scale, int32_t* probe_rows,
                                       int32_t* probe_tokens, float* o_probe_dense,
                                       float* o_probe_sparse, float* corr_a, float* corr_psi_t,
                                       float* corr_c, void* ws, size_t ws_bytes,
@@ -700,7 +713,7 @@ extern "C" int32_t sparsepr_probe_fit(const sparsepr_dims* dims, int32_t m, int3
   if (m < 1 || m > SPARSEPR_MAX_PROBES || rank < 0 || rank > SPARSEPR_MAX_RANK || !(lambda >= 0.0))
     return SPARSEPR_ERR_INVALID;
   if (!offsets_q || !offsets_kv || !perm_q || !cell_rowptr || !cell_col || !centroid_q || !q_g ||
-      !k_g || !v_g || !probe_rows || !probe_tokens || !o_probe_dense || !corr_a || !corr_psi_t ||
+      !k_g || !v_g || !v_shift || !probe_rows || !probe_tokens || !o_probe_dense || !corr_a || !corr_psi_t ||
       !corr_c)
     return SPARSEPR_ERR_INVALID;
   if (rank > 0 && lambda == 0.0) return SPARSEPR_ERR_INVALID;  // dual solve needs lam > 0
@@ -723,11 +736,11 @@ extern "C" int32_t sparsepr_probe_fit(const sparsepr_dims* dims, int32_t m, int3
     auto* vv = static_cast<const uint16_t*>(v_g);
     if (d == 128)
       probe_rows_kernel<uint16_t, 128><<<dim3(kChunks, H), 256, 0, stream>>>(
-          qq, kk, vv, offsets_kv, cell_rowptr, cell_col, probe_rows, w.group, dims->n_q,
+          qq, kk, vv, v_shift, offsets_kv, cell_rowptr, cell_col, probe_rows, w.group, dims->n_q,
           dims->n_k, dims->c_q, dims->c_k, m, sl2, w.part_s, w.part_n);
     else
       probe_rows_kernel<uint16_t, 64><<<dim3(kChunks, H), 256, 0, stream>>>(
-          qq, kk, vv, offsets_kv, cell_rowptr, cell_col, probe_rows, w.group, dims->n_q,
+          qq, kk, vv, v_shift, offsets_kv, cell_rowptr, cell_col, probe_rows, w.group, dims->n_q,
           dims->n_k, dims->c_q, dims->c_k, m, sl2, w.part_s, w.part_n);
   } else {
     select_kernel<float><<<dim3(dims->c_q, H), 256, 0, stream>>>(
@@ -739,11 +752,11 @@ extern "C" int32_t sparsepr_probe_fit(const sparsepr_dims* dims, int32_t m, int3
     auto* vv = static_cast<const float*>(v_g);
     if (d == 128)
       probe_rows_kernel<float, 128><<<dim3(kChunks, H), 256, 0, stream>>>(
-          qq, kk, vv, offsets_kv, cell_rowptr, cell_col, probe_rows, w.group, dims->n_q,
+          qq, kk, vv, v_shift, offsets_kv, cell_rowptr, cell_col, probe_rows, w.group, dims->n_q,
           dims->n_k, dims->c_q, dims->c_k, m, sl2, w.part_s, w.part_n);
     else
       probe_rows_kernel<float, 64><<<dim3(kChunks, H), 256, 0, stream>>>(
-          qq, kk, vv, offsets_kv, cell_rowptr, cell_col, probe_rows, w.group, dims->n_q,
+          qq, kk, vv, v_shift, offsets_kv, cell_rowptr, cell_col, probe_rows, w.group, dims->n_q,
           dims->n_k, dims->c_q, dims->c_k, m, sl2, w.part_s, w.part_n);
   }
   SPR_LAUNCH_CHECK();

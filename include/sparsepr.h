@@ -111,7 +111,12 @@ int32_t sparsepr_version(void);
  *     row.  Groups in ascending id, tokens ascending inside a group (stable).
  *   offsets_q [H][C_q+1], offsets_kv [H][C_k+1]: int32 first row of each
  *     group; an empty group has offsets[a] == offsets[a+1].
- *   q_g [H][N_q][d], k_g, v_g [H][N_k][d]: dims.dtype, bit-exact copies.
+ *   q_g [H][N_q][d], k_g [H][N_k][d]: dims.dtype, bit-exact copies.
+ *   v_g [H][N_k][d] and v_shift [H] (int32): for SPARSEPR_F32, an fp32 copy
+ *     and shift 0; for SPARSEPR_BF16, the fp16 operand of the PV product,
+ *     v_g = fp16(v * 2^-v_shift[h]) with v_shift[h] chosen so the head's
+ *     largest |v| lands in [2^14, 2^15): every bf16 value down to 2^-28 of
+ *     that maximum converts exactly (smaller ones round to fp16 subnormals).
  *   centroid_q [H][C_q][d], centroid_k [H][C_k][d]: fp64 group means of q
  *     and k (exact fp64 sums of the inputs, divided by the group size);
  *     rows of empty groups are 0.
@@ -121,7 +126,7 @@ int32_t sparsepr_partition_layout(const sparsepr_dims* dims /* host */,
                                   const void* q, const void* k, const void* v,
                                   int32_t* perm_q, int32_t* offsets_q,
                                   int32_t* perm_kv, int32_t* offsets_kv,
-                                  void* q_g, void* k_g, void* v_g,
+                                  void* q_g, void* k_g, void* v_g, int32_t* v_shift,
                                   double* centroid_q, double* centroid_k,
                                   void* ws, size_t ws_bytes, hipStream_t stream);
 
@@ -153,7 +158,7 @@ int32_t sparsepr_route_cells(const sparsepr_dims* dims /* host */,
  * S5. Renormalised hard-drop attention.  (SparsePR paper §3: a query of
  * group a attends only to keys of the groups selected for a, with the
  * softmax normalised over those keys.)
- *   q_g, k_g, v_g: group-major [H][N][d] in dims.dtype.
+ *   q_g, k_g, v_g, v_shift: group-major outputs of partition_layout.
  *   softmax_scale: logits are (q . k) * softmax_scale (1/sqrt(d) normally).
  * Outputs (group-major row order)
  *   o_sp [H][N_q][d]: fp32 sparse output.
@@ -165,6 +170,7 @@ int32_t sparsepr_sparse_attn(const sparsepr_dims* dims /* host */,
                              const int32_t* offsets_q, const int32_t* offsets_kv,
                              const int32_t* cell_rowptr, const int32_t* cell_col,
                              const void* q_g, const void* k_g, const void* v_g,
+                             const int32_t* v_shift,
                              float softmax_scale, float* o_sp, float* lse,
                              void* ws, size_t ws_bytes, hipStream_t stream);
 
@@ -199,7 +205,7 @@ int32_t sparsepr_probe_fit(const sparsepr_dims* dims /* host */, int32_t m, int3
                            const int32_t* cell_rowptr, const int32_t* cell_col,
                            const double* centroid_q,
                            const void* q_g, const void* k_g, const void* v_g,
-                           float softmax_scale,
+                           const int32_t* v_shift, float softmax_scale,
                            int32_t* probe_rows, int32_t* probe_tokens,
                            float* o_probe_dense, float* o_probe_sparse,
                            float* corr_a, float* corr_psi_t, float* corr_c,
