@@ -67,7 +67,7 @@ def test_workspace_sizes(lib):
 
 def _layout_status(lib, dims, null=False, ws_bytes=1 << 30):
     p = ctypes.c_void_p(0 if null else 4096)
-    args = [p] * 14
+    args = [p] * 15
     return lib.sparsepr_partition_layout(ctypes.byref(dims), *args, ctypes.c_void_p(4096),
                                          ws_bytes, None)
 
@@ -88,7 +88,7 @@ def test_argument_validation_before_launch(lib):
     # probe_fit: m out of range, rank out of range, lambda 0 with rank > 0
     for m, rank, lam in [(0, 16, 0.1), (65, 16, 0.1), (64, -1, 0.1), (64, 65, 0.1), (64, 16, 0.0),
                          (64, 16, float("nan"))]:
-        st = lib.sparsepr_probe_fit(ctypes.byref(good), m, rank, lam, *([P] * 9),
+        st = lib.sparsepr_probe_fit(ctypes.byref(good), m, rank, lam, *([P] * 10),
                                     ctypes.c_float(0.125), *([P] * 7), P, 1 << 30, None)
         assert st == fb.ERR_INVALID, (m, rank, lam)
     # correct: unsupported output dtype, misaligned output stride
