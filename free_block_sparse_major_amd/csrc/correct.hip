@@ -5,19 +5,18 @@
 // dense output, and the result returns to the original order.  With the
 // folded fit, out = o + (o A) Psi^T + c.
 //
-// HBM-bound: every block stages 64 group-major rows of O_sp through LDS with
-// fully coalesced 16-byte loads, then 4 lanes share a row (D/4 dims each):
-// u = o A is reduced across the 4 lanes, the row is rebuilt and written to
-// its original token position.  A block walks several row tiles so the
-// per-head A, Psi^T and c are loaded once per block.
+// HBM-bound: O_sp is read once and the output written once; the
+// 2 * d * rank FMAs per row run from registers with A and Psi broadcast from
+// LDS, loaded once per block of 4 waves x 4 row tiles.
 
 #include "common.h"
 
 namespace spr {
 namespace {
 
-constexpr int kRowsPerTile = 64;
-constexpr int kTilesPerBlock = 8;
+constexpr int kRowsPerTile = 64;     // one row per lane of a wave
+constexpr int kTilesPerWave = 4;
+constexpr int kStagePitch = 36;      // floats per staged row (32 + 4: conflict-free 16B reads)
 
 struct CorrArgs {
   const int32_t* perm_q;
@@ -31,77 +30,109 @@ struct CorrArgs {
   int out_bf16;
 };
 
+// Each wave owns 64-row tiles, one row per lane held in registers.  Rows
+// move between HBM and registers through a per-wave LDS stage in 32-column
+// slices: global accesses stay contiguous within each row, while a lane
+// reads or writes its own row in LDS.  A and Psi are stored k-contiguous
+// ([d][rank]) in LDS and read as broadcasts.  LDS traffic of one wave stays
+// inside that wave, whose LDS operations complete in program order.
 template <int D, int RK>
 __global__ __launch_bounds__(256) void correct_kernel(CorrArgs a) {
-  constexpr int DPL = D / 4;
-  const int h = blockIdx.y, tid = threadIdx.x;
-  __shared__ float sA[D][RK + 1];
-  __shared__ float sP[RK][D + 4];
+  constexpr int NSL = D / 32;                // 32-column slices
+  const int h = blockIdx.y, tid = threadIdx.x, wid = tid >> 6, lane = tid & 63;
+  __shared__ float4 sA4[D * RK / 4];         // A[i][k]
+  __shared__ float4 sP4[D * RK / 4];         // Psi^T transposed: P[i][k]
   __shared__ float sc[D];
-  __shared__ float tile[kRowsPerTile][D + 4];
+  __shared__ float stage[4][kRowsPerTile * kStagePitch];
+  float* sA = reinterpret_cast<float*>(sA4);
+  float* sP = reinterpret_cast<float*>(sP4);
   const float* Ah = a.corr_a + (long long)h * D * a.rank;
   const float* Ph = a.corr_psi_t + (long long)h * a.rank * D;
   for (int e = tid; e < D * RK; e += 256) {
     const int i = e / RK, k = e % RK;
-    sA[i][k] = k < a.rank ? Ah[i * a.rank + k] : 0.f;
-  }
-  for (int e = tid; e < RK * D; e += 256) {
-    const int k = e / D, i = e % D;
-    sP[k][i] = k < a.rank ? Ph[k * D + i] : 0.f;
+    sA[e] = k < a.rank ? Ah[i * a.rank + k] : 0.f;
+    sP[e] = k < a.rank ? Ph[k * D + i] : 0.f;
   }
   for (int i = tid; i < D; i += 256) sc[i] = a.corr_c[(long long)h * D + i];
-  const int r_in = tid >> 2, sl = tid & 3;
-  for (int tt = 0; tt < kTilesPerBlock; ++tt) {
-    const int row0 = (blockIdx.x * kTilesPerBlock + tt) * kRowsPerTile;
+  __syncthreads();
+  float* st = stage[wid];
+  for (int tt = 0; tt < kTilesPerWave; ++tt) {
+    const int row0 = ((blockIdx.x * 4 + wid) * kTilesPerWave + tt) * kRowsPerTile;
     if (row0 >= a.n_q) break;
     const int rows = min(kRowsPerTile, a.n_q - row0);
-    __syncthreads();
     const float* src = a.o_sp + ((long long)h * a.n_q + row0) * D;
-    for (int e = tid; e < rows * (D / 4); e += 256) {
-      const int r = e / (D / 4), c4 = e % (D / 4);
-      *reinterpret_cast<float4*>(&tile[r][4 * c4]) =
-          *reinterpret_cast<const float4*>(src + (long long)r * D + 4 * c4);
-    }
-    __syncthreads();
-    if (r_in >= rows) continue;
-    float o[DPL];
+    float o[D];
 #pragma unroll
-    for (int i = 0; i < DPL; ++i) o[i] = tile[r_in][sl * DPL + i];
+    for (int sl = 0; sl < NSL; ++sl) {
+      // slice sl of the 64 rows: 8 16-byte chunks per row, contiguous per row
+#pragma unroll
+      for (int it = 0; it < 8; ++it) {
+        const int e = it * 64 + lane, r = e >> 3, c = e & 7;
+        float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (r < rows) v = *reinterpret_cast<const float4*>(src + (long long)r * D + 32 * sl + 4 * c);
+        *reinterpret_cast<float4*>(st + r * kStagePitch + 4 * c) = v;
+      }
+#pragma unroll
+      for (int c = 0; c < 8; ++c) {
+        const float4 v = *reinterpret_cast<const float4*>(st + lane * kStagePitch + 4 * c);
+        o[32 * sl + 4 * c + 0] = v.x;
+        o[32 * sl + 4 * c + 1] = v.y;
+        o[32 * sl + 4 * c + 2] = v.z;
+        o[32 * sl + 4 * c + 3] = v.w;
+      }
+    }
     float u[RK];
 #pragma unroll
-    for (int k = 0; k < RK; ++k) {
-      float s = 0.f;
+    for (int k = 0; k < RK; ++k) u[k] = 0.f;
+#pragma unroll 4
+    for (int i = 0; i < D; ++i) {
 #pragma unroll
-      for (int i = 0; i < DPL; ++i) s = fmaf(o[i], sA[sl * DPL + i][k], s);
-      s += __shfl_xor(s, 1);
-      s += __shfl_xor(s, 2);
-      u[k] = s;
-    }
-#pragma unroll
-    for (int i = 0; i < DPL; ++i) {
-      float s = o[i] + sc[sl * DPL + i];
-#pragma unroll
-      for (int k = 0; k < RK; ++k) s = fmaf(u[k], sP[k][sl * DPL + i], s);
-      o[i] = s;
-    }
-    const int tok = a.perm_q[(long long)h * a.n_q + row0 + r_in];
-    const long long base = (long long)h * a.out_sh + (long long)tok * a.out_st + sl * DPL;
-    if (a.out_bf16) {
-      uint16_t* dst = static_cast<uint16_t*>(a.out) + base;
-#pragma unroll
-      for (int i = 0; i < DPL; i += 8) {
-        uint4 w;
-        w.x = uint32_t(f32_to_bf16_rne(o[i + 0])) | (uint32_t(f32_to_bf16_rne(o[i + 1])) << 16);
-        w.y = uint32_t(f32_to_bf16_rne(o[i + 2])) | (uint32_t(f32_to_bf16_rne(o[i + 3])) << 16);
-        w.z = uint32_t(f32_to_bf16_rne(o[i + 4])) | (uint32_t(f32_to_bf16_rne(o[i + 5])) << 16);
-        w.w = uint32_t(f32_to_bf16_rne(o[i + 6])) | (uint32_t(f32_to_bf16_rne(o[i + 7])) << 16);
-        *reinterpret_cast<uint4*>(dst + i) = w;
+      for (int k4 = 0; k4 < RK / 4; ++k4) {
+        const float4 w = sA4[i * (RK / 4) + k4];
+        u[4 * k4 + 0] = fmaf(o[i], w.x, u[4 * k4 + 0]);
+        u[4 * k4 + 1] = fmaf(o[i], w.y, u[4 * k4 + 1]);
+        u[4 * k4 + 2] = fmaf(o[i], w.z, u[4 * k4 + 2]);
+        u[4 * k4 + 3] = fmaf(o[i], w.w, u[4 * k4 + 3]);
       }
-    } else {
-      float* dst = static_cast<float*>(a.out) + base;
+    }
+#pragma unroll 4
+    for (int i = 0; i < D; ++i) {
+      float v = o[i] + sc[i];
 #pragma unroll
-      for (int i = 0; i < DPL; i += 4)
-        *reinterpret_cast<float4*>(dst + i) = make_float4(o[i], o[i + 1], o[i + 2], o[i + 3]);
+      for (int k4 = 0; k4 < RK / 4; ++k4) {
+        const float4 w = sP4[i * (RK / 4) + k4];
+        v = fmaf(u[4 * k4 + 0], w.x, v);
+        v = fmaf(u[4 * k4 + 1], w.y, v);
+        v = fmaf(u[4 * k4 + 2], w.z, v);
+        v = fmaf(u[4 * k4 + 3], w.w, v);
+      }
+      o[i] = v;
+    }
+    // write back in original token order through the stage
+    const int my_tok = lane < rows ? a.perm_q[(long long)h * a.n_q + row0 + lane] : 0;
+#pragma unroll
+    for (int sl = 0; sl < NSL; ++sl) {
+#pragma unroll
+      for (int c = 0; c < 8; ++c)
+        *reinterpret_cast<float4*>(st + lane * kStagePitch + 4 * c) =
+            make_float4(o[32 * sl + 4 * c], o[32 * sl + 4 * c + 1], o[32 * sl + 4 * c + 2],
+                        o[32 * sl + 4 * c + 3]);
+#pragma unroll
+      for (int it = 0; it < 8; ++it) {
+        const int e = it * 64 + lane, r = e >> 3, c = e & 7;
+        const int tok = __shfl(my_tok, r);
+        const float4 v = *reinterpret_cast<const float4*>(st + r * kStagePitch + 4 * c);
+        if (r >= rows) continue;
+        const long long base = (long long)h * a.out_sh + (long long)tok * a.out_st + 32 * sl + 4 * c;
+        if (a.out_bf16) {
+          uint2 w;
+          w.x = uint32_t(f32_to_bf16_rne(v.x)) | (uint32_t(f32_to_bf16_rne(v.y)) << 16);
+          w.y = uint32_t(f32_to_bf16_rne(v.z)) | (uint32_t(f32_to_bf16_rne(v.w)) << 16);
+          *reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.out) + base) = w;
+        } else {
+          *reinterpret_cast<float4*>(static_cast<float*>(a.out) + base) = v;
+        }
+      }
     }
   }
 }
@@ -169,7 +200,7 @@ extern "C" int32_t sparsepr_correct(const sparsepr_dims* dims, int32_t m, int32_
   a.n_q = dims->n_q;
   a.rank = rank;
   a.out_bf16 = out_dtype == SPARSEPR_BF16;
-  const int per_block = kRowsPerTile * kTilesPerBlock;
+  const int per_block = kRowsPerTile * kTilesPerWave * 4;
   dim3 grid((dims->n_q + per_block - 1) / per_block, dims->heads);
   if (dims->head_dim == 128) launch_correct<128>(a, grid, stream);
   else launch_correct<64>(a, grid, stream);

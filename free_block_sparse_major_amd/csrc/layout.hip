@@ -214,15 +214,17 @@ __global__ __launch_bounds__(kThreads) void gather_kernel(GatherArgs g) {
 
 // Largest |v| of every head of the caller's bf16 values (sign cleared; positive
 // bf16 bit patterns order like their values).  vmax must be zero on entry.
+constexpr int kVmaxRows = 1024;
 __global__ __launch_bounds__(kThreads) void vmax_kernel(const uint16_t* __restrict__ v, int n,
                                                        int d, int64_t stride_head,
                                                        int64_t stride_tok,
                                                        uint32_t* __restrict__ vmax) {
   const int h = blockIdx.y;
-  const int r0 = blockIdx.x * kGatherRows;
+  const int r0 = blockIdx.x * kVmaxRows;
   if (r0 >= n) return;
-  const int rows = min(kGatherRows, n - r0);
+  const int rows = min(kVmaxRows, n - r0);
   const int chunks = d / 8;
+  __shared__ uint32_t red[kThreads / 64];
   uint32_t mx = 0;
   for (int i = threadIdx.x; i < rows * chunks; i += kThreads) {
     const int r = i / chunks, c = i - r * chunks;
@@ -231,25 +233,39 @@ __global__ __launch_bounds__(kThreads) void vmax_kernel(const uint16_t* __restri
 #pragma unroll
     for (int j = 0; j < 4; ++j) mx = max(mx, max(ws[j] & 0x7fffu, (ws[j] >> 16) & 0x7fffu));
   }
-  mx = wave_max(mx);
-  if ((threadIdx.x & 63) == 0) atomicMax(&vmax[h], mx);
+  mx = block_max(mx, red);
+  if (threadIdx.x == 0) atomicMax(&vmax[h], mx);
 }
 
 // fp64 centroid of each group of the gathered q (kind 0) and k (kind 1).
-// Columns are split over threads, rows over `phases`; phase partials are
-// combined in a fixed order, so the result is deterministic.
+// A thread owns 8 consecutive dims (one 16-byte chunk) of a row phase; the
+// phase partials are combined in a fixed order, so the result is
+// deterministic.
 template <typename T>
-SPR_DEV double load_as_f64(const T* p);
+SPR_DEV void add_chunk(double* acc, const uint4& w);
 template <>
-SPR_DEV double load_as_f64<uint16_t>(const uint16_t* p) { return double(bf16_to_f32(*p)); }
+SPR_DEV void add_chunk<uint16_t>(double* acc, const uint4& w) {
+  const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    acc[2 * j] += double(__uint_as_float(ws[j] << 16));
+    acc[2 * j + 1] += double(__uint_as_float(ws[j] & 0xffff0000u));
+  }
+}
 template <>
-SPR_DEV double load_as_f64<float>(const float* p) { return double(*p); }
+SPR_DEV void add_chunk<float>(double* acc, const uint4& w) {
+  acc[0] += double(__uint_as_float(w.x));
+  acc[1] += double(__uint_as_float(w.y));
+  acc[2] += double(__uint_as_float(w.z));
+  acc[3] += double(__uint_as_float(w.w));
+}
 
 template <typename T>
 __global__ __launch_bounds__(kThreads) void centroid_kernel(const T* q_g, const T* k_g,
                                                             const int32_t* off_q, const int32_t* off_k,
                                                             double* cen_q, double* cen_k, int n_q,
                                                             int n_k, int c_q, int c_k, int d) {
+  constexpr int EPC = 16 / sizeof(T);          // elements per 16-byte chunk
   const int kind = blockIdx.z, h = blockIdx.y, a = blockIdx.x;
   const int C = kind == 0 ? c_q : c_k;
   if (a >= C) return;
@@ -257,17 +273,21 @@ __global__ __launch_bounds__(kThreads) void centroid_kernel(const T* q_g, const 
   const int32_t* off = (kind == 0 ? off_q : off_k) + int64_t(h) * (C + 1);
   const T* x = (kind == 0 ? q_g : k_g) + int64_t(h) * N * d;
   double* cen = (kind == 0 ? cen_q : cen_k) + (int64_t(h) * C + a) * d;
-  __shared__ double part[kThreads];
-  const int phases = kThreads / d;
-  const int j = threadIdx.x % d, ph = threadIdx.x / d;
+  __shared__ double part[kThreads * 8];
+  const int cpr = d / EPC;                     // chunks per row
+  const int phases = kThreads / cpr;
+  const int ch = threadIdx.x % cpr, ph = threadIdx.x / cpr;
   const int lo = off[a], hi = off[a + 1];
-  double s = 0.0;
-  for (int r = lo + ph; r < hi; r += phases) s += load_as_f64(x + int64_t(r) * d + j);
-  part[threadIdx.x] = s;
+  double acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  for (int r = lo + ph; r < hi; r += phases)
+    add_chunk<T>(acc, *reinterpret_cast<const uint4*>(x + int64_t(r) * d + ch * EPC));
+#pragma unroll
+  for (int e = 0; e < EPC; ++e) part[threadIdx.x * 8 + e] = acc[e];
   __syncthreads();
-  if (ph == 0) {
+  for (int j = threadIdx.x; j < d; j += kThreads) {
+    const int c = j / EPC, e = j % EPC;
     double t = 0.0;
-    for (int p = 0; p < phases; ++p) t += part[p * d + j];
+    for (int p2 = 0; p2 < phases; ++p2) t += part[(p2 * cpr + c) * 8 + e];
     cen[j] = hi > lo ? t / double(hi - lo) : 0.0;
   }
 }
@@ -343,7 +363,7 @@ extern "C" int32_t sparsepr_partition_layout(const sparsepr_dims* dims, const in
   g.v_shift = v_shift;
   const int maxn = dims->n_q > dims->n_k ? dims->n_q : dims->n_k;
   if (bf16) {
-    vmax_kernel<<<dim3((dims->n_k + kGatherRows - 1) / kGatherRows, H), kThreads, 0, stream>>>(
+    vmax_kernel<<<dim3((dims->n_k + kVmaxRows - 1) / kVmaxRows, H), kThreads, 0, stream>>>(
         static_cast<const uint16_t*>(v), dims->n_k, d, dims->kv_stride_head, dims->kv_stride_tok,
         vmax);
     SPR_LAUNCH_CHECK();

@@ -27,6 +27,7 @@
 // projection into A = diag(1/s) B Psi and c = mu_R - (mu_x A) Psi^T.
 
 #include "common.h"
+#include "mfma_tiles.h"
 
 namespace spr {
 namespace {
@@ -329,40 +330,265 @@ __global__ __launch_bounds__(256) void probe_rows_kernel(
 }
 
 // ---------------------------------------------------------------------------
+// exact probe rows, bf16 inputs: MFMA version
+// ---------------------------------------------------------------------------
+// Two waves per block (probes 0..31 and 32..63) sweep one key chunk in
+// 64-key tiles.  QK^T is a bf16 MFMA (exact products); each score is
+// classified as retained (its K/V group is selected for the probe's query
+// group) or omitted by a per-tile 64-bit mask per probe, built from the
+// group bitmask (keys are group-major, so a tile spans few groups).  The
+// retained and omitted classes keep separate running maxima.  PV runs on
+// fp16 MFMA with P split into hi + lo halves, so the partial numerators
+// carry ~2^-22 relative error.
+template <int D>
+__global__ __launch_bounds__(128) void probe_rows_mfma_kernel(
+    const uint16_t* __restrict__ q_g, const uint16_t* __restrict__ k_g,
+    const uint16_t* __restrict__ v_g, const int32_t* __restrict__ v_shift,
+    const int32_t* __restrict__ off_k, const int32_t* __restrict__ rowptr,
+    const int32_t* __restrict__ col, const int32_t* __restrict__ probe_rows,
+    const int32_t* __restrict__ probe_group, int n_q, int n_k, int c_q, int c_k, int m,
+    float c2, float* __restrict__ part_s, float* __restrict__ part_n) {
+  constexpr int CPR = D / 8, NS = D / 16, NDB = D / 32;
+  const int chunk = blockIdx.x, h = blockIdx.y, tid = threadIdx.x;
+  const int wid = tid >> 6, lane = tid & 63, n = lane & 31, g = lane >> 5;
+  __shared__ uint4 kt[64 * CPR], vt[64 * CPR];
+  __shared__ uint32_t mask[kMaxM][32];
+  __shared__ int32_t okl[SPARSEPR_MAX_GROUPS + 1];
+  __shared__ unsigned long long tmask[kMaxM];
+  for (int i = tid; i < kMaxM * 32; i += 128) (&mask[0][0])[i] = 0u;
+  const int32_t* ok = off_k + (long long)h * (c_k + 1);
+  for (int i = tid; i <= c_k; i += 128) okl[i] = ok[i];
+  __syncthreads();
+  {
+    const int pp = tid >> 1, half = tid & 1;
+    if (pp < m && probe_rows[(long long)h * m + pp] >= 0) {
+      const int grp = probe_group[(long long)h * m + pp];
+      const int32_t* rp = rowptr + (long long)h * (c_q + 1);
+      const int32_t* cl = col + (long long)h * c_q * c_k;
+      for (int i = rp[grp] + half; i < rp[grp + 1]; i += 2) {
+        const int b = cl[i];
+        atomicOr(&mask[pp][b >> 5], 1u << (b & 31));
+      }
+    }
+  }
+  const int p = wid * 32 + n;
+  const bool pvalid = p < m && probe_rows[(long long)h * m + p] >= 0;
+  bf16x8_t qf[NS];
+  {
+    const int row = pvalid ? probe_rows[(long long)h * m + p] : 0;
+    const uint16_t* qr = q_g + ((long long)h * n_q + row) * D;
+#pragma unroll
+    for (int s2 = 0; s2 < NS; ++s2) {
+      const uint4 w = pvalid ? *reinterpret_cast<const uint4*>(qr + 16 * s2 + 8 * g)
+                             : make_uint4(0, 0, 0, 0);
+      qf[s2] = __builtin_bit_cast(bf16x8_t, w);
+    }
+  }
+  const int per = (n_k + kChunks - 1) / kChunks;
+  const int k0 = chunk * per, k1 = min(n_k, k0 + per);
+  const char* Kh = reinterpret_cast<const char*>(k_g) + (long long)h * n_k * D * 2;
+  const char* Vh = reinterpret_cast<const char*>(v_g) + (long long)h * n_k * D * 2;
+  const float NEG = -__builtin_huge_valf();
+  const float slack = 8.f / c2;
+  float mS = NEG, mU = NEG, zS = 0.f, zU = 0.f;
+  f32x16_t oS[NDB], oU[NDB];
+#pragma unroll
+  for (int i = 0; i < NDB; ++i) oS[i] = oU[i] = f32x16_t{};
+
+  for (int t0 = k0; t0 < k1; t0 += 64) {
+    __syncthreads();
+    for (int e = tid; e < 64 * CPR; e += 128) {
+      const int r = e / CPR, c = e % CPR;
+      const int row = t0 + r;
+      uint4 kv = make_uint4(0, 0, 0, 0), vv = make_uint4(0, 0, 0, 0);
+      if (row < k1) {
+        kv = *reinterpret_cast<const uint4*>(Kh + (long long)row * D * 2 + c * 16);
+        vv = *reinterpret_cast<const uint4*>(Vh + (long long)row * D * 2 + c * 16);
+      }
+      kt[k_slot<D>(r, c)] = kv;
+      vt[v_slot<D>(r, c)] = vv;
+    }
+    if (tid < kMaxM) {
+      unsigned long long bits = 0ull;
+      if (tid < m && probe_rows[(long long)h * m + tid] >= 0) {
+        const int last = min(t0 + 64, k1) - 1;
+        int lo = 0, hi = c_k - 1;   // group of key t0: largest b with okl[b] <= t0
+        while (lo < hi) {
+          const int mid = (lo + hi + 1) >> 1;
+          if (okl[mid] <= t0) lo = mid;
+          else hi = mid - 1;
+        }
+        for (int b = lo; b < c_k && okl[b] <= last; ++b) {
+          if (!((mask[tid][b >> 5] >> (b & 31)) & 1u)) continue;
+          const int a0 = max(okl[b], t0) - t0, a1 = min(okl[b + 1], last + 1) - t0;
+          if (a1 <= a0) continue;
+          const unsigned long long span = a1 - a0 >= 64 ? ~0ull : ((1ull << (a1 - a0)) - 1ull);
+          bits |= span << a0;
+        }
+      }
+      tmask[tid] = bits;
+    }
+    __syncthreads();
+    f32x16_t s0 = f32x16_t{}, s1 = f32x16_t{};
+#pragma unroll
+    for (int s2 = 0; s2 < NS; ++s2) {
+      s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k_frag<D>(kt, n, s2, g), qf[s2], s0, 0, 0, 0);
+      s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k_frag<D>(kt, 32 + n, s2, g), qf[s2], s1, 0, 0, 0);
+    }
+    const unsigned long long bits = tmask[p];
+    const int tail = k1 - t0;
+    float tS = NEG, tU = NEG;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int ka = c_key(0, r, g), kb = c_key(1, r, g);
+      if (ka < tail) {
+        if ((bits >> ka) & 1ull) tS = fmaxf(tS, s0[r]);
+        else tU = fmaxf(tU, s0[r]);
+      }
+      if (kb < tail) {
+        if ((bits >> kb) & 1ull) tS = fmaxf(tS, s1[r]);
+        else tU = fmaxf(tU, s1[r]);
+      }
+    }
+    tS = fmaxf(tS, __shfl_xor(tS, 32));
+    tU = fmaxf(tU, __shfl_xor(tU, 32));
+    if (__ballot(tS > mS + slack)) {
+      const float nm = fmaxf(mS, tS);
+      const float al = nm == NEG ? 1.f : __builtin_amdgcn_exp2f((mS - nm) * c2);
+      mS = nm;
+      zS *= al;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) oS[db] *= al;
+    }
+    if (__ballot(tU > mU + slack)) {
+      const float nm = fmaxf(mU, tU);
+      const float al = nm == NEG ? 1.f : __builtin_amdgcn_exp2f((mU - nm) * c2);
+      mU = nm;
+      zU *= al;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) oU[db] *= al;
+    }
+    const float mcS = mS * c2, mcU = mU * c2;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int ka = c_key(0, r, g), kb = c_key(1, r, g);
+      const bool ia = (bits >> ka) & 1ull, ib = (bits >> kb) & 1ull;
+      const float ea = ka < tail ? __builtin_amdgcn_exp2f(__builtin_fmaf(s0[r], c2, ia ? -mcS : -mcU)) : 0.f;
+      const float eb = kb < tail ? __builtin_amdgcn_exp2f(__builtin_fmaf(s1[r], c2, ib ? -mcS : -mcU)) : 0.f;
+      s0[r] = ea;
+      s1[r] = eb;
+      zS += ia ? ea : 0.f;
+      zU += ia ? 0.f : ea;
+      zS += ib ? eb : 0.f;
+      zU += ib ? 0.f : eb;
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      f16x8_t sh, sl, uh, ul;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int r = 8 * (u & 1) + j;
+        const int kk = c_key(u >> 1, r, g);
+        const float e = (u >> 1) ? s1[r] : s0[r];
+        const _Float16 eh = static_cast<_Float16>(e);
+        const _Float16 el = static_cast<_Float16>(e - float(eh));
+        const bool in = (bits >> kk) & 1ull;
+        const _Float16 z16 = static_cast<_Float16>(0.f);
+        sh[j] = in ? eh : z16;
+        sl[j] = in ? el : z16;
+        uh[j] = in ? z16 : eh;
+        ul[j] = in ? z16 : el;
+      }
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) {
+        const f16x8_t vf = v_frag<D>(vt, lane, u, db);
+        oS[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf, sh, oS[db], 0, 0, 0);
+        oS[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf, sl, oS[db], 0, 0, 0);
+        oU[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf, uh, oU[db], 0, 0, 0);
+        oU[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf, ul, oU[db], 0, 0, 0);
+      }
+    }
+  }
+  zS += __shfl_xor(zS, 32);
+  zU += __shfl_xor(zU, 32);
+  if (p >= m) return;
+  const long long rec = ((long long)h * kChunks + chunk) * m + p;
+  if (g == 0) {
+    float* ps = part_s + rec * 4;
+    ps[0] = mS == NEG ? NEG : mS * c2;
+    ps[1] = mU == NEG ? NEG : mU * c2;
+    ps[2] = zS;
+    ps[3] = zU;
+  }
+  const float vs = __builtin_ldexpf(1.f, v_shift[h]);
+  float* pn = part_n + rec * 2 * D;
+#pragma unroll
+  for (int db = 0; db < NDB; ++db)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int dd = 32 * db + 8 * (r >> 2) + 4 * g + (r & 3);
+      pn[dd] = oS[db][r] * vs;
+      pn[D + dd] = oU[db][r] * vs;
+    }
+}
+
+// ---------------------------------------------------------------------------
 // merge chunks (fp64): O_dense, O_sp and R at every probe
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void merge_kernel(const float* __restrict__ part_s,
+__global__ __launch_bounds__(128) void merge_kernel(const float* __restrict__ part_s,
                                                    const float* __restrict__ part_n, int m,
                                                    int me, int d, float* __restrict__ o_dense,
                                                    float* __restrict__ o_sparse,
                                                    double* __restrict__ xp,
                                                    double* __restrict__ rp) {
-  const int h = blockIdx.x;
-  for (int e = threadIdx.x; e < me * d; e += 256) {
-    const int p = e / d, j = e % d;
-    double MS = -__builtin_huge_val(), MU = -__builtin_huge_val();
-    for (int c = 0; c < kChunks; ++c) {
+  const int p = blockIdx.x, h = blockIdx.y, tid = threadIdx.x;
+  if (p >= me) return;
+  __shared__ double fS[kChunks], fU[kChunks];
+  __shared__ double sh[4];  // MS, MU, zS, zU
+  const float NEGF = -__builtin_huge_valf();
+  if (tid < 64) {
+    // running maxima and partition sums over the chunks (one wave)
+    double ms = -__builtin_huge_val(), mu = -__builtin_huge_val();
+    for (int c = tid; c < kChunks; c += 64) {
       const float* ps = part_s + (((long long)h * kChunks + c) * m + p) * 4;
-      MS = fmax(MS, double(ps[0]));
-      MU = fmax(MU, double(ps[1]));
+      ms = fmax(ms, double(ps[0]));
+      mu = fmax(mu, double(ps[1]));
     }
-    double zS = 0, zU = 0, nS = 0, nU = 0;
+    ms = wave_max(ms);
+    mu = wave_max(mu);
+    double zs = 0.0, zu = 0.0;
+    for (int c = tid; c < kChunks; c += 64) {
+      const float* ps = part_s + (((long long)h * kChunks + c) * m + p) * 4;
+      const double a = ps[0] == NEGF ? 0.0 : exp2(double(ps[0]) - ms);
+      const double b = ps[1] == NEGF ? 0.0 : exp2(double(ps[1]) - mu);
+      fS[c] = a;
+      fU[c] = b;
+      zs += a * ps[2];
+      zu += b * ps[3];
+    }
+    zs = wave_sum(zs);
+    zu = wave_sum(zu);
+    if (tid == 0) {
+      sh[0] = ms;
+      sh[1] = mu;
+      sh[2] = zs;
+      sh[3] = zu;
+    }
+  }
+  __syncthreads();
+  const double MS = sh[0], MU = sh[1], zS = sh[2], zU = sh[3];
+  // common reference for the dense row
+  const double M = fmax(MS, MU);
+  const double wS = MS == -__builtin_huge_val() ? 0.0 : exp2(MS - M);
+  const double wU = MU == -__builtin_huge_val() ? 0.0 : exp2(MU - M);
+  const double Z = zS * wS + zU * wU;
+  for (int j = tid; j < d; j += 128) {
+    double nS = 0, nU = 0;
     for (int c = 0; c < kChunks; ++c) {
-      const long long rec = ((long long)h * kChunks + c) * m + p;
-      const float* ps = part_s + rec * 4;
-      const float* pn = part_n + rec * 2 * d;
-      const double fS = ps[0] == -__builtin_huge_valf() ? 0.0 : exp2(double(ps[0]) - MS);
-      const double fU = ps[1] == -__builtin_huge_valf() ? 0.0 : exp2(double(ps[1]) - MU);
-      zS += fS * ps[2];
-      zU += fU * ps[3];
-      nS += fS * pn[j];
-      nU += fU * pn[d + j];
+      const float* pn = part_n + (((long long)h * kChunks + c) * m + p) * 2 * d;
+      nS += fS[c] * pn[j];
+      nU += fU[c] * pn[d + j];
     }
-    // common max for the dense row
-    const double M = fmax(MS, MU);
-    const double wS = MS == -__builtin_huge_val() ? 0.0 : exp2(MS - M);
-    const double wU = MU == -__builtin_huge_val() ? 0.0 : exp2(MU - M);
-    const double Z = zS * wS + zU * wU;
     const double x = nS / zS;
     const double od = (nS * wS + nU * wU) / Z;
     const double r = wU * (zS * nU - zU * nS) / (Z * zS);
@@ -406,11 +632,13 @@ __global__ __launch_bounds__(256) void fit_kernel(FitArgs f) {
   __shared__ double E[kMaxM * kLd];   // Rw Rw^T, diagonalised in place
   __shared__ double U[kMaxM * kLd];   // eigenvectors (columns)
   __shared__ double rc[kMaxM / 2], rs[kMaxM / 2];
+  __shared__ int32_t pr_p[kMaxM / 2], pr_q[kMaxM / 2];
+  __shared__ double xs[kMaxM][33], rs2[kMaxM][33];   // column chunk staging
   __shared__ int32_t order[kMaxM];
   __shared__ double red[4];
   __shared__ double tcol[kMaxM];
   __shared__ int32_t sh_k;
-  __shared__ int32_t sh_stop;
+  __shared__ int32_t sh_rot;
 
   const double* X = f.xp + (long long)h * f.m * d;
   const double* R = f.rp + (long long)h * f.m * d;
@@ -453,106 +681,116 @@ __global__ __launch_bounds__(256) void fit_kernel(FitArgs f) {
     Rw[e] = sq * (R[e] - mur[j]);
   }
   __syncthreads();
-  // 4. Gram matrices
+  // 4. Gram matrices G = Xw Xw^T + lam I and E = Rw Rw^T, 32 columns of the
+  // weighted features / residuals staged in LDS at a time
   for (int e = tid; e < me * me; e += 256) {
-    const int p = e / me, qq = e % me;
-    if (qq > p) continue;
-    double gx = 0, gr = 0;
-    for (int j = 0; j < d; ++j) {
-      gx = fma(Xw[p * d + j], Xw[qq * d + j], gx);
-      gr = fma(Rw[p * d + j], Rw[qq * d + j], gr);
+    const int pp = e / me, qq = e - (e / me) * me;
+    G[pp * kLd + qq] = pp == qq ? f.lambda : 0.0;
+    E[pp * kLd + qq] = 0.0;
+    U[pp * kLd + qq] = pp == qq ? 1.0 : 0.0;
+  }
+  for (int d0 = 0; d0 < d; d0 += 32) {
+    __syncthreads();
+    for (int e = tid; e < me * 32; e += 256) {
+      const int pp = e >> 5, jj = e & 31;
+      xs[pp][jj] = Xw[pp * d + d0 + jj];
+      rs2[pp][jj] = Rw[pp * d + d0 + jj];
     }
-    if (p == qq) gx += f.lambda;
-    G[p * kLd + qq] = gx;
-    G[qq * kLd + p] = gx;
-    E[p * kLd + qq] = gr;
-    E[qq * kLd + p] = gr;
-    U[p * kLd + qq] = p == qq ? 1.0 : 0.0;
-    U[qq * kLd + p] = p == qq ? 1.0 : 0.0;
+    __syncthreads();
+    for (int e = tid; e < me * me; e += 256) {
+      const int pp = e / me, qq = e - (e / me) * me;
+      double gx = 0.0, gr = 0.0;
+#pragma unroll 8
+      for (int jj = 0; jj < 32; ++jj) {
+        gx = fma(xs[pp][jj], xs[qq][jj], gx);
+        gr = fma(rs2[pp][jj], rs2[qq][jj], gr);
+      }
+      G[pp * kLd + qq] += gx;
+      E[pp * kLd + qq] += gr;
+    }
   }
   __syncthreads();
-  // 5. Cholesky G = L L^T (right-looking, lower triangle)
+  // 5. Cholesky G = L L^T (right-looking, lower triangle); thread t updates
+  // rows i = k+1+t/4 (+64) and columns j = k+1+t%4 (+4)
   for (int k = 0; k < me; ++k) {
-    if (tid == 0) G[k * kLd + k] = sqrt(G[k * kLd + k]);
+    const double piv = sqrt(G[k * kLd + k]);
     __syncthreads();
-    const double piv = G[k * kLd + k];
     for (int i = k + 1 + tid; i < me; i += 256) G[i * kLd + k] /= piv;
+    if (tid == 0) G[k * kLd + k] = piv;
     __syncthreads();
-    const int rem = me - k - 1;
-    for (int e = tid; e < rem * rem; e += 256) {
-      const int i = k + 1 + e / rem, j = k + 1 + e % rem;
-      if (j <= i) G[i * kLd + j] -= G[i * kLd + k] * G[j * kLd + k];
+    for (int i = k + 1 + (tid >> 2); i < me; i += 64) {
+      const double lik = G[i * kLd + k];
+      for (int j = k + 1 + (tid & 3); j <= i; j += 4) G[i * kLd + j] -= lik * G[j * kLd + k];
     }
-    __syncthreads();
   }
-  // 6. cyclic Jacobi on E (round-robin pairs, disjoint rotations per round)
-  const int mp = (me + 1) & ~1;   // even player count; player me is a dummy if me is odd
-  const int npair = mp / 2;
-  for (int sweep = 0; sweep < 40; ++sweep) {
-    for (int rnd = 0; rnd < mp - 1; ++rnd) {
-      if (tid < npair) {
-        int pp, qq;
-        if (tid == 0) { pp = mp - 1; qq = rnd; }
-        else { pp = (rnd + tid) % (mp - 1); qq = (rnd - tid + (mp - 1)) % (mp - 1); }
-        double c = 1.0, s = 0.0;
-        if (pp < me && qq < me) {
-          const double apq = E[pp * kLd + qq];
-          if (apq != 0.0) {
-            const double app = E[pp * kLd + pp], aqq = E[qq * kLd + qq];
-            const double tau = (aqq - app) / (2.0 * apq);
-            const double t = (tau >= 0 ? 1.0 : -1.0) / (fabs(tau) + sqrt(1.0 + tau * tau));
-            c = 1.0 / sqrt(1.0 + t * t);
-            s = t * c;
+  __syncthreads();
+  // 6. cyclic Jacobi on E with round-robin disjoint pairs (pair table per
+  // round in LDS; thread t works on pair t/8, columns t%8 + 8l).  A rotation
+  // is skipped when |a_pq| is negligible next to the diagonal and next to the
+  // trace (the Gram route resolves eigenvalues to ~1e-16 of the trace); the
+  // iteration stops after a sweep without rotations.
+  {
+    double trp = 0.0;
+    for (int i = tid; i < me; i += 256) trp += fabs(E[i * kLd + i]);
+    const double tr = block_sum(trp, red);
+    const double abs_floor = 1e-300 + 1e-14 * tr;
+    const int mp = (me + 1) & ~1;   // even player count; player me is a dummy if me is odd
+    const int npair = mp / 2;
+    const int pi = tid >> 3, cj = tid & 7;
+    for (int sweep = 0; sweep < 20; ++sweep) {
+      if (tid == 0) sh_rot = 0;
+      for (int rnd = 0; rnd < mp - 1; ++rnd) {
+        if (tid < npair) {
+          int pp, qq;
+          if (tid == 0) { pp = mp - 1; qq = rnd; }
+          else {
+            pp = rnd + tid; pp -= pp >= mp - 1 ? mp - 1 : 0;
+            qq = rnd - tid; qq += qq < 0 ? mp - 1 : 0;
           }
+          double c = 1.0, sn = 0.0;
+          if (pp < me && qq < me) {
+            const double apq = E[pp * kLd + qq];
+            const double app = E[pp * kLd + pp], aqq = E[qq * kLd + qq];
+            if (fabs(apq) > 1e-15 * sqrt(fabs(app * aqq)) && fabs(apq) > abs_floor) {
+              const double tau = (aqq - app) / (2.0 * apq);
+              const double t = (tau >= 0 ? 1.0 : -1.0) / (fabs(tau) + sqrt(1.0 + tau * tau));
+              c = 1.0 / sqrt(1.0 + t * t);
+              sn = t * c;
+              sh_rot = 1;
+            }
+          }
+          rc[tid] = c;
+          rs[tid] = sn;
+          pr_p[tid] = pp;
+          pr_q[tid] = qq;
         }
-        rc[tid] = c;
-        rs[tid] = s;
+        __syncthreads();
+        const bool act = pi < npair && rs[pi] != 0.0;
+        const double ci = act ? rc[pi] : 1.0, si = act ? rs[pi] : 0.0;
+        const int p2 = act ? pr_p[pi] : 0, q2 = act ? pr_q[pi] : 0;
+        if (act)   // rows: E <- J^T E
+          for (int j = cj; j < me; j += 8) {
+            const double x1 = E[p2 * kLd + j], x2 = E[q2 * kLd + j];
+            E[p2 * kLd + j] = ci * x1 - si * x2;
+            E[q2 * kLd + j] = si * x1 + ci * x2;
+          }
+        __syncthreads();
+        if (act)   // columns: E <- E J, U <- U J
+          for (int j = cj; j < me; j += 8) {
+            const double x1 = E[j * kLd + p2], x2 = E[j * kLd + q2];
+            E[j * kLd + p2] = ci * x1 - si * x2;
+            E[j * kLd + q2] = si * x1 + ci * x2;
+            const double u1 = U[j * kLd + p2], u2 = U[j * kLd + q2];
+            U[j * kLd + p2] = ci * u1 - si * u2;
+            U[j * kLd + q2] = si * u1 + ci * u2;
+          }
+        __syncthreads();
       }
-      __syncthreads();
-      // rows: E <- J^T E
-      for (int e = tid; e < npair * me; e += 256) {
-        const int i = e / me, j = e % me;
-        int pp, qq;
-        if (i == 0) { pp = mp - 1; qq = rnd; }
-        else { pp = (rnd + i) % (mp - 1); qq = (rnd - i + (mp - 1)) % (mp - 1); }
-        if (pp >= me || qq >= me) continue;
-        const double c = rc[i], s = rs[i];
-        const double xp_ = E[pp * kLd + j], xq = E[qq * kLd + j];
-        E[pp * kLd + j] = c * xp_ - s * xq;
-        E[qq * kLd + j] = s * xp_ + c * xq;
-      }
-      __syncthreads();
-      // columns: E <- E J, U <- U J
-      for (int e = tid; e < npair * me; e += 256) {
-        const int i = e / me, j = e % me;
-        int pp, qq;
-        if (i == 0) { pp = mp - 1; qq = rnd; }
-        else { pp = (rnd + i) % (mp - 1); qq = (rnd - i + (mp - 1)) % (mp - 1); }
-        if (pp >= me || qq >= me) continue;
-        const double c = rc[i], s = rs[i];
-        const double xp_ = E[j * kLd + pp], xq = E[j * kLd + qq];
-        E[j * kLd + pp] = c * xp_ - s * xq;
-        E[j * kLd + qq] = s * xp_ + c * xq;
-        const double up = U[j * kLd + pp], uq = U[j * kLd + qq];
-        U[j * kLd + pp] = c * up - s * uq;
-        U[j * kLd + qq] = s * up + c * uq;
-      }
+      if (!sh_rot) break;
       __syncthreads();
     }
-    // convergence: off-diagonal mass relative to the diagonal
-    double off = 0.0, dg = 0.0;
-    for (int e = tid; e < me * me; e += 256) {
-      const int i = e / me, j = e % me;
-      const double v = E[i * kLd + j];
-      if (i == j) dg += v * v;
-      else off += v * v;
-    }
-    const double OFF = block_sum(off, red);
-    const double DG = block_sum(dg, red);
-    if (tid == 0) sh_stop = (OFF <= 1e-30 * DG) || DG == 0.0;
-    __syncthreads();
-    if (sh_stop) break;
   }
+  __syncthreads();
   // 7. order eigenvalues (descending, ties by index), decide kept directions
   if (tid < me) {
     const double li = E[tid * kLd + tid];
@@ -735,11 +973,11 @@ extern "C" int32_t sparsepr_probe_fit(const sparsepr_dims* dims, int32_t m, int3
     auto* kk = static_cast<const uint16_t*>(k_g);
     auto* vv = static_cast<const uint16_t*>(v_g);
     if (d == 128)
-      probe_rows_kernel<uint16_t, 128><<<dim3(kChunks, H), 256, 0, stream>>>(
+      probe_rows_mfma_kernel<128><<<dim3(kChunks, H), 128, 0, stream>>>(
           qq, kk, vv, v_shift, offsets_kv, cell_rowptr, cell_col, probe_rows, w.group, dims->n_q,
           dims->n_k, dims->c_q, dims->c_k, m, sl2, w.part_s, w.part_n);
     else
-      probe_rows_kernel<uint16_t, 64><<<dim3(kChunks, H), 256, 0, stream>>>(
+      probe_rows_mfma_kernel<64><<<dim3(kChunks, H), 128, 0, stream>>>(
           qq, kk, vv, v_shift, offsets_kv, cell_rowptr, cell_col, probe_rows, w.group, dims->n_q,
           dims->n_k, dims->c_q, dims->c_k, m, sl2, w.part_s, w.part_n);
   } else {
@@ -760,8 +998,8 @@ extern "C" int32_t sparsepr_probe_fit(const sparsepr_dims* dims, int32_t m, int3
           dims->n_k, dims->c_q, dims->c_k, m, sl2, w.part_s, w.part_n);
   }
   SPR_LAUNCH_CHECK();
-  merge_kernel<<<H, 256, 0, stream>>>(w.part_s, w.part_n, m, me, d, o_probe_dense, o_probe_sparse,
-                                      w.xp, w.rp);
+  merge_kernel<<<dim3(me, H), 128, 0, stream>>>(w.part_s, w.part_n, m, me, d, o_probe_dense,
+                                                o_probe_sparse, w.xp, w.rp);
   SPR_LAUNCH_CHECK();
   FitArgs fa;
   fa.off_q = offsets_q;
