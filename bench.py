@@ -101,6 +101,10 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--rho", default=None, help="override the executed-density target")
+    ap.add_argument("--dense-own", action="store_true",
+                    help="also time this library in dense mode (one group, every cell)")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MB",
+                    help="only run a plain device copy of MB megabytes (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the SparsePR call shards by head with no "
@@ -115,6 +119,16 @@ def main():
 
     import free_block_sparse_major_amd as fb
     import synthgen as sg
+
+    if args.copy_calibration:
+        nbytes = args.copy_calibration << 20
+        src = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_read": nbytes, "copy_bytes_written": nbytes, "copies": 5}))
+        return
 
     w = sg.workload(args.workload)
     if args.rho:
@@ -231,6 +245,26 @@ def main():
         out["dense_sdpa_ms"] = round(dense_ms, 3)
         out["speedup_vs_dense_sdpa"] = round(dense_ms / ms_call, 3)
         del qq, kk, vv
+    if args.dense_own:
+        # this library with one query group, one K/V group and every cell kept
+        zq = torch.zeros_like(lq)
+        dcall = fb.SparsePRCall(w.heads, w.n, w.n, w.head_dim, dtype, 1, 1, m=w.m, rank=w.r,
+                                lam=w.lam, budget=w.n * w.n,
+                                out_dtype=fb.BF16 if w.dtype == "bf16" else fb.F32)
+        dcall.layout(zq, zq, q, k, v)
+        dcall.route()
+        dcall.attend()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(3):
+            dcall.attend()
+        e1.record()
+        torch.cuda.synchronize()
+        own_ms = e0.elapsed_time(e1) / 3
+        out["dense_own_attn_ms"] = round(own_ms, 3)
+        out["dense_own_tflops"] = round(4.0 * d * H * n * n / (own_ms * 1e-3) / 1e12, 1)
+        del dcall
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, arr)
         out["cpu_baseline"]["value"] = round(out["cpu_baseline"]["value"], 1)
