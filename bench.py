@@ -29,6 +29,21 @@ PROFILE_PMC = os.path.join(ROOT, "profiles", "attn_bf16_kernel_wan_pmc.txt")
 KERNEL_SRC = os.path.join(ROOT, "free_block_sparse_major_amd", "csrc", "attn.hip")
 
 
+
+def _item_waves(heads, n_q, c_q):
+    """Waves per work item the attention launch picks for bf16 inputs (the
+    library's rule: 4 below 1024 query groups, else the best busy-wave share
+    for the mean group size in {4, 8, 12}, largest on ties)."""
+    if heads * c_q < 1024:
+        return 4
+    q = -(-n_q // (32 * c_q))
+    best, best_eff = 4, 0.0
+    for w in (4, 8, 12):
+        eff = q / (w * -(-q // w))
+        if eff >= best_eff - 1e-12:
+            best, best_eff = w, eff
+    return best
+
 def _src_hash(path):
     with open(path, "rb") as f:
         return hashlib.sha256(f.read()).hexdigest()[:16]
@@ -223,7 +238,8 @@ def main():
     traffic = _traffic_from_profile(w.name)
     out["roofline"] = {
         "bound": "mfma" if w.dtype == "bf16" else "alu",
-        "kernel": "attn_bf16_kernel<%d>" % d if w.dtype == "bf16" else "attn_f32_kernel<%d>" % d,
+        "kernel": ("attn_bf16_kernel<%d, %d>" % (d, _item_waves(w.heads, w.n, w.c_q))
+                   if w.dtype == "bf16" else "attn_f32_kernel<%d>" % d),
         "achieved": round(attn_tflops, 2),
         "peak": peak,
         "unit": "TFLOP/s",

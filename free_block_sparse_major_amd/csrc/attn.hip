@@ -106,18 +106,20 @@ SPR_DEV bool locate_item(const AttnArgs& p, int& h, int& a, int& kt) {
 
 // Loads the cell list of (h, a) into LDS: cstart = first K/V row of each
 // selected cell, cpos = exclusive prefix of the cell lengths; returns the
-// stream length L.  256 threads, <= 1024 cells.
+// stream length L.  NT threads, <= 1024 cells.
+template <int NT>
 SPR_DEV int load_cells(const AttnArgs& p, int h, int a, int32_t* cstart, int32_t* cpos,
                        long long* red) {
+  constexpr int PER = (SPARSEPR_MAX_GROUPS + NT - 1) / NT;
   const int32_t* rp = p.rowptr + (long long)h * (p.c_q + 1);
   const int c0 = rp[a], nc = rp[a + 1] - c0;
   const int32_t* cl = p.col + (long long)h * p.c_q * p.c_k + c0;
   const int32_t* ok = p.off_k + (long long)h * (p.c_k + 1);
-  int len[4];
+  int len[PER];
   long long s = 0;
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    int i = 4 * threadIdx.x + j;
+  for (int j = 0; j < PER; ++j) {
+    int i = PER * threadIdx.x + j;
     len[j] = 0;
     if (i < nc) {
       int b = cl[i];
@@ -130,8 +132,8 @@ SPR_DEV int load_cells(const AttnArgs& p, int h, int a, int32_t* cstart, int32_t
   long long tot;
   long long run = block_exclusive_scan(s, red, &tot);
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    int i = 4 * threadIdx.x + j;
+  for (int j = 0; j < PER; ++j) {
+    int i = PER * threadIdx.x + j;
     if (i < nc) cpos[i] = int32_t(run);
     run += len[j];
   }
@@ -167,11 +169,10 @@ SPR_DEV int find_cell(const int32_t* cpos, int nc, int pos) {
 // inside each 16-lane group, source lane r points at 4 values
 // V[k0 + r/4][d0 + 4(r%4) ..+3]; lane i then receives V[k0 + j][d0 + i] for
 // j = 0..3, i.e. 4 consecutive keys of its own column.
-template <int D>
 struct SmemCells {
   int32_t cstart[SPARSEPR_MAX_GROUPS];
   int32_t cpos[SPARSEPR_MAX_GROUPS + 1];
-  long long red[4];
+  long long red[16];
 };
 
 template <int B>
@@ -231,11 +232,14 @@ SPR_DEV uint32_t lds_addr_of(const void* p) {
 // (P then stays below 2^8, well inside fp16)
 constexpr float kRescaleSlack = 8.f;
 
-template <int D>
-__global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs p) {
+template <int D, int W>
+__global__ __launch_bounds__(64 * W, W <= 4 ? 2 : 1) void attn_bf16_kernel(AttnArgs p) {
+  constexpr int NT = 64 * W;          // threads
+  constexpr int ROWS = 32 * W;        // query rows per work item
   constexpr int CPR = D / 8;          // 16-byte chunks per row
   constexpr int RPI = 64 / CPR;       // rows per 1 KB wave load
-  constexpr int NI = 16 / RPI;        // wave loads per tensor per tile (each wave: 16 rows)
+  constexpr int NL = 64 / RPI;        // wave loads per tensor per tile
+  constexpr int NI = (NL + W - 1) / W;  // wave loads per tensor per tile and wave (at most)
   constexpr int NS = D / 16;          // k-steps of QK^T
   constexpr int NDB = D / 32;         // 32-wide d blocks of the output
   constexpr int RB = D * 2;           // row bytes (bf16 K, fp16 V)
@@ -243,20 +247,23 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs p) {
   // stage never alias reads of the other (no blanket wait before LDS reads)
   __shared__ uint4 k_s0[8 * D], k_s1[8 * D];   // 64 rows x D bf16
   __shared__ uint4 v_s0[8 * D], v_s1[8 * D];   // 64 rows x D fp16
-  __shared__ SmemCells<D> sm;
+  __shared__ SmemCells sm;
 
   int h, a, kt;
   if (!locate_item(p, h, a, kt)) return;
-  const int tid = threadIdx.x, wid = tid >> 6, lane = tid & 63, n = lane & 31, g = lane >> 5;
+  // wave index as a scalar: everything derived from it (LDS destinations of the
+  // tile loads, row ranges) stays in SGPRs
+  const int tid = threadIdx.x, wid = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63,
+            n = lane & 31, g = lane >> 5;
   const int32_t* oq = p.off_q + (long long)h * (p.c_q + 1);
-  const int r0 = oq[a] + kt * 128;
-  const int nrows = min(128, oq[a + 1] - r0);
-  const int L = load_cells(p, h, a, sm.cstart, sm.cpos, sm.red);
+  const int r0 = oq[a] + kt * ROWS;
+  const int nrows = min(ROWS, oq[a + 1] - r0);
+  const int L = load_cells<NT>(p, h, a, sm.cstart, sm.cpos, sm.red);
   const int ntiles = (L + 63) / 64;
   // cell table -> (next boundary, row delta): row(pos) = pos + delta of its cell
   const int nc = p.rowptr[(long long)h * (p.c_q + 1) + a + 1] -
                  p.rowptr[(long long)h * (p.c_q + 1) + a];
-  for (int i = tid; i < nc; i += 256) sm.cstart[i] -= sm.cpos[i];
+  for (int i = tid; i < nc; i += NT) sm.cstart[i] -= sm.cpos[i];
   __syncthreads();
 
   const uint32_t head_bytes = uint32_t(p.n_k) * RB;
@@ -285,35 +292,35 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs p) {
   // loop would wait on the whole vector-memory queue, tile prefetch included
   __builtin_amdgcn_s_waitcnt(0x0F70);
 
-  // loader: wave w fills tile rows 16w .. 16w+15; load i covers RPI rows.
-  // Per load a cursor (cell index, its end position, its row delta).
-  int cur_c[NI], cur_end[NI], cur_dl[NI];
-#pragma unroll
-  for (int i = 0; i < NI; ++i) {
-    cur_c[i] = 0;
-    cur_end[i] = sm.cpos[1];
-    cur_dl[i] = sm.cstart[0];
-  }
-  const int lrow = lane / CPR, lpc = lane % CPR;
+  // loader: wave load i of wave w covers tile rows RPI*(w + i*W) .. +RPI.
+  // tc (wave-uniform) is the cell holding the tile's first stream position;
+  // each lane walks forward from it to the cell of its own row (a tile spans
+  // few cells), so no per-lane cursor state is carried between tiles.
+  int tc = 0;
   auto issue_tile = [&](auto stage, int t) {
     constexpr int B = decltype(stage)::value;
     uint4* kbase = B == 0 ? k_s0 : k_s1;
     uint4* vbase = B == 0 ? v_s0 : v_s1;
+    while (sm.cpos[tc + 1] <= t * 64) ++tc;
+    tc = __builtin_amdgcn_readfirstlane(tc);
+    // lane-derived terms recomputed per issue rather than held across the loop
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
+    const int lrow = ln / CPR, lpc = ln % CPR;
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
-      const int row = 16 * wid + i * RPI + lrow;          // tile row of this lane
+      const int blk = wid + i * W;                        // wave-uniform
+      if (NL % W != 0 && blk >= NL) break;
+      const int row = blk * RPI + lrow;                   // tile row of this lane
       int pos = t * 64 + row;
       pos = pos < L ? pos : L - 1;                        // tail rows: any valid row
-      while (pos >= cur_end[i]) {
-        ++cur_c[i];
-        cur_end[i] = sm.cpos[cur_c[i] + 1];
-        cur_dl[i] = sm.cstart[cur_c[i]];
-      }
-      const uint32_t roff = uint32_t(pos + cur_dl[i]) * RB;
+      int c = tc;
+      while (pos >= sm.cpos[c + 1]) ++c;
+      const uint32_t roff = uint32_t(pos + sm.cstart[c]) * RB;
       const int kc = lpc ^ (row & (CPR - 1));
       const int vc = lpc ^ swz_v<D>(row);
-      uint4* kdst = kbase + (16 * wid + i * RPI) * CPR;
-      uint4* vdst = vbase + (16 * wid + i * RPI) * CPR;
+      uint4* kdst = kbase + blk * RPI * CPR;
+      uint4* vdst = vbase + blk * RPI * CPR;
       lds_dma16(krs, __builtin_amdgcn_readfirstlane(lds_addr_of(kdst)), roff + kc * 16);
       lds_dma16(vrs, __builtin_amdgcn_readfirstlane(lds_addr_of(vdst)), roff + vc * 16);
     }
@@ -414,6 +421,83 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs p) {
     }
   };
 
+  // Register-lean variant for large items: the 64-key tile is processed as
+  // two 32-key halves (one score block, half the P fragments live at once).
+  auto compute_half = [&](const uint4* kb_, const uint4* vb, int kbi, int tail) {
+    f32x16_t sacc = f32x16_t{};
+    // swizzle term recomputed per use (an opaque copy keeps the compiler from
+    // hoisting one address register per k-step out of the tile loop)
+    int sw = n & (CPR - 1);
+    asm volatile("" : "+v"(sw));
+    const uint4* krow = kb_ + (32 * kbi + n) * CPR;
+    bf16x8_t a0 = __builtin_bit_cast(bf16x8_t, krow[g ^ sw]);
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      bf16x8_t n0 = a0;
+      if (s + 1 < NS)
+        n0 = __builtin_bit_cast(bf16x8_t, krow[(2 * s + 2 + g) ^ sw]);
+      sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qf[s], sacc, 0, 0, 0);
+      a0 = n0;
+    }
+    if (tail < 32 * kbi + 32) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i)
+        if (32 * kbi + 8 * (i >> 2) + 4 * g + (i & 3) >= tail) sacc[i] = -__builtin_huge_valf();
+    }
+    float mloc = -__builtin_huge_valf();
+#pragma unroll
+    for (int i = 0; i < 16; ++i) mloc = fmaxf(mloc, sacc[i]);
+    mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
+    if (__ballot(mloc > m_run + slack)) {
+      const float m_new = fmaxf(m_run, mloc);
+      const float alpha = __builtin_amdgcn_exp2f((m_run - m_new) * c2);
+      m_run = m_new;
+      l_run *= alpha;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) oacc[db] *= alpha;
+    }
+    const float mc = m_run * c2;
+    f16x8_t pf[2];
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+      pf[i >> 3][i & 7] = static_cast<_Float16>(
+          __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[i], c2, -mc)));
+    float lsum = 0.f;
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int j = 0; j < 8; j += 2)
+        lsum = __builtin_amdgcn_fdot2(f16x2_t{pf[u][j], pf[u][j + 1]}, ones, lsum, false);
+    l_run += lsum;
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) {
+        const int row1 = 32 * kbi + 16 * u + 4 * gg + (gi >> 2);
+        const int row2 = row1 + 8;
+        const int ch = 4 * db + 2 * (G & 1) + ((gi & 3) >> 1);
+        const int hb = (gi & 1) * 8;
+        const char* b1 = reinterpret_cast<const char*>(vb + row1 * CPR + (ch ^ swz_v<D>(row1))) + hb;
+        const char* b2 = reinterpret_cast<const char*>(vb + row2 * CPR + (ch ^ swz_v<D>(row2))) + hb;
+        const v4i16_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)b1);
+        const v4i16_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)b2);
+        const f16x8_t af = __builtin_bit_cast(
+            f16x8_t, (short __attribute__((ext_vector_type(8)))){lo[0], lo[1], lo[2], lo[3],
+                                                                  hi[0], hi[1], hi[2], hi[3]});
+        oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af, pf[u], oacc[db], 0, 0, 0);
+      }
+    }
+  };
+  auto compute_lean = [&](auto stage, int t) {
+    constexpr int B = decltype(stage)::value;
+    const uint4* kb_ = B == 0 ? k_s0 : k_s1;
+    const uint4* vb = B == 0 ? v_s0 : v_s1;
+    const int tail = L - t * 64;
+    compute_half(kb_, vb, 0, tail);
+    if (t + 1 < ntiles) issue_tile(Stage<1 - B>{}, t + 1);
+    if (tail > 32) compute_half(kb_, vb, 1, tail);
+  };
+
   // Two-stage pipeline with one barrier per tile: after the barrier of step
   // t every wave has finished tile t-1, so the stage it used is refilled with
   // tile t+1 (issued from inside compute, behind the QK^T MFMAs) while tile t
@@ -422,8 +506,12 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs p) {
   auto step = [&](auto stage, int t) {
     constexpr int B = decltype(stage)::value;
     asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-    if (wave_active) compute(stage, t);
-    else if (t + 1 < ntiles) issue_tile(Stage<1 - B>{}, t + 1);
+    if (wave_active) {
+      if constexpr (W >= 12) compute_lean(stage, t);
+      else compute(stage, t);
+    } else if (t + 1 < ntiles) {
+      issue_tile(Stage<1 - B>{}, t + 1);
+    }
   };
   if (ntiles > 0) issue_tile(Stage<0>{}, 0);
   for (int t = 0; t < ntiles; t += 2) {
@@ -472,7 +560,7 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(AttnArgs p) {
   const int nrows = min(TQ, oq[a + 1] - r0);
   const int nc = p.rowptr[(long long)h * (p.c_q + 1) + a + 1] -
                  p.rowptr[(long long)h * (p.c_q + 1) + a];
-  const int L = load_cells(p, h, a, sm.cstart, sm.cpos, sm.red);
+  const int L = load_cells<256>(p, h, a, sm.cstart, sm.cpos, sm.red);
   const float* Kh = static_cast<const float*>(p.k) + (long long)h * p.n_k * D;
   const float* Vh = static_cast<const float*>(p.v) + (long long)h * p.n_k * D;
   const int qi = tid / LPQ, sl = tid % LPQ;
@@ -540,9 +628,41 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(AttnArgs p) {
   if (sl == 0 && p.lse) p.lse[(long long)h * p.n_q + r0 + qi] = (m_run + __log2f(l_run)) * kLn2;
 }
 
+// Waves (32 query rows each) per bf16 work item: 4 (two blocks per CU), 8 or
+// 12 (one block per CU).  All waves of an item share every K/V tile it loads,
+// so a larger item streams its group's K/V fewer times, but rows past the
+// group's end leave wave slots idle.  With q = ceil(mean group size / 32)
+// busy waves per group, the choice maximises q / (W * ceil(q / W)) and takes
+// the largest W on ties.  Calls with few groups per CU keep W = 4: there the
+// grid itself is short and more, smaller blocks balance better.
+int bf16_waves(const sparsepr_dims* d) {
+  const long long groups = (long long)d->heads * d->c_q;
+  if (groups < 4LL * 256) return 4;
+  const int q = int((d->n_q + 32LL * d->c_q - 1) / (32LL * d->c_q));
+  int best = 4;
+  double best_eff = 0.0;
+  for (int w : {4, 8, 12}) {
+    const double eff = double(q) / (double(w) * double((q + w - 1) / w));
+    if (eff >= best_eff - 1e-12) {
+      best = w;
+      best_eff = eff;
+    }
+  }
+  return best;
+}
+
 int rows_per_item(const sparsepr_dims* d) {
-  if (d->dtype == SPARSEPR_BF16) return 128;
+  if (d->dtype == SPARSEPR_BF16) return 32 * bf16_waves(d);
   return 256 / (d->head_dim / 32);
+}
+
+template <int D>
+void launch_bf16(const AttnArgs& a, int blocks, int waves, hipStream_t s) {
+  switch (waves) {
+    case 4: attn_bf16_kernel<D, 4><<<blocks, 256, 0, s>>>(a); break;
+    case 8: attn_bf16_kernel<D, 8><<<blocks, 512, 0, s>>>(a); break;
+    default: attn_bf16_kernel<D, 12><<<blocks, 768, 0, s>>>(a); break;
+  }
 }
 
 }  // namespace
@@ -600,8 +720,9 @@ extern "C" int32_t sparsepr_sparse_attn(const sparsepr_dims* dims, const int32_t
   a.scale_log2 = softmax_scale * kLog2e;
   a.grid_blocks = int(bound);
   if (dims->dtype == SPARSEPR_BF16) {
-    if (dims->head_dim == 128) attn_bf16_kernel<128><<<int(bound), 256, 0, stream>>>(a);
-    else attn_bf16_kernel<64><<<int(bound), 256, 0, stream>>>(a);
+    const int w = bf16_waves(dims);
+    if (dims->head_dim == 128) launch_bf16<128>(a, int(bound), w, stream);
+    else launch_bf16<64>(a, int(bound), w, stream);
   } else {
     if (dims->head_dim == 128) attn_f32_kernel<128><<<int(bound), 256, 0, stream>>>(a);
     else attn_f32_kernel<64><<<int(bound), 256, 0, stream>>>(a);

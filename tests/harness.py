@@ -49,12 +49,31 @@ def upload(w, heads_data, layout="hnd"):
     return (q.to(dev), k.to(dev), v.to(dev), lq.to(dev), lk.to(dev))
 
 
+def upload_arrays(w, arr):
+    """Device tensors from packed [H][N][d] arrays (synthgen.make_call_arrays)."""
+    import torch
+    dev = torch.device("cuda")
+    if w.dtype == "bf16":
+        cv = lambda a: torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
+    else:
+        cv = lambda a: torch.from_numpy(a).to(dev)
+    return (cv(arr["q"]), cv(arr["k"]), cv(arr["v"]), torch.from_numpy(arr["labels_q"]).to(dev),
+            torch.from_numpy(arr["labels_kv"]).to(dev))
+
+
 def run_gpu(w, heads_data, budget=None, rank=None, m=None, layout="hnd", out_dtype="f32",
-            overlap=True):
+            overlap=True, tensors=None, fetch_heads=None):
+    """Runs the whole call.  Inputs come from per-head dicts (`heads_data`) or,
+    for large shapes, from already uploaded `tensors` (heads_data is then
+    None).  `fetch_heads` limits the per-head outputs copied back."""
     import torch
     import free_block_sparse_major_amd as fb
-    H = len(heads_data)
-    q, k, v, lq, lk = upload(w, heads_data, layout)
+    if tensors is None:
+        H = len(heads_data)
+        q, k, v, lq, lk = upload(w, heads_data, layout)
+    else:
+        H = w.heads
+        q, k, v, lq, lk = tensors
     d = w.head_dim
     strides = None
     if layout == "nhd":
@@ -71,11 +90,12 @@ def run_gpu(w, heads_data, budget=None, rank=None, m=None, layout="hnd", out_dty
         "cell_rowptr", "cell_col", "routed_pairs", "o_sp", "lse", "probe_rows", "probe_tokens",
         "o_probe_dense", "o_probe_sparse", "corr_a", "corr_psi_t", "corr_c", "out")}
     out = {}
+    sel = (lambda t: t) if fetch_heads is None else (lambda t: t[list(fetch_heads)])
     for key, t in g.items():
         if t.dtype == torch.bfloat16:
             t = t.float()
-        out[key] = t.cpu().numpy()
-    out["q_g"] = call.q_g.float().cpu().numpy() if w.dtype == "bf16" else call.q_g.cpu().numpy()
+        out[key] = sel(t).cpu().numpy()
+    out["q_g"] = sel(call.q_g.float() if w.dtype == "bf16" else call.q_g).cpu().numpy()
     out["budget"] = call.budget
     out["call"] = call
     return out
