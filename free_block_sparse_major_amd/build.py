@@ -19,7 +19,7 @@ OBJDIR = os.path.join(HERE, "_build")
 
 ARCH = "gfx950"
 FLAGS = [
-    f"--offload-arch={ARCH}", "-O3", "-fPIC", "-std=c++17", "-I" + INCLUDE,
+    f"--offload-arch={ARCH}", "-O3", "-fPIC", "-std=c++20", "-I" + INCLUDE,
     # keep the compiler from forming packed fp32 VALU ops
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wno-unused-result",

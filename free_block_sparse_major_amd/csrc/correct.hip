@@ -5,18 +5,15 @@
 // dense output, and the result returns to the original order.  With the
 // folded fit, out = o + (o A) Psi^T + c.
 //
-// HBM-bound: O_sp is read once and the output written once; the
-// 2 * d * rank FMAs per row run from registers with A and Psi broadcast from
-// LDS, loaded once per block of 4 waves x 4 row tiles.
+// HBM-bound: O_sp is read once and the output written once.  One query row
+// per lane, held in registers; the 2 * d * rank FMAs per row take A and Psi
+// as wave-uniform operands (scalar loads of the per-head factors, which every
+// lane shares), so no LDS or cross-lane traffic is needed.
 
 #include "common.h"
 
 namespace spr {
 namespace {
-
-constexpr int kRowsPerTile = 64;     // one row per lane of a wave
-constexpr int kTilesPerWave = 4;
-constexpr int kStagePitch = 36;      // floats per staged row (32 + 4: conflict-free 16B reads)
 
 struct CorrArgs {
   const int32_t* perm_q;
@@ -30,110 +27,79 @@ struct CorrArgs {
   int out_bf16;
 };
 
-// Each wave owns 64-row tiles, one row per lane held in registers.  Rows
-// move between HBM and registers through a per-wave LDS stage in 32-column
-// slices: global accesses stay contiguous within each row, while a lane
-// reads or writes its own row in LDS.  A and Psi are stored k-contiguous
-// ([d][rank]) in LDS and read as broadcasts.  LDS traffic of one wave stays
-// inside that wave, whose LDS operations complete in program order.
 template <int D, int RK>
-__global__ __launch_bounds__(256) void correct_kernel(CorrArgs a) {
-  constexpr int NSL = D / 32;                // 32-column slices
-  const int h = blockIdx.y, tid = threadIdx.x, wid = tid >> 6, lane = tid & 63;
-  __shared__ float4 sA4[D * RK / 4];         // A[i][k]
-  __shared__ float4 sP4[D * RK / 4];         // Psi^T transposed: P[i][k]
-  __shared__ float sc[D];
-  __shared__ float stage[4][kRowsPerTile * kStagePitch];
-  float* sA = reinterpret_cast<float*>(sA4);
-  float* sP = reinterpret_cast<float*>(sP4);
-  const float* Ah = a.corr_a + (long long)h * D * a.rank;
-  const float* Ph = a.corr_psi_t + (long long)h * a.rank * D;
-  for (int e = tid; e < D * RK; e += 256) {
-    const int i = e / RK, k = e % RK;
-    sA[e] = k < a.rank ? Ah[i * a.rank + k] : 0.f;
-    sP[e] = k < a.rank ? Ph[k * D + i] : 0.f;
+__global__ __launch_bounds__(256) void correct_kernel(const int32_t* __restrict__ perm_q,
+                                                      const float* __restrict__ o_sp,
+                                                      const float* __restrict__ corr_a,
+                                                      const float* __restrict__ corr_psi_t,
+                                                      const float* __restrict__ corr_c,
+                                                      void* __restrict__ out, int64_t out_sh,
+                                                      int64_t out_st, int n_q, int rank,
+                                                      int out_bf16) {
+  const int h = blockIdx.y;
+  const int r = blockIdx.x * 256 + threadIdx.x;
+  const bool valid = r < n_q;
+  const float* __restrict__ Ah = corr_a + (long long)h * D * rank;      // [D][rank]
+  const float* __restrict__ Ph = corr_psi_t + (long long)h * rank * D;  // [rank][D]
+  const float* __restrict__ ch = corr_c + (long long)h * D;
+  const float* src = o_sp + ((long long)h * n_q + (valid ? r : 0)) * D;
+  float o[D];
+#pragma unroll
+  for (int c = 0; c < D / 4; ++c) {
+    const float4 v = *reinterpret_cast<const float4*>(src + 4 * c);
+    o[4 * c] = v.x;
+    o[4 * c + 1] = v.y;
+    o[4 * c + 2] = v.z;
+    o[4 * c + 3] = v.w;
   }
-  for (int i = tid; i < D; i += 256) sc[i] = a.corr_c[(long long)h * D + i];
-  __syncthreads();
-  float* st = stage[wid];
-  for (int tt = 0; tt < kTilesPerWave; ++tt) {
-    const int row0 = ((blockIdx.x * 4 + wid) * kTilesPerWave + tt) * kRowsPerTile;
-    if (row0 >= a.n_q) break;
-    const int rows = min(kRowsPerTile, a.n_q - row0);
-    const float* src = a.o_sp + ((long long)h * a.n_q + row0) * D;
-    float o[D];
+  const int tok = valid ? perm_q[(long long)h * n_q + r] : 0;
+  // u = o A: i outer, so each step reads one contiguous row A[i][0 .. RK)
+  float u[RK];
 #pragma unroll
-    for (int sl = 0; sl < NSL; ++sl) {
-      // slice sl of the 64 rows: 8 16-byte chunks per row, contiguous per row
+  for (int k = 0; k < RK; ++k) u[k] = 0.f;
+  if (rank == RK) {
 #pragma unroll
-      for (int it = 0; it < 8; ++it) {
-        const int e = it * 64 + lane, r = e >> 3, c = e & 7;
-        float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-        if (r < rows) v = *reinterpret_cast<const float4*>(src + (long long)r * D + 32 * sl + 4 * c);
-        *reinterpret_cast<float4*>(st + r * kStagePitch + 4 * c) = v;
-      }
+    for (int i = 0; i < D; ++i)
 #pragma unroll
-      for (int c = 0; c < 8; ++c) {
-        const float4 v = *reinterpret_cast<const float4*>(st + lane * kStagePitch + 4 * c);
-        o[32 * sl + 4 * c + 0] = v.x;
-        o[32 * sl + 4 * c + 1] = v.y;
-        o[32 * sl + 4 * c + 2] = v.z;
-        o[32 * sl + 4 * c + 3] = v.w;
-      }
+      for (int k = 0; k < RK; ++k) u[k] = fmaf(o[i], Ah[i * RK + k], u[k]);
+  } else {
+    for (int k = 0; k < rank; ++k) {
+      float acc = 0.f;
+#pragma unroll
+      for (int i = 0; i < D; ++i) acc = fmaf(o[i], Ah[i * rank + k], acc);
+#pragma unroll
+      for (int kk = 0; kk < RK; ++kk)
+        if (kk == k) u[kk] = acc;
     }
-    float u[RK];
+  }
+  // o + c + u Psi^T: k outer, so each step reads one contiguous row Psi^T[k]
 #pragma unroll
-    for (int k = 0; k < RK; ++k) u[k] = 0.f;
-#pragma unroll 4
-    for (int i = 0; i < D; ++i) {
+  for (int i = 0; i < D; ++i) o[i] += ch[i];
 #pragma unroll
-      for (int k4 = 0; k4 < RK / 4; ++k4) {
-        const float4 w = sA4[i * (RK / 4) + k4];
-        u[4 * k4 + 0] = fmaf(o[i], w.x, u[4 * k4 + 0]);
-        u[4 * k4 + 1] = fmaf(o[i], w.y, u[4 * k4 + 1]);
-        u[4 * k4 + 2] = fmaf(o[i], w.z, u[4 * k4 + 2]);
-        u[4 * k4 + 3] = fmaf(o[i], w.w, u[4 * k4 + 3]);
-      }
+  for (int k = 0; k < RK; ++k) {
+    if (k >= rank) break;
+#pragma unroll
+    for (int i = 0; i < D; ++i) o[i] = fmaf(u[k], Ph[k * D + i], o[i]);
+  }
+  if (!valid) return;
+  const long long base = (long long)h * out_sh + (long long)tok * out_st;
+  if (out_bf16) {
+    uint16_t* dst = static_cast<uint16_t*>(out) + base;
+#pragma unroll
+    for (int c = 0; c < D / 8; ++c) {
+      uint4 w;
+      w.x = uint32_t(f32_to_bf16_rne(o[8 * c])) | (uint32_t(f32_to_bf16_rne(o[8 * c + 1])) << 16);
+      w.y = uint32_t(f32_to_bf16_rne(o[8 * c + 2])) | (uint32_t(f32_to_bf16_rne(o[8 * c + 3])) << 16);
+      w.z = uint32_t(f32_to_bf16_rne(o[8 * c + 4])) | (uint32_t(f32_to_bf16_rne(o[8 * c + 5])) << 16);
+      w.w = uint32_t(f32_to_bf16_rne(o[8 * c + 6])) | (uint32_t(f32_to_bf16_rne(o[8 * c + 7])) << 16);
+      *reinterpret_cast<uint4*>(dst + 8 * c) = w;
     }
-#pragma unroll 4
-    for (int i = 0; i < D; ++i) {
-      float v = o[i] + sc[i];
+  } else {
+    float* dst = static_cast<float*>(out) + base;
 #pragma unroll
-      for (int k4 = 0; k4 < RK / 4; ++k4) {
-        const float4 w = sP4[i * (RK / 4) + k4];
-        v = fmaf(u[4 * k4 + 0], w.x, v);
-        v = fmaf(u[4 * k4 + 1], w.y, v);
-        v = fmaf(u[4 * k4 + 2], w.z, v);
-        v = fmaf(u[4 * k4 + 3], w.w, v);
-      }
-      o[i] = v;
-    }
-    // write back in original token order through the stage
-    const int my_tok = lane < rows ? a.perm_q[(long long)h * a.n_q + row0 + lane] : 0;
-#pragma unroll
-    for (int sl = 0; sl < NSL; ++sl) {
-#pragma unroll
-      for (int c = 0; c < 8; ++c)
-        *reinterpret_cast<float4*>(st + lane * kStagePitch + 4 * c) =
-            make_float4(o[32 * sl + 4 * c], o[32 * sl + 4 * c + 1], o[32 * sl + 4 * c + 2],
-                        o[32 * sl + 4 * c + 3]);
-#pragma unroll
-      for (int it = 0; it < 8; ++it) {
-        const int e = it * 64 + lane, r = e >> 3, c = e & 7;
-        const int tok = __shfl(my_tok, r);
-        const float4 v = *reinterpret_cast<const float4*>(st + r * kStagePitch + 4 * c);
-        if (r >= rows) continue;
-        const long long base = (long long)h * a.out_sh + (long long)tok * a.out_st + 32 * sl + 4 * c;
-        if (a.out_bf16) {
-          uint2 w;
-          w.x = uint32_t(f32_to_bf16_rne(v.x)) | (uint32_t(f32_to_bf16_rne(v.y)) << 16);
-          w.y = uint32_t(f32_to_bf16_rne(v.z)) | (uint32_t(f32_to_bf16_rne(v.w)) << 16);
-          *reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.out) + base) = w;
-        } else {
-          *reinterpret_cast<float4*>(static_cast<float*>(a.out) + base) = v;
-        }
-      }
-    }
+    for (int c = 0; c < D / 4; ++c)
+      *reinterpret_cast<float4*>(dst + 4 * c) =
+          make_float4(o[4 * c], o[4 * c + 1], o[4 * c + 2], o[4 * c + 3]);
   }
 }
 
@@ -157,9 +123,13 @@ __global__ __launch_bounds__(256) void probe_overwrite_kernel(const int32_t* __r
 
 template <int D>
 void launch_correct(const CorrArgs& a, dim3 grid, hipStream_t s) {
-  if (a.rank <= 16) correct_kernel<D, 16><<<grid, 256, 0, s>>>(a);
-  else if (a.rank <= 32) correct_kernel<D, 32><<<grid, 256, 0, s>>>(a);
-  else correct_kernel<D, 64><<<grid, 256, 0, s>>>(a);
+#define SPR_CORR(RK)                                                                          \
+  correct_kernel<D, RK><<<grid, 256, 0, s>>>(a.perm_q, a.o_sp, a.corr_a, a.corr_psi_t, a.corr_c, \
+                                             a.out, a.out_sh, a.out_st, a.n_q, a.rank, a.out_bf16)
+  if (a.rank <= 16) SPR_CORR(16);
+  else if (a.rank <= 32) SPR_CORR(32);
+  else SPR_CORR(64);
+#undef SPR_CORR
 }
 
 }  // namespace
@@ -200,8 +170,7 @@ extern "C" int32_t sparsepr_correct(const sparsepr_dims* dims, int32_t m, int32_
   a.n_q = dims->n_q;
   a.rank = rank;
   a.out_bf16 = out_dtype == SPARSEPR_BF16;
-  const int per_block = kRowsPerTile * kTilesPerWave * 4;
-  dim3 grid((dims->n_q + per_block - 1) / per_block, dims->heads);
+  dim3 grid((dims->n_q + 255) / 256, dims->heads);
   if (dims->head_dim == 128) launch_correct<128>(a, grid, stream);
   else launch_correct<64>(a, grid, stream);
   SPR_LAUNCH_CHECK();
