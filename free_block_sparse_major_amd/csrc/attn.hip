@@ -210,7 +210,13 @@ SPR_DEV v4i32_t head_rsrc(const void* base, uint32_t bytes) {
 // not pair it with later LDS reads of the other stage; completion is awaited
 // explicitly (vmcnt) before the barrier that publishes the stage.  M0 (the
 // LDS base) is read at issue and restored afterwards.
-SPR_DEV void lds_dma16(const v4i32_t& rsrc, uint32_t lds_addr, uint32_t voff) {
+SPR_DEV void lds_dma16(const v4i32_t& rsrc_in, uint32_t lds_addr, uint32_t voff) {
+  // the descriptor must sit in SGPRs (it is wave-uniform by construction)
+  v4i32_t rsrc;
+  rsrc[0] = __builtin_amdgcn_readfirstlane(rsrc_in[0]);
+  rsrc[1] = __builtin_amdgcn_readfirstlane(rsrc_in[1]);
+  rsrc[2] = __builtin_amdgcn_readfirstlane(rsrc_in[2]);
+  rsrc[3] = __builtin_amdgcn_readfirstlane(rsrc_in[3]);
   uint32_t saved;
   asm volatile(
       "s_mov_b32 %0, m0\n\t"
@@ -238,15 +244,16 @@ __global__ __launch_bounds__(64 * W, W <= 4 ? 2 : 1) void attn_bf16_kernel(AttnA
   constexpr int ROWS = 32 * W;        // query rows per work item
   constexpr int CPR = D / 8;          // 16-byte chunks per row
   constexpr int RPI = 64 / CPR;       // rows per 1 KB wave load
-  constexpr int NL = 64 / RPI;        // wave loads per tensor per tile
+  constexpr int KT = W >= 8 ? 128 : 64;  // keys per LDS tile
+  constexpr int NL = KT / RPI;        // wave loads per tensor per tile
   constexpr int NI = (NL + W - 1) / W;  // wave loads per tensor per tile and wave (at most)
   constexpr int NS = D / 16;          // k-steps of QK^T
   constexpr int NDB = D / 32;         // 32-wide d blocks of the output
   constexpr int RB = D * 2;           // row bytes (bf16 K, fp16 V)
   // separate objects per stage: lets the compiler see that loads into one
   // stage never alias reads of the other (no blanket wait before LDS reads)
-  __shared__ uint4 k_s0[8 * D], k_s1[8 * D];   // 64 rows x D bf16
-  __shared__ uint4 v_s0[8 * D], v_s1[8 * D];   // 64 rows x D fp16
+  __shared__ uint4 k_s0[KT / 8 * D], k_s1[KT / 8 * D];   // KT rows x D bf16
+  __shared__ uint4 v_s0[KT / 8 * D], v_s1[KT / 8 * D];   // KT rows x D fp16
   __shared__ SmemCells sm;
 
   int h, a, kt;
@@ -259,7 +266,7 @@ __global__ __launch_bounds__(64 * W, W <= 4 ? 2 : 1) void attn_bf16_kernel(AttnA
   const int r0 = oq[a] + kt * ROWS;
   const int nrows = min(ROWS, oq[a + 1] - r0);
   const int L = load_cells<NT>(p, h, a, sm.cstart, sm.cpos, sm.red);
-  const int ntiles = (L + 63) / 64;
+  const int ntiles = (L + KT - 1) / KT;
   // cell table -> (next boundary, row delta): row(pos) = pos + delta of its cell
   const int nc = p.rowptr[(long long)h * (p.c_q + 1) + a + 1] -
                  p.rowptr[(long long)h * (p.c_q + 1) + a];
@@ -293,16 +300,24 @@ __global__ __launch_bounds__(64 * W, W <= 4 ? 2 : 1) void attn_bf16_kernel(AttnA
   __builtin_amdgcn_s_waitcnt(0x0F70);
 
   // loader: wave load i of wave w covers tile rows RPI*(w + i*W) .. +RPI.
-  // tc (wave-uniform) is the cell holding the tile's first stream position;
-  // each lane walks forward from it to the cell of its own row (a tile spans
-  // few cells), so no per-lane cursor state is carried between tiles.
+  // tc (wave-uniform) is a cell with cpos[tc] <= the tile's first stream
+  // position.  One batch of independent LDS reads fetches the next four cell
+  // boundaries and row deltas; each lane counts the boundaries at or below
+  // its position (a tile rarely spans more than four cells; beyond that the
+  // lane walks on), so no chain of dependent LDS reads sits on the issue
+  // path and no per-lane state is carried between tiles.
   int tc = 0;
-  auto issue_tile = [&](auto stage, int t) {
+  auto issue_tile = [&](auto stage, int t) __attribute__((always_inline)) {
     constexpr int B = decltype(stage)::value;
     uint4* kbase = B == 0 ? k_s0 : k_s1;
     uint4* vbase = B == 0 ? v_s0 : v_s1;
-    while (sm.cpos[tc + 1] <= t * 64) ++tc;
-    tc = __builtin_amdgcn_readfirstlane(tc);
+    const int t0 = t * KT;
+    int e[4], dl[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      e[j] = __builtin_amdgcn_readfirstlane(sm.cpos[min(tc + 1 + j, nc)]);
+      dl[j] = __builtin_amdgcn_readfirstlane(sm.cstart[min(tc + j, nc - 1)]);
+    }
     // lane-derived terms recomputed per issue rather than held across the loop
     int ln = lane;
     asm volatile("" : "+v"(ln));
@@ -312,11 +327,16 @@ __global__ __launch_bounds__(64 * W, W <= 4 ? 2 : 1) void attn_bf16_kernel(AttnA
       const int blk = wid + i * W;                        // wave-uniform
       if (NL % W != 0 && blk >= NL) break;
       const int row = blk * RPI + lrow;                   // tile row of this lane
-      int pos = t * 64 + row;
+      int pos = t0 + row;
       pos = pos < L ? pos : L - 1;                        // tail rows: any valid row
-      int c = tc;
-      while (pos >= sm.cpos[c + 1]) ++c;
-      const uint32_t roff = uint32_t(pos + sm.cstart[c]) * RB;
+      const int k = int(e[0] <= pos) + int(e[1] <= pos) + int(e[2] <= pos) + int(e[3] <= pos);
+      int delta = k == 0 ? dl[0] : (k == 1 ? dl[1] : (k == 2 ? dl[2] : dl[3]));
+      if (k == 4) {
+        int c = tc + 4;
+        while (pos >= sm.cpos[c + 1]) ++c;
+        delta = sm.cstart[c];
+      }
+      const uint32_t roff = uint32_t(pos + delta) * RB;
       const int kc = lpc ^ (row & (CPR - 1));
       const int vc = lpc ^ swz_v<D>(row);
       uint4* kdst = kbase + blk * RPI * CPR;
@@ -324,6 +344,10 @@ __global__ __launch_bounds__(64 * W, W <= 4 ? 2 : 1) void attn_bf16_kernel(AttnA
       lds_dma16(krs, __builtin_amdgcn_readfirstlane(lds_addr_of(kdst)), roff + kc * 16);
       lds_dma16(vrs, __builtin_amdgcn_readfirstlane(lds_addr_of(vdst)), roff + vc * 16);
     }
+    // cells that end at or before the next tile's first position
+    const int t1 = t0 + KT;
+    tc += int(e[0] <= t1) + int(e[1] <= t1) + int(e[2] <= t1) + int(e[3] <= t1);
+    tc = __builtin_amdgcn_readfirstlane(min(tc, nc - 1));
   };
 
   f32x16_t oacc[NDB];
@@ -336,10 +360,83 @@ __global__ __launch_bounds__(64 * W, W <= 4 ? 2 : 1) void attn_bf16_kernel(AttnA
 
   // transposed-read addressing (fixed per lane): group G, index i in group
   const int G = lane >> 4, gi = lane & 15, gg = G >> 1;
-  auto compute = [&](auto stage, int t) {
+  // LDS -> MFMA software pipelines.  Fragments are read DEPTH MFMAs ahead
+  // into a rotating buffer; scheduling fences keep the compiler from
+  // regrouping the reads (it would otherwise wait on each read right before
+  // its MFMA and expose the full LDS latency every time).
+  // Fragment addresses are a per-lane base XOR a k-step term plus constant
+  // offsets: with the swizzles above, chunk(s) = chunk(0) ^ 2s for K and
+  // chunk(db) = chunk(0) ^ 4db for V.  The bases pass through an empty asm
+  // statement per call so the compiler recomputes the XORs (one VALU op per
+  // read) instead of hoisting a register per k-step out of the tile loop.
+  // K fragment (A operand of S^T = K Q^T): key row kr0 + 32 j + n, dims 16 s + 8 g ..
+  const int kbase0 = n * (CPR * 16) + ((g ^ (n & (CPR - 1))) * 16);
+  // V^T fragment (A operand of O^T = V^T P^T), 16-key step u, d block db:
+  // keys 16u + 4gg + gi/4 (first 4 slots) and +8 (last 4 slots)
+  const int vrow0 = 4 * gg + (gi >> 2);
+  const int vbase0 = vrow0 * (CPR * 16) +
+                     ((2 * (G & 1) + ((gi & 3) >> 1)) ^ swz_v<D>(vrow0)) * 16 + (gi & 1) * 8;
+  auto vfrag = [&](const uint4* vb, int vb0, int u, int db) __attribute__((always_inline)) {
+    const char* b1 = reinterpret_cast<const char*>(vb) + ((vb0 ^ (64 * db)) + u * 16 * CPR * 16);
+    const v4i16_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)b1);
+    const v4i16_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)(b1 + 8 * CPR * 16));
+    return __builtin_bit_cast(
+        f16x8_t, (short __attribute__((ext_vector_type(8)))){lo[0], lo[1], lo[2], lo[3], hi[0],
+                                                              hi[1], hi[2], hi[3]});
+  };
+  // S^T for NB 32-key blocks (key rows kr0 + 32 j + n)
+  auto qk_pipe = [&](const uint4* kb_, int kr0, auto nb_c, auto depth_c,
+                     f32x16_t* sacc) __attribute__((always_inline)) {
+    constexpr int NB = decltype(nb_c)::value, DEPTH = decltype(depth_c)::value;
+    int kb0 = kbase0;
+    asm volatile("" : "+v"(kb0));
+    const char* kc = reinterpret_cast<const char*>(kb_) + kr0 * CPR * 16;
+    auto kfrag = [&](int j, int s_) __attribute__((always_inline)) {
+      return *reinterpret_cast<const bf16x8_t*>(kc + ((kb0 ^ (32 * s_)) + j * 32 * CPR * 16));
+    };
+    bf16x8_t buf[DEPTH][NB];
+#pragma unroll
+    for (int d0 = 0; d0 < DEPTH; ++d0)
+#pragma unroll
+      for (int j = 0; j < NB; ++j) buf[d0][j] = kfrag(j, d0);
+#pragma unroll
+    for (int s_ = 0; s_ < NS; ++s_) {
+#pragma unroll
+      for (int j = 0; j < NB; ++j)
+        sacc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(buf[s_ % DEPTH][j], qf[s_], sacc[j], 0,
+                                                          0, 0);
+      if (s_ + DEPTH < NS) {
+#pragma unroll
+        for (int j = 0; j < NB; ++j) buf[s_ % DEPTH][j] = kfrag(j, s_ + DEPTH);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  // O^T += V^T P^T over NU 16-key steps starting at u0 (P fragment pf[u - u0])
+  auto pv_pipe = [&](const uint4* vb, int u0, auto nu_c, auto depth_c,
+                     const f16x8_t* pf) __attribute__((always_inline)) {
+    constexpr int NU = decltype(nu_c)::value, DEPTH = decltype(depth_c)::value;
+    constexpr int NF = NU * NDB;
+    int vb0 = vbase0;
+    asm volatile("" : "+v"(vb0));
+    f16x8_t buf[DEPTH];
+#pragma unroll
+    for (int f = 0; f < DEPTH; ++f) buf[f] = vfrag(vb, vb0, u0 + f / NDB, f % NDB);
+#pragma unroll
+    for (int f = 0; f < NF; ++f) {
+      oacc[f % NDB] =
+          __builtin_amdgcn_mfma_f32_32x32x16_f16(buf[f % DEPTH], pf[f / NDB], oacc[f % NDB], 0, 0, 0);
+      if (f + DEPTH < NF) buf[f % DEPTH] = vfrag(vb, vb0, u0 + (f + DEPTH) / NDB, (f + DEPTH) % NDB);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
+  // one 64-key sub-tile (rows 64 q ..) of the stage; the next tile's loads
+  // are issued behind the QK^T MFMAs of sub-tile 0
+  auto compute = [&](auto stage, int t, int q) __attribute__((always_inline)) {
     constexpr int B = decltype(stage)::value;
-    const uint4* kb_ = B == 0 ? k_s0 : k_s1;
-    const uint4* vb = B == 0 ? v_s0 : v_s1;
+    const uint4* kb_ = (B == 0 ? k_s0 : k_s1) + 64 * q * CPR;
+    const uint4* vb = (B == 0 ? v_s0 : v_s1) + 64 * q * CPR;
     // S^T = K Q^T for the two 32-key blocks, fragments read one step ahead
     f32x16_t sacc0 = f32x16_t{}, sacc1 = f32x16_t{};
     const int r_a = n, r_b = 32 + n;
@@ -358,8 +455,8 @@ __global__ __launch_bounds__(64 * W, W <= 4 ? 2 : 1) void attn_bf16_kernel(AttnA
       a1 = n1;
     }
     // next tile's loads go out while the QK^T MFMAs drain
-    if (t + 1 < ntiles) issue_tile(Stage<1 - B>{}, t + 1);
-    const int tail = L - t * 64;   // valid keys in this tile (may exceed 64)
+    if (q == 0 && t + 1 < ntiles) issue_tile(Stage<1 - B>{}, t + 1);
+    const int tail = L - t * KT - 64 * q;   // valid keys in this sub-tile (may exceed 64)
     if (tail < 64) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
@@ -400,45 +497,22 @@ __global__ __launch_bounds__(64 * W, W <= 4 ? 2 : 1) void attn_bf16_kernel(AttnA
         lsum = __builtin_amdgcn_fdot2(f16x2_t{pf[u][j], pf[u][j + 1]}, ones, lsum, false);
     l_run += lsum;
     // u outer, d blocks inner: NDB independent accumulation chains interleave
+    const int vb0 = vbase0;
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
+    for (int u = 0; u < 4; ++u)
 #pragma unroll
-      for (int db = 0; db < NDB; ++db) {
-        // keys 16u + 4gg + gi/4 (first 4 slots) and +8 (last 4 slots); d chunk
-        const int row1 = 16 * u + 4 * gg + (gi >> 2);
-        const int row2 = row1 + 8;
-        const int ch = 4 * db + 2 * (G & 1) + ((gi & 3) >> 1);
-        const int hb = (gi & 1) * 8;
-        const char* b1 = reinterpret_cast<const char*>(vb + row1 * CPR + (ch ^ swz_v<D>(row1))) + hb;
-        const char* b2 = reinterpret_cast<const char*>(vb + row2 * CPR + (ch ^ swz_v<D>(row2))) + hb;
-        const v4i16_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)b1);
-        const v4i16_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)b2);
-        const f16x8_t af = __builtin_bit_cast(
-            f16x8_t, (short __attribute__((ext_vector_type(8)))){lo[0], lo[1], lo[2], lo[3],
-                                                                  hi[0], hi[1], hi[2], hi[3]});
-        oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af, pf[u], oacc[db], 0, 0, 0);
-      }
-    }
+      for (int db = 0; db < NDB; ++db)
+        oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vfrag(vb, vb0, u, db), pf[u], oacc[db], 0,
+                                                          0, 0);
   };
 
   // Register-lean variant for large items: the 64-key tile is processed as
   // two 32-key halves (one score block, half the P fragments live at once).
-  auto compute_half = [&](const uint4* kb_, const uint4* vb, int kbi, int tail) {
-    f32x16_t sacc = f32x16_t{};
-    // swizzle term recomputed per use (an opaque copy keeps the compiler from
-    // hoisting one address register per k-step out of the tile loop)
-    int sw = n & (CPR - 1);
-    asm volatile("" : "+v"(sw));
-    const uint4* krow = kb_ + (32 * kbi + n) * CPR;
-    bf16x8_t a0 = __builtin_bit_cast(bf16x8_t, krow[g ^ sw]);
-#pragma unroll
-    for (int s = 0; s < NS; ++s) {
-      bf16x8_t n0 = a0;
-      if (s + 1 < NS)
-        n0 = __builtin_bit_cast(bf16x8_t, krow[(2 * s + 2 + g) ^ sw]);
-      sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qf[s], sacc, 0, 0, 0);
-      a0 = n0;
-    }
+  auto compute_half = [&](const uint4* kb_, const uint4* vb, int kbi, int tail) __attribute__((always_inline)) {
+    f32x16_t sacc1[1] = {f32x16_t{}};
+    qk_pipe(kb_, 32 * kbi, std::integral_constant<int, 1>{}, std::integral_constant<int, 4>{},
+            sacc1);
+    f32x16_t sacc = sacc1[0];
     if (tail < 32 * kbi + 32) {
 #pragma unroll
       for (int i = 0; i < 16; ++i)
@@ -469,33 +543,18 @@ __global__ __launch_bounds__(64 * W, W <= 4 ? 2 : 1) void attn_bf16_kernel(AttnA
       for (int j = 0; j < 8; j += 2)
         lsum = __builtin_amdgcn_fdot2(f16x2_t{pf[u][j], pf[u][j + 1]}, ones, lsum, false);
     l_run += lsum;
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-#pragma unroll
-      for (int db = 0; db < NDB; ++db) {
-        const int row1 = 32 * kbi + 16 * u + 4 * gg + (gi >> 2);
-        const int row2 = row1 + 8;
-        const int ch = 4 * db + 2 * (G & 1) + ((gi & 3) >> 1);
-        const int hb = (gi & 1) * 8;
-        const char* b1 = reinterpret_cast<const char*>(vb + row1 * CPR + (ch ^ swz_v<D>(row1))) + hb;
-        const char* b2 = reinterpret_cast<const char*>(vb + row2 * CPR + (ch ^ swz_v<D>(row2))) + hb;
-        const v4i16_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)b1);
-        const v4i16_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)b2);
-        const f16x8_t af = __builtin_bit_cast(
-            f16x8_t, (short __attribute__((ext_vector_type(8)))){lo[0], lo[1], lo[2], lo[3],
-                                                                  hi[0], hi[1], hi[2], hi[3]});
-        oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af, pf[u], oacc[db], 0, 0, 0);
-      }
-    }
+    pv_pipe(vb, 2 * kbi, std::integral_constant<int, 2>{}, std::integral_constant<int, 4>{}, pf);
   };
-  auto compute_lean = [&](auto stage, int t) {
+  auto compute_lean = [&](auto stage, int t) __attribute__((always_inline)) {
     constexpr int B = decltype(stage)::value;
     const uint4* kb_ = B == 0 ? k_s0 : k_s1;
     const uint4* vb = B == 0 ? v_s0 : v_s1;
-    const int tail = L - t * 64;
+    const int tail = L - t * KT;
     compute_half(kb_, vb, 0, tail);
     if (t + 1 < ntiles) issue_tile(Stage<1 - B>{}, t + 1);
-    if (tail > 32) compute_half(kb_, vb, 1, tail);
+#pragma unroll
+    for (int hq = 1; hq < KT / 32; ++hq)
+      if (tail > 32 * hq) compute_half(kb_, vb, hq, tail);
   };
 
   // Two-stage pipeline with one barrier per tile: after the barrier of step
@@ -503,12 +562,18 @@ __global__ __launch_bounds__(64 * W, W <= 4 ? 2 : 1) void attn_bf16_kernel(AttnA
   // tile t+1 (issued from inside compute, behind the QK^T MFMAs) while tile t
   // is computed.  Raw s_barrier: __syncthreads() would
   // also drain the loads in flight.
-  auto step = [&](auto stage, int t) {
+  auto step = [&](auto stage, int t) __attribute__((always_inline)) {
     constexpr int B = decltype(stage)::value;
     asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
     if (wave_active) {
-      if constexpr (W >= 12) compute_lean(stage, t);
-      else compute(stage, t);
+      if constexpr (W >= 12) {
+        compute_lean(stage, t);
+      } else {
+        compute(stage, t, 0);
+        if constexpr (KT == 128) {
+          if (L - t * KT > 64) compute(stage, t, 1);
+        }
+      }
     } else if (t + 1 < ntiles) {
       issue_tile(Stage<1 - B>{}, t + 1);
     }
