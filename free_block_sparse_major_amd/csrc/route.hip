@@ -64,23 +64,29 @@ __global__ __launch_bounds__(256) void score_kernel(const double* __restrict__ c
 }
 
 enum { kModeNone = 0, kModeAll = 1, kModeThresh = 2 };
+constexpr int kSelWaves = kSelThreads / 64;
+constexpr int kMaxRowChunks = SPARSEPR_MAX_GROUPS / 64;
 
+// One block per head.  Every pass walks the cell matrix row by row (one wave
+// per query group, lanes over K/V groups), so row quantities are
+// wave-uniform and the score reads are coalesced.
 __global__ __launch_bounds__(kSelThreads) void select_kernel(
     const double* __restrict__ scores, const int32_t* __restrict__ off_q,
     const int32_t* __restrict__ off_k, int c_q, int c_k, long long budget,
     int32_t* __restrict__ rowptr, int32_t* __restrict__ col, long long* __restrict__ routed) {
   const int h = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
-  const int nw = kSelThreads / 64;
   __shared__ int32_t na[SPARSEPR_MAX_GROUPS], mb[SPARSEPR_MAX_GROUPS];
   __shared__ int32_t forced[SPARSEPR_MAX_GROUPS], rc[SPARSEPR_MAX_GROUPS];
-  __shared__ long long hist[kBuckets];
+  __shared__ unsigned long long hist_w[kBuckets];
+  __shared__ uint32_t hist_c[kBuckets];
   __shared__ double cand_s[kCap];
   __shared__ int32_t cand_i[kCap];
-  __shared__ long long red[kSelThreads / 64];
-  __shared__ double redd[kSelThreads / 64];
+  __shared__ long long red[kSelWaves];
+  __shared__ double redd[kSelWaves];
   __shared__ int32_t slot;
   __shared__ long long sh_tp;
   __shared__ int32_t sh_j;
+  __shared__ uint32_t sh_cnt;
   __shared__ double sh_es;
   __shared__ int32_t sh_ei;
 
@@ -88,110 +94,168 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
   const int32_t* ok = off_k + int64_t(h) * (c_k + 1);
   for (int i = tid; i < c_q; i += kSelThreads) na[i] = oq[i + 1] - oq[i];
   for (int i = tid; i < c_k; i += kSelThreads) mb[i] = ok[i + 1] - ok[i];
-  __syncthreads();
   if (tid == 0) { sh_es = 0.0; sh_ei = -1; }
+  __syncthreads();
   const double* S = scores + int64_t(h) * c_q * c_k;
-  const int cells = c_q * c_k;
+  const int nbk = (c_k + 63) / 64;
 
-  // forced cell of every non-empty query group: best score, ties -> smaller b
-  for (int a = wid; a < c_q; a += nw) {
+  // pass 1: forced cell of every non-empty query group (best score, ties ->
+  // smaller b), forced pairs, candidate weight and candidate score range
+  long long fpart = 0, wpart = 0;
+  double lmin = __builtin_huge_val(), lmax = -__builtin_huge_val();
+  for (int a = wid; a < c_q; a += kSelWaves) {
+    const int n_a = na[a];
+    if (n_a == 0) {
+      if (lane == 0) forced[a] = -1;
+      continue;
+    }
+    double sv[kMaxRowChunks];
     double best = 0.0;
     int bb = -1;
-    if (na[a] > 0) {
-      for (int b = lane; b < c_k; b += 64) {
-        if (mb[b] == 0) continue;
-        double s = S[int64_t(a) * c_k + b];
-        if (bb < 0 || s > best) { best = s; bb = b; }
+#pragma unroll
+    for (int k = 0; k < kMaxRowChunks; ++k) {
+      const int b = 64 * k + lane;
+      sv[k] = 0.0;
+      if (k < nbk && b < c_k && mb[b] > 0) {
+        sv[k] = S[int64_t(a) * c_k + b];
+        if (bb < 0 || sv[k] > best) { best = sv[k]; bb = b; }
       }
     }
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) {
-      double s2 = __shfl_xor(best, o);
-      int b2 = __shfl_xor(bb, o);
-      bool take = b2 >= 0 && (bb < 0 || s2 > best || (s2 == best && b2 < bb));
-      if (take) { best = s2; bb = b2; }
+      const double s2 = __shfl_xor(best, o);
+      const int b2 = __shfl_xor(bb, o);
+      if (b2 >= 0 && (bb < 0 || s2 > best || (s2 == best && b2 < bb))) { best = s2; bb = b2; }
     }
-    if (lane == 0) forced[a] = bb;
+    if (lane == 0) {
+      forced[a] = bb;
+      if (bb >= 0) fpart += (long long)n_a * mb[bb];
+    }
+#pragma unroll
+    for (int k = 0; k < kMaxRowChunks; ++k) {
+      const int b = 64 * k + lane;
+      if (k < nbk && b < c_k && b != bb && mb[b] > 0) {
+        wpart += (long long)n_a * mb[b];
+        lmin = sv[k] < lmin ? sv[k] : lmin;
+        lmax = sv[k] > lmax ? sv[k] : lmax;
+      }
+    }
   }
-  __syncthreads();
-  long long fpart = 0;
-  for (int a = tid; a < c_q; a += kSelThreads)
-    if (forced[a] >= 0) fpart += (long long)na[a] * mb[forced[a]];
   const long long F = block_sum(fpart, red);
+  const long long W = block_sum(wpart, red);
+  double lo = block_min(lmin, redd);
+  double hi = block_max(lmax, redd);
 
-  auto is_cand = [&](int idx) -> bool {
-    int a = idx / c_k, b = idx - a * c_k;
-    return na[a] > 0 && mb[b] > 0 && b != forced[a];
-  };
-  auto weight = [&](int idx) -> long long {
-    int a = idx / c_k, b = idx - a * c_k;
-    return (long long)na[a] * mb[b];
+  // candidate cells (non-empty, not forced) of the rows this wave walks
+  auto for_cands = [&](auto&& fn) {
+    for (int a = wid; a < c_q; a += kSelWaves) {
+      const int n_a = na[a];
+      if (n_a == 0) continue;
+      const int fb = forced[a];
+      for (int k = 0; k < nbk; ++k) {
+        const int b = 64 * k + lane;
+        if (b < c_k && b != fb) {
+          const int m = mb[b];
+          if (m > 0) fn(S[int64_t(a) * c_k + b], (long long)n_a * m, a * c_k + b);
+        }
+      }
+    }
   };
 
   int mode = kModeNone;
   double es = 0.0;
   int ei = -1;
-  long long T = budget - F;
+  const long long T = budget - F;
   if (T > 0) {
-    long long wpart = 0;
-    for (int idx = tid; idx < cells; idx += kSelThreads)
-      if (is_cand(idx)) wpart += weight(idx);
-    const long long W = block_sum(wpart, red);
     if (W <= T) {
       mode = kModeAll;
     } else {
       mode = kModeThresh;
-      // initial score interval over all candidates
-      double lmin = __builtin_huge_val(), lmax = -__builtin_huge_val();
-      for (int idx = tid; idx < cells; idx += kSelThreads)
-        if (is_cand(idx)) {
-          double s = S[idx];
-          lmin = s < lmin ? s : lmin;
-          lmax = s > lmax ? s : lmax;
-        }
-      double lo = block_min(lmin, redd);
-      double hi = block_max(lmax, redd);
-      long long Tp = T;  // target inside [lo, hi]; weight above hi already taken
-      for (int iter = 0; iter < 200; ++iter) {
+      long long Tp = T;  // weight still to take inside [lo, hi] (everything above is taken)
+      for (int round = 0; round < 256; ++round) {
         if (lo == hi) {
-          // all remaining candidates tie on the score: order by cell index
+          // every remaining candidate has the same score: index order decides
+          const int cells = c_q * c_k;
           const int per = (cells + kSelThreads - 1) / kSelThreads;
           const int i0 = tid * per, i1 = min(cells, i0 + per);
+          auto cand_at = [&](int idx, long long& w) -> bool {
+            const int a = idx / c_k, b = idx - a * c_k;
+            if (na[a] == 0 || mb[b] == 0 || b == forced[a] || S[idx] != lo) return false;
+            w = (long long)na[a] * mb[b];
+            return true;
+          };
           long long part = 0;
-          for (int idx = i0; idx < i1; ++idx)
-            if (is_cand(idx) && S[idx] == lo) part += weight(idx);
+          for (int idx = i0; idx < i1; ++idx) {
+            long long w;
+            if (cand_at(idx, w)) part += w;
+          }
           long long tot;
           long long run = block_exclusive_scan(part, red, &tot);
-          for (int idx = i0; idx < i1; ++idx)
-            if (is_cand(idx) && S[idx] == lo) {
-              long long w = weight(idx);
+          for (int idx = i0; idx < i1; ++idx) {
+            long long w;
+            if (cand_at(idx, w)) {
               if (run < Tp && Tp <= run + w) { sh_es = lo; sh_ei = idx; }
               run += w;
             }
+          }
           __syncthreads();
           es = sh_es;
           ei = sh_ei;
           break;
         }
-        long long cpart = 0;
-        for (int idx = tid; idx < cells; idx += kSelThreads)
-          if (is_cand(idx)) {
-            double s = S[idx];
-            if (s >= lo && s <= hi) ++cpart;
+        // weighted histogram of the candidates in [lo, hi]; bucket() is
+        // monotone in the score, so equal scores share a bucket
+        const double scale = double(kBuckets) / (hi - lo);
+        auto bucket = [&](double sc) -> int {
+          const int bk = int((sc - lo) * scale);
+          return bk < 0 ? 0 : (bk < kBuckets ? bk : kBuckets - 1);
+        };
+        for (int i = tid; i < kBuckets; i += kSelThreads) { hist_w[i] = 0; hist_c[i] = 0; }
+        __syncthreads();
+        for_cands([&](double sc, long long w, int) {
+          if (sc >= lo && sc <= hi) {
+            const int bk = bucket(sc);
+            atomicAdd(&hist_w[bk], (unsigned long long)w);
+            atomicAdd(&hist_c[bk], 1u);
           }
-        const long long cnt = block_sum(cpart, red);
+        });
+        __syncthreads();
+        // crossing bucket: scanning down from the top, the first bucket at
+        // which the accumulated weight reaches Tp
+        {
+          constexpr int BPT = kBuckets / kSelThreads;
+          long long loc = 0;
+#pragma unroll
+          for (int j = 0; j < BPT; ++j) loc += (long long)hist_w[BPT * tid + j];
+          long long tot;
+          const long long pre = block_exclusive_scan(loc, red, &tot);
+          long long acc = tot - pre - loc;  // weight of the buckets above this thread's
+#pragma unroll
+          for (int j = BPT - 1; j >= 0; --j) {
+            const int bk = BPT * tid + j;
+            const long long w = (long long)hist_w[bk];
+            if (acc < Tp && Tp <= acc + w) {
+              sh_j = bk;
+              sh_tp = Tp - acc;
+              sh_cnt = hist_c[bk];
+            }
+            acc += w;
+          }
+        }
+        __syncthreads();
+        const int jb = sh_j;
+        Tp = sh_tp;
+        const uint32_t cnt = sh_cnt;
         if (cnt <= kCap) {
           if (tid == 0) slot = 0;
           __syncthreads();
-          for (int idx = tid; idx < cells; idx += kSelThreads)
-            if (is_cand(idx)) {
-              double s = S[idx];
-              if (s >= lo && s <= hi) {
-                int p = atomicAdd(&slot, 1);
-                cand_s[p] = s;
-                cand_i[p] = idx;
-              }
+          for_cands([&](double sc, long long, int idx) {
+            if (sc >= lo && sc <= hi && bucket(sc) == jb) {
+              const int p = atomicAdd(&slot, 1);
+              cand_s[p] = sc;
+              cand_i[p] = idx;
             }
+          });
           __syncthreads();
           const int n = slot;
           for (int i = tid; i < n; i += kSelThreads) {
@@ -199,10 +263,15 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
             const int ii = cand_i[i];
             long long pre = 0;
             for (int j = 0; j < n; ++j) {
-              double sj = cand_s[j];
-              if (sj > si || (sj == si && cand_i[j] < ii)) pre += weight(cand_i[j]);
+              const double sj = cand_s[j];
+              const int ij = cand_i[j];
+              if (sj > si || (sj == si && ij < ii)) {
+                const int aj = ij / c_k;
+                pre += (long long)na[aj] * mb[ij - aj * c_k];
+              }
             }
-            long long w = weight(ii);
+            const int ai = ii / c_k;
+            const long long w = (long long)na[ai] * mb[ii - ai * c_k];
             if (pre < Tp && Tp <= pre + w) { sh_es = si; sh_ei = ii; }
           }
           __syncthreads();
@@ -210,44 +279,14 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
           ei = sh_ei;
           break;
         }
-        // weighted histogram over [lo, hi]
-        for (int i = tid; i < kBuckets; i += kSelThreads) hist[i] = 0;
-        __syncthreads();
-        const double span = hi - lo;
-        auto bucket = [&](double s) -> int {
-          double f = (s - lo) / span * double(kBuckets);
-          int bk = int(f);
-          return bk < kBuckets ? bk : kBuckets - 1;
-        };
-        for (int idx = tid; idx < cells; idx += kSelThreads)
-          if (is_cand(idx)) {
-            double s = S[idx];
-            if (s >= lo && s <= hi) atomicAdd((unsigned long long*)&hist[bucket(s)],
-                                              (unsigned long long)weight(idx));
-          }
-        __syncthreads();
-        if (tid == 0) {
-          long long acc = 0;
-          int j = kBuckets - 1;
-          for (; j > 0; --j) {
-            if (acc + hist[j] >= Tp) break;
-            acc += hist[j];
-          }
-          sh_j = j;
-          sh_tp = Tp - acc;
-        }
-        __syncthreads();
-        const int jb = sh_j;
-        Tp = sh_tp;
+        // narrow to the exact score range of the crossing bucket
         double bmin = __builtin_huge_val(), bmax = -__builtin_huge_val();
-        for (int idx = tid; idx < cells; idx += kSelThreads)
-          if (is_cand(idx)) {
-            double s = S[idx];
-            if (s >= lo && s <= hi && bucket(s) == jb) {
-              bmin = s < bmin ? s : bmin;
-              bmax = s > bmax ? s : bmax;
-            }
+        for_cands([&](double sc, long long, int) {
+          if (sc >= lo && sc <= hi && bucket(sc) == jb) {
+            bmin = sc < bmin ? sc : bmin;
+            bmax = sc > bmax ? sc : bmax;
           }
+        });
         const double nlo = block_min(bmin, redd);
         const double nhi = block_max(bmax, redd);
         lo = nlo;
@@ -256,21 +295,21 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
     }
   }
 
-  // final selection -> per-row counts -> CSR
+  // final selection -> per-row counts -> CSR (b ascending)
   auto selected = [&](int a, int b) -> bool {
     if (na[a] == 0 || mb[b] == 0) return false;
     if (b == forced[a]) return true;
     if (mode == kModeAll) return true;
     if (mode == kModeNone) return false;
-    double s = S[int64_t(a) * c_k + b];
-    int idx = a * c_k + b;
-    return s > es || (s == es && idx <= ei);
+    const double sc = S[int64_t(a) * c_k + b];
+    const int idx = a * c_k + b;
+    return sc > es || (sc == es && idx <= ei);
   };
-  for (int a = wid; a < c_q; a += nw) {
+  for (int a = wid; a < c_q; a += kSelWaves) {
     int cnt = 0;
-    for (int b0 = 0; b0 < c_k; b0 += 64) {
-      int b = b0 + lane;
-      bool f = b < c_k && selected(a, b);
+    for (int k = 0; k < nbk; ++k) {
+      const int b = 64 * k + lane;
+      const bool f = b < c_k && selected(a, b);
       cnt += __popcll(__ballot(f));
     }
     if (lane == 0) rc[a] = cnt;
@@ -287,14 +326,14 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
   __syncthreads();
   int32_t* cl = col + int64_t(h) * c_q * c_k;
   long long ppart = 0;
-  for (int a = wid; a < c_q; a += nw) {
+  for (int a = wid; a < c_q; a += kSelWaves) {
     int pos = rc[a];
-    for (int b0 = 0; b0 < c_k; b0 += 64) {
-      int b = b0 + lane;
-      bool f = b < c_k && selected(a, b);
-      unsigned long long m = __ballot(f);
+    for (int k = 0; k < nbk; ++k) {
+      const int b = 64 * k + lane;
+      const bool f = b < c_k && selected(a, b);
+      const unsigned long long m = __ballot(f);
       if (f) {
-        int p = __popcll(m & ((1ull << lane) - 1ull));
+        const int p = __popcll(m & ((1ull << lane) - 1ull));
         cl[pos + p] = b;
         ppart += (long long)na[a] * mb[b];
       }
