@@ -103,6 +103,181 @@ __global__ __launch_bounds__(256) void correct_kernel(const int32_t* __restrict_
   }
 }
 
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+// fp32 -> (hi, lo) bf16 pair, both rounded to nearest even: hi + lo equals x
+// to about 2^-18 relative (the remainder x - hi is exact in fp32)
+SPR_DEV void split_bf16(float x, uint32_t& hi, uint32_t& lo) {
+  hi = f32_to_bf16_rne(x);
+  lo = f32_to_bf16_rne(x - __uint_as_float(hi << 16));
+}
+
+// Rank <= 16 on MFMA (16x16x32 and 16x16x16 bf16), every fp32 product as
+// three bf16 products (hi*hi + hi*lo + lo*hi).  Per 16-row tile of O:
+//   U^T   = A^T O^T        (16 x 16, K = D)
+//   corr^T = Psi U^T        (D x 16, K = 16)
+// The K order of the first product is chosen so that a lane loads exactly
+// the dims it later corrects: lane l (group G = l / 16) holds row l % 16 and
+// dims 16 b + 4 G + e (b < D / 16, e < 4).  The tile goes back to token
+// order through an LDS stage, one row per 32 (fp32: 64) consecutive lanes.
+template <int D>
+__global__ __launch_bounds__(256) void correct_mfma_kernel(const int32_t* __restrict__ perm_q,
+                                                           const float* __restrict__ o_sp,
+                                                           const float* __restrict__ corr_a,
+                                                           const float* __restrict__ corr_psi_t,
+                                                           const float* __restrict__ corr_c,
+                                                           void* __restrict__ out, int64_t out_sh,
+                                                           int64_t out_st, int n_q, int rank,
+                                                           int out_bf16, int tiles_per_wave) {
+  constexpr int NB = D / 16;           // 16-dim blocks
+  constexpr int KS = D / 32;           // k-steps of the first product
+  constexpr int PITCH = D + 4;         // staged row pitch in floats
+  __shared__ float stage[4][16 * PITCH];
+  const int h = blockIdx.y, tid = threadIdx.x, wid = tid >> 6, lane = tid & 63;
+  const int r16 = lane & 15, G = lane >> 4;
+  const float* Ah = corr_a + (long long)h * D * rank;      // [D][rank]
+  const float* Ph = corr_psi_t + (long long)h * rank * D;  // [rank][D]
+  const float* ch = corr_c + (long long)h * D;
+  // A^T operand, k-step s: row i = r16, dims 16 (2s + e / 4) + 4G + e % 4
+  bf16x8_t a_hi[KS], a_lo[KS];
+#pragma unroll
+  for (int s_ = 0; s_ < KS; ++s_) {
+    uint32_t hw[4], lw[4];
+#pragma unroll
+    for (int e = 0; e < 8; e += 2) {
+      const int d0 = 16 * (2 * s_ + e / 4) + 4 * G + (e % 4);
+      const float x0 = r16 < rank ? Ah[d0 * rank + r16] : 0.f;
+      const float x1 = r16 < rank ? Ah[(d0 + 1) * rank + r16] : 0.f;
+      uint32_t h0, l0, h1, l1;
+      split_bf16(x0, h0, l0);
+      split_bf16(x1, h1, l1);
+      hw[e / 2] = h0 | (h1 << 16);
+      lw[e / 2] = l0 | (l1 << 16);
+    }
+    a_hi[s_] = __builtin_bit_cast(bf16x8_t, make_uint4(hw[0], hw[1], hw[2], hw[3]));
+    a_lo[s_] = __builtin_bit_cast(bf16x8_t, make_uint4(lw[0], lw[1], lw[2], lw[3]));
+  }
+  // Psi operand, dim block b: row (dim) 16 b + r16, k = rank 4G + e
+  bf16x4_t p_hi[NB], p_lo[NB];
+  f32x4_t cvec[NB];
+#pragma unroll
+  for (int b = 0; b < NB; ++b) {
+    uint32_t hw[2], lw[2];
+#pragma unroll
+    for (int e = 0; e < 4; e += 2) {
+      const int k0 = 4 * G + e;
+      const float x0 = k0 < rank ? Ph[k0 * D + 16 * b + r16] : 0.f;
+      const float x1 = k0 + 1 < rank ? Ph[(k0 + 1) * D + 16 * b + r16] : 0.f;
+      uint32_t h0, l0, h1, l1;
+      split_bf16(x0, h0, l0);
+      split_bf16(x1, h1, l1);
+      hw[e / 2] = h0 | (h1 << 16);
+      lw[e / 2] = l0 | (l1 << 16);
+    }
+    p_hi[b] = __builtin_bit_cast(bf16x4_t, make_uint2(hw[0], hw[1]));
+    p_lo[b] = __builtin_bit_cast(bf16x4_t, make_uint2(lw[0], lw[1]));
+#pragma unroll
+    for (int e = 0; e < 4; ++e) cvec[b][e] = ch[16 * b + 4 * G + e];
+  }
+  float* st = stage[wid];
+  const int ntile = (n_q + 15) / 16;
+  for (int it = 0; it < tiles_per_wave; ++it) {
+    const int tile = (blockIdx.x * tiles_per_wave + it) * 4 + wid;
+    if (tile >= ntile) break;
+    const int row = tile * 16 + r16;
+    const bool valid = row < n_q;
+    const float* src = o_sp + ((long long)h * n_q + (valid ? row : 0)) * D;
+    f32x4_t o[NB];
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      const float4 v = valid ? *reinterpret_cast<const float4*>(src + 16 * b + 4 * G)
+                             : make_float4(0.f, 0.f, 0.f, 0.f);
+      o[b] = f32x4_t{v.x, v.y, v.z, v.w};
+    }
+    // U^T = A^T O^T
+    f32x4_t u = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s_ = 0; s_ < KS; ++s_) {
+      uint32_t hw[4], lw[4];
+#pragma unroll
+      for (int e = 0; e < 8; e += 2) {
+        const f32x4_t& ov = o[2 * s_ + e / 4];
+        uint32_t h0, l0, h1, l1;
+        split_bf16(ov[e % 4], h0, l0);
+        split_bf16(ov[e % 4 + 1], h1, l1);
+        hw[e / 2] = h0 | (h1 << 16);
+        lw[e / 2] = l0 | (l1 << 16);
+      }
+      const bf16x8_t b_hi = __builtin_bit_cast(bf16x8_t, make_uint4(hw[0], hw[1], hw[2], hw[3]));
+      const bf16x8_t b_lo = __builtin_bit_cast(bf16x8_t, make_uint4(lw[0], lw[1], lw[2], lw[3]));
+      u = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a_hi[s_], b_hi, u, 0, 0, 0);
+      u = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a_hi[s_], b_lo, u, 0, 0, 0);
+      u = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a_lo[s_], b_hi, u, 0, 0, 0);
+    }
+    // corr^T = Psi U^T (+ c, + o): accumulators start at o + c
+    uint32_t uh[2], ul[2];
+    {
+      uint32_t h0, l0, h1, l1, h2, l2, h3, l3;
+      split_bf16(u[0], h0, l0);
+      split_bf16(u[1], h1, l1);
+      split_bf16(u[2], h2, l2);
+      split_bf16(u[3], h3, l3);
+      uh[0] = h0 | (h1 << 16);
+      uh[1] = h2 | (h3 << 16);
+      ul[0] = l0 | (l1 << 16);
+      ul[1] = l2 | (l3 << 16);
+    }
+    const bf16x4_t ub_hi = __builtin_bit_cast(bf16x4_t, make_uint2(uh[0], uh[1]));
+    const bf16x4_t ub_lo = __builtin_bit_cast(bf16x4_t, make_uint2(ul[0], ul[1]));
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      f32x4_t acc = o[b] + cvec[b];
+      acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(p_hi[b], ub_hi, acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(p_hi[b], ub_lo, acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(p_lo[b], ub_hi, acc, 0, 0, 0);
+      // lane holds out[row][16 b + 4 G + e]: stage it
+      *reinterpret_cast<float4*>(st + r16 * PITCH + 16 * b + 4 * G) =
+          make_float4(acc[0], acc[1], acc[2], acc[3]);
+    }
+    // rows back to token order; LDS traffic of a wave stays in that wave
+    if (out_bf16) {
+      // 32 lanes per row, 4 values (8 bytes) per lane
+      constexpr int LPR = D / 4;
+      constexpr int RPS = 64 / LPR;
+#pragma unroll
+      for (int r2 = 0; r2 < 16; r2 += RPS) {
+        const int rr = r2 + lane / LPR, cc = (lane % LPR) * 4;
+        const int grow = tile * 16 + rr;
+        const float4 v = *reinterpret_cast<const float4*>(st + rr * PITCH + cc);
+        if (grow < n_q) {
+          const int tok = perm_q[(long long)h * n_q + grow];
+          uint2 w;
+          w.x = uint32_t(f32_to_bf16_rne(v.x)) | (uint32_t(f32_to_bf16_rne(v.y)) << 16);
+          w.y = uint32_t(f32_to_bf16_rne(v.z)) | (uint32_t(f32_to_bf16_rne(v.w)) << 16);
+          *reinterpret_cast<uint2*>(static_cast<uint16_t*>(out) + (long long)h * out_sh +
+                                    (long long)tok * out_st + cc) = w;
+        }
+      }
+    } else {
+      constexpr int LPR = D / 4;
+      constexpr int RPS = 64 / LPR;
+#pragma unroll
+      for (int r2 = 0; r2 < 16; r2 += RPS) {
+        const int rr = r2 + lane / LPR, cc = (lane % LPR) * 4;
+        const int grow = tile * 16 + rr;
+        const float4 v = *reinterpret_cast<const float4*>(st + rr * PITCH + cc);
+        if (grow < n_q) {
+          const int tok = perm_q[(long long)h * n_q + grow];
+          *reinterpret_cast<float4*>(static_cast<float*>(out) + (long long)h * out_sh +
+                                     (long long)tok * out_st + cc) = v;
+        }
+      }
+    }
+  }
+}
+
 // probe rows take their dense output (after the correction pass on the stream)
 __global__ __launch_bounds__(256) void probe_overwrite_kernel(const int32_t* __restrict__ tokens,
                                                               const float* __restrict__ dense,
@@ -170,9 +345,27 @@ extern "C" int32_t sparsepr_correct(const sparsepr_dims* dims, int32_t m, int32_
   a.n_q = dims->n_q;
   a.rank = rank;
   a.out_bf16 = out_dtype == SPARSEPR_BF16;
-  dim3 grid((dims->n_q + 255) / 256, dims->heads);
-  if (dims->head_dim == 128) launch_correct<128>(a, grid, stream);
-  else launch_correct<64>(a, grid, stream);
+  if (rank <= 16 && dims->dtype == SPARSEPR_BF16) {
+    // bf16 inputs (tolerance of the bf16 path): 16-row tiles on MFMA, 4 waves
+    // per block, a few tiles per wave; fp32 inputs keep the fp32 VALU kernel
+    constexpr int kTilesPerWave = 4;
+    const int ntile = (dims->n_q + 15) / 16;
+    dim3 grid((ntile + 4 * kTilesPerWave - 1) / (4 * kTilesPerWave), dims->heads);
+    if (dims->head_dim == 128)
+      correct_mfma_kernel<128><<<grid, 256, 0, stream>>>(perm_q, o_sp, corr_a, corr_psi_t, corr_c,
+                                                         out, out_stride_head, out_stride_tok,
+                                                         dims->n_q, rank, a.out_bf16,
+                                                         kTilesPerWave);
+    else
+      correct_mfma_kernel<64><<<grid, 256, 0, stream>>>(perm_q, o_sp, corr_a, corr_psi_t, corr_c,
+                                                        out, out_stride_head, out_stride_tok,
+                                                        dims->n_q, rank, a.out_bf16,
+                                                        kTilesPerWave);
+  } else {
+    dim3 grid((dims->n_q + 255) / 256, dims->heads);
+    if (dims->head_dim == 128) launch_correct<128>(a, grid, stream);
+    else launch_correct<64>(a, grid, stream);
+  }
   SPR_LAUNCH_CHECK();
   probe_overwrite_kernel<<<dims->heads, 256, 0, stream>>>(probe_tokens, o_probe_dense, m,
                                                           dims->head_dim, out, out_stride_head,
