@@ -26,8 +26,11 @@
 // cyclic Jacobi eigensolve of Rw Rw^T; finally B is folded with the
 // projection into A = diag(1/s) B Psi and c = mu_R - (mu_x A) Psi^T.
 
+#include <type_traits>
+
 #include "common.h"
 #include "mfma_tiles.h"
+#include "lds_dma.h"
 
 namespace spr {
 namespace {
@@ -332,46 +335,51 @@ __global__ __launch_bounds__(256) void probe_rows_kernel(
 // ---------------------------------------------------------------------------
 // exact probe rows, bf16 inputs: MFMA version
 // ---------------------------------------------------------------------------
-// Two waves per block (probes 0..31 and 32..63) sweep one key chunk in
-// 64-key tiles.  QK^T is a bf16 MFMA (exact products); each score is
-// classified as retained (its K/V group is selected for the probe's query
-// group) or omitted by a per-tile 64-bit mask per probe, built from the
-// group bitmask (keys are group-major, so a tile spans few groups).  The
-// retained and omitted classes keep separate running maxima.  PV runs on
-// fp16 MFMA with P split into hi + lo halves, so the partial numerators
-// carry ~2^-22 relative error.
+// Four waves per block sweep one key chunk in 64-key tiles: wave w handles
+// probes 32 (w & 1) .. +32 and half of the output dims (w >> 1), so every wave
+// forms the scores of its 32 probes (the cheap part) and accumulates the
+// numerators of its dims only.  Tiles are double buffered in LDS and loaded
+// straight from global memory one tile ahead; the per-probe retained-key
+// masks of a tile are built one tile ahead as well.  QK^T is a bf16 MFMA
+// (exact products); each score is classified as retained (its K/V group is
+// selected for the probe's query group) or omitted.  The retained and omitted
+// classes keep separate running maxima.  PV runs on fp16 MFMA with P split
+// into hi + lo halves, so the partial numerators carry ~2^-22 relative error.
 template <int D>
-__global__ __launch_bounds__(128) void probe_rows_mfma_kernel(
+__global__ __launch_bounds__(256, 2) void probe_rows_mfma_kernel(
     const uint16_t* __restrict__ q_g, const uint16_t* __restrict__ k_g,
     const uint16_t* __restrict__ v_g, const int32_t* __restrict__ v_shift,
     const int32_t* __restrict__ off_k, const int32_t* __restrict__ rowptr,
     const int32_t* __restrict__ col, const int32_t* __restrict__ probe_rows,
     const int32_t* __restrict__ probe_group, int n_q, int n_k, int c_q, int c_k, int m,
     float c2, float* __restrict__ part_s, float* __restrict__ part_n) {
-  constexpr int CPR = D / 8, NS = D / 16, NDB = D / 32;
+  constexpr int CPR = D / 8, NS = D / 16, NDB = D / 32, NDH = NDB / 2;
+  constexpr int RPI = 64 / CPR;       // tile rows per 1 KB wave load
   const int chunk = blockIdx.x, h = blockIdx.y, tid = threadIdx.x;
-  const int wid = tid >> 6, lane = tid & 63, n = lane & 31, g = lane >> 5;
-  __shared__ uint4 kt[64 * CPR], vt[64 * CPR];
+  const int wid = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63, n = lane & 31,
+            g = lane >> 5;
+  const int ph = wid & 1, dh = wid >> 1;
+  __shared__ uint4 kt0[64 * CPR], kt1[64 * CPR], vt0[64 * CPR], vt1[64 * CPR];
   __shared__ uint32_t mask[kMaxM][32];
   __shared__ int32_t okl[SPARSEPR_MAX_GROUPS + 1];
-  __shared__ unsigned long long tmask[kMaxM];
-  for (int i = tid; i < kMaxM * 32; i += 128) (&mask[0][0])[i] = 0u;
+  __shared__ unsigned long long tmask[2][kMaxM];
+  for (int i = tid; i < kMaxM * 32; i += 256) (&mask[0][0])[i] = 0u;
   const int32_t* ok = off_k + (long long)h * (c_k + 1);
-  for (int i = tid; i <= c_k; i += 128) okl[i] = ok[i];
+  for (int i = tid; i <= c_k; i += 256) okl[i] = ok[i];
   __syncthreads();
   {
-    const int pp = tid >> 1, half = tid & 1;
+    const int pp = tid >> 2, quarter = tid & 3;
     if (pp < m && probe_rows[(long long)h * m + pp] >= 0) {
       const int grp = probe_group[(long long)h * m + pp];
       const int32_t* rp = rowptr + (long long)h * (c_q + 1);
       const int32_t* cl = col + (long long)h * c_q * c_k;
-      for (int i = rp[grp] + half; i < rp[grp + 1]; i += 2) {
+      for (int i = rp[grp] + quarter; i < rp[grp + 1]; i += 4) {
         const int b = cl[i];
         atomicOr(&mask[pp][b >> 5], 1u << (b & 31));
       }
     }
   }
-  const int p = wid * 32 + n;
+  const int p = ph * 32 + n;
   const bool pvalid = p < m && probe_rows[(long long)h * m + p] >= 0;
   bf16x8_t qf[NS];
   {
@@ -386,68 +394,123 @@ __global__ __launch_bounds__(128) void probe_rows_mfma_kernel(
   }
   const int per = (n_k + kChunks - 1) / kChunks;
   const int k0 = chunk * per, k1 = min(n_k, k0 + per);
-  const char* Kh = reinterpret_cast<const char*>(k_g) + (long long)h * n_k * D * 2;
-  const char* Vh = reinterpret_cast<const char*>(v_g) + (long long)h * n_k * D * 2;
+  const uint32_t head_bytes = uint32_t(n_k) * D * 2;
+  const v4i32_t krs =
+      head_rsrc(reinterpret_cast<const char*>(k_g) + (long long)h * n_k * D * 2, head_bytes);
+  const v4i32_t vrs =
+      head_rsrc(reinterpret_cast<const char*>(v_g) + (long long)h * n_k * D * 2, head_bytes);
   const float NEG = -__builtin_huge_valf();
   const float slack = 8.f / c2;
   float mS = NEG, mU = NEG, zS = 0.f, zU = 0.f;
-  f32x16_t oS[NDB], oU[NDB];
+  f32x16_t oS[NDH], oU[NDH];
 #pragma unroll
-  for (int i = 0; i < NDB; ++i) oS[i] = oU[i] = f32x16_t{};
+  for (int i = 0; i < NDH; ++i) oS[i] = oU[i] = f32x16_t{};
 
-  for (int t0 = k0; t0 < k1; t0 += 64) {
-    __syncthreads();
-    for (int e = tid; e < 64 * CPR; e += 128) {
-      const int r = e / CPR, c = e % CPR;
-      const int row = t0 + r;
-      uint4 kv = make_uint4(0, 0, 0, 0), vv = make_uint4(0, 0, 0, 0);
-      if (row < k1) {
-        kv = *reinterpret_cast<const uint4*>(Kh + (long long)row * D * 2 + c * 16);
-        vv = *reinterpret_cast<const uint4*>(Vh + (long long)row * D * 2 + c * 16);
-      }
-      kt[k_slot<D>(r, c)] = kv;
-      vt[v_slot<D>(r, c)] = vv;
+  // wave w moves tile rows 16 w .. 16 w + 15 of K and of V (rows past the
+  // head's end read as zero; rows past the chunk are masked by `tail`)
+  auto issue = [&](int t0, uint4* kb, uint4* vb) __attribute__((always_inline)) {
+    const int lrow = lane / CPR, lpc = lane % CPR;
+#pragma unroll
+    for (int i = 0; i < 16 / RPI; ++i) {
+      const int r0 = wid * 16 + i * RPI;
+      const int r = r0 + lrow;
+      const uint32_t roff = uint32_t(t0 + r) * (D * 2);
+      lds_dma16(krs, __builtin_amdgcn_readfirstlane(lds_addr_of(kb + r0 * CPR)),
+                roff + (lpc ^ (r & (CPR - 1))) * 16);
+      lds_dma16(vrs, __builtin_amdgcn_readfirstlane(lds_addr_of(vb + r0 * CPR)),
+                roff + (lpc ^ swz_v<D>(r)) * 16);
     }
-    if (tid < kMaxM) {
-      unsigned long long bits = 0ull;
-      if (tid < m && probe_rows[(long long)h * m + tid] >= 0) {
-        const int last = min(t0 + 64, k1) - 1;
-        int lo = 0, hi = c_k - 1;   // group of key t0: largest b with okl[b] <= t0
-        while (lo < hi) {
-          const int mid = (lo + hi + 1) >> 1;
-          if (okl[mid] <= t0) lo = mid;
-          else hi = mid - 1;
-        }
-        for (int b = lo; b < c_k && okl[b] <= last; ++b) {
-          if (!((mask[tid][b >> 5] >> (b & 31)) & 1u)) continue;
-          const int a0 = max(okl[b], t0) - t0, a1 = min(okl[b + 1], last + 1) - t0;
-          if (a1 <= a0) continue;
-          const unsigned long long span = a1 - a0 >= 64 ? ~0ull : ((1ull << (a1 - a0)) - 1ull);
-          bits |= span << a0;
-        }
-      }
-      tmask[tid] = bits;
+  };
+  // retained-key mask of the tile at t0 for probe tid (tid < kMaxM); gb walks
+  // the K/V groups forward (the tiles of a chunk are visited in order)
+  int gb = 0;
+  if (tid < kMaxM) {
+    int lo = 0, hi = c_k - 1;   // group of key k0: largest b with okl[b] <= k0
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (okl[mid] <= k0) lo = mid;
+      else hi = mid - 1;
     }
-    __syncthreads();
+    gb = lo;
+  }
+  auto tile_mask = [&](int t0, unsigned long long* out) __attribute__((always_inline)) {
+    if (tid >= kMaxM) return;
+    unsigned long long bits = 0ull;
+    while (gb < c_k - 1 && okl[gb + 1] <= t0) ++gb;
+    if (tid < m && probe_rows[(long long)h * m + tid] >= 0) {
+      const int last = min(t0 + 64, k1) - 1;
+      for (int b = gb; b < c_k && okl[b] <= last; ++b) {
+        if (!((mask[tid][b >> 5] >> (b & 31)) & 1u)) continue;
+        const int a0 = max(okl[b], t0) - t0, a1 = min(okl[b + 1], last + 1) - t0;
+        if (a1 <= a0) continue;
+        const unsigned long long span = a1 - a0 >= 64 ? ~0ull : ((1ull << (a1 - a0)) - 1ull);
+        bits |= span << a0;
+      }
+    }
+    out[tid] = bits;
+  };
+
+  // Q fragments complete before any tile load is in flight (vmcnt counts both)
+  __builtin_amdgcn_s_waitcnt(0x0F70);
+  __syncthreads();   // group masks complete
+  if (k0 < k1) {
+    issue(k0, kt0, vt0);
+    tile_mask(k0, tmask[0]);
+  }
+  auto step = [&](auto stage, int t0) __attribute__((always_inline)) {
+    constexpr int stg = decltype(stage)::value;
+    // tile t0 in its stage and its masks visible; every wave is past the
+    // previous tile, whose stage now receives the next one
+    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    if (t0 + 64 < k1) {
+      if constexpr (stg == 0) issue(t0 + 64, kt1, vt1);
+      else issue(t0 + 64, kt0, vt0);
+      tile_mask(t0 + 64, tmask[stg ^ 1]);
+    }
+    const uint4* kt = stg == 0 ? kt0 : kt1;
+    const uint4* vt = stg == 0 ? vt0 : vt1;
     f32x16_t s0 = f32x16_t{}, s1 = f32x16_t{};
 #pragma unroll
     for (int s2 = 0; s2 < NS; ++s2) {
       s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k_frag<D>(kt, n, s2, g), qf[s2], s0, 0, 0, 0);
-      s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k_frag<D>(kt, 32 + n, s2, g), qf[s2], s1, 0, 0, 0);
+      s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k_frag<D>(kt, 32 + n, s2, g), qf[s2], s1, 0, 0,
+                                                   0);
     }
-    const unsigned long long bits = tmask[p];
+    // this lane's 16 keys of each 32-key block as a 16-bit retained mask:
+    // keys 8 (r / 4) + 4 g + r % 4 of block 0 and 32 + the same of block 1
+    const unsigned long long bits64 = tmask[stg][p];
+    uint32_t mb0 = 0, mb1 = 0;
+    {
+      const uint32_t lo = uint32_t(bits64) >> (4 * g), hi = uint32_t(bits64 >> 32) >> (4 * g);
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        mb0 |= ((lo >> (8 * q4)) & 0xfu) << (4 * q4);
+        mb1 |= ((hi >> (8 * q4)) & 0xfu) << (4 * q4);
+      }
+    }
     const int tail = k1 - t0;
+    // keys at or past the chunk end take no part: clear them from both classes
+    uint32_t va = 0xffffu, vb_ = 0xffffu;
+    if (tail < 64) {
+      va = 0;
+      vb_ = 0;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        va |= uint32_t(c_key(0, r, g) < tail) << r;
+        vb_ |= uint32_t(c_key(1, r, g) < tail) << r;
+      }
+    }
     float tS = NEG, tU = NEG;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const int ka = c_key(0, r, g), kb = c_key(1, r, g);
-      if (ka < tail) {
-        if ((bits >> ka) & 1ull) tS = fmaxf(tS, s0[r]);
-        else tU = fmaxf(tU, s0[r]);
+      const float xa = s0[r], xb = s1[r];
+      if ((va >> r) & 1u) {
+        if ((mb0 >> r) & 1u) tS = fmaxf(tS, xa);
+        else tU = fmaxf(tU, xa);
       }
-      if (kb < tail) {
-        if ((bits >> kb) & 1ull) tS = fmaxf(tS, s1[r]);
-        else tU = fmaxf(tU, s1[r]);
+      if ((vb_ >> r) & 1u) {
+        if ((mb1 >> r) & 1u) tS = fmaxf(tS, xb);
+        else tU = fmaxf(tU, xb);
       }
     }
     tS = fmaxf(tS, __shfl_xor(tS, 32));
@@ -458,7 +521,7 @@ __global__ __launch_bounds__(128) void probe_rows_mfma_kernel(
       mS = nm;
       zS *= al;
 #pragma unroll
-      for (int db = 0; db < NDB; ++db) oS[db] *= al;
+      for (int db = 0; db < NDH; ++db) oS[db] *= al;
     }
     if (__ballot(tU > mU + slack)) {
       const float nm = fmaxf(mU, tU);
@@ -466,15 +529,18 @@ __global__ __launch_bounds__(128) void probe_rows_mfma_kernel(
       mU = nm;
       zU *= al;
 #pragma unroll
-      for (int db = 0; db < NDB; ++db) oU[db] *= al;
+      for (int db = 0; db < NDH; ++db) oU[db] *= al;
     }
     const float mcS = mS * c2, mcU = mU * c2;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const int ka = c_key(0, r, g), kb = c_key(1, r, g);
-      const bool ia = (bits >> ka) & 1ull, ib = (bits >> kb) & 1ull;
-      const float ea = ka < tail ? __builtin_amdgcn_exp2f(__builtin_fmaf(s0[r], c2, ia ? -mcS : -mcU)) : 0.f;
-      const float eb = kb < tail ? __builtin_amdgcn_exp2f(__builtin_fmaf(s1[r], c2, ib ? -mcS : -mcU)) : 0.f;
+      const bool ia = (mb0 >> r) & 1u, ib = (mb1 >> r) & 1u;
+      const float ea = ((va >> r) & 1u)
+                           ? __builtin_amdgcn_exp2f(__builtin_fmaf(s0[r], c2, ia ? -mcS : -mcU))
+                           : 0.f;
+      const float eb = ((vb_ >> r) & 1u)
+                           ? __builtin_amdgcn_exp2f(__builtin_fmaf(s1[r], c2, ib ? -mcS : -mcU))
+                           : 0.f;
       s0[r] = ea;
       s1[r] = eb;
       zS += ia ? ea : 0.f;
@@ -488,11 +554,10 @@ __global__ __launch_bounds__(128) void probe_rows_mfma_kernel(
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         const int r = 8 * (u & 1) + j;
-        const int kk = c_key(u >> 1, r, g);
         const float e = (u >> 1) ? s1[r] : s0[r];
         const _Float16 eh = static_cast<_Float16>(e);
         const _Float16 el = static_cast<_Float16>(e - float(eh));
-        const bool in = (bits >> kk) & 1ull;
+        const bool in = ((u >> 1) ? (mb1 >> r) : (mb0 >> r)) & 1u;
         const _Float16 z16 = static_cast<_Float16>(0.f);
         sh[j] = in ? eh : z16;
         sl[j] = in ? el : z16;
@@ -500,20 +565,24 @@ __global__ __launch_bounds__(128) void probe_rows_mfma_kernel(
         ul[j] = in ? z16 : el;
       }
 #pragma unroll
-      for (int db = 0; db < NDB; ++db) {
-        const f16x8_t vf = v_frag<D>(vt, lane, u, db);
+      for (int db = 0; db < NDH; ++db) {
+        const f16x8_t vf = v_frag<D>(vt, lane, u, dh * NDH + db);
         oS[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf, sh, oS[db], 0, 0, 0);
         oS[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf, sl, oS[db], 0, 0, 0);
         oU[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf, uh, oU[db], 0, 0, 0);
         oU[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf, ul, oU[db], 0, 0, 0);
       }
     }
+  };
+  for (int t0 = k0; t0 < k1; t0 += 128) {
+    step(std::integral_constant<int, 0>{}, t0);
+    if (t0 + 64 < k1) step(std::integral_constant<int, 1>{}, t0 + 64);
   }
   zS += __shfl_xor(zS, 32);
   zU += __shfl_xor(zU, 32);
   if (p >= m) return;
   const long long rec = ((long long)h * kChunks + chunk) * m + p;
-  if (g == 0) {
+  if (g == 0 && dh == 0) {
     float* ps = part_s + rec * 4;
     ps[0] = mS == NEG ? NEG : mS * c2;
     ps[1] = mU == NEG ? NEG : mU * c2;
@@ -523,10 +592,10 @@ __global__ __launch_bounds__(128) void probe_rows_mfma_kernel(
   const float vs = __builtin_ldexpf(1.f, v_shift[h]);
   float* pn = part_n + rec * 2 * D;
 #pragma unroll
-  for (int db = 0; db < NDB; ++db)
+  for (int db = 0; db < NDH; ++db)
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const int dd = 32 * db + 8 * (r >> 2) + 4 * g + (r & 3);
+      const int dd = 32 * (dh * NDH + db) + 8 * (r >> 2) + 4 * g + (r & 3);
       pn[dd] = oS[db][r] * vs;
       pn[D + dd] = oU[db][r] * vs;
     }
@@ -973,11 +1042,11 @@ extern "C" int32_t sparsepr_probe_fit(const sparsepr_dims* dims, int32_t m, int3
     auto* kk = static_cast<const uint16_t*>(k_g);
     auto* vv = static_cast<const uint16_t*>(v_g);
     if (d == 128)
-      probe_rows_mfma_kernel<128><<<dim3(kChunks, H), 128, 0, stream>>>(
+      probe_rows_mfma_kernel<128><<<dim3(kChunks, H), 256, 0, stream>>>(
           qq, kk, vv, v_shift, offsets_kv, cell_rowptr, cell_col, probe_rows, w.group, dims->n_q,
           dims->n_k, dims->c_q, dims->c_k, m, sl2, w.part_s, w.part_n);
     else
-      probe_rows_mfma_kernel<64><<<dim3(kChunks, H), 128, 0, stream>>>(
+      probe_rows_mfma_kernel<64><<<dim3(kChunks, H), 256, 0, stream>>>(
           qq, kk, vv, v_shift, offsets_kv, cell_rowptr, cell_col, probe_rows, w.group, dims->n_q,
           dims->n_k, dims->c_q, dims->c_k, m, sl2, w.part_s, w.part_n);
   } else {
