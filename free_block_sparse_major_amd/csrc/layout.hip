@@ -181,34 +181,49 @@ __global__ __launch_bounds__(kThreads) void gather_kernel(GatherArgs g) {
   const char* src = g.src[kind] + int64_t(h) * g.stride_head[kind] * g.esize;
   char* dst = g.dst[kind] + (int64_t(h) * n + r0) * g.row_bytes;
   const int64_t st = g.stride_tok[kind] * g.esize;
-  if (kind == 2 && g.vmax) {
+  // a thread owns one 16-byte column chunk of every RPP-th row; the rows of a
+  // block are handled in unrolled batches so several loads are in flight
+  const int rpp = kThreads / chunks;            // rows per pass
+  const int c = threadIdx.x % chunks, rr = threadIdx.x / chunks;
+  constexpr int kUnroll = 4;
+  const bool conv = kind == 2 && g.vmax;
+  float sc = 1.f;
+  if (conv) {
     // values: bf16 -> fp16 after the exact per-head power-of-two scale
     const int sh = v_shift_of(g.vmax[h]);
-    const float sc = __builtin_ldexpf(1.f, -sh);
+    sc = __builtin_ldexpf(1.f, -sh);
     if (blockIdx.x == 0 && threadIdx.x == 0) g.v_shift[h] = sh;
-    for (int i = threadIdx.x; i < rows * chunks; i += kThreads) {
-      int r = i / chunks, c = i - r * chunks;
-      int tok = perm[r0 + r];
-      uint4 v = *reinterpret_cast<const uint4*>(src + tok * st + c * 16);
-      uint32_t w[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const _Float16 lo = static_cast<_Float16>(__uint_as_float(w[j] << 16) * sc);
-        const _Float16 hi = static_cast<_Float16>(__uint_as_float(w[j] & 0xffff0000u) * sc);
-        w[j] = uint32_t(__builtin_bit_cast(uint16_t, lo)) |
-               (uint32_t(__builtin_bit_cast(uint16_t, hi)) << 16);
-      }
-      *reinterpret_cast<uint4*>(dst + int64_t(r) * g.row_bytes + c * 16) =
-          make_uint4(w[0], w[1], w[2], w[3]);
-    }
-    return;
+  } else if (kind == 2 && blockIdx.x == 0 && threadIdx.x == 0 && g.v_shift) {
+    g.v_shift[h] = 0;
   }
-  if (kind == 2 && blockIdx.x == 0 && threadIdx.x == 0 && g.v_shift) g.v_shift[h] = 0;
-  for (int i = threadIdx.x; i < rows * chunks; i += kThreads) {
-    int r = i / chunks, c = i - r * chunks;
-    int tok = perm[r0 + r];
-    uint4 v = *reinterpret_cast<const uint4*>(src + tok * st + c * 16);
-    *reinterpret_cast<uint4*>(dst + int64_t(r) * g.row_bytes + c * 16) = v;
+  for (int r = rr; r < rows; r += kUnroll * rpp) {
+    uint4 v[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const int ru = r + u * rpp;
+      if (ru < rows) {
+        const int tok = perm[r0 + ru];
+        v[u] = *reinterpret_cast<const uint4*>(src + tok * st + c * 16);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const int ru = r + u * rpp;
+      if (ru >= rows) break;
+      uint4 w = v[u];
+      if (conv) {
+        uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const _Float16 lo = static_cast<_Float16>(__uint_as_float(ws[j] << 16) * sc);
+          const _Float16 hi = static_cast<_Float16>(__uint_as_float(ws[j] & 0xffff0000u) * sc);
+          ws[j] = uint32_t(__builtin_bit_cast(uint16_t, lo)) |
+                  (uint32_t(__builtin_bit_cast(uint16_t, hi)) << 16);
+        }
+        w = make_uint4(ws[0], ws[1], ws[2], ws[3]);
+      }
+      *reinterpret_cast<uint4*>(dst + int64_t(ru) * g.row_bytes + c * 16) = w;
+    }
   }
 }
 
@@ -279,7 +294,17 @@ __global__ __launch_bounds__(kThreads) void centroid_kernel(const T* q_g, const 
   const int ch = threadIdx.x % cpr, ph = threadIdx.x / cpr;
   const int lo = off[a], hi = off[a + 1];
   double acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-  for (int r = lo + ph; r < hi; r += phases)
+  // four rows' loads in flight per step; the additions keep row order
+  int r = lo + ph;
+  for (; r + 3 * phases < hi; r += 4 * phases) {
+    uint4 w[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      w[u] = *reinterpret_cast<const uint4*>(x + int64_t(r + u * phases) * d + ch * EPC);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) add_chunk<T>(acc, w[u]);
+  }
+  for (; r < hi; r += phases)
     add_chunk<T>(acc, *reinterpret_cast<const uint4*>(x + int64_t(r) * d + ch * EPC));
 #pragma unroll
   for (int e = 0; e < EPC; ++e) part[threadIdx.x * 8 + e] = acc[e];

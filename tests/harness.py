@@ -178,6 +178,10 @@ def compare_head(w, g, h, r, rows_orig=None, check_rows=True):
         corr_r = r["out"] - r["o_sp"]
         unprobed = ~np.isin(rows, r["probes"])
         errs["correction"] = rel_fro(corr_g[unprobed], corr_r[unprobed])
+        # the correction term on its own (final-output parity cannot see an error in a
+        # correction that is small next to O); looser bound, skipped where it vanishes
+        if np.linalg.norm(corr_r[unprobed]) > 1e-3 * np.linalg.norm(r["o_sp"][unprobed]):
+            assert errs["correction"] <= (1e-2 if w.dtype == "bf16" else 1e-4), errs
         assert errs["o_sp"] <= tol, errs
         assert errs["out"] <= tol, errs
         probed = np.isin(rows, r["probes"])
