@@ -240,8 +240,29 @@ __global__ __launch_bounds__(64 * W, W <= 4 ? 2 : 1) void attn_bf16_kernel(AttnA
   const int sv = p.v_shift[h];
 
   // query fragments: lane holds row n, dims 16s + 8g .. +8
-  const int qloc = wid * 32 + n;
-  const bool wave_active = wid * 32 < nrows;
+  // Row chunk (32 query rows) and key blocks of this wave.  Wave w sits on
+  // SIMD w % 4.  With 9 or 10 busy chunks in a 12-wave item, two SIMDs would
+  // carry three busy waves and two SIMDs only two; instead the idle waves take
+  // a share of the 32-key blocks of chunks 8 and 9 (disjoint per wave, the
+  // same rows), so every SIMD carries the same work per tile, and the partial
+  // softmax states are merged at the end.
+  const int nb = (nrows + 31) / 32;
+  int chunk = wid;
+  uint32_t kmask = (1u << (KT / 32)) - 1u;
+  int merge_slot = -1;   // helpers: slot of their partial state
+  if constexpr (W >= 12 && KT == 128) {
+    if (nb == 9 && wid >= 8) {
+      chunk = 8;
+      kmask = 1u << (wid - 8);
+      merge_slot = wid - 9;
+    } else if (nb == 10 && wid >= 8) {
+      chunk = 8 + (wid & 1);
+      kmask = wid < 10 ? 0x5u : 0xau;
+      merge_slot = wid - 10;
+    }
+  }
+  const int qloc = chunk * 32 + n;
+  const bool wave_active = chunk * 32 < nrows;
   const bool row_valid = qloc < nrows;
   bf16x8_t qf[NS];
   {
@@ -509,11 +530,11 @@ __global__ __launch_bounds__(64 * W, W <= 4 ? 2 : 1) void attn_bf16_kernel(AttnA
     const uint4* kb_ = B == 0 ? k_s0 : k_s1;
     const uint4* vb = B == 0 ? v_s0 : v_s1;
     const int tail = L - t * KT;
-    compute_half(kb_, vb, 0, tail);
+    if (kmask & 1u) compute_half(kb_, vb, 0, tail);
     if (t + 1 < ntiles) issue_tile(Stage<1 - B>{}, t + 1);
 #pragma unroll
     for (int hq = 1; hq < KT / 32; ++hq)
-      if (tail > 32 * hq) compute_half(kb_, vb, hq, tail);
+      if (((kmask >> hq) & 1u) && tail > 32 * hq) compute_half(kb_, vb, hq, tail);
   };
 
   // Two-stage pipeline with one barrier per tile: after the barrier of step
@@ -541,6 +562,51 @@ __global__ __launch_bounds__(64 * W, W <= 4 ? 2 : 1) void attn_bf16_kernel(AttnA
   for (int t = 0; t < ntiles; t += 2) {
     step(Stage<0>{}, t);
     if (t + 1 < ntiles) step(Stage<1>{}, t + 1);
+  }
+
+  if constexpr (W >= 12 && KT == 128) {
+    if (nb == 9 || nb == 10) {
+      // helpers park (O, m, l) in the free K/V stages, one slot each, value
+      // j of lane l at j * 64 + l; the owner of the chunk folds them in
+      constexpr int NV = NDB * 16 + 2;
+      static_assert(NV * 64 * 4 <= KT / 8 * D * 16, "merge slot fits a stage");
+      auto slot = [&](int i) -> float* {
+        return reinterpret_cast<float*>(i == 0 ? k_s0 : (i == 1 ? k_s1 : v_s0));
+      };
+      __syncthreads();
+      if (merge_slot >= 0) {
+        float* sl = slot(merge_slot);
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) sl[(db * 16 + r) * 64 + lane] = oacc[db][r];
+        sl[(NDB * 16) * 64 + lane] = m_run;
+        sl[(NDB * 16 + 1) * 64 + lane] = l_run;
+      }
+      __syncthreads();
+      if (merge_slot >= 0) return;
+      if (chunk == 8 || chunk == 9) {
+        const int first = nb == 9 ? 0 : (chunk - 8);
+        const int count = nb == 9 ? 3 : 1;
+        for (int si = first; si < first + count; ++si) {
+          const float* sl = slot(si);
+          const float mh = sl[(NDB * 16) * 64 + lane], lh = sl[(NDB * 16 + 1) * 64 + lane];
+          const float mn = fmaxf(m_run, mh);
+          const float a0 = m_run == -__builtin_huge_valf()
+                               ? 0.f
+                               : __builtin_amdgcn_exp2f((m_run - mn) * c2);
+          const float a1 =
+              mh == -__builtin_huge_valf() ? 0.f : __builtin_amdgcn_exp2f((mh - mn) * c2);
+#pragma unroll
+          for (int db = 0; db < NDB; ++db)
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+              oacc[db][r] = oacc[db][r] * a0 + sl[(db * 16 + r) * 64 + lane] * a1;
+          l_run = l_run * a0 + lh * a1;
+          m_run = mn;
+        }
+      }
+    }
   }
 
   if (!row_valid) return;
