@@ -281,48 +281,75 @@ __global__ __launch_bounds__(64 * W, W <= 4 ? 2 : 1) void attn_bf16_kernel(AttnA
 
   // loader: wave load i of wave w covers tile rows RPI*(w + i*W) .. +RPI.
   // tc (wave-uniform) is a cell with cpos[tc] <= the tile's first stream
-  // position.  One batch of independent LDS reads fetches the next four cell
-  // boundaries and row deltas; each lane counts the boundaries at or below
-  // its position (a tile rarely spans more than four cells; beyond that the
-  // lane walks on), so no chain of dependent LDS reads sits on the issue
-  // path and no per-lane state is carried between tiles.
+  // position.  One LDS read fetches the next four cell ends (lanes 0-3) and
+  // the row deltas of cells tc..tc+3 (lanes 4-7); they are broadcast to
+  // scalars.  A wave load whose RPI rows lie in one cell (the common case) is
+  // a scalar base plus a per-lane offset fixed for the whole kernel (with W a
+  // multiple of 4, a wave's load rows have the same residue mod 16, so the
+  // chunk swizzles below do not change from load to load).  A load that
+  // straddles a cell end or the stream's end takes the per-lane path: each
+  // lane counts the window boundaries at or below its position (walking on
+  // past the window if needed).
+  static_assert(W % 4 == 0, "per-lane load offsets assume W % 4 == 0");
   int tc = 0;
+  const int lrow0 = lane / CPR, lpc0 = lane % CPR;
+  const int lrow_w = wid * RPI + lrow0;                       // a load row of this wave
+  const uint32_t voff_k = uint32_t(lrow0 * RB + ((lpc0 ^ (lrow_w & (CPR - 1))) * 16));
+  const uint32_t voff_v = uint32_t(lrow0 * RB + ((lpc0 ^ swz_v<D>(lrow_w)) * 16));
   auto issue_tile = [&](auto stage, int t) __attribute__((always_inline)) {
     constexpr int B = decltype(stage)::value;
     uint4* kbase = B == 0 ? k_s0 : k_s1;
     uint4* vbase = B == 0 ? v_s0 : v_s1;
     const int t0 = t * KT;
+    int wv;
+    {
+      const int j = lane & 3;
+      wv = (lane & 4) ? sm.cstart[min(tc + j, nc - 1)] : sm.cpos[min(tc + 1 + j, nc)];
+    }
     int e[4], dl[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      e[j] = __builtin_amdgcn_readfirstlane(sm.cpos[min(tc + 1 + j, nc)]);
-      dl[j] = __builtin_amdgcn_readfirstlane(sm.cstart[min(tc + j, nc - 1)]);
+      e[j] = __builtin_amdgcn_readlane(wv, j);
+      dl[j] = __builtin_amdgcn_readlane(wv, 4 + j);
     }
-    // lane-derived terms recomputed per issue rather than held across the loop
-    int ln = lane;
-    asm volatile("" : "+v"(ln));
-    const int lrow = ln / CPR, lpc = ln % CPR;
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
       const int blk = wid + i * W;                        // wave-uniform
       if (NL % W != 0 && blk >= NL) break;
-      const int row = blk * RPI + lrow;                   // tile row of this lane
-      int pos = t0 + row;
-      pos = pos < L ? pos : L - 1;                        // tail rows: any valid row
-      const int k = int(e[0] <= pos) + int(e[1] <= pos) + int(e[2] <= pos) + int(e[3] <= pos);
-      int delta = k == 0 ? dl[0] : (k == 1 ? dl[1] : (k == 2 ? dl[2] : dl[3]));
-      if (k == 4) {
-        int c = tc + 4;
-        while (pos >= sm.cpos[c + 1]) ++c;
-        delta = sm.cstart[c];
-      }
-      const uint32_t roff = uint32_t(pos + delta) * RB;
-      const int kc = lpc ^ (row & (CPR - 1));
-      const int vc = lpc ^ swz_v<D>(row);
       uint4* kdst = kbase + blk * RPI * CPR;
       uint4* vdst = vbase + blk * RPI * CPR;
-      lds_dma16(krs, __builtin_amdgcn_readfirstlane(lds_addr_of(kdst)), roff + kc * 16);
-      lds_dma16(vrs, __builtin_amdgcn_readfirstlane(lds_addr_of(vdst)), roff + vc * 16);
+      const uint32_t lk = __builtin_amdgcn_readfirstlane(lds_addr_of(kdst));
+      const uint32_t lv = __builtin_amdgcn_readfirstlane(lds_addr_of(vdst));
+      const int p0 = t0 + blk * RPI;                       // first stream position
+      const int k0 = int(e[0] <= p0) + int(e[1] <= p0) + int(e[2] <= p0) + int(e[3] <= p0);
+      const int en = k0 == 0 ? e[0] : (k0 == 1 ? e[1] : (k0 == 2 ? e[2] : e[3]));
+      if (p0 + RPI <= en) {
+        // all rows in cell tc + k0 (en <= L, so none past the stream's end)
+        const int d0 = k0 == 0 ? dl[0] : (k0 == 1 ? dl[1] : (k0 == 2 ? dl[2] : dl[3]));
+        const uint32_t soff = uint32_t(p0 + d0) * RB;
+        lds_dma16_s(krs, lk, voff_k, soff);
+        lds_dma16_s(vrs, lv, voff_v, soff);
+      } else {
+        // lane-derived terms recomputed here rather than held across the loop
+        int ln = lane;
+        asm volatile("" : "+v"(ln));
+        const int lrow = ln / CPR, lpc = ln % CPR;
+        const int row = blk * RPI + lrow;                  // tile row of this lane
+        int pos = t0 + row;
+        pos = pos < L ? pos : L - 1;                       // tail rows: any valid row
+        const int k = int(e[0] <= pos) + int(e[1] <= pos) + int(e[2] <= pos) + int(e[3] <= pos);
+        int delta = k == 0 ? dl[0] : (k == 1 ? dl[1] : (k == 2 ? dl[2] : dl[3]));
+        if (k == 4) {
+          int c = tc + 4;
+          while (pos >= sm.cpos[c + 1]) ++c;
+          delta = sm.cstart[c];
+        }
+        const uint32_t roff = uint32_t(pos + delta) * RB;
+        const int kc = lpc ^ (row & (CPR - 1));
+        const int vc = lpc ^ swz_v<D>(row);
+        lds_dma16(krs, lk, roff + kc * 16);
+        lds_dma16(vrs, lv, roff + vc * 16);
+      }
     }
     // cells that end at or before the next tile's first position
     const int t1 = t0 + KT;
@@ -336,6 +363,7 @@ __global__ __launch_bounds__(64 * W, W <= 4 ? 2 : 1) void attn_bf16_kernel(AttnA
   float m_run = -__builtin_huge_valf(), l_run = 0.f;
   const float c2 = p.scale_log2;
   const float slack = kRescaleSlack / c2;   // in raw score units
+  float m_thr = -__builtin_huge_valf();      // m_run + slack
   const f16x2_t ones = {static_cast<_Float16>(1.f), static_cast<_Float16>(1.f)};
 
   // transposed-read addressing (fixed per lane): group G, index i in group
@@ -448,13 +476,16 @@ __global__ __launch_bounds__(64 * W, W <= 4 ? 2 : 1) void attn_bf16_kernel(AttnA
     float mloc = -__builtin_huge_valf();
 #pragma unroll
     for (int i = 0; i < 16; ++i) mloc = fmaxf(mloc, fmaxf(sacc0[i], sacc1[i]));
-    mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
     // lazy rescale: keep the old reference max unless the tile exceeds it by
-    // more than the slack (exact either way: O and l share the reference)
-    if (__ballot(mloc > m_run + slack)) {
+    // more than the slack (exact either way: O and l share the reference).
+    // A row exceeds iff one of its two lanes does, so the partner exchange
+    // is only needed on the (rare) rescale.
+    if (__ballot(mloc > m_thr)) {
+      mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
       const float m_new = fmaxf(m_run, mloc);
       const float alpha = __builtin_amdgcn_exp2f((m_run - m_new) * c2);
       m_run = m_new;
+      m_thr = m_run + slack;
       l_run *= alpha;
 #pragma unroll
       for (int db = 0; db < NDB; ++db) oacc[db] *= alpha;
@@ -501,11 +532,12 @@ __global__ __launch_bounds__(64 * W, W <= 4 ? 2 : 1) void attn_bf16_kernel(AttnA
     float mloc = -__builtin_huge_valf();
 #pragma unroll
     for (int i = 0; i < 16; ++i) mloc = fmaxf(mloc, sacc[i]);
-    mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
-    if (__ballot(mloc > m_run + slack)) {
+    if (__ballot(mloc > m_thr)) {
+      mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
       const float m_new = fmaxf(m_run, mloc);
       const float alpha = __builtin_amdgcn_exp2f((m_run - m_new) * c2);
       m_run = m_new;
+      m_thr = m_run + slack;
       l_run *= alpha;
 #pragma unroll
       for (int db = 0; db < NDB; ++db) oacc[db] *= alpha;

@@ -43,6 +43,28 @@ SPR_DEV void lds_dma16(const v4i32_t& rsrc_in, uint32_t lds_addr, uint32_t voff)
       : "memory");
 }
 
+// As lds_dma16, with a wave-uniform byte offset `soff` (SGPR) added to the
+// per-lane offset: a load whose rows share one scalar base needs no per-lane
+// address arithmetic.
+SPR_DEV void lds_dma16_s(const v4i32_t& rsrc_in, uint32_t lds_addr, uint32_t voff, uint32_t soff) {
+  v4i32_t rsrc;
+  rsrc[0] = __builtin_amdgcn_readfirstlane(rsrc_in[0]);
+  rsrc[1] = __builtin_amdgcn_readfirstlane(rsrc_in[1]);
+  rsrc[2] = __builtin_amdgcn_readfirstlane(rsrc_in[2]);
+  rsrc[3] = __builtin_amdgcn_readfirstlane(rsrc_in[3]);
+  const uint32_t so = __builtin_amdgcn_readfirstlane(soff);
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %2, %3, %4 offen lds\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(lds_addr), "v"(voff), "s"(rsrc), "s"(so)
+      : "memory");
+}
+
 SPR_DEV uint32_t lds_addr_of(const void* p) {
   return uint32_t(reinterpret_cast<size_t>(
       (const __attribute__((address_space(3))) void*)(p)));
