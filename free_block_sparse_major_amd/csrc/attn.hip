@@ -193,9 +193,11 @@ SPR_DEV int swz_v(int row) {
 typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
 
 
-// log2-domain growth of the running max tolerated before O and l are rescaled
-// (P then stays below 2^8, well inside fp16)
-constexpr float kRescaleSlack = 8.f;
+// Lazy rescale: P is formed against the running reference max and the row is
+// rescaled to a new reference only when a lane's sum of its P values in the
+// block exceeds this cap (every P above it, and any overflow to inf, implies
+// that).  P therefore stays at or below 2^8, well inside fp16.
+constexpr float kPSumCap = 256.f;
 
 template <int D, int W>
 __global__ __launch_bounds__(64 * W, W <= 4 ? 2 : 1) void attn_bf16_kernel(AttnArgs p) {
@@ -362,8 +364,7 @@ __global__ __launch_bounds__(64 * W, W <= 4 ? 2 : 1) void attn_bf16_kernel(AttnA
   for (int i = 0; i < NDB; ++i) oacc[i] = f32x16_t{};
   float m_run = -__builtin_huge_valf(), l_run = 0.f;
   const float c2 = p.scale_log2;
-  const float slack = kRescaleSlack / c2;   // in raw score units
-  float m_thr = -__builtin_huge_valf();      // m_run + slack
+  float mc_run = -__builtin_huge_valf();     // m_run * c2
   const f16x2_t ones = {static_cast<_Float16>(1.f), static_cast<_Float16>(1.f)};
 
   // transposed-read addressing (fixed per lane): group G, index i in group
@@ -473,39 +474,42 @@ __global__ __launch_bounds__(64 * W, W <= 4 ? 2 : 1) void attn_bf16_kernel(AttnA
         if (kk + 32 >= tail) sacc1[i] = -__builtin_huge_valf();
       }
     }
-    float mloc = -__builtin_huge_valf();
+    // P against the reference max, and this lane's share of the row sum (of
+    // the rounded P, the values the PV product uses)
+    f16x8_t pf[4];
+    float lsum;
+    auto form_p = [&]() __attribute__((always_inline)) {
 #pragma unroll
-    for (int i = 0; i < 16; ++i) mloc = fmaxf(mloc, fmaxf(sacc0[i], sacc1[i]));
-    // lazy rescale: keep the old reference max unless the tile exceeds it by
-    // more than the slack (exact either way: O and l share the reference).
-    // A row exceeds iff one of its two lanes does, so the partner exchange
-    // is only needed on the (rare) rescale.
-    if (__ballot(mloc > m_thr)) {
+      for (int i = 0; i < 16; ++i) {
+        pf[i >> 3][i & 7] = static_cast<_Float16>(
+            __builtin_amdgcn_exp2f(__builtin_fmaf(sacc0[i], c2, -mc_run)));
+        pf[2 + (i >> 3)][i & 7] = static_cast<_Float16>(
+            __builtin_amdgcn_exp2f(__builtin_fmaf(sacc1[i], c2, -mc_run)));
+      }
+      lsum = 0.f;
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int j = 0; j < 8; j += 2)
+          lsum = __builtin_amdgcn_fdot2(f16x2_t{pf[u][j], pf[u][j + 1]}, ones, lsum, false);
+    };
+    form_p();
+    // rescale (rare): the row's new reference is the larger of the old one and
+    // the block's max over both lanes of the row; O and l follow, P is formed again
+    if (__ballot(!(lsum <= kPSumCap))) {
+      float mloc = -__builtin_huge_valf();
+#pragma unroll
+      for (int i = 0; i < 16; ++i) mloc = fmaxf(mloc, fmaxf(sacc0[i], sacc1[i]));
       mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
       const float m_new = fmaxf(m_run, mloc);
       const float alpha = __builtin_amdgcn_exp2f((m_run - m_new) * c2);
       m_run = m_new;
-      m_thr = m_run + slack;
+      mc_run = m_run * c2;
       l_run *= alpha;
 #pragma unroll
       for (int db = 0; db < NDB; ++db) oacc[db] *= alpha;
+      form_p();
     }
-    const float mc = m_run * c2;
-    f16x8_t pf[4];
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      pf[i >> 3][i & 7] = static_cast<_Float16>(
-          __builtin_amdgcn_exp2f(__builtin_fmaf(sacc0[i], c2, -mc)));
-      pf[2 + (i >> 3)][i & 7] = static_cast<_Float16>(
-          __builtin_amdgcn_exp2f(__builtin_fmaf(sacc1[i], c2, -mc)));
-    }
-    // row sum of the rounded P (the values the PV product uses)
-    float lsum = 0.f;
-#pragma unroll
-    for (int u = 0; u < 4; ++u)
-#pragma unroll
-      for (int j = 0; j < 8; j += 2)
-        lsum = __builtin_amdgcn_fdot2(f16x2_t{pf[u][j], pf[u][j + 1]}, ones, lsum, false);
     l_run += lsum;
     // u outer, d blocks inner: NDB independent accumulation chains interleave
     const int vb0 = vbase0;
@@ -529,31 +533,35 @@ __global__ __launch_bounds__(64 * W, W <= 4 ? 2 : 1) void attn_bf16_kernel(AttnA
       for (int i = 0; i < 16; ++i)
         if (32 * kbi + 8 * (i >> 2) + 4 * g + (i & 3) >= tail) sacc[i] = -__builtin_huge_valf();
     }
-    float mloc = -__builtin_huge_valf();
+    f16x8_t pf[2];
+    float lsum;
+    auto form_p = [&]() __attribute__((always_inline)) {
 #pragma unroll
-    for (int i = 0; i < 16; ++i) mloc = fmaxf(mloc, sacc[i]);
-    if (__ballot(mloc > m_thr)) {
+      for (int i = 0; i < 16; ++i)
+        pf[i >> 3][i & 7] = static_cast<_Float16>(
+            __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[i], c2, -mc_run)));
+      lsum = 0.f;
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int j = 0; j < 8; j += 2)
+          lsum = __builtin_amdgcn_fdot2(f16x2_t{pf[u][j], pf[u][j + 1]}, ones, lsum, false);
+    };
+    form_p();
+    if (__ballot(!(lsum <= kPSumCap))) {
+      float mloc = -__builtin_huge_valf();
+#pragma unroll
+      for (int i = 0; i < 16; ++i) mloc = fmaxf(mloc, sacc[i]);
       mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
       const float m_new = fmaxf(m_run, mloc);
       const float alpha = __builtin_amdgcn_exp2f((m_run - m_new) * c2);
       m_run = m_new;
-      m_thr = m_run + slack;
+      mc_run = m_run * c2;
       l_run *= alpha;
 #pragma unroll
       for (int db = 0; db < NDB; ++db) oacc[db] *= alpha;
+      form_p();
     }
-    const float mc = m_run * c2;
-    f16x8_t pf[2];
-#pragma unroll
-    for (int i = 0; i < 16; ++i)
-      pf[i >> 3][i & 7] = static_cast<_Float16>(
-          __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[i], c2, -mc)));
-    float lsum = 0.f;
-#pragma unroll
-    for (int u = 0; u < 2; ++u)
-#pragma unroll
-      for (int j = 0; j < 8; j += 2)
-        lsum = __builtin_amdgcn_fdot2(f16x2_t{pf[u][j], pf[u][j + 1]}, ones, lsum, false);
     l_run += lsum;
     pv_pipe(vb, 2 * kbi, std::integral_constant<int, 2>{}, std::integral_constant<int, 4>{}, pf);
   };
