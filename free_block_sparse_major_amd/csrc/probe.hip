@@ -707,7 +707,7 @@ __global__ __launch_bounds__(256) void fit_kernel(FitArgs f) {
   __shared__ double red[4];
   __shared__ double tcol[kMaxM];
   __shared__ int32_t sh_k;
-  __shared__ int32_t sh_rot;
+  __shared__ int32_t sh_rot, sh_big;
 
   const double* X = f.xp + (long long)h * f.m * d;
   const double* R = f.rp + (long long)h * f.m * d;
@@ -796,9 +796,26 @@ __global__ __launch_bounds__(256) void fit_kernel(FitArgs f) {
   // 6. cyclic Jacobi on E with round-robin disjoint pairs (pair table per
   // round in LDS; thread t works on pair t/8, columns t%8 + 8l).  A rotation
   // is skipped when |a_pq| is negligible next to the diagonal and next to the
-  // trace (the Gram route resolves eigenvalues to ~1e-16 of the trace); the
-  // iteration stops after a sweep without rotations.
+  // trace (the Gram route resolves eigenvalues to ~1e-16 of the trace).  The
+  // iteration stops after a sweep without rotations, or after a sweep in
+  // which every rotation had |a_pq| below 1e-8 sqrt(a_pp a_qq) or below
+  // 1e-10 of the trace: convergence is quadratic, so what the next sweep
+  // would rotate is at the rounding level of the trace.  Rotation parameters use the hardware reciprocal / reciprocal
+  // square root refined by two Newton steps (about an ulp; c^2 + s^2 = 1 to
+  // rounding).
   {
+    auto rcp64 = [](double y) {
+      double r = __builtin_amdgcn_rcp(y);
+      r = r * fma(-y, r, 2.0);
+      r = r * fma(-y, r, 2.0);
+      return r;
+    };
+    auto rsq64 = [](double y) {
+      double r = __builtin_amdgcn_rsq(y);
+      r = r * fma(-0.5 * y * r, r, 1.5);
+      r = r * fma(-0.5 * y * r, r, 1.5);
+      return r;
+    };
     double trp = 0.0;
     for (int i = tid; i < me; i += 256) trp += fabs(E[i * kLd + i]);
     const double tr = block_sum(trp, red);
@@ -807,7 +824,10 @@ __global__ __launch_bounds__(256) void fit_kernel(FitArgs f) {
     const int npair = mp / 2;
     const int pi = tid >> 3, cj = tid & 7;
     for (int sweep = 0; sweep < 20; ++sweep) {
-      if (tid == 0) sh_rot = 0;
+      if (tid == 0) {
+        sh_rot = 0;
+        sh_big = 0;
+      }
       for (int rnd = 0; rnd < mp - 1; ++rnd) {
         if (tid < npair) {
           int pp, qq;
@@ -820,12 +840,15 @@ __global__ __launch_bounds__(256) void fit_kernel(FitArgs f) {
           if (pp < me && qq < me) {
             const double apq = E[pp * kLd + qq];
             const double app = E[pp * kLd + pp], aqq = E[qq * kLd + qq];
-            if (fabs(apq) > 1e-15 * sqrt(fabs(app * aqq)) && fabs(apq) > abs_floor) {
-              const double tau = (aqq - app) / (2.0 * apq);
-              const double t = (tau >= 0 ? 1.0 : -1.0) / (fabs(tau) + sqrt(1.0 + tau * tau));
-              c = 1.0 / sqrt(1.0 + t * t);
+            const double apq2 = apq * apq, dd = fabs(app * aqq);
+            if (apq2 > 1e-30 * dd && fabs(apq) > abs_floor) {
+              const double tau = (aqq - app) * rcp64(2.0 * apq);
+              const double u = fma(tau, tau, 1.0);
+              const double t = (tau >= 0 ? 1.0 : -1.0) * rcp64(fabs(tau) + u * rsq64(u));
+              c = rsq64(fma(t, t, 1.0));
               sn = t * c;
               sh_rot = 1;
+              if (apq2 > 1e-16 * dd && fabs(apq) > 1e-10 * tr) sh_big = 1;
             }
           }
           rc[tid] = c;
@@ -855,7 +878,7 @@ __global__ __launch_bounds__(256) void fit_kernel(FitArgs f) {
           }
         __syncthreads();
       }
-      if (!sh_rot) break;
+      if (!sh_rot || !sh_big) break;
       __syncthreads();
     }
   }
