@@ -45,6 +45,9 @@ __all__ = [
     "position_code",
     "f32_to_bf16_bits",
     "bf16_bits_to_f32",
+    "RCP_PARAMS",
+    "rcp_init",
+    "rcp_init_arrays",
 ]
 
 
@@ -93,7 +96,16 @@ WORKLOADS = {
     # HunyuanVideo-like 720p, 129 frames -> 33 x 45 x 80 tokens
     "hunyuan": Workload("hunyuan", heads=24, n=118800, head_dim=128, dtype="bf16",
                         components=256, kv_split=4, grid=(33, 45, 80), rho="0.26", seed=3),
+    # the Wan-like call with the partition built from the activations
+    # (response-coupled partitioning); the mixture labels are not used
+    "wan_rcp": Workload("wan_rcp", heads=40, n=75600, head_dim=128, dtype="bf16",
+                        components=256, kv_split=4, grid=(21, 45, 80), rho="0.22", seed=4),
 }
+
+# Response-coupled partitioning settings of the pages' full pipeline: M_s
+# sampled query rows, coordinate ranks r_K / r_Q, Lloyd iterations; the
+# requested group counts are the workload's C_k and C_q.
+RCP_PARAMS = {"m_s": 256, "r_k": 48, "r_q": 64, "iters": 10}
 
 
 def workload(name: str) -> Workload:
@@ -286,3 +298,23 @@ def make_call_arrays(w: Workload, variant: str = "default", threads: Optional[in
     with cf.ThreadPoolExecutor(nt) as ex:
         list(ex.map(work, range(nt)))
     return {"q": q, "k": k, "v": v, "labels_q": lq, "labels_kv": lk}
+
+
+def rcp_init(w: Workload, h: int):
+    """Initial k-means centre indices of head h for response-coupled
+    partitioning: C_k then C_q token indices drawn uniformly with replacement
+    from numpy PCG64(SeedSequence([seed, h, 1])) (a stream of its own, so the
+    activation draws are unchanged)."""
+    g = np.random.Generator(np.random.PCG64(np.random.SeedSequence([w.seed, h, 1])))
+    init_k = g.integers(0, w.n, size=w.c_k, dtype=np.int64).astype(np.int32)
+    init_q = g.integers(0, w.n, size=w.c_q, dtype=np.int64).astype(np.int32)
+    return init_k, init_q
+
+
+def rcp_init_arrays(w: Workload):
+    """rcp_init for every head: int32 [H, C_k] and [H, C_q]."""
+    ik = np.empty((w.heads, w.c_k), np.int32)
+    iq = np.empty((w.heads, w.c_q), np.int32)
+    for h in range(w.heads):
+        ik[h], iq[h] = rcp_init(w, h)
+    return ik, iq
