@@ -23,11 +23,13 @@ LIB_PATH = os.path.join(HERE, "libsparsepr.so")
 
 OK, ERR_INVALID, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = range(5)
 BF16, F32 = 0, 1
-CALL_PARTITION_LAYOUT, CALL_ROUTE_CELLS, CALL_SPARSE_ATTN, CALL_PROBE_FIT, CALL_CORRECT = range(5)
+(CALL_PARTITION_LAYOUT, CALL_ROUTE_CELLS, CALL_SPARSE_ATTN, CALL_PROBE_FIT, CALL_CORRECT,
+ CALL_RCP_PARTITION, CALL_PROBE_FIT_FEAT) = range(7)
 EXPORTED = (
     "sparsepr_partition_layout", "sparsepr_route_cells", "sparsepr_sparse_attn",
     "sparsepr_probe_fit", "sparsepr_correct", "sparsepr_workspace_bytes",
-    "sparsepr_status_string", "sparsepr_version",
+    "sparsepr_status_string", "sparsepr_version", "sparsepr_rcp_partition",
+    "sparsepr_probe_fit_feat",
 )
 
 
@@ -76,6 +78,11 @@ def load_library(path: str = LIB_PATH):
     lib.sparsepr_probe_fit.restype = I32
     lib.sparsepr_correct.argtypes = [DP, I32, I32] + [P] * 8 + [I32, I64, I64, P, SZ, P]
     lib.sparsepr_correct.restype = I32
+    lib.sparsepr_rcp_partition.argtypes = [DP, I32, I32, I32, I32] + [P] * 8 + [P, SZ, P]
+    lib.sparsepr_rcp_partition.restype = I32
+    lib.sparsepr_probe_fit_feat.argtypes = ([DP, I32, I32, D] + [P] * 6 + [I32] + [P] * 4
+                                            + [ctypes.c_float] + [P] * 7 + [P, SZ, P])
+    lib.sparsepr_probe_fit_feat.restype = I32
     _lib = lib
     return lib
 
@@ -164,6 +171,54 @@ def sparsepr_correct(dims, m, rank, perm_q, o_sp, probe_tokens, o_probe_dense, c
     _check(st, "sparsepr_correct")
 
 
+def sparsepr_rcp_partition(dims, m_s, r_k, r_q, iters, q, k, init_q, init_k, labels_q,
+                           labels_kv, phi_q, phi_k, ws, stream=None):
+    st = load_library().sparsepr_rcp_partition(
+        ctypes.byref(dims), int(m_s), int(r_k), int(r_q), int(iters), _ptr(q), _ptr(k),
+        _ptr(init_q), _ptr(init_k), _ptr(labels_q), _ptr(labels_kv), _ptr(phi_q), _ptr(phi_k),
+        _ptr(ws), ws.numel() * ws.element_size() if ws is not None else 0, _stream(stream))
+    _check(st, "sparsepr_rcp_partition")
+
+
+def sparsepr_probe_fit_feat(dims, m, rank, lam, offsets_q, offsets_kv, perm_q, cell_rowptr,
+                            cell_col, probe_feat, feat_dim, q_g, k_g, v_g, v_shift, softmax_scale,
+                            probe_rows, probe_tokens, o_probe_dense, o_probe_sparse, corr_a,
+                            corr_psi_t, corr_c, ws, stream=None):
+    st = load_library().sparsepr_probe_fit_feat(
+        ctypes.byref(dims), int(m), int(rank), float(lam), _ptr(offsets_q), _ptr(offsets_kv),
+        _ptr(perm_q), _ptr(cell_rowptr), _ptr(cell_col), _ptr(probe_feat), int(feat_dim),
+        _ptr(q_g), _ptr(k_g), _ptr(v_g), _ptr(v_shift), ctypes.c_float(softmax_scale),
+        _ptr(probe_rows), _ptr(probe_tokens), _ptr(o_probe_dense), _ptr(o_probe_sparse),
+        _ptr(corr_a), _ptr(corr_psi_t), _ptr(corr_c),
+        _ptr(ws), ws.numel() * ws.element_size() if ws is not None else 0, _stream(stream))
+    _check(st, "sparsepr_probe_fit_feat")
+
+
+class RcpPartition:
+    """Buffers for sparsepr_rcp_partition of one shape: labels_q, labels_kv
+    (int32 [H][N]), phi_q (fp32 [H][N_q][r_q]) and optionally phi_k."""
+
+    def __init__(self, heads, n_q, n_k, head_dim, dtype, c_q, c_k, m_s=256, r_k=48, r_q=64,
+                 iters=10, device="cuda", q_strides=None, kv_strides=None, keep_phi_k=False):
+        load_library()
+        self.dims = make_dims(heads, n_q, n_k, head_dim, dtype, c_q, c_k, q_strides, kv_strides)
+        self.m_s, self.r_k, self.r_q, self.iters = m_s, r_k, r_q, iters
+        dev = torch.device(device)
+        self.labels_q = torch.empty(heads, n_q, dtype=torch.int32, device=dev)
+        self.labels_kv = torch.empty(heads, n_k, dtype=torch.int32, device=dev)
+        self.phi_q = torch.empty(heads, n_q, r_q, dtype=torch.float32, device=dev)
+        self.phi_k = (torch.empty(heads, n_k, r_k, dtype=torch.float32, device=dev)
+                      if keep_phi_k else None)
+        nb = workspace_bytes(CALL_RCP_PARTITION, self.dims)
+        self.ws = torch.empty(max(nb, 256), dtype=torch.uint8, device=dev)
+
+    def __call__(self, q, k, init_q, init_k, stream=None):
+        sparsepr_rcp_partition(self.dims, self.m_s, self.r_k, self.r_q, self.iters, q, k, init_q,
+                               init_k, self.labels_q, self.labels_kv, self.phi_q, self.phi_k,
+                               self.ws, stream)
+        return self.labels_q, self.labels_kv
+
+
 # ----------------------------------------------------------------------------
 # budget (host, exact rational) and the chained call
 # ----------------------------------------------------------------------------
@@ -183,7 +238,7 @@ class SparsePRCall:
 
     def __init__(self, heads, n_q, n_k, head_dim, dtype, c_q, c_k, m=64, rank=16, lam=0.1,
                  rho="0.26", budget=None, out_dtype=F32, device="cuda", q_strides=None,
-                 kv_strides=None, overlap=True):
+                 kv_strides=None, overlap=True, feat_dim=0):
         load_library()
         self.dims = make_dims(heads, n_q, n_k, head_dim, dtype, c_q, c_k, q_strides, kv_strides)
         self.m, self.rank, self.lam = m, rank, lam
@@ -191,6 +246,10 @@ class SparsePRCall:
         self.scale = 1.0 / math.sqrt(head_dim)
         self.out_dtype = out_dtype
         self.overlap = overlap
+        # probe features (response-coupled partitions): set self.probe_feat to
+        # an fp32 [H][N_q][feat_dim] tensor before the call
+        self.feat_dim = int(feat_dim)
+        self.probe_feat = None
         H, d = heads, head_dim
         dev = torch.device(device)
         tdt = torch.bfloat16 if dtype == BF16 else torch.float32
@@ -228,7 +287,7 @@ class SparsePRCall:
         self.ws_layout = ws(CALL_PARTITION_LAYOUT)
         self.ws_route = ws(CALL_ROUTE_CELLS)
         self.ws_attn = ws(CALL_SPARSE_ATTN)
-        self.ws_probe = ws(CALL_PROBE_FIT)
+        self.ws_probe = ws(CALL_PROBE_FIT_FEAT if feat_dim else CALL_PROBE_FIT)
         self.side = torch.cuda.Stream(device=dev) if overlap else None
         self.ev_routed = torch.cuda.Event()
         self.ev_fit = torch.cuda.Event()
@@ -253,6 +312,16 @@ class SparsePRCall:
                              self.lse, self.ws_attn, stream)
 
     def probe_fit(self, stream=None):
+        if self.feat_dim:
+            if self.probe_feat is None:
+                raise SparsePRError("probe_feat is not set")
+            sparsepr_probe_fit_feat(self.dims, self.m, self.rank, self.lam, self.offsets_q,
+                                    self.offsets_kv, self.perm_q, self.cell_rowptr, self.cell_col,
+                                    self.probe_feat, self.feat_dim, self.q_g, self.k_g, self.v_g,
+                                    self.v_shift, self.scale, self.probe_rows, self.probe_tokens,
+                                    self.o_probe_dense, self.o_probe_sparse, self.corr_a,
+                                    self.corr_psi_t, self.corr_c, self.ws_probe, stream)
+            return
         sparsepr_probe_fit(self.dims, self.m, self.rank, self.lam, self.offsets_q,
                            self.offsets_kv, self.perm_q, self.cell_rowptr, self.cell_col,
                            self.centroid_q, self.q_g, self.k_g, self.v_g, self.v_shift,

@@ -328,6 +328,27 @@ size_t layout_ws_bytes(const sparsepr_dims* d) {
   return cv.used;
 }
 
+// Stable counting sort of labels[H][n] in [0, c) (the layout's own sort):
+// perm[h][j] = token of group-major row j, offsets[h][c+1].  ws holds the
+// per-tile counts.
+size_t group_sort_ws_bytes(int heads, int n, int c) {
+  const int ntiles = (n + kTile - 1) / kTile;
+  return (size_t(heads) * c * ntiles * sizeof(int32_t) + 255) & ~size_t(255);
+}
+
+int32_t group_sort(const int32_t* labels, int heads, int n, int c, int32_t* perm,
+                   int32_t* offsets, void* ws, hipStream_t stream) {
+  const int ntiles = (n + kTile - 1) / kTile;
+  KindArgs a{labels, perm, offsets, static_cast<int32_t*>(ws), n, c, ntiles};
+  hist_kernel<<<dim3(ntiles, heads, 1), kThreads, 0, stream>>>(a, a, nullptr, heads);
+  SPR_LAUNCH_CHECK();
+  scan_kernel<<<dim3(heads, 1), 1024, 0, stream>>>(a, a);
+  SPR_LAUNCH_CHECK();
+  scatter_kernel<<<dim3(ntiles, heads, 1), kThreads, 0, stream>>>(a, a);
+  SPR_LAUNCH_CHECK();
+  return SPARSEPR_OK;
+}
+
 }  // namespace spr
 
 using namespace spr;

@@ -971,6 +971,30 @@ __global__ __launch_bounds__(256) void fit_kernel(FitArgs f) {
   }
 }
 
+// Probe features of a response-coupled partition: rows of `feat` (token
+// order) copied to group-major order and their fp64 mean per group (row
+// order), so the select kernel measures distances in that space.  One wave
+// per group, lane j = feature j.
+__global__ __launch_bounds__(64) void feat_group_kernel(const float* __restrict__ feat,
+                                                        const int32_t* __restrict__ perm_q,
+                                                        const int32_t* __restrict__ off_q,
+                                                        int n_q, int c_q, int fd,
+                                                        float* __restrict__ feat_g,
+                                                        double* __restrict__ feat_cen) {
+  const int a = blockIdx.x, h = blockIdx.y, j = threadIdx.x;
+  if (j >= fd) return;
+  const int32_t* o = off_q + (long long)h * (c_q + 1);
+  const int lo = o[a], hi = o[a + 1];
+  const int32_t* pr = perm_q + (long long)h * n_q;
+  double s = 0.0;
+  for (int r = lo; r < hi; ++r) {
+    const float v = feat[((long long)h * n_q + pr[r]) * fd + j];
+    feat_g[((long long)h * n_q + r) * fd + j] = v;
+    s += double(v);
+  }
+  feat_cen[((long long)h * c_q + a) * fd + j] = hi > lo ? s / double(hi - lo) : 0.0;
+}
+
 struct ProbeWs {
   int32_t *m_a, *rank, *s_tab, *group;
   double* dist;
@@ -1023,31 +1047,41 @@ size_t probe_ws_bytes(const sparsepr_dims* d, int32_t m, int32_t rank) {
   return cv.used;
 }
 
+// probe_ws_bytes plus group-major feature rows and fp64 feature centroids
+// (feature dimension up to SPARSEPR_MAX_RANK)
+size_t probe_feat_ws_bytes(const sparsepr_dims* d, int32_t m, int32_t rank) {
+  Carver cv(nullptr);
+  const size_t H = d->heads;
+  cv.take<float>(H * d->n_q * SPARSEPR_MAX_RANK);
+  cv.take<double>(H * d->c_q * SPARSEPR_MAX_RANK);
+  return probe_ws_bytes(d, m, rank) + cv.used;
+}
+
 }  // namespace spr
 
 using namespace spr;
 
-extern "C" int32_t sparsepr_probe_fit(const sparsepr_dims* dims, int32_t m, int32_t rank,
-                                      double lambda, const int32_t* offsets_q,
-                                      const int32_t* offsets_kv, const int32_t* perm_q,
-                                      const int32_t* cell_rowptr, const int32_t* cell_col,
-                                      const double* centroid_q, const void* q_g, const void* k_g,
-                                      const void* v_g, const int32_t* v_shift,
-                                      float softmax_scale, int32_t* probe_rows,
-                                      int32_t* probe_tokens, float* o_probe_dense,
-                                      float* o_probe_sparse, float* corr_a, float* corr_psi_t,
-                                      float* corr_c, void* ws, size_t ws_bytes,
-                                      hipStream_t stream) {
+namespace {
+int32_t probe_fit_impl(const sparsepr_dims* dims, int32_t m, int32_t rank, double lambda,
+                       const int32_t* offsets_q, const int32_t* offsets_kv, const int32_t* perm_q,
+                       const int32_t* cell_rowptr, const int32_t* cell_col,
+                       const double* centroid_q, const float* feat, int32_t fd, const void* q_g,
+                       const void* k_g, const void* v_g, const int32_t* v_shift,
+                       float softmax_scale, int32_t* probe_rows, int32_t* probe_tokens,
+                       float* o_probe_dense, float* o_probe_sparse, float* corr_a,
+                       float* corr_psi_t, float* corr_c, void* ws, size_t ws_bytes,
+                       hipStream_t stream) {
   int32_t st = check_dims(dims);
   if (st != SPARSEPR_OK) return st;
   if (m < 1 || m > SPARSEPR_MAX_PROBES || rank < 0 || rank > SPARSEPR_MAX_RANK || !(lambda >= 0.0))
     return SPARSEPR_ERR_INVALID;
-  if (!offsets_q || !offsets_kv || !perm_q || !cell_rowptr || !cell_col || !centroid_q || !q_g ||
+  if (feat ? (fd < 1 || fd > SPARSEPR_MAX_RANK) : !centroid_q) return SPARSEPR_ERR_INVALID;
+  if (!offsets_q || !offsets_kv || !perm_q || !cell_rowptr || !cell_col || !q_g ||
       !k_g || !v_g || !v_shift || !probe_rows || !probe_tokens || !o_probe_dense || !corr_a || !corr_psi_t ||
       !corr_c)
     return SPARSEPR_ERR_INVALID;
   if (rank > 0 && lambda == 0.0) return SPARSEPR_ERR_INVALID;  // dual solve needs lam > 0
-  const size_t need = probe_ws_bytes(dims, m, rank);
+  const size_t need = feat ? probe_feat_ws_bytes(dims, m, rank) : probe_ws_bytes(dims, m, rank);
   if (!ws || ws_bytes < need) return SPARSEPR_ERR_WORKSPACE;
   ProbeWs w = carve_probe(ws, dims, m);
   const int H = dims->heads, d = dims->head_dim;
@@ -1056,11 +1090,26 @@ extern "C" int32_t sparsepr_probe_fit(const sparsepr_dims* dims, int32_t m, int3
                                       probe_rows, probe_tokens, w.group);
   SPR_LAUNCH_CHECK();
   const float sl2 = softmax_scale * kLog2e;
-  if (dims->dtype == SPARSEPR_BF16) {
-    select_kernel<uint16_t><<<dim3(dims->c_q, H), 256, 0, stream>>>(
-        static_cast<const uint16_t*>(q_g), centroid_q, offsets_q, perm_q, w.m_a, w.rank, w.s_tab,
-        dims->n_q, dims->c_q, d, m, w.dist, probe_rows, probe_tokens, w.group);
+  if (feat) {
+    // feature rows and centroids after the standard workspace
+    Carver cv(static_cast<char*>(ws) + probe_ws_bytes(dims, m, rank));
+    float* feat_g = cv.take<float>(size_t(H) * dims->n_q * fd);
+    double* feat_cen = cv.take<double>(size_t(H) * dims->c_q * fd);
+    feat_group_kernel<<<dim3(dims->c_q, H), 64, 0, stream>>>(feat, perm_q, offsets_q, dims->n_q,
+                                                             dims->c_q, fd, feat_g, feat_cen);
     SPR_LAUNCH_CHECK();
+    select_kernel<float><<<dim3(dims->c_q, H), 256, 0, stream>>>(
+        feat_g, feat_cen, offsets_q, perm_q, w.m_a, w.rank, w.s_tab, dims->n_q, dims->c_q, fd, m,
+        w.dist, probe_rows, probe_tokens, w.group);
+    SPR_LAUNCH_CHECK();
+  }
+  if (dims->dtype == SPARSEPR_BF16) {
+    if (!feat) {
+      select_kernel<uint16_t><<<dim3(dims->c_q, H), 256, 0, stream>>>(
+          static_cast<const uint16_t*>(q_g), centroid_q, offsets_q, perm_q, w.m_a, w.rank,
+          w.s_tab, dims->n_q, dims->c_q, d, m, w.dist, probe_rows, probe_tokens, w.group);
+      SPR_LAUNCH_CHECK();
+    }
     auto* qq = static_cast<const uint16_t*>(q_g);
     auto* kk = static_cast<const uint16_t*>(k_g);
     auto* vv = static_cast<const uint16_t*>(v_g);
@@ -1073,10 +1122,12 @@ extern "C" int32_t sparsepr_probe_fit(const sparsepr_dims* dims, int32_t m, int3
           qq, kk, vv, v_shift, offsets_kv, cell_rowptr, cell_col, probe_rows, w.group, dims->n_q,
           dims->n_k, dims->c_q, dims->c_k, m, sl2, w.part_s, w.part_n);
   } else {
-    select_kernel<float><<<dim3(dims->c_q, H), 256, 0, stream>>>(
-        static_cast<const float*>(q_g), centroid_q, offsets_q, perm_q, w.m_a, w.rank, w.s_tab,
-        dims->n_q, dims->c_q, d, m, w.dist, probe_rows, probe_tokens, w.group);
-    SPR_LAUNCH_CHECK();
+    if (!feat) {
+      select_kernel<float><<<dim3(dims->c_q, H), 256, 0, stream>>>(
+          static_cast<const float*>(q_g), centroid_q, offsets_q, perm_q, w.m_a, w.rank, w.s_tab,
+          dims->n_q, dims->c_q, d, m, w.dist, probe_rows, probe_tokens, w.group);
+      SPR_LAUNCH_CHECK();
+    }
     auto* qq = static_cast<const float*>(q_g);
     auto* kk = static_cast<const float*>(k_g);
     auto* vv = static_cast<const float*>(v_g);
@@ -1116,4 +1167,37 @@ extern "C" int32_t sparsepr_probe_fit(const sparsepr_dims* dims, int32_t m, int3
   fit_kernel<<<H, 256, 0, stream>>>(fa);
   SPR_LAUNCH_CHECK();
   return SPARSEPR_OK;
+}
+}  // namespace
+
+extern "C" int32_t sparsepr_probe_fit(const sparsepr_dims* dims, int32_t m, int32_t rank,
+                                      double lambda, const int32_t* offsets_q,
+                                      const int32_t* offsets_kv, const int32_t* perm_q,
+                                      const int32_t* cell_rowptr, const int32_t* cell_col,
+                                      const double* centroid_q, const void* q_g, const void* k_g,
+                                      const void* v_g, const int32_t* v_shift,
+                                      float softmax_scale, int32_t* probe_rows,
+                                      int32_t* probe_tokens, float* o_probe_dense,
+                                      float* o_probe_sparse, float* corr_a, float* corr_psi_t,
+                                      float* corr_c, void* ws, size_t ws_bytes,
+                                      hipStream_t stream) {
+  return probe_fit_impl(dims, m, rank, lambda, offsets_q, offsets_kv, perm_q, cell_rowptr,
+                        cell_col, centroid_q, nullptr, 0, q_g, k_g, v_g, v_shift, softmax_scale,
+                        probe_rows, probe_tokens, o_probe_dense, o_probe_sparse, corr_a,
+                        corr_psi_t, corr_c, ws, ws_bytes, stream);
+}
+
+extern "C" int32_t sparsepr_probe_fit_feat(
+    const sparsepr_dims* dims, int32_t m, int32_t rank, double lambda, const int32_t* offsets_q,
+    const int32_t* offsets_kv, const int32_t* perm_q, const int32_t* cell_rowptr,
+    const int32_t* cell_col, const float* probe_feat, int32_t feat_dim, const void* q_g,
+    const void* k_g, const void* v_g, const int32_t* v_shift, float softmax_scale,
+    int32_t* probe_rows, int32_t* probe_tokens, float* o_probe_dense, float* o_probe_sparse,
+    float* corr_a, float* corr_psi_t, float* corr_c, void* ws, size_t ws_bytes,
+    hipStream_t stream) {
+  if (!probe_feat) return SPARSEPR_ERR_INVALID;
+  return probe_fit_impl(dims, m, rank, lambda, offsets_q, offsets_kv, perm_q, cell_rowptr,
+                        cell_col, nullptr, probe_feat, feat_dim, q_g, k_g, v_g, v_shift,
+                        softmax_scale, probe_rows, probe_tokens, o_probe_dense, o_probe_sparse,
+                        corr_a, corr_psi_t, corr_c, ws, ws_bytes, stream);
 }

@@ -1,0 +1,640 @@
+// Response-coupled partitioning: the query and key/value groups of one
+// attention call, built from its own activations.
+//
+// SparsePR paper §4.1 (key-response coordinates for paired K/V groups,
+// query-response coordinates from K/V groups), App. B.1 (key response
+// metric), App. B.2 (query response metric, RMS normalisation with floor
+// 1e-6) and App. C.1 (clustering on the GPU, initial centres sampled from
+// the feature rows; metric construction, centroid statistics and the
+// factorisation in FP32).  Per head:
+//   1. M_K = Q_s^T Q_s / M_s over M_s evenly spaced query rows (fp32).
+//   2. F_K: the leading r_K eigenvectors of M_K (cyclic Jacobi in fp32), each
+//      scaled by the square root of its eigenvalue over the mean of the r_K
+//      retained (eigenvalues clamped at 0).
+//   3. phi_K = k F_K, held as a bf16 pair (hi = bf16(phi), lo = bf16(phi - hi)).
+//   4. Lloyd's k-means with C_k centres started at the rows init_k: the
+//      assignment is an MFMA product |c|^2 - 2 x.c with x.c taken as
+//      hi.hi + hi.lo + lo.hi (fp32 accumulation), ties to the smaller centre;
+//      the update is each cluster's mean in row order after a stable counting
+//      sort of the labels (an empty cluster keeps its centre).  The labels
+//      are those of the last assignment.
+//   5. K/V group centroids in the original key space (fp32, row order), their
+//      mean over the non-empty groups subtracted: M_Q = K~^T K~ / C_nonempty.
+//   6. F_Q from M_Q as in 2 (r_Q); phi_Q = u / max(RMS(u), 1e-6), u = q F_Q.
+//   7. k-means on phi_Q with C_q centres from init_q -> query labels.
+
+#include "common.h"
+
+namespace spr {
+
+size_t group_sort_ws_bytes(int heads, int n, int c);
+int32_t group_sort(const int32_t* labels, int heads, int n, int c, int32_t* perm,
+                   int32_t* offsets, void* ws, hipStream_t stream);
+
+namespace {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+
+constexpr int kMaxR = 64;          // padded coordinate rank (multiple of 16)
+constexpr int kMetricRows = 32;    // rows staged per metric step
+
+SPR_DEV float load_elem(const void* x, int dtype, long long off) {
+  return dtype == SPARSEPR_BF16 ? bf16_to_f32(static_cast<const uint16_t*>(x)[off])
+                                : static_cast<const float*>(x)[off];
+}
+
+// ---------------------------------------------------------------------------
+// metrics
+// ---------------------------------------------------------------------------
+// Thread t owns entries (a, b) with b = t % D and a = t / D + (256 / D) i; the
+// sum over rows runs in row order.
+template <int D>
+SPR_DEV void metric_accumulate(float (&xs)[kMetricRows][D + 1], int rows, float* acc) {
+  constexpr int NE = D * D / 256, AS = 256 / D;
+  const int b = threadIdx.x % D, a0 = threadIdx.x / D;
+  for (int rr = 0; rr < rows; ++rr) {
+    const float xb = xs[rr][b];
+#pragma unroll
+    for (int i = 0; i < NE; ++i) acc[i] = fmaf(xs[rr][a0 + AS * i], xb, acc[i]);
+  }
+}
+
+template <int D>
+SPR_DEV void metric_store(const float* acc, float scale, float* m) {
+  constexpr int NE = D * D / 256, AS = 256 / D;
+  const int b = threadIdx.x % D, a0 = threadIdx.x / D;
+#pragma unroll
+  for (int i = 0; i < NE; ++i) m[(a0 + AS * i) * D + b] = acc[i] * scale;
+}
+
+// M_K of head blockIdx.x from rows floor(i * n / m_s) of q (every row if n <= m_s).
+template <int D>
+__global__ __launch_bounds__(256) void key_metric_kernel(const void* q, int dtype, long long sh,
+                                                         long long st, int n, int m_s,
+                                                         float* __restrict__ mk) {
+  const int h = blockIdx.x;
+  __shared__ float xs[kMetricRows][D + 1];
+  const int ms = n < m_s ? n : m_s;
+  float acc[D * D / 256];
+#pragma unroll
+  for (int i = 0; i < D * D / 256; ++i) acc[i] = 0.f;
+  for (int r0 = 0; r0 < ms; r0 += kMetricRows) {
+    __syncthreads();
+    for (int e = threadIdx.x; e < kMetricRows * D; e += 256) {
+      const int rr = e / D, j = e % D, i = r0 + rr;
+      float v = 0.f;
+      if (i < ms) {
+        const long long row = n <= m_s ? i : (long long)i * n / m_s;
+        v = load_elem(q, dtype, h * sh + row * st + j);
+      }
+      xs[rr][j] = v;
+    }
+    __syncthreads();
+    metric_accumulate<D>(xs, min(kMetricRows, ms - r0), acc);
+  }
+  metric_store<D>(acc, 1.f / float(ms), mk + (long long)h * D * D);
+}
+
+// M_Q of head blockIdx.x from the K/V group centroids (empty groups skipped).
+template <int D>
+__global__ __launch_bounds__(256) void query_metric_kernel(const float* __restrict__ cent,
+                                                           const int32_t* __restrict__ offsets,
+                                                           int c, float* __restrict__ mq) {
+  const int h = blockIdx.x;
+  __shared__ float xs[kMetricRows][D + 1];
+  __shared__ int32_t nzl[SPARSEPR_MAX_GROUPS];
+  __shared__ float mu[D];
+  __shared__ int32_t s_nnz;
+  const int32_t* off = offsets + (long long)h * (c + 1);
+  const float* ce = cent + (long long)h * c * D;
+  {
+    // non-empty groups in ascending order: 4 groups per thread, block scan
+    __shared__ long long red[4];
+    const int b0 = 4 * threadIdx.x;
+    bool ne[4];
+    long long cnt = 0;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      ne[u] = b0 + u < c && off[b0 + u + 1] > off[b0 + u];
+      cnt += ne[u] ? 1 : 0;
+    }
+    long long tot;
+    long long pos = block_exclusive_scan(cnt, red, &tot);
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      if (ne[u]) nzl[pos++] = b0 + u;
+    if (threadIdx.x == 0) s_nnz = int(tot);
+  }
+  __syncthreads();
+  const int nnz = s_nnz;
+  if (threadIdx.x < D) {
+    float s = 0.f;
+    for (int i = 0; i < nnz; ++i) s += ce[(long long)nzl[i] * D + threadIdx.x];
+    mu[threadIdx.x] = s / float(nnz);
+  }
+  float acc[D * D / 256];
+#pragma unroll
+  for (int i = 0; i < D * D / 256; ++i) acc[i] = 0.f;
+  for (int r0 = 0; r0 < nnz; r0 += kMetricRows) {
+    __syncthreads();
+    for (int e = threadIdx.x; e < kMetricRows * D; e += 256) {
+      const int rr = e / D, j = e % D, i = r0 + rr;
+      xs[rr][j] = i < nnz ? ce[(long long)nzl[i] * D + j] - mu[j] : 0.f;
+    }
+    __syncthreads();
+    metric_accumulate<D>(xs, min(kMetricRows, nnz - r0), acc);
+  }
+  metric_store<D>(acc, 1.f / float(nnz > 0 ? nnz : 1), mq + (long long)h * D * D);
+}
+
+// ---------------------------------------------------------------------------
+// eigenvalue-weighted factor (cyclic Jacobi, fp32)
+// ---------------------------------------------------------------------------
+// Round-robin disjoint pairs, D/2 per round; thread t works on pair
+// t / (256 / (D/2)) and every (256 / (D/2))-th column.  A rotation is skipped
+// when |a_pq| is at the fp32 rounding level of the diagonal or of the trace;
+// the iteration stops after a sweep without rotations (at most 40 sweeps).
+// Output F[h] (D x rp, row-major): column c < r is the eigenvector of the
+// c-th largest eigenvalue (ties to the smaller index) times
+// sqrt(max(lambda, 0) / mean of the r retained); columns r..rp-1 are 0.
+template <int D>
+__global__ __launch_bounds__(256) void eig_factor_kernel(const float* __restrict__ m, int r, int rp,
+                                                         float* __restrict__ f) {
+  constexpr int NP = D / 2, PER = 256 / NP, NCOL = D / PER;
+  const int h = blockIdx.x, tid = threadIdx.x;
+  __shared__ float E[D][D + 1];
+  __shared__ float U[D][D + 1];
+  __shared__ float rc[NP], rs[NP];
+  __shared__ int32_t pr_p[NP], pr_q[NP];
+  __shared__ int32_t order[D];
+  __shared__ float red[4];
+  __shared__ float s_scale;
+  __shared__ int32_t sh_rot;
+  const float* mh = m + (long long)h * D * D;
+  for (int e = tid; e < D * D; e += 256) {
+    const int i = e / D, j = e % D;
+    E[i][j] = mh[e];
+    U[i][j] = i == j ? 1.f : 0.f;
+  }
+  __syncthreads();
+  float trp = 0.f;
+  for (int i = tid; i < D; i += 256) trp += fabsf(E[i][i]);
+  const float tr = block_sum(trp, red);
+  const float abs_floor = 1e-30f + 4e-7f * tr;   // above the fp32 rounding noise of the trace
+  const int pi = tid / PER, cj = tid % PER;
+  for (int sweep = 0; sweep < 40; ++sweep) {
+    if (tid == 0) sh_rot = 0;
+    for (int rnd = 0; rnd < D - 1; ++rnd) {
+      if (tid < NP) {
+        int pp, qq;
+        if (tid == 0) {
+          pp = D - 1;
+          qq = rnd;
+        } else {
+          pp = rnd + tid;
+          pp -= pp >= D - 1 ? D - 1 : 0;
+          qq = rnd - tid;
+          qq += qq < 0 ? D - 1 : 0;
+        }
+        float c = 1.f, sn = 0.f;
+        const float apq = E[pp][qq], app = E[pp][pp], aqq = E[qq][qq];
+        if (fabsf(apq) > 2e-7f * sqrtf(fabsf(app * aqq)) && fabsf(apq) > abs_floor) {
+          const float tau = (aqq - app) / (2.f * apq);
+          const float t = (tau >= 0.f ? 1.f : -1.f) / (fabsf(tau) + sqrtf(1.f + tau * tau));
+          c = 1.f / sqrtf(1.f + t * t);
+          sn = t * c;
+          sh_rot = 1;
+        }
+        rc[tid] = c;
+        rs[tid] = sn;
+        pr_p[tid] = pp;
+        pr_q[tid] = qq;
+      }
+      __syncthreads();
+      const bool act = rs[pi] != 0.f;
+      const float ci = rc[pi], si = rs[pi];
+      const int p2 = pr_p[pi], q2 = pr_q[pi];
+      if (act)
+#pragma unroll 4
+        for (int l = 0; l < NCOL; ++l) {   // rows: E <- J^T E
+          const int j = cj + PER * l;
+          const float x1 = E[p2][j], x2 = E[q2][j];
+          E[p2][j] = ci * x1 - si * x2;
+          E[q2][j] = si * x1 + ci * x2;
+        }
+      __syncthreads();
+      if (act)
+#pragma unroll 4
+        for (int l = 0; l < NCOL; ++l) {   // columns: E <- E J, U <- U J
+          const int j = cj + PER * l;
+          const float x1 = E[j][p2], x2 = E[j][q2];
+          E[j][p2] = ci * x1 - si * x2;
+          E[j][q2] = si * x1 + ci * x2;
+          const float u1 = U[j][p2], u2 = U[j][q2];
+          U[j][p2] = ci * u1 - si * u2;
+          U[j][q2] = si * u1 + ci * u2;
+        }
+      __syncthreads();
+    }
+    if (!sh_rot) break;
+    __syncthreads();
+  }
+  // rank of each eigenvalue: descending, ties to the smaller index
+  if (tid < D) {
+    const float li = E[tid][tid];
+    int rk = 0;
+    for (int j = 0; j < D; ++j) {
+      const float lj = E[j][j];
+      rk += (lj > li || (lj == li && j < tid)) ? 1 : 0;
+    }
+    order[rk] = tid;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    float s = 0.f;
+    for (int c = 0; c < r; ++c) s += fmaxf(E[order[c]][order[c]], 0.f);
+    s_scale = s / float(r);
+  }
+  __syncthreads();
+  const float mean = s_scale;
+  float* fh = f + (long long)h * D * rp;
+  for (int e = tid; e < D * rp; e += 256) {
+    const int j = e / rp, c = e % rp;
+    float v = 0.f;
+    if (c < r && mean > 0.f) {
+      const int ii = order[c];
+      v = U[j][ii] * sqrtf(fmaxf(E[ii][ii], 0.f) / mean);
+    }
+    fh[e] = v;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// projection (phi = x F, optionally RMS-normalised) and its bf16 pair
+// ---------------------------------------------------------------------------
+// 64 rows per block; thread t: row t / 4, columns 16 (t % 4) .. +16.
+template <int D>
+__global__ __launch_bounds__(256) void project_kernel(const void* x, int dtype, long long sh,
+                                                      long long st, int n,
+                                                      const float* __restrict__ f, int r, int rp,
+                                                      int rms, uint16_t* __restrict__ hi,
+                                                      uint16_t* __restrict__ lo,
+                                                      float* __restrict__ out) {
+  const int h = blockIdx.y, row0 = blockIdx.x * 64, tid = threadIdx.x;
+  __shared__ float fs[D][kMaxR];
+  __shared__ float xs[64][D + 1];
+  const float* fh = f + (long long)h * D * rp;
+  for (int e = tid; e < D * kMaxR; e += 256) {
+    const int j = e / kMaxR, c = e % kMaxR;
+    fs[j][c] = c < rp ? fh[j * rp + c] : 0.f;
+  }
+  for (int e = tid; e < 64 * D; e += 256) {
+    const int rr = e / D, j = e % D, i = row0 + rr;
+    xs[rr][j] = i < n ? load_elem(x, dtype, h * sh + (long long)i * st + j) : 0.f;
+  }
+  __syncthreads();
+  const int rr = tid >> 2, c0 = (tid & 3) * 16;
+  float acc[16];
+#pragma unroll
+  for (int c = 0; c < 16; ++c) acc[c] = 0.f;
+  for (int j = 0; j < D; ++j) {
+    const float xv = xs[rr][j];
+#pragma unroll
+    for (int c = 0; c < 16; ++c) acc[c] = fmaf(xv, fs[j][c0 + c], acc[c]);
+  }
+  float scale = 1.f;
+  if (rms) {
+    float ss = 0.f;
+#pragma unroll
+    for (int c = 0; c < 16; ++c) ss += c0 + c < r ? acc[c] * acc[c] : 0.f;
+    ss += __shfl_xor(ss, 1);
+    ss += __shfl_xor(ss, 2);
+    scale = 1.f / fmaxf(sqrtf(ss / float(r)), 1e-6f);
+  }
+  const int i = row0 + rr;
+  if (i >= n) return;
+  const long long o = ((long long)h * n + i) * rp;
+#pragma unroll
+  for (int c = 0; c < 16; ++c) {
+    const int col = c0 + c;
+    if (col < rp) {
+      const float v = acc[c] * scale;
+      const uint16_t bh = f32_to_bf16_rne(v);
+      hi[o + col] = bh;
+      lo[o + col] = f32_to_bf16_rne(v - bf16_to_f32(bh));
+      if (out && col < r) out[((long long)h * n + i) * r + col] = v;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// k-means
+// ---------------------------------------------------------------------------
+// Centre c of head h as fp32 (cent), bf16 pair and |c|^2 (fp32, wave sum).
+template <int RP>
+SPR_DEV void store_center(int h, int c, int C, float v, float* cent, uint16_t* chi, uint16_t* clo,
+                          float* cnorm) {
+  const int lane = threadIdx.x & 63;
+  const long long o = ((long long)h * C + c) * RP;
+  float sq = 0.f;
+  if (lane < RP) {
+    cent[o + lane] = v;
+    const uint16_t bh = f32_to_bf16_rne(v);
+    chi[o + lane] = bh;
+    clo[o + lane] = f32_to_bf16_rne(v - bf16_to_f32(bh));
+    sq = v * v;
+  }
+  sq = wave_sum(sq);
+  if (lane == 0) cnorm[(long long)h * C + c] = sq;
+}
+
+// Initial centres: the feature rows init[h][c] (hi + lo).  One wave per centre.
+template <int RP>
+__global__ __launch_bounds__(256) void kmeans_init_kernel(const uint16_t* __restrict__ xh,
+                                                          const uint16_t* __restrict__ xl, int n,
+                                                          const int32_t* __restrict__ init, int C,
+                                                          float* cent, uint16_t* chi,
+                                                          uint16_t* clo, float* cnorm) {
+  const int h = blockIdx.y, c = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
+  if (c >= C) return;
+  int row = init[(long long)h * C + c];
+  row = row < 0 ? 0 : (row >= n ? n - 1 : row);   // out-of-range indices are clamped
+  float v = 0.f;
+  if (lane < RP) {
+    const long long o = ((long long)h * n + row) * RP + lane;
+    v = bf16_to_f32(xh[o]) + bf16_to_f32(xl[o]);
+  }
+  store_center<RP>(h, c, C, v, cent, chi, clo, cnorm);
+}
+
+// Update: mean of each cluster's rows in row order (perm/offsets from the
+// stable sort of the labels); an empty cluster keeps its centre.
+template <int RP>
+__global__ __launch_bounds__(256) void kmeans_update_kernel(
+    const int32_t* __restrict__ perm, const int32_t* __restrict__ offsets,
+    const uint16_t* __restrict__ xh, const uint16_t* __restrict__ xl, int n, int C, float* cent,
+    uint16_t* chi, uint16_t* clo, float* cnorm) {
+  const int h = blockIdx.y, c = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
+  if (c >= C) return;
+  const int32_t* off = offsets + (long long)h * (C + 1);
+  const int b0 = off[c], b1 = off[c + 1];
+  const int32_t* pr = perm + (long long)h * n;
+  float v = 0.f;
+  if (lane < RP) {
+    if (b1 > b0) {
+      float s = 0.f;
+      for (int j = b0; j < b1; ++j) {
+        const long long o = ((long long)h * n + pr[j]) * RP + lane;
+        s += bf16_to_f32(xh[o]) + bf16_to_f32(xl[o]);
+      }
+      v = s / float(b1 - b0);
+    } else {
+      v = cent[((long long)h * C + c) * RP + lane];
+    }
+  }
+  store_center<RP>(h, c, C, v, cent, chi, clo, cnorm);
+}
+
+// Assignment: label = argmin_c |c|^2 - 2 x.c, ties to the smaller c.  Block =
+// 4 waves x 32 rows; centres pass through LDS 128 at a time (rows padded by
+// 16 bytes, so the 16 rows read by one 16-lane group hit distinct banks).
+// S^T tile = C_tile X^T on v_mfma_f32_32x32x16_bf16: lane l owns row l % 32
+// and 16 centres of each 32-centre block.
+constexpr int kCenterTile = 128;
+template <int RP>
+__global__ __launch_bounds__(256) void kmeans_assign_kernel(
+    const uint16_t* __restrict__ xh, const uint16_t* __restrict__ xl, int n,
+    const uint16_t* __restrict__ chi, const uint16_t* __restrict__ clo,
+    const float* __restrict__ cnorm, int C, int32_t* __restrict__ labels) {
+  constexpr int NS = RP / 16, LD = RP + 8;   // k-steps, LDS row length (bf16)
+  const int h = blockIdx.y, tid = threadIdx.x, wid = tid >> 6, lane = tid & 63;
+  const int nl = lane & 31, g = lane >> 5;
+  __shared__ __attribute__((aligned(16))) uint16_t sh[kCenterTile * LD];
+  __shared__ __attribute__((aligned(16))) uint16_t sl[kCenterTile * LD];
+  __shared__ float sn[kCenterTile];
+  const int row = blockIdx.x * 128 + wid * 32 + nl;
+  bf16x8_t bh[NS], bl[NS];
+  {
+    const long long o = ((long long)h * n + (row < n ? row : 0)) * RP;
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      const uint4 a = row < n ? *reinterpret_cast<const uint4*>(xh + o + 16 * s + 8 * g)
+                              : make_uint4(0, 0, 0, 0);
+      const uint4 b = row < n ? *reinterpret_cast<const uint4*>(xl + o + 16 * s + 8 * g)
+                              : make_uint4(0, 0, 0, 0);
+      bh[s] = __builtin_bit_cast(bf16x8_t, a);
+      bl[s] = __builtin_bit_cast(bf16x8_t, b);
+    }
+  }
+  float best = __builtin_huge_valf();
+  int bi = 0;   // a valid label even if no candidate compares below +inf (NaN input)
+  const uint16_t* ch = chi + (long long)h * C * RP;
+  const uint16_t* cl = clo + (long long)h * C * RP;
+  const float* cn = cnorm + (long long)h * C;
+  for (int t0 = 0; t0 < C; t0 += kCenterTile) {
+    __syncthreads();
+    for (int e = tid; e < kCenterTile * (RP / 8); e += 256) {
+      const int cc = e / (RP / 8), ch8 = e % (RP / 8), c = t0 + cc;
+      uint4 a = make_uint4(0, 0, 0, 0), b = make_uint4(0, 0, 0, 0);
+      if (c < C) {
+        a = *reinterpret_cast<const uint4*>(ch + (long long)c * RP + 8 * ch8);
+        b = *reinterpret_cast<const uint4*>(cl + (long long)c * RP + 8 * ch8);
+      }
+      *reinterpret_cast<uint4*>(sh + cc * LD + 8 * ch8) = a;
+      *reinterpret_cast<uint4*>(sl + cc * LD + 8 * ch8) = b;
+    }
+    for (int e = tid; e < kCenterTile; e += 256) sn[e] = t0 + e < C ? cn[t0 + e] : 0.f;
+    __syncthreads();
+#pragma unroll 1
+    for (int j = 0; j < kCenterTile / 32; ++j) {
+      if (t0 + 32 * j >= C) break;
+      f32x16_t acc = f32x16_t{};
+      const int crow = 32 * j + nl;
+#pragma unroll
+      for (int s = 0; s < NS; ++s) {
+        const bf16x8_t ah =
+            *reinterpret_cast<const bf16x8_t*>(sh + crow * LD + 16 * s + 8 * g);
+        const bf16x8_t al =
+            *reinterpret_cast<const bf16x8_t*>(sl + crow * LD + 16 * s + 8 * g);
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, bh[s], acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, bl[s], acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al, bh[s], acc, 0, 0, 0);
+      }
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int cc = 32 * j + 8 * (i >> 2) + 4 * g + (i & 3);
+        const float v = fmaf(-2.f, acc[i], sn[cc]);
+        if (t0 + cc < C && v < best) {
+          best = v;
+          bi = t0 + cc;
+        }
+      }
+    }
+  }
+  // the two lanes of a row hold interleaved centre subsets
+  const float ob = __shfl_xor(best, 32);
+  const int oi = __shfl_xor(bi, 32);
+  if (ob < best || (ob == best && oi < bi)) {
+    best = ob;
+    bi = oi;
+  }
+  if (g == 0 && row < n) labels[(long long)h * n + row] = bi;
+}
+
+// Mean of each K/V group's key rows in the original space (fp32, row order).
+// One wave per group; lane j covers dims j and j + 64.
+template <int D>
+__global__ __launch_bounds__(256) void key_centroid_kernel(const int32_t* __restrict__ perm,
+                                                           const int32_t* __restrict__ offsets,
+                                                           const void* k, int dtype, long long sh,
+                                                           long long st, int n, int C,
+                                                           float* __restrict__ cent) {
+  const int h = blockIdx.y, c = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
+  if (c >= C) return;
+  const int32_t* off = offsets + (long long)h * (C + 1);
+  const int b0 = off[c], b1 = off[c + 1];
+  const int32_t* pr = perm + (long long)h * n;
+  float s0 = 0.f, s1 = 0.f;
+  for (int j = b0; j < b1; ++j) {
+    const long long base = h * sh + (long long)pr[j] * st;
+    s0 += load_elem(k, dtype, base + lane);
+    if (D > 64) s1 += load_elem(k, dtype, base + 64 + lane);
+  }
+  float* o = cent + ((long long)h * C + c) * D;
+  o[lane] = b1 > b0 ? s0 / float(b1 - b0) : 0.f;
+  if (D > 64) o[64 + lane] = b1 > b0 ? s1 / float(b1 - b0) : 0.f;
+}
+
+struct RcpWs {
+  float *metric, *factor, *cent, *cnorm, *kcent;
+  uint16_t *xh, *xl, *chi, *clo;
+  int32_t *perm, *offsets;
+  void* sort_ws;
+};
+
+RcpWs carve_rcp(void* base, const sparsepr_dims* d, size_t* used) {
+  Carver cv(base);
+  const size_t H = d->heads, D = d->head_dim;
+  const size_t nmax = d->n_q > d->n_k ? d->n_q : d->n_k;
+  const int cmax = d->c_q > d->c_k ? d->c_q : d->c_k;
+  RcpWs w;
+  w.metric = cv.take<float>(H * D * D);
+  w.factor = cv.take<float>(H * D * kMaxR);
+  w.cent = cv.take<float>(H * cmax * kMaxR);
+  w.cnorm = cv.take<float>(H * cmax);
+  w.kcent = cv.take<float>(H * d->c_k * D);
+  w.xh = cv.take<uint16_t>(H * nmax * kMaxR);
+  w.xl = cv.take<uint16_t>(H * nmax * kMaxR);
+  w.chi = cv.take<uint16_t>(H * cmax * kMaxR);
+  w.clo = cv.take<uint16_t>(H * cmax * kMaxR);
+  w.perm = cv.take<int32_t>(H * nmax);
+  w.offsets = cv.take<int32_t>(H * (cmax + 1));
+  const size_t sq = group_sort_ws_bytes(d->heads, d->n_q, d->c_q);
+  const size_t sk = group_sort_ws_bytes(d->heads, d->n_k, d->c_k);
+  w.sort_ws = cv.take<char>(sq > sk ? sq : sk);
+  if (used) *used = cv.used;
+  return w;
+}
+
+template <int RP>
+int32_t run_kmeans(const RcpWs& w, int H, int n, int C, const int32_t* init, int iters,
+                   int32_t* labels, hipStream_t stream) {
+  const dim3 gc((C + 3) / 4, H);
+  kmeans_init_kernel<RP><<<gc, 256, 0, stream>>>(w.xh, w.xl, n, init, C, w.cent, w.chi, w.clo,
+                                                 w.cnorm);
+  SPR_LAUNCH_CHECK();
+  for (int it = 0; it < iters; ++it) {
+    kmeans_assign_kernel<RP><<<dim3((n + 127) / 128, H), 256, 0, stream>>>(
+        w.xh, w.xl, n, w.chi, w.clo, w.cnorm, C, labels);
+    SPR_LAUNCH_CHECK();
+    if (it + 1 == iters) break;   // the partition is the last assignment
+    int32_t st = group_sort(labels, H, n, C, w.perm, w.offsets, w.sort_ws, stream);
+    if (st != SPARSEPR_OK) return st;
+    kmeans_update_kernel<RP><<<gc, 256, 0, stream>>>(w.perm, w.offsets, w.xh, w.xl, n, C, w.cent,
+                                                     w.chi, w.clo, w.cnorm);
+    SPR_LAUNCH_CHECK();
+  }
+  return SPARSEPR_OK;
+}
+
+int32_t kmeans_rp(int rp, const RcpWs& w, int H, int n, int C, const int32_t* init, int iters,
+                  int32_t* labels, hipStream_t stream) {
+  switch (rp) {
+    case 16: return run_kmeans<16>(w, H, n, C, init, iters, labels, stream);
+    case 32: return run_kmeans<32>(w, H, n, C, init, iters, labels, stream);
+    case 48: return run_kmeans<48>(w, H, n, C, init, iters, labels, stream);
+    default: return run_kmeans<64>(w, H, n, C, init, iters, labels, stream);
+  }
+}
+
+template <int D>
+int32_t rcp_run(const sparsepr_dims* d, int m_s, int r_k, int r_q, int iters, const void* q,
+                const void* k, const int32_t* init_q, const int32_t* init_k, int32_t* labels_q,
+                int32_t* labels_kv, float* phi_q, float* phi_k, const RcpWs& w,
+                hipStream_t stream) {
+  const int H = d->heads;
+  const int rpk = (r_k + 15) / 16 * 16, rpq = (r_q + 15) / 16 * 16;
+  // key-response coordinates and K/V groups
+  key_metric_kernel<D><<<H, 256, 0, stream>>>(q, d->dtype, d->q_stride_head, d->q_stride_tok,
+                                              d->n_q, m_s, w.metric);
+  SPR_LAUNCH_CHECK();
+  eig_factor_kernel<D><<<H, 256, 0, stream>>>(w.metric, r_k, rpk, w.factor);
+  SPR_LAUNCH_CHECK();
+  project_kernel<D><<<dim3((d->n_k + 63) / 64, H), 256, 0, stream>>>(
+      k, d->dtype, d->kv_stride_head, d->kv_stride_tok, d->n_k, w.factor, r_k, rpk, 0, w.xh, w.xl,
+      phi_k);
+  SPR_LAUNCH_CHECK();
+  int32_t st = kmeans_rp(rpk, w, H, d->n_k, d->c_k, init_k, iters, labels_kv, stream);
+  if (st != SPARSEPR_OK) return st;
+  // query-response coordinates from the K/V groups, then query groups
+  st = group_sort(labels_kv, H, d->n_k, d->c_k, w.perm, w.offsets, w.sort_ws, stream);
+  if (st != SPARSEPR_OK) return st;
+  key_centroid_kernel<D><<<dim3((d->c_k + 3) / 4, H), 256, 0, stream>>>(
+      w.perm, w.offsets, k, d->dtype, d->kv_stride_head, d->kv_stride_tok, d->n_k, d->c_k,
+      w.kcent);
+  SPR_LAUNCH_CHECK();
+  query_metric_kernel<D><<<H, 256, 0, stream>>>(w.kcent, w.offsets, d->c_k, w.metric);
+  SPR_LAUNCH_CHECK();
+  eig_factor_kernel<D><<<H, 256, 0, stream>>>(w.metric, r_q, rpq, w.factor);
+  SPR_LAUNCH_CHECK();
+  project_kernel<D><<<dim3((d->n_q + 63) / 64, H), 256, 0, stream>>>(
+      q, d->dtype, d->q_stride_head, d->q_stride_tok, d->n_q, w.factor, r_q, rpq, 1, w.xh, w.xl,
+      phi_q);
+  SPR_LAUNCH_CHECK();
+  return kmeans_rp(rpq, w, H, d->n_q, d->c_q, init_q, iters, labels_q, stream);
+}
+
+}  // namespace
+
+size_t rcp_ws_bytes(const sparsepr_dims* d) {
+  size_t used = 0;
+  carve_rcp(nullptr, d, &used);
+  return used;
+}
+
+}  // namespace spr
+
+using namespace spr;
+
+extern "C" int32_t sparsepr_rcp_partition(const sparsepr_dims* dims, int32_t m_s, int32_t r_k,
+                                          int32_t r_q, int32_t iters, const void* q,
+                                          const void* k, const int32_t* init_q,
+                                          const int32_t* init_k, int32_t* labels_q,
+                                          int32_t* labels_kv, float* phi_q, float* phi_k,
+                                          void* ws, size_t ws_bytes, hipStream_t stream) {
+  int32_t st = check_dims(dims);
+  if (st != SPARSEPR_OK) return st;
+  if (!q || !k || !init_q || !init_k || !labels_q || !labels_kv) return SPARSEPR_ERR_INVALID;
+  if (m_s < 1 || iters < 1 || r_k < 1 || r_q < 1 || r_k > kMaxR || r_q > kMaxR ||
+      r_k > dims->head_dim || r_q > dims->head_dim)
+    return SPARSEPR_ERR_INVALID;
+  const size_t need = rcp_ws_bytes(dims);
+  if (!ws || ws_bytes < need) return SPARSEPR_ERR_WORKSPACE;
+  const RcpWs w = carve_rcp(ws, dims, nullptr);
+  if (dims->head_dim == 128)
+    return rcp_run<128>(dims, m_s, r_k, r_q, iters, q, k, init_q, init_k, labels_q, labels_kv,
+                        phi_q, phi_k, w, stream);
+  return rcp_run<64>(dims, m_s, r_k, r_q, iters, q, k, init_q, init_k, labels_q, labels_kv,
+                     phi_q, phi_k, w, stream);
+}

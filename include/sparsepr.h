@@ -59,7 +59,9 @@ enum {
   SPARSEPR_CALL_ROUTE_CELLS = 1,
   SPARSEPR_CALL_SPARSE_ATTN = 2,
   SPARSEPR_CALL_PROBE_FIT = 3,
-  SPARSEPR_CALL_CORRECT = 4
+  SPARSEPR_CALL_CORRECT = 4,
+  SPARSEPR_CALL_RCP_PARTITION = 5,
+  SPARSEPR_CALL_PROBE_FIT_FEAT = 6
 };
 
 #define SPARSEPR_MAX_GROUPS 1024
@@ -88,8 +90,8 @@ typedef struct sparsepr_dims {
 } sparsepr_dims;
 
 /* Workspace bytes needed by one call (0 if it needs none).  m and rank are
- * only used by SPARSEPR_CALL_PROBE_FIT.  Returns 0 for invalid dims too;
- * the call itself reports the error. */
+ * only used by SPARSEPR_CALL_PROBE_FIT and SPARSEPR_CALL_PROBE_FIT_FEAT.
+ * Returns 0 for invalid dims too; the call itself reports the error. */
 size_t sparsepr_workspace_bytes(int32_t which_call, const sparsepr_dims* dims /* host */,
                                 int32_t m, int32_t rank);
 
@@ -227,6 +229,65 @@ int32_t sparsepr_correct(const sparsepr_dims* dims /* host */, int32_t m, int32_
                          void* out, int32_t out_dtype,
                          int64_t out_stride_head, int64_t out_stride_tok,
                          void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * Partition step before S1: response-coupled partitioning.  (SparsePR paper
+ * §4.1; App. B.1 key response metric; App. B.2 query response metric and
+ * RMS normalisation; App. C.1 clustering on the GPU with initial centres
+ * sampled from the feature rows.)  Per head:
+ *   M_K = Q_s^T Q_s / M_s over the query rows floor(i N_q / m_s), i < m_s
+ *     (every row when N_q <= m_s);
+ *   F_K = the leading r_k eigenvectors of M_K, each scaled by
+ *     sqrt(max(lambda, 0) / mean of the r_k retained eigenvalues);
+ *   K/V labels = Lloyd's k-means (`iters` iterations, C_k = dims.c_k
+ *     centres starting at rows init_k) on phi_K = k F_K;
+ *   M_Q = K~^T K~ / C_nonempty, K~ = non-empty K/V group centroids in key
+ *     space minus their mean; F_Q likewise with r_q;
+ *   query labels = k-means (C_q = dims.c_q centres from init_q) on
+ *     phi_Q = u / max(RMS(u), 1e-6), u = q F_Q.
+ * One Lloyd iteration assigns every row to the centre with the smallest
+ * |c|^2 - 2 x.c (x.c from the bf16 pair of each operand, three products,
+ * fp32 accumulation; ties to the smaller index) and moves each centre to
+ * the mean of its rows (an empty cluster keeps its centre); the labels are
+ * those of the last assignment.  Metrics, factors and centroids are fp32.
+ *   m_s >= 1; r_k, r_q in 1..min(64, d); iters >= 1.
+ *   q, k: as for partition_layout (dims strides and dtype); v is not used.
+ *   init_q [H][C_q], init_k [H][C_k]: int32 row indices (clamped to [0, N)).
+ * Outputs
+ *   labels_q [H][N_q], labels_kv [H][N_k]: int32 group ids (inputs of
+ *     partition_layout); empty groups may occur.
+ *   phi_q [H][N_q][r_q]: fp32 query coordinates in token order (may be NULL;
+ *     the probe distances of a response-coupled partition use them, see
+ *     sparsepr_probe_fit_feat).
+ *   phi_k [H][N_k][r_k]: fp32 key coordinates in token order (may be NULL).
+ */
+int32_t sparsepr_rcp_partition(const sparsepr_dims* dims /* host */, int32_t m_s, int32_t r_k,
+                               int32_t r_q, int32_t iters, const void* q, const void* k,
+                               const int32_t* init_q, const int32_t* init_k,
+                               int32_t* labels_q, int32_t* labels_kv, float* phi_q, float* phi_k,
+                               void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * S6-S8 with probe features.  As sparsepr_probe_fit, but the distance of a
+ * row to its group's centroid is taken in the feature space `probe_feat`
+ * ([H][N_q][feat_dim] fp32, token order; feat_dim 1..64): the coordinates
+ * that formed the partition (SparsePR paper App. B.2: the query-response
+ * coordinates stratify probe selection).  Centroids are fp64 means of the
+ * features over each group, distances fp64.  Workspace:
+ * sparsepr_workspace_bytes(SPARSEPR_CALL_PROBE_FIT_FEAT, dims, m, rank).
+ */
+int32_t sparsepr_probe_fit_feat(const sparsepr_dims* dims /* host */, int32_t m, int32_t rank,
+                                double lambda,
+                                const int32_t* offsets_q, const int32_t* offsets_kv,
+                                const int32_t* perm_q,
+                                const int32_t* cell_rowptr, const int32_t* cell_col,
+                                const float* probe_feat, int32_t feat_dim,
+                                const void* q_g, const void* k_g, const void* v_g,
+                                const int32_t* v_shift, float softmax_scale,
+                                int32_t* probe_rows, int32_t* probe_tokens,
+                                float* o_probe_dense, float* o_probe_sparse,
+                                float* corr_a, float* corr_psi_t, float* corr_c,
+                                void* ws, size_t ws_bytes, hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -23,6 +23,23 @@ def rel_fro(a, b):
     return float(np.linalg.norm(a - b) / (den if den > 0 else 1.0))
 
 
+def ari(a, b):
+    """Adjusted Rand index of two labelings (pair counting)."""
+    a = np.asarray(a)
+    b = np.asarray(b)
+    n = a.size
+    _, ai = np.unique(a, return_inverse=True)
+    _, bi = np.unique(b, return_inverse=True)
+    cont = np.zeros((ai.max() + 1, bi.max() + 1), np.int64)
+    np.add.at(cont, (ai, bi), 1)
+    comb = lambda m: m * (m - 1) / 2.0
+    idx = comb(cont).sum()
+    ea, eb = comb(cont.sum(axis=1)).sum(), comb(cont.sum(axis=0)).sum()
+    exp = ea * eb / comb(n)
+    den = 0.5 * (ea + eb) - exp
+    return float((idx - exp) / den) if den != 0 else 1.0
+
+
 def tol_for(w):
     return 1e-5 if w.dtype == "f32" else 2e-3
 
@@ -62,7 +79,7 @@ def upload_arrays(w, arr):
 
 
 def run_gpu(w, heads_data, budget=None, rank=None, m=None, layout="hnd", out_dtype="f32",
-            overlap=True, tensors=None, fetch_heads=None):
+            overlap=True, tensors=None, fetch_heads=None, probe_feat=None):
     """Runs the whole call.  Inputs come from per-head dicts (`heads_data`) or,
     for large shapes, from already uploaded `tensors` (heads_data is then
     None).  `fetch_heads` limits the per-head outputs copied back."""
@@ -82,7 +99,9 @@ def run_gpu(w, heads_data, budget=None, rank=None, m=None, layout="hnd", out_dty
                            m=w.m if m is None else m, rank=w.r if rank is None else rank,
                            lam=w.lam, rho=w.rho, budget=budget,
                            out_dtype=fb.F32 if out_dtype == "f32" else fb.BF16,
-                           q_strides=strides, kv_strides=strides, overlap=overlap)
+                           q_strides=strides, kv_strides=strides, overlap=overlap,
+                           feat_dim=0 if probe_feat is None else probe_feat.shape[-1])
+    call.probe_feat = probe_feat
     call(lq, lk, q, k, v)
     torch.cuda.synchronize()
     g = {name: getattr(call, name) for name in (
@@ -101,11 +120,11 @@ def run_gpu(w, heads_data, budget=None, rank=None, m=None, layout="hnd", out_dty
     return out
 
 
-def oracle_head(w, hd, budget=None, rank=None, m=None, rows=None):
+def oracle_head(w, hd, budget=None, rank=None, m=None, rows=None, features=None):
     return oracle.run_head(hd["q"], hd["k"], hd["v"], hd["labels_q"], hd["labels_kv"], w.c_q,
                            w.c_k, w.rho, m=w.m if m is None else m,
                            rank=w.r if rank is None else rank, lam=w.lam, budget=budget,
-                           query_rows=rows)
+                           features=features, query_rows=rows)
 
 
 def cells_from_csr(rowptr, col, c_q, c_k):

@@ -1,0 +1,169 @@
+"""GPU parity of response-coupled partitioning (sparsepr_rcp_partition) and of
+the call that runs on its groups (probe distances in the query-response
+coordinates, sparsepr_probe_fit_feat).
+
+[paper] "Partition the Support, Reconstruct the Residual" §4.1, App. B.1,
+App. B.2, App. C.1.  Several partitions are correct up to rounding (k-means
+decisions near ties, eigenvector signs), so each stage is compared on what
+is unique, against the oracle run on the GPU's own inputs to that stage:
+  * the key and query coordinates through their row Gram matrices
+    (phi phi^T does not depend on eigenvector signs or on rotations inside
+    a repeated eigenvalue);
+  * the k-means labels against the oracle's Lloyd iteration run on the GPU
+    coordinates with the same initial rows (agreement and adjusted Rand
+    index: the assignment products are bf16 pairs, so near-ties may flip);
+  * the whole partition against the oracle's from scratch (adjusted Rand
+    index, reported);
+  * the call on the GPU groups against the oracle on the same groups and
+    probe features, to the usual parity bar."""
+import numpy as np
+import pytest
+
+import synthgen as sg
+from harness import ari, compare_head, oracle_head, rel_fro, run_gpu, say, upload, upload_arrays
+from oracle import rcp
+
+pytestmark = pytest.mark.gpu
+
+
+def _gram(phi, rows):
+    x = np.asarray(phi, np.float64)[rows]
+    return x @ x.T
+
+
+def run_partition(w, q, k, params, keep_phi_k=True):
+    import torch
+    import free_block_sparse_major_amd as fb
+    H = q.shape[0]
+    part = fb.RcpPartition(H, w.n, w.n, w.head_dim, fb.BF16 if w.dtype == "bf16" else fb.F32,
+                           w.c_q, w.c_k, m_s=params["m_s"], r_k=params["r_k"], r_q=params["r_q"],
+                           iters=params["iters"], keep_phi_k=keep_phi_k)
+    ik, iq = sg.rcp_init_arrays(w)
+    dev = torch.device("cuda")
+    part(q, k, torch.from_numpy(iq[:H]).to(dev), torch.from_numpy(ik[:H]).to(dev))
+    torch.cuda.synchronize()
+    return part, ik, iq
+
+
+def check_head(w, params, hd, h, part, ik, iq, full_oracle=True):
+    """Stage-by-stage checks of head h; returns a dict of measured numbers."""
+    rows_s = np.linspace(0, w.n - 1, min(w.n, 256)).astype(np.int64)
+    out = {}
+    q, k = hd["q"], hd["k"]
+    lab_kv = part.labels_kv[h].cpu().numpy()
+    lab_q = part.labels_q[h].cpu().numpy()
+    phi_q = part.phi_q[h].cpu().numpy().astype(np.float64)
+    phi_k = part.phi_k[h].cpu().numpy().astype(np.float64)
+    assert lab_kv.min() >= 0 and lab_kv.max() < w.c_k
+    assert lab_q.min() >= 0 and lab_q.max() < w.c_q
+    # key coordinates
+    ms_rows = rcp.sample_query_rows(w.n, params["m_s"])
+    f_k = rcp.response_factor(rcp.key_response_metric(q[ms_rows]), params["r_k"])
+    out["phi_k_gram"] = rel_fro(_gram(phi_k, rows_s), _gram(k @ f_k, rows_s))
+    # K/V k-means on the GPU coordinates
+    lab_kv_o, _, _ = rcp.kmeans(phi_k, ik[h], params["iters"])
+    out["kv_agree"] = float(np.mean(lab_kv_o == lab_kv))
+    out["kv_ari"] = ari(lab_kv_o, lab_kv)
+    # query coordinates from the GPU K/V groups
+    m_q, _ = rcp.query_response_metric(k, lab_kv, w.c_k)
+    phi_q_o = rcp.query_features(q, rcp.response_factor(m_q, params["r_q"]))
+    out["phi_q_gram"] = rel_fro(_gram(phi_q, rows_s), _gram(phi_q_o, rows_s))
+    out["phi_q_rms"] = float(np.abs((phi_q ** 2).mean(axis=1) - 1.0).max())
+    lab_q_o, _, _ = rcp.kmeans(phi_q, iq[h], params["iters"])
+    out["q_agree"] = float(np.mean(lab_q_o == lab_q))
+    out["q_ari"] = ari(lab_q_o, lab_q)
+    if full_oracle:
+        ref = rcp.rcp_partition(q, k, params["m_s"], params["r_k"], w.c_k, params["r_q"], w.c_q,
+                                ik[h], iq[h], params["iters"])
+        out["kv_ari_scratch"] = ari(ref["labels_kv"], lab_kv)
+        out["q_ari_scratch"] = ari(ref["labels_q"], lab_q)
+    return out
+
+
+def assert_stage_bounds(e):
+    # coordinates: fp32 metric, Jacobi factor and projection against fp64
+    assert e["phi_k_gram"] < 2e-3, e
+    assert e["phi_q_gram"] < 2e-3, e
+    assert e["phi_q_rms"] < 1e-4, e
+    # Lloyd's iteration on the same coordinates: only near-ties may differ
+    assert e["kv_agree"] > 0.99 and e["kv_ari"] > 0.98, e
+    assert e["q_agree"] > 0.99 and e["q_ari"] > 0.98, e
+
+
+SMALL = dict(m_s=128, r_k=24, r_q=32, iters=6)
+
+
+@pytest.mark.parametrize("head_dim,dtype", [(64, "bf16"), (128, "bf16"), (64, "f32")])
+def test_rcp_partition_small(head_dim, dtype):
+    w = sg.small_workload(name=f"rcp_{head_dim}_{dtype}", heads=2, n=3000, head_dim=head_dim,
+                          dtype=dtype, components=16, kv_split=2, grid=(5, 20, 30), rho="0.26",
+                          seed=31)
+    heads = sg.make_call(w)
+    q, k, v, _, _ = upload(w, heads)
+    part, ik, iq = run_partition(w, q, k, SMALL)
+    for h in range(w.heads):
+        e = check_head(w, SMALL, heads[h], h, part, ik, iq)
+        say(f"[rcp {w.name}] head {h}: {e}")
+        assert_stage_bounds(e)
+        assert e["kv_ari_scratch"] > 0.8 and e["q_ari_scratch"] > 0.8, e
+
+
+def test_rcp_deterministic():
+    w = sg.small_workload(name="rcp_det", heads=2, n=2500, head_dim=64, components=8,
+                          kv_split=2, rho="0.3", seed=32)
+    heads = sg.make_call(w)
+    q, k, _, _, _ = upload(w, heads)
+    a, _, _ = run_partition(w, q, k, SMALL)
+    la = (a.labels_q.clone(), a.labels_kv.clone(), a.phi_q.clone())
+    b, _, _ = run_partition(w, q, k, SMALL)
+    assert bool((la[0] == b.labels_q).all()) and bool((la[1] == b.labels_kv).all())
+    assert bool((la[2] == b.phi_q).all())
+
+
+def test_rcp_call_parity_small():
+    # the call on the GPU's groups, probes stratified in phi_Q
+    w = sg.small_workload(name="rcp_call", heads=2, n=3000, head_dim=128, components=16,
+                          kv_split=2, grid=(5, 20, 30), rho="0.26", seed=33)
+    heads = sg.make_call(w)
+    q, k, v, _, _ = upload(w, heads)
+    part, _, _ = run_partition(w, q, k, SMALL, keep_phi_k=False)
+    for h in range(w.heads):
+        heads[h]["labels_q"] = part.labels_q[h].cpu().numpy()
+        heads[h]["labels_kv"] = part.labels_kv[h].cpu().numpy()
+    g = run_gpu(w, heads, probe_feat=part.phi_q)
+    for h in range(w.heads):
+        feats = part.phi_q[h].cpu().numpy()
+        r = oracle_head(w, heads[h], features=feats)
+        errs = compare_head(w, g, h, r)
+        say(f"[rcp call] head {h}: {errs}")
+
+
+def test_rcp_full_size_sampled():
+    # the Wan-like call with its partition built on the GPU: every head is
+    # partitioned, head 0 is checked stage by stage, and the call on the GPU
+    # groups is compared on sampled rows of heads 0 and 39
+    w = sg.workload("wan_rcp")
+    params = sg.RCP_PARAMS
+    arr = sg.make_call_arrays(w)
+    tensors = upload_arrays(w, arr)
+    del arr
+    q, k, v, _, _ = tensors
+    part, ik, iq = run_partition(w, q, k, params)
+    pos = sg.position_code(w.grid, w.head_dim)
+    hd = sg.make_head(w, 0, pos=pos)
+    e = check_head(w, params, hd, 0, part, ik, iq)
+    say(f"[rcp wan] head 0: {e}")
+    assert_stage_bounds(e)
+    lab_q = part.labels_q.cpu().numpy()
+    say(f"[rcp wan] non-empty query groups per head: {[int((np.bincount(l, minlength=w.c_q) > 0).sum()) for l in lab_q[:4]]}")
+    from test_gpu_large import sample_rows
+    g = run_gpu(w, None, tensors=(q, k, v, part.labels_q, part.labels_kv), fetch_heads=[0, 39],
+                probe_feat=part.phi_q)
+    for j, h in enumerate([0, 39]):
+        hd = sg.make_head(w, h, pos=pos)
+        hd["labels_q"] = lab_q[h]
+        hd["labels_kv"] = part.labels_kv[h].cpu().numpy()
+        rows = sample_rows(hd["labels_q"], w.c_q, 1500, seed=2000 + h)
+        r = oracle_head(w, hd, rows=rows, features=part.phi_q[h].cpu().numpy())
+        errs = compare_head(w, g, j, r)
+        say(f"[rcp wan] call head {h}: {errs}")

@@ -207,6 +207,7 @@ def test_rcp_recovers_planted_response_groups():
 
 def test_ari_helper_against_brute_pairs():
     # the ARI used by the GPU tests, against its pair-counting definition
+    from harness import ari
     rng = np.random.default_rng(8)
     a, b = rng.integers(0, 3, 30), rng.integers(0, 4, 30)
     same_a = [a[i] == a[j] for i, j in itertools.combinations(range(30), 2)]
@@ -216,3 +217,5 @@ def test_ari_helper_against_brute_pairs():
     expect = (n11 - na * nb / npairs) / (0.5 * (na + nb) - na * nb / npairs)
     assert _ari(a, b) == pytest.approx(expect)
     assert _ari(a, a) == pytest.approx(1.0)
+    assert ari(a, b) == pytest.approx(expect)
+    assert ari(b + 7, (a * 3) % 5) == pytest.approx(_ari(b + 7, (a * 3) % 5))
