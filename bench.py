@@ -4,7 +4,9 @@ python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload wan]
 
 A step is one whole attention call (layout, routing, sparse attention,
 probes + fit on a side stream, correction) over all heads of the workload,
-inputs resident in HBM.  Prints one JSON line.  Only one GPU is used; the
+inputs resident in HBM.  For the workload `wan_rcp` the step also builds the
+partition itself (response-coupled partitioning) before the call, and the
+probe distances use the query-response coordinates.  Prints one JSON line.  Only one GPU is used; the
 path shards by head (see the design notes), and --gpus above 1 is refused.
 """
 from __future__ import annotations
@@ -65,7 +67,7 @@ def _traffic_from_profile(workload_name):
     return float(m_b.group(1))
 
 
-def cpu_baseline(w, arrays, budget_seconds=20.0):
+def cpu_baseline(w, arrays, budget_seconds=20.0, rcp_params=None):
     """The oracle, as it is, on the host cores: head 0 in full except the
     sparse attention, which runs on whole query groups until ~budget_seconds;
     scaled to ms per call over all heads and all rows."""
@@ -84,8 +86,15 @@ def cpu_baseline(w, arrays, budget_seconds=20.0):
     q, k, v = f32(arrays["q"][h]), f32(arrays["k"][h]), f32(arrays["v"][h])
     lq, lk = arrays["labels_q"][h], arrays["labels_kv"][h]
     t0 = time.time()
+    feats = None
+    if rcp_params is not None:
+        import synthgen as sg
+        ik, iq = sg.rcp_init(w, h)
+        part = oracle.rcp.rcp_partition(q, k, rcp_params["m_s"], rcp_params["r_k"], w.c_k,
+                                        rcp_params["r_q"], w.c_q, ik, iq, rcp_params["iters"])
+        lq, lk, feats = part["labels_q"], part["labels_kv"], part["phi_q"]
     r = oracle.run_head(q, k, v, lq, lk, w.c_q, w.c_k, w.rho, m=w.m, rank=w.r, lam=w.lam,
-                        query_rows=np.zeros(0, np.int64))
+                        features=feats, query_rows=np.zeros(0, np.int64))
     t_fixed = time.time() - t0
     # sparse attention + correction on whole query groups, largest first
     sizes = np.diff(r["offsets_q"])
@@ -102,7 +111,8 @@ def cpu_baseline(w, arrays, budget_seconds=20.0):
     per_head = t_fixed + t_rows * (w.n / max(rows_done, 1))
     ms_call = per_head * w.heads * 1e3
     return {"value": ms_call, "unit": "ms/call", "cores": int(cores), "kind": "oracle",
-            "sample": (f"head 0: routing/probes/fit in full ({t_fixed:.1f} s), sparse attention "
+            "sample": (f"head 0: {'partition/' if rcp_params else ''}routing/probes/fit in full "
+                       f"({t_fixed:.1f} s), sparse attention "
                        f"+ correction on {rows_done} of {w.n} query rows ({t_rows:.1f} s); "
                        f"scaled to {w.heads} heads x {w.n} rows, fp64 numpy")}
 
@@ -160,8 +170,30 @@ def main():
     lq = torch.from_numpy(arr["labels_q"]).to(dev)
     lk = torch.from_numpy(arr["labels_kv"]).to(dev)
     dtype = fb.BF16 if w.dtype == "bf16" else fb.F32
+    rcp = w.name.endswith("_rcp")
+    rp = sg.RCP_PARAMS if rcp else None
     call = fb.SparsePRCall(w.heads, w.n, w.n, w.head_dim, dtype, w.c_q, w.c_k, m=w.m, rank=w.r,
-                           lam=w.lam, rho=w.rho, out_dtype=fb.BF16 if w.dtype == "bf16" else fb.F32)
+                           lam=w.lam, rho=w.rho, out_dtype=fb.BF16 if w.dtype == "bf16" else fb.F32,
+                           feat_dim=rp["r_q"] if rcp else 0)
+    part = None
+    if rcp:
+        part = fb.RcpPartition(w.heads, w.n, w.n, w.head_dim, dtype, w.c_q, w.c_k, **rp)
+        ik, iq = sg.rcp_init_arrays(w)
+        init_k, init_q = torch.from_numpy(ik).to(dev), torch.from_numpy(iq).to(dev)
+        call.probe_feat = part.phi_q
+    rcp_events = []
+
+    def step(c):
+        """One whole call; with response-coupled partitioning the partition
+        is built first (timed with events on the current stream)."""
+        if part is None:
+            return c(lq, lk, q, k, v)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        part(q, k, init_q, init_k)
+        e1.record()
+        rcp_events.append((e0, e1))
+        return c(part.labels_q, part.labels_kv, q, k, v)
 
     # attention launches are bracketed with events on the stream they run on
     attn_events = []
@@ -176,21 +208,24 @@ def main():
         attn_events.append((e0, e1))
 
     for _ in range(args.warmup):
-        call(lq, lk, q, k, v)
+        step(call)
     torch.cuda.synchronize()
     call.attend = timed_attend
     attn_events.clear()
+    rcp_events.clear()
     torch.cuda.synchronize()
     t_start = time.perf_counter()
     e_start, e_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e_start.record()
     for _ in range(args.steps):
-        call(lq, lk, q, k, v)
+        step(call)
     e_end.record()
     torch.cuda.synchronize()
     wall_ms = (time.perf_counter() - t_start) * 1e3 / args.steps
     ms_call = e_start.elapsed_time(e_end) / args.steps
     attn_ms = sum(a.elapsed_time(b) for a, b in attn_events) / len(attn_events)
+    rcp_ms = (sum(a.elapsed_time(b) for a, b in rcp_events) / len(rcp_events)
+              if rcp_events else None)
     call.attend = orig_attend
 
     routed = int(call.routed_pairs.sum().item())
@@ -235,6 +270,36 @@ def main():
         "wall_ms_per_call": round(wall_ms, 4),
         "input_generation_s": round(gen_s, 1),
     }
+    if rcp:
+        out["config"]["partition"] = ("response-coupled on the GPU: M_s=%d, r_K=%d, r_Q=%d, "
+                                      "%d Lloyd iterations" % (rp["m_s"], rp["r_k"], rp["r_q"],
+                                                               rp["iters"]))
+        out["rcp_partition_ms"] = round(rcp_ms, 4)
+        lab = part.labels_q.cpu().numpy()
+        out["nonempty_query_groups_mean"] = round(float(np.mean(
+            [(np.bincount(l, minlength=w.c_q) > 0).sum() for l in lab])), 1)
+        # the step (partition + call) across executed-density targets
+        sweep = {}
+        for rho in ("0.12", "0.22", "0.26", "0.35"):
+            cs = fb.SparsePRCall(w.heads, w.n, w.n, w.head_dim, dtype, w.c_q, w.c_k, m=w.m,
+                                 rank=w.r, lam=w.lam, rho=rho,
+                                 out_dtype=fb.BF16 if w.dtype == "bf16" else fb.F32,
+                                 feat_dim=rp["r_q"])
+            cs.probe_feat = part.phi_q
+            for _ in range(2):
+                step(cs)
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(3):
+                step(cs)
+            e1.record()
+            torch.cuda.synchronize()
+            sweep[rho] = {"step_ms": round(e0.elapsed_time(e1) / 3, 3),
+                          "rho_exec": round(int(cs.routed_pairs.sum().item()) / (H * n * n)
+                                            + m_eff / n, 6)}
+            del cs
+        out["density_sweep"] = sweep
     traffic = _traffic_from_profile(w.name)
     out["roofline"] = {
         "bound": "mfma" if w.dtype == "bf16" else "alu",
@@ -286,14 +351,16 @@ def main():
         # the whole call at 26% executed density against the faster dense attention
         c26 = fb.SparsePRCall(w.heads, w.n, w.n, w.head_dim, dtype, w.c_q, w.c_k, m=w.m,
                               rank=w.r, lam=w.lam, rho="0.26",
-                              out_dtype=fb.BF16 if w.dtype == "bf16" else fb.F32)
+                              out_dtype=fb.BF16 if w.dtype == "bf16" else fb.F32,
+                              feat_dim=rp["r_q"] if rcp else 0)
+        c26.probe_feat = part.phi_q if rcp else None
         for _ in range(2):
-            c26(lq, lk, q, k, v)
+            step(c26)
         torch.cuda.synchronize()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
         for _ in range(5):
-            c26(lq, lk, q, k, v)
+            step(c26)
         e1.record()
         torch.cuda.synchronize()
         ms26 = e0.elapsed_time(e1) / 5
@@ -310,7 +377,7 @@ def main():
         out["dense_own_attn_ms"] = round(own_ms, 3)
         out["dense_own_tflops"] = round(4.0 * d * H * n * n / (own_ms * 1e-3) / 1e12, 1)
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(w, arr)
+        out["cpu_baseline"] = cpu_baseline(w, arr, rcp_params=rp)
         out["cpu_baseline"]["value"] = round(out["cpu_baseline"]["value"], 1)
     print(json.dumps(out), flush=True)
 
