@@ -972,27 +972,35 @@ __global__ __launch_bounds__(256) void fit_kernel(FitArgs f) {
 }
 
 // Probe features of a response-coupled partition: rows of `feat` (token
-// order) copied to group-major order and their fp64 mean per group (row
-// order), so the select kernel measures distances in that space.  One wave
-// per group, lane j = feature j.
-__global__ __launch_bounds__(64) void feat_group_kernel(const float* __restrict__ feat,
-                                                        const int32_t* __restrict__ perm_q,
-                                                        const int32_t* __restrict__ off_q,
-                                                        int n_q, int c_q, int fd,
-                                                        float* __restrict__ feat_g,
-                                                        double* __restrict__ feat_cen) {
-  const int a = blockIdx.x, h = blockIdx.y, j = threadIdx.x;
-  if (j >= fd) return;
+// order) copied to group-major order and their fp64 mean per group, so the
+// select kernel measures distances in that space.  One block per group:
+// thread (rl, j) handles feature j of rows rl, rl + 4, ... in order; the
+// four partial sums are added in a fixed order.
+__global__ __launch_bounds__(256) void feat_group_kernel(const float* __restrict__ feat,
+                                                         const int32_t* __restrict__ perm_q,
+                                                         const int32_t* __restrict__ off_q,
+                                                         int n_q, int c_q, int fd,
+                                                         float* __restrict__ feat_g,
+                                                         double* __restrict__ feat_cen) {
+  const int a = blockIdx.x, h = blockIdx.y, rl = threadIdx.x >> 6, j = threadIdx.x & 63;
+  __shared__ double part[4][64];
   const int32_t* o = off_q + (long long)h * (c_q + 1);
   const int lo = o[a], hi = o[a + 1];
   const int32_t* pr = perm_q + (long long)h * n_q;
   double s = 0.0;
-  for (int r = lo; r < hi; ++r) {
-    const float v = feat[((long long)h * n_q + pr[r]) * fd + j];
-    feat_g[((long long)h * n_q + r) * fd + j] = v;
-    s += double(v);
+  if (j < fd) {
+#pragma unroll 4
+    for (int r = lo + rl; r < hi; r += 4) {
+      const float v = feat[((long long)h * n_q + pr[r]) * fd + j];
+      feat_g[((long long)h * n_q + r) * fd + j] = v;
+      s += double(v);
+    }
   }
-  feat_cen[((long long)h * c_q + a) * fd + j] = hi > lo ? s / double(hi - lo) : 0.0;
+  part[rl][j] = s;
+  __syncthreads();
+  if (rl == 0 && j < fd)
+    feat_cen[((long long)h * c_q + a) * fd + j] =
+        hi > lo ? (((part[0][j] + part[1][j]) + part[2][j]) + part[3][j]) / double(hi - lo) : 0.0;
 }
 
 struct ProbeWs {
@@ -1095,8 +1103,8 @@ int32_t probe_fit_impl(const sparsepr_dims* dims, int32_t m, int32_t rank, doubl
     Carver cv(static_cast<char*>(ws) + probe_ws_bytes(dims, m, rank));
     float* feat_g = cv.take<float>(size_t(H) * dims->n_q * fd);
     double* feat_cen = cv.take<double>(size_t(H) * dims->c_q * fd);
-    feat_group_kernel<<<dim3(dims->c_q, H), 64, 0, stream>>>(feat, perm_q, offsets_q, dims->n_q,
-                                                             dims->c_q, fd, feat_g, feat_cen);
+    feat_group_kernel<<<dim3(dims->c_q, H), 256, 0, stream>>>(feat, perm_q, offsets_q, dims->n_q,
+                                                              dims->c_q, fd, feat_g, feat_cen);
     SPR_LAUNCH_CHECK();
     select_kernel<float><<<dim3(dims->c_q, H), 256, 0, stream>>>(
         feat_g, feat_cen, offsets_q, perm_q, w.m_a, w.rank, w.s_tab, dims->n_q, dims->c_q, fd, m,

@@ -163,8 +163,10 @@ __global__ __launch_bounds__(256) void eig_factor_kernel(const float* __restrict
                                                          float* __restrict__ f) {
   constexpr int NP = D / 2, PER = 256 / NP, NCOL = D / PER;
   const int h = blockIdx.x, tid = threadIdx.x;
-  __shared__ float E[D][D + 1];
-  __shared__ float U[D][D + 1];
+  // row stride D + 4: the row pass of 16 consecutive pairs x 4 columns per
+  // wave touches 64 distinct banks
+  __shared__ float E[D][D + 4];
+  __shared__ float U[D][D + 4];
   __shared__ float rc[NP], rs[NP];
   __shared__ int32_t pr_p[NP], pr_q[NP];
   __shared__ int32_t order[D];
@@ -215,25 +217,45 @@ __global__ __launch_bounds__(256) void eig_factor_kernel(const float* __restrict
       const bool act = rs[pi] != 0.f;
       const float ci = rc[pi], si = rs[pi];
       const int p2 = pr_p[pi], q2 = pr_q[pi];
+      // loads of 8 columns are issued before their stores (the compiler
+      // cannot tell the addresses apart and would serialise each pair)
+      constexpr int CH = 8;
       if (act)
-#pragma unroll 4
-        for (int l = 0; l < NCOL; ++l) {   // rows: E <- J^T E
-          const int j = cj + PER * l;
-          const float x1 = E[p2][j], x2 = E[q2][j];
-          E[p2][j] = ci * x1 - si * x2;
-          E[q2][j] = si * x1 + ci * x2;
+        for (int l0 = 0; l0 < NCOL; l0 += CH) {   // rows: E <- J^T E
+          float x1[CH], x2[CH];
+#pragma unroll
+          for (int u = 0; u < CH; ++u) {
+            const int j = cj + PER * (l0 + u);
+            x1[u] = E[p2][j];
+            x2[u] = E[q2][j];
+          }
+#pragma unroll
+          for (int u = 0; u < CH; ++u) {
+            const int j = cj + PER * (l0 + u);
+            E[p2][j] = ci * x1[u] - si * x2[u];
+            E[q2][j] = si * x1[u] + ci * x2[u];
+          }
         }
       __syncthreads();
       if (act)
-#pragma unroll 4
-        for (int l = 0; l < NCOL; ++l) {   // columns: E <- E J, U <- U J
-          const int j = cj + PER * l;
-          const float x1 = E[j][p2], x2 = E[j][q2];
-          E[j][p2] = ci * x1 - si * x2;
-          E[j][q2] = si * x1 + ci * x2;
-          const float u1 = U[j][p2], u2 = U[j][q2];
-          U[j][p2] = ci * u1 - si * u2;
-          U[j][q2] = si * u1 + ci * u2;
+        for (int l0 = 0; l0 < NCOL; l0 += CH) {   // columns: E <- E J, U <- U J
+          float x1[CH], x2[CH], u1[CH], u2[CH];
+#pragma unroll
+          for (int u = 0; u < CH; ++u) {
+            const int j = cj + PER * (l0 + u);
+            x1[u] = E[j][p2];
+            x2[u] = E[j][q2];
+            u1[u] = U[j][p2];
+            u2[u] = U[j][q2];
+          }
+#pragma unroll
+          for (int u = 0; u < CH; ++u) {
+            const int j = cj + PER * (l0 + u);
+            E[j][p2] = ci * x1[u] - si * x2[u];
+            E[j][q2] = si * x1[u] + ci * x2[u];
+            U[j][p2] = ci * u1[u] - si * u2[u];
+            U[j][q2] = si * u1[u] + ci * u2[u];
+          }
         }
       __syncthreads();
     }
@@ -273,7 +295,12 @@ __global__ __launch_bounds__(256) void eig_factor_kernel(const float* __restrict
 // ---------------------------------------------------------------------------
 // projection (phi = x F, optionally RMS-normalised) and its bf16 pair
 // ---------------------------------------------------------------------------
-// 64 rows per block; thread t: row t / 4, columns 16 (t % 4) .. +16.
+// phi^T = F^T x^T on v_mfma_f32_32x32x16_bf16, 4 waves x 32 rows per block:
+// lane l owns row l % 32 and 16 of each 32 columns (the partner lane l ^ 32
+// the other 16), so the RMS needs one exchange.  F enters as a bf16 pair
+// (F = F_hi + F_lo to 2^-16); bf16 rows are exact, fp32 rows are split too
+// (x_hi F_hi + x_hi F_lo + x_lo F_hi), fp32 accumulation.
+constexpr int kProjTiles = 4;   // 128-row tiles per block (F^T is staged once per block)
 template <int D>
 __global__ __launch_bounds__(256) void project_kernel(const void* x, int dtype, long long sh,
                                                       long long st, int n,
@@ -281,49 +308,104 @@ __global__ __launch_bounds__(256) void project_kernel(const void* x, int dtype, 
                                                       int rms, uint16_t* __restrict__ hi,
                                                       uint16_t* __restrict__ lo,
                                                       float* __restrict__ out) {
-  const int h = blockIdx.y, row0 = blockIdx.x * 64, tid = threadIdx.x;
-  __shared__ float fs[D][kMaxR];
-  __shared__ float xs[64][D + 1];
+  constexpr int NS = D / 16, LD = D + 8;   // k-steps; LDS row length of F^T (bf16)
+  const int h = blockIdx.y, tid = threadIdx.x, wid = tid >> 6, lane = tid & 63;
+  const int nl = lane & 31, g = lane >> 5;
+  __shared__ __attribute__((aligned(16))) uint16_t fth[kMaxR * LD];
+  __shared__ __attribute__((aligned(16))) uint16_t ftl[kMaxR * LD];
   const float* fh = f + (long long)h * D * rp;
-  for (int e = tid; e < D * kMaxR; e += 256) {
-    const int j = e / kMaxR, c = e % kMaxR;
-    fs[j][c] = c < rp ? fh[j * rp + c] : 0.f;
-  }
-  for (int e = tid; e < 64 * D; e += 256) {
-    const int rr = e / D, j = e % D, i = row0 + rr;
-    xs[rr][j] = i < n ? load_elem(x, dtype, h * sh + (long long)i * st + j) : 0.f;
+  for (int e = tid; e < kMaxR * D; e += 256) {
+    const int col = e / D, j = e % D;
+    const float v = col < rp ? fh[j * rp + col] : 0.f;
+    const uint16_t b = f32_to_bf16_rne(v);
+    fth[col * LD + j] = b;
+    ftl[col * LD + j] = f32_to_bf16_rne(v - bf16_to_f32(b));
   }
   __syncthreads();
-  const int rr = tid >> 2, c0 = (tid & 3) * 16;
-  float acc[16];
+  for (int tile = 0; tile < kProjTiles; ++tile) {
+  const int row = (blockIdx.x * kProjTiles + tile) * 128 + wid * 32 + nl;
+  const bool valid = row < n;
+  const long long xo = h * sh + (long long)(valid ? row : 0) * st;
+  bf16x8_t xh[NS], xl[NS];
+  const bool f32in = dtype != SPARSEPR_BF16;
 #pragma unroll
-  for (int c = 0; c < 16; ++c) acc[c] = 0.f;
-  for (int j = 0; j < D; ++j) {
-    const float xv = xs[rr][j];
+  for (int s = 0; s < NS; ++s) {
+    if (!f32in) {
+      const uint4 a = valid ? *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(x) + xo +
+                                                              16 * s + 8 * g)
+                            : make_uint4(0, 0, 0, 0);
+      xh[s] = __builtin_bit_cast(bf16x8_t, a);
+    } else {
+      const float* xr = static_cast<const float*>(x) + xo + 16 * s + 8 * g;
+      uint16_t bh[8], bl[8];
 #pragma unroll
-    for (int c = 0; c < 16; ++c) acc[c] = fmaf(xv, fs[j][c0 + c], acc[c]);
+      for (int e = 0; e < 8; ++e) {
+        const float v = valid ? xr[e] : 0.f;
+        bh[e] = f32_to_bf16_rne(v);
+        bl[e] = f32_to_bf16_rne(v - bf16_to_f32(bh[e]));
+      }
+      xh[s] = __builtin_bit_cast(bf16x8_t, bh);
+      xl[s] = __builtin_bit_cast(bf16x8_t, bl);
+    }
+  }
+  f32x16_t acc[kMaxR / 32];
+#pragma unroll
+  for (int cb = 0; cb < kMaxR / 32; ++cb) {
+    acc[cb] = f32x16_t{};
+    if (32 * cb >= rp) continue;
+    const int col = 32 * cb + nl;
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      const bf16x8_t ah = *reinterpret_cast<const bf16x8_t*>(fth + col * LD + 16 * s + 8 * g);
+      const bf16x8_t al = *reinterpret_cast<const bf16x8_t*>(ftl + col * LD + 16 * s + 8 * g);
+      acc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, xh[s], acc[cb], 0, 0, 0);
+      acc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al, xh[s], acc[cb], 0, 0, 0);
+      if (f32in) acc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, xl[s], acc[cb], 0, 0, 0);
+    }
   }
   float scale = 1.f;
   if (rms) {
     float ss = 0.f;
 #pragma unroll
-    for (int c = 0; c < 16; ++c) ss += c0 + c < r ? acc[c] * acc[c] : 0.f;
-    ss += __shfl_xor(ss, 1);
-    ss += __shfl_xor(ss, 2);
+    for (int cb = 0; cb < kMaxR / 32; ++cb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int col = 32 * cb + 8 * (i >> 2) + 4 * g + (i & 3);
+        ss += col < r ? acc[cb][i] * acc[cb][i] : 0.f;
+      }
+    ss += __shfl_xor(ss, 32);
     scale = 1.f / fmaxf(sqrtf(ss / float(r)), 1e-6f);
   }
-  const int i = row0 + rr;
-  if (i >= n) return;
-  const long long o = ((long long)h * n + i) * rp;
+  if (!valid) continue;
+  const long long o = ((long long)h * n + row) * rp;
+  // each group of 4 consecutive columns leaves as one 8-byte (bf16) or
+  // 16-byte (fp32) store; rp is a multiple of 16, so a group is all in or out
 #pragma unroll
-  for (int c = 0; c < 16; ++c) {
-    const int col = c0 + c;
-    if (col < rp) {
-      const float v = acc[c] * scale;
-      const uint16_t bh = f32_to_bf16_rne(v);
-      hi[o + col] = bh;
-      lo[o + col] = f32_to_bf16_rne(v - bf16_to_f32(bh));
-      if (out && col < r) out[((long long)h * n + i) * r + col] = v;
+  for (int cb = 0; cb < kMaxR / 32; ++cb)
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+      const int col = 32 * cb + 8 * q4 + 4 * g;
+      if (col >= rp) continue;
+      float v[4];
+      uint16_t bh[4], bl[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        v[e] = acc[cb][4 * q4 + e] * scale;
+        bh[e] = f32_to_bf16_rne(v[e]);
+        bl[e] = f32_to_bf16_rne(v[e] - bf16_to_f32(bh[e]));
+      }
+      *reinterpret_cast<uint2*>(hi + o + col) = __builtin_bit_cast(uint2, bh);
+      *reinterpret_cast<uint2*>(lo + o + col) = __builtin_bit_cast(uint2, bl);
+      if (out) {
+        float* op = out + ((long long)h * n + row) * r + col;
+        if (col + 4 <= r && (r & 3) == 0) {
+          *reinterpret_cast<float4*>(op) = make_float4(v[0], v[1], v[2], v[3]);
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (col + e < r) op[e] = v[e];
+        }
+      }
     }
   }
 }
@@ -368,31 +450,35 @@ __global__ __launch_bounds__(256) void kmeans_init_kernel(const uint16_t* __rest
   store_center<RP>(h, c, C, v, cent, chi, clo, cnorm);
 }
 
-// Update: mean of each cluster's rows in row order (perm/offsets from the
-// stable sort of the labels); an empty cluster keeps its centre.
+// Update: mean of each cluster's rows (perm/offsets from the stable sort of
+// the labels); an empty cluster keeps its centre.  One block per cluster:
+// thread (rl, j) sums coordinate j over the cluster's rows rl, rl + 4, ...
+// in order, and the four partial sums are added in a fixed order.
 template <int RP>
 __global__ __launch_bounds__(256) void kmeans_update_kernel(
     const int32_t* __restrict__ perm, const int32_t* __restrict__ offsets,
     const uint16_t* __restrict__ xh, const uint16_t* __restrict__ xl, int n, int C, float* cent,
     uint16_t* chi, uint16_t* clo, float* cnorm) {
-  const int h = blockIdx.y, c = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
-  if (c >= C) return;
+  const int h = blockIdx.y, c = blockIdx.x, rl = threadIdx.x >> 6, j = threadIdx.x & 63;
+  __shared__ float part[4][64];
   const int32_t* off = offsets + (long long)h * (C + 1);
   const int b0 = off[c], b1 = off[c + 1];
   const int32_t* pr = perm + (long long)h * n;
-  float v = 0.f;
-  if (lane < RP) {
-    if (b1 > b0) {
-      float s = 0.f;
-      for (int j = b0; j < b1; ++j) {
-        const long long o = ((long long)h * n + pr[j]) * RP + lane;
-        s += bf16_to_f32(xh[o]) + bf16_to_f32(xl[o]);
-      }
-      v = s / float(b1 - b0);
-    } else {
-      v = cent[((long long)h * C + c) * RP + lane];
+  float s = 0.f;
+  if (j < RP) {
+#pragma unroll 4
+    for (int r = b0 + rl; r < b1; r += 4) {
+      const long long o = ((long long)h * n + pr[r]) * RP + j;
+      s += bf16_to_f32(xh[o]) + bf16_to_f32(xl[o]);
     }
   }
+  part[rl][j] = s;
+  __syncthreads();
+  if (rl != 0) return;
+  float v = 0.f;
+  if (j < RP)
+    v = b1 > b0 ? (((part[0][j] + part[1][j]) + part[2][j]) + part[3][j]) / float(b1 - b0)
+                : cent[((long long)h * C + c) * RP + j];
   store_center<RP>(h, c, C, v, cent, chi, clo, cnorm);
 }
 
@@ -482,28 +568,31 @@ __global__ __launch_bounds__(256) void kmeans_assign_kernel(
   if (g == 0 && row < n) labels[(long long)h * n + row] = bi;
 }
 
-// Mean of each K/V group's key rows in the original space (fp32, row order).
-// One wave per group; lane j covers dims j and j + 64.
+// Mean of each K/V group's key rows in the original space (fp32).  One
+// block per group: thread (rl, j) sums dimension j over rows rl, rl + RL, ...
+// in order (RL = 256 / D row lanes); partial sums are added in a fixed order.
 template <int D>
 __global__ __launch_bounds__(256) void key_centroid_kernel(const int32_t* __restrict__ perm,
                                                            const int32_t* __restrict__ offsets,
                                                            const void* k, int dtype, long long sh,
                                                            long long st, int n, int C,
                                                            float* __restrict__ cent) {
-  const int h = blockIdx.y, c = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
-  if (c >= C) return;
+  constexpr int RL = 256 / D;
+  const int h = blockIdx.y, c = blockIdx.x, rl = threadIdx.x / D, j = threadIdx.x % D;
+  __shared__ float part[RL][D];
   const int32_t* off = offsets + (long long)h * (C + 1);
   const int b0 = off[c], b1 = off[c + 1];
   const int32_t* pr = perm + (long long)h * n;
-  float s0 = 0.f, s1 = 0.f;
-  for (int j = b0; j < b1; ++j) {
-    const long long base = h * sh + (long long)pr[j] * st;
-    s0 += load_elem(k, dtype, base + lane);
-    if (D > 64) s1 += load_elem(k, dtype, base + 64 + lane);
-  }
-  float* o = cent + ((long long)h * C + c) * D;
-  o[lane] = b1 > b0 ? s0 / float(b1 - b0) : 0.f;
-  if (D > 64) o[64 + lane] = b1 > b0 ? s1 / float(b1 - b0) : 0.f;
+  float s = 0.f;
+#pragma unroll 4
+  for (int r = b0 + rl; r < b1; r += RL) s += load_elem(k, dtype, h * sh + (long long)pr[r] * st + j);
+  part[rl][j] = s;
+  __syncthreads();
+  if (rl != 0) return;
+  float t = part[0][j];
+#pragma unroll
+  for (int i = 1; i < RL; ++i) t += part[i][j];
+  cent[((long long)h * C + c) * D + j] = b1 > b0 ? t / float(b1 - b0) : 0.f;
 }
 
 struct RcpWs {
@@ -551,8 +640,8 @@ int32_t run_kmeans(const RcpWs& w, int H, int n, int C, const int32_t* init, int
     if (it + 1 == iters) break;   // the partition is the last assignment
     int32_t st = group_sort(labels, H, n, C, w.perm, w.offsets, w.sort_ws, stream);
     if (st != SPARSEPR_OK) return st;
-    kmeans_update_kernel<RP><<<gc, 256, 0, stream>>>(w.perm, w.offsets, w.xh, w.xl, n, C, w.cent,
-                                                     w.chi, w.clo, w.cnorm);
+    kmeans_update_kernel<RP><<<dim3(C, H), 256, 0, stream>>>(w.perm, w.offsets, w.xh, w.xl, n, C,
+                                                             w.cent, w.chi, w.clo, w.cnorm);
     SPR_LAUNCH_CHECK();
   }
   return SPARSEPR_OK;
@@ -581,7 +670,7 @@ int32_t rcp_run(const sparsepr_dims* d, int m_s, int r_k, int r_q, int iters, co
   SPR_LAUNCH_CHECK();
   eig_factor_kernel<D><<<H, 256, 0, stream>>>(w.metric, r_k, rpk, w.factor);
   SPR_LAUNCH_CHECK();
-  project_kernel<D><<<dim3((d->n_k + 63) / 64, H), 256, 0, stream>>>(
+  project_kernel<D><<<dim3((d->n_k + 128 * kProjTiles - 1) / (128 * kProjTiles), H), 256, 0, stream>>>(
       k, d->dtype, d->kv_stride_head, d->kv_stride_tok, d->n_k, w.factor, r_k, rpk, 0, w.xh, w.xl,
       phi_k);
   SPR_LAUNCH_CHECK();
@@ -590,7 +679,7 @@ int32_t rcp_run(const sparsepr_dims* d, int m_s, int r_k, int r_q, int iters, co
   // query-response coordinates from the K/V groups, then query groups
   st = group_sort(labels_kv, H, d->n_k, d->c_k, w.perm, w.offsets, w.sort_ws, stream);
   if (st != SPARSEPR_OK) return st;
-  key_centroid_kernel<D><<<dim3((d->c_k + 3) / 4, H), 256, 0, stream>>>(
+  key_centroid_kernel<D><<<dim3(d->c_k, H), 256, 0, stream>>>(
       w.perm, w.offsets, k, d->dtype, d->kv_stride_head, d->kv_stride_tok, d->n_k, d->c_k,
       w.kcent);
   SPR_LAUNCH_CHECK();
@@ -598,7 +687,7 @@ int32_t rcp_run(const sparsepr_dims* d, int m_s, int r_k, int r_q, int iters, co
   SPR_LAUNCH_CHECK();
   eig_factor_kernel<D><<<H, 256, 0, stream>>>(w.metric, r_q, rpq, w.factor);
   SPR_LAUNCH_CHECK();
-  project_kernel<D><<<dim3((d->n_q + 63) / 64, H), 256, 0, stream>>>(
+  project_kernel<D><<<dim3((d->n_q + 128 * kProjTiles - 1) / (128 * kProjTiles), H), 256, 0, stream>>>(
       q, d->dtype, d->q_stride_head, d->q_stride_tok, d->n_q, w.factor, r_q, rpq, 1, w.xh, w.xl,
       phi_q);
   SPR_LAUNCH_CHECK();
