@@ -126,6 +126,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--rho", default=None, help="override the executed-density target")
+    ap.add_argument("--estimator", default="full", choices=("full", "mean", "scalar", "diagonal"),
+                    help="residual estimator (the full ridge with projection is the default)")
     ap.add_argument("--dense-own", action="store_true",
                     help="also time this library in dense mode (one group, every cell)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MB",
@@ -174,7 +176,7 @@ def main():
     rp = sg.RCP_PARAMS if rcp else None
     call = fb.SparsePRCall(w.heads, w.n, w.n, w.head_dim, dtype, w.c_q, w.c_k, m=w.m, rank=w.r,
                            lam=w.lam, rho=w.rho, out_dtype=fb.BF16 if w.dtype == "bf16" else fb.F32,
-                           feat_dim=rp["r_q"] if rcp else 0)
+                           feat_dim=rp["r_q"] if rcp else 0, estimator=args.estimator)
     part = None
     if rcp:
         part = fb.RcpPartition(w.heads, w.n, w.n, w.head_dim, dtype, w.c_q, w.c_k, **rp)
@@ -257,6 +259,7 @@ def main():
                          f"lambda={w.lam}, seed={w.seed}"),
             "heads": H, "tokens": n, "head_dim": d, "c_q": w.c_q, "c_k": w.c_k,
             "rho_target": w.rho, "m": w.m, "r": w.r, "lambda": w.lam,
+            "estimator": args.estimator,
             "parallelism": "single GPU",
         },
         "executed_pair_tflops": round(call_tflops, 2),

@@ -24,12 +24,14 @@ LIB_PATH = os.path.join(HERE, "libsparsepr.so")
 OK, ERR_INVALID, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = range(5)
 BF16, F32 = 0, 1
 (CALL_PARTITION_LAYOUT, CALL_ROUTE_CELLS, CALL_SPARSE_ATTN, CALL_PROBE_FIT, CALL_CORRECT,
- CALL_RCP_PARTITION, CALL_PROBE_FIT_FEAT) = range(7)
+ CALL_RCP_PARTITION, CALL_PROBE_FIT_EX) = range(7)
+EST_FULL, EST_MEAN, EST_SCALAR, EST_DIAGONAL = range(4)
+ESTIMATORS = {"full": EST_FULL, "mean": EST_MEAN, "scalar": EST_SCALAR, "diagonal": EST_DIAGONAL}
 EXPORTED = (
     "sparsepr_partition_layout", "sparsepr_route_cells", "sparsepr_sparse_attn",
     "sparsepr_probe_fit", "sparsepr_correct", "sparsepr_workspace_bytes",
     "sparsepr_status_string", "sparsepr_version", "sparsepr_rcp_partition",
-    "sparsepr_probe_fit_feat",
+    "sparsepr_probe_fit_ex", "sparsepr_correct_ex",
 )
 
 
@@ -80,9 +82,11 @@ def load_library(path: str = LIB_PATH):
     lib.sparsepr_correct.restype = I32
     lib.sparsepr_rcp_partition.argtypes = [DP, I32, I32, I32, I32] + [P] * 8 + [P, SZ, P]
     lib.sparsepr_rcp_partition.restype = I32
-    lib.sparsepr_probe_fit_feat.argtypes = ([DP, I32, I32, D] + [P] * 6 + [I32] + [P] * 4
-                                            + [ctypes.c_float] + [P] * 7 + [P, SZ, P])
-    lib.sparsepr_probe_fit_feat.restype = I32
+    lib.sparsepr_probe_fit_ex.argtypes = ([DP, I32, I32, D, I32] + [P] * 7 + [I32] + [P] * 4
+                                          + [ctypes.c_float] + [P] * 8 + [P, SZ, P])
+    lib.sparsepr_probe_fit_ex.restype = I32
+    lib.sparsepr_correct_ex.argtypes = [DP, I32, I32] + [P] * 9 + [I32, I64, I64, P, SZ, P]
+    lib.sparsepr_correct_ex.restype = I32
     _lib = lib
     return lib
 
@@ -180,18 +184,29 @@ def sparsepr_rcp_partition(dims, m_s, r_k, r_q, iters, q, k, init_q, init_k, lab
     _check(st, "sparsepr_rcp_partition")
 
 
-def sparsepr_probe_fit_feat(dims, m, rank, lam, offsets_q, offsets_kv, perm_q, cell_rowptr,
-                            cell_col, probe_feat, feat_dim, q_g, k_g, v_g, v_shift, softmax_scale,
-                            probe_rows, probe_tokens, o_probe_dense, o_probe_sparse, corr_a,
-                            corr_psi_t, corr_c, ws, stream=None):
-    st = load_library().sparsepr_probe_fit_feat(
-        ctypes.byref(dims), int(m), int(rank), float(lam), _ptr(offsets_q), _ptr(offsets_kv),
-        _ptr(perm_q), _ptr(cell_rowptr), _ptr(cell_col), _ptr(probe_feat), int(feat_dim),
-        _ptr(q_g), _ptr(k_g), _ptr(v_g), _ptr(v_shift), ctypes.c_float(softmax_scale),
-        _ptr(probe_rows), _ptr(probe_tokens), _ptr(o_probe_dense), _ptr(o_probe_sparse),
-        _ptr(corr_a), _ptr(corr_psi_t), _ptr(corr_c),
+def sparsepr_probe_fit_ex(dims, m, rank, lam, estimator, offsets_q, offsets_kv, perm_q,
+                          cell_rowptr, cell_col, centroid_q, probe_feat, feat_dim, q_g, k_g, v_g,
+                          v_shift, softmax_scale, probe_rows, probe_tokens, o_probe_dense,
+                          o_probe_sparse, corr_a, corr_psi_t, corr_c, corr_g, ws, stream=None):
+    st = load_library().sparsepr_probe_fit_ex(
+        ctypes.byref(dims), int(m), int(rank), float(lam), int(estimator), _ptr(offsets_q),
+        _ptr(offsets_kv), _ptr(perm_q), _ptr(cell_rowptr), _ptr(cell_col), _ptr(centroid_q),
+        _ptr(probe_feat), int(feat_dim), _ptr(q_g), _ptr(k_g), _ptr(v_g), _ptr(v_shift),
+        ctypes.c_float(softmax_scale), _ptr(probe_rows), _ptr(probe_tokens), _ptr(o_probe_dense),
+        _ptr(o_probe_sparse), _ptr(corr_a), _ptr(corr_psi_t), _ptr(corr_c), _ptr(corr_g),
         _ptr(ws), ws.numel() * ws.element_size() if ws is not None else 0, _stream(stream))
-    _check(st, "sparsepr_probe_fit_feat")
+    _check(st, "sparsepr_probe_fit_ex")
+
+
+def sparsepr_correct_ex(dims, m, rank, perm_q, o_sp, probe_tokens, o_probe_dense, corr_a,
+                        corr_psi_t, corr_c, corr_g, out, out_dtype, out_stride_head,
+                        out_stride_tok, stream=None):
+    st = load_library().sparsepr_correct_ex(
+        ctypes.byref(dims), int(m), int(rank), _ptr(perm_q), _ptr(o_sp), _ptr(probe_tokens),
+        _ptr(o_probe_dense), _ptr(corr_a), _ptr(corr_psi_t), _ptr(corr_c), _ptr(corr_g),
+        _ptr(out), int(out_dtype), int(out_stride_head), int(out_stride_tok), None, 0,
+        _stream(stream))
+    _check(st, "sparsepr_correct_ex")
 
 
 class RcpPartition:
@@ -238,7 +253,7 @@ class SparsePRCall:
 
     def __init__(self, heads, n_q, n_k, head_dim, dtype, c_q, c_k, m=64, rank=16, lam=0.1,
                  rho="0.26", budget=None, out_dtype=F32, device="cuda", q_strides=None,
-                 kv_strides=None, overlap=True, feat_dim=0):
+                 kv_strides=None, overlap=True, feat_dim=0, estimator="full"):
         load_library()
         self.dims = make_dims(heads, n_q, n_k, head_dim, dtype, c_q, c_k, q_strides, kv_strides)
         self.m, self.rank, self.lam = m, rank, lam
@@ -250,6 +265,8 @@ class SparsePRCall:
         # an fp32 [H][N_q][feat_dim] tensor before the call
         self.feat_dim = int(feat_dim)
         self.probe_feat = None
+        # residual estimator (full ridge with projection, or mean / scalar / diagonal)
+        self.estimator = ESTIMATORS[estimator]
         H, d = heads, head_dim
         dev = torch.device(device)
         tdt = torch.bfloat16 if dtype == BF16 else torch.float32
@@ -277,6 +294,7 @@ class SparsePRCall:
         self.corr_a = torch.empty(H, d, max(rank, 1), dtype=torch.float32, device=dev)
         self.corr_psi_t = torch.empty(H, max(rank, 1), d, dtype=torch.float32, device=dev)
         self.corr_c = torch.empty(H, d, dtype=torch.float32, device=dev)
+        self.corr_g = torch.zeros(H, d, dtype=torch.float32, device=dev)
         odt = torch.bfloat16 if out_dtype == BF16 else torch.float32
         self.out = torch.empty(H, n_q, d, dtype=odt, device=dev)
 
@@ -287,7 +305,8 @@ class SparsePRCall:
         self.ws_layout = ws(CALL_PARTITION_LAYOUT)
         self.ws_route = ws(CALL_ROUTE_CELLS)
         self.ws_attn = ws(CALL_SPARSE_ATTN)
-        self.ws_probe = ws(CALL_PROBE_FIT_FEAT if feat_dim else CALL_PROBE_FIT)
+        self._ex = bool(feat_dim) or self.estimator != EST_FULL
+        self.ws_probe = ws(CALL_PROBE_FIT_EX if self._ex else CALL_PROBE_FIT)
         self.side = torch.cuda.Stream(device=dev) if overlap else None
         self.ev_routed = torch.cuda.Event()
         self.ev_fit = torch.cuda.Event()
@@ -312,15 +331,17 @@ class SparsePRCall:
                              self.lse, self.ws_attn, stream)
 
     def probe_fit(self, stream=None):
-        if self.feat_dim:
-            if self.probe_feat is None:
+        if self._ex:
+            if self.feat_dim and self.probe_feat is None:
                 raise SparsePRError("probe_feat is not set")
-            sparsepr_probe_fit_feat(self.dims, self.m, self.rank, self.lam, self.offsets_q,
-                                    self.offsets_kv, self.perm_q, self.cell_rowptr, self.cell_col,
-                                    self.probe_feat, self.feat_dim, self.q_g, self.k_g, self.v_g,
-                                    self.v_shift, self.scale, self.probe_rows, self.probe_tokens,
-                                    self.o_probe_dense, self.o_probe_sparse, self.corr_a,
-                                    self.corr_psi_t, self.corr_c, self.ws_probe, stream)
+            sparsepr_probe_fit_ex(self.dims, self.m, self.rank, self.lam, self.estimator,
+                                  self.offsets_q, self.offsets_kv, self.perm_q, self.cell_rowptr,
+                                  self.cell_col, self.centroid_q,
+                                  self.probe_feat if self.feat_dim else None, self.feat_dim,
+                                  self.q_g, self.k_g, self.v_g, self.v_shift, self.scale,
+                                  self.probe_rows, self.probe_tokens, self.o_probe_dense,
+                                  self.o_probe_sparse, self.corr_a, self.corr_psi_t, self.corr_c,
+                                  self.corr_g, self.ws_probe, stream)
             return
         sparsepr_probe_fit(self.dims, self.m, self.rank, self.lam, self.offsets_q,
                            self.offsets_kv, self.perm_q, self.cell_rowptr, self.cell_col,
@@ -331,6 +352,12 @@ class SparsePRCall:
                            self.ws_probe, stream)
 
     def correct(self, stream=None):
+        if self.estimator != EST_FULL:
+            sparsepr_correct_ex(self.dims, self.m, self.rank, self.perm_q, self.o_sp,
+                                self.probe_tokens, self.o_probe_dense, self.corr_a,
+                                self.corr_psi_t, self.corr_c, self.corr_g, self.out,
+                                self.out_dtype, self.out.stride(0), self.out.stride(1), stream)
+            return
         sparsepr_correct(self.dims, self.m, self.rank, self.perm_q, self.o_sp, self.probe_tokens,
                          self.o_probe_dense, self.corr_a, self.corr_psi_t, self.corr_c, self.out,
                          self.out_dtype, self.out.stride(0), self.out.stride(1), stream)

@@ -21,6 +21,7 @@ struct CorrArgs {
   const float* corr_a;
   const float* corr_psi_t;
   const float* corr_c;
+  const float* corr_g;
   void* out;
   int64_t out_sh, out_st;
   int n_q, rank;
@@ -33,6 +34,7 @@ __global__ __launch_bounds__(256) void correct_kernel(const int32_t* __restrict_
                                                       const float* __restrict__ corr_a,
                                                       const float* __restrict__ corr_psi_t,
                                                       const float* __restrict__ corr_c,
+                                                      const float* __restrict__ corr_g,
                                                       void* __restrict__ out, int64_t out_sh,
                                                       int64_t out_st, int n_q, int rank,
                                                       int out_bf16) {
@@ -72,9 +74,15 @@ __global__ __launch_bounds__(256) void correct_kernel(const int32_t* __restrict_
         if (kk == k) u[kk] = acc;
     }
   }
-  // o + c + u Psi^T: k outer, so each step reads one contiguous row Psi^T[k]
+  // o + g o + c + u Psi^T: k outer, so each step reads one contiguous row Psi^T[k]
+  if (corr_g) {
+    const float* __restrict__ gh = corr_g + (long long)h * D;
 #pragma unroll
-  for (int i = 0; i < D; ++i) o[i] += ch[i];
+    for (int i = 0; i < D; ++i) o[i] = fmaf(gh[i], o[i], o[i] + ch[i]);
+  } else {
+#pragma unroll
+    for (int i = 0; i < D; ++i) o[i] += ch[i];
+  }
 #pragma unroll
   for (int k = 0; k < RK; ++k) {
     if (k >= rank) break;
@@ -128,6 +136,7 @@ __global__ __launch_bounds__(256) void correct_mfma_kernel(const int32_t* __rest
                                                            const float* __restrict__ corr_a,
                                                            const float* __restrict__ corr_psi_t,
                                                            const float* __restrict__ corr_c,
+                                                           const float* __restrict__ corr_g,
                                                            void* __restrict__ out, int64_t out_sh,
                                                            int64_t out_st, int n_q, int rank,
                                                            int out_bf16, int tiles_per_wave) {
@@ -161,7 +170,7 @@ __global__ __launch_bounds__(256) void correct_mfma_kernel(const int32_t* __rest
   }
   // Psi operand, dim block b: row (dim) 16 b + r16, k = rank 4G + e
   bf16x4_t p_hi[NB], p_lo[NB];
-  f32x4_t cvec[NB];
+  f32x4_t cvec[NB], gvec[NB];
 #pragma unroll
   for (int b = 0; b < NB; ++b) {
     uint32_t hw[2], lw[2];
@@ -179,7 +188,10 @@ __global__ __launch_bounds__(256) void correct_mfma_kernel(const int32_t* __rest
     p_hi[b] = __builtin_bit_cast(bf16x4_t, make_uint2(hw[0], hw[1]));
     p_lo[b] = __builtin_bit_cast(bf16x4_t, make_uint2(lw[0], lw[1]));
 #pragma unroll
-    for (int e = 0; e < 4; ++e) cvec[b][e] = ch[16 * b + 4 * G + e];
+    for (int e = 0; e < 4; ++e) {
+      cvec[b][e] = ch[16 * b + 4 * G + e];
+      gvec[b][e] = corr_g ? corr_g[(long long)h * D + 16 * b + 4 * G + e] : 0.f;
+    }
   }
   float* st = stage[wid];
   const int ntile = (n_q + 15) / 16;
@@ -233,7 +245,9 @@ __global__ __launch_bounds__(256) void correct_mfma_kernel(const int32_t* __rest
     const bf16x4_t ub_lo = __builtin_bit_cast(bf16x4_t, make_uint2(ul[0], ul[1]));
 #pragma unroll
     for (int b = 0; b < NB; ++b) {
-      f32x4_t acc = o[b] + cvec[b];
+      f32x4_t acc;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc[e] = fmaf(gvec[b][e], o[b][e], o[b][e] + cvec[b][e]);
       acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(p_hi[b], ub_hi, acc, 0, 0, 0);
       acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(p_hi[b], ub_lo, acc, 0, 0, 0);
       acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(p_lo[b], ub_hi, acc, 0, 0, 0);
@@ -300,7 +314,8 @@ template <int D>
 void launch_correct(const CorrArgs& a, dim3 grid, hipStream_t s) {
 #define SPR_CORR(RK)                                                                          \
   correct_kernel<D, RK><<<grid, 256, 0, s>>>(a.perm_q, a.o_sp, a.corr_a, a.corr_psi_t, a.corr_c, \
-                                             a.out, a.out_sh, a.out_st, a.n_q, a.rank, a.out_bf16)
+                                             a.corr_g, a.out, a.out_sh, a.out_st, a.n_q, a.rank,  \
+                                             a.out_bf16)
   if (a.rank <= 16) SPR_CORR(16);
   else if (a.rank <= 32) SPR_CORR(32);
   else SPR_CORR(64);
@@ -312,13 +327,12 @@ void launch_correct(const CorrArgs& a, dim3 grid, hipStream_t s) {
 
 using namespace spr;
 
-extern "C" int32_t sparsepr_correct(const sparsepr_dims* dims, int32_t m, int32_t rank,
-                                    const int32_t* perm_q, const float* o_sp,
-                                    const int32_t* probe_tokens, const float* o_probe_dense,
-                                    const float* corr_a, const float* corr_psi_t,
-                                    const float* corr_c, void* out, int32_t out_dtype,
-                                    int64_t out_stride_head, int64_t out_stride_tok, void* ws,
-                                    size_t ws_bytes, hipStream_t stream) {
+namespace {
+int32_t correct_impl(const sparsepr_dims* dims, int32_t m, int32_t rank, const int32_t* perm_q,
+                     const float* o_sp, const int32_t* probe_tokens, const float* o_probe_dense,
+                     const float* corr_a, const float* corr_psi_t, const float* corr_c,
+                     const float* corr_g, void* out, int32_t out_dtype, int64_t out_stride_head,
+                     int64_t out_stride_tok, void* ws, size_t ws_bytes, hipStream_t stream) {
   (void)ws;
   (void)ws_bytes;
   int32_t st = check_dims(dims);
@@ -339,6 +353,7 @@ extern "C" int32_t sparsepr_correct(const sparsepr_dims* dims, int32_t m, int32_
   a.corr_a = corr_a;
   a.corr_psi_t = corr_psi_t;
   a.corr_c = corr_c;
+  a.corr_g = corr_g;
   a.out = out;
   a.out_sh = out_stride_head;
   a.out_st = out_stride_tok;
@@ -353,12 +368,12 @@ extern "C" int32_t sparsepr_correct(const sparsepr_dims* dims, int32_t m, int32_
     dim3 grid((ntile + 4 * kTilesPerWave - 1) / (4 * kTilesPerWave), dims->heads);
     if (dims->head_dim == 128)
       correct_mfma_kernel<128><<<grid, 256, 0, stream>>>(perm_q, o_sp, corr_a, corr_psi_t, corr_c,
-                                                         out, out_stride_head, out_stride_tok,
+                                                         corr_g, out, out_stride_head, out_stride_tok,
                                                          dims->n_q, rank, a.out_bf16,
                                                          kTilesPerWave);
     else
       correct_mfma_kernel<64><<<grid, 256, 0, stream>>>(perm_q, o_sp, corr_a, corr_psi_t, corr_c,
-                                                        out, out_stride_head, out_stride_tok,
+                                                        corr_g, out, out_stride_head, out_stride_tok,
                                                         dims->n_q, rank, a.out_bf16,
                                                         kTilesPerWave);
   } else {
@@ -372,4 +387,30 @@ extern "C" int32_t sparsepr_correct(const sparsepr_dims* dims, int32_t m, int32_
                                                           out_stride_tok, a.out_bf16);
   SPR_LAUNCH_CHECK();
   return SPARSEPR_OK;
+}
+}  // namespace
+
+extern "C" int32_t sparsepr_correct(const sparsepr_dims* dims, int32_t m, int32_t rank,
+                                    const int32_t* perm_q, const float* o_sp,
+                                    const int32_t* probe_tokens, const float* o_probe_dense,
+                                    const float* corr_a, const float* corr_psi_t,
+                                    const float* corr_c, void* out, int32_t out_dtype,
+                                    int64_t out_stride_head, int64_t out_stride_tok, void* ws,
+                                    size_t ws_bytes, hipStream_t stream) {
+  return correct_impl(dims, m, rank, perm_q, o_sp, probe_tokens, o_probe_dense, corr_a,
+                      corr_psi_t, corr_c, nullptr, out, out_dtype, out_stride_head,
+                      out_stride_tok, ws, ws_bytes, stream);
+}
+
+extern "C" int32_t sparsepr_correct_ex(const sparsepr_dims* dims, int32_t m, int32_t rank,
+                                       const int32_t* perm_q, const float* o_sp,
+                                       const int32_t* probe_tokens, const float* o_probe_dense,
+                                       const float* corr_a, const float* corr_psi_t,
+                                       const float* corr_c, const float* corr_g, void* out,
+                                       int32_t out_dtype, int64_t out_stride_head,
+                                       int64_t out_stride_tok, void* ws, size_t ws_bytes,
+                                       hipStream_t stream) {
+  return correct_impl(dims, m, rank, perm_q, o_sp, probe_tokens, o_probe_dense, corr_a,
+                      corr_psi_t, corr_c, corr_g, out, out_dtype, out_stride_head,
+                      out_stride_tok, ws, ws_bytes, stream);
 }

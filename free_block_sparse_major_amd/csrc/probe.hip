@@ -686,7 +686,9 @@ struct FitArgs {
   float* corr_a;
   float* corr_psi_t;
   float* corr_c;
+  float* corr_g;      // [H][d] diagonal gain (may be null for the full estimator)
   int c_q, m, me, d, rank;
+  int estimator;      // SPARSEPR_EST_*
   double lambda;
 };
 
@@ -750,6 +752,37 @@ __global__ __launch_bounds__(256) void fit_kernel(FitArgs f) {
     Rw[e] = sq * (R[e] - mur[j]);
   }
   __syncthreads();
+  float* ocg = f.corr_g ? f.corr_g + (long long)h * d : nullptr;
+  if (f.estimator != SPARSEPR_EST_FULL) {
+    // restricted estimators ([paper] §5 Table 4, App. D.4): B = 0 (mean),
+    // a I (scalar, penalty lam d a^2) or diag(b) (diagonal), each minimising
+    // sum_p w~_p |Rbar_p - xbar_p B|^2 + lam |B|_F^2; folded to
+    // out = o + g * o + c with g = diag(B) / s, c = mu_R - mu_x * g
+    double sxr = 0.0, sxx = 0.0;
+    if (tid < d)
+      for (int p = 0; p < me; ++p) {
+        const double xv = Xw[p * d + tid], rv = Rw[p * d + tid];
+        sxr = fma(xv, rv, sxr);
+        sxx = fma(xv, xv, sxx);
+      }
+    const double tr = block_sum(sxr, red);
+    const double tx = block_sum(sxx, red);
+    if (tid < d) {
+      double b = 0.0;
+      if (f.estimator == SPARSEPR_EST_SCALAR) b = tr / (tx + f.lambda * double(d));
+      else if (f.estimator == SPARSEPR_EST_DIAGONAL) b = sxr / (sxx + f.lambda);
+      const double g = b / sc[tid];
+      if (ocg) ocg[tid] = float(g);
+      f.corr_c[(long long)h * d + tid] = float(mur[tid] - mux[tid] * g);
+    }
+    for (int e = tid; e < d * f.rank; e += 256) {
+      f.corr_a[(long long)h * d * f.rank + e] = 0.f;
+      f.corr_psi_t[(long long)h * f.rank * d + e] = 0.f;
+    }
+    return;
+  }
+  if (ocg)
+    for (int j = tid; j < d; j += 256) ocg[j] = 0.f;
   // 4. Gram matrices G = Xw Xw^T + lam I and E = Rw Rw^T, 32 columns of the
   // weighted features / residuals staged in LDS at a time
   for (int e = tid; e < me * me; e += 256) {
@@ -1071,6 +1104,7 @@ using namespace spr;
 
 namespace {
 int32_t probe_fit_impl(const sparsepr_dims* dims, int32_t m, int32_t rank, double lambda,
+                       int32_t estimator, float* corr_g,
                        const int32_t* offsets_q, const int32_t* offsets_kv, const int32_t* perm_q,
                        const int32_t* cell_rowptr, const int32_t* cell_col,
                        const double* centroid_q, const float* feat, int32_t fd, const void* q_g,
@@ -1084,11 +1118,14 @@ int32_t probe_fit_impl(const sparsepr_dims* dims, int32_t m, int32_t rank, doubl
   if (m < 1 || m > SPARSEPR_MAX_PROBES || rank < 0 || rank > SPARSEPR_MAX_RANK || !(lambda >= 0.0))
     return SPARSEPR_ERR_INVALID;
   if (feat ? (fd < 1 || fd > SPARSEPR_MAX_RANK) : !centroid_q) return SPARSEPR_ERR_INVALID;
+  if (estimator < SPARSEPR_EST_FULL || estimator > SPARSEPR_EST_DIAGONAL) return SPARSEPR_ERR_INVALID;
+  if (estimator != SPARSEPR_EST_FULL && !corr_g) return SPARSEPR_ERR_INVALID;
   if (!offsets_q || !offsets_kv || !perm_q || !cell_rowptr || !cell_col || !q_g ||
       !k_g || !v_g || !v_shift || !probe_rows || !probe_tokens || !o_probe_dense || !corr_a || !corr_psi_t ||
       !corr_c)
     return SPARSEPR_ERR_INVALID;
-  if (rank > 0 && lambda == 0.0) return SPARSEPR_ERR_INVALID;  // dual solve needs lam > 0
+  if (estimator == SPARSEPR_EST_FULL && rank > 0 && lambda == 0.0)
+    return SPARSEPR_ERR_INVALID;  // dual solve needs lam > 0
   const size_t need = feat ? probe_feat_ws_bytes(dims, m, rank) : probe_ws_bytes(dims, m, rank);
   if (!ws || ws_bytes < need) return SPARSEPR_ERR_WORKSPACE;
   ProbeWs w = carve_probe(ws, dims, m);
@@ -1166,6 +1203,8 @@ int32_t probe_fit_impl(const sparsepr_dims* dims, int32_t m, int32_t rank, doubl
   fa.corr_a = corr_a;
   fa.corr_psi_t = corr_psi_t;
   fa.corr_c = corr_c;
+  fa.corr_g = corr_g;
+  fa.estimator = estimator;
   fa.c_q = dims->c_q;
   fa.m = m;
   fa.me = me;
@@ -1189,23 +1228,24 @@ extern "C" int32_t sparsepr_probe_fit(const sparsepr_dims* dims, int32_t m, int3
                                       float* o_probe_sparse, float* corr_a, float* corr_psi_t,
                                       float* corr_c, void* ws, size_t ws_bytes,
                                       hipStream_t stream) {
-  return probe_fit_impl(dims, m, rank, lambda, offsets_q, offsets_kv, perm_q, cell_rowptr,
-                        cell_col, centroid_q, nullptr, 0, q_g, k_g, v_g, v_shift, softmax_scale,
+  return probe_fit_impl(dims, m, rank, lambda, SPARSEPR_EST_FULL, nullptr, offsets_q, offsets_kv,
+                        perm_q, cell_rowptr, cell_col, centroid_q, nullptr, 0, q_g, k_g, v_g,
+                        v_shift, softmax_scale,
                         probe_rows, probe_tokens, o_probe_dense, o_probe_sparse, corr_a,
                         corr_psi_t, corr_c, ws, ws_bytes, stream);
 }
 
-extern "C" int32_t sparsepr_probe_fit_feat(
-    const sparsepr_dims* dims, int32_t m, int32_t rank, double lambda, const int32_t* offsets_q,
-    const int32_t* offsets_kv, const int32_t* perm_q, const int32_t* cell_rowptr,
-    const int32_t* cell_col, const float* probe_feat, int32_t feat_dim, const void* q_g,
-    const void* k_g, const void* v_g, const int32_t* v_shift, float softmax_scale,
-    int32_t* probe_rows, int32_t* probe_tokens, float* o_probe_dense, float* o_probe_sparse,
-    float* corr_a, float* corr_psi_t, float* corr_c, void* ws, size_t ws_bytes,
-    hipStream_t stream) {
-  if (!probe_feat) return SPARSEPR_ERR_INVALID;
-  return probe_fit_impl(dims, m, rank, lambda, offsets_q, offsets_kv, perm_q, cell_rowptr,
-                        cell_col, nullptr, probe_feat, feat_dim, q_g, k_g, v_g, v_shift,
-                        softmax_scale, probe_rows, probe_tokens, o_probe_dense, o_probe_sparse,
-                        corr_a, corr_psi_t, corr_c, ws, ws_bytes, stream);
+extern "C" int32_t sparsepr_probe_fit_ex(
+    const sparsepr_dims* dims, int32_t m, int32_t rank, double lambda, int32_t estimator,
+    const int32_t* offsets_q, const int32_t* offsets_kv, const int32_t* perm_q,
+    const int32_t* cell_rowptr, const int32_t* cell_col, const double* centroid_q,
+    const float* probe_feat, int32_t feat_dim, const void* q_g, const void* k_g, const void* v_g,
+    const int32_t* v_shift, float softmax_scale, int32_t* probe_rows, int32_t* probe_tokens,
+    float* o_probe_dense, float* o_probe_sparse, float* corr_a, float* corr_psi_t, float* corr_c,
+    float* corr_g, void* ws, size_t ws_bytes, hipStream_t stream) {
+  return probe_fit_impl(dims, m, rank, lambda, estimator, corr_g, offsets_q, offsets_kv, perm_q,
+                        cell_rowptr, cell_col, probe_feat ? nullptr : centroid_q, probe_feat,
+                        feat_dim, q_g, k_g, v_g, v_shift, softmax_scale, probe_rows, probe_tokens,
+                        o_probe_dense, o_probe_sparse, corr_a, corr_psi_t, corr_c, ws, ws_bytes,
+                        stream);
 }

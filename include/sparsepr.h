@@ -61,7 +61,18 @@ enum {
   SPARSEPR_CALL_PROBE_FIT = 3,
   SPARSEPR_CALL_CORRECT = 4,
   SPARSEPR_CALL_RCP_PARTITION = 5,
-  SPARSEPR_CALL_PROBE_FIT_FEAT = 6
+  SPARSEPR_CALL_PROBE_FIT_EX = 6
+};
+
+/* Residual estimators of sparsepr_probe_fit_ex (SparsePR paper §5 Table 4,
+ * App. D.4): the full weighted ridge with output-subspace projection (the
+ * default of sparsepr_probe_fit), the weighted mean residual, and the affine
+ * variants with B = a I (scalar) and B = diag(b) (diagonal). */
+enum {
+  SPARSEPR_EST_FULL = 0,
+  SPARSEPR_EST_MEAN = 1,
+  SPARSEPR_EST_SCALAR = 2,
+  SPARSEPR_EST_DIAGONAL = 3
 };
 
 #define SPARSEPR_MAX_GROUPS 1024
@@ -90,7 +101,7 @@ typedef struct sparsepr_dims {
 } sparsepr_dims;
 
 /* Workspace bytes needed by one call (0 if it needs none).  m and rank are
- * only used by SPARSEPR_CALL_PROBE_FIT and SPARSEPR_CALL_PROBE_FIT_FEAT.
+ * only used by SPARSEPR_CALL_PROBE_FIT and SPARSEPR_CALL_PROBE_FIT_EX.
  * Returns 0 for invalid dims too; the call itself reports the error. */
 size_t sparsepr_workspace_bytes(int32_t which_call, const sparsepr_dims* dims /* host */,
                                 int32_t m, int32_t rank);
@@ -258,7 +269,7 @@ int32_t sparsepr_correct(const sparsepr_dims* dims /* host */, int32_t m, int32_
  *     partition_layout); empty groups may occur.
  *   phi_q [H][N_q][r_q]: fp32 query coordinates in token order (may be NULL;
  *     the probe distances of a response-coupled partition use them, see
- *     sparsepr_probe_fit_feat).
+ *     sparsepr_probe_fit_ex).
  *   phi_k [H][N_k][r_k]: fp32 key coordinates in token order (may be NULL).
  */
 int32_t sparsepr_rcp_partition(const sparsepr_dims* dims /* host */, int32_t m_s, int32_t r_k,
@@ -268,26 +279,51 @@ int32_t sparsepr_rcp_partition(const sparsepr_dims* dims /* host */, int32_t m_s
                                void* ws, size_t ws_bytes, hipStream_t stream);
 
 /*
- * S6-S8 with probe features.  As sparsepr_probe_fit, but the distance of a
- * row to its group's centroid is taken in the feature space `probe_feat`
- * ([H][N_q][feat_dim] fp32, token order; feat_dim 1..64): the coordinates
- * that formed the partition (SparsePR paper App. B.2: the query-response
- * coordinates stratify probe selection).  Centroids are fp64 means of the
- * features over each group, distances fp64.  Workspace:
- * sparsepr_workspace_bytes(SPARSEPR_CALL_PROBE_FIT_FEAT, dims, m, rank).
+ * S6-S8 with options.  As sparsepr_probe_fit, plus:
+ *   probe_feat [H][N_q][feat_dim] fp32 token order (feat_dim 1..64), or
+ *     NULL: when given, the distance of a row to its group's centroid is
+ *     taken in that feature space (the coordinates that formed the partition;
+ *     SparsePR paper App. B.2: the query-response coordinates stratify the
+ *     probes), with fp64 feature means and distances; centroid_q is then not
+ *     read (may be NULL).
+ *   estimator: SPARSEPR_EST_*.  The restricted estimators use the weights,
+ *     means and feature scale of the full fit and minimise the same weighted
+ *     squared error with penalty lambda * |B|_F^2 (so lambda * d * a^2 for
+ *     B = a I); the mean is not penalised and the output is not truncated
+ *     (`rank` is ignored; corr_a and corr_psi_t are zeroed).
+ *   corr_g [H][d] fp32: diagonal gain g = diag(B) / s of the folded
+ *     correction out = o + (o A) Psi^T + g * o + c; zero for
+ *     SPARSEPR_EST_FULL (may then be NULL), required otherwise.
+ * Workspace: sparsepr_workspace_bytes(SPARSEPR_CALL_PROBE_FIT_EX, dims, m, rank).
  */
-int32_t sparsepr_probe_fit_feat(const sparsepr_dims* dims /* host */, int32_t m, int32_t rank,
-                                double lambda,
-                                const int32_t* offsets_q, const int32_t* offsets_kv,
-                                const int32_t* perm_q,
-                                const int32_t* cell_rowptr, const int32_t* cell_col,
-                                const float* probe_feat, int32_t feat_dim,
-                                const void* q_g, const void* k_g, const void* v_g,
-                                const int32_t* v_shift, float softmax_scale,
-                                int32_t* probe_rows, int32_t* probe_tokens,
-                                float* o_probe_dense, float* o_probe_sparse,
-                                float* corr_a, float* corr_psi_t, float* corr_c,
-                                void* ws, size_t ws_bytes, hipStream_t stream);
+int32_t sparsepr_probe_fit_ex(const sparsepr_dims* dims /* host */, int32_t m, int32_t rank,
+                              double lambda, int32_t estimator,
+                              const int32_t* offsets_q, const int32_t* offsets_kv,
+                              const int32_t* perm_q,
+                              const int32_t* cell_rowptr, const int32_t* cell_col,
+                              const double* centroid_q,
+                              const float* probe_feat, int32_t feat_dim,
+                              const void* q_g, const void* k_g, const void* v_g,
+                              const int32_t* v_shift, float softmax_scale,
+                              int32_t* probe_rows, int32_t* probe_tokens,
+                              float* o_probe_dense, float* o_probe_sparse,
+                              float* corr_a, float* corr_psi_t, float* corr_c, float* corr_g,
+                              void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * S9 with a diagonal gain: as sparsepr_correct with
+ *   out = o + (o A) Psi^T + g * o + c
+ * for unprobed rows (corr_g [H][d] from sparsepr_probe_fit_ex; NULL means
+ * g = 0, which is sparsepr_correct).
+ */
+int32_t sparsepr_correct_ex(const sparsepr_dims* dims /* host */, int32_t m, int32_t rank,
+                            const int32_t* perm_q, const float* o_sp,
+                            const int32_t* probe_tokens, const float* o_probe_dense,
+                            const float* corr_a, const float* corr_psi_t, const float* corr_c,
+                            const float* corr_g,
+                            void* out, int32_t out_dtype,
+                            int64_t out_stride_head, int64_t out_stride_tok,
+                            void* ws, size_t ws_bytes, hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -41,6 +41,9 @@ __all__ = [
     "fit_correction",
     "fold_correction",
     "apply_correction",
+    "fit_estimator",
+    "apply_estimator",
+    "ESTIMATORS",
     "run_head",
     "executed_density",
 ]
@@ -307,11 +310,59 @@ def apply_correction(o_sp, fit):
 
 
 # ----------------------------------------------------------------------------
+# estimator variants (mean-only, scalar and diagonal affine)
+# ----------------------------------------------------------------------------
+
+ESTIMATORS = ("full", "mean", "scalar", "diagonal")
+
+
+def fit_estimator(x, R, w, lam, kind, feat_eps=1e-6):
+    """Restricted estimators compared with the full ridge ([paper] §5 Table 4
+    and App. D.4): correction by the weighted mean residual, and affine
+    variants mu_R + xbar B with B = a I (scalar) or B = diag(b) (diagonal).
+    Each minimises sum_p w~_p ||Rbar_p - xbar_p B||^2 + lam ||B||_F^2 (so the
+    scalar penalty is lam d a^2); the mean is not penalised and the output
+    is not truncated.  Weights, means and the feature scale are those of the
+    full fit.  Returns dict(g, c, ...) with the folded correction
+    out = o + g * o + c (g = diag(B) / s, c = mu_R - mu_x * g)."""
+    x = np.asarray(x, np.float64)
+    R = np.asarray(R, np.float64)
+    w = np.asarray(w, np.float64)
+    M, d = x.shape
+    w_hat = w / w.sum()
+    w_til = M * w / w.sum()
+    mu_x = w_hat @ x
+    mu_R = w_hat @ R
+    s = np.sqrt(w_hat @ (x - mu_x) ** 2 + feat_eps)
+    xb = (x - mu_x) / s
+    Rb = R - mu_R
+    if kind == "mean":
+        b = np.zeros(d)
+    elif kind == "scalar":
+        a = float(np.sum(w_til[:, None] * xb * Rb)) / (float(np.sum(w_til[:, None] * xb * xb)) + lam * d)
+        b = np.full(d, a)
+    elif kind == "diagonal":
+        b = (w_til @ (xb * Rb)) / (w_til @ (xb * xb) + lam)
+    else:
+        raise ValueError(kind)
+    g = b / s
+    c = mu_R - mu_x * g
+    return {"kind": kind, "b": b, "g": g, "c": c, "mu_x": mu_x, "mu_R": mu_R, "s": s,
+            "w_til": w_til}
+
+
+def apply_estimator(o_sp, est):
+    """Corrected rows mu_R + o + ((o - mu_x) / s) * b."""
+    o_sp = np.asarray(o_sp, np.float64)
+    return o_sp + est["mu_R"] + ((o_sp - est["mu_x"]) / est["s"]) * est["b"]
+
+
+# ----------------------------------------------------------------------------
 # whole call for one head
 # ----------------------------------------------------------------------------
 
 def run_head(q, k, v, labels_q, labels_kv, c_q, c_k, rho, m=64, rank=16, lam=0.1,
-             budget=None, features=None, query_rows=None):
+             budget=None, features=None, query_rows=None, estimator="full"):
     """Every step of one attention call for one head.
 
     query_rows: None -> sparse attention and final output for every query;
@@ -342,12 +393,18 @@ def run_head(q, k, v, labels_q, labels_kv, c_q, c_k, rho, m=64, rank=16, lam=0.1
     dense_p, _ = dense_attention_rows(q[probes], k, v, scale)
     x_p, _ = sparse_attention_rows(q[probes], pg, k, v, labels_kv, z, scale)
     R_p = dense_p - x_p
-    fit = fit_correction(x_p, R_p, w, lam, rank)
-    A, Psi, c, T = fold_correction(fit)
+    if estimator == "full":
+        fit = fit_correction(x_p, R_p, w, lam, rank)
+        A, Psi, c, T = fold_correction(fit)
+        g = np.zeros(d)
+    else:
+        fit = fit_estimator(x_p, R_p, w, lam, estimator)
+        A, Psi, T = np.zeros((d, 0)), np.zeros((d, 0)), np.zeros((d, d))
+        c, g = fit["c"], fit["g"]
 
     rows = np.arange(n_q) if query_rows is None else np.asarray(query_rows)
     o_sp, lse = sparse_attention_rows(q[rows], labels_q[rows], k, v, labels_kv, z, scale)
-    out = apply_correction(o_sp, fit)
+    out = apply_correction(o_sp, fit) if estimator == "full" else apply_estimator(o_sp, fit)
     is_probe = np.isin(rows, probes)
     if is_probe.any():
         where = {int(t): i for i, t in enumerate(probes)}
@@ -358,6 +415,6 @@ def run_head(q, k, v, labels_q, labels_kv, c_q, c_k, rho, m=64, rank=16, lam=0.1
         "qbar": qbar, "kbar": kbar, "budget": budget, "z": z, "routed_pairs": routed,
         "scores": scores, "probes": probes, "probe_counts": counts, "probe_weights": w,
         "dense_p": dense_p, "x_p": x_p, "R_p": R_p, "fit": fit, "A": A, "Psi": Psi,
-        "c": c, "T": T, "rows": rows, "o_sp": o_sp, "lse": lse, "out": out,
-        "scale": scale,
+        "c": c, "T": T, "g": g, "rows": rows, "o_sp": o_sp, "lse": lse, "out": out,
+        "scale": scale, "estimator": estimator,
     }

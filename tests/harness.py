@@ -79,7 +79,7 @@ def upload_arrays(w, arr):
 
 
 def run_gpu(w, heads_data, budget=None, rank=None, m=None, layout="hnd", out_dtype="f32",
-            overlap=True, tensors=None, fetch_heads=None, probe_feat=None):
+            overlap=True, tensors=None, fetch_heads=None, probe_feat=None, estimator="full"):
     """Runs the whole call.  Inputs come from per-head dicts (`heads_data`) or,
     for large shapes, from already uploaded `tensors` (heads_data is then
     None).  `fetch_heads` limits the per-head outputs copied back."""
@@ -100,14 +100,15 @@ def run_gpu(w, heads_data, budget=None, rank=None, m=None, layout="hnd", out_dty
                            lam=w.lam, rho=w.rho, budget=budget,
                            out_dtype=fb.F32 if out_dtype == "f32" else fb.BF16,
                            q_strides=strides, kv_strides=strides, overlap=overlap,
-                           feat_dim=0 if probe_feat is None else probe_feat.shape[-1])
+                           feat_dim=0 if probe_feat is None else probe_feat.shape[-1],
+                           estimator=estimator)
     call.probe_feat = probe_feat
     call(lq, lk, q, k, v)
     torch.cuda.synchronize()
     g = {name: getattr(call, name) for name in (
         "perm_q", "perm_kv", "offsets_q", "offsets_kv", "centroid_q", "centroid_k",
         "cell_rowptr", "cell_col", "routed_pairs", "o_sp", "lse", "probe_rows", "probe_tokens",
-        "o_probe_dense", "o_probe_sparse", "corr_a", "corr_psi_t", "corr_c", "out")}
+        "o_probe_dense", "o_probe_sparse", "corr_a", "corr_psi_t", "corr_c", "corr_g", "out")}
     out = {}
     sel = (lambda t: t) if fetch_heads is None else (lambda t: t[list(fetch_heads)])
     for key, t in g.items():
@@ -120,11 +121,12 @@ def run_gpu(w, heads_data, budget=None, rank=None, m=None, layout="hnd", out_dty
     return out
 
 
-def oracle_head(w, hd, budget=None, rank=None, m=None, rows=None, features=None):
+def oracle_head(w, hd, budget=None, rank=None, m=None, rows=None, features=None,
+                estimator="full"):
     return oracle.run_head(hd["q"], hd["k"], hd["v"], hd["labels_q"], hd["labels_kv"], w.c_q,
                            w.c_k, w.rho, m=w.m if m is None else m,
                            rank=w.r if rank is None else rank, lam=w.lam, budget=budget,
-                           features=features, query_rows=rows)
+                           features=features, query_rows=rows, estimator=estimator)
 
 
 def cells_from_csr(rowptr, col, c_q, c_k):
@@ -185,6 +187,15 @@ def compare_head(w, g, h, r, rows_orig=None, check_rows=True):
     T_gpu = g["corr_a"][h][:, :k] @ g["corr_psi_t"][h][:k, :] if k > 0 else np.zeros((d, d))
     errs["T"] = rel_fro(T_gpu, r["T"]) if np.linalg.norm(r["T"]) > 0 else float(np.abs(T_gpu).max())
     errs["c"] = rel_fro(g["corr_c"][h], r["c"])
+    assert errs["c"] <= tol, errs
+    if r.get("estimator", "full") == "full":
+        assert errs["T"] <= tol, errs
+    else:
+        # restricted estimators: diagonal gain g = diag(B) / s, no low-rank part
+        errs["g"] = (rel_fro(g["corr_g"][h], r["g"]) if np.linalg.norm(r["g"]) > 0
+                     else float(np.abs(g["corr_g"][h]).max()))
+        assert errs["g"] <= tol, errs
+        assert not np.any(g["corr_a"][h]) and not np.any(g["corr_psi_t"][h])
     # sparse output rows and final output
     if check_rows:
         rows = r["rows"]

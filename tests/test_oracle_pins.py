@@ -563,3 +563,79 @@ def test_generator_shapes_and_labels():
     x = np.array([1.0, 1.00390625, 1.01171875, -2.5e-5], dtype=np.float32)
     b = sg.f32_to_bf16_bits(x)
     assert sg.bf16_bits_to_f32(b).tolist()[:3] == [1.0, 1.0, 1.015625]
+
+
+# ----------------------------------------------------------------------------
+# estimator variants ([paper] §5 Table 4, App. D.4)
+# ----------------------------------------------------------------------------
+
+def _est_case(seed=21, M=12, d=5):
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal((M, d))
+    R = 0.3 * x @ rng.standard_normal((d, d)) + 0.1 * rng.standard_normal((M, d))
+    w = rng.uniform(0.5, 3.0, M)
+    return x, R, w
+
+
+def _objective(xb, Rb, w_til, B, lam):
+    res = Rb - xb @ B
+    return float(np.sum(w_til[:, None] * res * res) + lam * np.sum(B * B))
+
+
+def test_scalar_estimator_minimises_penalised_objective():
+    # the scalar variant minimises the common objective over B = a I, so the
+    # penalty is lam * d * a^2 (Table 4 note); brute check of the minimum
+    x, R, w = _est_case()
+    lam = 0.7
+    e = oracle.fit_estimator(x, R, w, lam, "scalar")
+    xb = (x - e["mu_x"]) / e["s"]
+    Rb = R - e["mu_R"]
+    a = e["b"][0]
+    d = x.shape[1]
+    f = lambda t: _objective(xb, Rb, e["w_til"], t * np.eye(d), lam)
+    grid = np.linspace(a - 1.0, a + 1.0, 2001)
+    vals = np.array([f(t) for t in grid])
+    assert abs(grid[np.argmin(vals)] - a) <= 1e-3
+    h = 1e-5
+    assert abs((f(a + h) - f(a - h)) / (2 * h)) < 1e-6 * max(1.0, abs(f(a)))
+
+
+def test_diagonal_estimator_is_per_dimension_ridge():
+    # diagonal variant: dimension j solves an independent ridge; checked with
+    # lstsq on the augmented system [sqrt(w~) xbar_j; sqrt(lam)] b = [sqrt(w~) Rbar_j; 0]
+    x, R, w = _est_case(22)
+    lam = 0.4
+    e = oracle.fit_estimator(x, R, w, lam, "diagonal")
+    xb = (x - e["mu_x"]) / e["s"]
+    Rb = R - e["mu_R"]
+    sw = np.sqrt(e["w_til"])
+    for j in range(x.shape[1]):
+        A = np.concatenate([sw * xb[:, j], [math.sqrt(lam)]])[:, None]
+        y = np.concatenate([sw * Rb[:, j], [0.0]])
+        bj = np.linalg.lstsq(A, y, rcond=None)[0][0]
+        assert np.isclose(e["b"][j], bj, rtol=1e-12, atol=1e-14)
+
+
+def test_estimators_coincide_in_one_dimension_and_limits():
+    # d = 1: scalar, diagonal and the full (unprojected) ridge are one model
+    x, R, w = _est_case(23, M=9, d=1)
+    lam = 0.3
+    full = oracle.fit_correction(x, R, w, lam, rank=1)
+    A, Psi, c, T = oracle.fold_correction(full)
+    for kind in ("scalar", "diagonal"):
+        e = oracle.fit_estimator(x, R, w, lam, kind)
+        assert np.allclose(e["g"], np.diag(T), rtol=1e-10)
+        assert np.allclose(e["c"], c, rtol=1e-10, atol=1e-14)
+    # mean-only: the weighted mean residual, no gain
+    x, R, w = _est_case(24)
+    e = oracle.fit_estimator(x, R, w, 0.1, "mean")
+    assert not np.any(e["g"])
+    assert np.allclose(e["c"], (w / w.sum()) @ R)
+    # lam -> infinity: every affine variant tends to the mean-only correction
+    for kind in ("scalar", "diagonal"):
+        e = oracle.fit_estimator(x, R, w, 1e12, kind)
+        assert np.abs(e["g"]).max() < 1e-9
+    # the folded form reproduces mu_R + xbar B
+    e = oracle.fit_estimator(x, R, w, 0.2, "diagonal")
+    o = np.random.default_rng(25).standard_normal((4, x.shape[1]))
+    assert np.allclose(oracle.apply_estimator(o, e), o + e["g"] * o + e["c"])
