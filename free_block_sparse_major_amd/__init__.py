@@ -24,14 +24,16 @@ LIB_PATH = os.path.join(HERE, "libsparsepr.so")
 OK, ERR_INVALID, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = range(5)
 BF16, F32 = 0, 1
 (CALL_PARTITION_LAYOUT, CALL_ROUTE_CELLS, CALL_SPARSE_ATTN, CALL_PROBE_FIT, CALL_CORRECT,
- CALL_RCP_PARTITION, CALL_PROBE_FIT_EX) = range(7)
+ CALL_RCP_PARTITION, CALL_PROBE_FIT_EX, CALL_ROUTE_CELLS_EX) = range(8)
+ROUTE_GLOBAL, ROUTE_PER_GROUP = range(2)
+ROUTE_RULES = {"global": ROUTE_GLOBAL, "per_group": ROUTE_PER_GROUP}
 EST_FULL, EST_MEAN, EST_SCALAR, EST_DIAGONAL = range(4)
 ESTIMATORS = {"full": EST_FULL, "mean": EST_MEAN, "scalar": EST_SCALAR, "diagonal": EST_DIAGONAL}
 EXPORTED = (
     "sparsepr_partition_layout", "sparsepr_route_cells", "sparsepr_sparse_attn",
     "sparsepr_probe_fit", "sparsepr_correct", "sparsepr_workspace_bytes",
     "sparsepr_status_string", "sparsepr_version", "sparsepr_rcp_partition",
-    "sparsepr_probe_fit_ex", "sparsepr_correct_ex",
+    "sparsepr_probe_fit_ex", "sparsepr_correct_ex", "sparsepr_route_cells_ex",
 )
 
 
@@ -87,6 +89,8 @@ def load_library(path: str = LIB_PATH):
     lib.sparsepr_probe_fit_ex.restype = I32
     lib.sparsepr_correct_ex.argtypes = [DP, I32, I32] + [P] * 9 + [I32, I64, I64, P, SZ, P]
     lib.sparsepr_correct_ex.restype = I32
+    lib.sparsepr_route_cells_ex.argtypes = [DP, I32, P, P, P, P, I64, P, P, P, P, SZ, P]
+    lib.sparsepr_route_cells_ex.restype = I32
     _lib = lib
     return lib
 
@@ -143,6 +147,15 @@ def sparsepr_route_cells(dims, offsets_q, offsets_kv, centroid_q, centroid_k, bu
         int(budget), _ptr(cell_rowptr), _ptr(cell_col), _ptr(routed_pairs), _ptr(ws),
         ws.numel() * ws.element_size() if ws is not None else 0, _stream(stream))
     _check(st, "sparsepr_route_cells")
+
+
+def sparsepr_route_cells_ex(dims, rule, offsets_q, offsets_kv, centroid_q, centroid_k, budget,
+                            cell_rowptr, cell_col, routed_pairs, ws, stream=None):
+    st = load_library().sparsepr_route_cells_ex(
+        ctypes.byref(dims), int(rule), _ptr(offsets_q), _ptr(offsets_kv), _ptr(centroid_q),
+        _ptr(centroid_k), int(budget), _ptr(cell_rowptr), _ptr(cell_col), _ptr(routed_pairs),
+        _ptr(ws), ws.numel() * ws.element_size() if ws is not None else 0, _stream(stream))
+    _check(st, "sparsepr_route_cells_ex")
 
 
 def sparsepr_sparse_attn(dims, offsets_q, offsets_kv, cell_rowptr, cell_col, q_g, k_g, v_g,
@@ -244,6 +257,12 @@ def routed_pair_budget(rho, n_q, n_k, m):
     return max(0, math.ceil((Fraction(rho) * n_q - m_eff) * n_k))
 
 
+def key_token_budget(rho, n_q, n_k, m):
+    """Key tokens per query of the per-group rule: ceil((rho*N_q - M_eff)*N_k/N_q), >= 0."""
+    m_eff = min(m, n_q)
+    return max(0, math.ceil((Fraction(rho) * n_q - m_eff) * n_k / n_q))
+
+
 class SparsePRCall:
     """Device buffers and stream plumbing for repeated calls of one shape.
 
@@ -253,11 +272,18 @@ class SparsePRCall:
 
     def __init__(self, heads, n_q, n_k, head_dim, dtype, c_q, c_k, m=64, rank=16, lam=0.1,
                  rho="0.26", budget=None, out_dtype=F32, device="cuda", q_strides=None,
-                 kv_strides=None, overlap=True, feat_dim=0, estimator="full"):
+                 kv_strides=None, overlap=True, feat_dim=0, estimator="full",
+                 route_rule="global"):
         load_library()
         self.dims = make_dims(heads, n_q, n_k, head_dim, dtype, c_q, c_k, q_strides, kv_strides)
         self.m, self.rank, self.lam = m, rank, lam
-        self.budget = routed_pair_budget(rho, n_q, n_k, m) if budget is None else int(budget)
+        self.route_rule = ROUTE_RULES[route_rule]
+        if budget is not None:
+            self.budget = int(budget)
+        elif self.route_rule == ROUTE_GLOBAL:
+            self.budget = routed_pair_budget(rho, n_q, n_k, m)
+        else:
+            self.budget = key_token_budget(rho, n_q, n_k, m)
         self.scale = 1.0 / math.sqrt(head_dim)
         self.out_dtype = out_dtype
         self.overlap = overlap
@@ -303,7 +329,8 @@ class SparsePRCall:
             return torch.empty(max(nb, 256), dtype=torch.uint8, device=dev)
 
         self.ws_layout = ws(CALL_PARTITION_LAYOUT)
-        self.ws_route = ws(CALL_ROUTE_CELLS)
+        self.ws_route = ws(CALL_ROUTE_CELLS if self.route_rule == ROUTE_GLOBAL
+                           else CALL_ROUTE_CELLS_EX)
         self.ws_attn = ws(CALL_SPARSE_ATTN)
         self._ex = bool(feat_dim) or self.estimator != EST_FULL
         self.ws_probe = ws(CALL_PROBE_FIT_EX if self._ex else CALL_PROBE_FIT)
@@ -320,6 +347,12 @@ class SparsePRCall:
                                   self.ws_layout, stream)
 
     def route(self, stream=None):
+        if self.route_rule != ROUTE_GLOBAL:
+            sparsepr_route_cells_ex(self.dims, self.route_rule, self.offsets_q, self.offsets_kv,
+                                    self.centroid_q, self.centroid_k, self.budget,
+                                    self.cell_rowptr, self.cell_col, self.routed_pairs,
+                                    self.ws_route, stream)
+            return
         sparsepr_route_cells(self.dims, self.offsets_q, self.offsets_kv, self.centroid_q,
                              self.centroid_k, self.budget, self.cell_rowptr, self.cell_col,
                              self.routed_pairs, self.ws_route, stream)

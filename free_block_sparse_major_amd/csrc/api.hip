@@ -5,6 +5,7 @@ namespace spr {
 
 size_t layout_ws_bytes(const sparsepr_dims* d);
 size_t route_ws_bytes(const sparsepr_dims* d);
+size_t route_ex_ws_bytes(const sparsepr_dims* d);
 size_t attn_ws_bytes(const sparsepr_dims* d);
 size_t probe_ws_bytes(const sparsepr_dims* d, int32_t m, int32_t rank);
 size_t probe_feat_ws_bytes(const sparsepr_dims* d, int32_t m, int32_t rank);
@@ -44,6 +45,7 @@ extern "C" size_t sparsepr_workspace_bytes(int32_t which, const sparsepr_dims* d
       return spr::probe_ws_bytes(dims, m, rank);
     case SPARSEPR_CALL_CORRECT: return 0;
     case SPARSEPR_CALL_RCP_PARTITION: return spr::rcp_ws_bytes(dims);
+    case SPARSEPR_CALL_ROUTE_CELLS_EX: return spr::route_ex_ws_bytes(dims);
     case SPARSEPR_CALL_PROBE_FIT_EX:
       if (m < 1 || m > SPARSEPR_MAX_PROBES || rank < 0 || rank > SPARSEPR_MAX_RANK) return 0;
       return spr::probe_feat_ws_bytes(dims, m, rank);

@@ -344,7 +344,153 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
   if (tid == 0) routed[h] = P;
 }
 
+// ---------------------------------------------------------------------------
+// Per-group rule ([paper] §4.3): each query group ranks the non-empty K/V
+// groups by decreasing score (ties -> smaller b) and keeps the shortest
+// prefix whose key-token count reaches the common per-query budget (at
+// least its top cell).  One block per (a, h) sorts its row of scores in LDS
+// (bitonic, (ordered score, b) keys), scans the group sizes in that order
+// and writes its selected b ascending into a per-row slot; a per-head scan
+// gives the CSR row pointers and a copy pass compacts the rows.
+// ---------------------------------------------------------------------------
+// fp64 -> uint64 whose ascending order is the descending order of the score
+SPR_DEV unsigned long long desc_key(double s) {
+  unsigned long long u = __double_as_longlong(s);
+  u = (u >> 63) ? ~u : (u | 0x8000000000000000ull);   // ascending order of s
+  return ~u;
+}
+
+__global__ __launch_bounds__(256) void group_route_kernel(
+    const double* __restrict__ scores, const int32_t* __restrict__ off_q,
+    const int32_t* __restrict__ off_k, int c_q, int c_k, long long key_budget,
+    int32_t* __restrict__ slots, int32_t* __restrict__ counts, long long* __restrict__ pairs) {
+  const int a = blockIdx.x, h = blockIdx.y, tid = threadIdx.x;
+  constexpr int N = SPARSEPR_MAX_GROUPS;
+  __shared__ unsigned long long key[N];
+  __shared__ int32_t idx[N];
+  __shared__ int32_t take[N];
+  __shared__ long long red[4];
+  const int32_t* oq = off_q + (long long)h * (c_q + 1);
+  const int32_t* ok = off_k + (long long)h * (c_k + 1);
+  const long long na = oq[a + 1] - oq[a];
+  const long long row = (long long)h * c_q + a;
+  if (na == 0) {
+    if (tid == 0) {
+      counts[row] = 0;
+      pairs[row] = 0;
+    }
+    return;
+  }
+  int np2 = 1;
+  while (np2 < c_k) np2 <<= 1;
+  const double* S = scores + row * c_k;
+  for (int b = tid; b < np2; b += 256) {
+    const bool ne = b < c_k && ok[b + 1] > ok[b];
+    key[b] = ne ? desc_key(S[b]) : ~0ull;   // empty / padding sort last
+    idx[b] = b;
+    take[b] = 0;
+  }
+  __syncthreads();
+  for (int size = 2; size <= np2; size <<= 1) {
+    for (int stride = size >> 1; stride > 0; stride >>= 1) {
+      for (int p = tid; p < np2 / 2; p += 256) {
+        const int i = 2 * p - (p & (stride - 1)), j = i + stride;
+        const bool up = (i & size) == 0;
+        const unsigned long long ki = key[i], kj = key[j];
+        const int ii = idx[i], ij = idx[j];
+        const bool gt = ki > kj || (ki == kj && ii > ij);
+        if (gt == up) {
+          key[i] = kj;
+          key[j] = ki;
+          idx[i] = ij;
+          idx[j] = ii;
+        }
+      }
+      __syncthreads();
+    }
+  }
+  // inclusive prefix of group sizes in sorted order (4 entries per thread)
+  long long v[4], loc = 0;
+  const int base = 4 * tid;
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int i = base + u;
+    v[u] = (i < np2 && key[i] != ~0ull) ? (long long)(ok[idx[i] + 1] - ok[idx[i]]) : 0;
+    loc += v[u];
+  }
+  long long tot;
+  long long run = block_exclusive_scan(loc, red, &tot);
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int i = base + u;
+    // selected: non-empty and the prefix before it is still below the budget
+    // (the top cell always)
+    if (i < np2 && key[i] != ~0ull && (i == 0 || run < key_budget)) take[idx[i]] = 1;
+    run += v[u];
+  }
+  __syncthreads();
+  // selected b ascending into the row's slot, and the row's pair count
+  long long cnt = 0, keys = 0;
+  int t4[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int b = base + u;
+    t4[u] = b < c_k ? take[b] : 0;
+    cnt += t4[u];
+    keys += t4[u] ? (long long)(ok[b + 1] - ok[b]) : 0;
+  }
+  long long ntot;
+  long long pos = block_exclusive_scan(cnt, red, &ntot);
+  const long long ksum = block_sum(keys, red);
+  int32_t* out = slots + row * c_k;
+#pragma unroll
+  for (int u = 0; u < 4; ++u)
+    if (t4[u]) out[pos++] = base + u;
+  if (tid == 0) {
+    counts[row] = int32_t(ntot);
+    pairs[row] = na * ksum;
+  }
+}
+
+// per head: row pointers (exclusive scan of the counts) and the pair total
+__global__ __launch_bounds__(1024) void group_rowptr_kernel(const int32_t* __restrict__ counts,
+                                                            const long long* __restrict__ pairs,
+                                                            int c_q, int32_t* __restrict__ rowptr,
+                                                            long long* __restrict__ routed) {
+  const int h = blockIdx.x, tid = threadIdx.x;
+  __shared__ long long red[16];
+  const long long c = tid < c_q ? counts[(long long)h * c_q + tid] : 0;
+  const long long p = tid < c_q ? pairs[(long long)h * c_q + tid] : 0;
+  long long tot;
+  const long long ex = block_exclusive_scan(c, red, &tot);
+  if (tid < c_q) rowptr[(long long)h * (c_q + 1) + tid] = int32_t(ex);
+  if (tid == 0) rowptr[(long long)h * (c_q + 1) + c_q] = int32_t(tot);
+  const long long ps = block_sum(p, red);
+  if (tid == 0) routed[h] = ps;
+}
+
+__global__ __launch_bounds__(256) void group_copy_kernel(const int32_t* __restrict__ slots,
+                                                         const int32_t* __restrict__ counts,
+                                                         const int32_t* __restrict__ rowptr,
+                                                         int c_q, int c_k,
+                                                         int32_t* __restrict__ col) {
+  const int a = blockIdx.x, h = blockIdx.y;
+  const long long row = (long long)h * c_q + a;
+  const int n = counts[row], dst = rowptr[(long long)h * (c_q + 1) + a];
+  for (int i = threadIdx.x; i < n; i += 256)
+    col[(long long)h * c_q * c_k + dst + i] = slots[row * c_k + i];
+}
+
 }  // namespace
+
+size_t route_ex_ws_bytes(const sparsepr_dims* d) {
+  Carver cv(nullptr);
+  cv.take<double>(size_t(d->heads) * d->c_q * d->c_k);
+  cv.take<int32_t>(size_t(d->heads) * d->c_q * d->c_k);
+  cv.take<int32_t>(size_t(d->heads) * d->c_q);
+  cv.take<long long>(size_t(d->heads) * d->c_q);
+  return cv.used;
+}
 
 size_t route_ws_bytes(const sparsepr_dims* d) {
   Carver cv(nullptr);
@@ -355,6 +501,47 @@ size_t route_ws_bytes(const sparsepr_dims* d) {
 }  // namespace spr
 
 using namespace spr;
+
+extern "C" int32_t sparsepr_route_cells_ex(const sparsepr_dims* dims, int32_t rule,
+                                           const int32_t* offsets_q, const int32_t* offsets_kv,
+                                           const double* centroid_q, const double* centroid_k,
+                                           int64_t budget, int32_t* cell_rowptr,
+                                           int32_t* cell_col, int64_t* routed_pairs, void* ws,
+                                           size_t ws_bytes, hipStream_t stream) {
+  if (rule == SPARSEPR_ROUTE_GLOBAL)
+    return sparsepr_route_cells(dims, offsets_q, offsets_kv, centroid_q, centroid_k, budget,
+                                cell_rowptr, cell_col, routed_pairs, ws, ws_bytes, stream);
+  if (rule != SPARSEPR_ROUTE_PER_GROUP) return SPARSEPR_ERR_INVALID;
+  int32_t st = check_dims(dims);
+  if (st != SPARSEPR_OK) return st;
+  if (!offsets_q || !offsets_kv || !centroid_q || !centroid_k || !cell_rowptr || !cell_col ||
+      !routed_pairs)
+    return SPARSEPR_ERR_INVALID;
+  const size_t need = route_ex_ws_bytes(dims);
+  if (!ws || ws_bytes < need) return SPARSEPR_ERR_WORKSPACE;
+  const int H = dims->heads, d = dims->head_dim;
+  Carver cv(ws);
+  double* scores = cv.take<double>(size_t(H) * dims->c_q * dims->c_k);
+  int32_t* slots = cv.take<int32_t>(size_t(H) * dims->c_q * dims->c_k);
+  int32_t* counts = cv.take<int32_t>(size_t(H) * dims->c_q);
+  long long* pairs = cv.take<long long>(size_t(H) * dims->c_q);
+  dim3 g1((dims->c_q + 15) / 16, (dims->c_k + 63) / 64, H);
+  score_kernel<<<g1, 256, 0, stream>>>(centroid_q, centroid_k, scores, dims->c_q, dims->c_k, d,
+                                       __builtin_sqrt(double(d)));
+  SPR_LAUNCH_CHECK();
+  group_route_kernel<<<dim3(dims->c_q, H), 256, 0, stream>>>(scores, offsets_q, offsets_kv,
+                                                             dims->c_q, dims->c_k,
+                                                             (long long)budget, slots, counts,
+                                                             pairs);
+  SPR_LAUNCH_CHECK();
+  group_rowptr_kernel<<<H, 1024, 0, stream>>>(counts, pairs, dims->c_q, cell_rowptr,
+                                              (long long*)routed_pairs);
+  SPR_LAUNCH_CHECK();
+  group_copy_kernel<<<dim3(dims->c_q, H), 256, 0, stream>>>(slots, counts, cell_rowptr, dims->c_q,
+                                                            dims->c_k, cell_col);
+  SPR_LAUNCH_CHECK();
+  return SPARSEPR_OK;
+}
 
 extern "C" int32_t sparsepr_route_cells(const sparsepr_dims* dims, const int32_t* offsets_q,
                                         const int32_t* offsets_kv, const double* centroid_q,

@@ -61,7 +61,14 @@ enum {
   SPARSEPR_CALL_PROBE_FIT = 3,
   SPARSEPR_CALL_CORRECT = 4,
   SPARSEPR_CALL_RCP_PARTITION = 5,
-  SPARSEPR_CALL_PROBE_FIT_EX = 6
+  SPARSEPR_CALL_PROBE_FIT_EX = 6,
+  SPARSEPR_CALL_ROUTE_CELLS_EX = 7
+};
+
+/* Routing rules of sparsepr_route_cells_ex. */
+enum {
+  SPARSEPR_ROUTE_GLOBAL = 0,     /* sparsepr_route_cells: one pair budget per head */
+  SPARSEPR_ROUTE_PER_GROUP = 1   /* a common key-token budget per query */
 };
 
 /* Residual estimators of sparsepr_probe_fit_ex (SparsePR paper §5 Table 4,
@@ -166,6 +173,23 @@ int32_t sparsepr_route_cells(const sparsepr_dims* dims /* host */,
                              int64_t routed_pair_budget,
                              int32_t* cell_rowptr, int32_t* cell_col, int64_t* routed_pairs,
                              void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * S4 with a choice of rule.  SPARSEPR_ROUTE_GLOBAL is sparsepr_route_cells
+ * (`budget` = routed pairs).  SPARSEPR_ROUTE_PER_GROUP is the rule of the
+ * SparsePR paper §4.3: every non-empty query group ranks the non-empty K/V
+ * groups by decreasing score s_ab (fp64 centroid logit; ties -> smaller b)
+ * and keeps the shortest prefix whose key tokens sum(|G_b|) reach `budget`
+ * (key tokens per query: the caller passes ceil((rho*N_q - M) * N_k / N_q));
+ * a group keeps at least its top cell.  Outputs as sparsepr_route_cells.
+ * Workspace: sparsepr_workspace_bytes(SPARSEPR_CALL_ROUTE_CELLS_EX, ...).
+ */
+int32_t sparsepr_route_cells_ex(const sparsepr_dims* dims /* host */, int32_t rule,
+                                const int32_t* offsets_q, const int32_t* offsets_kv,
+                                const double* centroid_q, const double* centroid_k,
+                                int64_t budget,
+                                int32_t* cell_rowptr, int32_t* cell_col, int64_t* routed_pairs,
+                                void* ws, size_t ws_bytes, hipStream_t stream);
 
 /*
  * S5. Renormalised hard-drop attention.  (SparsePR paper §3: a query of

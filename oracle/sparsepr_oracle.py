@@ -33,6 +33,8 @@ __all__ = [
     "group_means",
     "routed_pair_budget",
     "route_cells",
+    "key_token_budget",
+    "route_cells_per_group",
     "sparse_attention",
     "sparse_attention_rows",
     "dense_attention_rows",
@@ -145,6 +147,46 @@ def route_cells(qbar, kbar, n_a, m_b, budget, head_dim):
         take = min(k + 1, A.size)
         z[A[:take], B[:take]] = True
         pairs = int(cum[take - 1])
+    return z, pairs, s
+
+
+def key_token_budget(rho, n_q, n_k, m):
+    """Common key-token budget per query of the per-group rule: rho_route * N_k
+    with rho_route = rho - M/N_q ([paper] §4.3), i.e. (rho*N_q - M)*N_k/N_q;
+    READING: "reaches" the budget is the same as reaching its ceiling,
+    computed exactly; clamped at 0."""
+    m_eff = min(m, n_q)
+    b = (Fraction(rho) * n_q - m_eff) * n_k / n_q
+    return max(0, math.ceil(b))
+
+
+def route_cells_per_group(qbar, kbar, n_a, m_b, key_budget, head_dim):
+    """The pages' routing rule ([paper] §4.3): each query group ranks the
+    non-empty K/V groups by decreasing score and keeps the shortest prefix
+    whose key-token count reaches the common per-query budget; a cell costs
+    |G_a||G_b| interactions.  The score is the centroid logit (READING: the
+    value-aware score is not printed); ties go to the smaller b.  READING:
+    with a budget of 0 a group still keeps its top cell.
+
+    Returns z [Cq, Ck] bool, routed pair count, score matrix."""
+    n_a = np.asarray(n_a, dtype=np.int64)
+    m_b = np.asarray(m_b, dtype=np.int64)
+    Cq, Ck = n_a.size, m_b.size
+    s = np.full((Cq, Ck), -np.inf)
+    qa = np.nonzero(n_a > 0)[0]
+    kb = np.nonzero(m_b > 0)[0]
+    z = np.zeros((Cq, Ck), dtype=bool)
+    if not (qa.size and kb.size):
+        return z, 0, s
+    s[np.ix_(qa, kb)] = (qbar[qa] @ kbar[kb].T) / math.sqrt(head_dim)
+    pairs = 0
+    for a in qa:
+        order = kb[np.lexsort((kb, -s[a, kb]))]       # score desc, then b asc
+        cum = np.cumsum(m_b[order])
+        k = int(np.searchsorted(cum, key_budget, side="left"))   # first prefix reaching it
+        take = max(1, min(k + 1, order.size))
+        z[a, order[:take]] = True
+        pairs += int(n_a[a] * cum[take - 1])
     return z, pairs, s
 
 
@@ -362,7 +404,8 @@ def apply_estimator(o_sp, est):
 # ----------------------------------------------------------------------------
 
 def run_head(q, k, v, labels_q, labels_kv, c_q, c_k, rho, m=64, rank=16, lam=0.1,
-             budget=None, features=None, query_rows=None, estimator="full"):
+             budget=None, features=None, query_rows=None, estimator="full",
+             route_rule="global"):
     """Every step of one attention call for one head.
 
     query_rows: None -> sparse attention and final output for every query;
@@ -382,9 +425,14 @@ def run_head(q, k, v, labels_q, labels_kv, c_q, c_k, rho, m=64, rank=16, lam=0.1
     m_b = np.diff(off_kv)
     qbar = group_means(q, labels_q, c_q)
     kbar = group_means(k, labels_kv, c_k)
-    if budget is None:
-        budget = routed_pair_budget(rho, n_q, n_k, m)
-    z, routed, scores = route_cells(qbar, kbar, n_a, m_b, budget, d)
+    if route_rule == "global":
+        if budget is None:
+            budget = routed_pair_budget(rho, n_q, n_k, m)
+        z, routed, scores = route_cells(qbar, kbar, n_a, m_b, budget, d)
+    else:
+        if budget is None:
+            budget = key_token_budget(rho, n_q, n_k, m)
+        z, routed, scores = route_cells_per_group(qbar, kbar, n_a, m_b, budget, d)
 
     feats = q if features is None else np.asarray(features, np.float64)
     probes, counts = select_probes(feats, labels_q, c_q, m)

@@ -639,3 +639,73 @@ def test_estimators_coincide_in_one_dimension_and_limits():
     e = oracle.fit_estimator(x, R, w, 0.2, "diagonal")
     o = np.random.default_rng(25).standard_normal((4, x.shape[1]))
     assert np.allclose(oracle.apply_estimator(o, e), o + e["g"] * o + e["c"])
+
+
+# ----------------------------------------------------------------------------
+# per-group routing rule ([paper] §4.3)
+# ----------------------------------------------------------------------------
+
+def test_key_token_budget_hand_values():
+    # (rho*N_q - M) * N_k / N_q, ceiling: 0.22 at the Wan shape
+    # (0.22*75600 - 64) * 75600 / 75600 = 16568 exactly
+    assert oracle.key_token_budget("0.22", 75600, 75600, 64) == 16568
+    # 0.26 at 4096 tokens: (1064.96 - 64) = 1000.96 -> 1001
+    assert oracle.key_token_budget("0.26", 4096, 4096, 64) == 1001
+    assert oracle.key_token_budget("0.01", 4096, 4096, 64) == 0
+
+
+def _brute_per_group(qbar, kbar, n_a, m_b, budget, d):
+    """Written out with plain loops: for every non-empty query group, every
+    prefix of the (score desc, b asc) order is tried from the shortest."""
+    Cq, Ck = len(n_a), len(m_b)
+    z = np.zeros((Cq, Ck), bool)
+    pairs = 0
+    for a in range(Cq):
+        if n_a[a] == 0:
+            continue
+        cand = [(-float(np.dot(qbar[a], kbar[b]) / math.sqrt(d)), b) for b in range(Ck) if m_b[b] > 0]
+        cand.sort()
+        chosen = []
+        total = 0
+        for _, b in cand:
+            chosen.append(b)
+            total += m_b[b]
+            if total >= budget:
+                break
+        for b in chosen:
+            z[a, b] = True
+        pairs += n_a[a] * total
+    return z, pairs
+
+
+def test_per_group_routing_brute_force_with_ties():
+    rng = np.random.default_rng(31)
+    d = 4
+    for trial in range(30):
+        Cq, Ck = 5, 7
+        qbar = rng.integers(-2, 3, (Cq, d)).astype(float)     # integer data: exact ties
+        kbar = rng.integers(-2, 3, (Ck, d)).astype(float)
+        n_a = rng.integers(0, 4, Cq)
+        m_b = rng.integers(0, 5, Ck)
+        if m_b.sum() == 0:
+            m_b[0] = 1
+        for budget in (0, 1, 3, 6, 50):
+            z, pairs, _ = oracle.route_cells_per_group(qbar, kbar, n_a, m_b, budget, d)
+            zb, pb = _brute_per_group(qbar, kbar, n_a, m_b, budget, d)
+            assert np.array_equal(z, zb) and pairs == pb, (trial, budget)
+            # invariants: every non-empty group keeps a cell, reaches the budget
+            # unless it holds every non-empty K/V group, and is minimal
+            for a in np.nonzero(n_a)[0]:
+                keys = int(m_b[z[a]].sum())
+                assert z[a].any()
+                assert keys >= budget or z[a].sum() == (m_b > 0).sum()
+            assert not z[:, m_b == 0].any() and not z[n_a == 0].any()
+
+
+def test_per_group_full_budget_selects_everything():
+    rng = np.random.default_rng(32)
+    qbar, kbar = rng.standard_normal((3, 5)), rng.standard_normal((6, 5))
+    n_a, m_b = np.array([2, 0, 3]), np.array([1, 4, 0, 2, 2, 1])
+    z, pairs, _ = oracle.route_cells_per_group(qbar, kbar, n_a, m_b, int(m_b.sum()), 5)
+    assert np.array_equal(z, np.outer(n_a > 0, m_b > 0))
+    assert pairs == int(n_a.sum() * m_b.sum())
