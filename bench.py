@@ -67,7 +67,8 @@ def _traffic_from_profile(workload_name):
     return float(m_b.group(1))
 
 
-def cpu_baseline(w, arrays, budget_seconds=20.0, rcp_params=None):
+def cpu_baseline(w, arrays, budget_seconds=20.0, rcp_params=None, estimator="full",
+                 route_rule="global"):
     """The oracle, as it is, on the host cores: head 0 in full except the
     sparse attention, which runs on whole query groups until ~budget_seconds;
     scaled to ms per call over all heads and all rows."""
@@ -94,7 +95,8 @@ def cpu_baseline(w, arrays, budget_seconds=20.0, rcp_params=None):
                                         rcp_params["r_q"], w.c_q, ik, iq, rcp_params["iters"])
         lq, lk, feats = part["labels_q"], part["labels_kv"], part["phi_q"]
     r = oracle.run_head(q, k, v, lq, lk, w.c_q, w.c_k, w.rho, m=w.m, rank=w.r, lam=w.lam,
-                        features=feats, query_rows=np.zeros(0, np.int64))
+                        features=feats, query_rows=np.zeros(0, np.int64), estimator=estimator,
+                        route_rule=route_rule)
     t_fixed = time.time() - t0
     # sparse attention + correction on whole query groups, largest first
     sizes = np.diff(r["offsets_q"])
@@ -105,7 +107,10 @@ def cpu_baseline(w, arrays, budget_seconds=20.0, rcp_params=None):
         rows = r["perm_q"][r["offsets_q"][a]:r["offsets_q"][a + 1]]
         t1 = time.time()
         o, _ = oracle.sparse_attention_rows(q[rows], lq[rows], k, v, lk, r["z"], r["scale"])
-        oracle.apply_correction(o, r["fit"])
+        if estimator == "full":
+            oracle.apply_correction(o, r["fit"])
+        else:
+            oracle.apply_estimator(o, r["fit"])
         t_rows += time.time() - t1
         rows_done += rows.size
     per_head = t_fixed + t_rows * (w.n / max(rows_done, 1))
@@ -128,6 +133,9 @@ def main():
     ap.add_argument("--rho", default=None, help="override the executed-density target")
     ap.add_argument("--estimator", default="full", choices=("full", "mean", "scalar", "diagonal"),
                     help="residual estimator (the full ridge with projection is the default)")
+    ap.add_argument("--route-rule", default="global", choices=("global", "per_group"),
+                    help="cell selection: one executed-pair budget per head (default) or a "
+                         "key-token budget per query group")
     ap.add_argument("--dense-own", action="store_true",
                     help="also time this library in dense mode (one group, every cell)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MB",
@@ -176,7 +184,8 @@ def main():
     rp = sg.RCP_PARAMS if rcp else None
     call = fb.SparsePRCall(w.heads, w.n, w.n, w.head_dim, dtype, w.c_q, w.c_k, m=w.m, rank=w.r,
                            lam=w.lam, rho=w.rho, out_dtype=fb.BF16 if w.dtype == "bf16" else fb.F32,
-                           feat_dim=rp["r_q"] if rcp else 0, estimator=args.estimator)
+                           feat_dim=rp["r_q"] if rcp else 0, estimator=args.estimator,
+                           route_rule=args.route_rule)
     part = None
     if rcp:
         part = fb.RcpPartition(w.heads, w.n, w.n, w.head_dim, dtype, w.c_q, w.c_k, **rp)
@@ -260,6 +269,7 @@ def main():
             "heads": H, "tokens": n, "head_dim": d, "c_q": w.c_q, "c_k": w.c_k,
             "rho_target": w.rho, "m": w.m, "r": w.r, "lambda": w.lam,
             "estimator": args.estimator,
+            "route_rule": args.route_rule,
             "parallelism": "single GPU",
         },
         "executed_pair_tflops": round(call_tflops, 2),
@@ -287,7 +297,7 @@ def main():
             cs = fb.SparsePRCall(w.heads, w.n, w.n, w.head_dim, dtype, w.c_q, w.c_k, m=w.m,
                                  rank=w.r, lam=w.lam, rho=rho,
                                  out_dtype=fb.BF16 if w.dtype == "bf16" else fb.F32,
-                                 feat_dim=rp["r_q"])
+                                 feat_dim=rp["r_q"], route_rule=args.route_rule)
             cs.probe_feat = part.phi_q
             for _ in range(2):
                 step(cs)
@@ -355,7 +365,7 @@ def main():
         c26 = fb.SparsePRCall(w.heads, w.n, w.n, w.head_dim, dtype, w.c_q, w.c_k, m=w.m,
                               rank=w.r, lam=w.lam, rho="0.26",
                               out_dtype=fb.BF16 if w.dtype == "bf16" else fb.F32,
-                              feat_dim=rp["r_q"] if rcp else 0)
+                              feat_dim=rp["r_q"] if rcp else 0, route_rule=args.route_rule)
         c26.probe_feat = part.phi_q if rcp else None
         for _ in range(2):
             step(c26)
@@ -380,7 +390,8 @@ def main():
         out["dense_own_attn_ms"] = round(own_ms, 3)
         out["dense_own_tflops"] = round(4.0 * d * H * n * n / (own_ms * 1e-3) / 1e12, 1)
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(w, arr, rcp_params=rp)
+        out["cpu_baseline"] = cpu_baseline(w, arr, rcp_params=rp, estimator=args.estimator,
+                                           route_rule=args.route_rule)
         out["cpu_baseline"]["value"] = round(out["cpu_baseline"]["value"], 1)
     print(json.dumps(out), flush=True)
 
