@@ -219,3 +219,153 @@ def test_ari_helper_against_brute_pairs():
     assert _ari(a, a) == pytest.approx(1.0)
     assert ari(a, b) == pytest.approx(expect)
     assert ari(b + 7, (a * 3) % 5) == pytest.approx(_ari(b + 7, (a * 3) % 5))
+
+
+# ----------------------------------------------------------------------------
+# later calls: subspace-iteration factors and warm-started k-means
+# ([paper] App. C.1)
+# ----------------------------------------------------------------------------
+
+def _spd(d, lam, rng):
+    v = _orthogonal(d, rng)
+    return v @ np.diag(lam) @ v.T, v
+
+
+def _projector(x):
+    qx, _ = np.linalg.qr(x)
+    return qx @ qx.T
+
+
+def test_cholesky_drop_matches_numpy_and_drops_dependent_columns():
+    rng = np.random.default_rng(40)
+    y = rng.standard_normal((9, 5))
+    g = y.T @ y
+    low = rcp.cholesky_drop(g)
+    assert np.allclose(low, np.linalg.cholesky(g), atol=1e-12)
+    # column 3 a combination of columns 0 and 1: its pivot vanishes
+    y[:, 3] = 2.0 * y[:, 0] - y[:, 1]
+    low = rcp.cholesky_drop(y.T @ y)
+    assert not np.any(low[:, 3])
+    x = rcp.cholesky_orthonormalise(y)
+    assert not np.any(x[:, 3])
+    keep = [0, 1, 2, 4]
+    assert np.allclose(x[:, keep].T @ x[:, keep], np.eye(4), atol=1e-12)
+    # the kept columns span Y's column space
+    assert np.allclose(x @ (x.T @ y), y, atol=1e-10)
+    # Gram-Schmidt order: column j lies in the span of Y's first j+1 columns
+    for j in keep:
+        sub = y[:, :j + 1]
+        assert np.allclose(sub @ np.linalg.lstsq(sub, x[:, j], rcond=None)[0], x[:, j], atol=1e-10)
+
+
+def test_subspace_factor_fixed_point_at_eigenbasis():
+    # from the exact leading eigenvectors of an unchanged metric, M U = U Lam,
+    # the Cholesky factor is Lam and the basis, weights and factor repeat
+    rng = np.random.default_rng(41)
+    lam = np.array([9.0, 6.0, 4.0, 2.5, 1.0, 0.5, 0.2, 0.1])
+    m, _ = _spd(8, lam, rng)
+    u, lam_r, f = rcp.response_basis(m, 3)
+    x, lam_x, f_x = rcp.subspace_factor(m, u, steps=2)
+    assert np.allclose(x, u, atol=1e-12)
+    assert np.allclose(lam_x, lam[:3], rtol=1e-12)
+    assert np.allclose(f_x, f, atol=1e-12)
+
+
+def test_subspace_two_steps_span_m_squared_start():
+    # two orthogonal-iteration steps span M^2 X0, with orthonormal columns
+    rng = np.random.default_rng(42)
+    m, _ = _spd(10, np.linspace(5.0, 0.5, 10), rng)
+    x0 = rng.standard_normal((10, 4))
+    x, lam_x, _ = rcp.subspace_factor(m, x0, steps=2)
+    assert np.allclose(x.T @ x, np.eye(4), atol=1e-12)
+    assert np.allclose(_projector(x), _projector(m @ m @ x0), atol=1e-10)
+    assert np.allclose(lam_x, [x[:, j] @ m @ x[:, j] for j in range(4)], rtol=1e-12)
+
+
+def test_subspace_converges_to_eigen_factor_full_and_deficient_rank():
+    rng = np.random.default_rng(43)
+    # distinct eigenvalues with a gap after the third
+    m, _ = _spd(7, np.array([8.0, 5.0, 3.0, 0.4, 0.3, 0.2, 0.1]), rng)
+    x, _, f = rcp.subspace_factor(m, rng.standard_normal((7, 3)), steps=300)
+    f_ref = rcp.response_factor(m, 3)
+    assert np.allclose(f @ f.T, f_ref @ f_ref.T, atol=1e-9)
+    # rank 2 metric asked for 4 directions: two columns drop, the weights of
+    # the rest are the eigenvalues over the mean of all 4 (zeros included)
+    m2, _ = _spd(6, np.array([3.0, 1.0, 0.0, 0.0, 0.0, 0.0]), rng)
+    x, lam_x, f = rcp.subspace_factor(m2, rng.standard_normal((6, 4)), steps=300)
+    assert int(np.sum(np.any(x != 0.0, axis=0))) == 2
+    f_ref = rcp.response_factor(m2, 4)
+    assert np.allclose(f @ f.T, f_ref @ f_ref.T, atol=1e-9)
+    # a rotated basis of the exact eigenspace: the span and the trace of the
+    # Rayleigh quotients are kept after two steps
+    u, lam_r, _ = rcp.response_basis(m, 3)
+    rot = _orthogonal(3, rng)
+    x, lam_x, _ = rcp.subspace_factor(m, u @ rot, steps=2)
+    assert np.allclose(_projector(x), u @ u.T, atol=1e-10)
+    assert np.isclose(lam_x.sum(), lam_r.sum(), rtol=1e-12)
+
+
+def test_project_centers_and_group_means_by_loops():
+    rng = np.random.default_rng(44)
+    c, f = rng.standard_normal((5, 6)), rng.standard_normal((6, 3))
+    lin = rcp.project_centers(c, f, False)
+    for i in range(5):
+        u = [sum(c[i, a] * f[a, j] for a in range(6)) for j in range(3)]
+        assert np.allclose(lin[i], u)
+        rms = np.sqrt(np.mean(np.square(u)))
+        assert np.allclose(rcp.project_centers(c, f, True)[i], np.array(u) / rms)
+    x = rng.standard_normal((12, 3))
+    labels = np.array([0, 2, 2, 0, 3, 3, 3, 0, 2, 2, 0, 3])       # group 1 empty
+    fb = rng.standard_normal((4, 3))
+    g = rcp.group_means(x, labels, 4, fb)
+    for b in range(4):
+        rows = [x[i] for i in range(12) if labels[i] == b]
+        assert np.allclose(g[b], np.mean(rows, axis=0) if rows else fb[b])
+
+
+def _planted(rng, d=16, n=240, comp=4):
+    mu_k = rng.normal(0, 3.0, (comp, d))
+    lab = np.repeat(np.arange(comp), n // comp)
+    k = mu_k[lab] + rng.normal(0, 0.1, (n, d))
+    q_lab = np.tile(np.arange(comp), n // comp)
+    q = 2.0 * mu_k[q_lab] + rng.normal(0, 0.1, (n, d))
+    return q, k, lab, q_lab
+
+
+def test_warm_call_on_unchanged_inputs_repeats_the_partition():
+    # a converged first call leaves bases that are a fixed point of the
+    # subspace iteration and key centroids that map to the k-means centres,
+    # so one Lloyd iteration of the later call gives the same K/V groups; the
+    # query centres differ only by the RMS step (same groups when separated)
+    rng = np.random.default_rng(45)
+    q, k, lab, q_lab = _planted(rng)
+    init_k = [0, 70, 130, 200]
+    init_q = [0, 1, 2, 3]
+    cold = rcp.rcp_partition(q, k, m_s=64, r_k=6, c_k=4, r_q=3, c_q=4, init_k=init_k,
+                             init_q=init_q, iters=30)
+    warm = rcp.rcp_partition(q, k, m_s=64, r_k=6, c_k=4, r_q=3, c_q=4, init_k=None, init_q=None,
+                             iters=1, state=cold["state"])
+    assert np.array_equal(warm["labels_kv"], cold["labels_kv"])
+    assert np.allclose(warm["f_k"] @ warm["f_k"].T, cold["f_k"] @ cold["f_k"].T, atol=1e-10)
+    assert _ari(warm["labels_q"], cold["labels_q"]) == pytest.approx(1.0)
+    # the state's key centroids are the group means in the original space
+    for b in range(4):
+        assert np.allclose(cold["state"]["cent_k"][b], k[cold["labels_kv"] == b].mean(axis=0))
+
+
+def test_state_of_an_empty_group_is_its_initial_row_then_kept():
+    x = np.array([[0.0], [1.0], [4.0], [5.0]])
+    k = np.concatenate([x, 0.5 * x], axis=1)
+    q = k.copy()
+    # duplicate initial rows: K/V group 1 is empty after one iteration (ties
+    # go to the smaller index)
+    cold = rcp.rcp_partition(q, k, m_s=4, r_k=1, c_k=3, r_q=1, c_q=2, init_k=[0, 0, 3],
+                             init_q=[0, 3], iters=1)
+    assert not np.any(cold["labels_kv"] == 1)
+    assert np.allclose(cold["state"]["cent_k"][1], k[0])
+    warm = rcp.rcp_partition(q, k, m_s=4, r_k=1, c_k=3, r_q=1, c_q=2, init_k=None, init_q=None,
+                             iters=2, state=cold["state"])
+    # the later call starts group 1 at that row, which then takes row 0
+    assert np.array_equal(warm["labels_kv"], [1, 0, 2, 2])
+    assert np.allclose(warm["state"]["cent_k"][1], k[0])
+    assert np.allclose(warm["state"]["cent_k"][0], k[1])
