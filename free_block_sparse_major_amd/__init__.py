@@ -34,6 +34,7 @@ EXPORTED = (
     "sparsepr_probe_fit", "sparsepr_correct", "sparsepr_workspace_bytes",
     "sparsepr_status_string", "sparsepr_version", "sparsepr_rcp_partition",
     "sparsepr_probe_fit_ex", "sparsepr_correct_ex", "sparsepr_route_cells_ex",
+    "sparsepr_rcp_partition_ex",
 )
 
 
@@ -91,6 +92,10 @@ def load_library(path: str = LIB_PATH):
     lib.sparsepr_correct_ex.restype = I32
     lib.sparsepr_route_cells_ex.argtypes = [DP, I32, P, P, P, P, I64, P, P, P, P, SZ, P]
     lib.sparsepr_route_cells_ex.restype = I32
+    # dims, m_s, r_k, r_q, iters, warm, q, k, init_q, init_k, basis_q, basis_k, cent_q, cent_k,
+    # labels_q, labels_kv, phi_q, phi_k, ws, ws_bytes, stream
+    lib.sparsepr_rcp_partition_ex.argtypes = [DP, I32, I32, I32, I32, I32] + [P] * 12 + [P, SZ, P]
+    lib.sparsepr_rcp_partition_ex.restype = I32
     _lib = lib
     return lib
 
@@ -197,6 +202,17 @@ def sparsepr_rcp_partition(dims, m_s, r_k, r_q, iters, q, k, init_q, init_k, lab
     _check(st, "sparsepr_rcp_partition")
 
 
+def sparsepr_rcp_partition_ex(dims, m_s, r_k, r_q, iters, warm, q, k, init_q, init_k, basis_q,
+                              basis_k, cent_q, cent_k, labels_q, labels_kv, phi_q, phi_k, ws,
+                              stream=None):
+    st = load_library().sparsepr_rcp_partition_ex(
+        ctypes.byref(dims), int(m_s), int(r_k), int(r_q), int(iters), int(warm), _ptr(q), _ptr(k),
+        _ptr(init_q), _ptr(init_k), _ptr(basis_q), _ptr(basis_k), _ptr(cent_q), _ptr(cent_k),
+        _ptr(labels_q), _ptr(labels_kv), _ptr(phi_q), _ptr(phi_k),
+        _ptr(ws), ws.numel() * ws.element_size() if ws is not None else 0, _stream(stream))
+    _check(st, "sparsepr_rcp_partition_ex")
+
+
 def sparsepr_probe_fit_ex(dims, m, rank, lam, estimator, offsets_q, offsets_kv, perm_q,
                           cell_rowptr, cell_col, centroid_q, probe_feat, feat_dim, q_g, k_g, v_g,
                           v_shift, softmax_scale, probe_rows, probe_tokens, o_probe_dense,
@@ -224,10 +240,15 @@ def sparsepr_correct_ex(dims, m, rank, perm_q, o_sp, probe_tokens, o_probe_dense
 
 class RcpPartition:
     """Buffers for sparsepr_rcp_partition of one shape: labels_q, labels_kv
-    (int32 [H][N]), phi_q (fp32 [H][N_q][r_q]) and optionally phi_k."""
+    (int32 [H][N]), phi_q (fp32 [H][N_q][r_q]) and optionally phi_k.
+
+    With keep_state=True the partition keeps the state of later calls
+    (sparsepr_rcp_partition_ex): the first call starts from init rows, and
+    every call after it (warm=True) from the state the previous one left."""
 
     def __init__(self, heads, n_q, n_k, head_dim, dtype, c_q, c_k, m_s=256, r_k=48, r_q=64,
-                 iters=10, device="cuda", q_strides=None, kv_strides=None, keep_phi_k=False):
+                 iters=10, device="cuda", q_strides=None, kv_strides=None, keep_phi_k=False,
+                 keep_state=False):
         load_library()
         self.dims = make_dims(heads, n_q, n_k, head_dim, dtype, c_q, c_k, q_strides, kv_strides)
         self.m_s, self.r_k, self.r_q, self.iters = m_s, r_k, r_q, iters
@@ -239,11 +260,31 @@ class RcpPartition:
                       if keep_phi_k else None)
         nb = workspace_bytes(CALL_RCP_PARTITION, self.dims)
         self.ws = torch.empty(max(nb, 256), dtype=torch.uint8, device=dev)
+        self.keep_state = keep_state
+        self.has_state = False
+        if keep_state:
+            f32 = torch.float32
+            self.basis_q = torch.empty(heads, head_dim, r_q, dtype=f32, device=dev)
+            self.basis_k = torch.empty(heads, head_dim, r_k, dtype=f32, device=dev)
+            self.cent_q = torch.empty(heads, c_q, head_dim, dtype=f32, device=dev)
+            self.cent_k = torch.empty(heads, c_k, head_dim, dtype=f32, device=dev)
 
-    def __call__(self, q, k, init_q, init_k, stream=None):
-        sparsepr_rcp_partition(self.dims, self.m_s, self.r_k, self.r_q, self.iters, q, k, init_q,
-                               init_k, self.labels_q, self.labels_kv, self.phi_q, self.phi_k,
-                               self.ws, stream)
+    def __call__(self, q, k, init_q=None, init_k=None, warm=False, iters=None, stream=None):
+        iters = self.iters if iters is None else iters
+        if not self.keep_state:
+            if warm:
+                raise ValueError("warm calls need keep_state=True")
+            sparsepr_rcp_partition(self.dims, self.m_s, self.r_k, self.r_q, iters, q, k, init_q,
+                                   init_k, self.labels_q, self.labels_kv, self.phi_q, self.phi_k,
+                                   self.ws, stream)
+            return self.labels_q, self.labels_kv
+        if warm and not self.has_state:
+            raise ValueError("a warm call needs the state of an earlier call")
+        sparsepr_rcp_partition_ex(self.dims, self.m_s, self.r_k, self.r_q, iters, int(warm), q, k,
+                                  init_q, init_k, self.basis_q, self.basis_k, self.cent_q,
+                                  self.cent_k, self.labels_q, self.labels_kv, self.phi_q,
+                                  self.phi_k, self.ws, stream)
+        self.has_state = True
         return self.labels_q, self.labels_kv
 
 

@@ -22,6 +22,15 @@
 //      mean over the non-empty groups subtracted: M_Q = K~^T K~ / C_nonempty.
 //   6. F_Q from M_Q as in 2 (r_Q); phi_Q = u / max(RMS(u), 1e-6), u = q F_Q.
 //   7. k-means on phi_Q with C_q centres from init_q -> query labels.
+//
+// Later calls of the same layer (App. C.1) start from the state an earlier
+// call left: the factors come from two subspace iterations started at the
+// previous orthonormal bases (fp64, Cholesky orthonormalisation, directions
+// weighted by their Rayleigh quotients), and k-means starts from the previous
+// group centroids in the original space mapped by the current coordinates.
+// The state written back is the bases and each group's mean in the original
+// space (an empty group keeps its previous centroid; on a first call, its
+// initial row).
 
 #include "common.h"
 
@@ -160,7 +169,8 @@ __global__ __launch_bounds__(256) void query_metric_kernel(const float* __restri
 // sqrt(max(lambda, 0) / mean of the r retained); columns r..rp-1 are 0.
 template <int D>
 __global__ __launch_bounds__(256) void eig_factor_kernel(const float* __restrict__ m, int r, int rp,
-                                                         float* __restrict__ f) {
+                                                         float* __restrict__ f,
+                                                         float* __restrict__ basis) {
   constexpr int NP = D / 2, PER = 256 / NP, NCOL = D / PER;
   const int h = blockIdx.x, tid = threadIdx.x;
   // row stride D + 4: the row pass of 16 consecutive pairs x 4 columns per
@@ -290,6 +300,142 @@ __global__ __launch_bounds__(256) void eig_factor_kernel(const float* __restrict
     }
     fh[e] = v;
   }
+  // the leading r eigenvectors themselves (basis[h] is D x r, row-major)
+  if (basis) {
+    float* bh = basis + (long long)h * D * r;
+    for (int e = tid; e < D * r; e += 256) bh[e] = U[e / r][order[e % r]];
+  }
+}
+
+// ---------------------------------------------------------------------------
+// later calls: subspace-iteration factor (fp64, one block per head)
+// ---------------------------------------------------------------------------
+// X starts at the previous basis (D x r).  One step: Y = M X; G = Y^T Y;
+// G = L L^T by a right-looking Cholesky in which a pivot at or below 1e-10 of
+// the largest diagonal entry of G drops its column (L column 0); X = Y L^-T
+// by forward substitution, row by row.  After the steps, lambda_j = x_j^T M
+// x_j (clamped at 0) and F = X diag(sqrt(lambda / mean lambda)).  Sums run
+// in a fixed order (deterministic).  basis_in may alias basis_out.
+constexpr double kCholDrop = 1e-10;
+template <int D>
+__global__ __launch_bounds__(256) void subspace_factor_kernel(const float* __restrict__ m,
+                                                              const float* basis_in, int r,
+                                                              int rp, int steps,
+                                                              float* __restrict__ f,
+                                                              float* basis_out) {
+  constexpr int TPR = 256 / D, NU = kMaxR / TPR;   // threads per row, columns per thread
+  const int h = blockIdx.x, tid = threadIdx.x;
+  __shared__ double X[D][kMaxR + 1];
+  __shared__ double G[kMaxR][kMaxR + 1];
+  __shared__ double lam[kMaxR];
+  __shared__ double s_ref, s_mean;
+  __shared__ int32_t s_keep;
+  const float* mh = m + (long long)h * D * D;
+  const float* bi = basis_in + (long long)h * D * r;
+  for (int e = tid; e < D * r; e += 256) X[e / r][e % r] = double(bi[e]);
+  __syncthreads();
+  const int row = tid / TPR, jc = tid % TPR;
+  // acc[u] = (M X)[row][jc + TPR u], k in order
+  auto mx = [&](double (&acc)[NU]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int u = 0; u < NU; ++u) acc[u] = 0.0;
+    const float* mr = mh + (long long)row * D;
+    for (int k = 0; k < D; ++k) {
+      const double mik = double(mr[k]);
+#pragma unroll
+      for (int u = 0; u < NU; ++u)
+        if (jc + TPR * u < r) acc[u] = fma(mik, X[k][jc + TPR * u], acc[u]);
+    }
+  };
+  for (int step = 0; step < steps; ++step) {
+    double acc[NU];
+    mx(acc);
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < NU; ++u)
+      if (jc + TPR * u < r) X[row][jc + TPR * u] = acc[u];
+    __syncthreads();
+    for (int e = tid; e < r * r; e += 256) {
+      const int a = e / r, b = e % r;
+      double sacc = 0.0;
+      for (int i = 0; i < D; ++i) sacc = fma(X[i][a], X[i][b], sacc);
+      G[a][b] = sacc;
+    }
+    __syncthreads();
+    if (tid == 0) {
+      double mxd = 0.0;
+      for (int j = 0; j < r; ++j) mxd = fmax(mxd, G[j][j]);
+      s_ref = mxd;
+    }
+    __syncthreads();
+    for (int j = 0; j < r; ++j) {
+      if (tid == 0) {
+        const double piv = G[j][j];
+        const bool keep = piv > kCholDrop * s_ref && piv > 0.0;
+        G[j][j] = keep ? sqrt(piv) : 0.0;
+        s_keep = keep ? 1 : 0;
+      }
+      __syncthreads();
+      const bool keep = s_keep != 0;
+      const double ljj = G[j][j];
+      for (int i = j + 1 + tid; i < r; i += 256) G[i][j] = keep ? G[i][j] / ljj : 0.0;
+      __syncthreads();
+      if (keep) {
+        const int w = r - j - 1;
+        for (int e = tid; e < w * w; e += 256) {
+          const int i = j + 1 + e / w, l = j + 1 + e % w;
+          if (l <= i) G[i][l] = fma(-G[i][j], G[l][j], G[i][l]);
+        }
+      }
+      __syncthreads();
+    }
+    // X = Y L^-T, one row per thread, in place
+    if (tid < D) {
+      for (int j = 0; j < r; ++j) {
+        double v = X[tid][j];
+        for (int k = 0; k < j; ++k) v = fma(-X[tid][k], G[j][k], v);
+        X[tid][j] = G[j][j] > 0.0 ? v / G[j][j] : 0.0;
+      }
+    }
+    __syncthreads();
+  }
+  // Rayleigh quotients: Z = M X staged 64 rows at a time through G
+  {
+    double acc[NU];
+    mx(acc);
+    if (tid < kMaxR) lam[tid] = 0.0;
+    for (int c0 = 0; c0 < D; c0 += kMaxR) {
+      __syncthreads();
+      if (row >= c0 && row < c0 + kMaxR) {
+#pragma unroll
+        for (int u = 0; u < NU; ++u)
+          if (jc + TPR * u < r) G[row - c0][jc + TPR * u] = acc[u] * X[row][jc + TPR * u];
+      }
+      __syncthreads();
+      if (tid < r) {
+        double sacc = lam[tid];
+        for (int i = 0; i < kMaxR && c0 + i < D; ++i) sacc += G[i][tid];
+        lam[tid] = sacc;
+      }
+    }
+    __syncthreads();
+  }
+  if (tid == 0) {
+    double sm = 0.0;
+    for (int j = 0; j < r; ++j) sm += fmax(lam[j], 0.0);
+    s_mean = sm / double(r);
+  }
+  __syncthreads();
+  const double mean = s_mean;
+  float* fh = f + (long long)h * D * rp;
+  for (int e = tid; e < D * rp; e += 256) {
+    const int i = e / rp, j = e % rp;
+    float v = 0.f;
+    if (j < r && mean > 0.0) v = float(X[i][j] * sqrt(fmax(lam[j], 0.0) / mean));
+    fh[e] = v;
+  }
+  float* bo = basis_out + (long long)h * D * r;
+  for (int e = tid; e < D * r; e += 256) bo[e] = float(X[e / r][e % r]);
 }
 
 // ---------------------------------------------------------------------------
@@ -450,6 +596,30 @@ __global__ __launch_bounds__(256) void kmeans_init_kernel(const uint16_t* __rest
   store_center<RP>(h, c, C, v, cent, chi, clo, cnorm);
 }
 
+// Initial centres of a later call: the previous centroids cent[h][c] (original
+// space, D values) mapped by the current factor F (D x rp): u = c F (fp32, in
+// order), RMS-normalised over the r coordinates (floor 1e-6) for query
+// coordinates.  One wave per centre, lane j < RP owns coordinate j.
+template <int D, int RP>
+__global__ __launch_bounds__(256) void kmeans_init_proj_kernel(const float* __restrict__ prev,
+                                                               const float* __restrict__ f, int r,
+                                                               int rms, int C, float* cent,
+                                                               uint16_t* chi, uint16_t* clo,
+                                                               float* cnorm) {
+  const int h = blockIdx.y, c = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
+  if (c >= C) return;
+  const float* pc = prev + ((long long)h * C + c) * D;
+  const float* fh = f + (long long)h * D * RP;
+  float u = 0.f;
+  if (lane < RP)
+    for (int i = 0; i < D; ++i) u = fmaf(pc[i], fh[i * RP + lane], u);
+  if (rms) {
+    const float ss = wave_sum(lane < r ? u * u : 0.f);
+    u *= 1.f / fmaxf(sqrtf(ss / float(r)), 1e-6f);
+  }
+  store_center<RP>(h, c, C, u, cent, chi, clo, cnorm);
+}
+
 // Update: mean of each cluster's rows (perm/offsets from the stable sort of
 // the labels); an empty cluster keeps its centre.  One block per cluster:
 // thread (rl, j) sums coordinate j over the cluster's rows rl, rl + 4, ...
@@ -568,14 +738,17 @@ __global__ __launch_bounds__(256) void kmeans_assign_kernel(
   if (g == 0 && row < n) labels[(long long)h * n + row] = bi;
 }
 
-// Mean of each K/V group's key rows in the original space (fp32).  One
-// block per group: thread (rl, j) sums dimension j over rows rl, rl + RL, ...
-// in order (RL = 256 / D row lanes); partial sums are added in a fixed order.
+// Mean of each group's rows in the original space (fp32).  One block per
+// group: thread (rl, j) sums dimension j over rows rl, rl + RL, ... in order
+// (RL = 256 / D row lanes); partial sums are added in a fixed order.  An
+// empty group takes its initial row init[h][c] when init is given and keeps
+// its entry otherwise (the centroid of an earlier call).
 template <int D>
 __global__ __launch_bounds__(256) void key_centroid_kernel(const int32_t* __restrict__ perm,
                                                            const int32_t* __restrict__ offsets,
                                                            const void* k, int dtype, long long sh,
                                                            long long st, int n, int C,
+                                                           const int32_t* __restrict__ init,
                                                            float* __restrict__ cent) {
   constexpr int RL = 256 / D;
   const int h = blockIdx.y, c = blockIdx.x, rl = threadIdx.x / D, j = threadIdx.x % D;
@@ -592,7 +765,14 @@ __global__ __launch_bounds__(256) void key_centroid_kernel(const int32_t* __rest
   float t = part[0][j];
 #pragma unroll
   for (int i = 1; i < RL; ++i) t += part[i][j];
-  cent[((long long)h * C + c) * D + j] = b1 > b0 ? t / float(b1 - b0) : 0.f;
+  float* out = cent + ((long long)h * C + c) * D + j;
+  if (b1 > b0) {
+    *out = t / float(b1 - b0);
+  } else if (init) {
+    int row = init[(long long)h * C + c];
+    row = row < 0 ? 0 : (row >= n ? n - 1 : row);
+    *out = load_elem(k, dtype, h * sh + (long long)row * st + j);
+  }
 }
 
 struct RcpWs {
@@ -626,13 +806,16 @@ RcpWs carve_rcp(void* base, const sparsepr_dims* d, size_t* used) {
   return w;
 }
 
+// init == nullptr: the centres were set by kmeans_init_proj_kernel
 template <int RP>
 int32_t run_kmeans(const RcpWs& w, int H, int n, int C, const int32_t* init, int iters,
                    int32_t* labels, hipStream_t stream) {
   const dim3 gc((C + 3) / 4, H);
-  kmeans_init_kernel<RP><<<gc, 256, 0, stream>>>(w.xh, w.xl, n, init, C, w.cent, w.chi, w.clo,
-                                                 w.cnorm);
-  SPR_LAUNCH_CHECK();
+  if (init) {
+    kmeans_init_kernel<RP><<<gc, 256, 0, stream>>>(w.xh, w.xl, n, init, C, w.cent, w.chi, w.clo,
+                                                   w.cnorm);
+    SPR_LAUNCH_CHECK();
+  }
   for (int it = 0; it < iters; ++it) {
     kmeans_assign_kernel<RP><<<dim3((n + 127) / 128, H), 256, 0, stream>>>(
         w.xh, w.xl, n, w.chi, w.clo, w.cnorm, C, labels);
@@ -658,40 +841,88 @@ int32_t kmeans_rp(int rp, const RcpWs& w, int H, int n, int C, const int32_t* in
 }
 
 template <int D>
+void init_proj(int rp, const float* prev, const RcpWs& w, int r, int rms, int H, int C,
+               hipStream_t stream) {
+  const dim3 gc((C + 3) / 4, H);
+  switch (rp) {
+    case 16: kmeans_init_proj_kernel<D, 16><<<gc, 256, 0, stream>>>(prev, w.factor, r, rms, C, w.cent, w.chi, w.clo, w.cnorm); break;
+    case 32: kmeans_init_proj_kernel<D, 32><<<gc, 256, 0, stream>>>(prev, w.factor, r, rms, C, w.cent, w.chi, w.clo, w.cnorm); break;
+    case 48: kmeans_init_proj_kernel<D, 48><<<gc, 256, 0, stream>>>(prev, w.factor, r, rms, C, w.cent, w.chi, w.clo, w.cnorm); break;
+    default: kmeans_init_proj_kernel<D, 64><<<gc, 256, 0, stream>>>(prev, w.factor, r, rms, C, w.cent, w.chi, w.clo, w.cnorm); break;
+  }
+}
+
+// The state of a later call (all four set, or all null for a call that
+// keeps none): bases [H][D][r] and original-space centroids [H][C][D].
+struct RcpState {
+  int warm;
+  float *basis_q, *basis_k, *cent_q, *cent_k;
+};
+
+template <int D>
 int32_t rcp_run(const sparsepr_dims* d, int m_s, int r_k, int r_q, int iters, const void* q,
                 const void* k, const int32_t* init_q, const int32_t* init_k, int32_t* labels_q,
-                int32_t* labels_kv, float* phi_q, float* phi_k, const RcpWs& w,
-                hipStream_t stream) {
+                int32_t* labels_kv, float* phi_q, float* phi_k, const RcpState& s,
+                const RcpWs& w, hipStream_t stream) {
   const int H = d->heads;
   const int rpk = (r_k + 15) / 16 * 16, rpq = (r_q + 15) / 16 * 16;
+  const bool keep = s.cent_k != nullptr;
   // key-response coordinates and K/V groups
   key_metric_kernel<D><<<H, 256, 0, stream>>>(q, d->dtype, d->q_stride_head, d->q_stride_tok,
                                               d->n_q, m_s, w.metric);
   SPR_LAUNCH_CHECK();
-  eig_factor_kernel<D><<<H, 256, 0, stream>>>(w.metric, r_k, rpk, w.factor);
+  if (s.warm)
+    subspace_factor_kernel<D><<<H, 256, 0, stream>>>(w.metric, s.basis_k, r_k, rpk, 2, w.factor,
+                                                     s.basis_k);
+  else
+    eig_factor_kernel<D><<<H, 256, 0, stream>>>(w.metric, r_k, rpk, w.factor, s.basis_k);
   SPR_LAUNCH_CHECK();
   project_kernel<D><<<dim3((d->n_k + 128 * kProjTiles - 1) / (128 * kProjTiles), H), 256, 0, stream>>>(
       k, d->dtype, d->kv_stride_head, d->kv_stride_tok, d->n_k, w.factor, r_k, rpk, 0, w.xh, w.xl,
       phi_k);
   SPR_LAUNCH_CHECK();
-  int32_t st = kmeans_rp(rpk, w, H, d->n_k, d->c_k, init_k, iters, labels_kv, stream);
+  if (s.warm) {
+    init_proj<D>(rpk, s.cent_k, w, r_k, 0, H, d->c_k, stream);
+    SPR_LAUNCH_CHECK();
+  }
+  int32_t st = kmeans_rp(rpk, w, H, d->n_k, d->c_k, s.warm ? nullptr : init_k, iters, labels_kv,
+                         stream);
   if (st != SPARSEPR_OK) return st;
-  // query-response coordinates from the K/V groups, then query groups
+  // query-response coordinates from the K/V groups, then query groups; the
+  // K/V centroids go straight to the state when it is kept
   st = group_sort(labels_kv, H, d->n_k, d->c_k, w.perm, w.offsets, w.sort_ws, stream);
   if (st != SPARSEPR_OK) return st;
+  float* kcent = keep ? s.cent_k : w.kcent;
   key_centroid_kernel<D><<<dim3(d->c_k, H), 256, 0, stream>>>(
       w.perm, w.offsets, k, d->dtype, d->kv_stride_head, d->kv_stride_tok, d->n_k, d->c_k,
-      w.kcent);
+      s.warm ? nullptr : init_k, kcent);
   SPR_LAUNCH_CHECK();
-  query_metric_kernel<D><<<H, 256, 0, stream>>>(w.kcent, w.offsets, d->c_k, w.metric);
+  query_metric_kernel<D><<<H, 256, 0, stream>>>(kcent, w.offsets, d->c_k, w.metric);
   SPR_LAUNCH_CHECK();
-  eig_factor_kernel<D><<<H, 256, 0, stream>>>(w.metric, r_q, rpq, w.factor);
+  if (s.warm)
+    subspace_factor_kernel<D><<<H, 256, 0, stream>>>(w.metric, s.basis_q, r_q, rpq, 2, w.factor,
+                                                     s.basis_q);
+  else
+    eig_factor_kernel<D><<<H, 256, 0, stream>>>(w.metric, r_q, rpq, w.factor, s.basis_q);
   SPR_LAUNCH_CHECK();
   project_kernel<D><<<dim3((d->n_q + 128 * kProjTiles - 1) / (128 * kProjTiles), H), 256, 0, stream>>>(
       q, d->dtype, d->q_stride_head, d->q_stride_tok, d->n_q, w.factor, r_q, rpq, 1, w.xh, w.xl,
       phi_q);
   SPR_LAUNCH_CHECK();
-  return kmeans_rp(rpq, w, H, d->n_q, d->c_q, init_q, iters, labels_q, stream);
+  if (s.warm) {
+    init_proj<D>(rpq, s.cent_q, w, r_q, 1, H, d->c_q, stream);
+    SPR_LAUNCH_CHECK();
+  }
+  st = kmeans_rp(rpq, w, H, d->n_q, d->c_q, s.warm ? nullptr : init_q, iters, labels_q, stream);
+  if (st != SPARSEPR_OK || !keep) return st;
+  // query group centroids for the next call
+  st = group_sort(labels_q, H, d->n_q, d->c_q, w.perm, w.offsets, w.sort_ws, stream);
+  if (st != SPARSEPR_OK) return st;
+  key_centroid_kernel<D><<<dim3(d->c_q, H), 256, 0, stream>>>(
+      w.perm, w.offsets, q, d->dtype, d->q_stride_head, d->q_stride_tok, d->n_q, d->c_q,
+      s.warm ? nullptr : init_q, s.cent_q);
+  SPR_LAUNCH_CHECK();
+  return SPARSEPR_OK;
 }
 
 }  // namespace
@@ -721,9 +952,38 @@ extern "C" int32_t sparsepr_rcp_partition(const sparsepr_dims* dims, int32_t m_s
   const size_t need = rcp_ws_bytes(dims);
   if (!ws || ws_bytes < need) return SPARSEPR_ERR_WORKSPACE;
   const RcpWs w = carve_rcp(ws, dims, nullptr);
+  const RcpState s{0, nullptr, nullptr, nullptr, nullptr};
   if (dims->head_dim == 128)
     return rcp_run<128>(dims, m_s, r_k, r_q, iters, q, k, init_q, init_k, labels_q, labels_kv,
-                        phi_q, phi_k, w, stream);
+                        phi_q, phi_k, s, w, stream);
   return rcp_run<64>(dims, m_s, r_k, r_q, iters, q, k, init_q, init_k, labels_q, labels_kv,
-                     phi_q, phi_k, w, stream);
+                     phi_q, phi_k, s, w, stream);
+}
+
+extern "C" int32_t sparsepr_rcp_partition_ex(const sparsepr_dims* dims, int32_t m_s, int32_t r_k,
+                                             int32_t r_q, int32_t iters, int32_t warm,
+                                             const void* q, const void* k, const int32_t* init_q,
+                                             const int32_t* init_k, float* basis_q,
+                                             float* basis_k, float* cent_q, float* cent_k,
+                                             int32_t* labels_q, int32_t* labels_kv, float* phi_q,
+                                             float* phi_k, void* ws, size_t ws_bytes,
+                                             hipStream_t stream) {
+  int32_t st = check_dims(dims);
+  if (st != SPARSEPR_OK) return st;
+  if (!q || !k || !labels_q || !labels_kv || !basis_q || !basis_k || !cent_q || !cent_k)
+    return SPARSEPR_ERR_INVALID;
+  if (warm != 0 && warm != 1) return SPARSEPR_ERR_INVALID;
+  if (!warm && (!init_q || !init_k)) return SPARSEPR_ERR_INVALID;
+  if (m_s < 1 || iters < 1 || r_k < 1 || r_q < 1 || r_k > kMaxR || r_q > kMaxR ||
+      r_k > dims->head_dim || r_q > dims->head_dim)
+    return SPARSEPR_ERR_INVALID;
+  const size_t need = rcp_ws_bytes(dims);
+  if (!ws || ws_bytes < need) return SPARSEPR_ERR_WORKSPACE;
+  const RcpWs w = carve_rcp(ws, dims, nullptr);
+  const RcpState s{warm, basis_q, basis_k, cent_q, cent_k};
+  if (dims->head_dim == 128)
+    return rcp_run<128>(dims, m_s, r_k, r_q, iters, q, k, init_q, init_k, labels_q, labels_kv,
+                        phi_q, phi_k, s, w, stream);
+  return rcp_run<64>(dims, m_s, r_k, r_q, iters, q, k, init_q, init_k, labels_q, labels_kv,
+                     phi_q, phi_k, s, w, stream);
 }

@@ -303,6 +303,39 @@ int32_t sparsepr_rcp_partition(const sparsepr_dims* dims /* host */, int32_t m_s
                                void* ws, size_t ws_bytes, hipStream_t stream);
 
 /*
+ * Response-coupled partitioning across calls: a first call and later calls
+ * of the same layer.  (SparsePR paper App. C.1: later calls start k-means
+ * from the previous centroids in the original space projected into the
+ * current response coordinates, and update the metric factors with two
+ * subspace iterations started from the previous factors, using a Cholesky
+ * factorisation.)  As sparsepr_rcp_partition, plus a state the call reads
+ * (warm = 1) and always writes back:
+ *   basis_k [H][d][r_k], basis_q [H][d][r_q] fp32: orthonormal bases of the
+ *     response coordinates.  A first call (warm = 0) stores the leading
+ *     eigenvectors; a later call runs two steps X <- Y L^-T, Y = M X,
+ *     Y^T Y = L L^T (fp64; a Cholesky pivot at or below 1e-10 of the largest
+ *     diagonal entry of Y^T Y drops its direction, which stays 0), and
+ *     weights direction j by sqrt(max(x_j^T M x_j, 0) / mean over the r).
+ *   cent_k [H][C_k][d], cent_q [H][C_q][d] fp32: each group's mean in the
+ *     original key or query space.  A later call starts k-means at
+ *     cent_k F_K and at phi_Q(cent_q) (RMS-normalised); a group left empty
+ *     keeps its previous centroid, and on a first call its initial row.
+ *   warm: 0 = first call (init_q, init_k required), 1 = later call (the
+ *     state must hold a previous call's output for the same dims, r_k and
+ *     r_q; init_q, init_k are not read and may be NULL).
+ * The state buffers are read and overwritten in place; calls that share a
+ * state must not overlap.  Every pointer but init_q, init_k, phi_q, phi_k is
+ * required.  Workspace: sparsepr_workspace_bytes(SPARSEPR_CALL_RCP_PARTITION,
+ * dims, 0, 0).
+ */
+int32_t sparsepr_rcp_partition_ex(const sparsepr_dims* dims /* host */, int32_t m_s, int32_t r_k,
+                                  int32_t r_q, int32_t iters, int32_t warm, const void* q,
+                                  const void* k, const int32_t* init_q, const int32_t* init_k,
+                                  float* basis_q, float* basis_k, float* cent_q, float* cent_k,
+                                  int32_t* labels_q, int32_t* labels_kv, float* phi_q,
+                                  float* phi_k, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
  * S6-S8 with options.  As sparsepr_probe_fit, plus:
  *   probe_feat [H][N_q][feat_dim] fp32 token order (feat_dim 1..64), or
  *     NULL: when given, the distance of a row to its group's centroid is

@@ -48,6 +48,8 @@ __all__ = [
     "RCP_PARAMS",
     "rcp_init",
     "rcp_init_arrays",
+    "drift_head",
+    "drift_arrays",
 ]
 
 
@@ -318,3 +320,51 @@ def rcp_init_arrays(w: Workload):
     for h in range(w.heads):
         ik[h], iq[h] = rcp_init(w, h)
     return ik, iq
+
+
+def _drift_gen(w: Workload, h: int, step: int):
+    return np.random.Generator(np.random.PCG64(np.random.SeedSequence([w.seed, h, 2, step])))
+
+
+def drift_head(w: Workload, hd: dict, h: int, step: int, eps: float, names=("q", "k", "v")):
+    """The activations of a later call of the same layer (the next denoising
+    step): x + eps * N(0, 1) for each tensor in `names`, drawn in that order
+    from PCG64(SeedSequence([seed, h, 2, step])), nearest-even bf16 for bf16
+    workloads.  Labels are copied unchanged."""
+    g = _drift_gen(w, h, step)
+    out = dict(hd)
+    for name in names:
+        x = hd[name].astype(np.float32) + np.float32(eps) * g.standard_normal(
+            hd[name].shape, dtype=np.float32)
+        if w.dtype == "bf16":
+            out[name + "_bits"] = f32_to_bf16_bits(x)
+            out[name] = bf16_bits_to_f32(out[name + "_bits"])
+        else:
+            out[name] = x
+    return out
+
+
+def drift_arrays(w: Workload, arr: dict, step: int, eps: float, names=("q", "k"),
+                 threads: Optional[int] = None):
+    """drift_head for packed [H, N, d] arrays (make_call_arrays), in place of
+    a copy; same values head by head.  Heads run in parallel threads."""
+    import concurrent.futures as cf
+    import os
+
+    out = dict(arr)
+    for name in names:
+        out[name] = np.empty_like(arr[name])
+    bf16 = w.dtype == "bf16"
+    nt = threads or max(1, min(8, os.cpu_count() or 1, w.heads))
+
+    def work(tid):
+        for h in range(tid, w.heads, nt):
+            g = _drift_gen(w, h, step)
+            for name in names:
+                src = bf16_bits_to_f32(arr[name][h]) if bf16 else arr[name][h]
+                x = src + np.float32(eps) * g.standard_normal(src.shape, dtype=np.float32)
+                out[name][h] = f32_to_bf16_bits(x) if bf16 else x
+
+    with cf.ThreadPoolExecutor(nt) as ex:
+        list(ex.map(work, range(nt)))
+    return out

@@ -100,6 +100,18 @@ def test_argument_validation_before_launch(lib):
     # route: workspace too small
     st = lib.sparsepr_route_cells(ctypes.byref(good), P, P, P, P, 100, P, P, P, P, 8, None)
     assert st == fb.ERR_WORKSPACE
+    # partition across calls: warm flag, missing init on a first call, missing
+    # state, rank above 64, workspace too small
+    def part_ex(warm=0, init=P, state=P, r_k=16, ws_bytes=1 << 30):
+        return lib.sparsepr_rcp_partition_ex(ctypes.byref(good), 64, r_k, 16, 2, warm, P, P, init,
+                                             init, state, state, state, state, P, P, None, None, P,
+                                             ws_bytes, None)
+    assert part_ex(warm=2) == fb.ERR_INVALID
+    assert part_ex(init=None) == fb.ERR_INVALID
+    assert part_ex(state=None) == fb.ERR_INVALID
+    assert part_ex(warm=1, state=None) == fb.ERR_INVALID
+    assert part_ex(r_k=65) == fb.ERR_INVALID
+    assert part_ex(ws_bytes=16) == fb.ERR_WORKSPACE
 
 
 def test_budget_matches_oracle_closed_form():

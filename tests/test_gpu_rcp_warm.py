@@ -1,0 +1,243 @@
+"""GPU parity of response-coupled partitioning across calls
+(sparsepr_rcp_partition_ex): a first call on one set of activations, then a
+later call on the activations of the next step (a seeded drift), started
+from the state the first call left.
+
+[paper] "Partition the Support, Reconstruct the Residual" App. C.1 (later
+calls: k-means from the previous centroids in the original space projected
+into the current coordinates; factors from two subspace iterations started
+at the previous factors, with a Cholesky factorisation).  Each stage is
+checked against the oracle run on the GPU's own inputs to that stage:
+  * the state of the first call: eigenvector residuals and orthonormality of
+    the bases, the key coordinates against the bases and the oracle metric,
+    and the centroids as group means of the original rows;
+  * the later call's bases against the oracle's subspace iteration from the
+    same previous bases (no sign freedom: Cholesky pivots are positive), the
+    coordinates through their row Gram matrices, the labels against the
+    oracle's Lloyd iteration from the projected centroids on the GPU
+    coordinates, and the new state;
+  * the whole later call against the oracle's from the same state (adjusted
+    Rand index, reported)."""
+import numpy as np
+import pytest
+
+import synthgen as sg
+from harness import ari, rel_fro, say, upload, upload_arrays
+from oracle import rcp
+from test_gpu_rcp import SMALL, _gram
+
+pytestmark = pytest.mark.gpu
+
+EPS = 0.1   # drift of q and k between the two calls (activations ~ N(0, 1.5^2) means)
+
+
+def _partition(w, params, keep_phi_k=True):
+    import free_block_sparse_major_amd as fb
+    return fb.RcpPartition(w.heads, w.n, w.n, w.head_dim, fb.BF16 if w.dtype == "bf16" else fb.F32,
+                           w.c_q, w.c_k, m_s=params["m_s"], r_k=params["r_k"], r_q=params["r_q"],
+                           iters=params["iters"], keep_phi_k=keep_phi_k, keep_state=True)
+
+
+def _state(part):
+    return {name: getattr(part, name).cpu().numpy().astype(np.float64)
+            for name in ("basis_k", "basis_q", "cent_k", "cent_q")}
+
+
+def _labels(part):
+    return part.labels_kv.cpu().numpy(), part.labels_q.cpu().numpy()
+
+
+def check_first_call(w, params, q, k, h, part, ik, iq):
+    """State left by a first call, head h (q, k: fp64 arrays of that head)."""
+    out = {}
+    st = _state(part)
+    lab_kv, lab_q = (x[h] for x in _labels(part))
+    bk, bq = st["basis_k"][h], st["basis_q"][h]
+    m_k = rcp.key_response_metric(q[rcp.sample_query_rows(w.n, params["m_s"])])
+    m_q, _ = rcp.query_response_metric(k, lab_kv, w.c_k)
+    for name, b, m in (("k", bk, m_k), ("q", bq, m_q)):
+        out[f"orth_{name}"] = float(np.abs(b.T @ b - np.eye(b.shape[1])).max())
+        mb = m @ b
+        lam = np.sum(b * mb, axis=0)
+        out[f"eig_res_{name}"] = float(np.linalg.norm(mb - b * lam) / np.linalg.norm(m))
+    # key coordinates = k (basis * weights), weights from the oracle metric
+    lam = np.maximum(np.sum(bk * (m_k @ bk), axis=0), 0.0)
+    f = bk * np.sqrt(lam / lam.mean())
+    rows = np.linspace(0, w.n - 1, min(w.n, 256)).astype(np.int64)
+    out["phi_k_vs_basis"] = rel_fro(_gram(part.phi_k[h].cpu().numpy(), rows), _gram(k @ f, rows))
+    out["cent_k"] = rel_fro(st["cent_k"][h], rcp.group_means(k, lab_kv, w.c_k, k[ik[h]]))
+    out["cent_q"] = rel_fro(st["cent_q"][h], rcp.group_means(q, lab_q, w.c_q, q[iq[h]]))
+    return out
+
+
+def check_later_call(w, params, q, k, h, part, prev, full_oracle=True):
+    """Later call of head h from the previous state `prev` (dict of arrays)."""
+    out = {}
+    st = _state(part)
+    lab_kv, lab_q = (x[h] for x in _labels(part))
+    phi_k = part.phi_k[h].cpu().numpy().astype(np.float64)
+    phi_q = part.phi_q[h].cpu().numpy().astype(np.float64)
+    rows = np.linspace(0, w.n - 1, min(w.n, 256)).astype(np.int64)
+    # key factors from the previous basis
+    m_k = rcp.key_response_metric(q[rcp.sample_query_rows(w.n, params["m_s"])])
+    xk, _, fk = rcp.subspace_factor(m_k, prev["basis_k"][h])
+    out["basis_k"] = rel_fro(st["basis_k"][h], xk)
+    out["phi_k_gram"] = rel_fro(_gram(phi_k, rows), _gram(k @ fk, rows))
+    # K/V labels: Lloyd from the projected previous centroids on the GPU coordinates
+    init = rcp.project_centers(prev["cent_k"][h], fk, False)
+    lab_o, _, _ = rcp.kmeans(phi_k, None, params["iters"], init_centers=init)
+    out["kv_agree"] = float(np.mean(lab_o == lab_kv))
+    out["kv_ari"] = ari(lab_o, lab_kv)
+    # query side from the GPU K/V groups
+    m_q, _ = rcp.query_response_metric(k, lab_kv, w.c_k)
+    xq, _, fq = rcp.subspace_factor(m_q, prev["basis_q"][h])
+    out["basis_q"] = rel_fro(st["basis_q"][h], xq)
+    out["phi_q_gram"] = rel_fro(_gram(phi_q, rows), _gram(rcp.query_features(q, fq), rows))
+    init = rcp.project_centers(prev["cent_q"][h], fq, True)
+    lab_o, _, _ = rcp.kmeans(phi_q, None, params["iters"], init_centers=init)
+    out["q_agree"] = float(np.mean(lab_o == lab_q))
+    out["q_ari"] = ari(lab_o, lab_q)
+    # new state: group means, empty groups keep the previous centroid
+    out["cent_k"] = rel_fro(st["cent_k"][h], rcp.group_means(k, lab_kv, w.c_k, prev["cent_k"][h]))
+    out["cent_q"] = rel_fro(st["cent_q"][h], rcp.group_means(q, lab_q, w.c_q, prev["cent_q"][h]))
+    if full_oracle:
+        prev_h = {name: prev[name][h] for name in prev}
+        ref = rcp.rcp_partition(q, k, params["m_s"], params["r_k"], w.c_k, params["r_q"], w.c_q,
+                                None, None, params["iters"], state=prev_h)
+        out["kv_ari_scratch"] = ari(ref["labels_kv"], lab_kv)
+        out["q_ari_scratch"] = ari(ref["labels_q"], lab_q)
+    return out
+
+
+def assert_first_bounds(e):
+    # fp32 cyclic Jacobi: each of ~d x sweeps rotations touching a column adds
+    # about one fp32 rounding (6e-8), so d x sweeps x 6e-8 stays below 2e-4
+    assert e["orth_k"] < 2e-4 and e["orth_q"] < 2e-4, e
+    # Jacobi eigenvectors of the fp32 metric against the fp64 one
+    assert e["eig_res_k"] < 2e-4 and e["eig_res_q"] < 2e-4, e
+    assert e["phi_k_vs_basis"] < 2e-3, e
+    assert e["cent_k"] < 1e-5 and e["cent_q"] < 1e-5, e
+
+
+def assert_later_bounds(e):
+    # fp64 subspace iteration on the fp32 metric against the fp64 one
+    assert e["basis_k"] < 2e-3 and e["basis_q"] < 2e-3, e
+    assert e["phi_k_gram"] < 2e-3 and e["phi_q_gram"] < 2e-3, e
+    assert e["kv_agree"] > 0.99 and e["kv_ari"] > 0.98, e
+    assert e["q_agree"] > 0.99 and e["q_ari"] > 0.98, e
+    assert e["cent_k"] < 1e-5 and e["cent_q"] < 1e-5, e
+
+
+def _f64(hd, name):
+    return np.asarray(hd[name], np.float64)
+
+
+@pytest.mark.parametrize("head_dim,dtype,warm_iters", [(64, "bf16", None), (128, "bf16", None),
+                                                       (64, "f32", None), (128, "bf16", 2)])
+def test_rcp_later_call_small(head_dim, dtype, warm_iters):
+    import torch
+    w = sg.small_workload(name=f"rcpw_{head_dim}_{dtype}", heads=2, n=3000, head_dim=head_dim,
+                          dtype=dtype, components=16, kv_split=2, grid=(5, 20, 30), rho="0.26",
+                          seed=51)
+    heads0 = sg.make_call(w)
+    heads1 = [sg.drift_head(w, heads0[h], h, 1, EPS, names=("q", "k")) for h in range(w.heads)]
+    q0, k0, _, _, _ = upload(w, heads0)
+    q1, k1, _, _, _ = upload(w, heads1)
+    part = _partition(w, SMALL)
+    ik, iq = sg.rcp_init_arrays(w)
+    dev = torch.device("cuda")
+    part(q0, k0, torch.from_numpy(iq).to(dev), torch.from_numpy(ik).to(dev))
+    torch.cuda.synchronize()
+    for h in range(w.heads):
+        e = check_first_call(w, SMALL, _f64(heads0[h], "q"), _f64(heads0[h], "k"), h, part, ik, iq)
+        say(f"[rcp first {w.name}] head {h}: {e}")
+        assert_first_bounds(e)
+    prev = _state(part)
+    lab0 = _labels(part)
+    params = dict(SMALL, iters=warm_iters or SMALL["iters"])
+    part(q1, k1, warm=True, iters=params["iters"])
+    torch.cuda.synchronize()
+    lab1 = _labels(part)
+    for h in range(w.heads):
+        e = check_later_call(w, params, _f64(heads1[h], "q"), _f64(heads1[h], "k"), h, part, prev)
+        e["kv_ari_vs_first"] = ari(lab0[0][h], lab1[0][h])
+        e["q_ari_vs_first"] = ari(lab0[1][h], lab1[1][h])
+        say(f"[rcp later {w.name} iters={params['iters']}] head {h}: {e}")
+        assert_later_bounds(e)
+        assert e["kv_ari_scratch"] > 0.8 and e["q_ari_scratch"] > 0.8, e
+
+
+def _wcss(x, labels):
+    """Within-group sum of squares of the rows of x (fp64)."""
+    tot = 0.0
+    for b in np.unique(labels):
+        xb = x[labels == b]
+        tot += float(((xb - xb.mean(axis=0)) ** 2).sum())
+    return tot
+
+
+def test_rcp_later_call_deterministic_and_unchanged_inputs():
+    # the same sequence twice gives the same bits.  On unchanged inputs the
+    # previous bases are a fixed point of the subspace iteration and the key
+    # centroids map to the K/V centres the first call would move to next, so
+    # the later call continues Lloyd's iteration: the K/V objective in the key
+    # coordinates does not increase (query centres differ by the RMS step, so
+    # only the agreement is reported there)
+    import torch
+    w = sg.small_workload(name="rcpw_det", heads=2, n=2500, head_dim=64, components=8,
+                          kv_split=2, rho="0.3", seed=52)
+    heads = sg.make_call(w)
+    q, k, _, _, _ = upload(w, heads)
+    ik, iq = sg.rcp_init_arrays(w)
+    dev = torch.device("cuda")
+    runs = []
+    for _ in range(2):
+        part = _partition(w, SMALL)
+        part(q, k, torch.from_numpy(iq).to(dev), torch.from_numpy(ik).to(dev))
+        first = _labels(part)
+        part(q, k, warm=True)
+        torch.cuda.synchronize()
+        runs.append((first, _labels(part), part.phi_q.clone(), part.basis_k.clone(),
+                     part.cent_q.clone(), part.phi_k.cpu().numpy().astype(np.float64)))
+    (f0, l0, p0, b0, c0, phik), (f1, l1, p1, b1, c1, _) = runs
+    assert all(np.array_equal(a, b) for a, b in zip(l0, l1))
+    assert bool((p0 == p1).all()) and bool((b0 == b1).all()) and bool((c0 == c1).all())
+    for h in range(w.heads):
+        before, after = _wcss(phik[h], f0[0][h]), _wcss(phik[h], l0[0][h])
+        a_kv, a_q = ari(f0[0][h], l0[0][h]), ari(f0[1][h], l0[1][h])
+        say(f"[rcp later unchanged] head {h}: K/V objective {before:.6g} -> {after:.6g}, "
+            f"ARI vs first call kv {a_kv:.4f} q {a_q:.4f}")
+        assert after <= before * (1 + 1e-6)
+
+
+def test_rcp_later_call_full_size_sampled():
+    # the Wan-like shape: a first call, then a later call on drifted q and k;
+    # head 0 is checked stage by stage on both calls
+    import torch
+    w = sg.workload("wan_rcp")
+    params = sg.RCP_PARAMS
+    arr0 = sg.make_call_arrays(w)
+    arr1 = sg.drift_arrays(w, arr0, 1, EPS)
+    q0, k0, _, _, _ = upload_arrays(w, arr0)
+    q1, k1, _, _, _ = upload_arrays(w, arr1)
+    part = _partition(w, params)
+    ik, iq = sg.rcp_init_arrays(w)
+    dev = torch.device("cuda")
+    part(q0, k0, torch.from_numpy(iq).to(dev), torch.from_numpy(ik).to(dev))
+    torch.cuda.synchronize()
+    f32 = (lambda a: sg.bf16_bits_to_f32(a).astype(np.float64))
+    e = check_first_call(w, params, f32(arr0["q"][0]), f32(arr0["k"][0]), 0, part, ik, iq)
+    say(f"[rcp first wan] head 0: {e}")
+    assert_first_bounds(e)
+    prev = _state(part)
+    del q0, k0
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    part(q1, k1, warm=True)
+    e1.record()
+    torch.cuda.synchronize()
+    say(f"[rcp later wan] partition {e0.elapsed_time(e1):.2f} ms (first call included warm-up)")
+    e = check_later_call(w, params, f32(arr1["q"][0]), f32(arr1["k"][0]), 0, part, prev,
+                         full_oracle=False)
+    say(f"[rcp later wan] head 0: {e}")
+    assert_later_bounds(e)
