@@ -304,17 +304,53 @@ def key_token_budget(rho, n_q, n_k, m):
     return max(0, math.ceil((Fraction(rho) * n_q - m_eff) * n_k / n_q))
 
 
+class _HeadOffset:
+    """A device address `h0` heads into a tensor with the given head stride
+    (elements); passed to the ABI like a tensor."""
+
+    def __init__(self, t, h0, stride_head):
+        self._p = t.data_ptr() + int(h0) * int(stride_head) * t.element_size()
+
+    def data_ptr(self):
+        return self._p
+
+
+_PER_HEAD = ("perm_q", "perm_kv", "offsets_q", "offsets_kv", "q_g", "k_g", "v_g", "v_shift",
+             "centroid_q", "centroid_k", "cell_rowptr", "cell_col", "routed_pairs", "o_sp", "lse",
+             "probe_rows", "probe_tokens", "o_probe_dense", "o_probe_sparse", "corr_a",
+             "corr_psi_t", "corr_c", "corr_g", "out")
+
+
+class _Heads:
+    """Heads h0..h1 of a call: their dims, views of the call's buffers and a
+    workspace set."""
+
+    def __init__(self, call, h0, h1, ws):
+        self.h0, self.h1 = h0, h1
+        d = call.dims
+        self.dims = Dims(h1 - h0, d.n_q, d.n_k, d.head_dim, d.dtype, d.c_q, d.c_k, 0,
+                         d.q_stride_head, d.q_stride_tok, d.kv_stride_head, d.kv_stride_tok)
+        for name in _PER_HEAD:
+            setattr(self, name, getattr(call, name)[h0:h1])
+        self.ws_layout, self.ws_route, self.ws_attn, self.ws_probe = ws
+
+
 class SparsePRCall:
     """Device buffers and stream plumbing for repeated calls of one shape.
 
     Inputs are torch tensors on the GPU: q [H][N_q][d], k, v [H][N_k][d]
     (bf16 or f32, or any layout with contiguous last dim given via strides),
-    labels int32 [H][N].  Outputs stay resident on the device."""
+    labels int32 [H][N].  Outputs stay resident on the device.
+
+    head_chunks > 1 splits a call into that many ranges of heads, issued on
+    two alternating streams (with the probe fits on a third), so that the
+    layout and routing of one range run while the attention of the previous
+    one does; every head is computed exactly as in a whole call."""
 
     def __init__(self, heads, n_q, n_k, head_dim, dtype, c_q, c_k, m=64, rank=16, lam=0.1,
                  rho="0.26", budget=None, out_dtype=F32, device="cuda", q_strides=None,
                  kv_strides=None, overlap=True, feat_dim=0, estimator="full",
-                 route_rule="global"):
+                 route_rule="global", head_chunks=1):
         load_library()
         self.dims = make_dims(heads, n_q, n_k, head_dim, dtype, c_q, c_k, q_strides, kv_strides)
         self.m, self.rank, self.lam = m, rank, lam
@@ -364,81 +400,110 @@ class SparsePRCall:
         self.corr_g = torch.zeros(H, d, dtype=torch.float32, device=dev)
         odt = torch.bfloat16 if out_dtype == BF16 else torch.float32
         self.out = torch.empty(H, n_q, d, dtype=odt, device=dev)
-
-        def ws(which):
-            nb = workspace_bytes(which, self.dims, m, rank)
-            return torch.empty(max(nb, 256), dtype=torch.uint8, device=dev)
-
-        self.ws_layout = ws(CALL_PARTITION_LAYOUT)
-        self.ws_route = ws(CALL_ROUTE_CELLS if self.route_rule == ROUTE_GLOBAL
-                           else CALL_ROUTE_CELLS_EX)
-        self.ws_attn = ws(CALL_SPARSE_ATTN)
         self._ex = bool(feat_dim) or self.estimator != EST_FULL
-        self.ws_probe = ws(CALL_PROBE_FIT_EX if self._ex else CALL_PROBE_FIT)
+
+        def ws_set(dims):
+            def ws(which):
+                nb = workspace_bytes(which, dims, m, rank)
+                return torch.empty(max(nb, 256), dtype=torch.uint8, device=dev)
+            return (ws(CALL_PARTITION_LAYOUT),
+                    ws(CALL_ROUTE_CELLS if self.route_rule == ROUTE_GLOBAL else CALL_ROUTE_CELLS_EX),
+                    ws(CALL_SPARSE_ATTN),
+                    ws(CALL_PROBE_FIT_EX if self._ex else CALL_PROBE_FIT))
+
+        self._whole = _Heads(self, 0, H, ws_set(self.dims))
+        self.ws_layout, self.ws_route, self.ws_attn, self.ws_probe = (
+            self._whole.ws_layout, self._whole.ws_route, self._whole.ws_attn, self._whole.ws_probe)
         self.side = torch.cuda.Stream(device=dev) if overlap else None
         self.ev_routed = torch.cuda.Event()
         self.ev_fit = torch.cuda.Event()
+        # head ranges of a chunked call: two workspace sets, used alternately
+        self.chunks = None
+        k = max(1, min(int(head_chunks), H))
+        if k > 1:
+            bounds = [H * i // k for i in range(k + 1)]
+            hc = max(b - a for a, b in zip(bounds, bounds[1:]))
+            cdims = make_dims(hc, n_q, n_k, head_dim, dtype, c_q, c_k, q_strides, kv_strides)
+            sets = (ws_set(cdims), ws_set(cdims))
+            self.chunks = [_Heads(self, a, b, sets[i % 2])
+                           for i, (a, b) in enumerate(zip(bounds, bounds[1:]))]
+            self.stream_b = torch.cuda.Stream(device=dev)
+            self.ev_start = torch.cuda.Event()
+            self.ev_b_done = torch.cuda.Event()
+            self.ev_routed_c = [torch.cuda.Event() for _ in self.chunks]
+            self.ev_fit_c = [torch.cuda.Event() for _ in self.chunks]
 
-    # individual stages -------------------------------------------------------
-    def layout(self, labels_q, labels_kv, q, k, v, stream=None):
-        sparsepr_partition_layout(self.dims, labels_q, labels_kv, q, k, v, self.perm_q,
-                                  self.offsets_q, self.perm_kv, self.offsets_kv, self.q_g,
-                                  self.k_g, self.v_g, self.v_shift, self.centroid_q,
-                                  self.centroid_k,
-                                  self.ws_layout, stream)
+    # individual stages (all heads, or the head range `part`) ---------------
+    def layout(self, labels_q, labels_kv, q, k, v, stream=None, part=None):
+        p = part or self._whole
+        d = self.dims
+        sparsepr_partition_layout(p.dims, labels_q[p.h0:p.h1], labels_kv[p.h0:p.h1],
+                                  _HeadOffset(q, p.h0, d.q_stride_head),
+                                  _HeadOffset(k, p.h0, d.kv_stride_head),
+                                  _HeadOffset(v, p.h0, d.kv_stride_head), p.perm_q,
+                                  p.offsets_q, p.perm_kv, p.offsets_kv, p.q_g,
+                                  p.k_g, p.v_g, p.v_shift, p.centroid_q,
+                                  p.centroid_k,
+                                  p.ws_layout, stream)
 
-    def route(self, stream=None):
+    def route(self, stream=None, part=None):
+        p = part or self._whole
         if self.route_rule != ROUTE_GLOBAL:
-            sparsepr_route_cells_ex(self.dims, self.route_rule, self.offsets_q, self.offsets_kv,
-                                    self.centroid_q, self.centroid_k, self.budget,
-                                    self.cell_rowptr, self.cell_col, self.routed_pairs,
-                                    self.ws_route, stream)
+            sparsepr_route_cells_ex(p.dims, self.route_rule, p.offsets_q, p.offsets_kv,
+                                    p.centroid_q, p.centroid_k, self.budget,
+                                    p.cell_rowptr, p.cell_col, p.routed_pairs,
+                                    p.ws_route, stream)
             return
-        sparsepr_route_cells(self.dims, self.offsets_q, self.offsets_kv, self.centroid_q,
-                             self.centroid_k, self.budget, self.cell_rowptr, self.cell_col,
-                             self.routed_pairs, self.ws_route, stream)
+        sparsepr_route_cells(p.dims, p.offsets_q, p.offsets_kv, p.centroid_q,
+                             p.centroid_k, self.budget, p.cell_rowptr, p.cell_col,
+                             p.routed_pairs, p.ws_route, stream)
 
-    def attend(self, stream=None):
-        sparsepr_sparse_attn(self.dims, self.offsets_q, self.offsets_kv, self.cell_rowptr,
-                             self.cell_col, self.q_g, self.k_g, self.v_g, self.v_shift,
-                             self.scale, self.o_sp,
-                             self.lse, self.ws_attn, stream)
+    def attend(self, stream=None, part=None):
+        p = part or self._whole
+        sparsepr_sparse_attn(p.dims, p.offsets_q, p.offsets_kv, p.cell_rowptr,
+                             p.cell_col, p.q_g, p.k_g, p.v_g, p.v_shift,
+                             self.scale, p.o_sp,
+                             p.lse, p.ws_attn, stream)
 
-    def probe_fit(self, stream=None):
+    def probe_fit(self, stream=None, part=None):
+        p = part or self._whole
         if self._ex:
             if self.feat_dim and self.probe_feat is None:
                 raise SparsePRError("probe_feat is not set")
-            sparsepr_probe_fit_ex(self.dims, self.m, self.rank, self.lam, self.estimator,
-                                  self.offsets_q, self.offsets_kv, self.perm_q, self.cell_rowptr,
-                                  self.cell_col, self.centroid_q,
-                                  self.probe_feat if self.feat_dim else None, self.feat_dim,
-                                  self.q_g, self.k_g, self.v_g, self.v_shift, self.scale,
-                                  self.probe_rows, self.probe_tokens, self.o_probe_dense,
-                                  self.o_probe_sparse, self.corr_a, self.corr_psi_t, self.corr_c,
-                                  self.corr_g, self.ws_probe, stream)
+            feat = self.probe_feat[p.h0:p.h1] if self.feat_dim else None
+            sparsepr_probe_fit_ex(p.dims, self.m, self.rank, self.lam, self.estimator,
+                                  p.offsets_q, p.offsets_kv, p.perm_q, p.cell_rowptr,
+                                  p.cell_col, p.centroid_q, feat, self.feat_dim,
+                                  p.q_g, p.k_g, p.v_g, p.v_shift, self.scale,
+                                  p.probe_rows, p.probe_tokens, p.o_probe_dense,
+                                  p.o_probe_sparse, p.corr_a, p.corr_psi_t, p.corr_c,
+                                  p.corr_g, p.ws_probe, stream)
             return
-        sparsepr_probe_fit(self.dims, self.m, self.rank, self.lam, self.offsets_q,
-                           self.offsets_kv, self.perm_q, self.cell_rowptr, self.cell_col,
-                           self.centroid_q, self.q_g, self.k_g, self.v_g, self.v_shift,
+        sparsepr_probe_fit(p.dims, self.m, self.rank, self.lam, p.offsets_q,
+                           p.offsets_kv, p.perm_q, p.cell_rowptr, p.cell_col,
+                           p.centroid_q, p.q_g, p.k_g, p.v_g, p.v_shift,
                            self.scale,
-                           self.probe_rows, self.probe_tokens, self.o_probe_dense,
-                           self.o_probe_sparse, self.corr_a, self.corr_psi_t, self.corr_c,
-                           self.ws_probe, stream)
+                           p.probe_rows, p.probe_tokens, p.o_probe_dense,
+                           p.o_probe_sparse, p.corr_a, p.corr_psi_t, p.corr_c,
+                           p.ws_probe, stream)
 
-    def correct(self, stream=None):
+    def correct(self, stream=None, part=None):
+        p = part or self._whole
         if self.estimator != EST_FULL:
-            sparsepr_correct_ex(self.dims, self.m, self.rank, self.perm_q, self.o_sp,
-                                self.probe_tokens, self.o_probe_dense, self.corr_a,
-                                self.corr_psi_t, self.corr_c, self.corr_g, self.out,
-                                self.out_dtype, self.out.stride(0), self.out.stride(1), stream)
+            sparsepr_correct_ex(p.dims, self.m, self.rank, p.perm_q, p.o_sp,
+                                p.probe_tokens, p.o_probe_dense, p.corr_a,
+                                p.corr_psi_t, p.corr_c, p.corr_g, p.out,
+                                self.out_dtype, p.out.stride(0), p.out.stride(1), stream)
             return
-        sparsepr_correct(self.dims, self.m, self.rank, self.perm_q, self.o_sp, self.probe_tokens,
-                         self.o_probe_dense, self.corr_a, self.corr_psi_t, self.corr_c, self.out,
-                         self.out_dtype, self.out.stride(0), self.out.stride(1), stream)
+        sparsepr_correct(p.dims, self.m, self.rank, p.perm_q, p.o_sp, p.probe_tokens,
+                         p.o_probe_dense, p.corr_a, p.corr_psi_t, p.corr_c, p.out,
+                         self.out_dtype, p.out.stride(0), p.out.stride(1), stream)
 
     def __call__(self, labels_q, labels_kv, q, k, v):
         """One whole attention call on the current stream (probe fit on the
         side stream when overlap is on).  Returns the output tensor."""
+        if self.chunks is not None:
+            return self._chunked(labels_q, labels_kv, q, k, v)
         main = torch.cuda.current_stream()
         self.layout(labels_q, labels_kv, q, k, v)
         self.route()
@@ -453,4 +518,33 @@ class SparsePRCall:
             self.attend()
             self.probe_fit()
         self.correct()
+        return self.out
+
+    def _chunked(self, labels_q, labels_kv, q, k, v):
+        """Head ranges on the current stream and stream_b in turn.  A range
+        reuses the workspace set of the range two before it, which ran on the
+        same stream (and whose probe fit ran earlier on the in-order side
+        stream), so stream order alone keeps the sets from being shared."""
+        main = torch.cuda.current_stream()
+        self.ev_start.record(main)
+        self.stream_b.wait_event(self.ev_start)
+        if self.side is not None:
+            self.side.wait_event(self.ev_start)
+        for i, p in enumerate(self.chunks):
+            s = main if i % 2 == 0 else self.stream_b
+            self.layout(labels_q, labels_kv, q, k, v, stream=s, part=p)
+            self.route(stream=s, part=p)
+            if self.side is not None:
+                self.ev_routed_c[i].record(s)
+                self.side.wait_event(self.ev_routed_c[i])
+                self.probe_fit(stream=self.side, part=p)
+                self.ev_fit_c[i].record(self.side)
+                self.attend(stream=s, part=p)
+                s.wait_event(self.ev_fit_c[i])
+            else:
+                self.attend(stream=s, part=p)
+                self.probe_fit(stream=s, part=p)
+            self.correct(stream=s, part=p)
+        self.ev_b_done.record(self.stream_b)
+        main.wait_event(self.ev_b_done)
         return self.out
