@@ -14,6 +14,11 @@
 // without sorting: a 4096-bucket weighted histogram over the score range
 // narrows the search to one bucket, repeated until at most kCap candidates
 // remain, which are ranked by brute force in LDS.  Pair counts are int64.
+//
+// Work split: row_stats_kernel takes each query group's forced cell and its
+// candidate weight and score range (one wave per group); select_kernel (one
+// block per head) reduces them and searches the crossing cell; count_kernel
+// and emit_kernel then apply the selection row by row and write the CSR.
 
 #include "common.h"
 
@@ -67,16 +72,102 @@ enum { kModeNone = 0, kModeAll = 1, kModeThresh = 2 };
 constexpr int kSelWaves = kSelThreads / 64;
 constexpr int kMaxRowChunks = SPARSEPR_MAX_GROUPS / 64;
 
-// One block per head.  Every pass walks the cell matrix row by row (one wave
-// per query group, lanes over K/V groups), so row quantities are
-// wave-uniform and the score reads are coalesced.
+// Per-head outcome of the crossing search: every cell with (s, a c_k + b)
+// ordered at or before (es, ei) is selected (mode kModeThresh), every
+// candidate (kModeAll) or none besides the forced cells (kModeNone).
+struct SelState {
+  double es;
+  int32_t ei;
+  int32_t mode;
+};
+
+// Pass 1, one wave per query group a: forced cell (best score over the
+// non-empty K/V groups, ties -> smaller b; -1 for an empty group), forced
+// pairs, candidate weight (the other non-empty cells) and candidate score range.
+__global__ __launch_bounds__(256) void row_stats_kernel(
+    const double* __restrict__ scores, const int32_t* __restrict__ off_q,
+    const int32_t* __restrict__ off_k, int c_q, int c_k, int32_t* __restrict__ forced,
+    long long* __restrict__ row_f, long long* __restrict__ row_w, double* __restrict__ row_min,
+    double* __restrict__ row_max) {
+  const int h = blockIdx.y, a = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
+  if (a >= c_q) return;
+  const int32_t* oq = off_q + int64_t(h) * (c_q + 1);
+  const int32_t* ok = off_k + int64_t(h) * (c_k + 1);
+  const long long o = int64_t(h) * c_q + a;
+  const int n_a = oq[a + 1] - oq[a];
+  if (n_a == 0) {
+    if (lane == 0) {
+      forced[o] = -1;
+      row_f[o] = 0;
+      row_w[o] = 0;
+      row_min[o] = __builtin_huge_val();
+      row_max[o] = -__builtin_huge_val();
+    }
+    return;
+  }
+  const double* S = scores + (int64_t(h) * c_q + a) * c_k;
+  const int nbk = (c_k + 63) / 64;
+  double sv[kMaxRowChunks];
+  int mbv[kMaxRowChunks];
+  double best = 0.0;
+  int bb = -1;
+#pragma unroll
+  for (int k = 0; k < kMaxRowChunks; ++k) {
+    const int b = 64 * k + lane;
+    sv[k] = 0.0;
+    mbv[k] = 0;
+    if (k < nbk && b < c_k) {
+      mbv[k] = ok[b + 1] - ok[b];
+      if (mbv[k] > 0) {
+        sv[k] = S[b];
+        if (bb < 0 || sv[k] > best) { best = sv[k]; bb = b; }
+      }
+    }
+  }
+#pragma unroll
+  for (int sh = 32; sh > 0; sh >>= 1) {
+    const double s2 = __shfl_xor(best, sh);
+    const int b2 = __shfl_xor(bb, sh);
+    if (b2 >= 0 && (bb < 0 || s2 > best || (s2 == best && b2 < bb))) { best = s2; bb = b2; }
+  }
+  long long wpart = 0;
+  double lmin = __builtin_huge_val(), lmax = -__builtin_huge_val();
+#pragma unroll
+  for (int k = 0; k < kMaxRowChunks; ++k) {
+    const int b = 64 * k + lane;
+    if (k < nbk && b < c_k && b != bb && mbv[k] > 0) {
+      wpart += (long long)n_a * mbv[k];
+      lmin = sv[k] < lmin ? sv[k] : lmin;
+      lmax = sv[k] > lmax ? sv[k] : lmax;
+    }
+  }
+  wpart = wave_sum(wpart);
+#pragma unroll
+  for (int sh = 32; sh > 0; sh >>= 1) {
+    lmin = fmin(lmin, __shfl_xor(lmin, sh));
+    lmax = fmax(lmax, __shfl_xor(lmax, sh));
+  }
+  if (lane == 0) {
+    forced[o] = bb;
+    row_f[o] = bb >= 0 ? (long long)n_a * (ok[bb + 1] - ok[bb]) : 0;
+    row_w[o] = wpart;
+    row_min[o] = lmin;
+    row_max[o] = lmax;
+  }
+}
+
+// One block per head: the crossing search.  Every pass walks the cell matrix
+// row by row (one wave per query group, lanes over K/V groups), so row
+// quantities are wave-uniform and the score reads are coalesced.
 __global__ __launch_bounds__(kSelThreads) void select_kernel(
     const double* __restrict__ scores, const int32_t* __restrict__ off_q,
     const int32_t* __restrict__ off_k, int c_q, int c_k, long long budget,
-    int32_t* __restrict__ rowptr, int32_t* __restrict__ col, long long* __restrict__ routed) {
+    const int32_t* __restrict__ forced_g, const long long* __restrict__ row_f,
+    const long long* __restrict__ row_w, const double* __restrict__ row_min,
+    const double* __restrict__ row_max, SelState* __restrict__ state) {
   const int h = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   __shared__ int32_t na[SPARSEPR_MAX_GROUPS], mb[SPARSEPR_MAX_GROUPS];
-  __shared__ int32_t forced[SPARSEPR_MAX_GROUPS], rc[SPARSEPR_MAX_GROUPS];
+  __shared__ int32_t forced[SPARSEPR_MAX_GROUPS];
   __shared__ unsigned long long hist_w[kBuckets];
   __shared__ uint32_t hist_c[kBuckets];
   __shared__ double cand_s[kCap];
@@ -92,59 +183,25 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
 
   const int32_t* oq = off_q + int64_t(h) * (c_q + 1);
   const int32_t* ok = off_k + int64_t(h) * (c_k + 1);
-  for (int i = tid; i < c_q; i += kSelThreads) na[i] = oq[i + 1] - oq[i];
-  for (int i = tid; i < c_k; i += kSelThreads) mb[i] = ok[i + 1] - ok[i];
-  if (tid == 0) { sh_es = 0.0; sh_ei = -1; }
-  __syncthreads();
-  const double* S = scores + int64_t(h) * c_q * c_k;
-  const int nbk = (c_k + 63) / 64;
-
-  // pass 1: forced cell of every non-empty query group (best score, ties ->
-  // smaller b), forced pairs, candidate weight and candidate score range
+  const long long ro = int64_t(h) * c_q;
   long long fpart = 0, wpart = 0;
   double lmin = __builtin_huge_val(), lmax = -__builtin_huge_val();
-  for (int a = wid; a < c_q; a += kSelWaves) {
-    const int n_a = na[a];
-    if (n_a == 0) {
-      if (lane == 0) forced[a] = -1;
-      continue;
-    }
-    double sv[kMaxRowChunks];
-    double best = 0.0;
-    int bb = -1;
-#pragma unroll
-    for (int k = 0; k < kMaxRowChunks; ++k) {
-      const int b = 64 * k + lane;
-      sv[k] = 0.0;
-      if (k < nbk && b < c_k && mb[b] > 0) {
-        sv[k] = S[int64_t(a) * c_k + b];
-        if (bb < 0 || sv[k] > best) { best = sv[k]; bb = b; }
-      }
-    }
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-      const double s2 = __shfl_xor(best, o);
-      const int b2 = __shfl_xor(bb, o);
-      if (b2 >= 0 && (bb < 0 || s2 > best || (s2 == best && b2 < bb))) { best = s2; bb = b2; }
-    }
-    if (lane == 0) {
-      forced[a] = bb;
-      if (bb >= 0) fpart += (long long)n_a * mb[bb];
-    }
-#pragma unroll
-    for (int k = 0; k < kMaxRowChunks; ++k) {
-      const int b = 64 * k + lane;
-      if (k < nbk && b < c_k && b != bb && mb[b] > 0) {
-        wpart += (long long)n_a * mb[b];
-        lmin = sv[k] < lmin ? sv[k] : lmin;
-        lmax = sv[k] > lmax ? sv[k] : lmax;
-      }
-    }
+  for (int i = tid; i < c_q; i += kSelThreads) {
+    na[i] = oq[i + 1] - oq[i];
+    forced[i] = forced_g[ro + i];
+    fpart += row_f[ro + i];
+    wpart += row_w[ro + i];
+    lmin = fmin(lmin, row_min[ro + i]);
+    lmax = fmax(lmax, row_max[ro + i]);
   }
+  for (int i = tid; i < c_k; i += kSelThreads) mb[i] = ok[i + 1] - ok[i];
+  if (tid == 0) { sh_es = 0.0; sh_ei = -1; }
   const long long F = block_sum(fpart, red);
   const long long W = block_sum(wpart, red);
   double lo = block_min(lmin, redd);
   double hi = block_max(lmax, redd);
+  const double* S = scores + int64_t(h) * c_q * c_k;
+  const int nbk = (c_k + 63) / 64;
 
   // candidate cells (non-empty, not forced) of the rows this wave walks
   auto for_cands = [&](auto&& fn) {
@@ -295,53 +352,92 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
     }
   }
 
-  // final selection -> per-row counts -> CSR (b ascending)
-  auto selected = [&](int a, int b) -> bool {
-    if (na[a] == 0 || mb[b] == 0) return false;
-    if (b == forced[a]) return true;
-    if (mode == kModeAll) return true;
-    if (mode == kModeNone) return false;
-    const double sc = S[int64_t(a) * c_k + b];
-    const int idx = a * c_k + b;
-    return sc > es || (sc == es && idx <= ei);
-  };
-  for (int a = wid; a < c_q; a += kSelWaves) {
-    int cnt = 0;
-    for (int k = 0; k < nbk; ++k) {
-      const int b = 64 * k + lane;
-      const bool f = b < c_k && selected(a, b);
-      cnt += __popcll(__ballot(f));
-    }
-    if (lane == 0) rc[a] = cnt;
+  if (tid == 0) state[h] = SelState{es, ei, mode};
+}
+
+// Whether cell (a, b) of head h is selected (the forced cell, or ordered at
+// or before the crossing cell).
+SPR_DEV bool cell_selected(const SelState& st, int n_a, int m_b, int fb, int a, int b, int c_k,
+                           const double* S) {
+  if (n_a == 0 || m_b == 0) return false;
+  if (b == fb) return true;
+  if (st.mode == kModeAll) return true;
+  if (st.mode == kModeNone) return false;
+  const double sc = S[int64_t(a) * c_k + b];
+  const int idx = a * c_k + b;
+  return sc > st.es || (sc == st.es && idx <= st.ei);
+}
+
+// Selected cells and pairs of each query group (one wave per group).
+__global__ __launch_bounds__(256) void count_kernel(
+    const double* __restrict__ scores, const int32_t* __restrict__ off_q,
+    const int32_t* __restrict__ off_k, int c_q, int c_k, const int32_t* __restrict__ forced,
+    const SelState* __restrict__ state, int32_t* __restrict__ row_cnt,
+    long long* __restrict__ row_p) {
+  const int h = blockIdx.y, a = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
+  if (a >= c_q) return;
+  const int32_t* oq = off_q + int64_t(h) * (c_q + 1);
+  const int32_t* ok = off_k + int64_t(h) * (c_k + 1);
+  const SelState st = state[h];
+  const int n_a = oq[a + 1] - oq[a], fb = forced[int64_t(h) * c_q + a];
+  const double* S = scores + int64_t(h) * c_q * c_k;
+  int cnt = 0;
+  long long pp = 0;
+  for (int b0 = 0; b0 < c_k; b0 += 64) {
+    const int b = b0 + lane;
+    const int m_b = b < c_k ? ok[b + 1] - ok[b] : 0;
+    const bool f = b < c_k && cell_selected(st, n_a, m_b, fb, a, b, c_k, S);
+    cnt += __popcll(__ballot(f));
+    if (f) pp += (long long)n_a * m_b;
   }
-  __syncthreads();
-  long long mine = tid < c_q ? rc[tid] : 0;
-  long long tot;
-  long long pre = block_exclusive_scan(mine, red, &tot);
+  pp = wave_sum(pp);
+  if (lane == 0) {
+    row_cnt[int64_t(h) * c_q + a] = cnt;
+    row_p[int64_t(h) * c_q + a] = pp;
+  }
+}
+
+// CSR rows (b ascending) and row pointers; the last group's wave also writes
+// the end pointer and the head's routed pairs.  One wave per group.
+__global__ __launch_bounds__(256) void emit_kernel(
+    const double* __restrict__ scores, const int32_t* __restrict__ off_q,
+    const int32_t* __restrict__ off_k, int c_q, int c_k, const int32_t* __restrict__ forced,
+    const SelState* __restrict__ state, const int32_t* __restrict__ row_cnt,
+    const long long* __restrict__ row_p, int32_t* __restrict__ rowptr,
+    int32_t* __restrict__ col, long long* __restrict__ routed) {
+  const int h = blockIdx.y, a = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
+  if (a >= c_q) return;
+  const int32_t* oq = off_q + int64_t(h) * (c_q + 1);
+  const int32_t* ok = off_k + int64_t(h) * (c_k + 1);
+  const int32_t* rc = row_cnt + int64_t(h) * c_q;
+  long long pre = 0;
+  for (int i = lane; i < a; i += 64) pre += rc[i];
+  pre = wave_sum(pre);
   int32_t* rp = rowptr + int64_t(h) * (c_q + 1);
-  if (tid < c_q) rp[tid] = int32_t(pre);
-  if (tid == 0) rp[c_q] = int32_t(tot);
-  __syncthreads();
-  if (tid < c_q) rc[tid] = int32_t(pre);  // reuse as row start
-  __syncthreads();
-  int32_t* cl = col + int64_t(h) * c_q * c_k;
-  long long ppart = 0;
-  for (int a = wid; a < c_q; a += kSelWaves) {
-    int pos = rc[a];
-    for (int k = 0; k < nbk; ++k) {
-      const int b = 64 * k + lane;
-      const bool f = b < c_k && selected(a, b);
-      const unsigned long long m = __ballot(f);
-      if (f) {
-        const int p = __popcll(m & ((1ull << lane) - 1ull));
-        cl[pos + p] = b;
-        ppart += (long long)na[a] * mb[b];
-      }
-      pos += __popcll(m);
+  if (lane == 0) rp[a] = int32_t(pre);
+  if (a == c_q - 1) {
+    long long pt = 0;
+    const long long* rpp = row_p + int64_t(h) * c_q;
+    for (int i = lane; i < c_q; i += 64) pt += rpp[i];
+    pt = wave_sum(pt);
+    if (lane == 0) {
+      rp[c_q] = int32_t(pre + rc[a]);
+      routed[h] = pt;
     }
   }
-  const long long P = block_sum(ppart, red);
-  if (tid == 0) routed[h] = P;
+  const SelState st = state[h];
+  const int n_a = oq[a + 1] - oq[a], fb = forced[int64_t(h) * c_q + a];
+  const double* S = scores + int64_t(h) * c_q * c_k;
+  int32_t* cl = col + int64_t(h) * c_q * c_k;
+  int pos = int(pre);
+  for (int b0 = 0; b0 < c_k; b0 += 64) {
+    const int b = b0 + lane;
+    const int m_b = b < c_k ? ok[b + 1] - ok[b] : 0;
+    const bool f = b < c_k && cell_selected(st, n_a, m_b, fb, a, b, c_k, S);
+    const unsigned long long m = __ballot(f);
+    if (f) cl[pos + __popcll(m & ((1ull << lane) - 1ull))] = b;
+    pos += __popcll(m);
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -492,10 +588,37 @@ size_t route_ex_ws_bytes(const sparsepr_dims* d) {
   return cv.used;
 }
 
+// global rule: scores, then per-row statistics, the per-head search outcome
+// and the per-row counts
+struct SelWs {
+  double* scores;
+  int32_t *forced, *row_cnt;
+  long long *row_f, *row_w, *row_p;
+  double *row_min, *row_max;
+  SelState* state;
+};
+
+SelWs carve_sel(void* base, const sparsepr_dims* d, size_t* used) {
+  Carver cv(base);
+  const size_t H = d->heads, R = H * d->c_q;
+  SelWs w;
+  w.scores = cv.take<double>(R * d->c_k);
+  w.forced = cv.take<int32_t>(R);
+  w.row_cnt = cv.take<int32_t>(R);
+  w.row_f = cv.take<long long>(R);
+  w.row_w = cv.take<long long>(R);
+  w.row_p = cv.take<long long>(R);
+  w.row_min = cv.take<double>(R);
+  w.row_max = cv.take<double>(R);
+  w.state = cv.take<SelState>(H);
+  if (used) *used = cv.used;
+  return w;
+}
+
 size_t route_ws_bytes(const sparsepr_dims* d) {
-  Carver cv(nullptr);
-  cv.take<double>(size_t(d->heads) * d->c_q * d->c_k);
-  return cv.used;
+  size_t used = 0;
+  carve_sel(nullptr, d, &used);
+  return used;
 }
 
 }  // namespace spr
@@ -556,16 +679,26 @@ extern "C" int32_t sparsepr_route_cells(const sparsepr_dims* dims, const int32_t
     return SPARSEPR_ERR_INVALID;
   const size_t need = route_ws_bytes(dims);
   if (!ws || ws_bytes < need) return SPARSEPR_ERR_WORKSPACE;
-  Carver cv(ws);
-  double* scores = cv.take<double>(size_t(dims->heads) * dims->c_q * dims->c_k);
-  const int H = dims->heads, d = dims->head_dim;
-  dim3 g1((dims->c_q + 15) / 16, (dims->c_k + 63) / 64, H);
-  score_kernel<<<g1, 256, 0, stream>>>(centroid_q, centroid_k, scores, dims->c_q, dims->c_k, d,
+  const SelWs w = carve_sel(ws, dims, nullptr);
+  const int H = dims->heads, d = dims->head_dim, c_q = dims->c_q, c_k = dims->c_k;
+  dim3 g1((c_q + 15) / 16, (c_k + 63) / 64, H);
+  score_kernel<<<g1, 256, 0, stream>>>(centroid_q, centroid_k, w.scores, c_q, c_k, d,
                                        __builtin_sqrt(double(d)));
   SPR_LAUNCH_CHECK();
-  select_kernel<<<H, kSelThreads, 0, stream>>>(scores, offsets_q, offsets_kv, dims->c_q,
-                                               dims->c_k, (long long)routed_pair_budget,
-                                               cell_rowptr, cell_col, (long long*)routed_pairs);
+  const dim3 gr((c_q + 3) / 4, H);
+  row_stats_kernel<<<gr, 256, 0, stream>>>(w.scores, offsets_q, offsets_kv, c_q, c_k, w.forced,
+                                           w.row_f, w.row_w, w.row_min, w.row_max);
+  SPR_LAUNCH_CHECK();
+  select_kernel<<<H, kSelThreads, 0, stream>>>(w.scores, offsets_q, offsets_kv, c_q, c_k,
+                                               (long long)routed_pair_budget, w.forced, w.row_f,
+                                               w.row_w, w.row_min, w.row_max, w.state);
+  SPR_LAUNCH_CHECK();
+  count_kernel<<<gr, 256, 0, stream>>>(w.scores, offsets_q, offsets_kv, c_q, c_k, w.forced,
+                                       w.state, w.row_cnt, w.row_p);
+  SPR_LAUNCH_CHECK();
+  emit_kernel<<<gr, 256, 0, stream>>>(w.scores, offsets_q, offsets_kv, c_q, c_k, w.forced,
+                                      w.state, w.row_cnt, w.row_p, cell_rowptr, cell_col,
+                                      (long long*)routed_pairs);
   SPR_LAUNCH_CHECK();
   return SPARSEPR_OK;
 }
