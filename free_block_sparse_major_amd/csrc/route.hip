@@ -29,42 +29,53 @@ constexpr int kSelThreads = 1024;
 constexpr int kBuckets = 4096;
 constexpr int kCap = 2048;
 
-// scores[h][a][b] = dot(cq[h][a], ck[h][b]) / sqrt_d, fp64; tile 16 x 64.
-__global__ __launch_bounds__(256) void score_kernel(const double* __restrict__ cq,
-                                                   const double* __restrict__ ck,
-                                                   double* __restrict__ scores, int c_q, int c_k,
-                                                   int d, double sqrt_d) {
-  const int a0 = blockIdx.x * 16, b0 = blockIdx.y * 64, h = blockIdx.z;
-  __shared__ double As[16][33];
+typedef double f64x4_t __attribute__((ext_vector_type(4)));
+
+// scores[h][a][b] = dot(cq[h][a], ck[h][b]) / sqrt_d in fp64, on
+// v_mfma_f64_16x16x4_f64: a block of 4 waves computes a
+// 64 x 64 tile, wave w rows 16 w .. 16 w + 15 and four 16-column blocks;
+// centroid rows pass through LDS 32 dimensions at a time.  Operand lane l
+// holds row (A) or column (B) l % 16 at k = l / 16; result lane l holds
+// column l % 16 of rows l / 16 + 4 i, i < 4 (checked with an in-bounds probe).  Products accumulate in
+// fp64 (in a different order than the oracle's, within fp64 rounding).
+__global__ __launch_bounds__(256) void score_mfma_kernel(const double* __restrict__ cq,
+                                                         const double* __restrict__ ck,
+                                                         double* __restrict__ scores, int c_q,
+                                                         int c_k, int d, double sqrt_d) {
+  const int a0 = blockIdx.x * 64, b0 = blockIdx.y * 64, h = blockIdx.z;
+  const int tid = threadIdx.x, wid = tid >> 6, lane = tid & 63, r = lane & 15, kq = lane >> 4;
+  __shared__ double As[64][33];
   __shared__ double Bs[64][33];
-  const int ta = threadIdx.x >> 4, tb = threadIdx.x & 15;
   const double* Q = cq + int64_t(h) * c_q * d;
   const double* K = ck + int64_t(h) * c_k * d;
-  double acc[4] = {0.0, 0.0, 0.0, 0.0};
-  for (int d0 = 0; d0 < d; d0 += 32) {
-    for (int i = threadIdx.x; i < 16 * 32; i += 256) {
-      int r = i >> 5, c = i & 31;
-      As[r][c] = a0 + r < c_q ? Q[int64_t(a0 + r) * d + d0 + c] : 0.0;
-    }
-    for (int i = threadIdx.x; i < 64 * 32; i += 256) {
-      int r = i >> 5, c = i & 31;
-      Bs[r][c] = b0 + r < c_k ? K[int64_t(b0 + r) * d + d0 + c] : 0.0;
-    }
-    __syncthreads();
-#pragma unroll 8
-    for (int j = 0; j < 32; ++j) {
-      double av = As[ta][j];
+  f64x4_t acc[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) acc[i] = fma(av, Bs[tb + 16 * i][j], acc[i]);
+  for (int j = 0; j < 4; ++j) acc[j] = f64x4_t{0.0, 0.0, 0.0, 0.0};
+  for (int d0 = 0; d0 < d; d0 += 32) {
+    __syncthreads();
+    for (int i = tid; i < 64 * 32; i += 256) {
+      const int rr = i >> 5, c = i & 31;
+      As[rr][c] = a0 + rr < c_q ? Q[int64_t(a0 + rr) * d + d0 + c] : 0.0;
+      Bs[rr][c] = b0 + rr < c_k ? K[int64_t(b0 + rr) * d + d0 + c] : 0.0;
     }
     __syncthreads();
+#pragma unroll
+    for (int kk = 0; kk < 32; kk += 4) {
+      const double av = As[16 * wid + r][kk + kq];
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        acc[j] = __builtin_amdgcn_mfma_f64_16x16x4f64(av, Bs[16 * j + r][kk + kq], acc[j], 0, 0, 0);
+    }
   }
-  const int a = a0 + ta;
-  if (a >= c_q) return;
-  double* S = scores + (int64_t(h) * c_q + a) * c_k;
-  for (int i = 0; i < 4; ++i) {
-    int b = b0 + tb + 16 * i;
-    if (b < c_k) S[b] = acc[i] / sqrt_d;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int b = b0 + 16 * j + r;
+    if (b >= c_k) continue;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int a = a0 + 16 * wid + kq + 4 * i;
+      if (a < c_q) scores[(int64_t(h) * c_q + a) * c_k + b] = acc[j][i] / sqrt_d;
+    }
   }
 }
 
@@ -648,9 +659,9 @@ extern "C" int32_t sparsepr_route_cells_ex(const sparsepr_dims* dims, int32_t ru
   int32_t* slots = cv.take<int32_t>(size_t(H) * dims->c_q * dims->c_k);
   int32_t* counts = cv.take<int32_t>(size_t(H) * dims->c_q);
   long long* pairs = cv.take<long long>(size_t(H) * dims->c_q);
-  dim3 g1((dims->c_q + 15) / 16, (dims->c_k + 63) / 64, H);
-  score_kernel<<<g1, 256, 0, stream>>>(centroid_q, centroid_k, scores, dims->c_q, dims->c_k, d,
-                                       __builtin_sqrt(double(d)));
+  dim3 g1((dims->c_q + 63) / 64, (dims->c_k + 63) / 64, H);
+  score_mfma_kernel<<<g1, 256, 0, stream>>>(centroid_q, centroid_k, scores, dims->c_q, dims->c_k,
+                                            d, __builtin_sqrt(double(d)));
   SPR_LAUNCH_CHECK();
   group_route_kernel<<<dim3(dims->c_q, H), 256, 0, stream>>>(scores, offsets_q, offsets_kv,
                                                              dims->c_q, dims->c_k,
@@ -681,9 +692,9 @@ extern "C" int32_t sparsepr_route_cells(const sparsepr_dims* dims, const int32_t
   if (!ws || ws_bytes < need) return SPARSEPR_ERR_WORKSPACE;
   const SelWs w = carve_sel(ws, dims, nullptr);
   const int H = dims->heads, d = dims->head_dim, c_q = dims->c_q, c_k = dims->c_k;
-  dim3 g1((c_q + 15) / 16, (c_k + 63) / 64, H);
-  score_kernel<<<g1, 256, 0, stream>>>(centroid_q, centroid_k, w.scores, c_q, c_k, d,
-                                       __builtin_sqrt(double(d)));
+  dim3 g1((c_q + 63) / 64, (c_k + 63) / 64, H);
+  score_mfma_kernel<<<g1, 256, 0, stream>>>(centroid_q, centroid_k, w.scores, c_q, c_k, d,
+                                            __builtin_sqrt(double(d)));
   SPR_LAUNCH_CHECK();
   const dim3 gr((c_q + 3) / 4, H);
   row_stats_kernel<<<gr, 256, 0, stream>>>(w.scores, offsets_q, offsets_kv, c_q, c_k, w.forced,
