@@ -130,7 +130,9 @@ SPR_DEV void split_bf16(float x, uint32_t& hi, uint32_t& lo) {
 // the dims it later corrects: lane l (group G = l / 16) holds row l % 16 and
 // dims 16 b + 4 G + e (b < D / 16, e < 4).  The tile goes back to token
 // order through an LDS stage, one row per 32 (fp32: 64) consecutive lanes.
-template <int D>
+// HAS_G: the diagonal gain term of the restricted estimators is present.
+// c (and g) are read from LDS per tile, which keeps them out of registers.
+template <int D, bool HAS_G>
 __global__ __launch_bounds__(256) void correct_mfma_kernel(const int32_t* __restrict__ perm_q,
                                                            const float* __restrict__ o_sp,
                                                            const float* __restrict__ corr_a,
@@ -144,6 +146,8 @@ __global__ __launch_bounds__(256) void correct_mfma_kernel(const int32_t* __rest
   constexpr int KS = D / 32;           // k-steps of the first product
   constexpr int PITCH = D + 4;         // staged row pitch in floats
   __shared__ float stage[4][16 * PITCH];
+  __shared__ __attribute__((aligned(16))) float c_s[D];
+  __shared__ __attribute__((aligned(16))) float g_s[HAS_G ? D : 4];
   const int h = blockIdx.y, tid = threadIdx.x, wid = tid >> 6, lane = tid & 63;
   const int r16 = lane & 15, G = lane >> 4;
   const float* Ah = corr_a + (long long)h * D * rank;      // [D][rank]
@@ -168,9 +172,13 @@ __global__ __launch_bounds__(256) void correct_mfma_kernel(const int32_t* __rest
     a_hi[s_] = __builtin_bit_cast(bf16x8_t, make_uint4(hw[0], hw[1], hw[2], hw[3]));
     a_lo[s_] = __builtin_bit_cast(bf16x8_t, make_uint4(lw[0], lw[1], lw[2], lw[3]));
   }
+  for (int i = tid; i < D; i += 256) {
+    c_s[i] = ch[i];
+    if constexpr (HAS_G) g_s[i] = corr_g[(long long)h * D + i];
+  }
+  __syncthreads();
   // Psi operand, dim block b: row (dim) 16 b + r16, k = rank 4G + e
   bf16x4_t p_hi[NB], p_lo[NB];
-  f32x4_t cvec[NB], gvec[NB];
 #pragma unroll
   for (int b = 0; b < NB; ++b) {
     uint32_t hw[2], lw[2];
@@ -187,11 +195,6 @@ __global__ __launch_bounds__(256) void correct_mfma_kernel(const int32_t* __rest
     }
     p_hi[b] = __builtin_bit_cast(bf16x4_t, make_uint2(hw[0], hw[1]));
     p_lo[b] = __builtin_bit_cast(bf16x4_t, make_uint2(lw[0], lw[1]));
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      cvec[b][e] = ch[16 * b + 4 * G + e];
-      gvec[b][e] = corr_g ? corr_g[(long long)h * D + 16 * b + 4 * G + e] : 0.f;
-    }
   }
   float* st = stage[wid];
   const int ntile = (n_q + 15) / 16;
@@ -246,8 +249,19 @@ __global__ __launch_bounds__(256) void correct_mfma_kernel(const int32_t* __rest
 #pragma unroll
     for (int b = 0; b < NB; ++b) {
       f32x4_t acc;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) acc[e] = fmaf(gvec[b][e], o[b][e], o[b][e] + cvec[b][e]);
+      const float4 cv = *reinterpret_cast<const float4*>(c_s + 16 * b + 4 * G);
+      if constexpr (HAS_G) {
+        const float4 gv = *reinterpret_cast<const float4*>(g_s + 16 * b + 4 * G);
+        acc[0] = fmaf(gv.x, o[b][0], o[b][0] + cv.x);
+        acc[1] = fmaf(gv.y, o[b][1], o[b][1] + cv.y);
+        acc[2] = fmaf(gv.z, o[b][2], o[b][2] + cv.z);
+        acc[3] = fmaf(gv.w, o[b][3], o[b][3] + cv.w);
+      } else {
+        acc[0] = o[b][0] + cv.x;
+        acc[1] = o[b][1] + cv.y;
+        acc[2] = o[b][2] + cv.z;
+        acc[3] = o[b][3] + cv.w;
+      }
       acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(p_hi[b], ub_hi, acc, 0, 0, 0);
       acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(p_hi[b], ub_lo, acc, 0, 0, 0);
       acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(p_lo[b], ub_hi, acc, 0, 0, 0);
@@ -366,16 +380,18 @@ int32_t correct_impl(const sparsepr_dims* dims, int32_t m, int32_t rank, const i
     constexpr int kTilesPerWave = 4;
     const int ntile = (dims->n_q + 15) / 16;
     dim3 grid((ntile + 4 * kTilesPerWave - 1) / (4 * kTilesPerWave), dims->heads);
-    if (dims->head_dim == 128)
-      correct_mfma_kernel<128><<<grid, 256, 0, stream>>>(perm_q, o_sp, corr_a, corr_psi_t, corr_c,
-                                                         corr_g, out, out_stride_head, out_stride_tok,
-                                                         dims->n_q, rank, a.out_bf16,
-                                                         kTilesPerWave);
-    else
-      correct_mfma_kernel<64><<<grid, 256, 0, stream>>>(perm_q, o_sp, corr_a, corr_psi_t, corr_c,
-                                                        corr_g, out, out_stride_head, out_stride_tok,
-                                                        dims->n_q, rank, a.out_bf16,
-                                                        kTilesPerWave);
+    auto launch = [&](auto kern) {
+      kern<<<grid, 256, 0, stream>>>(perm_q, o_sp, corr_a, corr_psi_t, corr_c, corr_g, out,
+                                     out_stride_head, out_stride_tok, dims->n_q, rank, a.out_bf16,
+                                     kTilesPerWave);
+    };
+    if (dims->head_dim == 128) {
+      if (corr_g) launch(correct_mfma_kernel<128, true>);
+      else launch(correct_mfma_kernel<128, false>);
+    } else {
+      if (corr_g) launch(correct_mfma_kernel<64, true>);
+      else launch(correct_mfma_kernel<64, false>);
+    }
   } else {
     dim3 grid((dims->n_q + 255) / 256, dims->heads);
     if (dims->head_dim == 128) launch_correct<128>(a, grid, stream);
