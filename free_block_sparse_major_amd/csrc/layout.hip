@@ -168,65 +168,6 @@ SPR_DEV int v_shift_of(uint32_t vmax_bits) {
   return s < -100 ? -100 : (s > 100 ? 100 : s);
 }
 
-constexpr int kGatherRows = 64;
-
-__global__ __launch_bounds__(kThreads) void gather_kernel(GatherArgs g) {
-  const int kind = blockIdx.z, h = blockIdx.y;
-  const int n = g.n[kind];
-  const int r0 = blockIdx.x * kGatherRows;
-  if (r0 >= n) return;
-  const int chunks = g.row_bytes >> 4;
-  const int rows = min(kGatherRows, n - r0);
-  const int32_t* perm = g.perm[kind] + int64_t(h) * n;
-  const char* src = g.src[kind] + int64_t(h) * g.stride_head[kind] * g.esize;
-  char* dst = g.dst[kind] + (int64_t(h) * n + r0) * g.row_bytes;
-  const int64_t st = g.stride_tok[kind] * g.esize;
-  // a thread owns one 16-byte column chunk of every RPP-th row; the rows of a
-  // block are handled in unrolled batches so several loads are in flight
-  const int rpp = kThreads / chunks;            // rows per pass
-  const int c = threadIdx.x % chunks, rr = threadIdx.x / chunks;
-  constexpr int kUnroll = 4;
-  const bool conv = kind == 2 && g.vmax;
-  float sc = 1.f;
-  if (conv) {
-    // values: bf16 -> fp16 after the exact per-head power-of-two scale
-    const int sh = v_shift_of(g.vmax[h]);
-    sc = __builtin_ldexpf(1.f, -sh);
-    if (blockIdx.x == 0 && threadIdx.x == 0) g.v_shift[h] = sh;
-  } else if (kind == 2 && blockIdx.x == 0 && threadIdx.x == 0 && g.v_shift) {
-    g.v_shift[h] = 0;
-  }
-  for (int r = rr; r < rows; r += kUnroll * rpp) {
-    uint4 v[kUnroll];
-#pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      const int ru = r + u * rpp;
-      if (ru < rows) {
-        const int tok = perm[r0 + ru];
-        v[u] = *reinterpret_cast<const uint4*>(src + tok * st + c * 16);
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      const int ru = r + u * rpp;
-      if (ru >= rows) break;
-      uint4 w = v[u];
-      if (conv) {
-        uint32_t ws[4] = {w.x, w.y, w.z, w.w};
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const _Float16 lo = static_cast<_Float16>(__uint_as_float(ws[j] << 16) * sc);
-          const _Float16 hi = static_cast<_Float16>(__uint_as_float(ws[j] & 0xffff0000u) * sc);
-          ws[j] = uint32_t(__builtin_bit_cast(uint16_t, lo)) |
-                  (uint32_t(__builtin_bit_cast(uint16_t, hi)) << 16);
-        }
-        w = make_uint4(ws[0], ws[1], ws[2], ws[3]);
-      }
-      *reinterpret_cast<uint4*>(dst + int64_t(ru) * g.row_bytes + c * 16) = w;
-    }
-  }
-}
-
 // Largest |v| of every head of the caller's bf16 values (sign cleared; positive
 // bf16 bit patterns order like their values).  vmax must be zero on entry.
 constexpr int kVmaxRows = 1024;
@@ -252,10 +193,7 @@ __global__ __launch_bounds__(kThreads) void vmax_kernel(const uint16_t* __restri
   if (threadIdx.x == 0) atomicMax(&vmax[h], mx);
 }
 
-// fp64 centroid of each group of the gathered q (kind 0) and k (kind 1).
-// A thread owns 8 consecutive dims (one 16-byte chunk) of a row phase; the
-// phase partials are combined in a fixed order, so the result is
-// deterministic.
+// fp64 sums of one 16-byte chunk of a row (8 bf16 or 4 fp32 values)
 template <typename T>
 SPR_DEV void add_chunk(double* acc, const uint4& w);
 template <>
@@ -275,37 +213,85 @@ SPR_DEV void add_chunk<float>(double* acc, const uint4& w) {
   acc[3] += double(__uint_as_float(w.w));
 }
 
+// Gather fused with the fp64 centroids, one block per group: kind 0 copies
+// the query rows of group a (q -> q_g) and kind 1 the key and value rows of
+// K/V group a (k -> k_g, v -> v_g in fp16 after the head's shift).  The rows
+// of a group are the group-major rows off[a] .. off[a + 1]; thread (ch, ph)
+// copies chunk ch of rows off[a] + ph + i * phases and adds them in that
+// order, and the phase partials are combined in a fixed order, so every
+// centroid is the same sum as a separate pass over the gathered rows.
 template <typename T>
-__global__ __launch_bounds__(kThreads) void centroid_kernel(const T* q_g, const T* k_g,
-                                                            const int32_t* off_q, const int32_t* off_k,
-                                                            double* cen_q, double* cen_k, int n_q,
-                                                            int n_k, int c_q, int c_k, int d) {
-  constexpr int EPC = 16 / sizeof(T);          // elements per 16-byte chunk
+__global__ __launch_bounds__(kThreads) void gather_group_kernel(GatherArgs g,
+                                                                const int32_t* __restrict__ off_q,
+                                                                const int32_t* __restrict__ off_k,
+                                                                double* __restrict__ cen_q,
+                                                                double* __restrict__ cen_k,
+                                                                int c_q, int c_k, int d) {
+  constexpr int EPC = 16 / sizeof(T);
   const int kind = blockIdx.z, h = blockIdx.y, a = blockIdx.x;
   const int C = kind == 0 ? c_q : c_k;
   if (a >= C) return;
-  const int N = kind == 0 ? n_q : n_k;
+  const int n = g.n[kind];
   const int32_t* off = (kind == 0 ? off_q : off_k) + int64_t(h) * (C + 1);
-  const T* x = (kind == 0 ? q_g : k_g) + int64_t(h) * N * d;
   double* cen = (kind == 0 ? cen_q : cen_k) + (int64_t(h) * C + a) * d;
+  const int32_t* perm = g.perm[kind] + int64_t(h) * n;
+  const char* src = g.src[kind] + int64_t(h) * g.stride_head[kind] * g.esize;
+  char* dst = g.dst[kind] + int64_t(h) * n * g.row_bytes;
+  const int64_t st = g.stride_tok[kind] * g.esize;
+  const bool with_v = kind == 1;
+  const char* vsrc = g.src[2] + int64_t(h) * g.stride_head[2] * g.esize;
+  char* vdst = g.dst[2] + int64_t(h) * n * g.row_bytes;
+  const int64_t vst = g.stride_tok[2] * g.esize;
+  const bool conv = g.vmax != nullptr;
+  float sc = 1.f;
+  if (with_v) {
+    const int sh = conv ? v_shift_of(g.vmax[h]) : 0;
+    sc = __builtin_ldexpf(1.f, -sh);
+    if (a == 0 && threadIdx.x == 0 && g.v_shift) g.v_shift[h] = sh;
+  }
   __shared__ double part[kThreads * 8];
-  const int cpr = d / EPC;                     // chunks per row
+  const int cpr = d / EPC;
   const int phases = kThreads / cpr;
   const int ch = threadIdx.x % cpr, ph = threadIdx.x / cpr;
   const int lo = off[a], hi = off[a + 1];
   double acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-  // four rows' loads in flight per step; the additions keep row order
+  auto put_v = [&](int row, uint4 w) __attribute__((always_inline)) {
+    if (conv) {
+      uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const _Float16 l16 = static_cast<_Float16>(__uint_as_float(ws[j] << 16) * sc);
+        const _Float16 h16 = static_cast<_Float16>(__uint_as_float(ws[j] & 0xffff0000u) * sc);
+        ws[j] = uint32_t(__builtin_bit_cast(uint16_t, l16)) |
+                (uint32_t(__builtin_bit_cast(uint16_t, h16)) << 16);
+      }
+      w = make_uint4(ws[0], ws[1], ws[2], ws[3]);
+    }
+    *reinterpret_cast<uint4*>(vdst + int64_t(row) * g.row_bytes + ch * 16) = w;
+  };
   int r = lo + ph;
   for (; r + 3 * phases < hi; r += 4 * phases) {
-    uint4 w[4];
+    uint4 w[4], wv[4];
 #pragma unroll
-    for (int u = 0; u < 4; ++u)
-      w[u] = *reinterpret_cast<const uint4*>(x + int64_t(r + u * phases) * d + ch * EPC);
+    for (int u = 0; u < 4; ++u) {
+      const int tok = perm[r + u * phases];
+      w[u] = *reinterpret_cast<const uint4*>(src + tok * st + ch * 16);
+      if (with_v) wv[u] = *reinterpret_cast<const uint4*>(vsrc + tok * vst + ch * 16);
+    }
 #pragma unroll
-    for (int u = 0; u < 4; ++u) add_chunk<T>(acc, w[u]);
+    for (int u = 0; u < 4; ++u) {
+      *reinterpret_cast<uint4*>(dst + int64_t(r + u * phases) * g.row_bytes + ch * 16) = w[u];
+      add_chunk<T>(acc, w[u]);
+      if (with_v) put_v(r + u * phases, wv[u]);
+    }
   }
-  for (; r < hi; r += phases)
-    add_chunk<T>(acc, *reinterpret_cast<const uint4*>(x + int64_t(r) * d + ch * EPC));
+  for (; r < hi; r += phases) {
+    const int tok = perm[r];
+    const uint4 w = *reinterpret_cast<const uint4*>(src + tok * st + ch * 16);
+    *reinterpret_cast<uint4*>(dst + int64_t(r) * g.row_bytes + ch * 16) = w;
+    add_chunk<T>(acc, w);
+    if (with_v) put_v(r, *reinterpret_cast<const uint4*>(vsrc + tok * vst + ch * 16));
+  }
 #pragma unroll
   for (int e = 0; e < EPC; ++e) part[threadIdx.x * 8 + e] = acc[e];
   __syncthreads();
@@ -407,25 +393,19 @@ extern "C" int32_t sparsepr_partition_layout(const sparsepr_dims* dims, const in
   g.esize = es;
   g.vmax = bf16 ? vmax : nullptr;
   g.v_shift = v_shift;
-  const int maxn = dims->n_q > dims->n_k ? dims->n_q : dims->n_k;
   if (bf16) {
     vmax_kernel<<<dim3((dims->n_k + kVmaxRows - 1) / kVmaxRows, H), kThreads, 0, stream>>>(
         static_cast<const uint16_t*>(v), dims->n_k, d, dims->kv_stride_head, dims->kv_stride_tok,
         vmax);
     SPR_LAUNCH_CHECK();
   }
-  gather_kernel<<<dim3((maxn + kGatherRows - 1) / kGatherRows, H, 3), kThreads, 0, stream>>>(g);
-  SPR_LAUNCH_CHECK();
-
   const int maxc = dims->c_q > dims->c_k ? dims->c_q : dims->c_k;
   if (dims->dtype == SPARSEPR_BF16)
-    centroid_kernel<uint16_t><<<dim3(maxc, H, 2), kThreads, 0, stream>>>(
-        static_cast<const uint16_t*>(q_g), static_cast<const uint16_t*>(k_g), offsets_q,
-        offsets_kv, centroid_q, centroid_k, dims->n_q, dims->n_k, dims->c_q, dims->c_k, d);
+    gather_group_kernel<uint16_t><<<dim3(maxc, H, 2), kThreads, 0, stream>>>(
+        g, offsets_q, offsets_kv, centroid_q, centroid_k, dims->c_q, dims->c_k, d);
   else
-    centroid_kernel<float><<<dim3(maxc, H, 2), kThreads, 0, stream>>>(
-        static_cast<const float*>(q_g), static_cast<const float*>(k_g), offsets_q, offsets_kv,
-        centroid_q, centroid_k, dims->n_q, dims->n_k, dims->c_q, dims->c_k, d);
+    gather_group_kernel<float><<<dim3(maxc, H, 2), kThreads, 0, stream>>>(
+        g, offsets_q, offsets_kv, centroid_q, centroid_k, dims->c_q, dims->c_k, d);
   SPR_LAUNCH_CHECK();
   return SPARSEPR_OK;
 }
