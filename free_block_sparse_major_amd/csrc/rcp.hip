@@ -653,13 +653,15 @@ __global__ __launch_bounds__(256) void kmeans_update_kernel(
 }
 
 // Assignment: label = argmin_c |c|^2 - 2 x.c, ties to the smaller c.  Block =
-// 4 waves x 32 rows; centres pass through LDS 128 at a time (rows padded by
-// 16 bytes, so the 16 rows read by one 16-lane group hit distinct banks).
+// kAssignWaves waves x 32 rows; centres pass through LDS 128 at a time (rows
+// padded by 16 bytes, so the 16 rows read by one 16-lane group hit distinct
+// banks), so each centre tile read from L2 serves 32 kAssignWaves rows.
 // S^T tile = C_tile X^T on v_mfma_f32_32x32x16_bf16: lane l owns row l % 32
 // and 16 centres of each 32-centre block.
 constexpr int kCenterTile = 128;
+constexpr int kAssignWaves = 8;
 template <int RP>
-__global__ __launch_bounds__(256) void kmeans_assign_kernel(
+__global__ __launch_bounds__(64 * kAssignWaves) void kmeans_assign_kernel(
     const uint16_t* __restrict__ xh, const uint16_t* __restrict__ xl, int n,
     const uint16_t* __restrict__ chi, const uint16_t* __restrict__ clo,
     const float* __restrict__ cnorm, int C, int32_t* __restrict__ labels) {
@@ -669,7 +671,8 @@ __global__ __launch_bounds__(256) void kmeans_assign_kernel(
   __shared__ __attribute__((aligned(16))) uint16_t sh[kCenterTile * LD];
   __shared__ __attribute__((aligned(16))) uint16_t sl[kCenterTile * LD];
   __shared__ float sn[kCenterTile];
-  const int row = blockIdx.x * 128 + wid * 32 + nl;
+  constexpr int NT = 64 * kAssignWaves;
+  const int row = blockIdx.x * (32 * kAssignWaves) + wid * 32 + nl;
   bf16x8_t bh[NS], bl[NS];
   {
     const long long o = ((long long)h * n + (row < n ? row : 0)) * RP;
@@ -690,7 +693,7 @@ __global__ __launch_bounds__(256) void kmeans_assign_kernel(
   const float* cn = cnorm + (long long)h * C;
   for (int t0 = 0; t0 < C; t0 += kCenterTile) {
     __syncthreads();
-    for (int e = tid; e < kCenterTile * (RP / 8); e += 256) {
+    for (int e = tid; e < kCenterTile * (RP / 8); e += NT) {
       const int cc = e / (RP / 8), ch8 = e % (RP / 8), c = t0 + cc;
       uint4 a = make_uint4(0, 0, 0, 0), b = make_uint4(0, 0, 0, 0);
       if (c < C) {
@@ -700,7 +703,7 @@ __global__ __launch_bounds__(256) void kmeans_assign_kernel(
       *reinterpret_cast<uint4*>(sh + cc * LD + 8 * ch8) = a;
       *reinterpret_cast<uint4*>(sl + cc * LD + 8 * ch8) = b;
     }
-    for (int e = tid; e < kCenterTile; e += 256) sn[e] = t0 + e < C ? cn[t0 + e] : 0.f;
+    for (int e = tid; e < kCenterTile; e += NT) sn[e] = t0 + e < C ? cn[t0 + e] : 0.f;
     __syncthreads();
 #pragma unroll 1
     for (int j = 0; j < kCenterTile / 32; ++j) {
@@ -817,7 +820,8 @@ int32_t run_kmeans(const RcpWs& w, int H, int n, int C, const int32_t* init, int
     SPR_LAUNCH_CHECK();
   }
   for (int it = 0; it < iters; ++it) {
-    kmeans_assign_kernel<RP><<<dim3((n + 127) / 128, H), 256, 0, stream>>>(
+    kmeans_assign_kernel<RP><<<dim3((n + 32 * kAssignWaves - 1) / (32 * kAssignWaves), H),
+                               64 * kAssignWaves, 0, stream>>>(
         w.xh, w.xl, n, w.chi, w.clo, w.cnorm, C, labels);
     SPR_LAUNCH_CHECK();
     if (it + 1 == iters) break;   // the partition is the last assignment
