@@ -32,12 +32,12 @@ constexpr int kCap = 2048;
 typedef double f64x4_t __attribute__((ext_vector_type(4)));
 
 // scores[h][a][b] = dot(cq[h][a], ck[h][b]) / sqrt_d in fp64, on
-// v_mfma_f64_16x16x4_f64: a block of 4 waves computes a
-// 64 x 64 tile, wave w rows 16 w .. 16 w + 15 and four 16-column blocks;
-// centroid rows pass through LDS 32 dimensions at a time.  Operand lane l
-// holds row (A) or column (B) l % 16 at k = l / 16; result lane l holds
-// column l % 16 of rows l / 16 + 4 i, i < 4 (checked with an in-bounds probe).  Products accumulate in
-// fp64 (in a different order than the oracle's, within fp64 rounding).
+// v_mfma_f64_16x16x4_f64: a block of 4 waves computes a 64 x 64 tile, wave w
+// rows 16 w .. 16 w + 15 and four 16-column blocks; centroid rows pass
+// through LDS 32 dimensions at a time.  Operand lane l holds row (A) or
+// column (B) l % 16 at k = l / 16; result lane l holds column l % 16 of rows
+// l / 16 + 4 i, i < 4.  Products accumulate in fp64, in a different order
+// than a sequential dot product (within fp64 rounding).
 __global__ __launch_bounds__(256) void score_mfma_kernel(const double* __restrict__ cq,
                                                          const double* __restrict__ ck,
                                                          double* __restrict__ scores, int c_q,

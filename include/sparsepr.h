@@ -16,6 +16,24 @@
  * second stream concurrently with sparse_attn (both only read what
  * partition_layout and route_cells wrote).
  *
+ * The comments of this library number the steps of a call:
+ *   S1 stable counting sort of the labels (permutation, group offsets)
+ *   S2 gather of Q, K, V into group-major order (V as scaled fp16)
+ *   S3 fp64 group centroids                       -- partition_layout
+ *   S4 cell routing                               -- route_cells
+ *   S5 sparse attention                           -- sparse_attn
+ *   S6 probe selection (Algorithm A.1)
+ *   S7 exact probe rows (retained / omitted sums)
+ *   S8 weighted ridge fit and residual subspace   -- probe_fit
+ *   S9 correction and restore to token order      -- correct
+ *
+ * Further entry points: sparsepr_rcp_partition builds the query and K/V
+ * groups from the call's own activations (before S1), and
+ * sparsepr_rcp_partition_ex does so across the calls of a layer;
+ * sparsepr_route_cells_ex, sparsepr_probe_fit_ex and sparsepr_correct_ex
+ * add the per-group routing rule, probe features and the restricted
+ * residual estimators.
+ *
  * Conventions shared by every call
  *   - Every pointer argument is a DEVICE pointer unless marked (host).
  *     Every buffer is allocated, owned and freed by the caller; the library
