@@ -15,7 +15,11 @@ Source pages (cited by title and section):
   [project] The SparsePR project page (method cards, Tables 1-2).
 
 Every step works per attention head: the fit is per query head ([paper]
-App. A.2, first paragraph).  All floating point is fp64; the inputs are the
+App. A.2, first paragraph).  The section comments below number the steps of
+a call: S1 group-major layout (permutation, offsets, gather), S3 group
+means, S4 budget and routing, S5 renormalised hard-drop attention, S6 probe
+selection, S7 exact probe rows, S8 ridge fit and residual subspace, S9
+corrected output.  All floating point is fp64; the inputs are the
 exact fp32 values (or the bf16 values widened exactly).
 
 Readings taken where the pages are silent or garbled are marked READING and
