@@ -122,18 +122,19 @@ __global__ __launch_bounds__(256) void row_stats_kernel(
   int mbv[kMaxRowChunks];
   double best = 0.0;
   int bb = -1;
+  // every load first (scores and group sizes are independent), then the
+  // candidate tests, so the loads of a row are in flight together
 #pragma unroll
   for (int k = 0; k < kMaxRowChunks; ++k) {
     const int b = 64 * k + lane;
-    sv[k] = 0.0;
-    mbv[k] = 0;
-    if (k < nbk && b < c_k) {
-      mbv[k] = ok[b + 1] - ok[b];
-      if (mbv[k] > 0) {
-        sv[k] = S[b];
-        if (bb < 0 || sv[k] > best) { best = sv[k]; bb = b; }
-      }
-    }
+    const bool in = k < nbk && b < c_k;
+    sv[k] = in ? S[b] : 0.0;
+    mbv[k] = in ? ok[b + 1] - ok[b] : 0;
+  }
+#pragma unroll
+  for (int k = 0; k < kMaxRowChunks; ++k) {
+    const int b = 64 * k + lane;
+    if (mbv[k] > 0 && (bb < 0 || sv[k] > best)) { best = sv[k]; bb = b; }
   }
 #pragma unroll
   for (int sh = 32; sh > 0; sh >>= 1) {
