@@ -215,17 +215,25 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
   const double* S = scores + int64_t(h) * c_q * c_k;
   const int nbk = (c_k + 63) / 64;
 
-  // candidate cells (non-empty, not forced) of the rows this wave walks
+  // candidate cells (non-empty, not forced) of the rows this wave walks; a
+  // row's scores are loaded together before its candidates are visited
   auto for_cands = [&](auto&& fn) {
     for (int a = wid; a < c_q; a += kSelWaves) {
       const int n_a = na[a];
       if (n_a == 0) continue;
       const int fb = forced[a];
-      for (int k = 0; k < nbk; ++k) {
+      double sv[kMaxRowChunks];
+#pragma unroll
+      for (int k = 0; k < kMaxRowChunks; ++k) {
         const int b = 64 * k + lane;
-        if (b < c_k && b != fb) {
+        sv[k] = k < nbk && b < c_k ? S[int64_t(a) * c_k + b] : 0.0;
+      }
+#pragma unroll
+      for (int k = 0; k < kMaxRowChunks; ++k) {
+        const int b = 64 * k + lane;
+        if (k < nbk && b < c_k && b != fb) {
           const int m = mb[b];
-          if (m > 0) fn(S[int64_t(a) * c_k + b], (long long)n_a * m, a * c_k + b);
+          if (m > 0) fn(sv[k], (long long)n_a * m, a * c_k + b);
         }
       }
     }
