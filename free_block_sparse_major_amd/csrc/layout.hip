@@ -51,24 +51,38 @@ __global__ __launch_bounds__(kThreads) void hist_kernel(KindArgs qa, KindArgs ka
 }
 
 // One block per (head, kind): exclusive scan of counts[c][tile] in (c, tile)
-// order, in place.  offsets[c] = base of (c, tile 0), offsets[C] = N.
+// order, in place.  offsets[c] = base of (c, tile 0), offsets[C] = N.  Each
+// wave scans a contiguous segment 64 entries at a time (coalesced loads, a
+// shuffle scan per 64), after the segment totals are scanned across waves.
 __global__ __launch_bounds__(1024) void scan_kernel(KindArgs qa, KindArgs ka) {
   const KindArgs& A = blockIdx.y == 0 ? qa : ka;
   const int h = blockIdx.x;
-  __shared__ long long red[16];
+  constexpr int kWaves = 1024 / 64;
+  __shared__ long long wt[kWaves];
+  const int wid = threadIdx.x >> 6, lane = threadIdx.x & 63;
   int32_t* cnt = A.counts + int64_t(h) * A.c * A.ntiles;
   const long long len = int64_t(A.c) * A.ntiles;
-  const long long per = (len + blockDim.x - 1) / blockDim.x;
-  const long long lo = per * threadIdx.x;
-  const long long hi = lo + per < len ? lo + per : len;
+  const long long seg = (len + kWaves - 1) / kWaves;
+  const long long lo = seg * wid < len ? seg * wid : len;
+  const long long hi = lo + seg < len ? lo + seg : len;
   long long s = 0;
-  for (long long i = lo; i < hi; ++i) s += cnt[i];
-  long long total;
-  long long run = block_exclusive_scan(s, red, &total);
-  for (long long i = lo; i < hi; ++i) {
-    int32_t v = cnt[i];
-    cnt[i] = int32_t(run);
-    run += v;
+  for (long long i = lo + lane; i < hi; i += 64) s += cnt[i];
+  s = wave_sum(s);
+  if (lane == 0) wt[wid] = s;
+  __syncthreads();
+  long long carry = 0;
+  for (int w = 0; w < wid; ++w) carry += wt[w];
+  for (long long base = lo; base < hi; base += 64) {
+    const long long i = base + lane;
+    const int v = i < hi ? cnt[i] : 0;
+    int x = v;   // inclusive scan of the 64 entries
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int y = __shfl_up(x, o);
+      if (lane >= o) x += y;
+    }
+    if (i < hi) cnt[i] = int32_t(carry + x - v);
+    carry += __shfl(x, 63);
   }
   __syncthreads();
   int32_t* off = A.offsets + int64_t(h) * (A.c + 1);
