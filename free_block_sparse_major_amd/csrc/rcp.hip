@@ -622,33 +622,62 @@ __global__ __launch_bounds__(256) void kmeans_init_proj_kernel(const float* __re
 
 // Update: mean of each cluster's rows (perm/offsets from the stable sort of
 // the labels); an empty cluster keeps its centre.  One block per cluster:
-// thread (rl, j) sums coordinate j over the cluster's rows rl, rl + 4, ...
-// in order, and the four partial sums are added in a fixed order.
+// thread (ph, ch) adds chunk ch (8 coordinates, hi + lo of the bf16 pair) of
+// the cluster's rows ph, ph + phases, ... in order, and wave 0 adds the phase
+// partials of each coordinate in a fixed order.
 template <int RP>
 __global__ __launch_bounds__(256) void kmeans_update_kernel(
     const int32_t* __restrict__ perm, const int32_t* __restrict__ offsets,
     const uint16_t* __restrict__ xh, const uint16_t* __restrict__ xl, int n, int C, float* cent,
     uint16_t* chi, uint16_t* clo, float* cnorm) {
-  const int h = blockIdx.y, c = blockIdx.x, rl = threadIdx.x >> 6, j = threadIdx.x & 63;
-  __shared__ float part[4][64];
+  constexpr int CPR = RP / 8, PH = 256 / CPR;
+  const int h = blockIdx.y, c = blockIdx.x, tid = threadIdx.x;
+  const int ch = tid % CPR, ph = tid / CPR;
+  __shared__ float part[PH * CPR][8];
   const int32_t* off = offsets + (long long)h * (C + 1);
   const int b0 = off[c], b1 = off[c + 1];
   const int32_t* pr = perm + (long long)h * n;
-  float s = 0.f;
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  auto add = [&](const uint4& a, const uint4& b) __attribute__((always_inline)) {
+    const uint32_t wa[4] = {a.x, a.y, a.z, a.w}, wb[4] = {b.x, b.y, b.z, b.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      acc[2 * e] += __uint_as_float(wa[e] << 16) + __uint_as_float(wb[e] << 16);
+      acc[2 * e + 1] += __uint_as_float(wa[e] & 0xffff0000u) + __uint_as_float(wb[e] & 0xffff0000u);
+    }
+  };
+  if (ph < PH) {
+    int r = b0 + ph;
+    for (; r + PH < b1; r += 2 * PH) {
+      const long long o0 = ((long long)h * n + pr[r]) * RP + 8 * ch;
+      const long long o1 = ((long long)h * n + pr[r + PH]) * RP + 8 * ch;
+      const uint4 a0 = *reinterpret_cast<const uint4*>(xh + o0);
+      const uint4 l0 = *reinterpret_cast<const uint4*>(xl + o0);
+      const uint4 a1 = *reinterpret_cast<const uint4*>(xh + o1);
+      const uint4 l1 = *reinterpret_cast<const uint4*>(xl + o1);
+      add(a0, l0);
+      add(a1, l1);
+    }
+    for (; r < b1; r += PH) {
+      const long long o = ((long long)h * n + pr[r]) * RP + 8 * ch;
+      add(*reinterpret_cast<const uint4*>(xh + o), *reinterpret_cast<const uint4*>(xl + o));
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) part[tid][e] = acc[e];
+  }
+  __syncthreads();
+  if (tid >= 64) return;
+  const int j = tid;
+  float v = 0.f;
   if (j < RP) {
-#pragma unroll 4
-    for (int r = b0 + rl; r < b1; r += 4) {
-      const long long o = ((long long)h * n + pr[r]) * RP + j;
-      s += bf16_to_f32(xh[o]) + bf16_to_f32(xl[o]);
+    if (b1 > b0) {
+      float t = 0.f;
+      for (int p2 = 0; p2 < PH; ++p2) t += part[p2 * CPR + j / 8][j % 8];
+      v = t / float(b1 - b0);
+    } else {
+      v = cent[((long long)h * C + c) * RP + j];
     }
   }
-  part[rl][j] = s;
-  __syncthreads();
-  if (rl != 0) return;
-  float v = 0.f;
-  if (j < RP)
-    v = b1 > b0 ? (((part[0][j] + part[1][j]) + part[2][j]) + part[3][j]) / float(b1 - b0)
-                : cent[((long long)h * C + c) * RP + j];
   store_center<RP>(h, c, C, v, cent, chi, clo, cnorm);
 }
 
@@ -742,10 +771,12 @@ __global__ __launch_bounds__(64 * kAssignWaves) void kmeans_assign_kernel(
 }
 
 // Mean of each group's rows in the original space (fp32).  One block per
-// group: thread (rl, j) sums dimension j over rows rl, rl + RL, ... in order
-// (RL = 256 / D row lanes); partial sums are added in a fixed order.  An
-// empty group takes its initial row init[h][c] when init is given and keeps
-// its entry otherwise (the centroid of an earlier call).
+// group: thread (ph, ch) adds the 16-byte chunk ch of rows ph, ph + phases,
+// ... of the group in order (8 bf16 or 4 fp32 values), and the phase partials
+// of each dimension are added in a fixed order.  An empty group takes its
+// initial row init[h][c] when init is given and keeps its entry otherwise
+// (the centroid of an earlier call).  Rows are 16-byte aligned (as for the
+// layout call).
 template <int D>
 __global__ __launch_bounds__(256) void key_centroid_kernel(const int32_t* __restrict__ perm,
                                                            const int32_t* __restrict__ offsets,
@@ -753,28 +784,60 @@ __global__ __launch_bounds__(256) void key_centroid_kernel(const int32_t* __rest
                                                            long long st, int n, int C,
                                                            const int32_t* __restrict__ init,
                                                            float* __restrict__ cent) {
-  constexpr int RL = 256 / D;
-  const int h = blockIdx.y, c = blockIdx.x, rl = threadIdx.x / D, j = threadIdx.x % D;
-  __shared__ float part[RL][D];
+  const int h = blockIdx.y, c = blockIdx.x, tid = threadIdx.x;
+  const bool bf = dtype == SPARSEPR_BF16;
+  const int epc = bf ? 8 : 4;             // elements per 16-byte chunk
+  const int cpr = D / epc, phases = 256 / cpr;
+  const int ch = tid % cpr, ph = tid / cpr;
+  __shared__ float part[256][8];
   const int32_t* off = offsets + (long long)h * (C + 1);
   const int b0 = off[c], b1 = off[c + 1];
   const int32_t* pr = perm + (long long)h * n;
-  float s = 0.f;
-#pragma unroll 4
-  for (int r = b0 + rl; r < b1; r += RL) s += load_elem(k, dtype, h * sh + (long long)pr[r] * st + j);
-  part[rl][j] = s;
-  __syncthreads();
-  if (rl != 0) return;
-  float t = part[0][j];
+  const size_t es = bf ? 2 : 4;
+  const char* base = static_cast<const char*>(k) + (long long)h * sh * es;
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  auto add = [&](const uint4& w) __attribute__((always_inline)) {
+    if (bf) {
+      const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
-  for (int i = 1; i < RL; ++i) t += part[i][j];
-  float* out = cent + ((long long)h * C + c) * D + j;
-  if (b1 > b0) {
-    *out = t / float(b1 - b0);
-  } else if (init) {
-    int row = init[(long long)h * C + c];
-    row = row < 0 ? 0 : (row >= n ? n - 1 : row);
-    *out = load_elem(k, dtype, h * sh + (long long)row * st + j);
+      for (int e = 0; e < 4; ++e) {
+        acc[2 * e] += __uint_as_float(ws[e] << 16);
+        acc[2 * e + 1] += __uint_as_float(ws[e] & 0xffff0000u);
+      }
+    } else {
+      acc[0] += __uint_as_float(w.x);
+      acc[1] += __uint_as_float(w.y);
+      acc[2] += __uint_as_float(w.z);
+      acc[3] += __uint_as_float(w.w);
+    }
+  };
+  int r = b0 + ph;
+  for (; r + 3 * phases < b1; r += 4 * phases) {
+    uint4 w[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      w[u] = *reinterpret_cast<const uint4*>(base + ((long long)pr[r + u * phases] * st) * es +
+                                             ch * 16);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) add(w[u]);
+  }
+  for (; r < b1; r += phases)
+    add(*reinterpret_cast<const uint4*>(base + ((long long)pr[r] * st) * es + ch * 16));
+#pragma unroll
+  for (int e = 0; e < 8; ++e) part[tid][e] = acc[e];
+  __syncthreads();
+  for (int j = tid; j < D; j += 256) {
+    const int cj = j / epc, e = j % epc;
+    float t = 0.f;
+    for (int p2 = 0; p2 < phases; ++p2) t += part[p2 * cpr + cj][e];
+    float* out = cent + ((long long)h * C + c) * D + j;
+    if (b1 > b0) {
+      *out = t / float(b1 - b0);
+    } else if (init) {
+      int row = init[(long long)h * C + c];
+      row = row < 0 ? 0 : (row >= n ? n - 1 : row);
+      *out = load_elem(k, dtype, h * sh + (long long)row * st + j);
+    }
   }
 }
 
