@@ -144,6 +144,9 @@ def main():
                          "every step runs a later call from the previous call's state")
     ap.add_argument("--warm-iters", type=int, default=None,
                     help="Lloyd iterations of later calls (default: those of the first call)")
+    ap.add_argument("--serial", action="store_true",
+                    help="run the probe fit on the main stream after the attention (no side "
+                         "stream): per-kernel durations without sharing the GPU")
     ap.add_argument("--dense-own", action="store_true",
                     help="also time this library in dense mode (one group, every cell)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MB",
@@ -151,7 +154,8 @@ def main():
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the SparsePR call shards by head with no "
-              "communication, so a multi-GPU figure is not produced by this build.",
+              "communication; its multi-GPU throughput is N times the single-GPU figure "
+              "and is not measured here.",
               file=sys.stderr)
         sys.exit(2)
 
@@ -193,7 +197,8 @@ def main():
     call = fb.SparsePRCall(w.heads, w.n, w.n, w.head_dim, dtype, w.c_q, w.c_k, m=w.m, rank=w.r,
                            lam=w.lam, rho=w.rho, out_dtype=fb.BF16 if w.dtype == "bf16" else fb.F32,
                            feat_dim=rp["r_q"] if rcp else 0, estimator=args.estimator,
-                           route_rule=args.route_rule, head_chunks=args.head_chunks)
+                           route_rule=args.route_rule, head_chunks=args.head_chunks,
+                           overlap=not args.serial)
     part = None
     if rcp:
         part = fb.RcpPartition(w.heads, w.n, w.n, w.head_dim, dtype, w.c_q, w.c_k, **rp,
@@ -292,6 +297,7 @@ def main():
             "estimator": args.estimator,
             "route_rule": args.route_rule,
             "head_chunks": args.head_chunks,
+            "probe_fit": "main stream after the attention" if args.serial else "side stream",
             "parallelism": "single GPU",
         },
         "executed_pair_tflops": round(call_tflops, 2),

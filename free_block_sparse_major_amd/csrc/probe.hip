@@ -133,12 +133,29 @@ __global__ __launch_bounds__(256) void select_kernel(
   for (int j = tid; j < d; j += 256) cs[j] = c[j];
   __syncthreads();
   double* dh = dist + (long long)h * n_q;
+  // a row's coordinates in order, read 16 bytes at a time when rows are
+  // 16-byte aligned (the same sum as element by element)
+  constexpr int EPV = 16 / sizeof(T);
+  const bool vec = d % EPV == 0;
   for (int r = lo + tid; r < hi; r += 256) {
     const T* x = q_g + ((long long)h * n_q + r) * d;
     double s = 0.0;
-    for (int j = 0; j < d; ++j) {
-      double t = double(to_f32(x[j])) - cs[j];
-      s = fma(t, t, s);
+    if (vec) {
+      for (int j0 = 0; j0 < d; j0 += EPV) {
+        const uint4 w = *reinterpret_cast<const uint4*>(x + j0);
+        T e[EPV];
+        __builtin_memcpy(e, &w, 16);
+#pragma unroll
+        for (int u = 0; u < EPV; ++u) {
+          const double t = double(to_f32(e[u])) - cs[j0 + u];
+          s = fma(t, t, s);
+        }
+      }
+    } else {
+      for (int j = 0; j < d; ++j) {
+        const double t = double(to_f32(x[j])) - cs[j];
+        s = fma(t, t, s);
+      }
     }
     dh[r] = sqrt(s);
   }
@@ -1015,11 +1032,40 @@ __global__ __launch_bounds__(256) void feat_group_kernel(const float* __restrict
                                                          int n_q, int c_q, int fd,
                                                          float* __restrict__ feat_g,
                                                          double* __restrict__ feat_cen) {
-  const int a = blockIdx.x, h = blockIdx.y, rl = threadIdx.x >> 6, j = threadIdx.x & 63;
-  __shared__ double part[4][64];
+  const int a = blockIdx.x, h = blockIdx.y, tid = threadIdx.x;
   const int32_t* o = off_q + (long long)h * (c_q + 1);
   const int lo = o[a], hi = o[a + 1];
   const int32_t* pr = perm_q + (long long)h * n_q;
+  if (fd % 4 == 0) {
+    // 16-byte chunks: thread (ph, ch) copies chunk ch of rows ph, ph + phases,
+    // ... in order and adds them in fp64; phase partials in a fixed order
+    __shared__ double pc[256][4];
+    const int cpr = fd / 4, phases = 256 / cpr;
+    const int ch = tid % cpr, ph = tid / cpr;
+    double acc[4] = {0.0, 0.0, 0.0, 0.0};
+    if (ph < phases) {
+      for (int r = lo + ph; r < hi; r += phases) {
+        const float4 v = *reinterpret_cast<const float4*>(feat + ((long long)h * n_q + pr[r]) * fd +
+                                                          4 * ch);
+        *reinterpret_cast<float4*>(feat_g + ((long long)h * n_q + r) * fd + 4 * ch) = v;
+        acc[0] += double(v.x);
+        acc[1] += double(v.y);
+        acc[2] += double(v.z);
+        acc[3] += double(v.w);
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) pc[tid][e] = acc[e];
+    }
+    __syncthreads();
+    for (int j = tid; j < fd; j += 256) {
+      double t = 0.0;
+      for (int p2 = 0; p2 < phases; ++p2) t += pc[p2 * cpr + j / 4][j % 4];
+      feat_cen[((long long)h * c_q + a) * fd + j] = hi > lo ? t / double(hi - lo) : 0.0;
+    }
+    return;
+  }
+  const int rl = tid >> 6, j = tid & 63;
+  __shared__ double part[4][64];
   double s = 0.0;
   if (j < fd) {
 #pragma unroll 4

@@ -1,6 +1,6 @@
 """GPU parity of response-coupled partitioning (sparsepr_rcp_partition) and of
 the call that runs on its groups (probe distances in the query-response
-coordinates, sparsepr_probe_fit_feat).
+coordinates, sparsepr_probe_fit_ex with a feature array).
 
 [paper] "Partition the Support, Reconstruct the Residual" §4.1, App. B.1,
 App. B.2, App. C.1.  Several partitions are correct up to rounding (k-means
@@ -167,3 +167,20 @@ def test_rcp_full_size_sampled():
         r = oracle_head(w, hd, rows=rows, features=part.phi_q[h].cpu().numpy())
         errs = compare_head(w, g, j, r)
         say(f"[rcp wan] call head {h}: {errs}")
+
+
+@pytest.mark.parametrize("fd", [5, 20])
+def test_probe_feature_widths(fd):
+    # probe features of a width that is (20) or is not (5) a whole number of
+    # 16-byte chunks; the groups are the synthetic call's own
+    import torch
+    w = sg.small_workload(name=f"feat_{fd}", heads=2, n=3000, head_dim=64, components=16,
+                          kv_split=2, grid=(5, 20, 30), rho="0.26", seed=34)
+    heads = sg.make_call(w)
+    rng = np.random.default_rng(100 + fd)
+    feats = rng.standard_normal((w.heads, w.n, fd), dtype=np.float32)
+    g = run_gpu(w, heads, probe_feat=torch.from_numpy(feats).to("cuda"))
+    for h in range(w.heads):
+        r = oracle_head(w, heads[h], features=feats[h])
+        errs = compare_head(w, g, h, r)
+        say(f"[feat {fd}] head {h}: {errs}")
