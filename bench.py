@@ -147,6 +147,11 @@ def main():
     ap.add_argument("--serial", action="store_true",
                     help="run the probe fit on the main stream after the attention (no side "
                          "stream): per-kernel durations without sharing the GPU")
+    ap.add_argument("--flush", choices=("auto", "on", "off"), default="auto",
+                    help="also time calls each preceded by a 512 MB scratch write that evicts "
+                         "the inputs from the caches (auto: when Q, K and V fit in the 256 MB "
+                         "Infinity Cache)")
+    ap.add_argument("--flush-calls", type=int, default=10)
     ap.add_argument("--dense-own", action="store_true",
                     help="also time this library in dense mode (one group, every cell)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MB",
@@ -246,9 +251,14 @@ def main():
     torch.cuda.synchronize()
     t_start = time.perf_counter()
     e_start, e_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    # events between the steps give per-call times (median, minimum) within
+    # the same timed region
+    step_marks = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps - 1)]
     e_start.record()
-    for _ in range(args.steps):
+    for i in range(args.steps):
         step(call)
+        if i + 1 < args.steps:
+            step_marks[i].record()
     e_end.record()
     torch.cuda.synchronize()
     wall_ms = (time.perf_counter() - t_start) * 1e3 / args.steps
@@ -264,6 +274,28 @@ def main():
     torch.cuda.synchronize()
     attn_ms = sum(a.elapsed_time(b) for a, b in attn_events) / len(attn_events)
     call.attend = orig_attend
+    marks = [e_start] + step_marks + [e_end]
+    per_call = sorted(a.elapsed_time(b) for a, b in zip(marks[:-1], marks[1:]))
+    call_ms_median = per_call[len(per_call) // 2]
+    call_ms_min = per_call[0]
+
+    # cache-flushed calls: a 512 MB write (a fill kernel) before each call,
+    # outside the events that time the call
+    input_bytes = sum(t.numel() * t.element_size() for t in (q, k, v))
+    flushed_ms = None
+    if args.flush == "on" or (args.flush == "auto" and input_bytes < (256 << 20)):
+        scratch = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+        times = []
+        for _ in range(args.flush_calls):
+            scratch.fill_(1)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            step(call)
+            e1.record()
+            torch.cuda.synchronize()
+            times.append(e0.elapsed_time(e1))
+        del scratch
+        flushed_ms = sorted(times)[len(times) // 2]
 
     routed = int(call.routed_pairs.sum().item())
     H, n, d, m_eff = w.heads, w.n, w.head_dim, min(w.m, w.n)
@@ -309,8 +341,12 @@ def main():
         "rho_route": round(rho_route, 6),
         "rho_exec": round(rho_exec, 6),
         "wall_ms_per_call": round(wall_ms, 4),
+        "call_ms_median": round(call_ms_median, 4),
+        "call_ms_min": round(call_ms_min, 4),
         "input_generation_s": round(gen_s, 1),
     }
+    if flushed_ms is not None:
+        out["call_ms_flushed_median"] = round(flushed_ms, 4)
     if rcp:
         out["config"]["partition"] = ("response-coupled on the GPU: M_s=%d, r_K=%d, r_Q=%d, "
                                       "%d Lloyd iterations" % (rp["m_s"], rp["r_k"], rp["r_q"],
