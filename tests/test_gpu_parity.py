@@ -36,6 +36,10 @@ CASES = {
                                            seed=29), "default", {"layout": "nhd"}),
     "bf16_budget_zero": (sg.small_workload(heads=2, n=600, head_dim=64, components=6, rho="0.3",
                                            seed=30), "default", {"budget": 0}),
+    # the largest group counts on both sides (1024 query groups, 1024 K/V groups),
+    # a few rows each and some groups empty
+    "bf16_max_groups": (sg.small_workload(heads=1, n=4096, head_dim=64, components=1024,
+                                          kv_split=1, rho="0.3", seed=35), "default", {}),
 }
 
 
