@@ -377,7 +377,7 @@ int32_t correct_impl(const sparsepr_dims* dims, int32_t m, int32_t rank, const i
   if (rank <= 16 && dims->dtype == SPARSEPR_BF16) {
     // bf16 inputs (tolerance of the bf16 path): 16-row tiles on MFMA, 4 waves
     // per block, a few tiles per wave; fp32 inputs keep the fp32 VALU kernel
-    constexpr int kTilesPerWave = 4;
+    constexpr int kTilesPerWave = 8;
     const int ntile = (dims->n_q + 15) / 16;
     dim3 grid((ntile + 4 * kTilesPerWave - 1) / (4 * kTilesPerWave), dims->heads);
     auto launch = [&](auto kern) {
