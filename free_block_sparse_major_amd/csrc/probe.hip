@@ -1023,20 +1023,23 @@ __global__ __launch_bounds__(256) void fit_kernel(FitArgs f) {
 
 // Probe features of a response-coupled partition: rows of `feat` (token
 // order) copied to group-major order and their fp64 mean per group, so the
-// select kernel measures distances in that space.  One block per group:
-// thread (rl, j) handles feature j of rows rl, rl + 4, ... in order; the
-// four partial sums are added in a fixed order.
+// select kernel measures distances in that space.  One block per group.
+// With `chunked` (rows of whole 16-byte chunks, 16-byte aligned arrays),
+// thread (ph, ch) copies chunk ch of rows ph, ph + phases, ...; otherwise
+// thread (rl, j) handles feature j of rows rl, rl + 4, ....  Either way each
+// thread adds its rows in order and the partials are combined in a fixed
+// order.
 __global__ __launch_bounds__(256) void feat_group_kernel(const float* __restrict__ feat,
                                                          const int32_t* __restrict__ perm_q,
                                                          const int32_t* __restrict__ off_q,
-                                                         int n_q, int c_q, int fd,
+                                                         int n_q, int c_q, int fd, int chunked,
                                                          float* __restrict__ feat_g,
                                                          double* __restrict__ feat_cen) {
   const int a = blockIdx.x, h = blockIdx.y, tid = threadIdx.x;
   const int32_t* o = off_q + (long long)h * (c_q + 1);
   const int lo = o[a], hi = o[a + 1];
   const int32_t* pr = perm_q + (long long)h * n_q;
-  if (fd % 4 == 0) {
+  if (chunked) {
     // 16-byte chunks: thread (ph, ch) copies chunk ch of rows ph, ph + phases,
     // ... in order and adds them in fp64; phase partials in a fixed order
     __shared__ double pc[256][4];
@@ -1186,8 +1189,12 @@ int32_t probe_fit_impl(const sparsepr_dims* dims, int32_t m, int32_t rank, doubl
     Carver cv(static_cast<char*>(ws) + probe_ws_bytes(dims, m, rank));
     float* feat_g = cv.take<float>(size_t(H) * dims->n_q * fd);
     double* feat_cen = cv.take<double>(size_t(H) * dims->c_q * fd);
+    // 16-byte chunks when rows are whole chunks and both arrays start on 16 bytes
+    const int chunked = fd % 4 == 0 && (reinterpret_cast<uintptr_t>(feat) & 15) == 0 &&
+                        (reinterpret_cast<uintptr_t>(feat_g) & 15) == 0;
     feat_group_kernel<<<dim3(dims->c_q, H), 256, 0, stream>>>(feat, perm_q, offsets_q, dims->n_q,
-                                                              dims->c_q, fd, feat_g, feat_cen);
+                                                              dims->c_q, fd, chunked, feat_g,
+                                                              feat_cen);
     SPR_LAUNCH_CHECK();
     select_kernel<float><<<dim3(dims->c_q, H), 256, 0, stream>>>(
         feat_g, feat_cen, offsets_q, perm_q, w.m_a, w.rank, w.s_tab, dims->n_q, dims->c_q, fd, m,

@@ -169,17 +169,21 @@ def test_rcp_full_size_sampled():
         say(f"[rcp wan] call head {h}: {errs}")
 
 
-@pytest.mark.parametrize("fd", [5, 20])
-def test_probe_feature_widths(fd):
+@pytest.mark.parametrize("fd,offset", [(5, 0), (20, 0), (20, 1)])
+def test_probe_feature_widths(fd, offset):
     # probe features of a width that is (20) or is not (5) a whole number of
-    # 16-byte chunks; the groups are the synthetic call's own
+    # 16-byte chunks, and a view that starts 4 bytes past a 16-byte boundary;
+    # the groups are the synthetic call's own
     import torch
     w = sg.small_workload(name=f"feat_{fd}", heads=2, n=3000, head_dim=64, components=16,
                           kv_split=2, grid=(5, 20, 30), rho="0.26", seed=34)
     heads = sg.make_call(w)
     rng = np.random.default_rng(100 + fd)
     feats = rng.standard_normal((w.heads, w.n, fd), dtype=np.float32)
-    g = run_gpu(w, heads, probe_feat=torch.from_numpy(feats).to("cuda"))
+    flat = torch.zeros(feats.size + offset, dtype=torch.float32, device="cuda")
+    dev_feats = flat[offset:].view(w.heads, w.n, fd)
+    dev_feats.copy_(torch.from_numpy(feats))
+    g = run_gpu(w, heads, probe_feat=dev_feats)
     for h in range(w.heads):
         r = oracle_head(w, heads[h], features=feats[h])
         errs = compare_head(w, g, h, r)
