@@ -134,6 +134,9 @@ inline size_t elem_bytes(int dtype) { return dtype == SPARSEPR_BF16 ? 2 : 4; }
 
 // Validates the shape; returns a status code.
 int32_t check_dims(const sparsepr_dims* d);
+// rows of q, k and v are read in 16-byte chunks: their base pointers must be
+// 16-byte aligned (the strides are checked by check_dims)
+inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
 
 }  // namespace spr
 

@@ -365,6 +365,9 @@ extern "C" int32_t sparsepr_partition_layout(const sparsepr_dims* dims, const in
   if (!labels_q || !labels_kv || !q || !k || !v || !perm_q || !offsets_q || !perm_kv ||
       !offsets_kv || !q_g || !k_g || !v_g || !v_shift || !centroid_q || !centroid_k)
     return SPARSEPR_ERR_INVALID;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(q_g) || !aligned16(k_g) ||
+      !aligned16(v_g))
+    return SPARSEPR_ERR_INVALID;
   const size_t need = layout_ws_bytes(dims);
   if (need > 0 && (!ws || ws_bytes < need)) return SPARSEPR_ERR_WORKSPACE;
   const int H = dims->heads, d = dims->head_dim;

@@ -1013,6 +1013,7 @@ extern "C" int32_t sparsepr_rcp_partition(const sparsepr_dims* dims, int32_t m_s
   int32_t st = check_dims(dims);
   if (st != SPARSEPR_OK) return st;
   if (!q || !k || !init_q || !init_k || !labels_q || !labels_kv) return SPARSEPR_ERR_INVALID;
+  if (!aligned16(q) || !aligned16(k)) return SPARSEPR_ERR_INVALID;
   if (m_s < 1 || iters < 1 || r_k < 1 || r_q < 1 || r_k > kMaxR || r_q > kMaxR ||
       r_k > dims->head_dim || r_q > dims->head_dim)
     return SPARSEPR_ERR_INVALID;
@@ -1039,6 +1040,7 @@ extern "C" int32_t sparsepr_rcp_partition_ex(const sparsepr_dims* dims, int32_t 
   if (st != SPARSEPR_OK) return st;
   if (!q || !k || !labels_q || !labels_kv || !basis_q || !basis_k || !cent_q || !cent_k)
     return SPARSEPR_ERR_INVALID;
+  if (!aligned16(q) || !aligned16(k)) return SPARSEPR_ERR_INVALID;
   if (warm != 0 && warm != 1) return SPARSEPR_ERR_INVALID;
   if (!warm && (!init_q || !init_k)) return SPARSEPR_ERR_INVALID;
   if (m_s < 1 || iters < 1 || r_k < 1 || r_q < 1 || r_k > kMaxR || r_q > kMaxR ||

@@ -121,6 +121,10 @@ typedef struct sparsepr_dims {
   int32_t c_q;         /* query groups, 1..1024 */
   int32_t c_k;         /* key/value groups, 1..1024 */
   int32_t reserved;    /* must be 0 */
+  /* element strides of q (and of k, v); each a multiple of 16 bytes, with
+   * stride_tok >= head_dim.  The q, k, v base pointers passed to the calls
+   * must be 16-byte aligned (rows are read in 16-byte chunks); otherwise the
+   * call returns SPARSEPR_ERR_INVALID. */
   int64_t q_stride_head, q_stride_tok;
   int64_t kv_stride_head, kv_stride_tok;
 } sparsepr_dims;

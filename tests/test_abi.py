@@ -65,8 +65,8 @@ def test_workspace_sizes(lib):
     assert fb.workspace_bytes(fb.CALL_PROBE_FIT, ok, m=64, rank=65) == 0
 
 
-def _layout_status(lib, dims, null=False, ws_bytes=1 << 30):
-    p = ctypes.c_void_p(0 if null else 4096)
+def _layout_status(lib, dims, null=False, ws_bytes=1 << 30, addr=4096):
+    p = ctypes.c_void_p(0 if null else addr)
     args = [p] * 15
     return lib.sparsepr_partition_layout(ctypes.byref(dims), *args, ctypes.c_void_p(4096),
                                          ws_bytes, None)
@@ -83,6 +83,8 @@ def test_argument_validation_before_launch(lib):
     assert _layout_status(lib, fb.make_dims(2, 300, 300, 64, fb.BF16, 8, 8,
                                             q_strides=(300 * 64, 60))) == fb.ERR_INVALID
     assert _layout_status(lib, good, null=True) == fb.ERR_INVALID
+    # q, k, v read in 16-byte chunks: a base 4 bytes past a boundary is refused
+    assert _layout_status(lib, good, addr=4100) == fb.ERR_INVALID
     assert _layout_status(lib, good, ws_bytes=16) == fb.ERR_WORKSPACE
     P = ctypes.c_void_p(4096)
     # probe_fit: m out of range, rank out of range, lambda 0 with rank > 0
