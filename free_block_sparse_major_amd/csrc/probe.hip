@@ -719,14 +719,12 @@ __global__ __launch_bounds__(256) void fit_kernel(FitArgs f) {
   __shared__ double G[kMaxM * kLd];   // Cholesky factor (lower)
   __shared__ double E[kMaxM * kLd];   // Rw Rw^T, diagonalised in place
   __shared__ double U[kMaxM * kLd];   // eigenvectors (columns)
-  __shared__ double rc[kMaxM / 2], rs[kMaxM / 2];
-  __shared__ int32_t pr_p[kMaxM / 2], pr_q[kMaxM / 2];
   __shared__ double xs[kMaxM][33], rs2[kMaxM][33];   // column chunk staging
   __shared__ int32_t order[kMaxM];
   __shared__ double red[4];
   __shared__ double tcol[kMaxM];
   __shared__ int32_t sh_k;
-  __shared__ int32_t sh_rot, sh_big;
+  __shared__ int32_t sh_rot[2], sh_big[2];   // per sweep parity
 
   const double* X = f.xp + (long long)h * f.m * d;
   const double* R = f.rp + (long long)h * f.m * d;
@@ -843,8 +841,11 @@ __global__ __launch_bounds__(256) void fit_kernel(FitArgs f) {
     }
   }
   __syncthreads();
-  // 6. cyclic Jacobi on E with round-robin disjoint pairs (pair table per
-  // round in LDS; thread t works on pair t/8, columns t%8 + 8l).  A rotation
+  // 6. cyclic Jacobi on E with round-robin disjoint pairs (thread t works on
+  // pair t/8, columns t%8 + 8l; the eight threads of a pair, one wave's
+  // lanes, each compute the pair's rotation from E, so no broadcast and no
+  // barrier separate it from the row pass: a wave's LDS accesses run in
+  // order, and other pairs touch other rows).  A rotation
   // is skipped when |a_pq| is negligible next to the diagonal and next to the
   // trace (the Gram route resolves eigenvalues to ~1e-16 of the trace).  The
   // iteration stops after a sweep without rotations, or after a sweep in
@@ -873,20 +874,27 @@ __global__ __launch_bounds__(256) void fit_kernel(FitArgs f) {
     const int mp = (me + 1) & ~1;   // even player count; player me is a dummy if me is odd
     const int npair = mp / 2;
     const int pi = tid >> 3, cj = tid & 7;
+    if (tid == 0) {
+      sh_rot[0] = 0;
+      sh_big[0] = 0;
+    }
+    __syncthreads();
     for (int sweep = 0; sweep < 20; ++sweep) {
-      if (tid == 0) {
-        sh_rot = 0;
-        sh_big = 0;
-      }
+      // flags of sweep s live in slot s & 1.  Slot par ^ 1 (read by every
+      // thread at the end of the previous sweep) is cleared for the next
+      // sweep only after this sweep's first barrier, which every thread
+      // reaches after that read
+      const int par = sweep & 1;
       for (int rnd = 0; rnd < mp - 1; ++rnd) {
-        if (tid < npair) {
+        int p2 = 0, q2 = 0;
+        double ci = 1.0, si = 0.0;
+        if (pi < npair) {
           int pp, qq;
-          if (tid == 0) { pp = mp - 1; qq = rnd; }
+          if (pi == 0) { pp = mp - 1; qq = rnd; }
           else {
-            pp = rnd + tid; pp -= pp >= mp - 1 ? mp - 1 : 0;
-            qq = rnd - tid; qq += qq < 0 ? mp - 1 : 0;
+            pp = rnd + pi; pp -= pp >= mp - 1 ? mp - 1 : 0;
+            qq = rnd - pi; qq += qq < 0 ? mp - 1 : 0;
           }
-          double c = 1.0, sn = 0.0;
           if (pp < me && qq < me) {
             const double apq = E[pp * kLd + qq];
             const double app = E[pp * kLd + pp], aqq = E[qq * kLd + qq];
@@ -895,21 +903,18 @@ __global__ __launch_bounds__(256) void fit_kernel(FitArgs f) {
               const double tau = (aqq - app) * rcp64(2.0 * apq);
               const double u = fma(tau, tau, 1.0);
               const double t = (tau >= 0 ? 1.0 : -1.0) * rcp64(fabs(tau) + u * rsq64(u));
-              c = rsq64(fma(t, t, 1.0));
-              sn = t * c;
-              sh_rot = 1;
-              if (apq2 > 1e-16 * dd && fabs(apq) > 1e-10 * tr) sh_big = 1;
+              ci = rsq64(fma(t, t, 1.0));
+              si = t * ci;
+              p2 = pp;
+              q2 = qq;
+              if (cj == 0) {
+                sh_rot[par] = 1;
+                if (apq2 > 1e-16 * dd && fabs(apq) > 1e-10 * tr) sh_big[par] = 1;
+              }
             }
           }
-          rc[tid] = c;
-          rs[tid] = sn;
-          pr_p[tid] = pp;
-          pr_q[tid] = qq;
         }
-        __syncthreads();
-        const bool act = pi < npair && rs[pi] != 0.0;
-        const double ci = act ? rc[pi] : 1.0, si = act ? rs[pi] : 0.0;
-        const int p2 = act ? pr_p[pi] : 0, q2 = act ? pr_q[pi] : 0;
+        const bool act = si != 0.0;
         if (act)   // rows: E <- J^T E
           for (int j = cj; j < me; j += 8) {
             const double x1 = E[p2 * kLd + j], x2 = E[q2 * kLd + j];
@@ -917,6 +922,10 @@ __global__ __launch_bounds__(256) void fit_kernel(FitArgs f) {
             E[q2 * kLd + j] = si * x1 + ci * x2;
           }
         __syncthreads();
+        if (rnd == 0 && tid == 0) {
+          sh_rot[par ^ 1] = 0;
+          sh_big[par ^ 1] = 0;
+        }
         if (act)   // columns: E <- E J, U <- U J
           for (int j = cj; j < me; j += 8) {
             const double x1 = E[j * kLd + p2], x2 = E[j * kLd + q2];
@@ -928,8 +937,7 @@ __global__ __launch_bounds__(256) void fit_kernel(FitArgs f) {
           }
         __syncthreads();
       }
-      if (!sh_rot || !sh_big) break;
-      __syncthreads();
+      if (!sh_rot[par] || !sh_big[par]) break;
     }
   }
   __syncthreads();
