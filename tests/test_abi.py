@@ -120,3 +120,27 @@ def test_budget_matches_oracle_closed_form():
     import oracle
     for rho, n, m in [("0.26", 4096, 64), ("0.22", 75600, 64), ("0.26", 118800, 64), ("0.3", 50, 64)]:
         assert fb.routed_pair_budget(rho, n, n, m) == oracle.routed_pair_budget(rho, n, n, m)
+
+
+def test_product_path_does_not_load_the_oracle():
+    """The package (binding and build helper) never imports the CPU oracle:
+    every step of a call runs in libsparsepr.so."""
+    import subprocess
+    import sys
+    code = ("import sys; import free_block_sparse_major_amd as fb; "
+            "import free_block_sparse_major_amd.build; "
+            "print(any(m == 'oracle' or m.startswith('oracle.') for m in sys.modules))")
+    out = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True,
+                         cwd=os.path.dirname(os.path.dirname(os.path.abspath(__file__))))
+    assert out.returncode == 0, out.stderr
+    assert out.stdout.strip() == "False"
+
+
+def test_bench_refuses_more_than_one_gpu():
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    out = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--gpus", "2"],
+                         capture_output=True, text=True, cwd=root, timeout=120)
+    assert out.returncode == 2
+    assert "one GPU" in out.stderr
