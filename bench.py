@@ -6,8 +6,13 @@ A step is one whole attention call (layout, routing, sparse attention,
 probes + fit on a side stream, correction) over all heads of the workload,
 inputs resident in HBM.  For the workload `wan_rcp` the step also builds the
 partition itself (response-coupled partitioning) before the call, and the
-probe distances use the query-response coordinates.  Prints one JSON line.  Only one GPU is used; the
-path shards by head (see the design notes), and --gpus above 1 is refused.
+probe distances use the query-response coordinates.  Prints one JSON line:
+the mean time of the timed steps (`value`), the per-call median and minimum
+from events between the steps, the attention kernel against the bf16 MFMA
+peak (`roofline`), the CPU oracle on a bounded sample (`cpu_baseline`) and,
+for inputs that fit the Infinity Cache, calls timed after a 512 MB cache-
+evicting write.  Only one GPU is used; the path shards by head, and --gpus
+above 1 is refused.
 """
 from __future__ import annotations
 
