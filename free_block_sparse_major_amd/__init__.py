@@ -34,7 +34,7 @@ EXPORTED = (
     "sparsepr_probe_fit", "sparsepr_correct", "sparsepr_workspace_bytes",
     "sparsepr_status_string", "sparsepr_version", "sparsepr_rcp_partition",
     "sparsepr_probe_fit_ex", "sparsepr_correct_ex", "sparsepr_route_cells_ex",
-    "sparsepr_rcp_partition_ex",
+    "sparsepr_rcp_partition_ex", "sparsepr_debug_check",
 )
 
 
@@ -96,6 +96,10 @@ def load_library(path: str = LIB_PATH):
     # labels_q, labels_kv, phi_q, phi_k, ws, ws_bytes, stream
     lib.sparsepr_rcp_partition_ex.argtypes = [DP, I32, I32, I32, I32, I32] + [P] * 12 + [P, SZ, P]
     lib.sparsepr_rcp_partition_ex.restype = I32
+    # dims, m, labels_q, labels_kv, offsets_q, offsets_kv, perm_q, perm_kv, cell_rowptr,
+    # cell_col, routed_pairs, probe_rows, probe_tokens, error_word, stream
+    lib.sparsepr_debug_check.argtypes = [DP, I32] + [P] * 12 + [P]
+    lib.sparsepr_debug_check.restype = I32
     _lib = lib
     return lib
 
@@ -236,6 +240,21 @@ def sparsepr_correct_ex(dims, m, rank, perm_q, o_sp, probe_tokens, o_probe_dense
         _ptr(out), int(out_dtype), int(out_stride_head), int(out_stride_tok), None, 0,
         _stream(stream))
     _check(st, "sparsepr_correct_ex")
+
+
+def sparsepr_debug_check(dims, m, labels_q, labels_kv, offsets_q, offsets_kv, perm_q, perm_kv,
+                         cell_rowptr, cell_col, routed_pairs, probe_rows, probe_tokens,
+                         error_word, stream=None):
+    st = load_library().sparsepr_debug_check(
+        ctypes.byref(dims), int(m), _ptr(labels_q), _ptr(labels_kv), _ptr(offsets_q),
+        _ptr(offsets_kv), _ptr(perm_q), _ptr(perm_kv), _ptr(cell_rowptr), _ptr(cell_col),
+        _ptr(routed_pairs), _ptr(probe_rows), _ptr(probe_tokens), _ptr(error_word),
+        _stream(stream))
+    _check(st, "sparsepr_debug_check")
+
+
+DBG_LABELS, DBG_OFFSETS, DBG_PERM, DBG_ROWPTR, DBG_CELLS, DBG_ROUTE, DBG_PROBES = (
+    1, 2, 4, 8, 16, 32, 64)
 
 
 class RcpPartition:

@@ -28,6 +28,11 @@ int32_t check_dims(const sparsepr_dims* d) {
     return SPARSEPR_ERR_INVALID;
   // group-major tensors are indexed with 32-bit rows inside a head
   if (int64_t(d->c_q) * d->c_k > (int64_t(1) << 30)) return SPARSEPR_ERR_UNSUPPORTED;
+  // the bf16 kernels address one head's K or V rows through a buffer
+  // resource with 32-bit byte offsets (and the fp32 kernels share the limit)
+  if (int64_t(d->n_k) * d->head_dim * es >= (int64_t(1) << 32) ||
+      int64_t(d->n_q) * d->head_dim * 4 >= (int64_t(1) << 32))
+    return SPARSEPR_ERR_UNSUPPORTED;
   return SPARSEPR_OK;
 }
 

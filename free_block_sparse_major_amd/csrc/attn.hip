@@ -27,13 +27,11 @@
 
 #include "common.h"
 #include "lds_dma.h"
+#include "mfma_tiles.h"
 
 namespace spr {
 namespace {
 
-typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
-typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
@@ -181,16 +179,6 @@ struct Stage {
   static constexpr int value = B;
 };
 
-typedef short v4i16_t __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) v4i16_t lds_v4i16_t;
-typedef __attribute__((address_space(3))) void lds_void_t;
-
-template <int D>
-SPR_DEV int swz_v(int row) {
-  return D == 128 ? 4 * (row & 3) : 4 * ((row >> 1) & 1);
-}
-
-typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
 
 
 // Lazy rescale: P is formed against the running reference max and the row is

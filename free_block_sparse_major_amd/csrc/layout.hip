@@ -29,6 +29,11 @@ struct KindArgs {
   int n, c, ntiles;
 };
 
+// Labels outside [0, C) are a caller error (sparsepr_debug_check reports
+// them); they are sorted as the nearest valid group, so perm stays a
+// permutation and every later kernel indexes in bounds.
+SPR_DEV int clamp_label(int l, int c) { return l < 0 ? 0 : (l >= c ? c - 1 : l); }
+
 __global__ __launch_bounds__(kThreads) void hist_kernel(KindArgs qa, KindArgs ka, uint32_t* vmax,
                                                        int heads) {
   const KindArgs& A = blockIdx.z == 0 ? qa : ka;
@@ -43,7 +48,7 @@ __global__ __launch_bounds__(kThreads) void hist_kernel(KindArgs qa, KindArgs ka
   const int t0 = tile * kTile;
   for (int i = threadIdx.x; i < kTile; i += kThreads) {
     int t = t0 + i;
-    if (t < A.n) atomicAdd(&hist[lab[t]], 1);
+    if (t < A.n) atomicAdd(&hist[clamp_label(lab[t], A.c)], 1);
   }
   __syncthreads();
   int32_t* cnt = A.counts + int64_t(h) * A.c * A.ntiles;
@@ -108,7 +113,7 @@ __global__ __launch_bounds__(kThreads) void scatter_kernel(KindArgs qa, KindArgs
     int t = t0 + i;
     uint32_t key = 0xffffffffu;  // padding sorts last
     if (t < A.n) {
-      int l = lab[t];
+      int l = clamp_label(lab[t], A.c);
       key = (uint32_t(l) << 10) | uint32_t(i);
       atomicAdd(&hist[l], 1);
     }

@@ -79,13 +79,16 @@ __global__ __launch_bounds__(256) void score_mfma_kernel(const double* __restric
   }
 }
 
-enum { kModeNone = 0, kModeAll = 1, kModeThresh = 2 };
+enum { kModeNone = 0, kModeAll = 1, kModeThresh = 2, kModeFailed = 3 };
 constexpr int kSelWaves = kSelThreads / 64;
 constexpr int kMaxRowChunks = SPARSEPR_MAX_GROUPS / 64;
 
 // Per-head outcome of the crossing search: every cell with (s, a c_k + b)
 // ordered at or before (es, ei) is selected (mode kModeThresh), every
 // candidate (kModeAll) or none besides the forced cells (kModeNone).
+// kModeFailed: the search found no crossing cell, which finite scores never
+// cause (see select_kernel); the head keeps its forced cells only and its
+// routed pair count is reported as -1.
 struct SelState {
   double es;
   int32_t ei;
@@ -249,6 +252,14 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
     } else {
       mode = kModeThresh;
       long long Tp = T;  // weight still to take inside [lo, hi] (everything above is taken)
+      // Termination: each round either ends (a tie range or at most kCap
+      // candidates) or replaces [lo, hi] by the exact score range of one of
+      // kBuckets = 2^12 equal-width buckets.  The range of finite fp64
+      // scores is below 2^1025 and distinct scores differ by at least
+      // 2^-1074, so at most 175 rounds are ever needed; a non-finite score
+      // (NaN or Inf inputs) can leave the crossing unresolved, which is
+      // reported.
+      bool found = false;
       for (int round = 0; round < 256; ++round) {
         if (lo == hi) {
           // every remaining candidate has the same score: index order decides
@@ -278,6 +289,7 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
           __syncthreads();
           es = sh_es;
           ei = sh_ei;
+          found = true;
           break;
         }
         // weighted histogram of the candidates in [lo, hi]; bucket() is
@@ -354,6 +366,7 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
           __syncthreads();
           es = sh_es;
           ei = sh_ei;
+          found = true;
           break;
         }
         // narrow to the exact score range of the crossing bucket
@@ -368,7 +381,9 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
         const double nhi = block_max(bmax, redd);
         lo = nlo;
         hi = nhi;
+        if (!(lo <= hi)) break;   // NaN bounds: no crossing can be found
       }
+      if (!found || ei < 0) mode = kModeFailed;
     }
   }
 
@@ -382,7 +397,7 @@ SPR_DEV bool cell_selected(const SelState& st, int n_a, int m_b, int fb, int a, 
   if (n_a == 0 || m_b == 0) return false;
   if (b == fb) return true;
   if (st.mode == kModeAll) return true;
-  if (st.mode == kModeNone) return false;
+  if (st.mode == kModeNone || st.mode == kModeFailed) return false;
   const double sc = S[int64_t(a) * c_k + b];
   const int idx = a * c_k + b;
   return sc > st.es || (sc == st.es && idx <= st.ei);
@@ -442,7 +457,7 @@ __global__ __launch_bounds__(256) void emit_kernel(
     pt = wave_sum(pt);
     if (lane == 0) {
       rp[c_q] = int32_t(pre + rc[a]);
-      routed[h] = pt;
+      routed[h] = state[h].mode == kModeFailed ? -1LL : pt;
     }
   }
   const SelState st = state[h];

@@ -45,9 +45,11 @@
  *     sparsepr_workspace_bytes(call, dims, m, rank) (256-byte aligned).
  *     A workspace may be reused by the next call on the same stream.
  *   - Tensors listed as [H][N][d] are dense, row-major, head-major.
- *   - Data errors (labels outside [0, C), NaN inputs) are the caller's
- *     contract and are not detected: NaN/Inf propagate into the outputs,
- *     and out-of-range labels give undefined results.
+ *   - Data errors are the caller's contract: NaN/Inf inputs propagate into
+ *     the outputs, and a label outside [0, C) is sorted as the nearest valid
+ *     group (so every kernel stays inside its buffers, but the results are
+ *     meaningless).  sparsepr_debug_check validates a call's integer data
+ *     on the device and reports such errors in an error word.
  *   - Return value: SPARSEPR_OK, or an error code; on error nothing was
  *     launched.
  */
@@ -65,7 +67,8 @@ extern "C" {
 enum {
   SPARSEPR_OK = 0,
   SPARSEPR_ERR_INVALID = 1,      /* null pointer, bad size, m < 1, rank < 0, ... */
-  SPARSEPR_ERR_UNSUPPORTED = 2,  /* head_dim not 64/128, dtype, C_q or C_k > 1024 */
+  SPARSEPR_ERR_UNSUPPORTED = 2,  /* head_dim not 64/128, dtype, C_q or C_k > 1024,
+                                    N_k*d*(element bytes) or N_q*d*4 at or above 2^32 */
   SPARSEPR_ERR_WORKSPACE = 3,    /* ws_bytes smaller than required */
   SPARSEPR_ERR_HIP = 4           /* a kernel launch failed */
 };
@@ -98,6 +101,19 @@ enum {
   SPARSEPR_EST_MEAN = 1,
   SPARSEPR_EST_SCALAR = 2,
   SPARSEPR_EST_DIAGONAL = 3
+};
+
+/* Error bits of sparsepr_debug_check. */
+enum {
+  SPARSEPR_DBG_LABELS = 1,    /* a label outside [0, C_q) or [0, C_k) */
+  SPARSEPR_DBG_OFFSETS = 2,   /* offsets not 0 .. N non-decreasing */
+  SPARSEPR_DBG_PERM = 4,      /* perm not the stable counting sort of the labels */
+  SPARSEPR_DBG_ROWPTR = 8,    /* cell_rowptr not 0 .. <= C_q*C_k non-decreasing */
+  SPARSEPR_DBG_CELLS = 16,    /* a column outside [0, C_k), not ascending, an empty K/V
+                                 group selected, or a query group with cells iff empty */
+  SPARSEPR_DBG_ROUTE = 32,    /* routed_pairs[h] < 0: routing met non-finite scores */
+  SPARSEPR_DBG_PROBES = 64    /* probe rows out of range, repeated, not -1 past
+                                 min(m, N_q), or a token not perm_q of its row */
 };
 
 #define SPARSEPR_MAX_GROUPS 1024
@@ -187,7 +203,9 @@ int32_t sparsepr_partition_layout(const sparsepr_dims* dims /* host */,
  *   cell_col [H][C_q*C_k]: int32, selected b of query group a in
  *     cell_col[h][rowptr[a] .. rowptr[a+1]), ascending; slots past
  *     rowptr[C_q] are left untouched.
- *   routed_pairs [H]: int64, sum of |G_a||G_b| over selected cells.
+ *   routed_pairs [H]: int64, sum of |G_a||G_b| over selected cells; -1 if
+ *     the head's scores were not finite (NaN/Inf inputs), in which case the
+ *     head keeps only its forced cells.
  */
 int32_t sparsepr_route_cells(const sparsepr_dims* dims /* host */,
                              const int32_t* offsets_q, const int32_t* offsets_kv,
@@ -403,6 +421,41 @@ int32_t sparsepr_correct_ex(const sparsepr_dims* dims /* host */, int32_t m, int
                             void* out, int32_t out_dtype,
                             int64_t out_stride_head, int64_t out_stride_tok,
                             void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * Debug validation of a call's integer data (read-only; for tests and
+ * debugging, not needed by a correct caller).  The quantities are those of
+ * the SparsePR paper's problem setup (§3: query and key index sets
+ * partitioned into groups; cells G_a x G_b selected or not) and of its probe
+ * step (App. A.2, Algorithm A.1: min(M, N_q) distinct probe rows).
+ * Every array argument but error_word may be NULL, and is then not checked:
+ *   labels_q [H][N_q], labels_kv [H][N_k]: in [0, C_q), [0, C_k).
+ *   offsets_q [H][C_q+1], offsets_kv [H][C_k+1]: start at 0, non-decreasing,
+ *     end at N.
+ *   perm_q, perm_kv [H][N]: inside each group, tokens in [0, N), strictly
+ *     ascending, each labelled with its group (needs offsets; labels if
+ *     given).  With valid offsets this makes perm the stable counting sort.
+ *   cell_rowptr [H][C_q+1], cell_col [H][C_q*C_k] (both or neither): CSR
+ *     rows starting at 0 and within C_q*C_k, columns in [0, C_k) strictly
+ *     ascending; with offsets also: no empty K/V group selected, and a query
+ *     group has cells if and only if it is non-empty.
+ *   routed_pairs [H]: not negative.
+ *   probe_rows, probe_tokens [H][m] (m in 1..64): as sparsepr_probe_fit
+ *     writes them; tokens are compared with perm_q when both are given.
+ * error_word: one device uint32, overwritten with the OR of the
+ *   SPARSEPR_DBG_* bits found (0 when everything checked is valid); read it
+ *   after the stream reaches the call.  A value that fails a check is never
+ *   used as an index; values are used as indices only after they have been
+ *   checked against the extent of the array they index.
+ */
+int32_t sparsepr_debug_check(const sparsepr_dims* dims /* host */, int32_t m,
+                             const int32_t* labels_q, const int32_t* labels_kv,
+                             const int32_t* offsets_q, const int32_t* offsets_kv,
+                             const int32_t* perm_q, const int32_t* perm_kv,
+                             const int32_t* cell_rowptr, const int32_t* cell_col,
+                             const int64_t* routed_pairs, const int32_t* probe_rows,
+                             const int32_t* probe_tokens, uint32_t* error_word,
+                             hipStream_t stream);
 
 #ifdef __cplusplus
 }

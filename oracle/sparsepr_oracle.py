@@ -44,6 +44,7 @@ __all__ = [
     "dense_attention_rows",
     "select_probes",
     "probe_weights",
+    "probe_distance_gap",
     "fit_correction",
     "fold_correction",
     "apply_correction",
@@ -282,6 +283,24 @@ def select_probes(features, labels_q, n_groups, m):
     return np.asarray(probes, dtype=np.int64), counts
 
 
+def probe_distance_gap(features, labels_q, counts):
+    """Smallest fp64 distance gap that Algorithm A.1 decides on: within each
+    probed group, between consecutive rows of the (distance, token) order up
+    to and including the first row not taken.  A diagnostic of near-ties in
+    the probe choice (a zero gap means a tie that the token index breaks)."""
+    f = np.asarray(features, dtype=np.float64)
+    labels_q = np.asarray(labels_q)
+    gap = math.inf
+    for a in np.nonzero(np.asarray(counts) > 0)[0]:
+        rows = np.nonzero(labels_q == a)[0]
+        c = f[rows].sum(axis=0) / rows.size
+        dist = np.sort(np.sqrt(((f[rows] - c) ** 2).sum(axis=1)))
+        upto = min(int(counts[a]) + 1, dist.size)
+        if upto >= 2:
+            gap = min(gap, float(np.diff(dist[:upto]).min()))
+    return gap
+
+
 def probe_weights(probe_groups, group_sizes, probe_counts):
     """Coverage weight w_p = |G_a| / m_a for a probe of group a ([review]
     step (4); READING: m_a is the number of probes drawn from group a)."""
@@ -466,6 +485,7 @@ def run_head(q, k, v, labels_q, labels_kv, c_q, c_k, rho, m=64, rank=16, lam=0.1
         "perm_q": perm_q, "offsets_q": off_q, "perm_kv": perm_kv, "offsets_kv": off_kv,
         "qbar": qbar, "kbar": kbar, "budget": budget, "z": z, "routed_pairs": routed,
         "scores": scores, "probes": probes, "probe_counts": counts, "probe_weights": w,
+        "probe_gap": probe_distance_gap(feats, labels_q, counts),
         "dense_p": dense_p, "x_p": x_p, "R_p": R_p, "fit": fit, "A": A, "Psi": Psi,
         "c": c, "T": T, "g": g, "rows": rows, "o_sp": o_sp, "lse": lse, "out": out,
         "scale": scale, "estimator": estimator,

@@ -116,6 +116,35 @@ def test_argument_validation_before_launch(lib):
     assert part_ex(ws_bytes=16) == fb.ERR_WORKSPACE
 
 
+def test_debug_check_and_size_limits(lib):
+    """The debug check refuses a missing error word, a row-pointer array
+    without columns and an m outside 1..64 before launching; shapes whose
+    per-head K/V bytes reach 2^32 are refused as unsupported (the bf16 kernels
+    address a head through 32-bit buffer offsets)."""
+    good = fb.make_dims(2, 300, 300, 64, fb.BF16, 8, 8)
+    P = ctypes.c_void_p(4096)
+    N = None
+
+    def dbg(m=64, rowptr=P, col=P, err=P, probes=P):
+        return lib.sparsepr_debug_check(ctypes.byref(good), m, N, N, N, N, N, N, rowptr, col, N,
+                                        probes, N, err, None)
+    assert dbg(err=None) == fb.ERR_INVALID
+    assert dbg(col=None) == fb.ERR_INVALID
+    assert dbg(m=0) == fb.ERR_INVALID
+    assert dbg(m=65) == fb.ERR_INVALID
+    assert lib.sparsepr_debug_check(ctypes.byref(fb.make_dims(1, 10, 10, 96, fb.BF16, 2, 2)), 1,
+                                    *([N] * 11), P, None) == fb.ERR_UNSUPPORTED
+    # 2^32 / (128 * 2) = 16777216 keys: the first refused count for bf16, d = 128
+    assert _layout_status(lib, fb.make_dims(1, 1000, 16777216, 128, fb.BF16, 8, 8)) == \
+        fb.ERR_UNSUPPORTED
+    assert fb.workspace_bytes(fb.CALL_SPARSE_ATTN,
+                              fb.make_dims(1, 1000, 16777215, 128, fb.BF16, 8, 8)) > 0
+    assert _layout_status(lib, fb.make_dims(1, 1000, 8388608, 128, fb.F32, 8, 8)) == \
+        fb.ERR_UNSUPPORTED
+    assert _layout_status(lib, fb.make_dims(1, 8388608, 1000, 128, fb.BF16, 8, 8)) == \
+        fb.ERR_UNSUPPORTED
+
+
 def test_budget_matches_oracle_closed_form():
     import oracle
     for rho, n, m in [("0.26", 4096, 64), ("0.22", 75600, 64), ("0.26", 118800, 64), ("0.3", 50, 64)]:

@@ -21,5 +21,5 @@ def test_estimator_variants(estimator, head_dim, dtype):
     g = run_gpu(w, heads, estimator=estimator)
     for h in range(w.heads):
         r = oracle_head(w, heads[h], estimator=estimator)
-        errs = compare_head(w, g, h, r)
+        errs = compare_head(w, g, h, r, hd=heads[h])
         say(f"[{estimator} {dtype} d={head_dim}] head {h}: {errs}")

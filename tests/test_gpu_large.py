@@ -59,7 +59,7 @@ def _check(w, heads, expect_waves, rows_per_head=3000):
         hd = sg.make_head(w, h, pos=pos)
         rows = sample_rows(hd["labels_q"], w.c_q, min(rows_per_head, w.n), seed=1000 + h)
         r = oracle_head(w, hd, rows=rows)
-        errs = compare_head(w, g, j, r)
+        errs = compare_head(w, g, j, r, hd=hd)
         say(f"[large {w.name}] head {h}: {errs}")
         for k, v in errs.items():
             worst[k] = max(worst.get(k, 0.0), v)
@@ -84,7 +84,11 @@ def test_twelve_wave_items_d64():
     _check(w, [0, 15], 12)
 
 
-@pytest.mark.parametrize("name,heads,waves", [("wan", [0, 39], 12), ("hunyuan", [0, 23], 8)])
+@pytest.mark.parametrize("name,heads,waves", [("wan", [0, 39], 12), ("hunyuan", [0, 23], 8),
+                                               ("cogvideox", [0, 3, 7], 4)])
 def test_full_size_sampled(name, heads, waves):
+    # the full workloads in the benchmark's launch configuration: the
+    # CogVideoX-like call (8 x 17550, d=64, 64 x 64 groups of ~274 rows) runs
+    # 4-wave items, several per query group, with a ragged last item
     w = sg.workload(name)
     _check(w, heads, waves, rows_per_head=2000)

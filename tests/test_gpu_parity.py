@@ -53,7 +53,7 @@ def _run_case(name, check_fit=True):
     worst = {}
     for h, hd in enumerate(data):
         r = oracle_head(w, hd, budget=budget)
-        errs = compare_head(w, g, h, r)
+        errs = compare_head(w, g, h, r, hd=hd)
         for k2, v in errs.items():
             worst[k2] = max(worst.get(k2, 0.0), v)
     say(f"[case {name}] errors {worst}")

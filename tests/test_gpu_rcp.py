@@ -134,7 +134,7 @@ def test_rcp_call_parity_small():
     for h in range(w.heads):
         feats = part.phi_q[h].cpu().numpy()
         r = oracle_head(w, heads[h], features=feats)
-        errs = compare_head(w, g, h, r)
+        errs = compare_head(w, g, h, r, hd=heads[h])
         say(f"[rcp call] head {h}: {errs}")
 
 
@@ -154,6 +154,13 @@ def test_rcp_full_size_sampled():
     e = check_head(w, params, hd, 0, part, ik, iq)
     say(f"[rcp wan] head 0: {e}")
     assert_stage_bounds(e)
+    # the whole partition against the oracle's from scratch (fp64 metrics,
+    # factors and Lloyd iterations from the same initial rows).  Near-tie
+    # assignments flip with the fp32/bf16-pair rounding of the coordinates and
+    # the flips carry through the 10 iterations, so the partitions are not
+    # identical; a systematic error in the coordinates would move many rows
+    # (ARI far below 0.9).  Measured at this shape: 0.994 K/V, 0.986 queries.
+    assert e["kv_ari_scratch"] >= 0.97 and e["q_ari_scratch"] >= 0.97, e
     lab_q = part.labels_q.cpu().numpy()
     say(f"[rcp wan] non-empty query groups per head: {[int((np.bincount(l, minlength=w.c_q) > 0).sum()) for l in lab_q[:4]]}")
     from test_gpu_large import sample_rows
@@ -165,7 +172,7 @@ def test_rcp_full_size_sampled():
         hd["labels_kv"] = part.labels_kv[h].cpu().numpy()
         rows = sample_rows(hd["labels_q"], w.c_q, 1500, seed=2000 + h)
         r = oracle_head(w, hd, rows=rows, features=part.phi_q[h].cpu().numpy())
-        errs = compare_head(w, g, j, r)
+        errs = compare_head(w, g, j, r, hd=hd)
         say(f"[rcp wan] call head {h}: {errs}")
 
 
@@ -186,5 +193,5 @@ def test_probe_feature_widths(fd, offset):
     g = run_gpu(w, heads, probe_feat=dev_feats)
     for h in range(w.heads):
         r = oracle_head(w, heads[h], features=feats[h])
-        errs = compare_head(w, g, h, r)
+        errs = compare_head(w, g, h, r, hd=heads[h])
         say(f"[feat {fd}] head {h}: {errs}")

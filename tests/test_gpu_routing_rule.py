@@ -23,7 +23,7 @@ def test_per_group_rule(head_dim, dtype, rho):
     for h in range(w.heads):
         r = oracle_head(w, heads[h], route_rule="per_group")
         assert g["budget"] == r["budget"]
-        errs = compare_head(w, g, h, r)
+        errs = compare_head(w, g, h, r, hd=heads[h])
         say(f"[per_group {dtype} d={head_dim} rho={rho}] head {h}: {errs}")
 
 
@@ -35,7 +35,7 @@ def test_per_group_rule_edge_budgets():
     for budget in (0, w.n):
         g = run_gpu(w, heads, budget=budget, route_rule="per_group")
         r = oracle_head(w, heads[0], budget=budget, route_rule="per_group")
-        errs = compare_head(w, g, 0, r)
+        errs = compare_head(w, g, 0, r, hd=heads[0])
         say(f"[per_group budget {budget}] {errs}")
         counts = np.diff(g["cell_rowptr"][0])
         if budget == 0:
@@ -55,5 +55,5 @@ def test_per_group_rule_full_size_sampled():
         hd = sg.make_head(w, h, pos=pos)
         rows = sample_rows(hd["labels_q"], w.c_q, 1500, seed=3000 + h)
         r = oracle_head(w, hd, rows=rows, route_rule="per_group")
-        errs = compare_head(w, g, j, r)
+        errs = compare_head(w, g, j, r, hd=hd)
         say(f"[per_group wan] head {h}: {errs}")

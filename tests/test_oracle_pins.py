@@ -337,6 +337,24 @@ def test_probes_golden():
         assert np.allclose(w, [float(t) for t in weights.split()], rtol=0, atol=1e-15)
 
 
+def test_probe_distance_gap_hand_values():
+    # the golden example above: group 2's two rows tie at distance 2 -> gap 0
+    kv, _ = _read_kv("probe_example.txt")
+    labels = np.array([int(t) for t in kv["labels"]])
+    feats = np.array([[float(t)] for t in kv["features"]])
+    for m in (5, 8, 20):
+        _, c = oracle.select_probes(feats, labels, 4, m)
+        assert oracle.probe_distance_gap(feats, labels, c) == 0.0
+    # groups 0 and 1 only (distances 0,1,2,3 and 1,2,3), M = 3 takes two rows of
+    # group 0 and one of group 1: the decided gaps are all 1
+    keep = labels <= 1
+    _, c = oracle.select_probes(feats[keep], labels[keep], 2, 3)
+    assert c.tolist() == [2, 1]
+    assert oracle.probe_distance_gap(feats[keep], labels[keep], c) == 1.0
+    # one row per group: nothing to decide
+    assert oracle.probe_distance_gap(np.zeros((2, 1)), np.array([0, 1]), np.array([1, 1])) == math.inf
+
+
 def _brute_probes(f, labels, C, M):
     n = len(labels)
     order = {}
