@@ -34,7 +34,7 @@ EXPORTED = (
     "sparsepr_probe_fit", "sparsepr_correct", "sparsepr_workspace_bytes",
     "sparsepr_status_string", "sparsepr_version", "sparsepr_rcp_partition",
     "sparsepr_probe_fit_ex", "sparsepr_correct_ex", "sparsepr_route_cells_ex",
-    "sparsepr_rcp_partition_ex", "sparsepr_debug_check",
+    "sparsepr_rcp_partition_ex", "sparsepr_debug_check", "sparsepr_sparse_attn_noalloc",
 )
 
 
@@ -78,6 +78,9 @@ def load_library(path: str = LIB_PATH):
     lib.sparsepr_route_cells.restype = I32
     lib.sparsepr_sparse_attn.argtypes = [DP, P, P, P, P, P, P, P, P, ctypes.c_float, P, P, P, SZ, P]
     lib.sparsepr_sparse_attn.restype = I32
+    lib.sparsepr_sparse_attn_noalloc.argtypes = [DP, P, P, P, P, P, P, P, P, ctypes.c_float, P,
+                                                 P, P]
+    lib.sparsepr_sparse_attn_noalloc.restype = I32
     lib.sparsepr_probe_fit.argtypes = ([DP, I32, I32, D] + [P] * 10 + [ctypes.c_float] + [P] * 7
                                        + [P, SZ, P])
     lib.sparsepr_probe_fit.restype = I32
@@ -174,6 +177,15 @@ def sparsepr_sparse_attn(dims, offsets_q, offsets_kv, cell_rowptr, cell_col, q_g
         _ptr(q_g), _ptr(k_g), _ptr(v_g), _ptr(v_shift), ctypes.c_float(softmax_scale), _ptr(o_sp), _ptr(lse),
         _ptr(ws), ws.numel() * ws.element_size() if ws is not None else 0, _stream(stream))
     _check(st, "sparsepr_sparse_attn")
+
+
+def sparsepr_sparse_attn_noalloc(dims, offsets_q, offsets_kv, cell_rowptr, cell_col, q_g, k_g,
+                                 v_g, v_shift, softmax_scale, o_sp, lse, stream=None):
+    st = load_library().sparsepr_sparse_attn_noalloc(
+        ctypes.byref(dims), _ptr(offsets_q), _ptr(offsets_kv), _ptr(cell_rowptr), _ptr(cell_col),
+        _ptr(q_g), _ptr(k_g), _ptr(v_g), _ptr(v_shift), ctypes.c_float(softmax_scale),
+        _ptr(o_sp), _ptr(lse), _stream(stream))
+    _check(st, "sparsepr_sparse_attn_noalloc")
 
 
 def sparsepr_probe_fit(dims, m, rank, lam, offsets_q, offsets_kv, perm_q, cell_rowptr, cell_col,

@@ -29,6 +29,8 @@
 #include "lds_dma.h"
 #include "mfma_tiles.h"
 
+#include <mutex>
+
 namespace spr {
 namespace {
 
@@ -795,22 +797,27 @@ size_t attn_ws_bytes(const sparsepr_dims* d) {
 
 using namespace spr;
 
-extern "C" int32_t sparsepr_sparse_attn(const sparsepr_dims* dims, const int32_t* offsets_q,
-                                        const int32_t* offsets_kv, const int32_t* cell_rowptr,
-                                        const int32_t* cell_col, const void* q_g, const void* k_g,
-                                        const void* v_g, const int32_t* v_shift,
-                                        float softmax_scale, float* o_sp,
-                                        float* lse, void* ws, size_t ws_bytes,
-                                        hipStream_t stream) {
+namespace {
+
+int32_t check_attn_args(const sparsepr_dims* dims, const int32_t* offsets_q,
+                        const int32_t* offsets_kv, const int32_t* cell_rowptr,
+                        const int32_t* cell_col, const void* q_g, const void* k_g,
+                        const void* v_g, const int32_t* v_shift, const float* o_sp) {
   int32_t st = check_dims(dims);
   if (st != SPARSEPR_OK) return st;
   if (!offsets_q || !offsets_kv || !cell_rowptr || !cell_col || !q_g || !k_g || !v_g ||
       !v_shift || !o_sp)
     return SPARSEPR_ERR_INVALID;
-  const size_t need = attn_ws_bytes(dims);
-  if (!ws || ws_bytes < need) return SPARSEPR_ERR_WORKSPACE;
-  Carver cv(ws);
-  int32_t* tiles = cv.take<int32_t>(size_t(dims->heads) * dims->c_q + 1);
+  return SPARSEPR_OK;
+}
+
+// The work-item table (H*C_q + 1 int32, rewritten in full by every call)
+// and the attention launch, shared by both entry points.
+int32_t launch_attn(const sparsepr_dims* dims, const int32_t* offsets_q,
+                    const int32_t* offsets_kv, const int32_t* cell_rowptr,
+                    const int32_t* cell_col, const void* q_g, const void* k_g, const void* v_g,
+                    const int32_t* v_shift, float softmax_scale, float* o_sp, float* lse,
+                    int32_t* tiles, hipStream_t stream) {
   const int tq = rows_per_item(dims);
   tile_table_kernel<<<1, 1024, 0, stream>>>(offsets_q, dims->heads, dims->c_q, tq, tiles);
   SPR_LAUNCH_CHECK();
@@ -847,4 +854,72 @@ extern "C" int32_t sparsepr_sparse_attn(const sparsepr_dims* dims, const int32_t
   }
   SPR_LAUNCH_CHECK();
   return SPARSEPR_OK;
+}
+
+// Scratch of the entry point that allocates nothing: the work-item table in
+// a fixed device array.  In host code `scratch` names a host-side stand-in;
+// its device address on each GPU comes from hipGetSymbolAddress, taken once
+// per device with that device current, and only that address is passed on.
+constexpr int kNoAllocTableEntries = 65537;   // H * C_q + 1 <= 65537 (256 KiB)
+static __device__ __align__(256) int32_t scratch[kNoAllocTableEntries];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+int32_t* g_scratch_ptr[kMaxDevices] = {};
+
+int32_t* scratch_on_current_device(int32_t* status) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    *status = SPARSEPR_ERR_HIP;
+    return nullptr;
+  }
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) {
+      *status = SPARSEPR_ERR_HIP;
+      return nullptr;
+    }
+    g_scratch_ptr[dev] = static_cast<int32_t*>(p);
+  }
+  *status = SPARSEPR_OK;
+  return g_scratch_ptr[dev];
+}
+
+}  // namespace
+
+extern "C" int32_t sparsepr_sparse_attn(const sparsepr_dims* dims, const int32_t* offsets_q,
+                                        const int32_t* offsets_kv, const int32_t* cell_rowptr,
+                                        const int32_t* cell_col, const void* q_g, const void* k_g,
+                                        const void* v_g, const int32_t* v_shift,
+                                        float softmax_scale, float* o_sp,
+                                        float* lse, void* ws, size_t ws_bytes,
+                                        hipStream_t stream) {
+  int32_t st = check_attn_args(dims, offsets_q, offsets_kv, cell_rowptr, cell_col, q_g, k_g, v_g,
+                               v_shift, o_sp);
+  if (st != SPARSEPR_OK) return st;
+  const size_t need = attn_ws_bytes(dims);
+  if (!ws || ws_bytes < need) return SPARSEPR_ERR_WORKSPACE;
+  Carver cv(ws);
+  int32_t* tiles = cv.take<int32_t>(size_t(dims->heads) * dims->c_q + 1);
+  return launch_attn(dims, offsets_q, offsets_kv, cell_rowptr, cell_col, q_g, k_g, v_g, v_shift,
+                     softmax_scale, o_sp, lse, tiles, stream);
+}
+
+extern "C" int32_t sparsepr_sparse_attn_noalloc(const sparsepr_dims* dims,
+                                                const int32_t* offsets_q,
+                                                const int32_t* offsets_kv,
+                                                const int32_t* cell_rowptr,
+                                                const int32_t* cell_col, const void* q_g,
+                                                const void* k_g, const void* v_g,
+                                                const int32_t* v_shift, float softmax_scale,
+                                                float* o_sp, float* lse, hipStream_t stream) {
+  int32_t st = check_attn_args(dims, offsets_q, offsets_kv, cell_rowptr, cell_col, q_g, k_g, v_g,
+                               v_shift, o_sp);
+  if (st != SPARSEPR_OK) return st;
+  if (int64_t(dims->heads) * dims->c_q + 1 > kNoAllocTableEntries) return SPARSEPR_ERR_UNSUPPORTED;
+  int32_t* tiles = scratch_on_current_device(&st);
+  if (st != SPARSEPR_OK) return st;
+  return launch_attn(dims, offsets_q, offsets_kv, cell_rowptr, cell_col, q_g, k_g, v_g, v_shift,
+                     softmax_scale, o_sp, lse, tiles, stream);
 }

@@ -38,7 +38,8 @@
  *   - Every pointer argument is a DEVICE pointer unless marked (host).
  *     Every buffer is allocated, owned and freed by the caller; the library
  *     keeps no pointer after a call returns and holds no mutable global
- *     state.  Calls are thread-safe.
+ *     state (except the device array of sparsepr_sparse_attn_noalloc).
+ *     Calls are thread-safe.
  *   - Calls are asynchronous on `stream` and never synchronise the device;
  *     inputs must stay valid until the stream reaches the call.
  *   - Scratch memory is the caller's `ws` of `ws_bytes` bytes, at least
@@ -250,6 +251,27 @@ int32_t sparsepr_sparse_attn(const sparsepr_dims* dims /* host */,
                              const int32_t* v_shift,
                              float softmax_scale, float* o_sp, float* lse,
                              void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * S5 for callers that cannot allocate memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc): as
+ * sparsepr_sparse_attn, without a workspace.  The call allocates nothing;
+ * its work-item table lives in a fixed device array of the library
+ * (65537 int32 = 256 KiB, held on each GPU the library runs on until the
+ * process ends), so H * C_q + 1 must not exceed 65537 (otherwise
+ * SPARSEPR_ERR_UNSUPPORTED).  The table is rewritten in full by every call.
+ * Every call on one GPU shares that array: calls that overlap on one GPU
+ * (different streams, or threads) race and must be serialised by the
+ * caller.  The first call on a device looks the array up with that device
+ * current (SPARSEPR_ERR_HIP if the lookup fails).
+ */
+int32_t sparsepr_sparse_attn_noalloc(const sparsepr_dims* dims /* host */,
+                                     const int32_t* offsets_q, const int32_t* offsets_kv,
+                                     const int32_t* cell_rowptr, const int32_t* cell_col,
+                                     const void* q_g, const void* k_g, const void* v_g,
+                                     const int32_t* v_shift,
+                                     float softmax_scale, float* o_sp, float* lse,
+                                     hipStream_t stream);
 
 /*
  * S6-S8. Probes and correction fit.  (SparsePR paper App. A.2, Algorithm
