@@ -72,18 +72,54 @@ def _traffic_from_profile(workload_name):
     return float(m_b.group(1))
 
 
-def cpu_baseline(w, arrays, budget_seconds=20.0, rcp_params=None, estimator="full",
-                 route_rule="global"):
-    """The oracle, as it is, on the host cores: head 0 in full except the
-    sparse attention, which runs on whole query groups until ~budget_seconds;
-    scaled to ms per call over all heads and all rows."""
+def host_info():
+    """The host the oracle is timed on: CPU model, logical CPUs usable by this
+    process, physical cores (from lscpu, if present) and numpy's BLAS."""
+    import subprocess
     import numpy as np
-    import oracle
+    info = {"logical_cpus": os.cpu_count()}
+    try:
+        info["usable_cpus"] = len(os.sched_getaffinity(0))
+    except Exception:  # pragma: no cover
+        pass
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    info["cpu_model"] = line.split(":", 1)[1].strip()
+                    break
+    except OSError:  # pragma: no cover
+        pass
+    try:
+        out = subprocess.run(["lscpu", "-p=core,socket"], capture_output=True, text=True,
+                             timeout=20).stdout
+        cores = {l for l in out.splitlines() if l and not l.startswith("#")}
+        if cores:
+            info["physical_cores"] = len(cores)
+    except Exception:  # pragma: no cover
+        pass
+    try:
+        blas = np.show_config(mode="dicts")["Build Dependencies"]["blas"]
+        info["blas"] = f"{blas.get('name')} {blas.get('version')}"
+    except Exception:  # pragma: no cover
+        pass
     try:
         from threadpoolctl import threadpool_info
-        cores = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+        pools = [p for p in threadpool_info() if p.get("user_api") == "blas"]
+        if pools:
+            info["blas_threads"] = max(p.get("num_threads", 1) for p in pools)
+            info["blas_internal"] = pools[0].get("internal_api")
     except Exception:  # pragma: no cover
-        cores = os.cpu_count() or 1
+        pass
+    return info
+
+
+def _head0_inputs(w, arrays, rcp_params):
+    """Head 0 of the workload as the oracle takes it (fp32 values of the bf16
+    inputs), with its partition: the given labels, or the oracle's own
+    response-coupled partition."""
+    import numpy as np
+    import oracle
     h = 0
     if w.dtype == "bf16":
         f32 = lambda a: (a.astype(np.uint32) << 16).view(np.float32)
@@ -91,7 +127,6 @@ def cpu_baseline(w, arrays, budget_seconds=20.0, rcp_params=None, estimator="ful
         f32 = lambda a: a
     q, k, v = f32(arrays["q"][h]), f32(arrays["k"][h]), f32(arrays["v"][h])
     lq, lk = arrays["labels_q"][h], arrays["labels_kv"][h]
-    t0 = time.time()
     feats = None
     if rcp_params is not None:
         import synthgen as sg
@@ -99,32 +134,88 @@ def cpu_baseline(w, arrays, budget_seconds=20.0, rcp_params=None, estimator="ful
         part = oracle.rcp.rcp_partition(q, k, rcp_params["m_s"], rcp_params["r_k"], w.c_k,
                                         rcp_params["r_q"], w.c_q, ik, iq, rcp_params["iters"])
         lq, lk, feats = part["labels_q"], part["labels_kv"], part["phi_q"]
+    return q, k, v, lq, lk, feats
+
+
+def cpu_baseline(w, arrays, budget_seconds=10.0, rcp_params=None, estimator="full",
+                 route_rule="global"):
+    """The oracle, as it is, on the host cores, extrapolated from head 0:
+    routing, probes and fit of head 0 in full (fp64), then the sparse
+    attention + correction on whole query groups (largest first) until
+    ~budget_seconds, once in the oracle's fp32 arithmetic mode (`value`) and
+    once in fp64 (`value_fp64`, half the budget); each scaled to all rows and
+    all heads of the call (ms per call)."""
+    import numpy as np
+    import oracle
+    info = host_info()
+    t0 = time.time()
+    q, k, v, lq, lk, feats = _head0_inputs(w, arrays, rcp_params)
     r = oracle.run_head(q, k, v, lq, lk, w.c_q, w.c_k, w.rho, m=w.m, rank=w.r, lam=w.lam,
                         features=feats, query_rows=np.zeros(0, np.int64), estimator=estimator,
                         route_rule=route_rule)
     t_fixed = time.time() - t0
-    # sparse attention + correction on whole query groups, largest first
     sizes = np.diff(r["offsets_q"])
-    rows_done, t_rows = 0, 0.0
-    for a in np.argsort(-sizes, kind="stable"):
-        if t_rows > budget_seconds or sizes[a] == 0:
-            break
-        rows = r["perm_q"][r["offsets_q"][a]:r["offsets_q"][a + 1]]
-        t1 = time.time()
-        o, _ = oracle.sparse_attention_rows(q[rows], lq[rows], k, v, lk, r["z"], r["scale"])
-        if estimator == "full":
-            oracle.apply_correction(o, r["fit"])
-        else:
-            oracle.apply_estimator(o, r["fit"])
-        t_rows += time.time() - t1
-        rows_done += rows.size
-    per_head = t_fixed + t_rows * (w.n / max(rows_done, 1))
-    ms_call = per_head * w.heads * 1e3
-    return {"value": ms_call, "unit": "ms/call", "cores": int(cores), "kind": "oracle",
-            "sample": (f"head 0: {'partition/' if rcp_params else ''}routing/probes/fit in full "
-                       f"({t_fixed:.1f} s), sparse attention "
-                       f"+ correction on {rows_done} of {w.n} query rows ({t_rows:.1f} s); "
-                       f"scaled to {w.heads} heads x {w.n} rows, fp64 numpy")}
+
+    def rows_timed(dtype, budget):
+        rows_done, t_rows = 0, 0.0
+        for a in np.argsort(-sizes, kind="stable"):
+            if t_rows > budget or sizes[a] == 0:
+                break
+            rows = r["perm_q"][r["offsets_q"][a]:r["offsets_q"][a + 1]]
+            t1 = time.time()
+            o, _ = oracle.sparse_attention_rows(q[rows], lq[rows], k, v, lk, r["z"], r["scale"],
+                                                dtype=dtype)
+            if estimator == "full":
+                oracle.apply_correction(o, r["fit"])
+            else:
+                oracle.apply_estimator(o, r["fit"])
+            t_rows += time.time() - t1
+            rows_done += rows.size
+        return rows_done, t_rows
+
+    n32, t32 = rows_timed(np.float32, budget_seconds)
+    n64, t64 = rows_timed(np.float64, budget_seconds / 2)
+    ms = lambda n_rows, t: (t_fixed + t * (w.n / max(n_rows, 1))) * w.heads * 1e3
+    cores = info.get("blas_threads") or info.get("usable_cpus") or os.cpu_count() or 1
+    return {"value": ms(n32, t32), "unit": "ms/call", "cores": int(cores), "kind": "oracle",
+            "value_fp64": ms(n64, t64),
+            "sample": (f"extrapolated from head 0 of {w.heads}: "
+                       f"{'partition/' if rcp_params else ''}routing/probes/fit in full (fp64, "
+                       f"{t_fixed:.1f} s); sparse attention + correction on whole query groups, "
+                       f"largest first: {n32} of {w.n} rows in {t32:.1f} s in the fp32 mode "
+                       f"(value), {n64} rows in {t64:.1f} s in fp64 (value_fp64); each scaled "
+                       f"to {w.heads} heads x {w.n} rows"),
+            "host": info}
+
+
+def correction_quality(w, arrays, call, rcp_params=None, count=2048):
+    """Per-row relative error against dense attention on `count` evenly spaced
+    unprobed rows of head 0, before and after the correction (mean, p99): the
+    oracle's own hard-drop and corrected rows, and the GPU call's.  Information
+    only (the synthetic inputs are not the pages' activations)."""
+    import numpy as np
+    import oracle
+    q, k, v, lq, lk, feats = _head0_inputs(w, arrays, rcp_params)
+    rep = oracle.correction_report(q, k, v, lq, lk, w.c_q, w.c_k, w.rho, m=w.m, rank=w.r,
+                                   lam=w.lam, count=count, features=feats)
+    rows = rep["rows"]
+    out = {"head": 0, "rows": int(rows.size), "rho_exec": round(rep["rho_exec"], 6),
+           "oracle": {"before": rep["before"], "after": rep["after"]}}
+    if rcp_params is None:
+        perm = call.perm_q[0].cpu().numpy()
+        inv = np.empty_like(perm)
+        inv[perm] = np.arange(perm.size)
+        o_sp = call.o_sp[0].cpu().numpy()[inv[rows]]
+        o_out = call.out[0].float().cpu().numpy()[rows]
+        out["gpu"] = {"before": oracle.row_error_stats(o_sp, rep["dense"]),
+                      "after": oracle.row_error_stats(o_out, rep["dense"]),
+                      "output_dtype": str(call.out.dtype).replace("torch.", "")}
+    for side in ("oracle", "gpu"):
+        for when in out.get(side, {}):
+            if isinstance(out[side][when], dict):
+                out[side][when] = {k2: (round(v2, 5) if isinstance(v2, float) else v2)
+                                   for k2, v2 in out[side][when].items()}
+    return out
 
 
 def main():
@@ -476,9 +567,15 @@ def main():
         out["dense_own_attn_ms"] = round(own_ms, 3)
         out["dense_own_tflops"] = round(4.0 * d * H * n * n / (own_ms * 1e-3) / 1e12, 1)
     if not args.no_cpu_baseline:
+        if args.estimator == "full" and args.route_rule == "global":
+            # the same call once more, so its outputs are this workload's
+            step(call)
+            torch.cuda.synchronize()
+            out["correction_error"] = correction_quality(w, arr, call, rcp_params=rp)
         out["cpu_baseline"] = cpu_baseline(w, arr, rcp_params=rp, estimator=args.estimator,
                                            route_rule=args.route_rule)
         out["cpu_baseline"]["value"] = round(out["cpu_baseline"]["value"], 1)
+        out["cpu_baseline"]["value_fp64"] = round(out["cpu_baseline"]["value_fp64"], 1)
     print(json.dumps(out), flush=True)
 
 

@@ -53,6 +53,9 @@ __all__ = [
     "ESTIMATORS",
     "run_head",
     "executed_density",
+    "evaluation_rows",
+    "row_error_stats",
+    "correction_report",
 ]
 
 
@@ -211,20 +214,21 @@ def _softmax_rows(logits, vals):
     return (e @ vals) / den, (mx[:, 0] + np.log(den[:, 0]))
 
 
-def sparse_attention_rows(q_rows, row_groups, k, v, kv_labels, z, scale):
+def sparse_attention_rows(q_rows, row_groups, k, v, kv_labels, z, scale, dtype=np.float64):
     """Hard-drop output for selected query rows ([paper] §3: for a query of
     group a only keys of selected groups are kept and the softmax is
     renormalised over them).  q_rows [n, d]; row_groups [n] query group ids;
-    k, v, kv_labels in any token order.  Returns (out [n, d], lse [n])."""
-    q_rows = np.asarray(q_rows, dtype=np.float64)
-    k = np.asarray(k, dtype=np.float64)
-    v = np.asarray(v, dtype=np.float64)
-    out = np.zeros((q_rows.shape[0], k.shape[1]))
-    lse = np.zeros(q_rows.shape[0])
+    k, v, kv_labels in any token order.  Returns (out [n, d], lse [n]).
+    dtype: the arithmetic type (fp64 for parity; fp32 is only a timing mode)."""
+    q_rows = np.asarray(q_rows, dtype=dtype)
+    k = np.asarray(k, dtype=dtype)
+    v = np.asarray(v, dtype=dtype)
+    out = np.zeros((q_rows.shape[0], k.shape[1]), dtype=dtype)
+    lse = np.zeros(q_rows.shape[0], dtype=dtype)
     for a in np.unique(row_groups):
         sel = np.nonzero(row_groups == a)[0]
         keys = np.nonzero(z[a][kv_labels])[0]
-        o, l = _softmax_rows((q_rows[sel] @ k[keys].T) * scale, v[keys])
+        o, l = _softmax_rows((q_rows[sel] @ k[keys].T) * dtype(scale), v[keys])
         out[sel] = o
         lse[sel] = l
     return out, lse
@@ -235,11 +239,11 @@ def sparse_attention(q, labels_q, k, v, labels_kv, z, scale):
     return sparse_attention_rows(q, np.asarray(labels_q), k, v, np.asarray(labels_kv), z, scale)
 
 
-def dense_attention_rows(q_rows, k, v, scale):
+def dense_attention_rows(q_rows, k, v, scale, dtype=np.float64):
     """softmax(q K^T * scale) V over all keys ([paper] §3 dense attention; the
     1/sqrt(d) scale is the common attention scale named in §4.1)."""
-    q_rows = np.asarray(q_rows, dtype=np.float64)
-    return _softmax_rows((q_rows @ np.asarray(k, np.float64).T) * scale, np.asarray(v, np.float64))
+    q_rows = np.asarray(q_rows, dtype=dtype)
+    return _softmax_rows((q_rows @ np.asarray(k, dtype).T) * dtype(scale), np.asarray(v, dtype))
 
 
 # ----------------------------------------------------------------------------
@@ -420,6 +424,53 @@ def apply_estimator(o_sp, est):
     """Corrected rows mu_R + o + ((o - mu_x) / s) * b."""
     o_sp = np.asarray(o_sp, np.float64)
     return o_sp + est["mu_R"] + ((o_sp - est["mu_x"]) / est["s"]) * est["b"]
+
+
+# ----------------------------------------------------------------------------
+# quality of the correction (information only)
+# ----------------------------------------------------------------------------
+
+def evaluation_rows(n_q, probes, count=2048):
+    """`count` evenly spaced rows among the unprobed query tokens (ascending
+    token order): the unprobed tokens u_0 < u_1 < ... and rows
+    u_floor(i * len(u) / count) for i < count (all of them if fewer).
+    READING: the pages' evaluation takes 2048 evenly spaced query rows and
+    scores unprobed rows only ([paper] App. D; §5 Table 2)."""
+    unprobed = np.setdiff1d(np.arange(n_q, dtype=np.int64), np.asarray(probes, np.int64))
+    if unprobed.size <= count:
+        return unprobed
+    return unprobed[(np.arange(count, dtype=np.int64) * unprobed.size) // count]
+
+
+def row_error_stats(rows_out, rows_dense):
+    """Per-row relative L2 error ||o_i - o_i^dense|| / ||o_i^dense|| over the
+    given rows: its mean and 99th percentile (numpy's linear interpolation)."""
+    a = np.asarray(rows_out, np.float64)
+    b = np.asarray(rows_dense, np.float64)
+    e = np.linalg.norm(a - b, axis=1) / np.linalg.norm(b, axis=1)
+    return {"mean": float(e.mean()), "p99": float(np.percentile(e, 99)), "rows": int(e.size)}
+
+
+def correction_report(q, k, v, labels_q, labels_kv, c_q, c_k, rho, m=64, rank=16, lam=0.1,
+                      count=2048, **kw):
+    """The executed density and the error of the hard-drop output against
+    dense attention before and after the fitted correction, on `count`
+    evenly spaced unprobed rows ([paper] §4.3: rho_exec = rho_route + M/N_q;
+    App. D and §5 Table 2: per-row relative error of unprobed rows, mean and
+    p99; [abstract] page: the correction lowers that error).  Information
+    only: nothing is asserted on these numbers."""
+    r0 = run_head(q, k, v, labels_q, labels_kv, c_q, c_k, rho, m=m, rank=rank, lam=lam,
+                  query_rows=np.zeros(0, np.int64), **kw)
+    rows = evaluation_rows(len(labels_q), r0["probes"], count)
+    r = run_head(q, k, v, labels_q, labels_kv, c_q, c_k, rho, m=m, rank=rank, lam=lam,
+                 query_rows=rows, **kw)
+    dense, _ = dense_attention_rows(np.asarray(q, np.float64)[rows], k, v, r["scale"])
+    return {
+        "rows": rows, "dense": dense, "result": r,
+        "rho_exec": float(executed_density(r["routed_pairs"], len(labels_q), len(labels_kv), m)),
+        "before": row_error_stats(r["o_sp"], dense),
+        "after": row_error_stats(r["out"], dense),
+    }
 
 
 # ----------------------------------------------------------------------------

@@ -727,3 +727,72 @@ def test_per_group_full_budget_selects_everything():
     z, pairs, _ = oracle.route_cells_per_group(qbar, kbar, n_a, m_b, int(m_b.sum()), 5)
     assert np.array_equal(z, np.outer(n_a > 0, m_b > 0))
     assert pairs == int(n_a.sum() * m_b.sum())
+
+
+# ----------------------------------------------------------------------------
+# O-13: error of the hard-drop output before / after the correction
+# ----------------------------------------------------------------------------
+
+def test_evaluation_rows_hand_values():
+    # unprobed tokens of 10 with probes {2, 5}: 0 1 3 4 6 7 8 9; four evenly
+    # spaced ones sit at positions 0, 2, 4, 6
+    assert oracle.evaluation_rows(10, [2, 5], 4).tolist() == [0, 3, 6, 8]
+    assert oracle.evaluation_rows(10, [2, 5], 8).tolist() == [0, 1, 3, 4, 6, 7, 8, 9]
+    assert oracle.evaluation_rows(10, [2, 5], 50).tolist() == [0, 1, 3, 4, 6, 7, 8, 9]
+    rows = oracle.evaluation_rows(75600, np.arange(64) * 1000, 2048)
+    assert rows.size == 2048 and np.all(np.diff(rows) > 0)
+    assert not np.isin(rows, np.arange(64) * 1000).any()
+
+
+def test_row_error_stats_hand_values():
+    st = oracle.row_error_stats([[1.0, 0.0], [0.0, 2.0]], [[1.0, 1.0], [0.0, 1.0]])
+    # errors 1/sqrt(2) and 1
+    assert abs(st["mean"] - (2 ** -0.5 + 1.0) / 2) < 1e-15
+    assert abs(st["p99"] - (2 ** -0.5 + 0.99 * (1.0 - 2 ** -0.5))) < 1e-15
+    assert st["rows"] == 2
+
+
+def test_correction_report_full_density_is_exact():
+    # one query group, one K/V group: the single cell is kept, the hard-drop
+    # output is dense attention and the residual is 0, so both errors vanish
+    rng = np.random.default_rng(7)
+    n, d = 300, 16
+    q, k, v = (rng.standard_normal((n, d)) for _ in range(3))
+    lab = np.zeros(n, np.int64)
+    rep = oracle.correction_report(q, k, v, lab, lab, 1, 1, "1", m=16, rank=4, count=100)
+    assert rep["rows"].size == 100
+    assert rep["before"]["mean"] < 1e-13 and rep["after"]["p99"] < 1e-13
+    assert abs(rep["rho_exec"] - 1.0) < 1e-12 or rep["rho_exec"] >= 1.0
+
+
+def test_correction_report_matches_its_parts():
+    # the report's numbers are the per-row errors of the call's own outputs
+    w = sg.small_workload(heads=1, n=700, head_dim=32, components=6, kv_split=2, rho="0.3",
+                          seed=17)
+    hd = sg.make_call(w)[0]
+    rep = oracle.correction_report(hd["q"], hd["k"], hd["v"], hd["labels_q"], hd["labels_kv"],
+                                   w.c_q, w.c_k, w.rho, m=w.m, rank=w.r, lam=w.lam, count=256)
+    r = rep["result"]
+    assert not np.isin(rep["rows"], r["probes"]).any()
+    e_b = [np.linalg.norm(r["o_sp"][i] - rep["dense"][i]) / np.linalg.norm(rep["dense"][i])
+           for i in range(len(rep["rows"]))]
+    e_a = [np.linalg.norm(r["out"][i] - rep["dense"][i]) / np.linalg.norm(rep["dense"][i])
+           for i in range(len(rep["rows"]))]
+    assert abs(rep["before"]["mean"] - sum(e_b) / len(e_b)) < 1e-12
+    assert abs(rep["after"]["mean"] - sum(e_a) / len(e_a)) < 1e-12
+    assert rep["rho_exec"] == float(oracle.executed_density(r["routed_pairs"], w.n, w.n, w.m))
+
+
+def test_fp32_timing_mode_tracks_fp64():
+    # the fp32 arithmetic mode (used only to time the oracle) stays within
+    # fp32 rounding of the fp64 result
+    w = sg.small_workload(heads=1, n=600, head_dim=64, components=5, rho="0.4", seed=18)
+    hd = sg.make_call(w)[0]
+    r = oracle.run_head(hd["q"], hd["k"], hd["v"], hd["labels_q"], hd["labels_kv"], w.c_q, w.c_k,
+                        w.rho, m=w.m, rank=w.r, lam=w.lam, query_rows=np.zeros(0, np.int64))
+    o64, _ = oracle.sparse_attention_rows(hd["q"], hd["labels_q"], hd["k"], hd["v"],
+                                          hd["labels_kv"], r["z"], r["scale"])
+    o32, _ = oracle.sparse_attention_rows(hd["q"], hd["labels_q"], hd["k"], hd["v"],
+                                          hd["labels_kv"], r["z"], r["scale"], dtype=np.float32)
+    assert o32.dtype == np.float32
+    assert np.linalg.norm(o32 - o64) / np.linalg.norm(o64) < 1e-5
