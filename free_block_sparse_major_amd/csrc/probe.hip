@@ -710,61 +710,278 @@ struct FitArgs {
 };
 
 constexpr int kLd = kMaxM + 1;
+constexpr int kFitThreads = 512;   // threads of the fit kernel (8 waves, 2 per SIMD)
+typedef double f64x4_t __attribute__((ext_vector_type(4)));
+constexpr double kEps64 = 2.220446049250313e-16;
+constexpr double kTiny = 1e-290;   // pivot floor of the normalised tridiagonal matrix
 
-__global__ __launch_bounds__(256) void fit_kernel(FitArgs f) {
+// 1 / y from the hardware estimate and one Newton step (a few ulp)
+SPR_DEV double rcp64(double y) {
+  const double r = __builtin_amdgcn_rcp(y);
+  return fma(fma(-y, r, 1.0), r, r);
+}
+
+// Cross-lane moves of fp64 values with DPP (two 32-bit halves).
+template <int CTRL>
+SPR_DEV double dpp_f64(double v) {
+  const unsigned long long u = static_cast<unsigned long long>(__double_as_longlong(v));
+  const int lo = __builtin_amdgcn_update_dpp(0, int(uint32_t(u)), CTRL, 0xf, 0xf, false);
+  const int hi = __builtin_amdgcn_update_dpp(0, int(uint32_t(u >> 32)), CTRL, 0xf, 0xf, false);
+  return __longlong_as_double(
+      static_cast<long long>((static_cast<unsigned long long>(uint32_t(hi)) << 32) | uint32_t(lo)));
+}
+
+// Sum over aligned groups of GL lanes (4, 8 or 16): lane pairs meet by quad
+// permutations, then half-row and row mirrors; every lane of a group ends
+// with the same bits.
+template <int GL>
+SPR_DEV double group_sum_f64(double v) {
+  v += dpp_f64<0xB1>(v);                    // quad_perm [1,0,3,2]
+  v += dpp_f64<0x4E>(v);                    // quad_perm [2,3,0,1]
+  if constexpr (GL >= 8) v += dpp_f64<0x141>(v);   // row_half_mirror
+  if constexpr (GL >= 16) v += dpp_f64<0x140>(v);  // row_mirror
+  return v;
+}
+
+SPR_DEV double readlane_f64(double v, int l) {
+  const unsigned long long u = static_cast<unsigned long long>(__double_as_longlong(v));
+  const uint32_t lo = uint32_t(__builtin_amdgcn_readlane(int(uint32_t(u)), l));
+  const uint32_t hi = uint32_t(__builtin_amdgcn_readlane(int(uint32_t(u >> 32)), l));
+  return __longlong_as_double(static_cast<long long>((static_cast<unsigned long long>(hi) << 32) | lo));
+}
+
+// Wave-wide sum, the same value in every lane.
+SPR_DEV double wave_sum_f64(double v) {
+  v = group_sum_f64<16>(v);
+  return (readlane_f64(v, 0) + readlane_f64(v, 16)) + (readlane_f64(v, 32) + readlane_f64(v, 48));
+}
+
+// Sum over aligned groups of GL lanes, GL a power of two up to 64.
+template <int GL>
+SPR_DEV double group_sum_any(double v) {
+  if constexpr (GL <= 16) {
+    return group_sum_f64<GL>(v);
+  } else {
+    v = group_sum_f64<16>(v);
+    v += __shfl_xor(v, 16);
+    if constexpr (GL == 64) v += __shfl_xor(v, 32);
+    return v;
+  }
+}
+
+// Value of lane (lane & ~3) + q of the quad (q uniform).
+SPR_DEV double quad_bcast_f64(double v, int q) {
+  switch (q) {
+    case 0: return dpp_f64<0x00>(v);
+    case 1: return dpp_f64<0x55>(v);
+    case 2: return dpp_f64<0xAA>(v);
+    default: return dpp_f64<0xFF>(v);
+  }
+}
+
+// v[i] for a uniform runtime i, as a chain of selects on register values
+// (the empty asm keeps the compiler from turning the chain into an indexed
+// load, which would move the whole array to scratch memory)
+SPR_DEV double pick16(const double (&v)[16], int i) {
+  double r = v[0];
+#pragma unroll
+  for (int t = 1; t < 16; ++t) {
+    double x = v[t];
+    asm volatile("" : "+v"(x));
+    r = i == t ? x : r;
+  }
+  return r;
+}
+
+// U = H_0 ... H_(n-3) Z for `cap` vectors (rows c of zs): groups of GB
+// lanes per vector, lane g keeps elements g*EPL .. +EPL in registers.
+template <int GB>
+SPR_DEV void back_transform(double* zs, const double* vs, const double* tbeta, int n, int cap,
+                            int tid) {
+  constexpr int EPL = 64 / GB;
+  const int c = tid / GB, g = tid % GB;
+  if (c >= cap) return;
+  double* zc = zs + c * kLd;
+  const int i0 = g * EPL;
+  double zv[EPL];
+#pragma unroll
+  for (int t = 0; t < EPL; ++t) zv[t] = i0 + t < n ? zc[i0 + t] : 0.0;
+  for (int k = n - 3; k >= 0; --k) {
+    const double bk = tbeta[k];
+    if (bk == 0.0) continue;   // uniform: tbeta is shared
+    const double* vk = vs + k * kLd;
+    double vv[EPL];
+    double dot = 0.0;
+#pragma unroll
+    for (int t = 0; t < EPL; ++t) {
+      const int i = i0 + t;
+      vv[t] = i > k && i < n ? vk[i] : 0.0;
+      dot = fma(vv[t], zv[t], dot);
+    }
+    dot = group_sum_any<GB>(dot);
+    const double tt = bk * dot;
+#pragma unroll
+    for (int t = 0; t < EPL; ++t) zv[t] = fma(-tt, vv[t], zv[t]);
+  }
+#pragma unroll
+  for (int t = 0; t < EPL; ++t)
+    if (i0 + t < n) zc[i0 + t] = zv[t];
+}
+
+// Sturm counts of the normalised tridiagonal matrix at two points (two
+// independent recurrences interleaved): eigenvalues below x1 and below x2.
+// st[i] = (d_(i+1), e_i^2), i < n - 1.
+SPR_DEV void sturm_count2(double d0, const double2* st, int n, double x1, double x2, int& c1,
+                          int& c2) {
+  double q1 = d0 - x1, q2 = d0 - x2;
+  int n1 = 0, n2 = 0;
+  auto step = [&](double2 s) {
+    if (fabs(q1) < kTiny) q1 = -kTiny;
+    if (fabs(q2) < kTiny) q2 = -kTiny;
+    n1 += q1 < 0.0 ? 1 : 0;
+    n2 += q2 < 0.0 ? 1 : 0;
+    q1 = (s.x - x1) - s.y * rcp64(q1);
+    q2 = (s.x - x2) - s.y * rcp64(q2);
+  };
+  int i = 0;
+  for (; i + 4 <= n - 1; i += 4) {
+    const double2 s0 = st[i], s1 = st[i + 1], s2 = st[i + 2], s3 = st[i + 3];
+    step(s0);
+    step(s1);
+    step(s2);
+    step(s3);
+  }
+  for (; i < n - 1; ++i) step(st[i]);
+  if (fabs(q1) < kTiny) q1 = -kTiny;
+  if (fabs(q2) < kTiny) q2 = -kTiny;
+  c1 = n1 + (q1 < 0.0 ? 1 : 0);
+  c2 = n2 + (q2 < 0.0 ? 1 : 0);
+}
+
+__global__ __launch_bounds__(kFitThreads) void fit_kernel(FitArgs f) {
   const int h = blockIdx.x, tid = threadIdx.x;
   const int me = f.me, d = f.d;
-  __shared__ double w[kMaxM], wt[kMaxM];
-  __shared__ double mux[128], mur[128], sc[128];
-  __shared__ double G[kMaxM * kLd];   // Cholesky factor (lower)
-  __shared__ double E[kMaxM * kLd];   // Rw Rw^T, diagonalised in place
-  __shared__ double U[kMaxM * kLd];   // eigenvectors (columns)
-  __shared__ double xs[kMaxM][33], rs2[kMaxM][33];   // column chunk staging
-  __shared__ int32_t order[kMaxM];
-  __shared__ double red[4];
+  const int lane = tid & 63, wid = tid >> 6;
+  __shared__ double w[kMaxM], sqw[kMaxM];
+  __shared__ double mux[128], mur[128], sc[128], isc[128];
+  __shared__ double part[2][256];
+  // pool: X and R staged (phases 1-4), then G / G^-1, E / Householder
+  // vectors, eigenvector rows Zs, scratch rows Ws
+  __shared__ __align__(16) double pool[4 * kMaxM * kLd];
+  double* G = pool;
+  double* E = pool + kMaxM * kLd;
+  double* Zs = pool + 2 * kMaxM * kLd;
+  double* Ws = pool + 3 * kMaxM * kLd;
+  __shared__ double gjrow[2][2][kMaxM];   // Gauss-Jordan pivot row (A part, B part), by parity
+  __shared__ double colE[2][kMaxM], pbuf[2][kMaxM];
+  __shared__ double td[kMaxM], te[kMaxM], tbeta[kMaxM];      // T and the reflectors
+  __shared__ double tdn[kMaxM], ten[kMaxM];                   // normalised T
+  __shared__ double2 st2[kMaxM];                              // (d_(i+1), e_i^2), normalised
+  __shared__ double lamn[kMaxM], tbuf[kMaxM];
+  __shared__ double red[kFitThreads / 64];
   __shared__ double tcol[kMaxM];
+  __shared__ double sh_sw;
   __shared__ int32_t sh_k;
-  __shared__ int32_t sh_rot[2], sh_big[2];   // per sweep parity
 
   const double* X = f.xp + (long long)h * f.m * d;
   const double* R = f.rp + (long long)h * f.m * d;
   double* Xw = f.xw + (long long)h * f.m * d;
   double* Rw = f.rw + (long long)h * f.m * d;
+  const int ldx = d + 1;            // padded row stride of the staged X and R
+  double* Xs = pool;                // me x ldx
+  double* Rs = pool + 2 * kMaxM * kLd;
 
-  // 1. coverage weights |G_a| / m_a
+  // 1. coverage weights |G_a| / m_a and their sum; X and R staged in LDS
   const int32_t* oq = f.off_q + (long long)h * (f.c_q + 1);
   if (tid < me) {
     const int a = f.probe_group[(long long)h * f.m + tid];
     w[tid] = double(oq[a + 1] - oq[a]) / double(f.m_a[(long long)h * f.c_q + a]);
   }
-  __syncthreads();
-  double sw = 0.0;
-  for (int p = 0; p < me; ++p) sw += w[p];
-  if (tid < me) wt[tid] = double(me) * w[tid] / sw;
-  // 2. weighted means and feature scale (unit-sum weights)
-  if (tid < d) {
-    double mx = 0, mr = 0;
-    for (int p = 0; p < me; ++p) {
-      const double wh = w[p] / sw;
-      mx += wh * X[p * d + tid];
-      mr += wh * R[p * d + tid];
+  {
+    // 16-byte loads, all in flight before the first store (me * d / 2 <= 4096)
+    const int n2 = me * d / 2;
+    constexpr int NL = 4096 / kFitThreads;
+    double2 xv[NL], rv[NL];
+#pragma unroll
+    for (int t = 0; t < NL; ++t) {
+      const int e = tid + kFitThreads * t;
+      xv[t] = e < n2 ? reinterpret_cast<const double2*>(X)[e] : double2{0.0, 0.0};
+      rv[t] = e < n2 ? reinterpret_cast<const double2*>(R)[e] : double2{0.0, 0.0};
     }
-    double var = 0;
-    for (int p = 0; p < me; ++p) {
-      const double t = X[p * d + tid] - mx;
-      var += (w[p] / sw) * t * t;
+#pragma unroll
+    for (int t = 0; t < NL; ++t) {
+      const int e = tid + kFitThreads * t;
+      if (e < n2) {
+        const int p = (2 * e) / d, j = 2 * e - p * d;
+        Xs[p * ldx + j] = xv[t].x;
+        Xs[p * ldx + j + 1] = xv[t].y;
+        Rs[p * ldx + j] = rv[t].x;
+        Rs[p * ldx + j + 1] = rv[t].y;
+      }
+    }
+  }
+  __syncthreads();
+  if (wid == 0) {
+    const double sw = wave_sum_f64(lane < me ? w[lane] : 0.0);
+    if (lane == 0) sh_sw = sw;
+  }
+  __syncthreads();
+  const double sw = sh_sw;
+  if (tid < me) sqw[tid] = sqrt(double(me) * w[tid] / sw);   // sqrt of the unit-mean weight
+  // 2. weighted means and feature scale (unit-sum weights): column j = tid % d,
+  // the NP = 256 / d threads of a column take rows p = tid / d (+ NP)
+  const int NP = 256 / d, jc = tid % d, pp0 = tid / d;
+  if (tid < 256) {
+    double mx = 0.0, mr = 0.0;
+    for (int p = pp0; p < me; p += NP) {
+      const double wh = w[p] / sw;
+      mx = fma(wh, Xs[p * ldx + jc], mx);
+      mr = fma(wh, Rs[p * ldx + jc], mr);
+    }
+    part[0][tid] = mx;
+    part[1][tid] = mr;
+  }
+  __syncthreads();
+  if (tid < d) {
+    double mx = 0.0, mr = 0.0;
+    for (int i = 0; i < NP; ++i) {
+      mx += part[0][tid + i * d];
+      mr += part[1][tid + i * d];
     }
     mux[tid] = mx;
     mur[tid] = mr;
-    sc[tid] = sqrt(var + 1e-6);
   }
   __syncthreads();
-  // 3. weighted, standardised features and centred residuals
-  for (int e = tid; e < me * d; e += 256) {
-    const int p = e / d, j = e % d;
-    const double sq = sqrt(wt[p]);
-    Xw[e] = sq * (X[e] - mux[j]) / sc[j];
-    Rw[e] = sq * (R[e] - mur[j]);
+  if (tid < 256) {
+    const double mx = mux[jc];
+    double var = 0.0;
+    for (int p = pp0; p < me; p += NP) {
+      const double t = Xs[p * ldx + jc] - mx;
+      var = fma(w[p] / sw * t, t, var);
+    }
+    part[0][tid] = var;
+  }
+  __syncthreads();
+  if (tid < d) {
+    double var = 0.0;
+    for (int i = 0; i < NP; ++i) var += part[0][tid + i * d];
+    sc[tid] = sqrt(var + 1e-6);
+    isc[tid] = 1.0 / sc[tid];
+  }
+  __syncthreads();
+  // 3. weighted, standardised features and centred residuals, in place in
+  // LDS (rows past me are zero) and to global memory for the last step
+  for (int e = tid; e < kMaxM * d; e += kFitThreads) {
+    const int p = e / d, j = e - p * d;
+    double xv = 0.0, rv = 0.0;
+    if (p < me) {
+      xv = sqw[p] * (Xs[p * ldx + j] - mux[j]) * isc[j];
+      rv = sqw[p] * (Rs[p * ldx + j] - mur[j]);
+      Xw[p * d + j] = xv;
+      Rw[p * d + j] = rv;
+    }
+    Xs[p * ldx + j] = xv;
+    Rs[p * ldx + j] = rv;
   }
   __syncthreads();
   float* ocg = f.corr_g ? f.corr_g + (long long)h * d : nullptr;
@@ -776,7 +993,7 @@ __global__ __launch_bounds__(256) void fit_kernel(FitArgs f) {
     double sxr = 0.0, sxx = 0.0;
     if (tid < d)
       for (int p = 0; p < me; ++p) {
-        const double xv = Xw[p * d + tid], rv = Rw[p * d + tid];
+        const double xv = Xs[p * ldx + tid], rv = Rs[p * ldx + tid];
         sxr = fma(xv, rv, sxr);
         sxx = fma(xv, xv, sxx);
       }
@@ -790,7 +1007,7 @@ __global__ __launch_bounds__(256) void fit_kernel(FitArgs f) {
       if (ocg) ocg[tid] = float(g);
       f.corr_c[(long long)h * d + tid] = float(mur[tid] - mux[tid] * g);
     }
-    for (int e = tid; e < d * f.rank; e += 256) {
+    for (int e = tid; e < d * f.rank; e += kFitThreads) {
       f.corr_a[(long long)h * d * f.rank + e] = 0.f;
       f.corr_psi_t[(long long)h * f.rank * d + e] = 0.f;
     }
@@ -798,212 +1015,471 @@ __global__ __launch_bounds__(256) void fit_kernel(FitArgs f) {
   }
   if (ocg)
     for (int j = tid; j < d; j += 256) ocg[j] = 0.f;
-  // 4. Gram matrices G = Xw Xw^T + lam I and E = Rw Rw^T, 32 columns of the
-  // weighted features / residuals staged in LDS at a time
-  for (int e = tid; e < me * me; e += 256) {
-    const int pp = e / me, qq = e - (e / me) * me;
-    G[pp * kLd + qq] = pp == qq ? f.lambda : 0.0;
-    E[pp * kLd + qq] = 0.0;
-    U[pp * kLd + qq] = pp == qq ? 1.0 : 0.0;
-  }
-  for (int d0 = 0; d0 < d; d0 += 32) {
-    __syncthreads();
-    for (int e = tid; e < me * 32; e += 256) {
-      const int pp = e >> 5, jj = e & 31;
-      xs[pp][jj] = Xw[pp * d + d0 + jj];
-      rs2[pp][jj] = Rw[pp * d + d0 + jj];
-    }
-    __syncthreads();
-    for (int e = tid; e < me * me; e += 256) {
-      const int pp = e / me, qq = e - (e / me) * me;
-      double gx = 0.0, gr = 0.0;
-#pragma unroll 8
-      for (int jj = 0; jj < 32; ++jj) {
-        gx = fma(xs[pp][jj], xs[qq][jj], gx);
-        gr = fma(rs2[pp][jj], rs2[qq][jj], gr);
-      }
-      G[pp * kLd + qq] += gx;
-      E[pp * kLd + qq] += gr;
-    }
-  }
-  __syncthreads();
-  // 5. Cholesky G = L L^T (right-looking, lower triangle); thread t updates
-  // rows i = k+1+t/4 (+64) and columns j = k+1+t%4 (+4)
-  for (int k = 0; k < me; ++k) {
-    const double piv = sqrt(G[k * kLd + k]);
-    __syncthreads();
-    for (int i = k + 1 + tid; i < me; i += 256) G[i * kLd + k] /= piv;
-    if (tid == 0) G[k * kLd + k] = piv;
-    __syncthreads();
-    for (int i = k + 1 + (tid >> 2); i < me; i += 64) {
-      const double lik = G[i * kLd + k];
-      for (int j = k + 1 + (tid & 3); j <= i; j += 4) G[i * kLd + j] -= lik * G[j * kLd + k];
-    }
-  }
-  __syncthreads();
-  // 6. cyclic Jacobi on E with round-robin disjoint pairs (thread t works on
-  // pair t/8, columns t%8 + 8l; the eight threads of a pair, one wave's
-  // lanes, each compute the pair's rotation from E, so no broadcast and no
-  // barrier separate it from the row pass: a wave's LDS accesses run in
-  // order, and other pairs touch other rows).  A rotation
-  // is skipped when |a_pq| is negligible next to the diagonal and next to the
-  // trace (the Gram route resolves eigenvalues to ~1e-16 of the trace).  The
-  // iteration stops after a sweep without rotations, or after a sweep in
-  // which every rotation had |a_pq| below 1e-8 sqrt(a_pp a_qq) or below
-  // 1e-10 of the trace: convergence is quadratic, so what the next sweep
-  // would rotate is at the rounding level of the trace.  Rotation parameters use the hardware reciprocal / reciprocal
-  // square root refined by two Newton steps (about an ulp; c^2 + s^2 = 1 to
-  // rounding).
+  // 4. Gram matrices G = Xw Xw^T + lam I and E = Rw Rw^T on fp64 MFMA
+  // (v_mfma_f64_16x16x4: operand lane l holds row l % 16 at k = l / 16;
+  // result lane l holds column l % 16 of rows l / 16 + 4 i): wave w forms
+  // rows 16 w .. 16 w + 15 of both.
   {
-    auto rcp64 = [](double y) {
-      double r = __builtin_amdgcn_rcp(y);
-      r = r * fma(-y, r, 2.0);
-      r = r * fma(-y, r, 2.0);
-      return r;
-    };
-    auto rsq64 = [](double y) {
-      double r = __builtin_amdgcn_rsq(y);
-      r = r * fma(-0.5 * y * r, r, 1.5);
-      r = r * fma(-0.5 * y * r, r, 1.5);
-      return r;
-    };
-    double trp = 0.0;
-    for (int i = tid; i < me; i += 256) trp += fabs(E[i * kLd + i]);
-    const double tr = block_sum(trp, red);
-    const double abs_floor = 1e-300 + 1e-14 * tr;
-    const int mp = (me + 1) & ~1;   // even player count; player me is a dummy if me is odd
-    const int npair = mp / 2;
-    const int pi = tid >> 3, cj = tid & 7;
-    if (tid == 0) {
-      sh_rot[0] = 0;
-      sh_big[0] = 0;
+    const int r16 = lane & 15, kq = lane >> 4;
+    const int gw = wid & 3;   // only waves 0..3 form products
+    f64x4_t gacc[4], eacc[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) gacc[t] = eacc[t] = f64x4_t{0.0, 0.0, 0.0, 0.0};
+    for (int kk = 0; wid < 4 && kk < d; kk += 4) {
+      const double ax = Xs[(16 * gw + r16) * ldx + kk + kq];
+      const double ar = Rs[(16 * gw + r16) * ldx + kk + kq];
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const double bx = Xs[(16 * t + r16) * ldx + kk + kq];
+        const double br = Rs[(16 * t + r16) * ldx + kk + kq];
+        gacc[t] = __builtin_amdgcn_mfma_f64_16x16x4f64(ax, bx, gacc[t], 0, 0, 0);
+        eacc[t] = __builtin_amdgcn_mfma_f64_16x16x4f64(ar, br, eacc[t], 0, 0, 0);
+      }
+    }
+    __syncthreads();   // X and R are no longer read; G and E overwrite them
+    if (wid < 4) {
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int row = 16 * gw + kq + 4 * i, col = 16 * t + r16;
+          G[row * kLd + col] = gacc[t][i] + (row == col ? f.lambda : 0.0);
+          E[row * kLd + col] = eacc[t][i];
+        }
+    }
+  }
+  __syncthreads();
+  // 5. One pass over k = 0 .. n-1 with two barriers per step does both
+  //   a. Gauss-Jordan elimination of [G | I] (G is symmetric positive
+  //      definite, so no pivoting; rows keep their scale, so the left half
+  //      ends diagonal): afterwards row i of G^-1 is row i of the right half
+  //      over the final a_ii;
+  //   b. Householder reduction of E to tridiagonal form T = Q^T E Q: step k
+  //      maps column k below the diagonal onto alpha e_1 with
+  //      H = I - beta v v^T (v kept in row k of E; d, e in td, te).
+  // Thread t keeps row t / RT, columns CW (t % RT) .. + CW - 1 of both
+  // matrices in registers (RT = threads per row, CW = 64 / RT columns each):
+  // the threads of a row are adjacent lanes of one DPP row.
+  constexpr int RT = kFitThreads / 64, CW = 64 / RT;
+  const int n = me;
+  const int rr = tid / RT, qq = tid % RT, c0 = CW * qq;
+  double ga[CW], gb[CW], er[CW];
+#pragma unroll
+  for (int i = 0; i < CW; ++i) {
+    const int j = c0 + i;
+    const bool in = rr < n && j < n;
+    ga[i] = in ? G[rr * kLd + j] : 0.0;
+    gb[i] = in && rr == j ? 1.0 : 0.0;
+    er[i] = in ? E[rr * kLd + j] : 0.0;
+  }
+  __syncthreads();   // E is reused for the Householder vectors below
+  // step k = CW kb + KI: the register index KI is a compile-time constant
+  auto elim_step = [&](auto ki_c, int kb) __attribute__((always_inline)) {
+    constexpr int KI = decltype(ki_c)::value;
+    const int k = CW * kb + KI;
+    const int par = KI & 1;
+    // publish: Gauss-Jordan pivot row k, column k of E
+    if (rr == k) {
+#pragma unroll
+      for (int i = 0; i < CW; i += 2) {
+        reinterpret_cast<double2*>(&gjrow[par][0][c0 + i])[0] = double2{ga[i], ga[i + 1]};
+        reinterpret_cast<double2*>(&gjrow[par][1][c0 + i])[0] = double2{gb[i], gb[i + 1]};
+      }
+    }
+    if (qq == kb && rr < n) colE[par][rr] = er[KI];
+    __syncthreads();
+    // a. rows i != k: row_i -= (a_ik / a_kk) row_k
+    {
+      const double aik = __shfl(ga[KI], (lane & ~(RT - 1)) | kb);
+      const double fct = rr == k ? 0.0 : aik * rcp64(gjrow[par][0][k]);
+#pragma unroll
+      for (int i = 0; i < CW; i += 2) {
+        const double2 ka = reinterpret_cast<const double2*>(&gjrow[par][0][c0 + i])[0];
+        const double2 kbv = reinterpret_cast<const double2*>(&gjrow[par][1][c0 + i])[0];
+        ga[i] = fma(-fct, ka.x, ga[i]);
+        ga[i + 1] = fma(-fct, ka.y, ga[i + 1]);
+        gb[i] = fma(-fct, kbv.x, gb[i]);
+        gb[i + 1] = fma(-fct, kbv.y, gb[i + 1]);
+      }
+    }
+    // b. Householder step k (k + 2 < n): x = E[k+1.., k]
+    const int m = n - k - 1;
+    const bool hh = k + 2 < n;
+    double alpha = 0.0, beta = 0.0;
+    double vj[CW];
+    if (hh) {
+      double xraw = colE[par][(k + 1 + lane) & (kMaxM - 1)];
+      asm volatile("" : "+v"(xraw));
+      const double xl = lane < m ? xraw : 0.0;
+      const double x0 = colE[par][k + 1];
+      const double nx2 = wave_sum_f64(xl * xl);
+      if (nx2 > 0.0) {
+        const double nx = sqrt(nx2);
+        alpha = x0 > 0.0 ? -nx : nx;
+        beta = rcp64(nx2 - alpha * x0);   // 2 / |v|^2, |v|^2 = 2 (|x|^2 - alpha x0)
+      }
+      if (wid == 0) {
+        // v = x - alpha e_1, stored in row k of E (entries k+1 ..)
+        if (lane < m) E[k * kLd + k + 1 + lane] = lane == 0 ? xl - alpha : xl;
+        if (lane == 0) {
+          td[k] = colE[par][k];
+          te[k] = alpha;
+          tbeta[k] = beta;
+        }
+      }
+      // v at this thread's columns (0 outside k+1 .. n-1)
+      double cv[CW];
+#pragma unroll
+      for (int i = 0; i < CW; i += 2) {
+        const double2 c2 = reinterpret_cast<const double2*>(&colE[par][c0 + i])[0];
+        cv[i] = c2.x;
+        cv[i + 1] = c2.y;
+      }
+#pragma unroll
+      for (int i = 0; i < CW; ++i) {
+        const int j = c0 + i;
+        vj[i] = j > k && j < n ? (j == k + 1 ? cv[i] - alpha : cv[i]) : 0.0;
+      }
+      if (beta != 0.0) {
+        // p_r = beta sum_j E[r][j] v_j over j > k, RT threads per row
+        double s2 = 0.0;
+#pragma unroll
+        for (int i = 0; i < CW; ++i) s2 = fma(er[i], vj[i], s2);
+        s2 = group_sum_f64<RT>(s2);
+        if (qq == 0 && rr > k && rr < n) pbuf[par][rr] = beta * s2;
+      }
     }
     __syncthreads();
-    for (int sweep = 0; sweep < 20; ++sweep) {
-      // flags of sweep s live in slot s & 1.  Slot par ^ 1 (read by every
-      // thread at the end of the previous sweep) is cleared for the next
-      // sweep only after this sweep's first barrier, which every thread
-      // reaches after that read
-      const int par = sweep & 1;
-      for (int rnd = 0; rnd < mp - 1; ++rnd) {
-        int p2 = 0, q2 = 0;
-        double ci = 1.0, si = 0.0;
-        if (pi < npair) {
-          int pp, qq;
-          if (pi == 0) { pp = mp - 1; qq = rnd; }
-          else {
-            pp = rnd + pi; pp -= pp >= mp - 1 ? mp - 1 : 0;
-            qq = rnd - pi; qq += qq < 0 ? mp - 1 : 0;
-          }
-          if (pp < me && qq < me) {
-            const double apq = E[pp * kLd + qq];
-            const double app = E[pp * kLd + pp], aqq = E[qq * kLd + qq];
-            const double apq2 = apq * apq, dd = fabs(app * aqq);
-            if (apq2 > 1e-30 * dd && fabs(apq) > abs_floor) {
-              const double tau = (aqq - app) * rcp64(2.0 * apq);
-              const double u = fma(tau, tau, 1.0);
-              const double t = (tau >= 0 ? 1.0 : -1.0) * rcp64(fabs(tau) + u * rsq64(u));
-              ci = rsq64(fma(t, t, 1.0));
-              si = t * ci;
-              p2 = pp;
-              q2 = qq;
-              if (cj == 0) {
-                sh_rot[par] = 1;
-                if (apq2 > 1e-16 * dd && fabs(apq) > 1e-10 * tr) sh_big[par] = 1;
-              }
-            }
-          }
+    if (hh && beta != 0.0) {
+      // w = p - (beta/2)(p.v) v;  E22 <- E22 - v w^T - w v^T
+      const int li = (k + 1 + lane) & (kMaxM - 1);
+      double craw = colE[par][li], praw = pbuf[par][li];
+      asm volatile("" : "+v"(craw), "+v"(praw));
+      const double vl = lane < m ? (lane == 0 ? craw - alpha : craw) : 0.0;
+      const double pl = lane < m ? praw : 0.0;
+      const double K = 0.5 * beta * wave_sum_f64(pl * vl);
+      if (rr > k && rr < n) {
+        const double vr = rr == k + 1 ? colE[par][rr] - alpha : colE[par][rr];
+        const double wr = pbuf[par][rr] - K * vr;
+        double pj[CW];
+#pragma unroll
+        for (int i = 0; i < CW; i += 2) {
+          const double2 p2 = reinterpret_cast<const double2*>(&pbuf[par][c0 + i])[0];
+          pj[i] = p2.x;
+          pj[i + 1] = p2.y;
         }
-        const bool act = si != 0.0;
-        if (act)   // rows: E <- J^T E
-          for (int j = cj; j < me; j += 8) {
-            const double x1 = E[p2 * kLd + j], x2 = E[q2 * kLd + j];
-            E[p2 * kLd + j] = ci * x1 - si * x2;
-            E[q2 * kLd + j] = si * x1 + ci * x2;
-          }
-        __syncthreads();
-        if (rnd == 0 && tid == 0) {
-          sh_rot[par ^ 1] = 0;
-          sh_big[par ^ 1] = 0;
+#pragma unroll
+        for (int i = 0; i < CW; ++i) {
+          const int j = c0 + i;
+          const double wj = j > k && j < n ? pj[i] - K * vj[i] : 0.0;
+          er[i] -= fma(vr, wj, wr * vj[i]);
         }
-        if (act)   // columns: E <- E J, U <- U J
-          for (int j = cj; j < me; j += 8) {
-            const double x1 = E[j * kLd + p2], x2 = E[j * kLd + q2];
-            E[j * kLd + p2] = ci * x1 - si * x2;
-            E[j * kLd + q2] = si * x1 + ci * x2;
-            const double u1 = U[j * kLd + p2], u2 = U[j * kLd + q2];
-            U[j * kLd + p2] = ci * u1 - si * u2;
-            U[j * kLd + q2] = si * u1 + ci * u2;
-          }
-        __syncthreads();
       }
-      if (!sh_rot[par] || !sh_big[par]) break;
     }
+  };
+  static_assert(CW == 8, "the unrolled steps below assume 8 columns per thread");
+  for (int kb = 0; kb * CW < n; ++kb) {
+    const int kn = n - CW * kb;   // steps left in this block (uniform)
+    elim_step(std::integral_constant<int, 0>{}, kb);
+    if (kn > 1) elim_step(std::integral_constant<int, 1>{}, kb);
+    if (kn > 2) elim_step(std::integral_constant<int, 2>{}, kb);
+    if (kn > 3) elim_step(std::integral_constant<int, 3>{}, kb);
+    if (kn > 4) elim_step(std::integral_constant<int, 4>{}, kb);
+    if (kn > 5) elim_step(std::integral_constant<int, 5>{}, kb);
+    if (kn > 6) elim_step(std::integral_constant<int, 6>{}, kb);
+    if (kn > 7) elim_step(std::integral_constant<int, 7>{}, kb);
   }
-  __syncthreads();
-  // 7. order eigenvalues (descending, ties by index), decide kept directions
-  if (tid < me) {
-    const double li = E[tid * kLd + tid];
-    int r = 0;
-    for (int j = 0; j < me; ++j) {
-      const double lj = E[j * kLd + j];
-      if (lj > li || (lj == li && j < tid)) ++r;
-    }
-    order[r] = tid;
+  // the final a_rr sits in column rr: lane (rr, rr / CW), register rr % CW
+  {
+    double arr = 0.0;
+#pragma unroll
+    for (int i = 0; i < CW; ++i) arr = c0 + i == rr ? ga[i] : arr;
+    arr = group_sum_f64<RT>(arr);   // the row's threads: one holds a_rr, the rest 0
+    const double ia = rr < n ? 1.0 / arr : 0.0;
+#pragma unroll
+    for (int i = 0; i < CW; ++i) gb[i] *= ia;
   }
-  __syncthreads();
+  // G^-1 to LDS (rows of the right half); the last 2 x 2 block of T
+#pragma unroll
+  for (int i = 0; i < CW; ++i) {
+    const int j = c0 + i;
+    if (rr < n && j < n) G[rr * kLd + j] = gb[i];
+    if (n >= 2 && rr == n - 2 && j == n - 2) td[n - 2] = er[i];
+    if (n >= 2 && rr == n - 1 && j == n - 2) te[n - 2] = er[i];
+    if (rr == n - 1 && j == n - 1) td[n - 1] = er[i];
+  }
   if (tid == 0) {
-    const double l1 = E[order[0] * kLd + order[0]];
+    te[n - 1] = 0.0;
+    if (n >= 2) tbeta[n - 2] = 0.0;
+    tbeta[n - 1] = 0.0;
+  }
+  __syncthreads();
+  // 6. Leading eigenpairs of T (and so of E):
+  //   a. the `cap` largest eigenvalues by multisection of Sturm counts: the
+  //      lanes of one wave share a target and test points of its interval;
+  //   b. each eigenvector of T from the twisted factorisation of T - lambda I
+  //      (forward and backward pivots; the twist where |gamma| is smallest);
+  //   c. the vectors are checked for orthogonality; a set that is not (close
+  //      eigenvalues) is re-orthogonalised, and a vector lost that way is
+  //      recomputed by inverse iteration orthogonal to the earlier ones;
+  //   d. back-transformation U = H_0 H_1 ... H_(n-3) Z.
+  int cap = f.rank < n ? f.rank : n;
+  cap = cap < d ? cap : d;
+  // Gershgorin bounds of T; T is normalised by tn = max |bound|
+  double glo = __builtin_huge_val(), ghi = -__builtin_huge_val();
+  if (tid < n) {
+    const double rad = (tid > 0 ? fabs(te[tid - 1]) : 0.0) + (tid + 1 < n ? fabs(te[tid]) : 0.0);
+    glo = td[tid] - rad;
+    ghi = td[tid] + rad;
+  }
+  glo = block_min(glo, red);
+  ghi = block_max(ghi, red);
+  const double tn = fmax(fabs(glo), fabs(ghi));
+  if (tn > 0.0) {
+    if (tid < kMaxM) lamn[tid] = 0.0;
+    if (tid < n) {
+      const double inv = 1.0 / tn;
+      tdn[tid] = td[tid] * inv;
+      const double en = te[tid] * inv;
+      ten[tid] = en;
+      if (tid + 1 < n) st2[tid] = double2{td[tid + 1] * inv, en * en};
+    }
+    __syncthreads();
+    const double lo0 = glo / tn - 4.0 * kEps64, hi0 = ghi / tn + 4.0 * kEps64;
+    int P = 64;
+    while (P > 1 && P * cap > 256) P >>= 1;   // waves 0..3: one per SIMD
+    const int j = tid / P, s = tid % P;
+    const bool act = j < cap;
+    const int target = n - 1 - j;       // ascending index of the j-th largest
+    const double d0 = tdn[0];
+    double a = lo0, b = hi0;
+    for (int round = 0; round < 40; ++round) {
+      // wave-uniform stop: every active interval at the rounding level of |T|
+      const bool done = !act || (b - a) <= 2.0 * kEps64 * fmax(fabs(a), fabs(b)) + 4.0 * kEps64;
+      if (__all(done)) break;
+      // 2 P interior points of [a, b], two per lane
+      const double x1 = a + (b - a) * (double(2 * s + 1) / double(2 * P + 1));
+      const double x2 = a + (b - a) * (double(2 * s + 2) / double(2 * P + 1));
+      int c1 = 0, c2 = 0;
+      if (act) sturm_count2(d0, st2, n, x1, x2, c1, c2);
+      // new interval: largest point with count <= target, smallest point
+      // with count > target (over the P lanes of the target)
+      double na = c2 <= target ? x2 : (c1 <= target ? x1 : a);
+      double nb = c1 > target ? x1 : (c2 > target ? x2 : b);
+      for (int o = 1; o < P; o <<= 1) {
+        na = fmax(na, __shfl_xor(na, o));
+        nb = fmin(nb, __shfl_xor(nb, o));
+      }
+      a = na;
+      b = nb;
+    }
+    if (act && s == 0) lamn[j] = 0.5 * (a + b);
+    __syncthreads();
+    // b. twisted factorisation, one thread per target: forward pivots Dp
+    // (kept in Ws), ratios e_i / Dp_i (kept in Zs); backward pivots Dm with
+    // gamma_i = Dp_i + Dm_i - (d_i - mu), ratios e_(i-1) / Dm_i (kept in Ws)
+    if (tid < cap) {
+      const int c = tid;
+      const double mu = lamn[c];
+      double* zr = Zs + c * kLd;
+      double* wr = Ws + c * kLd;
+      double dp = tdn[0] - mu;
+      wr[0] = dp;
+      for (int i = 1; i < n; ++i) {
+        const double2 s2 = st2[i - 1];            // (d_i, e_(i-1)^2)
+        const double ri = rcp64(fabs(dp) < kTiny ? -kTiny : dp);
+        zr[i - 1] = ten[i - 1] * ri;
+        dp = (s2.x - mu) - s2.y * ri;
+        wr[i] = dp;
+      }
+      double dm = tdn[n - 1] - mu;
+      double gbest = fabs(wr[n - 1]);
+      int rt = n - 1;
+      for (int i = n - 2; i >= 0; --i) {
+        const double ri = rcp64(fabs(dm) < kTiny ? -kTiny : dm);
+        const double dpi = wr[i];
+        const double ei = ten[i];
+        wr[i + 1] = ei * ri;
+        const double ai = tdn[i] - mu;
+        dm = ai - ei * ei * ri;
+        const double g = fabs(dpi + dm - ai);
+        if (g < gbest) {
+          gbest = g;
+          rt = i;
+        }
+      }
+      // z: z_rt = 1, z_i = -(e_i / Dp_i) z_(i+1) below, -(e_(i-1) / Dm_i) z_(i-1) above
+      double z = 1.0, nrm = 1.0;
+      for (int i = rt - 1; i >= 0; --i) {
+        z = -zr[i] * z;
+        zr[i] = z;
+        nrm = fma(z, z, nrm);
+      }
+      zr[rt] = 1.0;
+      z = 1.0;
+      for (int i = rt + 1; i < n; ++i) {
+        z = -wr[i] * z;
+        zr[i] = z;
+        nrm = fma(z, z, nrm);
+      }
+      const double sc_n = 1.0 / sqrt(nrm);
+      for (int i = 0; i < n; ++i) zr[i] *= sc_n;
+    }
+    __syncthreads();
+    // c. orthogonality of the computed vectors
+    double worst = 0.0;
+    for (int e = tid; e < cap * cap; e += kFitThreads) {
+      const int c1 = e / cap, c2 = e - c1 * cap;
+      if (c2 <= c1) {
+        double dot = 0.0;
+        for (int i = 0; i < n; ++i) dot = fma(Zs[c1 * kLd + i], Zs[c2 * kLd + i], dot);
+        const double dev = c2 == c1 ? fabs(dot - 1.0) : fabs(dot);
+        worst = dev == dev ? fmax(worst, dev) : 1.0;   // NaN counts as lost
+      }
+    }
+    worst = block_max(worst, red);
+    if (!(worst <= 1e-10) && wid == 0) {
+      // rare: classical Gram-Schmidt twice, in descending order; a vector
+      // that loses more than half its norm is recomputed by inverse
+      // iteration (Thomas solves of T - mu I) kept orthogonal to the earlier
+      // ones.  Lanes hold vector elements.
+      for (int c = 0; c < cap; ++c) {
+        double* zc = Zs + c * kLd;
+        double zi = lane < n ? zc[lane] : 0.0;
+        if (!(zi == zi)) zi = 0.0;
+        auto orth = [&](double v) {
+          for (int pass = 0; pass < 2; ++pass)
+            for (int c2 = 0; c2 < c; ++c2) {
+              const double u = lane < n ? Zs[c2 * kLd + lane] : 0.0;
+              v -= wave_sum_f64(u * v) * u;
+            }
+          return v;
+        };
+        zi = orth(zi);
+        double nz = sqrt(wave_sum_f64(zi * zi));
+        if (!(nz >= 0.5)) {
+          const double mu = lamn[c];
+          // deterministic start: a fixed pseudo-random vector per target
+          uint32_t hsh = uint32_t(lane * 2654435761u) ^ uint32_t((c + 1) * 40503u);
+          hsh ^= hsh >> 13;
+          hsh *= 0x5bd1e995u;
+          hsh ^= hsh >> 15;
+          zi = lane < n ? double(int32_t(hsh & 0xffff) - 32768) : 0.0;
+          for (int it = 0; it < 4; ++it) {
+            zi = orth(zi);
+            if (lane < n) Ws[lane] = zi;
+            if (lane == 0) {
+              // (T - mu I) y = b, LU without pivoting, tiny pivots raised
+              double u_prev = tdn[0] - mu;
+              if (fabs(u_prev) < kEps64) u_prev = kEps64;
+              tbuf[0] = u_prev;
+              for (int i = 1; i < n; ++i) {
+                const double l = ten[i - 1] / u_prev;
+                double u = (tdn[i] - mu) - l * ten[i - 1];
+                if (fabs(u) < kEps64) u = kEps64;
+                Ws[i] -= l * Ws[i - 1];
+                tbuf[i] = u;
+                u_prev = u;
+              }
+              Ws[n - 1] /= tbuf[n - 1];
+              for (int i = n - 2; i >= 0; --i) Ws[i] = (Ws[i] - ten[i] * Ws[i + 1]) / tbuf[i];
+            }
+            zi = lane < n ? Ws[lane] : 0.0;
+            const double nn = sqrt(wave_sum_f64(zi * zi));
+            zi = nn > 0.0 ? zi / nn : 0.0;
+          }
+          zi = orth(zi);
+          nz = sqrt(wave_sum_f64(zi * zi));
+        }
+        zi = nz > 0.0 ? zi / nz : 0.0;
+        if (lane < n) zc[lane] = zi;
+      }
+    }
+    __syncthreads();
+    // d. U = H_0 ... H_(n-3) Z
+    // GB lanes per vector with GB * cap <= kFitThreads
+    static_assert(kFitThreads == 512, "back-transformation groups assume 512 threads");
+    if (cap <= 8) back_transform<64>(Zs, E, tbeta, n, cap, tid);
+    else if (cap <= 16) back_transform<32>(Zs, E, tbeta, n, cap, tid);
+    else if (cap <= 32) back_transform<16>(Zs, E, tbeta, n, cap, tid);
+    else back_transform<8>(Zs, E, tbeta, n, cap, tid);
+  } else {
+    if (tid < kMaxM) lamn[tid] = 0.0;
+  }
+  __syncthreads();
+  // 7. kept directions: descending eigenvalues above the resolution of the
+  // Gram route (64 eps lambda_1) and with sigma > 1e-10 sigma_1
+  if (tid == 0) {
+    const double l1 = lamn[0] * tn;
     const double s1 = l1 > 0 ? sqrt(l1) : 0.0;
     int k = 0;
     if (s1 > 0) {
-      const double floor_l = 64.0 * 2.220446049250313e-16 * l1;  // resolution of the Gram route
-      for (int i = 0; i < me; ++i) {
-        const double li = E[order[i] * kLd + order[i]];
+      const double floor_l = 64.0 * 2.220446049250313e-16 * l1;
+      for (int i = 0; i < cap; ++i) {
+        const double li = lamn[i] * tn;
         if (li > floor_l && sqrt(li) > 1e-10 * s1) ++k;
         else break;
       }
     }
-    int cap = f.rank < me ? f.rank : me;
-    cap = cap < d ? cap : d;
-    sh_k = k < cap ? k : cap;
+    sh_k = k;
   }
   __syncthreads();
   const int k = sh_k;
-  double* Z = f.zbuf + (long long)h * kMaxM * kMaxM;
-  // 8. z_c = G^-1 (u_c sigma_c): forward then backward substitution, one thread per c
-  if (tid < k) {
-    const int ii = order[tid];
-    const double sig = sqrt(E[ii * kLd + ii]);
-    double* z = Z + tid * kMaxM;
-    for (int i = 0; i < me; ++i) {
-      double s = U[i * kLd + ii] * sig;
-      for (int j = 0; j < i; ++j) s -= G[i * kLd + j] * z[j];
-      z[i] = s / G[i * kLd + i];
-    }
-    for (int i = me - 1; i >= 0; --i) {
-      double s = z[i];
-      for (int j = i + 1; j < me; ++j) s -= G[j * kLd + i] * z[j];
-      z[i] = s / G[i * kLd + i];
-    }
+  // 8. y_c = G^-1 (u_c sigma_c), into row c of Ws
+  for (int e = tid; e < k * n; e += kFitThreads) {
+    const int c = e / n, i = e - c * n;
+    const double sig = sqrt(lamn[c] * tn);
+    double s = 0.0;
+    for (int p = 0; p < n; ++p) s = fma(G[i * kLd + p], Zs[c * kLd + p], s);
+    Ws[c * kLd + i] = s * sig;
   }
   __syncthreads();
+  // A[:, c] = diag(1/s) Xw^T y_c,  Psi[:, c] = Rw^T u_c / sigma_c: Xw and Rw
+  // staged again into the free G and E areas; thread (column j, c-phase)
+  // runs over the probes, 8 c at a time
   double* Ab = f.abuf + (long long)h * d * kMaxM;
   double* Pb = f.pbuf + (long long)h * d * kMaxM;
-  for (int e = tid; e < d * k; e += 256) {
-    const int j = e / k, c = e % k;
-    const int ii = order[c];
-    const double sig = sqrt(E[ii * kLd + ii]);
-    const double* z = Z + c * kMaxM;
-    double bpsi = 0.0, psi = 0.0;
-    for (int p = 0; p < me; ++p) {
-      bpsi = fma(Xw[p * d + j], z[p], bpsi);
-      psi = fma(Rw[p * d + j], U[p * kLd + ii], psi);
+  for (int pass = 0; pass < 2; ++pass) {
+    const double* src = pass == 0 ? Xw : Rw;
+    double* st = G;                      // me x d, contiguous over G and E
+    {
+      const int n2 = me * d / 2;
+      constexpr int NL = 4096 / kFitThreads;
+      double2 v2[NL];
+#pragma unroll
+      for (int t = 0; t < NL; ++t) {
+        const int e = tid + kFitThreads * t;
+        v2[t] = e < n2 ? reinterpret_cast<const double2*>(src)[e] : double2{0.0, 0.0};
+      }
+#pragma unroll
+      for (int t = 0; t < NL; ++t) {
+        const int e = tid + kFitThreads * t;
+        if (e < n2) reinterpret_cast<double2*>(st)[e] = v2[t];
+      }
     }
-    Ab[j * kMaxM + c] = bpsi / sc[j];
-    Pb[j * kMaxM + c] = psi / sig;
+    __syncthreads();
+    const double* vecs = pass == 0 ? Ws : Zs;
+    for (int cb = (tid / d) * 8; cb < k; cb += (kFitThreads / d) * 8) {
+      double acc[8];
+#pragma unroll
+      for (int c = 0; c < 8; ++c) acc[c] = 0.0;
+      for (int p = 0; p < me; ++p) {
+        const double xv = st[p * d + jc];
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+          const int cc = cb + c < k ? cb + c : k - 1;
+          acc[c] = fma(xv, vecs[cc * kLd + p], acc[c]);
+        }
+      }
+#pragma unroll
+      for (int c = 0; c < 8; ++c)
+        if (cb + c < k) {
+          if (pass == 0) Ab[jc * kMaxM + cb + c] = acc[c] * isc[jc];
+          else Pb[jc * kMaxM + cb + c] = acc[c] / sqrt(lamn[cb + c] * tn);
+        }
+    }
+    __syncthreads();
   }
-  __syncthreads();
   // 9. c = mu_R - (mu_x A) Psi^T
   if (tid < k) {
     double t = 0.0;
@@ -1014,11 +1490,11 @@ __global__ __launch_bounds__(256) void fit_kernel(FitArgs f) {
   float* oa = f.corr_a + (long long)h * d * f.rank;
   float* op = f.corr_psi_t + (long long)h * f.rank * d;
   float* ocv = f.corr_c + (long long)h * d;
-  for (int e = tid; e < d * f.rank; e += 256) {
+  for (int e = tid; e < d * f.rank; e += kFitThreads) {
     const int j = e / f.rank, c = e % f.rank;
     oa[e] = c < k ? float(Ab[j * kMaxM + c]) : 0.f;
   }
-  for (int e = tid; e < f.rank * d; e += 256) {
+  for (int e = tid; e < f.rank * d; e += kFitThreads) {
     const int c = e / d, j = e % d;
     op[e] = c < k ? float(Pb[j * kMaxM + c]) : 0.f;
   }
@@ -1272,7 +1748,7 @@ int32_t probe_fit_impl(const sparsepr_dims* dims, int32_t m, int32_t rank, doubl
   fa.d = d;
   fa.rank = rank;
   fa.lambda = lambda;
-  fit_kernel<<<H, 256, 0, stream>>>(fa);
+  fit_kernel<<<H, kFitThreads, 0, stream>>>(fa);
   SPR_LAUNCH_CHECK();
   return SPARSEPR_OK;
 }
