@@ -39,16 +39,16 @@ KERNEL_SRC = os.path.join(ROOT, "free_block_sparse_major_amd", "csrc", "attn.hip
 
 def _item_waves(heads, n_q, c_q):
     """Waves per work item the attention launch picks for bf16 inputs (the
-    library's rule: 4 below 1024 query groups, else the best busy-wave share
-    for the mean group size in {4, 8, 12}, largest on ties)."""
-    if heads * c_q < 1024:
-        return 4
+    library's rule: the best busy-wave share for the mean group size in
+    {4, 8, 12}, largest on ties; 4 when that gives fewer items than CUs)."""
     q = -(-n_q // (32 * c_q))
     best, best_eff = 4, 0.0
     for w in (4, 8, 12):
         eff = q / (w * -(-q // w))
         if eff >= best_eff - 1e-12:
             best, best_eff = w, eff
+    if heads * c_q * -(-q // best) < 256:
+        return 4
     return best
 
 def _src_hash(path):

@@ -551,6 +551,25 @@ class SparsePRCall:
         self.correct()
         return self.out
 
+    def capture(self, labels_q, labels_kv, q, k, v):
+        """Records one whole call on these input tensors into a HIP graph
+        (torch.cuda.CUDAGraph); `replay()` then reruns it with one launch.
+        The library allocates nothing and issues no memset, so every kernel
+        of the call is captured; the inputs must stay at the same addresses
+        (copy new values into them before a replay)."""
+        self(labels_q, labels_kv, q, k, v)   # warm-up outside the capture
+        torch.cuda.synchronize()
+        self.graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(self.graph):
+            self(labels_q, labels_kv, q, k, v)
+        torch.cuda.synchronize()
+        return self.graph
+
+    def replay(self):
+        """Reruns the captured call (see `capture`); returns the output tensor."""
+        self.graph.replay()
+        return self.out
+
     def _chunked(self, labels_q, labels_kv, q, k, v):
         """Head ranges on the current stream and stream_b in turn.  A range
         reuses the workspace set of the range two before it, which ran on the

@@ -753,11 +753,11 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(AttnArgs p) {
 // so a larger item streams its group's K/V fewer times, but rows past the
 // group's end leave wave slots idle.  With q = ceil(mean group size / 32)
 // busy waves per group, the choice maximises q / (W * ceil(q / W)) and takes
-// the largest W on ties.  Calls with few groups per CU keep W = 4: there the
-// grid itself is short and more, smaller blocks balance better.
+// the largest W on ties.  A call whose items would then number fewer than
+// the 256 compute units keeps W = 4: there the grid itself is short and more,
+// smaller blocks balance better.
 int bf16_waves(const sparsepr_dims* d) {
   const long long groups = (long long)d->heads * d->c_q;
-  if (groups < 4LL * 256) return 4;
   const int q = int((d->n_q + 32LL * d->c_q - 1) / (32LL * d->c_q));
   int best = 4;
   double best_eff = 0.0;
@@ -768,6 +768,7 @@ int bf16_waves(const sparsepr_dims* d) {
       best_eff = eff;
     }
   }
+  if (groups * ((q + best - 1) / best) < 256) return 4;
   return best;
 }
 

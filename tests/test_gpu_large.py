@@ -17,24 +17,26 @@ pytestmark = pytest.mark.gpu
 
 
 def item_waves(heads, n_q, c_q):
-    """Host-side mirror of the attention launch rule for bf16 inputs: 4 waves
-    when there are fewer than 1024 query groups, else the shape in {4, 8, 12}
-    with the best busy-wave share for the mean group size (largest on ties)."""
-    if heads * c_q < 1024:
-        return 4
+    """Host-side mirror of the attention launch rule for bf16 inputs: the shape
+    in {4, 8, 12} with the best busy-wave share for the mean group size
+    (largest on ties), or 4 waves when that would give fewer work items than
+    the 256 compute units."""
     q = -(-n_q // (32 * c_q))
     best, best_eff = 4, 0.0
     for w in (4, 8, 12):
         eff = q / (w * -(-q // w))
         if eff >= best_eff - 1e-12:
             best, best_eff = w, eff
+    if heads * c_q * -(-q // best) < 256:
+        return 4
     return best
 
 
 def test_item_waves_rule():
     assert item_waves(40, 75600, 256) == 12
     assert item_waves(24, 118800, 256) == 8
-    assert item_waves(8, 17550, 64) == 4
+    assert item_waves(8, 17550, 64) == 12
+    assert item_waves(2, 700, 8) == 4
 
 
 def sample_rows(labels, c_q, count, seed):
@@ -85,10 +87,10 @@ def test_twelve_wave_items_d64():
 
 
 @pytest.mark.parametrize("name,heads,waves", [("wan", [0, 39], 12), ("hunyuan", [0, 23], 8),
-                                               ("cogvideox", [0, 3, 7], 4)])
+                                               ("cogvideox", [0, 3, 7], 12)])
 def test_full_size_sampled(name, heads, waves):
     # the full workloads in the benchmark's launch configuration: the
     # CogVideoX-like call (8 x 17550, d=64, 64 x 64 groups of ~274 rows) runs
-    # 4-wave items, several per query group, with a ragged last item
+    # one 12-wave item per query group, 9 busy waves with the helper split
     w = sg.workload(name)
     _check(w, heads, waves, rows_per_head=2000)
