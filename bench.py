@@ -29,7 +29,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
-F32_PEAK_TFLOPS = 157.3        # MI355X fp32 (matrix and vector)
+F32_PEAK_TFLOPS = 157.3        # MI355X fp32 matrix (v_mfma_f32_*_f32)
 HBM_PEAK_GBS = 8000.0
 METRIC = "ms per sparse-attention call (all heads) + executed-pair TFLOPS, % bf16 peak"
 PROFILE_PMC = os.path.join(ROOT, "profiles", "attn_bf16_kernel_wan_pmc.txt")
@@ -488,7 +488,7 @@ def main():
         out["density_sweep"] = sweep
     traffic = _traffic_from_profile(w.name)
     out["roofline"] = {
-        "bound": "mfma" if w.dtype == "bf16" else "alu",
+        "bound": "mfma",
         "kernel": ("attn_bf16_kernel<%d, %d>" % (d, _item_waves(w.heads, w.n, w.c_q))
                    if w.dtype == "bf16" else "attn_f32_kernel<%d>" % d),
         "achieved": round(attn_tflops, 2),

@@ -53,6 +53,9 @@ struct AttnArgs {
   int H, n_q, n_k, c_q, c_k;
   float scale_log2;      // softmax_scale * log2(e)
   int grid_blocks;       // launched blocks (multiple of 8)
+  int splits;            // fp32 kernel: key-stream splits per item (1: no partials)
+  float* part_o;         // [splits][H * n_q][D] unnormalised partial outputs
+  float* part_ml;        // [splits][H * n_q][2] (max * scale_log2, sum) per partial
 };
 
 // tiles[h*c_q + a] = sum over earlier (h, a) of ceil(n_a / tq); tiles[H*c_q] = total.
@@ -656,25 +659,36 @@ __global__ __launch_bounds__(64 * W, W <= 4 ? 2 : 1) void attn_bf16_kernel(AttnA
 }
 
 // ---------------------------------------------------------------------------
-// fp32 VALU kernel: LPQ lanes per query, 32 dims per lane, 32-key LDS tiles
+// fp32 kernel on fp32 MFMA (v_mfma_f32_32x32x2_f32: exact products, fp32
+// accumulation): 4 waves of 32 query rows, 32-key LDS tiles.
+// S^T = K Q^T: A = K (lane l: key l % 32, dim 2 s + l / 32), B = Q^T (lane l:
+// query l % 32, same dims), held in registers.  The result lane l holds
+// query l % 32 and keys 8 (r / 4) + 4 (l / 32) + r % 4 (r < 16).  PV takes
+// the keys in the order the lanes hold them: k-step u pairs key
+// kap(u, h) = 8 (u / 4) + 4 h + u % 4 of lane half h, so the B operand of
+// O^T = V^T P^T is register u of P as it stands and the A operand is
+// V[kap(u, l / 32)][32 db + l % 32].  Softmax is an fp32 online softmax over
+// exact fp32 P (no rounding of P before the product).
 // ---------------------------------------------------------------------------
 template <int D>
 struct SmemF32 {
-  float k[32][D + 4];
-  float v[32][D + 4];
+  float kv[2][32][D + 1];   // K tile, V tile (rows padded: K is read by key)
   int32_t cstart[SPARSEPR_MAX_GROUPS];
   int32_t cpos[SPARSEPR_MAX_GROUPS + 1];
   long long red[4];
 };
 
+typedef float f32x16v_t __attribute__((ext_vector_type(16)));
+
 template <int D>
 __global__ __launch_bounds__(256) void attn_f32_kernel(AttnArgs p) {
-  constexpr int LPQ = D / 32;
-  constexpr int TQ = 256 / LPQ;
+  constexpr int NS = D / 2;     // k-steps of S^T
+  constexpr int NDB = D / 32;   // 32-dim blocks of O^T
+  constexpr int TQ = 128;       // query rows per item
   __shared__ SmemF32<D> sm;
   int h, a, kt;
   if (!locate_item(p, h, a, kt)) return;
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, wid = tid >> 6, lane = tid & 63, n = lane & 31, hf = lane >> 5;
   const int32_t* oq = p.off_q + (long long)h * (p.c_q + 1);
   const int r0 = oq[a] + kt * TQ;
   const int nrows = min(TQ, oq[a + 1] - r0);
@@ -683,69 +697,151 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(AttnArgs p) {
   const int L = load_cells<256>(p, h, a, sm.cstart, sm.cpos, sm.red);
   const float* Kh = static_cast<const float*>(p.k) + (long long)h * p.n_k * D;
   const float* Vh = static_cast<const float*>(p.v) + (long long)h * p.n_k * D;
-  const int qi = tid / LPQ, sl = tid % LPQ;
-  const bool valid = qi < nrows;
-  float q[32], o[32];
-  const float* qrow = static_cast<const float*>(p.q) +
-                      ((long long)h * p.n_q + r0 + (valid ? qi : 0)) * D + 32 * sl;
+  const int qloc = wid * 32 + n;
+  const bool wave_active = wid * 32 < nrows;
+  const bool row_valid = qloc < nrows;
+  // Q^T fragments: dims 2 s + hf of this lane's query
+  float qf[NS];
+  {
+    const float* qrow = static_cast<const float*>(p.q) +
+                        ((long long)h * p.n_q + r0 + (row_valid ? qloc : 0)) * D;
 #pragma unroll
-  for (int i = 0; i < 32; ++i) {
-    q[i] = valid ? qrow[i] : 0.f;
-    o[i] = 0.f;
+    for (int s = 0; s < NS; ++s) qf[s] = row_valid ? qrow[2 * s + hf] : 0.f;
   }
+  f32x16v_t oacc[NDB];
+#pragma unroll
+  for (int i = 0; i < NDB; ++i) oacc[i] = f32x16v_t{};
+  const float c2 = p.scale_log2;
   float m_run = -__builtin_huge_valf(), l_run = 0.f;
-  const int ntiles = (L + 31) / 32;
-  for (int t = 0; t < ntiles; ++t) {
+  // split blockIdx.y of p.splits takes a contiguous range of the item's tiles
+  const int ntiles_all = (L + 31) / 32;
+  const int per = (ntiles_all + p.splits - 1) / p.splits;
+  const int t_lo = min(ntiles_all, int(blockIdx.y) * per);
+  const int ntiles = min(ntiles_all, t_lo + per);
+  for (int t = t_lo; t < ntiles; ++t) {
     __syncthreads();
+    // 32 keys x D of K and of V: thread e moves one float4 of each
     for (int e = tid; e < 32 * (D / 4); e += 256) {
       const int r = e / (D / 4), c4 = e % (D / 4);
       const int pos = t * 32 + r;
-      float4 kv = make_float4(0, 0, 0, 0), vv = make_float4(0, 0, 0, 0);
+      float4 kv4 = make_float4(0, 0, 0, 0), vv4 = make_float4(0, 0, 0, 0);
       if (pos < L) {
         const int c = find_cell(sm.cpos, nc, pos);
         const long long row = sm.cstart[c] + (pos - sm.cpos[c]);
-        kv = *reinterpret_cast<const float4*>(Kh + row * D + 4 * c4);
-        vv = *reinterpret_cast<const float4*>(Vh + row * D + 4 * c4);
+        kv4 = *reinterpret_cast<const float4*>(Kh + row * D + 4 * c4);
+        vv4 = *reinterpret_cast<const float4*>(Vh + row * D + 4 * c4);
       }
-      *reinterpret_cast<float4*>(&sm.k[r][4 * c4]) = kv;
-      *reinterpret_cast<float4*>(&sm.v[r][4 * c4]) = vv;
+      float* kd = &sm.kv[0][r][4 * c4];
+      float* vd = &sm.kv[1][r][4 * c4];
+      kd[0] = kv4.x; kd[1] = kv4.y; kd[2] = kv4.z; kd[3] = kv4.w;
+      vd[0] = vv4.x; vd[1] = vv4.y; vd[2] = vv4.z; vd[3] = vv4.w;
     }
     __syncthreads();
+    if (!wave_active) continue;
+    // S^T for the 32 keys of the tile
+    f32x16v_t sacc = f32x16v_t{};
+#pragma unroll
+    for (int s = 0; s < NS; ++s)
+      sacc = __builtin_amdgcn_mfma_f32_32x32x2f32(sm.kv[0][n][2 * s + hf], qf[s], sacc, 0, 0, 0);
     const int tail = L - t * 32;
-    float s[32];
     float mloc = -__builtin_huge_valf();
 #pragma unroll
-    for (int j = 0; j < 32; ++j) {
-      float acc = 0.f;
-#pragma unroll
-      for (int i = 0; i < 32; ++i) acc = fmaf(q[i], sm.k[j][32 * sl + i], acc);
-#pragma unroll
-      for (int o2 = 1; o2 < LPQ; o2 <<= 1) acc += __shfl_xor(acc, o2);
-      s[j] = j < tail ? acc * p.scale_log2 : -__builtin_huge_valf();
-      mloc = fmaxf(mloc, s[j]);
+    for (int r = 0; r < 16; ++r) {
+      const int key = 8 * (r >> 2) + 4 * hf + (r & 3);
+      if (key >= tail) sacc[r] = -__builtin_huge_valf();
+      mloc = fmaxf(mloc, sacc[r]);
     }
+    mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
     const float m_new = fmaxf(m_run, mloc);
-    const float alpha = exp2f(m_run - m_new);
+    const float alpha = __builtin_amdgcn_exp2f((m_run - m_new) * c2);
     m_run = m_new;
-    l_run *= alpha;
+    const float mc = m_new * c2;
+    float lsum = 0.f;
 #pragma unroll
-    for (int i = 0; i < 32; ++i) o[i] *= alpha;
+    for (int r = 0; r < 16; ++r) {
+      sacc[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[r], c2, -mc));
+      lsum += sacc[r];
+    }
+    l_run = l_run * alpha + lsum;
 #pragma unroll
-    for (int j = 0; j < 32; ++j) {
-      const float e = exp2f(s[j] - m_new);
-      l_run += e;
+    for (int db = 0; db < NDB; ++db) oacc[db] *= alpha;
+    // O^T += V^T P^T, keys in the lanes' own order
 #pragma unroll
-      for (int i = 0; i < 32; ++i) o[i] = fmaf(e, sm.v[j][32 * sl + i], o[i]);
+    for (int u = 0; u < 16; ++u) {
+      const int key = 8 * (u >> 2) + 4 * hf + (u & 3);
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+        oacc[db] = __builtin_amdgcn_mfma_f32_32x32x2f32(sm.kv[1][key][32 * db + n], sacc[u],
+                                                        oacc[db], 0, 0, 0);
     }
   }
-  if (!valid) return;
-  const float inv = 1.f / l_run;
-  float* orow = p.o + ((long long)h * p.n_q + r0 + qi) * D + 32 * sl;
+  if (!row_valid) return;
+  const float l_tot = l_run + __shfl_xor(l_run, 32);
+  const long long grow = (long long)h * p.n_q + r0 + qloc;
+  if (p.splits > 1) {
+    // unnormalised partial and its (max, sum); a split without keys leaves
+    // (-inf, 0) and zeros
+    const long long prow = (long long)blockIdx.y * p.H * p.n_q + grow;
+    float* po = p.part_o + prow * D;
 #pragma unroll
-  for (int i = 0; i < 32; i += 4)
-    *reinterpret_cast<float4*>(orow + i) =
-        make_float4(o[i] * inv, o[i + 1] * inv, o[i + 2] * inv, o[i + 3] * inv);
-  if (sl == 0 && p.lse) p.lse[(long long)h * p.n_q + r0 + qi] = (m_run + __log2f(l_run)) * kLn2;
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int i4 = 0; i4 < 4; ++i4)
+        *reinterpret_cast<float4*>(po + 32 * db + 8 * i4 + 4 * hf) =
+            make_float4(oacc[db][4 * i4 + 0], oacc[db][4 * i4 + 1], oacc[db][4 * i4 + 2],
+                        oacc[db][4 * i4 + 3]);
+    if (hf == 0) {
+      p.part_ml[2 * prow] = m_run == -__builtin_huge_valf() ? m_run : m_run * c2;
+      p.part_ml[2 * prow + 1] = l_tot;
+    }
+    return;
+  }
+  const float inv = 1.f / l_tot;
+  // O^T lane l: query l % 32, dims 32 db + 8 (r / 4) + 4 (l / 32) + r % 4
+  float* orow = p.o + grow * D;
+#pragma unroll
+  for (int db = 0; db < NDB; ++db)
+#pragma unroll
+    for (int i4 = 0; i4 < 4; ++i4) {
+      float4 v = make_float4(oacc[db][4 * i4 + 0] * inv, oacc[db][4 * i4 + 1] * inv,
+                             oacc[db][4 * i4 + 2] * inv, oacc[db][4 * i4 + 3] * inv);
+      *reinterpret_cast<float4*>(orow + 32 * db + 8 * i4 + 4 * hf) = v;
+    }
+  if (hf == 0 && p.lse) p.lse[grow] = (m_run * c2 + __log2f(l_tot)) * kLn2;
+}
+
+// Split partials of the fp32 kernel combined per row: weights 2^(m_s - M)
+// with M the largest partial maximum (log2 units), then O = sum w_s O_s /
+// sum w_s l_s.  D / 4 threads per row, four dims each.
+template <int D>
+__global__ __launch_bounds__(256) void attn_split_merge_kernel(const float* __restrict__ part_o,
+                                                               const float* __restrict__ part_ml,
+                                                               int splits, long long rows,
+                                                               float* __restrict__ o,
+                                                               float* __restrict__ lse) {
+  constexpr int TPR = D / 4;
+  const long long row = (long long)blockIdx.x * (256 / TPR) + threadIdx.x / TPR;
+  const int c4 = threadIdx.x % TPR;
+  if (row >= rows) return;
+  float M = -__builtin_huge_valf();
+  for (int s = 0; s < splits; ++s) M = fmaxf(M, part_ml[2 * (s * rows + row)]);
+  float l = 0.f;
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int s = 0; s < splits; ++s) {
+    const float ms = part_ml[2 * (s * rows + row)];
+    if (ms == -__builtin_huge_valf()) continue;
+    const float wgt = __builtin_amdgcn_exp2f(ms - M);
+    l = fmaf(wgt, part_ml[2 * (s * rows + row) + 1], l);
+    const float4 v = reinterpret_cast<const float4*>(part_o + (s * rows + row) * D)[c4];
+    acc.x = fmaf(wgt, v.x, acc.x);
+    acc.y = fmaf(wgt, v.y, acc.y);
+    acc.z = fmaf(wgt, v.z, acc.z);
+    acc.w = fmaf(wgt, v.w, acc.w);
+  }
+  const float inv = 1.f / l;
+  reinterpret_cast<float4*>(o + row * D)[c4] =
+      make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
+  if (c4 == 0 && lse) lse[row] = (M + __log2f(l)) * kLn2;
 }
 
 // Waves (32 query rows each) per bf16 work item: 4 (two blocks per CU), 8 or
@@ -774,7 +870,7 @@ int bf16_waves(const sparsepr_dims* d) {
 
 int rows_per_item(const sparsepr_dims* d) {
   if (d->dtype == SPARSEPR_BF16) return 32 * bf16_waves(d);
-  return 256 / (d->head_dim / 32);
+  return 128;   // fp32: 4 waves of 32 query rows
 }
 
 template <int D>
@@ -788,9 +884,24 @@ void launch_bf16(const AttnArgs& a, int blocks, int waves, hipStream_t s) {
 
 }  // namespace
 
+// fp32 calls with few work items split every item's key stream over up to
+// 8 blocks (partials merged afterwards), so the grid reaches about two
+// blocks per compute unit.
+int f32_splits(const sparsepr_dims* d) {
+  if (d->dtype != SPARSEPR_F32) return 1;
+  const long long items = (long long)d->heads * ((d->n_q + 127) / 128);
+  long long s = 512 / (items > 0 ? items : 1);
+  return int(s < 1 ? 1 : (s > 8 ? 8 : s));
+}
+
 size_t attn_ws_bytes(const sparsepr_dims* d) {
   Carver cv(nullptr);
   cv.take<int32_t>(size_t(d->heads) * d->c_q + 1);
+  const int sp = f32_splits(d);
+  if (sp > 1) {
+    cv.take<float>(size_t(sp) * d->heads * d->n_q * d->head_dim);
+    cv.take<float>(size_t(sp) * d->heads * d->n_q * 2);
+  }
   return cv.used;
 }
 
@@ -818,7 +929,8 @@ int32_t launch_attn(const sparsepr_dims* dims, const int32_t* offsets_q,
                     const int32_t* offsets_kv, const int32_t* cell_rowptr,
                     const int32_t* cell_col, const void* q_g, const void* k_g, const void* v_g,
                     const int32_t* v_shift, float softmax_scale, float* o_sp, float* lse,
-                    int32_t* tiles, hipStream_t stream) {
+                    int32_t* tiles, int splits, float* part_o, float* part_ml,
+                    hipStream_t stream) {
   const int tq = rows_per_item(dims);
   tile_table_kernel<<<1, 1024, 0, stream>>>(offsets_q, dims->heads, dims->c_q, tq, tiles);
   SPR_LAUNCH_CHECK();
@@ -845,13 +957,29 @@ int32_t launch_attn(const sparsepr_dims* dims, const int32_t* offsets_q,
   a.c_k = dims->c_k;
   a.scale_log2 = softmax_scale * kLog2e;
   a.grid_blocks = int(bound);
+  a.splits = splits;
+  a.part_o = part_o;
+  a.part_ml = part_ml;
   if (dims->dtype == SPARSEPR_BF16) {
     const int w = bf16_waves(dims);
     if (dims->head_dim == 128) launch_bf16<128>(a, int(bound), w, stream);
     else launch_bf16<64>(a, int(bound), w, stream);
   } else {
-    if (dims->head_dim == 128) attn_f32_kernel<128><<<int(bound), 256, 0, stream>>>(a);
-    else attn_f32_kernel<64><<<int(bound), 256, 0, stream>>>(a);
+    const dim3 grid{unsigned(bound), unsigned(splits), 1u};
+    if (dims->head_dim == 128) attn_f32_kernel<128><<<grid, 256, 0, stream>>>(a);
+    else attn_f32_kernel<64><<<grid, 256, 0, stream>>>(a);
+    SPR_LAUNCH_CHECK();
+    if (splits > 1) {
+      const long long rows = (long long)dims->heads * dims->n_q;
+      const int rpb = 256 / (dims->head_dim / 4);
+      const unsigned mb = unsigned((rows + rpb - 1) / rpb);
+      if (dims->head_dim == 128)
+        attn_split_merge_kernel<128><<<mb, 256, 0, stream>>>(part_o, part_ml, splits, rows, o_sp,
+                                                             lse);
+      else
+        attn_split_merge_kernel<64><<<mb, 256, 0, stream>>>(part_o, part_ml, splits, rows, o_sp,
+                                                            lse);
+    }
   }
   SPR_LAUNCH_CHECK();
   return SPARSEPR_OK;
@@ -903,8 +1031,15 @@ extern "C" int32_t sparsepr_sparse_attn(const sparsepr_dims* dims, const int32_t
   if (!ws || ws_bytes < need) return SPARSEPR_ERR_WORKSPACE;
   Carver cv(ws);
   int32_t* tiles = cv.take<int32_t>(size_t(dims->heads) * dims->c_q + 1);
+  const int sp = f32_splits(dims);
+  float* part_o = nullptr;
+  float* part_ml = nullptr;
+  if (sp > 1) {
+    part_o = cv.take<float>(size_t(sp) * dims->heads * dims->n_q * dims->head_dim);
+    part_ml = cv.take<float>(size_t(sp) * dims->heads * dims->n_q * 2);
+  }
   return launch_attn(dims, offsets_q, offsets_kv, cell_rowptr, cell_col, q_g, k_g, v_g, v_shift,
-                     softmax_scale, o_sp, lse, tiles, stream);
+                     softmax_scale, o_sp, lse, tiles, sp, part_o, part_ml, stream);
 }
 
 extern "C" int32_t sparsepr_sparse_attn_noalloc(const sparsepr_dims* dims,
@@ -921,6 +1056,7 @@ extern "C" int32_t sparsepr_sparse_attn_noalloc(const sparsepr_dims* dims,
   if (int64_t(dims->heads) * dims->c_q + 1 > kNoAllocTableEntries) return SPARSEPR_ERR_UNSUPPORTED;
   int32_t* tiles = scratch_on_current_device(&st);
   if (st != SPARSEPR_OK) return st;
+  // no partial buffers: fp32 calls run unsplit here
   return launch_attn(dims, offsets_q, offsets_kv, cell_rowptr, cell_col, q_g, k_g, v_g, v_shift,
-                     softmax_scale, o_sp, lse, tiles, stream);
+                     softmax_scale, o_sp, lse, tiles, 1, nullptr, nullptr, stream);
 }
