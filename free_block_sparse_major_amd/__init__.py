@@ -24,7 +24,7 @@ LIB_PATH = os.path.join(HERE, "libsparsepr.so")
 OK, ERR_INVALID, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = range(5)
 BF16, F32 = 0, 1
 (CALL_PARTITION_LAYOUT, CALL_ROUTE_CELLS, CALL_SPARSE_ATTN, CALL_PROBE_FIT, CALL_CORRECT,
- CALL_RCP_PARTITION, CALL_PROBE_FIT_EX, CALL_ROUTE_CELLS_EX) = range(8)
+ CALL_RCP_PARTITION, CALL_PROBE_FIT_EX, CALL_ROUTE_CELLS_EX, CALL_SPARSE_ATTN_CORRECT) = range(9)
 ROUTE_GLOBAL, ROUTE_PER_GROUP = range(2)
 ROUTE_RULES = {"global": ROUTE_GLOBAL, "per_group": ROUTE_PER_GROUP}
 EST_FULL, EST_MEAN, EST_SCALAR, EST_DIAGONAL = range(4)
@@ -35,6 +35,7 @@ EXPORTED = (
     "sparsepr_status_string", "sparsepr_version", "sparsepr_rcp_partition",
     "sparsepr_probe_fit_ex", "sparsepr_correct_ex", "sparsepr_route_cells_ex",
     "sparsepr_rcp_partition_ex", "sparsepr_debug_check", "sparsepr_sparse_attn_noalloc",
+    "sparsepr_sparse_attn_correct",
 )
 
 
@@ -81,6 +82,12 @@ def load_library(path: str = LIB_PATH):
     lib.sparsepr_sparse_attn_noalloc.argtypes = [DP, P, P, P, P, P, P, P, P, ctypes.c_float, P,
                                                  P, P]
     lib.sparsepr_sparse_attn_noalloc.restype = I32
+    # dims, m, rank, offsets_q, offsets_kv, cell_rowptr, cell_col, q_g, k_g, v_g, v_shift,
+    # scale, perm_q, probe_tokens, o_probe_dense, corr_a, corr_psi_t, corr_c, corr_g, out,
+    # out_dtype, out_stride_head, out_stride_tok, lse, ws, ws_bytes, stream
+    lib.sparsepr_sparse_attn_correct.argtypes = ([DP, I32, I32] + [P] * 8 + [ctypes.c_float]
+                                                 + [P] * 8 + [I32, I64, I64, P, P, SZ, P])
+    lib.sparsepr_sparse_attn_correct.restype = I32
     lib.sparsepr_probe_fit.argtypes = ([DP, I32, I32, D] + [P] * 10 + [ctypes.c_float] + [P] * 7
                                        + [P, SZ, P])
     lib.sparsepr_probe_fit.restype = I32
@@ -186,6 +193,21 @@ def sparsepr_sparse_attn_noalloc(dims, offsets_q, offsets_kv, cell_rowptr, cell_
         _ptr(q_g), _ptr(k_g), _ptr(v_g), _ptr(v_shift), ctypes.c_float(softmax_scale),
         _ptr(o_sp), _ptr(lse), _stream(stream))
     _check(st, "sparsepr_sparse_attn_noalloc")
+
+
+def sparsepr_sparse_attn_correct(dims, m, rank, offsets_q, offsets_kv, cell_rowptr, cell_col,
+                                 q_g, k_g, v_g, v_shift, softmax_scale, perm_q, probe_tokens,
+                                 o_probe_dense, corr_a, corr_psi_t, corr_c, corr_g, out,
+                                 out_dtype, out_stride_head, out_stride_tok, lse, ws,
+                                 stream=None):
+    st = load_library().sparsepr_sparse_attn_correct(
+        ctypes.byref(dims), int(m), int(rank), _ptr(offsets_q), _ptr(offsets_kv),
+        _ptr(cell_rowptr), _ptr(cell_col), _ptr(q_g), _ptr(k_g), _ptr(v_g), _ptr(v_shift),
+        ctypes.c_float(softmax_scale), _ptr(perm_q), _ptr(probe_tokens), _ptr(o_probe_dense),
+        _ptr(corr_a), _ptr(corr_psi_t), _ptr(corr_c), _ptr(corr_g), _ptr(out), int(out_dtype),
+        int(out_stride_head), int(out_stride_tok), _ptr(lse), _ptr(ws),
+        ws.numel() * ws.element_size() if ws is not None else 0, _stream(stream))
+    _check(st, "sparsepr_sparse_attn_correct")
 
 
 def sparsepr_probe_fit(dims, m, rank, lam, offsets_q, offsets_kv, perm_q, cell_rowptr, cell_col,
@@ -376,12 +398,16 @@ class SparsePRCall:
     head_chunks > 1 splits a call into that many ranges of heads, issued on
     two alternating streams (with the probe fits on a third), so that the
     layout and routing of one range run while the attention of the previous
-    one does; every head is computed exactly as in a whole call."""
+    one does; every head is computed exactly as in a whole call.
+
+    fused=True runs the probe-first order: the probe fit before the attention,
+    and the attention writes the corrected output in token order
+    (sparsepr_sparse_attn_correct), so O_sp is neither stored nor read."""
 
     def __init__(self, heads, n_q, n_k, head_dim, dtype, c_q, c_k, m=64, rank=16, lam=0.1,
                  rho="0.26", budget=None, out_dtype=F32, device="cuda", q_strides=None,
                  kv_strides=None, overlap=True, feat_dim=0, estimator="full",
-                 route_rule="global", head_chunks=1):
+                 route_rule="global", head_chunks=1, fused=False):
         load_library()
         self.dims = make_dims(heads, n_q, n_k, head_dim, dtype, c_q, c_k, q_strides, kv_strides)
         self.m, self.rank, self.lam = m, rank, lam
@@ -442,6 +468,12 @@ class SparsePRCall:
                     ws(CALL_SPARSE_ATTN),
                     ws(CALL_PROBE_FIT_EX if self._ex else CALL_PROBE_FIT))
 
+        self.fused = bool(fused)
+        if self.fused and head_chunks != 1:
+            raise ValueError("the fused order runs whole calls (head_chunks=1)")
+        if self.fused:
+            nb = workspace_bytes(CALL_SPARSE_ATTN_CORRECT, self.dims, m, rank)
+            self.ws_attn_correct = torch.empty(max(nb, 256), dtype=torch.uint8, device=dev)
         self._whole = _Heads(self, 0, H, ws_set(self.dims))
         self.ws_layout, self.ws_route, self.ws_attn, self.ws_probe = (
             self._whole.ws_layout, self._whole.ws_route, self._whole.ws_attn, self._whole.ws_probe)
@@ -530,11 +562,28 @@ class SparsePRCall:
                          p.o_probe_dense, p.corr_a, p.corr_psi_t, p.corr_c, p.out,
                          self.out_dtype, p.out.stride(0), p.out.stride(1), stream)
 
+    def attend_correct(self, stream=None):
+        """The attention with the correction in its epilogue (fused order)."""
+        p = self._whole
+        sparsepr_sparse_attn_correct(p.dims, self.m, self.rank, p.offsets_q, p.offsets_kv,
+                                     p.cell_rowptr, p.cell_col, p.q_g, p.k_g, p.v_g, p.v_shift,
+                                     self.scale, p.perm_q, p.probe_tokens, p.o_probe_dense,
+                                     p.corr_a, p.corr_psi_t, p.corr_c,
+                                     p.corr_g if self.estimator != EST_FULL else None, p.out,
+                                     self.out_dtype, p.out.stride(0), p.out.stride(1), p.lse,
+                                     self.ws_attn_correct, stream)
+
     def __call__(self, labels_q, labels_kv, q, k, v):
         """One whole attention call on the current stream (probe fit on the
         side stream when overlap is on).  Returns the output tensor."""
         if self.chunks is not None:
             return self._chunked(labels_q, labels_kv, q, k, v)
+        if self.fused:
+            self.layout(labels_q, labels_kv, q, k, v)
+            self.route()
+            self.probe_fit()
+            self.attend_correct()
+            return self.out
         main = torch.cuda.current_stream()
         self.layout(labels_q, labels_kv, q, k, v)
         self.route()

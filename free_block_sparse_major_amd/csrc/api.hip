@@ -51,6 +51,9 @@ extern "C" size_t sparsepr_workspace_bytes(int32_t which, const sparsepr_dims* d
     case SPARSEPR_CALL_CORRECT: return 0;
     case SPARSEPR_CALL_RCP_PARTITION: return spr::rcp_ws_bytes(dims);
     case SPARSEPR_CALL_ROUTE_CELLS_EX: return spr::route_ex_ws_bytes(dims);
+    case SPARSEPR_CALL_SPARSE_ATTN_CORRECT:
+      if (rank < 0 || rank > SPARSEPR_MAX_RANK) return 0;
+      return spr::attn_correct_ws_bytes(dims, rank);
     case SPARSEPR_CALL_PROBE_FIT_EX:
       if (m < 1 || m > SPARSEPR_MAX_PROBES || rank < 0 || rank > SPARSEPR_MAX_RANK) return 0;
       return spr::probe_feat_ws_bytes(dims, m, rank);

@@ -53,6 +53,16 @@ struct AttnArgs {
   int H, n_q, n_k, c_q, c_k;
   float scale_log2;      // softmax_scale * log2(e)
   int grid_blocks;       // launched blocks (multiple of 8)
+  // fused correction (the attention writes the corrected output in token
+  // order instead of O_sp): out = o + (o A) Psi^T + g * o + c
+  const int32_t* perm_q;     // [H][N_q] group-major row -> token
+  const float* corr_a;       // [H][D][rank]
+  const float* corr_psi_t;   // [H][rank][D]
+  const float* corr_c;       // [H][D]
+  const float* corr_g;       // [H][D] or null
+  void* out;
+  long long out_sh, out_st;  // element strides of out
+  int out_bf16, rank;
   int splits;            // fp32 kernel: key-stream splits per item (1: no partials)
   float* part_o;         // [splits][H * n_q][D] unnormalised partial outputs
   float* part_ml;        // [splits][H * n_q][2] (max * scale_log2, sum) per partial
@@ -192,7 +202,10 @@ struct Stage {
 // that).  P therefore stays at or below 2^8, well inside fp16.
 constexpr float kPSumCap = 256.f;
 
-template <int D, int W>
+// Maximum rank of the correction fused into the attention epilogue.
+constexpr int kFusedRank = 16;
+
+template <int D, int W, bool FUSED>
 __global__ __launch_bounds__(64 * W, W <= 4 ? 2 : 1) void attn_bf16_kernel(AttnArgs p) {
   constexpr int NT = 64 * W;          // threads
   constexpr int ROWS = 32 * W;        // query rows per work item
@@ -209,9 +222,25 @@ __global__ __launch_bounds__(64 * W, W <= 4 ? 2 : 1) void attn_bf16_kernel(AttnA
   __shared__ uint4 k_s0[KT / 8 * D], k_s1[KT / 8 * D];   // KT rows x D bf16
   __shared__ uint4 v_s0[KT / 8 * D], v_s1[KT / 8 * D];   // KT rows x D fp16
   __shared__ SmemCells sm;
+  // fused correction: A (D x kFusedRank), Psi^T (kFusedRank x D), c and g
+  __shared__ float corr_s[FUSED ? (2 * kFusedRank + 2) * D : 1];
 
   int h, a, kt;
   if (!locate_item(p, h, a, kt)) return;
+  if constexpr (FUSED) {
+    // rows of A padded to kFusedRank columns; unused columns read as 0
+    const float* A = p.corr_a + (long long)h * D * p.rank;
+    const float* Pt = p.corr_psi_t + (long long)h * p.rank * D;
+    for (int e = threadIdx.x; e < D * kFusedRank; e += NT) {
+      const int j = e / kFusedRank, c = e % kFusedRank;
+      corr_s[e] = c < p.rank ? A[j * p.rank + c] : 0.f;
+      corr_s[D * kFusedRank + e] = e < p.rank * D ? Pt[e] : 0.f;
+    }
+    for (int j = threadIdx.x; j < D; j += NT) {
+      corr_s[2 * D * kFusedRank + j] = p.corr_c[(long long)h * D + j];
+      corr_s[2 * D * kFusedRank + D + j] = p.corr_g ? p.corr_g[(long long)h * D + j] : 0.f;
+    }
+  }
   // wave index as a scalar: everything derived from it (LDS destinations of the
   // tile loads, row ranges) stays in SGPRs
   const int tid = threadIdx.x, wid = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63,
@@ -645,15 +674,71 @@ __global__ __launch_bounds__(64 * W, W <= 4 ? 2 : 1) void attn_bf16_kernel(AttnA
   if (!row_valid) return;
   const float l_tot = l_run + __shfl_xor(l_run, 32);
   const float inv = __builtin_ldexpf(1.f, sv) / l_tot;
-  float* orow = p.o + ((long long)h * p.n_q + r0 + qloc) * D;
+  if constexpr (FUSED) {
+    // o (this lane: dims 32 db + 8 i4 + 4 g + 0..3), u = o A over both lanes
+    // of the row, then out = o + g * o + c + u Psi^T, written to the row's
+    // token (the correction step of the call, SparsePR review step (5))
+    float u[kFusedRank];
 #pragma unroll
-  for (int db = 0; db < NDB; ++db)
+    for (int c = 0; c < kFusedRank; ++c) u[c] = 0.f;
 #pragma unroll
-    for (int i4 = 0; i4 < 4; ++i4) {
-      float4 v = make_float4(oacc[db][4 * i4 + 0] * inv, oacc[db][4 * i4 + 1] * inv,
-                             oacc[db][4 * i4 + 2] * inv, oacc[db][4 * i4 + 3] * inv);
-      *reinterpret_cast<float4*>(orow + 32 * db + 8 * i4 + 4 * g) = v;
-    }
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int j = 32 * db + 8 * (r >> 2) + 4 * g + (r & 3);
+        const float o = oacc[db][r] * inv;
+        const float4* arow = reinterpret_cast<const float4*>(corr_s + j * kFusedRank);
+#pragma unroll
+        for (int c4 = 0; c4 < kFusedRank / 4; ++c4) {
+          const float4 av = arow[c4];
+          u[4 * c4 + 0] = fmaf(o, av.x, u[4 * c4 + 0]);
+          u[4 * c4 + 1] = fmaf(o, av.y, u[4 * c4 + 1]);
+          u[4 * c4 + 2] = fmaf(o, av.z, u[4 * c4 + 2]);
+          u[4 * c4 + 3] = fmaf(o, av.w, u[4 * c4 + 3]);
+        }
+      }
+#pragma unroll
+    for (int c = 0; c < kFusedRank; ++c) u[c] += __shfl_xor(u[c], 32);
+    const float* pst = corr_s + D * kFusedRank;
+    const float* cs = corr_s + 2 * D * kFusedRank;
+    const int tok = p.perm_q[(long long)h * p.n_q + r0 + qloc];
+    const long long obase = (long long)h * p.out_sh + (long long)tok * p.out_st;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int i4 = 0; i4 < 4; ++i4) {
+        const int j0 = 32 * db + 8 * i4 + 4 * g;
+        float v[4];
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+          const int j = j0 + jj;
+          const float o = oacc[db][4 * i4 + jj] * inv;
+          float acc = fmaf(cs[D + j], o, o + cs[j]);
+#pragma unroll
+          for (int c = 0; c < kFusedRank; ++c) acc = fmaf(u[c], pst[c * D + j], acc);
+          v[jj] = acc;
+        }
+        if (p.out_bf16) {
+          uint2 pk;
+          pk.x = uint32_t(f32_to_bf16_rne(v[0])) | (uint32_t(f32_to_bf16_rne(v[1])) << 16);
+          pk.y = uint32_t(f32_to_bf16_rne(v[2])) | (uint32_t(f32_to_bf16_rne(v[3])) << 16);
+          *reinterpret_cast<uint2*>(static_cast<uint16_t*>(p.out) + obase + j0) = pk;
+        } else {
+          *reinterpret_cast<float4*>(static_cast<float*>(p.out) + obase + j0) =
+              make_float4(v[0], v[1], v[2], v[3]);
+        }
+      }
+  } else {
+    float* orow = p.o + ((long long)h * p.n_q + r0 + qloc) * D;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int i4 = 0; i4 < 4; ++i4) {
+        float4 v = make_float4(oacc[db][4 * i4 + 0] * inv, oacc[db][4 * i4 + 1] * inv,
+                               oacc[db][4 * i4 + 2] * inv, oacc[db][4 * i4 + 3] * inv);
+        *reinterpret_cast<float4*>(orow + 32 * db + 8 * i4 + 4 * g) = v;
+      }
+  }
   if (g == 0 && p.lse)
     p.lse[(long long)h * p.n_q + r0 + qloc] = (m_run * c2 + __log2f(l_tot)) * kLn2;
 }
@@ -873,12 +958,12 @@ int rows_per_item(const sparsepr_dims* d) {
   return 128;   // fp32: 4 waves of 32 query rows
 }
 
-template <int D>
+template <int D, bool FUSED = false>
 void launch_bf16(const AttnArgs& a, int blocks, int waves, hipStream_t s) {
   switch (waves) {
-    case 4: attn_bf16_kernel<D, 4><<<blocks, 256, 0, s>>>(a); break;
-    case 8: attn_bf16_kernel<D, 8><<<blocks, 512, 0, s>>>(a); break;
-    default: attn_bf16_kernel<D, 12><<<blocks, 768, 0, s>>>(a); break;
+    case 4: attn_bf16_kernel<D, 4, FUSED><<<blocks, 256, 0, s>>>(a); break;
+    case 8: attn_bf16_kernel<D, 8, FUSED><<<blocks, 512, 0, s>>>(a); break;
+    default: attn_bf16_kernel<D, 12, FUSED><<<blocks, 768, 0, s>>>(a); break;
   }
 }
 
@@ -892,6 +977,21 @@ int f32_splits(const sparsepr_dims* d) {
   const long long items = (long long)d->heads * ((d->n_q + 127) / 128);
   long long s = 512 / (items > 0 ? items : 1);
   return int(s < 1 ? 1 : (s > 8 ? 8 : s));
+}
+
+// The fused call runs the correction in the attention epilogue for bf16
+// inputs with rank <= kFusedRank; otherwise it computes O_sp into its
+// workspace and runs the correction kernel.
+bool fused_epilogue(const sparsepr_dims* d, int rank) {
+  return d->dtype == SPARSEPR_BF16 && rank <= kFusedRank;
+}
+
+size_t attn_ws_bytes(const sparsepr_dims* d);
+
+size_t attn_correct_ws_bytes(const sparsepr_dims* d, int rank) {
+  size_t nb = (attn_ws_bytes(d) + 255) & ~size_t(255);
+  if (!fused_epilogue(d, rank)) nb += size_t(d->heads) * d->n_q * d->head_dim * sizeof(float);
+  return nb;
 }
 
 size_t attn_ws_bytes(const sparsepr_dims* d) {
@@ -930,7 +1030,7 @@ int32_t launch_attn(const sparsepr_dims* dims, const int32_t* offsets_q,
                     const int32_t* cell_col, const void* q_g, const void* k_g, const void* v_g,
                     const int32_t* v_shift, float softmax_scale, float* o_sp, float* lse,
                     int32_t* tiles, int splits, float* part_o, float* part_ml,
-                    hipStream_t stream) {
+                    hipStream_t stream, const AttnArgs* fuse = nullptr) {
   const int tq = rows_per_item(dims);
   tile_table_kernel<<<1, 1024, 0, stream>>>(offsets_q, dims->heads, dims->c_q, tq, tiles);
   SPR_LAUNCH_CHECK();
@@ -960,10 +1060,32 @@ int32_t launch_attn(const sparsepr_dims* dims, const int32_t* offsets_q,
   a.splits = splits;
   a.part_o = part_o;
   a.part_ml = part_ml;
+  a.perm_q = nullptr;
+  a.corr_a = a.corr_psi_t = a.corr_c = a.corr_g = nullptr;
+  a.out = nullptr;
+  a.out_sh = a.out_st = 0;
+  a.out_bf16 = a.rank = 0;
+  if (fuse) {
+    a.perm_q = fuse->perm_q;
+    a.corr_a = fuse->corr_a;
+    a.corr_psi_t = fuse->corr_psi_t;
+    a.corr_c = fuse->corr_c;
+    a.corr_g = fuse->corr_g;
+    a.out = fuse->out;
+    a.out_sh = fuse->out_sh;
+    a.out_st = fuse->out_st;
+    a.out_bf16 = fuse->out_bf16;
+    a.rank = fuse->rank;
+  }
   if (dims->dtype == SPARSEPR_BF16) {
     const int w = bf16_waves(dims);
-    if (dims->head_dim == 128) launch_bf16<128>(a, int(bound), w, stream);
-    else launch_bf16<64>(a, int(bound), w, stream);
+    if (fuse) {
+      if (dims->head_dim == 128) launch_bf16<128, true>(a, int(bound), w, stream);
+      else launch_bf16<64, true>(a, int(bound), w, stream);
+    } else {
+      if (dims->head_dim == 128) launch_bf16<128>(a, int(bound), w, stream);
+      else launch_bf16<64>(a, int(bound), w, stream);
+    }
   } else {
     const dim3 grid{unsigned(bound), unsigned(splits), 1u};
     if (dims->head_dim == 128) attn_f32_kernel<128><<<grid, 256, 0, stream>>>(a);
@@ -1059,4 +1181,66 @@ extern "C" int32_t sparsepr_sparse_attn_noalloc(const sparsepr_dims* dims,
   // no partial buffers: fp32 calls run unsplit here
   return launch_attn(dims, offsets_q, offsets_kv, cell_rowptr, cell_col, q_g, k_g, v_g, v_shift,
                      softmax_scale, o_sp, lse, tiles, 1, nullptr, nullptr, stream);
+}
+
+extern "C" int32_t sparsepr_sparse_attn_correct(
+    const sparsepr_dims* dims, int32_t m, int32_t rank, const int32_t* offsets_q,
+    const int32_t* offsets_kv, const int32_t* cell_rowptr, const int32_t* cell_col,
+    const void* q_g, const void* k_g, const void* v_g, const int32_t* v_shift,
+    float softmax_scale, const int32_t* perm_q, const int32_t* probe_tokens,
+    const float* o_probe_dense, const float* corr_a, const float* corr_psi_t,
+    const float* corr_c, const float* corr_g, void* out, int32_t out_dtype,
+    int64_t out_stride_head, int64_t out_stride_tok, float* lse, void* ws, size_t ws_bytes,
+    hipStream_t stream) {
+  int32_t st = check_dims(dims);
+  if (st != SPARSEPR_OK) return st;
+  if (!offsets_q || !offsets_kv || !cell_rowptr || !cell_col || !q_g || !k_g || !v_g ||
+      !v_shift || !perm_q || !probe_tokens || !o_probe_dense || !corr_a || !corr_psi_t ||
+      !corr_c || !out)
+    return SPARSEPR_ERR_INVALID;
+  if (m < 1 || m > SPARSEPR_MAX_PROBES || rank < 0 || rank > SPARSEPR_MAX_RANK)
+    return SPARSEPR_ERR_INVALID;
+  if (out_dtype != SPARSEPR_BF16 && out_dtype != SPARSEPR_F32) return SPARSEPR_ERR_UNSUPPORTED;
+  const int64_t es = out_dtype == SPARSEPR_BF16 ? 2 : 4;
+  if (((out_stride_head * es) & 15) || ((out_stride_tok * es) & 15) ||
+      out_stride_tok < dims->head_dim || out_stride_head < 0)
+    return SPARSEPR_ERR_INVALID;
+  if (!ws || ws_bytes < attn_correct_ws_bytes(dims, rank)) return SPARSEPR_ERR_WORKSPACE;
+  Carver cv(ws);
+  int32_t* tiles = cv.take<int32_t>(size_t(dims->heads) * dims->c_q + 1);
+  const int sp = f32_splits(dims);
+  float* part_o = nullptr;
+  float* part_ml = nullptr;
+  if (sp > 1) {
+    part_o = cv.take<float>(size_t(sp) * dims->heads * dims->n_q * dims->head_dim);
+    part_ml = cv.take<float>(size_t(sp) * dims->heads * dims->n_q * 2);
+  }
+  if (fused_epilogue(dims, rank)) {
+    AttnArgs fz;
+    fz.perm_q = perm_q;
+    fz.corr_a = corr_a;
+    fz.corr_psi_t = corr_psi_t;
+    fz.corr_c = corr_c;
+    fz.corr_g = corr_g;
+    fz.out = out;
+    fz.out_sh = out_stride_head;
+    fz.out_st = out_stride_tok;
+    fz.out_bf16 = out_dtype == SPARSEPR_BF16;
+    fz.rank = rank;
+    st = launch_attn(dims, offsets_q, offsets_kv, cell_rowptr, cell_col, q_g, k_g, v_g, v_shift,
+                     softmax_scale, nullptr, lse, tiles, sp, part_o, part_ml, stream, &fz);
+    if (st != SPARSEPR_OK) return st;
+    return launch_probe_overwrite(dims, m, probe_tokens, o_probe_dense, out,
+                                  out_dtype == SPARSEPR_BF16, out_stride_head, out_stride_tok,
+                                  stream);
+  }
+  // correction as its own kernel, O_sp in the workspace
+  size_t off = (attn_ws_bytes(dims) + 255) & ~size_t(255);
+  float* o_sp = reinterpret_cast<float*>(static_cast<char*>(ws) + off);
+  st = launch_attn(dims, offsets_q, offsets_kv, cell_rowptr, cell_col, q_g, k_g, v_g, v_shift,
+                   softmax_scale, o_sp, lse, tiles, sp, part_o, part_ml, stream);
+  if (st != SPARSEPR_OK) return st;
+  return sparsepr_correct_ex(dims, m, rank, perm_q, o_sp, probe_tokens, o_probe_dense, corr_a,
+                             corr_psi_t, corr_c, corr_g, out, out_dtype, out_stride_head,
+                             out_stride_tok, nullptr, 0, stream);
 }

@@ -134,6 +134,12 @@ inline size_t elem_bytes(int dtype) { return dtype == SPARSEPR_BF16 ? 2 : 4; }
 
 // Validates the shape; returns a status code.
 int32_t check_dims(const sparsepr_dims* d);
+// Probe rows take their dense output in the token-order output (S9).
+int32_t launch_probe_overwrite(const sparsepr_dims* d, int m, const int32_t* tokens,
+                               const float* dense, void* out, int out_bf16, int64_t sh,
+                               int64_t st, hipStream_t stream);
+// Workspace of sparsepr_sparse_attn_correct.
+size_t attn_correct_ws_bytes(const sparsepr_dims* d, int rank);
 // rows of q, k and v are read in 16-byte chunks: their base pointers must be
 // 16-byte aligned (the strides are checked by check_dims)
 inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }

@@ -339,6 +339,17 @@ void launch_correct(const CorrArgs& a, dim3 grid, hipStream_t s) {
 }  // namespace
 }  // namespace spr
 
+namespace spr {
+int32_t launch_probe_overwrite(const sparsepr_dims* d, int m, const int32_t* tokens,
+                               const float* dense, void* out, int out_bf16, int64_t sh,
+                               int64_t st, hipStream_t stream) {
+  probe_overwrite_kernel<<<d->heads, 256, 0, stream>>>(tokens, dense, m, d->head_dim, out, sh, st,
+                                                       out_bf16);
+  SPR_LAUNCH_CHECK();
+  return SPARSEPR_OK;
+}
+}  // namespace spr
+
 using namespace spr;
 
 namespace {

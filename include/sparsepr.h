@@ -84,7 +84,8 @@ enum {
   SPARSEPR_CALL_CORRECT = 4,
   SPARSEPR_CALL_RCP_PARTITION = 5,
   SPARSEPR_CALL_PROBE_FIT_EX = 6,
-  SPARSEPR_CALL_ROUTE_CELLS_EX = 7
+  SPARSEPR_CALL_ROUTE_CELLS_EX = 7,
+  SPARSEPR_CALL_SPARSE_ATTN_CORRECT = 8
 };
 
 /* Routing rules of sparsepr_route_cells_ex. */
@@ -326,6 +327,38 @@ int32_t sparsepr_correct(const sparsepr_dims* dims /* host */, int32_t m, int32_
                          void* out, int32_t out_dtype,
                          int64_t out_stride_head, int64_t out_stride_tok,
                          void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * S5 + S9 in one call: the probe-first order of a call.  (SparsePR paper
+ * App. A.1: the exact probe rows come with their hard-drop rows from the
+ * retained / omitted partial sums, so probe_fit does not need the output of
+ * sparse_attn and can run before it; the review's step (5): unprobed rows get
+ * their sparse output plus the predicted residual, probe rows their dense
+ * output, in the original token order.)  Run sparsepr_probe_fit (or _ex)
+ * first; this call then computes the hard-drop attention of every row and
+ * writes
+ *   out[h][perm_q[h][r]] = o + (o A) Psi^T + g * o + c   (unprobed rows)
+ *   out[h][probe token]  = o_probe_dense                  (probe rows)
+ * so no O_sp is stored.  Arguments as sparsepr_sparse_attn and
+ * sparsepr_correct_ex (corr_g may be NULL: g = 0); lse may be NULL.
+ * For bf16 inputs with rank <= 16 the correction runs in the attention
+ * epilogue (exact fp32 products); otherwise the call keeps O_sp in its
+ * workspace and runs the correction kernel after the attention.
+ * Workspace: sparsepr_workspace_bytes(SPARSEPR_CALL_SPARSE_ATTN_CORRECT,
+ * dims, m, rank).
+ */
+int32_t sparsepr_sparse_attn_correct(const sparsepr_dims* dims /* host */, int32_t m,
+                                     int32_t rank, const int32_t* offsets_q,
+                                     const int32_t* offsets_kv, const int32_t* cell_rowptr,
+                                     const int32_t* cell_col, const void* q_g, const void* k_g,
+                                     const void* v_g, const int32_t* v_shift,
+                                     float softmax_scale, const int32_t* perm_q,
+                                     const int32_t* probe_tokens, const float* o_probe_dense,
+                                     const float* corr_a, const float* corr_psi_t,
+                                     const float* corr_c, const float* corr_g, void* out,
+                                     int32_t out_dtype, int64_t out_stride_head,
+                                     int64_t out_stride_tok, float* lse, void* ws,
+                                     size_t ws_bytes, hipStream_t stream);
 
 /*
  * Partition step before S1: response-coupled partitioning.  (SparsePR paper

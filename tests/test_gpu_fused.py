@@ -1,0 +1,92 @@
+"""GPU parity of the probe-first order of a call (SparsePRCall(fused=True)):
+the probe fit runs before the attention, and sparsepr_sparse_attn_correct
+writes the corrected output in token order without storing O_sp (SparsePR
+paper App. A.1: the probe rows' sparse and dense outputs come from one pass
+over their keys, so the fit does not need O_sp).  Compared with the oracle
+like the usual order; the O_sp buffer is filled with NaN and never written."""
+import numpy as np
+import pytest
+
+import synthgen as sg
+from harness import compare_head, oracle_head, run_gpu, say, upload_arrays
+
+pytestmark = pytest.mark.gpu
+
+CASES = {
+    # bf16, rank <= 16: correction in the attention epilogue (4-, 8- and 12-wave items)
+    "d64_small": (sg.small_workload(name="fz64", heads=2, n=2500, head_dim=64, components=12,
+                                    kv_split=2, rho="0.3", seed=101), {}),
+    "d128_grid": (sg.small_workload(name="fz128", heads=3, n=3000, head_dim=128, components=16,
+                                    kv_split=4, grid=(3, 20, 50), rho="0.26", seed=102), {}),
+    "d128_items12": (sg.small_workload(name="fz12", heads=8, n=128 * 300, head_dim=128,
+                                       components=128, kv_split=4, rho="0.22", seed=103), {}),
+    "d64_items12": (sg.small_workload(name="fz12d64", heads=16, n=64 * 290, head_dim=64,
+                                      components=64, rho="0.3", seed=104), {}),
+    "bf16_out": (sg.small_workload(name="fzbf", heads=2, n=2000, head_dim=128, components=10,
+                                   rho="0.3", seed=105), {"out_dtype": "bf16"}),
+    "diagonal": (sg.small_workload(name="fzdiag", heads=2, n=2100, head_dim=128, components=12,
+                                   kv_split=2, rho="0.3", seed=106), {"estimator": "diagonal"}),
+    "rank0": (sg.small_workload(name="fzr0", heads=1, n=900, head_dim=64, components=7, m=33,
+                                r=0, rho="0.35", seed=107), {}),
+    # rank above 16 and fp32 inputs: O_sp in the workspace and the correction kernel
+    "rank_cap64": (sg.small_workload(name="fzcap", heads=1, n=900, head_dim=64, components=7,
+                                     m=20, r=64, rho="0.35", seed=108), {}),
+    "f32": (sg.small_workload(name="fzf32", heads=2, n=1500, head_dim=128, dtype="f32",
+                              components=12, kv_split=2, rho="0.3", seed=109), {}),
+}
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_fused_order(name):
+    w, kw = CASES[name]
+    say(f"[fused {name}] {w}")
+    data = sg.make_call(w)
+    est = kw.get("estimator", "full")
+    g = run_gpu(w, data, fused=True, **kw)
+    assert np.isnan(g["o_sp"]).all()
+    for h, hd in enumerate(data):
+        r = oracle_head(w, hd, estimator=est)
+        if kw.get("out_dtype") == "bf16":
+            # bf16 output: an RNE cast of a value within the fp32 bar
+            out = g["out"][h]
+            ref = r["out"]
+            rel = np.linalg.norm(out - ref) / np.linalg.norm(ref)
+            assert rel <= 2e-3 + 2 ** -8, rel
+            continue
+        errs = compare_head(w, g, h, r, hd=hd, fused=True)
+        say(f"[fused {name}] head {h}: {errs}")
+
+
+def test_fused_matches_usual_order():
+    # same inputs: the two orders agree to the tolerance of the path
+    w = sg.small_workload(name="fzcmp", heads=2, n=3000, head_dim=128, components=16,
+                          kv_split=2, rho="0.26", seed=110)
+    data = sg.make_call(w)
+    a = run_gpu(w, data, fused=False)
+    b = run_gpu(w, data, fused=True)
+    for key in ("perm_q", "cell_rowptr", "probe_tokens", "corr_c"):
+        assert np.array_equal(a[key], b[key]), key
+    for h in range(w.heads):
+        # cell_col holds capacity for every cell; only the routed prefix is written
+        used = int(a["cell_rowptr"][h][-1])
+        assert np.array_equal(a["cell_col"][h][:used], b["cell_col"][h][:used])
+    assert np.abs(a["lse"] - b["lse"]).max() < 1e-5
+    rel = np.linalg.norm(a["out"] - b["out"]) / np.linalg.norm(a["out"])
+    say(f"[fused vs usual] rel {rel:.2e}")
+    assert rel < 1e-4
+
+
+def test_fused_full_size_sampled():
+    w = sg.workload("wan")
+    arr = sg.make_call_arrays(w)
+    tensors = upload_arrays(w, arr)
+    del arr
+    from test_gpu_large import sample_rows
+    g = run_gpu(w, None, tensors=tensors, fetch_heads=[0, 39], fused=True)
+    pos = sg.position_code(w.grid, w.head_dim)
+    for j, h in enumerate([0, 39]):
+        hd = sg.make_head(w, h, pos=pos)
+        rows = sample_rows(hd["labels_q"], w.c_q, 1500, seed=4000 + h)
+        r = oracle_head(w, hd, rows=rows)
+        errs = compare_head(w, g, j, r, hd=hd, fused=True)
+        say(f"[fused wan] head {h}: {errs}")
