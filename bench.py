@@ -235,6 +235,9 @@ def main():
     ap.add_argument("--head-chunks", type=int, default=1,
                     help="split each call into this many head ranges on alternating streams "
                          "(layout and routing of one range overlap the attention of the last)")
+    ap.add_argument("--order", default="usual", choices=("usual", "fused"),
+                    help="usual: attention, probe fit on a side stream, then the correction "
+                         "kernel; fused: probe fit first, correction in the attention epilogue")
     ap.add_argument("--rcp-warm", action="store_true",
                     help="with a response-coupled workload: after a first call in the warm-up, "
                          "every step runs a later call from the previous call's state")
@@ -299,7 +302,7 @@ def main():
                            lam=w.lam, rho=w.rho, out_dtype=fb.BF16 if w.dtype == "bf16" else fb.F32,
                            feat_dim=rp["r_q"] if rcp else 0, estimator=args.estimator,
                            route_rule=args.route_rule, head_chunks=args.head_chunks,
-                           overlap=not args.serial)
+                           overlap=not args.serial, fused=args.order == "fused")
     part = None
     if rcp:
         part = fb.RcpPartition(w.heads, w.n, w.n, w.head_dim, dtype, w.c_q, w.c_k, **rp,
@@ -328,7 +331,8 @@ def main():
 
     # attention launches are bracketed with events on the stream they run on
     attn_events = []
-    orig_attend = call.attend
+    attn_name = "attend_correct" if call.fused else "attend"
+    orig_attend = getattr(call, attn_name)
 
     def timed_attend(stream=None, part=None):
         s = torch.cuda.current_stream() if stream is None else stream
@@ -341,7 +345,7 @@ def main():
     for _ in range(args.warmup):
         step(call)
     torch.cuda.synchronize()
-    call.attend = timed_attend
+    setattr(call, attn_name, timed_attend)
     attn_events.clear()
     rcp_events.clear()
     torch.cuda.synchronize()
@@ -366,10 +370,10 @@ def main():
         # kernel is timed on launches over all heads, back to back
         attn_events.clear()
         for _ in range(3):
-            call.attend()
+            getattr(call, attn_name)()
     torch.cuda.synchronize()
     attn_ms = sum(a.elapsed_time(b) for a, b in attn_events) / len(attn_events)
-    call.attend = orig_attend
+    setattr(call, attn_name, orig_attend)
     marks = [e_start] + step_marks + [e_end]
     per_call = sorted(a.elapsed_time(b) for a, b in zip(marks[:-1], marks[1:]))
     call_ms_median = per_call[len(per_call) // 2]
@@ -425,7 +429,10 @@ def main():
             "estimator": args.estimator,
             "route_rule": args.route_rule,
             "head_chunks": args.head_chunks,
-            "probe_fit": "main stream after the attention" if args.serial else "side stream",
+            "order": args.order,
+            "probe_fit": ("before the attention, correction in its epilogue"
+                          if args.order == "fused" else
+                          "main stream after the attention" if args.serial else "side stream"),
             "parallelism": "single GPU",
         },
         "executed_pair_tflops": round(call_tflops, 2),
@@ -489,7 +496,8 @@ def main():
     traffic = _traffic_from_profile(w.name)
     out["roofline"] = {
         "bound": "mfma",
-        "kernel": ("attn_bf16_kernel<%d, %d>" % (d, _item_waves(w.heads, w.n, w.c_q))
+        "kernel": ("attn_bf16_kernel<%d, %d%s>" % (d, _item_waves(w.heads, w.n, w.c_q),
+                                                    ", fused correction" if call.fused else "")
                    if w.dtype == "bf16" else "attn_f32_kernel<%d>" % d),
         "achieved": round(attn_tflops, 2),
         "peak": peak,

@@ -385,7 +385,8 @@ class _Heads:
                          d.q_stride_head, d.q_stride_tok, d.kv_stride_head, d.kv_stride_tok)
         for name in _PER_HEAD:
             setattr(self, name, getattr(call, name)[h0:h1])
-        self.ws_layout, self.ws_route, self.ws_attn, self.ws_probe = ws
+        self.ws_layout, self.ws_route, self.ws_attn, self.ws_probe = ws[:4]
+        self.ws_attn_correct = ws[4] if len(ws) > 4 else None
 
 
 class SparsePRCall:
@@ -459,22 +460,22 @@ class SparsePRCall:
         self.out = torch.empty(H, n_q, d, dtype=odt, device=dev)
         self._ex = bool(feat_dim) or self.estimator != EST_FULL
 
+        self.fused = bool(fused)
+
         def ws_set(dims):
             def ws(which):
                 nb = workspace_bytes(which, dims, m, rank)
                 return torch.empty(max(nb, 256), dtype=torch.uint8, device=dev)
-            return (ws(CALL_PARTITION_LAYOUT),
-                    ws(CALL_ROUTE_CELLS if self.route_rule == ROUTE_GLOBAL else CALL_ROUTE_CELLS_EX),
-                    ws(CALL_SPARSE_ATTN),
-                    ws(CALL_PROBE_FIT_EX if self._ex else CALL_PROBE_FIT))
+            wss = (ws(CALL_PARTITION_LAYOUT),
+                   ws(CALL_ROUTE_CELLS if self.route_rule == ROUTE_GLOBAL else CALL_ROUTE_CELLS_EX),
+                   ws(CALL_SPARSE_ATTN),
+                   ws(CALL_PROBE_FIT_EX if self._ex else CALL_PROBE_FIT))
+            if self.fused:
+                wss += (ws(CALL_SPARSE_ATTN_CORRECT),)
+            return wss
 
-        self.fused = bool(fused)
-        if self.fused and head_chunks != 1:
-            raise ValueError("the fused order runs whole calls (head_chunks=1)")
-        if self.fused:
-            nb = workspace_bytes(CALL_SPARSE_ATTN_CORRECT, self.dims, m, rank)
-            self.ws_attn_correct = torch.empty(max(nb, 256), dtype=torch.uint8, device=dev)
         self._whole = _Heads(self, 0, H, ws_set(self.dims))
+        self.ws_attn_correct = self._whole.ws_attn_correct
         self.ws_layout, self.ws_route, self.ws_attn, self.ws_probe = (
             self._whole.ws_layout, self._whole.ws_route, self._whole.ws_attn, self._whole.ws_probe)
         self.side = torch.cuda.Stream(device=dev) if overlap else None
@@ -562,21 +563,23 @@ class SparsePRCall:
                          p.o_probe_dense, p.corr_a, p.corr_psi_t, p.corr_c, p.out,
                          self.out_dtype, p.out.stride(0), p.out.stride(1), stream)
 
-    def attend_correct(self, stream=None):
+    def attend_correct(self, stream=None, part=None):
         """The attention with the correction in its epilogue (fused order)."""
-        p = self._whole
+        p = part or self._whole
         sparsepr_sparse_attn_correct(p.dims, self.m, self.rank, p.offsets_q, p.offsets_kv,
                                      p.cell_rowptr, p.cell_col, p.q_g, p.k_g, p.v_g, p.v_shift,
                                      self.scale, p.perm_q, p.probe_tokens, p.o_probe_dense,
                                      p.corr_a, p.corr_psi_t, p.corr_c,
                                      p.corr_g if self.estimator != EST_FULL else None, p.out,
                                      self.out_dtype, p.out.stride(0), p.out.stride(1), p.lse,
-                                     self.ws_attn_correct, stream)
+                                     p.ws_attn_correct, stream)
 
     def __call__(self, labels_q, labels_kv, q, k, v):
         """One whole attention call on the current stream (probe fit on the
         side stream when overlap is on).  Returns the output tensor."""
         if self.chunks is not None:
+            if self.fused:
+                return self._chunked_fused(labels_q, labels_kv, q, k, v)
             return self._chunked(labels_q, labels_kv, q, k, v)
         if self.fused:
             self.layout(labels_q, labels_kv, q, k, v)
@@ -617,6 +620,35 @@ class SparsePRCall:
     def replay(self):
         """Reruns the captured call (see `capture`); returns the output tensor."""
         self.graph.replay()
+        return self.out
+
+    def _chunked_fused(self, labels_q, labels_kv, q, k, v):
+        """Fused order over head ranges: layout and routing of every range on
+        the current stream, the probe fit of each range on the side stream as
+        soon as its routing is done, and the attention with the correction of
+        range i on stream_b (even i) or the current stream (odd i) once its
+        fit is done.  The fit of range i runs while later ranges are laid out
+        and routed or while earlier ranges are attended, and two attention
+        launches overlap each other's tails.  Attention launches on one
+        stream share a workspace set; the two streams use different sets."""
+        main = torch.cuda.current_stream()
+        side = self.side if self.side is not None else main
+        self.ev_start.record(main)
+        self.stream_b.wait_event(self.ev_start)
+        side.wait_event(self.ev_start)
+        for i, p in enumerate(self.chunks):
+            self.layout(labels_q, labels_kv, q, k, v, stream=main, part=p)
+            self.route(stream=main, part=p)
+            self.ev_routed_c[i].record(main)
+            side.wait_event(self.ev_routed_c[i])
+            self.probe_fit(stream=side, part=p)
+            self.ev_fit_c[i].record(side)
+        for i, p in enumerate(self.chunks):
+            s = self.stream_b if i % 2 == 0 else main
+            s.wait_event(self.ev_fit_c[i])
+            self.attend_correct(stream=s, part=p)
+        self.ev_b_done.record(self.stream_b)
+        main.wait_event(self.ev_b_done)
         return self.out
 
     def _chunked(self, labels_q, labels_kv, q, k, v):

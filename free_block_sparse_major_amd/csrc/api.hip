@@ -19,12 +19,22 @@ int32_t check_dims(const sparsepr_dims* d) {
   if (d->dtype != SPARSEPR_BF16 && d->dtype != SPARSEPR_F32) return SPARSEPR_ERR_UNSUPPORTED;
   if (d->c_q > SPARSEPR_MAX_GROUPS || d->c_k > SPARSEPR_MAX_GROUPS) return SPARSEPR_ERR_UNSUPPORTED;
   const int64_t es = int64_t(elem_bytes(d->dtype));
-  // rows are moved with 16-byte accesses
-  if (((d->q_stride_head * es) & 15) || ((d->q_stride_tok * es) & 15) ||
-      ((d->kv_stride_head * es) & 15) || ((d->kv_stride_tok * es) & 15))
+  // rows are moved with 16-byte accesses: strides in elements are multiples
+  // of 16 / es (tested without forming stride * es, which may overflow)
+  const int64_t align = 16 / es;
+  if ((d->q_stride_head % align) || (d->q_stride_tok % align) || (d->kv_stride_head % align) ||
+      (d->kv_stride_tok % align))
     return SPARSEPR_ERR_INVALID;
   if (d->q_stride_tok < d->head_dim || d->kv_stride_tok < d->head_dim ||
       d->q_stride_head < 0 || d->kv_stride_head < 0)
+    return SPARSEPR_ERR_INVALID;
+  // the byte extent of q and of k, v must be addressable with int64 offsets
+  auto extent_ok = [&](int64_t sh, int64_t st, int64_t n) {
+    const __int128 last = __int128(d->heads - 1) * sh + __int128(n - 1) * st + d->head_dim;
+    return last * es <= (__int128(1) << 62);
+  };
+  if (!extent_ok(d->q_stride_head, d->q_stride_tok, d->n_q) ||
+      !extent_ok(d->kv_stride_head, d->kv_stride_tok, d->n_k))
     return SPARSEPR_ERR_INVALID;
   // group-major tensors are indexed with 32-bit rows inside a head
   if (int64_t(d->c_q) * d->c_k > (int64_t(1) << 30)) return SPARSEPR_ERR_UNSUPPORTED;
@@ -33,6 +43,15 @@ int32_t check_dims(const sparsepr_dims* d) {
   if (int64_t(d->n_k) * d->head_dim * es >= (int64_t(1) << 32) ||
       int64_t(d->n_q) * d->head_dim * 4 >= (int64_t(1) << 32))
     return SPARSEPR_ERR_UNSUPPORTED;
+  return SPARSEPR_OK;
+}
+
+int32_t check_out_strides(const sparsepr_dims* d, int32_t out_dtype, int64_t sh, int64_t st) {
+  const int64_t es = out_dtype == SPARSEPR_BF16 ? 2 : 4;
+  const int64_t align = 16 / es;
+  if ((sh % align) || (st % align) || st < d->head_dim || sh < 0) return SPARSEPR_ERR_INVALID;
+  const __int128 last = __int128(d->heads - 1) * sh + __int128(d->n_q - 1) * st + d->head_dim;
+  if (last * es > (__int128(1) << 62)) return SPARSEPR_ERR_INVALID;
   return SPARSEPR_OK;
 }
 

@@ -49,6 +49,7 @@ struct AttnArgs {
   float* o;
   float* lse;
   const int32_t* tiles;  // [H*c_q + 1] exclusive prefix of per-group tile counts
+  const int2* items;     // launch order of the work items (h * c_q + a, tile), or null
   const int32_t* v_shift;  // [H] v_g holds fp16(v * 2^-v_shift) (bf16 path)
   int H, n_q, n_k, c_q, c_k;
   float scale_log2;      // softmax_scale * log2(e)
@@ -93,8 +94,102 @@ __global__ __launch_bounds__(1024) void tile_table_kernel(const int32_t* __restr
   if (threadIdx.x == 0) tiles[len] = int32_t(tot);
 }
 
-// Maps a launched block to (h, a, tile-in-group).  Blocks are dealt to the 8
-// XCDs round-robin by id.  The remap hands each XCD runs of kXcdRun
+// Longest-first order of the work items.  Block b orders the query groups
+// of head b (the last block those of the last two heads together) by
+// descending cost L_a * min(n_a, tq), L_a the length of the group's key
+// stream, ties by group index; the items of a group stay consecutive (tile
+// order) and heads keep their order, so the items in flight still cover
+// about one head's K/V, and the list ends with the shortest items of the last
+// two heads (largest-first list scheduling evens out the finishing times).
+// The list is indexed by block id.  Blocks are dealt to the 8 XCDs round-robin,
+// so XCD x runs positions x, x + 8, ...; positions 8..15 of every complete
+// 16-position window are reversed, so that no XCD always takes the larger
+// item of each consecutive 8 (the XCDs' shares of the sorted costs balance).
+constexpr int kOrderMax = 2 * SPARSEPR_MAX_GROUPS;
+__global__ __launch_bounds__(1024) void item_order_kernel(
+    const int32_t* __restrict__ off_q, const int32_t* __restrict__ off_k,
+    const int32_t* __restrict__ rowptr, const int32_t* __restrict__ col, int H, int c_q, int c_k,
+    int tq, const int32_t* __restrict__ tiles, int2* __restrict__ items) {
+  __shared__ unsigned long long key[kOrderMax];
+  __shared__ long long red[16];
+  const int h0 = blockIdx.x;
+  const int nh = (H >= 2 && h0 == H - 2) ? 2 : 1;
+  const int nent = nh * c_q;
+  for (int e = threadIdx.x; e < kOrderMax; e += blockDim.x) {
+    unsigned long long v = 0;   // padding sorts last
+    if (e < nent) {
+      const int h = h0 + e / c_q, a = e % c_q;
+      const int32_t* oq = off_q + (long long)h * (c_q + 1);
+      const int n = oq[a + 1] - oq[a];
+      long long cost = -1;     // empty group: no items, sorts after the others
+      if (n > 0) {
+        const int32_t* rp = rowptr + (long long)h * (c_q + 1);
+        const int32_t* cl = col + (long long)h * c_q * c_k;
+        const int32_t* ok = off_k + (long long)h * (c_k + 1);
+        long long L = 0;
+        for (int i = rp[a]; i < rp[a + 1]; ++i) L += ok[cl[i] + 1] - ok[cl[i]];
+        cost = L * (long long)(n < tq ? n : tq);
+      }
+      v = ((unsigned long long)(cost + 2) << 12) | (unsigned long long)(4095 - e);
+    }
+    key[e] = v;
+  }
+  __syncthreads();
+  // bitonic sort of the first N >= nent entries (the rest is padding), descending
+  int N = 64;
+  while (N < nent) N <<= 1;
+  for (int k = 2; k <= N; k <<= 1) {
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      for (int pr = threadIdx.x; pr < N / 2; pr += blockDim.x) {
+        const int i = (pr / j) * 2 * j + (pr % j), l = i + j;
+        const unsigned long long x = key[i], y = key[l];
+        const bool desc = (i & k) == 0;
+        if (desc ? (x < y) : (x > y)) {
+          key[i] = y;
+          key[l] = x;
+        }
+      }
+      __syncthreads();
+    }
+  }
+  // items per sorted entry, scanned in sorted order (two entries per thread)
+  auto entry_tiles = [&](int r, int& ent) {
+    ent = 4095 - int(key[r] & 4095ull);
+    if (ent >= nent) return 0;
+    const int h = h0 + ent / c_q, a = ent % c_q;
+    const int32_t* oq = off_q + (long long)h * (c_q + 1);
+    const int n = oq[a + 1] - oq[a];
+    return (n + tq - 1) / tq;
+  };
+  const int per = kOrderMax / blockDim.x;
+  int ent[kOrderMax / 1024 > 0 ? kOrderMax / 1024 : 1];
+  int cnt[kOrderMax / 1024 > 0 ? kOrderMax / 1024 : 1];
+  long long s = 0;
+  for (int j = 0; j < per; ++j) {
+    cnt[j] = entry_tiles(per * threadIdx.x + j, ent[j]);
+    s += cnt[j];
+  }
+  long long tot;
+  long long run = block_exclusive_scan(s, red, &tot) + tiles[(long long)h0 * c_q];
+  const long long total = tiles[(long long)H * c_q];
+  const long long full = total / 16 * 16;   // positions in complete 16-windows
+  for (int j = 0; j < per; ++j) {
+    if (cnt[j] > 0) {
+      const int h = h0 + ent[j] / c_q, a = ent[j] % c_q;
+      for (int t = 0; t < cnt[j]; ++t) {
+        long long pos = run + t;
+        if (pos < full && (pos & 8)) pos = (pos & ~7ll) + 7 - (pos & 7);
+        items[pos] = make_int2(h * c_q + a, t);
+      }
+    }
+    run += cnt[j];
+  }
+}
+
+// Maps a launched block to (h, a, tile-in-group).  With the ordered list (the
+// entry points with a workspace) the block id indexes it.  Otherwise (the
+// entry point without one) items go in (h, a, tile) order: blocks are dealt
+// to the 8 XCDs round-robin by id, and the remap hands each XCD runs of kXcdRun
 // consecutive work items (tiles of one query group, same K/V stream, share
 // that XCD's L2) while the 8 XCDs interleave run by run, so the blocks in
 // flight across the GPU cover about one head: its K/V (tens of MB) stays in
@@ -102,9 +197,18 @@ __global__ __launch_bounds__(1024) void tile_table_kernel(const int32_t* __restr
 constexpr int kXcdRun = 8;
 SPR_DEV bool locate_item(const AttnArgs& p, int& h, int& a, int& kt) {
   const int bid = blockIdx.x;
+  const int total = p.tiles[p.H * p.c_q];
+  if (p.items) {
+    // ordered list, indexed by block id (blocks past the end exit)
+    if (bid >= total) return false;
+    const int2 it = p.items[bid];
+    h = it.x / p.c_q;
+    a = it.x - h * p.c_q;
+    kt = it.y;
+    return true;
+  }
   const int x = bid & 7, j = bid >> 3;
   const int lid = (j / kXcdRun) * (8 * kXcdRun) + x * kXcdRun + (j % kXcdRun);
-  const int total = p.tiles[p.H * p.c_q];
   if (lid >= total) return false;
   int lo = 0, hi = p.H * p.c_q - 1;
   while (lo < hi) {
@@ -205,6 +309,147 @@ constexpr float kPSumCap = 256.f;
 // Maximum rank of the correction fused into the attention epilogue.
 constexpr int kFusedRank = 16;
 
+// ---------------------------------------------------------------------------
+// Correction in the attention epilogue, on bf16 MFMA with hi/lo operand
+// splits (x = hi + lo, both bf16; products hi*hi + hi*lo + lo*hi accumulated
+// in fp32: about 2^-16 relative per product, against 2^-8 for plain bf16).
+//   u^T (ranks x rows) = A^T (ranks x D) O^T (D x rows)   [K = D, in 16-dim steps]
+//   out^T = O^T + g * O^T + c + Psi (D x ranks) u^T        [K = 16 ranks]
+// The O^T accumulator of the attention is the B operand of the first product
+// as it stands: in 16-dim step s (d block s / 2, half t = s % 2) lane (n, g)
+// supplies registers 8 t .. 8 t + 7 of its block, i.e. dims
+//   dim(s, g, i) = 32 (s / 2) + 16 t + 8 (i / 4) + 4 g + i % 4,
+// and the A^T tile lane (rank rho, g) supplies A[dim(s, g, i)][rho] (zero for
+// rho >= 16).  The result u^T holds in lane (n, g) the ranks
+//   rho(g, i) = 8 (i / 4) + 4 g + i % 4,  i = 0..7
+// in registers 0..7 (8..15 are ranks 16..31, zero), which is the B operand of
+// the second product with that rank order; the Psi tile lane (dim, g)
+// supplies Psi^T[rho(g, i)][dim].  The second product's C layout is the O^T
+// layout, so the accumulator starts at o + g * o + c.
+// LDS (uint4 = 8 bf16):
+//   [0, 4D)      A^T: ((s * 2 + g) * 16 + rho) * 2 + {hi, lo}
+//   [4D, 8D)     Psi: ((db * 64) + lane) * 2 + {hi, lo}
+//   [8D, 8D+D/2) c[D] then g[D] as floats
+// ---------------------------------------------------------------------------
+SPR_DEV uint32_t bf16_hi_bits(float x) { return __float_as_uint(x) >> 16; }  // truncation
+SPR_DEV float bf16_hi_float(float x) { return __uint_as_float(__float_as_uint(x) & 0xffff0000u); }
+
+// 8 floats -> (hi, lo) bf16 octets
+SPR_DEV void split8(const float* x, uint4& hi, uint4& lo) {
+  uint32_t h[4], l[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const float x0 = x[2 * k], x1 = x[2 * k + 1];
+    h[k] = bf16_hi_bits(x0) | (bf16_hi_bits(x1) << 16);
+    l[k] = uint32_t(f32_to_bf16_rne(x0 - bf16_hi_float(x0))) |
+           (uint32_t(f32_to_bf16_rne(x1 - bf16_hi_float(x1))) << 16);
+  }
+  hi = make_uint4(h[0], h[1], h[2], h[3]);
+  lo = make_uint4(l[0], l[1], l[2], l[3]);
+}
+
+template <int D, int NT>
+SPR_DEV void stage_correction(const AttnArgs& p, int h, uint4* cs) {
+  const float* A = p.corr_a + (long long)h * D * p.rank;
+  const float* Pt = p.corr_psi_t + (long long)h * p.rank * D;
+  const int rank = p.rank;
+  // A^T tiles: D / 16 steps x 2 lane halves x 16 ranks
+  for (int e = threadIdx.x; e < 2 * D; e += NT) {
+    const int rho = e & 15, g = (e >> 4) & 1, st = e >> 5;
+    float x[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int dim = 32 * (st >> 1) + 16 * (st & 1) + 8 * (i >> 2) + 4 * g + (i & 3);
+      x[i] = rho < rank ? A[dim * rank + rho] : 0.f;
+    }
+    split8(x, cs[2 * e], cs[2 * e + 1]);
+  }
+  // Psi tiles: D / 32 blocks x 64 lanes
+  for (int e = threadIdx.x; e < 2 * D; e += NT) {
+    const int ln = e & 63, db = e >> 6, g = ln >> 5, dim = 32 * db + (ln & 31);
+    float x[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int rho = 8 * (i >> 2) + 4 * g + (i & 3);
+      x[i] = rho < rank ? Pt[rho * D + dim] : 0.f;
+    }
+    split8(x, cs[4 * D + 2 * e], cs[4 * D + 2 * e + 1]);
+  }
+  float* cg = reinterpret_cast<float*>(cs + 8 * D);
+  for (int j = threadIdx.x; j < D; j += NT) {
+    cg[j] = p.corr_c[(long long)h * D + j];
+    cg[D + j] = p.corr_g ? p.corr_g[(long long)h * D + j] : 0.f;
+  }
+}
+
+template <int D>
+SPR_DEV void fused_epilogue_mfma(const AttnArgs& p, const uint4* cs, const f32x16_t* oacc,
+                                 float inv, int lane, bool store, long long obase) {
+  constexpr int NDB = D / 32;
+  const int g = lane >> 5, rl = lane & 31;
+  const bool rank_lane = rl < 16;
+  f32x16_t uacc = {};
+#pragma unroll
+  for (int st = 0; st < D / 16; ++st) {
+    float x[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) x[i] = oacc[st >> 1][8 * (st & 1) + i] * inv;
+    uint4 bh, bl;
+    split8(x, bh, bl);
+    uint4 ah = make_uint4(0, 0, 0, 0), al = ah;
+    if (rank_lane) {
+      const int e = (st * 2 + g) * 16 + rl;
+      ah = cs[2 * e];
+      al = cs[2 * e + 1];
+    }
+    const bf16x8_t Ah = __builtin_bit_cast(bf16x8_t, ah), Al = __builtin_bit_cast(bf16x8_t, al);
+    const bf16x8_t Bh = __builtin_bit_cast(bf16x8_t, bh), Bl = __builtin_bit_cast(bf16x8_t, bl);
+    uacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(Ah, Bh, uacc, 0, 0, 0);
+    uacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(Ah, Bl, uacc, 0, 0, 0);
+    uacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(Al, Bh, uacc, 0, 0, 0);
+  }
+  float uv[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) uv[i] = uacc[i];
+  uint4 uh, ul;
+  split8(uv, uh, ul);
+  const bf16x8_t Uh = __builtin_bit_cast(bf16x8_t, uh), Ul = __builtin_bit_cast(bf16x8_t, ul);
+  const float* cvec = reinterpret_cast<const float*>(cs + 8 * D);
+  const float* gvec = cvec + D;
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) {
+    f32x16_t acc;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int j = 32 * db + 8 * (r >> 2) + 4 * g + (r & 3);
+      const float o = oacc[db][r] * inv;
+      acc[r] = fmaf(gvec[j], o, o + cvec[j]);
+    }
+    const int e = db * 64 + lane;
+    const bf16x8_t Ph = __builtin_bit_cast(bf16x8_t, cs[4 * D + 2 * e]);
+    const bf16x8_t Pl = __builtin_bit_cast(bf16x8_t, cs[4 * D + 2 * e + 1]);
+    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(Ph, Uh, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(Ph, Ul, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(Pl, Uh, acc, 0, 0, 0);
+    if (!store) continue;
+#pragma unroll
+    for (int i4 = 0; i4 < 4; ++i4) {
+      const int j0 = 32 * db + 8 * i4 + 4 * g;
+      if (p.out_bf16) {
+        uint2 pk;
+        pk.x = uint32_t(f32_to_bf16_rne(acc[4 * i4])) |
+               (uint32_t(f32_to_bf16_rne(acc[4 * i4 + 1])) << 16);
+        pk.y = uint32_t(f32_to_bf16_rne(acc[4 * i4 + 2])) |
+               (uint32_t(f32_to_bf16_rne(acc[4 * i4 + 3])) << 16);
+        *reinterpret_cast<uint2*>(static_cast<uint16_t*>(p.out) + obase + j0) = pk;
+      } else {
+        *reinterpret_cast<float4*>(static_cast<float*>(p.out) + obase + j0) =
+            make_float4(acc[4 * i4], acc[4 * i4 + 1], acc[4 * i4 + 2], acc[4 * i4 + 3]);
+      }
+    }
+  }
+}
+
 template <int D, int W, bool FUSED>
 __global__ __launch_bounds__(64 * W, W <= 4 ? 2 : 1) void attn_bf16_kernel(AttnArgs p) {
   constexpr int NT = 64 * W;          // threads
@@ -222,25 +467,13 @@ __global__ __launch_bounds__(64 * W, W <= 4 ? 2 : 1) void attn_bf16_kernel(AttnA
   __shared__ uint4 k_s0[KT / 8 * D], k_s1[KT / 8 * D];   // KT rows x D bf16
   __shared__ uint4 v_s0[KT / 8 * D], v_s1[KT / 8 * D];   // KT rows x D fp16
   __shared__ SmemCells sm;
-  // fused correction: A (D x kFusedRank), Psi^T (kFusedRank x D), c and g
-  __shared__ float corr_s[FUSED ? (2 * kFusedRank + 2) * D : 1];
+  // fused correction operands, staged as bf16 hi/lo pairs in MFMA operand
+  // order (see fused_epilogue_mfma): A^T tiles, Psi tiles, then c and g
+  __shared__ uint4 corr_s[FUSED ? 8 * D + D / 2 : 1];
 
   int h, a, kt;
   if (!locate_item(p, h, a, kt)) return;
-  if constexpr (FUSED) {
-    // rows of A padded to kFusedRank columns; unused columns read as 0
-    const float* A = p.corr_a + (long long)h * D * p.rank;
-    const float* Pt = p.corr_psi_t + (long long)h * p.rank * D;
-    for (int e = threadIdx.x; e < D * kFusedRank; e += NT) {
-      const int j = e / kFusedRank, c = e % kFusedRank;
-      corr_s[e] = c < p.rank ? A[j * p.rank + c] : 0.f;
-      corr_s[D * kFusedRank + e] = e < p.rank * D ? Pt[e] : 0.f;
-    }
-    for (int j = threadIdx.x; j < D; j += NT) {
-      corr_s[2 * D * kFusedRank + j] = p.corr_c[(long long)h * D + j];
-      corr_s[2 * D * kFusedRank + D + j] = p.corr_g ? p.corr_g[(long long)h * D + j] : 0.f;
-    }
-  }
+  if constexpr (FUSED) stage_correction<D, NT>(p, h, corr_s);
   // wave index as a scalar: everything derived from it (LDS destinations of the
   // tile loads, row ranges) stays in SGPRs
   const int tid = threadIdx.x, wid = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63,
@@ -671,64 +904,23 @@ __global__ __launch_bounds__(64 * W, W <= 4 ? 2 : 1) void attn_bf16_kernel(AttnA
     }
   }
 
+  if constexpr (FUSED) {
+    // the epilogue's MFMAs take operands from every lane: the whole wave runs
+    // them (rows past the end with o = 0) and only valid rows store
+    if (!wave_active) return;
+    const float l_tot = l_run + __shfl_xor(l_run, 32);
+    const float inv = row_valid ? __builtin_ldexpf(1.f, sv) / l_tot : 0.f;
+    const int tok = row_valid ? p.perm_q[(long long)h * p.n_q + r0 + qloc] : 0;
+    fused_epilogue_mfma<D>(p, corr_s, oacc, inv, lane, row_valid,
+                           (long long)h * p.out_sh + (long long)tok * p.out_st);
+    if (g == 0 && p.lse && row_valid)
+      p.lse[(long long)h * p.n_q + r0 + qloc] = (m_run * c2 + __log2f(l_tot)) * kLn2;
+    return;
+  }
   if (!row_valid) return;
   const float l_tot = l_run + __shfl_xor(l_run, 32);
   const float inv = __builtin_ldexpf(1.f, sv) / l_tot;
-  if constexpr (FUSED) {
-    // o (this lane: dims 32 db + 8 i4 + 4 g + 0..3), u = o A over both lanes
-    // of the row, then out = o + g * o + c + u Psi^T, written to the row's
-    // token (the correction step of the call, SparsePR review step (5))
-    float u[kFusedRank];
-#pragma unroll
-    for (int c = 0; c < kFusedRank; ++c) u[c] = 0.f;
-#pragma unroll
-    for (int db = 0; db < NDB; ++db)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int j = 32 * db + 8 * (r >> 2) + 4 * g + (r & 3);
-        const float o = oacc[db][r] * inv;
-        const float4* arow = reinterpret_cast<const float4*>(corr_s + j * kFusedRank);
-#pragma unroll
-        for (int c4 = 0; c4 < kFusedRank / 4; ++c4) {
-          const float4 av = arow[c4];
-          u[4 * c4 + 0] = fmaf(o, av.x, u[4 * c4 + 0]);
-          u[4 * c4 + 1] = fmaf(o, av.y, u[4 * c4 + 1]);
-          u[4 * c4 + 2] = fmaf(o, av.z, u[4 * c4 + 2]);
-          u[4 * c4 + 3] = fmaf(o, av.w, u[4 * c4 + 3]);
-        }
-      }
-#pragma unroll
-    for (int c = 0; c < kFusedRank; ++c) u[c] += __shfl_xor(u[c], 32);
-    const float* pst = corr_s + D * kFusedRank;
-    const float* cs = corr_s + 2 * D * kFusedRank;
-    const int tok = p.perm_q[(long long)h * p.n_q + r0 + qloc];
-    const long long obase = (long long)h * p.out_sh + (long long)tok * p.out_st;
-#pragma unroll
-    for (int db = 0; db < NDB; ++db)
-#pragma unroll
-      for (int i4 = 0; i4 < 4; ++i4) {
-        const int j0 = 32 * db + 8 * i4 + 4 * g;
-        float v[4];
-#pragma unroll
-        for (int jj = 0; jj < 4; ++jj) {
-          const int j = j0 + jj;
-          const float o = oacc[db][4 * i4 + jj] * inv;
-          float acc = fmaf(cs[D + j], o, o + cs[j]);
-#pragma unroll
-          for (int c = 0; c < kFusedRank; ++c) acc = fmaf(u[c], pst[c * D + j], acc);
-          v[jj] = acc;
-        }
-        if (p.out_bf16) {
-          uint2 pk;
-          pk.x = uint32_t(f32_to_bf16_rne(v[0])) | (uint32_t(f32_to_bf16_rne(v[1])) << 16);
-          pk.y = uint32_t(f32_to_bf16_rne(v[2])) | (uint32_t(f32_to_bf16_rne(v[3])) << 16);
-          *reinterpret_cast<uint2*>(static_cast<uint16_t*>(p.out) + obase + j0) = pk;
-        } else {
-          *reinterpret_cast<float4*>(static_cast<float*>(p.out) + obase + j0) =
-              make_float4(v[0], v[1], v[2], v[3]);
-        }
-      }
-  } else {
+  {
     float* orow = p.o + ((long long)h * p.n_q + r0 + qloc) * D;
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
@@ -994,9 +1186,16 @@ size_t attn_correct_ws_bytes(const sparsepr_dims* d, int rank) {
   return nb;
 }
 
+// work items of a launch: sum_a ceil(n_a / tq) <= N_q / tq + C_q per head
+long long item_bound(const sparsepr_dims* d) {
+  const int tq = rows_per_item(d);
+  return (long long)d->heads * ((d->n_q + tq - 1) / tq + d->c_q);
+}
+
 size_t attn_ws_bytes(const sparsepr_dims* d) {
   Carver cv(nullptr);
   cv.take<int32_t>(size_t(d->heads) * d->c_q + 1);
+  cv.take<int2>(size_t(item_bound(d)));
   const int sp = f32_splits(d);
   if (sp > 1) {
     cv.take<float>(size_t(sp) * d->heads * d->n_q * d->head_dim);
@@ -1029,13 +1228,22 @@ int32_t launch_attn(const sparsepr_dims* dims, const int32_t* offsets_q,
                     const int32_t* offsets_kv, const int32_t* cell_rowptr,
                     const int32_t* cell_col, const void* q_g, const void* k_g, const void* v_g,
                     const int32_t* v_shift, float softmax_scale, float* o_sp, float* lse,
-                    int32_t* tiles, int splits, float* part_o, float* part_ml,
+                    int32_t* tiles, int2* items, int splits, float* part_o, float* part_ml,
                     hipStream_t stream, const AttnArgs* fuse = nullptr) {
   const int tq = rows_per_item(dims);
   tile_table_kernel<<<1, 1024, 0, stream>>>(offsets_q, dims->heads, dims->c_q, tq, tiles);
   SPR_LAUNCH_CHECK();
-  // upper bound of work items: sum_a ceil(n_a / tq) <= N_q / tq + C_q per head
-  long long bound = (long long)dims->heads * ((dims->n_q + tq - 1) / tq + dims->c_q);
+  // the ordered list pays where compute units take many items each; with a
+  // few per unit (under 8 on average, by the bound) the natural order ran faster
+  if (item_bound(dims) < 8LL * 256) items = nullptr;
+  if (items) {
+    const unsigned nblk = unsigned(dims->heads >= 2 ? dims->heads - 1 : 1);
+    item_order_kernel<<<nblk, 1024, 0, stream>>>(offsets_q, offsets_kv, cell_rowptr, cell_col,
+                                                 dims->heads, dims->c_q, dims->c_k, tq, tiles,
+                                                 items);
+    SPR_LAUNCH_CHECK();
+  }
+  long long bound = item_bound(dims);
   bound = (bound + 8 * kXcdRun - 1) / (8 * kXcdRun) * (8 * kXcdRun);
   if (bound > 0x7fffffffLL) return SPARSEPR_ERR_UNSUPPORTED;
   AttnArgs a;
@@ -1049,6 +1257,7 @@ int32_t launch_attn(const sparsepr_dims* dims, const int32_t* offsets_q,
   a.o = o_sp;
   a.lse = lse;
   a.tiles = tiles;
+  a.items = items;
   a.v_shift = v_shift;
   a.H = dims->heads;
   a.n_q = dims->n_q;
@@ -1153,6 +1362,7 @@ extern "C" int32_t sparsepr_sparse_attn(const sparsepr_dims* dims, const int32_t
   if (!ws || ws_bytes < need) return SPARSEPR_ERR_WORKSPACE;
   Carver cv(ws);
   int32_t* tiles = cv.take<int32_t>(size_t(dims->heads) * dims->c_q + 1);
+  int2* items = cv.take<int2>(size_t(item_bound(dims)));
   const int sp = f32_splits(dims);
   float* part_o = nullptr;
   float* part_ml = nullptr;
@@ -1161,7 +1371,7 @@ extern "C" int32_t sparsepr_sparse_attn(const sparsepr_dims* dims, const int32_t
     part_ml = cv.take<float>(size_t(sp) * dims->heads * dims->n_q * 2);
   }
   return launch_attn(dims, offsets_q, offsets_kv, cell_rowptr, cell_col, q_g, k_g, v_g, v_shift,
-                     softmax_scale, o_sp, lse, tiles, sp, part_o, part_ml, stream);
+                     softmax_scale, o_sp, lse, tiles, items, sp, part_o, part_ml, stream);
 }
 
 extern "C" int32_t sparsepr_sparse_attn_noalloc(const sparsepr_dims* dims,
@@ -1180,7 +1390,7 @@ extern "C" int32_t sparsepr_sparse_attn_noalloc(const sparsepr_dims* dims,
   if (st != SPARSEPR_OK) return st;
   // no partial buffers: fp32 calls run unsplit here
   return launch_attn(dims, offsets_q, offsets_kv, cell_rowptr, cell_col, q_g, k_g, v_g, v_shift,
-                     softmax_scale, o_sp, lse, tiles, 1, nullptr, nullptr, stream);
+                     softmax_scale, o_sp, lse, tiles, nullptr, 1, nullptr, nullptr, stream);
 }
 
 extern "C" int32_t sparsepr_sparse_attn_correct(
@@ -1201,13 +1411,12 @@ extern "C" int32_t sparsepr_sparse_attn_correct(
   if (m < 1 || m > SPARSEPR_MAX_PROBES || rank < 0 || rank > SPARSEPR_MAX_RANK)
     return SPARSEPR_ERR_INVALID;
   if (out_dtype != SPARSEPR_BF16 && out_dtype != SPARSEPR_F32) return SPARSEPR_ERR_UNSUPPORTED;
-  const int64_t es = out_dtype == SPARSEPR_BF16 ? 2 : 4;
-  if (((out_stride_head * es) & 15) || ((out_stride_tok * es) & 15) ||
-      out_stride_tok < dims->head_dim || out_stride_head < 0)
+  if (check_out_strides(dims, out_dtype, out_stride_head, out_stride_tok) != SPARSEPR_OK)
     return SPARSEPR_ERR_INVALID;
   if (!ws || ws_bytes < attn_correct_ws_bytes(dims, rank)) return SPARSEPR_ERR_WORKSPACE;
   Carver cv(ws);
   int32_t* tiles = cv.take<int32_t>(size_t(dims->heads) * dims->c_q + 1);
+  int2* items = cv.take<int2>(size_t(item_bound(dims)));
   const int sp = f32_splits(dims);
   float* part_o = nullptr;
   float* part_ml = nullptr;
@@ -1228,7 +1437,8 @@ extern "C" int32_t sparsepr_sparse_attn_correct(
     fz.out_bf16 = out_dtype == SPARSEPR_BF16;
     fz.rank = rank;
     st = launch_attn(dims, offsets_q, offsets_kv, cell_rowptr, cell_col, q_g, k_g, v_g, v_shift,
-                     softmax_scale, nullptr, lse, tiles, sp, part_o, part_ml, stream, &fz);
+                     softmax_scale, nullptr, lse, tiles, items, sp, part_o, part_ml, stream,
+                     &fz);
     if (st != SPARSEPR_OK) return st;
     return launch_probe_overwrite(dims, m, probe_tokens, o_probe_dense, out,
                                   out_dtype == SPARSEPR_BF16, out_stride_head, out_stride_tok,
@@ -1238,7 +1448,7 @@ extern "C" int32_t sparsepr_sparse_attn_correct(
   size_t off = (attn_ws_bytes(dims) + 255) & ~size_t(255);
   float* o_sp = reinterpret_cast<float*>(static_cast<char*>(ws) + off);
   st = launch_attn(dims, offsets_q, offsets_kv, cell_rowptr, cell_col, q_g, k_g, v_g, v_shift,
-                   softmax_scale, o_sp, lse, tiles, sp, part_o, part_ml, stream);
+                   softmax_scale, o_sp, lse, tiles, items, sp, part_o, part_ml, stream);
   if (st != SPARSEPR_OK) return st;
   return sparsepr_correct_ex(dims, m, rank, perm_q, o_sp, probe_tokens, o_probe_dense, corr_a,
                              corr_psi_t, corr_c, corr_g, out, out_dtype, out_stride_head,

@@ -134,6 +134,11 @@ inline size_t elem_bytes(int dtype) { return dtype == SPARSEPR_BF16 ? 2 : 4; }
 
 // Validates the shape; returns a status code.
 int32_t check_dims(const sparsepr_dims* d);
+// Output strides (elements of out_dtype) of a [H][N_q][d] output: 16-byte
+// aligned rows, stride_tok >= d, stride_head >= 0, extent addressable with
+// int64 offsets.  SPARSEPR_OK or SPARSEPR_ERR_INVALID.
+int32_t check_out_strides(const sparsepr_dims* d, int32_t out_dtype, int64_t stride_head,
+                          int64_t stride_tok);
 // Probe rows take their dense output in the token-order output (S9).
 int32_t launch_probe_overwrite(const sparsepr_dims* d, int m, const int32_t* tokens,
                                const float* dense, void* out, int out_bf16, int64_t sh,

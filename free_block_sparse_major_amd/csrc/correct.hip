@@ -368,9 +368,7 @@ int32_t correct_impl(const sparsepr_dims* dims, int32_t m, int32_t rank, const i
       !out)
     return SPARSEPR_ERR_INVALID;
   if (out_dtype != SPARSEPR_BF16 && out_dtype != SPARSEPR_F32) return SPARSEPR_ERR_UNSUPPORTED;
-  const int64_t es = out_dtype == SPARSEPR_BF16 ? 2 : 4;
-  if (((out_stride_head * es) & 15) || ((out_stride_tok * es) & 15) ||
-      out_stride_tok < dims->head_dim || out_stride_head < 0)
+  if (check_out_strides(dims, out_dtype, out_stride_head, out_stride_tok) != SPARSEPR_OK)
     return SPARSEPR_ERR_INVALID;
   CorrArgs a;
   a.perm_q = perm_q;

@@ -80,7 +80,7 @@ def upload_arrays(w, arr):
 
 def run_gpu(w, heads_data, budget=None, rank=None, m=None, layout="hnd", out_dtype="f32",
             overlap=True, tensors=None, fetch_heads=None, probe_feat=None, estimator="full",
-            route_rule="global", fused=False):
+            route_rule="global", fused=False, head_chunks=1):
     """Runs the whole call.  Inputs come from per-head dicts (`heads_data`) or,
     for large shapes, from already uploaded `tensors` (heads_data is then
     None).  `fetch_heads` limits the per-head outputs copied back."""
@@ -102,7 +102,8 @@ def run_gpu(w, heads_data, budget=None, rank=None, m=None, layout="hnd", out_dty
                            out_dtype=fb.F32 if out_dtype == "f32" else fb.BF16,
                            q_strides=strides, kv_strides=strides, overlap=overlap,
                            feat_dim=0 if probe_feat is None else probe_feat.shape[-1],
-                           estimator=estimator, route_rule=route_rule, fused=fused)
+                           estimator=estimator, route_rule=route_rule, fused=fused,
+                           head_chunks=head_chunks)
     call.probe_feat = probe_feat
     if fused:
         # the fused order stores no O_sp: mark the buffer so a stray read shows

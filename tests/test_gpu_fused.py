@@ -76,6 +76,23 @@ def test_fused_matches_usual_order():
     assert rel < 1e-4
 
 
+@pytest.mark.parametrize("chunks", [2, 3])
+def test_fused_head_ranges(chunks):
+    # head ranges of the fused order (fits on the side stream, attention on two
+    # streams) give the whole fused call's result
+    w = sg.small_workload(name=f"fzchunk{chunks}", heads=5, n=2000, head_dim=128, components=12,
+                          kv_split=2, rho="0.3", seed=111)
+    data = sg.make_call(w)
+    a = run_gpu(w, data, fused=True)
+    b = run_gpu(w, data, fused=True, head_chunks=chunks)
+    for key in ("perm_q", "cell_rowptr", "probe_tokens", "corr_c", "corr_a", "lse", "out"):
+        assert np.array_equal(a[key], b[key]), key
+    for h, hd in enumerate(data):
+        r = oracle_head(w, hd)
+        errs = compare_head(w, b, h, r, hd=hd, fused=True)
+        say(f"[fused ranges {chunks}] head {h}: {errs}")
+
+
 def test_fused_full_size_sampled():
     w = sg.workload("wan")
     arr = sg.make_call_arrays(w)
