@@ -111,25 +111,48 @@ __global__ __launch_bounds__(1024) void item_order_kernel(
     const int32_t* __restrict__ rowptr, const int32_t* __restrict__ col, int H, int c_q, int c_k,
     int tq, const int32_t* __restrict__ tiles, int2* __restrict__ items) {
   __shared__ unsigned long long key[kOrderMax];
+  __shared__ int32_t len_g[kOrderMax];
+  __shared__ int32_t okl[SPARSEPR_MAX_GROUPS + 1], rpl[SPARSEPR_MAX_GROUPS + 1];
   __shared__ long long red[16];
   const int h0 = blockIdx.x;
   const int nh = (H >= 2 && h0 == H - 2) ? 2 : 1;
   const int nent = nh * c_q;
+  for (int e = threadIdx.x; e < kOrderMax; e += blockDim.x) len_g[e] = 0;
+  // key-stream length of every group: 16 lanes per group sum the K/V group
+  // sizes of its cells (contiguous in the cell table) and reduce
+  const int lane = threadIdx.x & 15, wv = threadIdx.x >> 4, nwv = blockDim.x >> 4;
+  for (int hh = 0; hh < nh; ++hh) {
+    const int h = h0 + hh;
+    __syncthreads();
+    for (int i = threadIdx.x; i <= c_k; i += blockDim.x) okl[i] = off_k[(long long)h * (c_k + 1) + i];
+    for (int i = threadIdx.x; i <= c_q; i += blockDim.x) rpl[i] = rowptr[(long long)h * (c_q + 1) + i];
+    __syncthreads();
+    const int32_t* cl = col + (long long)h * c_q * c_k;
+    for (int a = wv; a < c_q; a += nwv) {
+      const int c0 = rpl[a], c1 = rpl[a + 1];
+      int sum = 0;
+      for (int i = c0 + lane; i < c1; i += 4 * 16) {
+        int b[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) b[u] = i + 16 * u < c1 ? cl[i + 16 * u] : -1;
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+          if (b[u] >= 0) sum += okl[b[u] + 1] - okl[b[u]];
+      }
+#pragma unroll
+      for (int o = 8; o > 0; o >>= 1) sum += __shfl_xor(sum, o);
+      if (lane == 0) len_g[hh * c_q + a] = sum;
+    }
+  }
+  __syncthreads();
   for (int e = threadIdx.x; e < kOrderMax; e += blockDim.x) {
     unsigned long long v = 0;   // padding sorts last
     if (e < nent) {
       const int h = h0 + e / c_q, a = e % c_q;
       const int32_t* oq = off_q + (long long)h * (c_q + 1);
       const int n = oq[a + 1] - oq[a];
-      long long cost = -1;     // empty group: no items, sorts after the others
-      if (n > 0) {
-        const int32_t* rp = rowptr + (long long)h * (c_q + 1);
-        const int32_t* cl = col + (long long)h * c_q * c_k;
-        const int32_t* ok = off_k + (long long)h * (c_k + 1);
-        long long L = 0;
-        for (int i = rp[a]; i < rp[a + 1]; ++i) L += ok[cl[i] + 1] - ok[cl[i]];
-        cost = L * (long long)(n < tq ? n : tq);
-      }
+      // empty group: no items, sorts after the others
+      const long long cost = n > 0 ? (long long)len_g[e] * (long long)(n < tq ? n : tq) : -1;
       v = ((unsigned long long)(cost + 2) << 12) | (unsigned long long)(4095 - e);
     }
     key[e] = v;
