@@ -601,11 +601,14 @@ __global__ __launch_bounds__(64 * W, W <= 4 ? 2 : 1) void attn_bf16_kernel(AttnA
       const uint32_t lk = __builtin_amdgcn_readfirstlane(lds_addr_of(kdst));
       const uint32_t lv = __builtin_amdgcn_readfirstlane(lds_addr_of(vdst));
       const int p0 = t0 + blk * RPI;                       // first stream position
-      const int k0 = int(e[0] <= p0) + int(e[1] <= p0) + int(e[2] <= p0) + int(e[3] <= p0);
-      const int en = k0 == 0 ? e[0] : (k0 == 1 ? e[1] : (k0 == 2 ? e[2] : e[3]));
+      // the first window cell ending after p0 (cell ends increase): its end and
+      // row delta, chosen by scalar compare-and-select (e[3] if none does)
+      int en = e[3], d0 = dl[3];
+      if (p0 < e[2]) en = e[2], d0 = dl[2];
+      if (p0 < e[1]) en = e[1], d0 = dl[1];
+      if (p0 < e[0]) en = e[0], d0 = dl[0];
       if (p0 + RPI <= en) {
-        // all rows in cell tc + k0 (en <= L, so none past the stream's end)
-        const int d0 = k0 == 0 ? dl[0] : (k0 == 1 ? dl[1] : (k0 == 2 ? dl[2] : dl[3]));
+        // all rows in that cell (en <= L, so none past the stream's end)
         const uint32_t soff = uint32_t(p0 + d0) * RB;
         lds_dma16_s(krs, lk, voff_k, soff);
         lds_dma16_s(vrs, lv, voff_v, soff);

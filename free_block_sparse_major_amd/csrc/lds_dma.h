@@ -23,7 +23,7 @@ SPR_DEV v4i32_t head_rsrc(const void* base, uint32_t bytes) {
 // lds_addr + 16 * lane.  Issued in asm so the compiler's wait insertion does
 // not pair it with later LDS reads of the other stage; completion is awaited
 // explicitly (vmcnt) before the barrier that publishes the stage.  M0 (the
-// LDS base) is read at issue and restored afterwards.
+// LDS base) is declared clobbered, so the compiler restores it where it needs it.
 SPR_DEV void lds_dma16(const v4i32_t& rsrc_in, uint32_t lds_addr, uint32_t voff) {
   // the descriptor must sit in SGPRs (it is wave-uniform by construction)
   v4i32_t rsrc;
@@ -31,16 +31,13 @@ SPR_DEV void lds_dma16(const v4i32_t& rsrc_in, uint32_t lds_addr, uint32_t voff)
   rsrc[1] = __builtin_amdgcn_readfirstlane(rsrc_in[1]);
   rsrc[2] = __builtin_amdgcn_readfirstlane(rsrc_in[2]);
   rsrc[3] = __builtin_amdgcn_readfirstlane(rsrc_in[3]);
-  uint32_t saved;
   asm volatile(
-      "s_mov_b32 %0, m0\n\t"
-      "s_mov_b32 m0, %1\n\t"
+      "s_mov_b32 m0, %0\n\t"
       "s_nop 0\n\t"
-      "buffer_load_dwordx4 %2, %3, 0 offen lds\n\t"
-      "s_mov_b32 m0, %0"
-      : "=&s"(saved)
+      "buffer_load_dwordx4 %1, %2, 0 offen lds"
+      :
       : "s"(lds_addr), "v"(voff), "s"(rsrc)
-      : "memory");
+      : "memory", "m0");
 }
 
 // As lds_dma16, with a wave-uniform byte offset `soff` (SGPR) added to the
@@ -53,16 +50,13 @@ SPR_DEV void lds_dma16_s(const v4i32_t& rsrc_in, uint32_t lds_addr, uint32_t vof
   rsrc[2] = __builtin_amdgcn_readfirstlane(rsrc_in[2]);
   rsrc[3] = __builtin_amdgcn_readfirstlane(rsrc_in[3]);
   const uint32_t so = __builtin_amdgcn_readfirstlane(soff);
-  uint32_t saved;
   asm volatile(
-      "s_mov_b32 %0, m0\n\t"
-      "s_mov_b32 m0, %1\n\t"
+      "s_mov_b32 m0, %0\n\t"
       "s_nop 0\n\t"
-      "buffer_load_dwordx4 %2, %3, %4 offen lds\n\t"
-      "s_mov_b32 m0, %0"
-      : "=&s"(saved)
+      "buffer_load_dwordx4 %1, %2, %3 offen lds"
+      :
       : "s"(lds_addr), "v"(voff), "s"(rsrc), "s"(so)
-      : "memory");
+      : "memory", "m0");
 }
 
 SPR_DEV uint32_t lds_addr_of(const void* p) {
