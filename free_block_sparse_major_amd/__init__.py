@@ -396,7 +396,8 @@ class SparsePRCall:
     (bf16 or f32, or any layout with contiguous last dim given via strides),
     labels int32 [H][N].  Outputs stay resident on the device.
 
-    head_chunks > 1 splits a call into that many ranges of heads, issued on
+    head_chunks > 1 (or a list of head counts) splits a call into that many
+    ranges of heads, issued on
     two alternating streams (with the probe fits on a third), so that the
     layout and routing of one range run while the attention of the previous
     one does; every head is computed exactly as in a whole call.
@@ -483,9 +484,19 @@ class SparsePRCall:
         self.ev_fit = torch.cuda.Event()
         # head ranges of a chunked call: two workspace sets, used alternately
         self.chunks = None
-        k = max(1, min(int(head_chunks), H))
-        if k > 1:
+        if isinstance(head_chunks, (list, tuple)):
+            # explicit head counts per range, in order
+            sizes = [int(x) for x in head_chunks]
+            if any(x < 1 for x in sizes) or sum(sizes) != H:
+                raise ValueError("head_chunks counts must be positive and sum to the heads")
+            k = len(sizes)
+            bounds = [0]
+            for x in sizes:
+                bounds.append(bounds[-1] + x)
+        else:
+            k = max(1, min(int(head_chunks), H))
             bounds = [H * i // k for i in range(k + 1)]
+        if k > 1:
             hc = max(b - a for a, b in zip(bounds, bounds[1:]))
             cdims = make_dims(hc, n_q, n_k, head_dim, dtype, c_q, c_k, q_strides, kv_strides)
             sets = (ws_set(cdims), ws_set(cdims))

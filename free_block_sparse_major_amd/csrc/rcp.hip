@@ -681,12 +681,15 @@ __global__ __launch_bounds__(256) void kmeans_update_kernel(
   store_center<RP>(h, c, C, v, cent, chi, clo, cnorm);
 }
 
-// Assignment: label = argmin_c |c|^2 - 2 x.c, ties to the smaller c.  Block =
-// kAssignWaves waves x 32 rows; centres pass through LDS 128 at a time (rows
-// padded by 16 bytes, so the 16 rows read by one 16-lane group hit distinct
-// banks), so each centre tile read from L2 serves 32 kAssignWaves rows.
-// S^T tile = C_tile X^T on v_mfma_f32_32x32x16_bf16: lane l owns row l % 32
-// and 16 centres of each 32-centre block.
+// Assignment: label = argmin_c |c|^2 - 2 x.c = argmax_c x.c - |c|^2 / 2, ties
+// to the smaller c.  Block = kAssignWaves waves x 32 rows; centres pass
+// through LDS 128 at a time (rows padded by 16 bytes, so the 16 rows read by
+// one 16-lane group hit distinct banks), so each centre tile read from L2
+// serves 32 kAssignWaves rows.  S^T tile = C_tile X^T on
+// v_mfma_f32_32x32x16_bf16: lane l owns row l % 32 and 16 centres of each
+// 32-centre block.  The accumulator starts at -|c|^2 / 2 (-inf past the last
+// centre), so the products land on the score itself and the argmax needs
+// one compare per centre.
 constexpr int kCenterTile = 128;
 constexpr int kAssignWaves = 8;
 template <int RP>
@@ -699,7 +702,7 @@ __global__ __launch_bounds__(64 * kAssignWaves) void kmeans_assign_kernel(
   const int nl = lane & 31, g = lane >> 5;
   __shared__ __attribute__((aligned(16))) uint16_t sh[kCenterTile * LD];
   __shared__ __attribute__((aligned(16))) uint16_t sl[kCenterTile * LD];
-  __shared__ float sn[kCenterTile];
+  __shared__ __attribute__((aligned(16))) float sn[kCenterTile];
   constexpr int NT = 64 * kAssignWaves;
   const int row = blockIdx.x * (32 * kAssignWaves) + wid * 32 + nl;
   bf16x8_t bh[NS], bl[NS];
@@ -715,8 +718,8 @@ __global__ __launch_bounds__(64 * kAssignWaves) void kmeans_assign_kernel(
       bl[s] = __builtin_bit_cast(bf16x8_t, b);
     }
   }
-  float best = __builtin_huge_valf();
-  int bi = 0;   // a valid label even if no candidate compares below +inf (NaN input)
+  float best = -__builtin_huge_valf();
+  int bi = 0;   // a valid label even if no candidate compares above -inf (NaN input)
   const uint16_t* ch = chi + (long long)h * C * RP;
   const uint16_t* cl = clo + (long long)h * C * RP;
   const float* cn = cnorm + (long long)h * C;
@@ -732,12 +735,23 @@ __global__ __launch_bounds__(64 * kAssignWaves) void kmeans_assign_kernel(
       *reinterpret_cast<uint4*>(sh + cc * LD + 8 * ch8) = a;
       *reinterpret_cast<uint4*>(sl + cc * LD + 8 * ch8) = b;
     }
-    for (int e = tid; e < kCenterTile; e += NT) sn[e] = t0 + e < C ? cn[t0 + e] : 0.f;
+    for (int e = tid; e < kCenterTile; e += NT)
+      sn[e] = t0 + e < C ? -0.5f * cn[t0 + e] : -__builtin_huge_valf();
     __syncthreads();
 #pragma unroll 1
     for (int j = 0; j < kCenterTile / 32; ++j) {
       if (t0 + 32 * j >= C) break;
-      f32x16_t acc = f32x16_t{};
+      // accumulator in the C layout: register 4 q + r holds centre
+      // 32 j + 8 q + 4 g + r, i.e. four consecutive scores per q
+      f32x16_t acc;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const float4 v4 = *reinterpret_cast<const float4*>(sn + 32 * j + 8 * q + 4 * g);
+        acc[4 * q] = v4.x;
+        acc[4 * q + 1] = v4.y;
+        acc[4 * q + 2] = v4.z;
+        acc[4 * q + 3] = v4.w;
+      }
       const int crow = 32 * j + nl;
 #pragma unroll
       for (int s = 0; s < NS; ++s) {
@@ -751,11 +765,9 @@ __global__ __launch_bounds__(64 * kAssignWaves) void kmeans_assign_kernel(
       }
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        const int cc = 32 * j + 8 * (i >> 2) + 4 * g + (i & 3);
-        const float v = fmaf(-2.f, acc[i], sn[cc]);
-        if (t0 + cc < C && v < best) {
-          best = v;
-          bi = t0 + cc;
+        if (acc[i] > best) {
+          best = acc[i];
+          bi = t0 + 32 * j + 8 * (i >> 2) + 4 * g + (i & 3);
         }
       }
     }
@@ -763,7 +775,7 @@ __global__ __launch_bounds__(64 * kAssignWaves) void kmeans_assign_kernel(
   // the two lanes of a row hold interleaved centre subsets
   const float ob = __shfl_xor(best, 32);
   const int oi = __shfl_xor(bi, 32);
-  if (ob < best || (ob == best && oi < bi)) {
+  if (ob > best || (ob == best && oi < bi)) {
     best = ob;
     bi = oi;
   }
