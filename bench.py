@@ -232,14 +232,16 @@ def main():
     ap.add_argument("--route-rule", default="global", choices=("global", "per_group"),
                     help="cell selection: one executed-pair budget per head (default) or a "
                          "key-token budget per query group")
-    ap.add_argument("--head-chunks", type=int, default=1,
+    ap.add_argument("--head-chunks", type=lambda x: [int(v) for v in x.split(",")] if "," in x
+                    else int(x), default=1,
                     help="split each call into this many head ranges on alternating streams "
                          "(layout and routing of one range overlap the attention of the last)")
     ap.add_argument("--order", default="auto", choices=("auto", "usual", "fused"),
                     help="usual: attention, probe fit on a side stream, then the correction "
                          "kernel; fused: probe fit first, correction in the attention epilogue; "
-                         "auto: fused over two head ranges for bf16 calls of 16 heads or more "
-                         "(measured faster there), usual otherwise")
+                         "auto: fused over two head ranges (a quarter of the heads, then the "
+                         "rest) for bf16 calls of 16 heads or more (measured faster there), "
+                         "usual otherwise")
     ap.add_argument("--rcp-warm", action="store_true",
                     help="with a response-coupled workload: after a first call in the warm-up, "
                          "every step runs a later call from the previous call's state")
@@ -290,7 +292,9 @@ def main():
         big = w.dtype == "bf16" and w.heads >= 16 and w.r <= 16
         args.order = "fused" if big else "usual"
         if big and args.head_chunks == 1:
-            args.head_chunks = 2
+            # a quarter of the heads first: its probe fit is short and its
+            # attention starts early; the rest are fitted meanwhile
+            args.head_chunks = [w.heads // 4, w.heads - w.heads // 4]
     t0 = time.time()
     arr = sg.make_call_arrays(w)
     gen_s = time.time() - t0
@@ -513,7 +517,7 @@ def main():
         "traffic": traffic,
         "launch": ("all heads, inside the timed calls" if call.chunks is None else
                    "all heads, back to back after the timed calls (the calls run it in %d head "
-                   "ranges)" % args.head_chunks),
+                   "ranges)" % len(call.chunks)),
     }
     def own_dense_ms():
         # this library with one query group, one K/V group and every cell kept

@@ -160,18 +160,19 @@ __global__ __launch_bounds__(256) void query_metric_kernel(const float* __restri
 // ---------------------------------------------------------------------------
 // eigenvalue-weighted factor (cyclic Jacobi, fp32)
 // ---------------------------------------------------------------------------
-// Round-robin disjoint pairs, D/2 per round; thread t works on pair
-// t / (256 / (D/2)) and every (256 / (D/2))-th column.  A rotation is skipped
+// Round-robin disjoint pairs, D/2 per round; thread t of kEigThreads works on
+// pair t / (kEigThreads / (D/2)) and every (kEigThreads / (D/2))-th column.  A rotation is skipped
 // when |a_pq| is at the fp32 rounding level of the diagonal or of the trace;
 // the iteration stops after a sweep without rotations (at most 40 sweeps).
 // Output F[h] (D x rp, row-major): column c < r is the eigenvector of the
 // c-th largest eigenvalue (ties to the smaller index) times
 // sqrt(max(lambda, 0) / mean of the r retained); columns r..rp-1 are 0.
+constexpr int kEigThreads = 1024;
 template <int D>
-__global__ __launch_bounds__(256) void eig_factor_kernel(const float* __restrict__ m, int r, int rp,
+__global__ __launch_bounds__(kEigThreads) void eig_factor_kernel(const float* __restrict__ m, int r, int rp,
                                                          float* __restrict__ f,
                                                          float* __restrict__ basis) {
-  constexpr int NP = D / 2, PER = 256 / NP, NCOL = D / PER;
+  constexpr int NT = kEigThreads, NP = D / 2, PER = NT / NP, NCOL = D / PER;
   const int h = blockIdx.x, tid = threadIdx.x;
   // row stride D + 4: the row pass of 16 consecutive pairs x 4 columns per
   // wave touches 64 distinct banks
@@ -180,18 +181,18 @@ __global__ __launch_bounds__(256) void eig_factor_kernel(const float* __restrict
   __shared__ float rc[NP], rs[NP];
   __shared__ int32_t pr_p[NP], pr_q[NP];
   __shared__ int32_t order[D];
-  __shared__ float red[4];
+  __shared__ float red[NT / 64];
   __shared__ float s_scale;
   __shared__ int32_t sh_rot;
   const float* mh = m + (long long)h * D * D;
-  for (int e = tid; e < D * D; e += 256) {
+  for (int e = tid; e < D * D; e += NT) {
     const int i = e / D, j = e % D;
     E[i][j] = mh[e];
     U[i][j] = i == j ? 1.f : 0.f;
   }
   __syncthreads();
   float trp = 0.f;
-  for (int i = tid; i < D; i += 256) trp += fabsf(E[i][i]);
+  for (int i = tid; i < D; i += NT) trp += fabsf(E[i][i]);
   const float tr = block_sum(trp, red);
   const float abs_floor = 1e-30f + 4e-7f * tr;   // above the fp32 rounding noise of the trace
   const int pi = tid / PER, cj = tid % PER;
@@ -229,7 +230,7 @@ __global__ __launch_bounds__(256) void eig_factor_kernel(const float* __restrict
       const int p2 = pr_p[pi], q2 = pr_q[pi];
       // loads of 8 columns are issued before their stores (the compiler
       // cannot tell the addresses apart and would serialise each pair)
-      constexpr int CH = 8;
+      constexpr int CH = NCOL < 8 ? NCOL : 8;
       if (act)
         for (int l0 = 0; l0 < NCOL; l0 += CH) {   // rows: E <- J^T E
           float x1[CH], x2[CH];
@@ -291,7 +292,7 @@ __global__ __launch_bounds__(256) void eig_factor_kernel(const float* __restrict
   __syncthreads();
   const float mean = s_scale;
   float* fh = f + (long long)h * D * rp;
-  for (int e = tid; e < D * rp; e += 256) {
+  for (int e = tid; e < D * rp; e += NT) {
     const int j = e / rp, c = e % rp;
     float v = 0.f;
     if (c < r && mean > 0.f) {
@@ -303,7 +304,7 @@ __global__ __launch_bounds__(256) void eig_factor_kernel(const float* __restrict
   // the leading r eigenvectors themselves (basis[h] is D x r, row-major)
   if (basis) {
     float* bh = basis + (long long)h * D * r;
-    for (int e = tid; e < D * r; e += 256) bh[e] = U[e / r][order[e % r]];
+    for (int e = tid; e < D * r; e += NT) bh[e] = U[e / r][order[e % r]];
   }
 }
 
@@ -954,7 +955,7 @@ int32_t rcp_run(const sparsepr_dims* d, int m_s, int r_k, int r_q, int iters, co
     subspace_factor_kernel<D><<<H, 256, 0, stream>>>(w.metric, s.basis_k, r_k, rpk, 2, w.factor,
                                                      s.basis_k);
   else
-    eig_factor_kernel<D><<<H, 256, 0, stream>>>(w.metric, r_k, rpk, w.factor, s.basis_k);
+    eig_factor_kernel<D><<<H, kEigThreads, 0, stream>>>(w.metric, r_k, rpk, w.factor, s.basis_k);
   SPR_LAUNCH_CHECK();
   project_kernel<D><<<dim3((d->n_k + 128 * kProjTiles - 1) / (128 * kProjTiles), H), 256, 0, stream>>>(
       k, d->dtype, d->kv_stride_head, d->kv_stride_tok, d->n_k, w.factor, r_k, rpk, 0, w.xh, w.xl,
@@ -982,7 +983,7 @@ int32_t rcp_run(const sparsepr_dims* d, int m_s, int r_k, int r_q, int iters, co
     subspace_factor_kernel<D><<<H, 256, 0, stream>>>(w.metric, s.basis_q, r_q, rpq, 2, w.factor,
                                                      s.basis_q);
   else
-    eig_factor_kernel<D><<<H, 256, 0, stream>>>(w.metric, r_q, rpq, w.factor, s.basis_q);
+    eig_factor_kernel<D><<<H, kEigThreads, 0, stream>>>(w.metric, r_q, rpq, w.factor, s.basis_q);
   SPR_LAUNCH_CHECK();
   project_kernel<D><<<dim3((d->n_q + 128 * kProjTiles - 1) / (128 * kProjTiles), H), 256, 0, stream>>>(
       q, d->dtype, d->q_stride_head, d->q_stride_tok, d->n_q, w.factor, r_q, rpq, 1, w.xh, w.xl,
