@@ -202,6 +202,10 @@ def correction_quality(w, arrays, call, rcp_params=None, count=2048):
     out = {"head": 0, "rows": int(rows.size), "rho_exec": round(rep["rho_exec"], 6),
            "oracle": {"before": rep["before"], "after": rep["after"]}}
     if rcp_params is None:
+        if call.fused:
+            # the probe-first order stores no O_sp: the uncorrected rows come
+            # from the plain attention call on the same layout and cells
+            call.attend()
         perm = call.perm_q[0].cpu().numpy()
         inv = np.empty_like(perm)
         inv[perm] = np.arange(perm.size)
