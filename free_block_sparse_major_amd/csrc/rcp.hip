@@ -8,9 +8,10 @@
 // the feature rows; metric construction, centroid statistics and the
 // factorisation in FP32).  Per head:
 //   1. M_K = Q_s^T Q_s / M_s over M_s evenly spaced query rows (fp32).
-//   2. F_K: the leading r_K eigenvectors of M_K (cyclic Jacobi in fp32), each
-//      scaled by the square root of its eigenvalue over the mean of the r_K
-//      retained (eigenvalues clamped at 0).
+//   2. F_K: the leading r_K eigenvectors of M_K (fp64: Householder reduction
+//      to tridiagonal form, bisection, twisted factorisations; the pages do
+//      this step in FP32), each scaled by the square root of its eigenvalue
+//      over the mean of the r_K retained (eigenvalues clamped at 0).
 //   3. phi_K = k F_K, held as a bf16 pair (hi = bf16(phi), lo = bf16(phi - hi)).
 //   4. Lloyd's k-means with C_k centres started at the rows init_k: the
 //      assignment is an MFMA product |c|^2 - 2 x.c with x.c taken as
@@ -32,7 +33,10 @@
 // space (an empty group keeps its previous centroid; on a first call, its
 // initial row).
 
+#include <utility>
+
 #include "common.h"
+#include "f64_lanes.h"
 
 namespace spr {
 
@@ -157,154 +161,384 @@ __global__ __launch_bounds__(256) void query_metric_kernel(const float* __restri
   metric_store<D>(acc, 1.f / float(nnz > 0 ? nnz : 1), mq + (long long)h * D * D);
 }
 
-// ---------------------------------------------------------------------------
-// eigenvalue-weighted factor (cyclic Jacobi, fp32)
-// ---------------------------------------------------------------------------
-// Round-robin disjoint pairs, D/2 per round; thread t of kEigThreads works on
-// pair t / (kEigThreads / (D/2)) and every (kEigThreads / (D/2))-th column.  A rotation is skipped
-// when |a_pq| is at the fp32 rounding level of the diagonal or of the trace;
-// the iteration stops after a sweep without rotations (at most 40 sweeps).
-// Output F[h] (D x rp, row-major): column c < r is the eigenvector of the
-// c-th largest eigenvalue (ties to the smaller index) times
-// sqrt(max(lambda, 0) / mean of the r retained); columns r..rp-1 are 0.
 constexpr int kEigThreads = 1024;
+
+// ---------------------------------------------------------------------------
+// eigenvalue-weighted factor (fp64 tridiagonal eigensolver)
+// ---------------------------------------------------------------------------
+// The r leading eigenpairs of the symmetric D x D metric in fp64, one block of
+// kEigThreads threads per head (r <= 64):
+//   a. Householder reduction to tridiagonal form T = Q^T M Q.  Thread t keeps
+//      row t / RT, columns CW (t % RT) .. + CW - 1 of the matrix in
+//      registers.  Step k publishes column k through LDS, every wave forms
+//      v = x - alpha e_1 and beta = 2 / |v|^2 from it, the rows form
+//      p = beta A v, and the rank-2 update A -= v w^T + w v^T with
+//      w = p - (beta / 2)(p.v) v follows (two barriers per step).  v is kept
+//      in fp32 for the back-transformation;
+//   b. the r largest eigenvalues of T by multisection of Sturm counts (T
+//      normalised by its Gershgorin bound);
+//   c. each eigenvector of T from the twisted factorisation of T - lambda I
+//      (the twist where |gamma| is smallest).  If the vectors are not
+//      orthogonal to 1e-10 (close eigenvalues), they are re-orthogonalised
+//      in descending order, and a vector that loses more than half its norm
+//      is recomputed by inverse iteration kept orthogonal to the earlier ones;
+//   d. U = H_0 ... H_(D-3) Z, 16 lanes per vector (no barriers).
+// Output: F[h] (D x rp), column c < r = eigenvector of
+// the c-th largest eigenvalue times sqrt(max(lambda, 0) / mean of the r
+// retained); basis[h] (D x r) the eigenvectors themselves.
 template <int D>
-__global__ __launch_bounds__(kEigThreads) void eig_factor_kernel(const float* __restrict__ m, int r, int rp,
-                                                         float* __restrict__ f,
-                                                         float* __restrict__ basis) {
-  constexpr int NT = kEigThreads, NP = D / 2, PER = NT / NP, NCOL = D / PER;
-  const int h = blockIdx.x, tid = threadIdx.x;
-  // row stride D + 4: the row pass of 16 consecutive pairs x 4 columns per
-  // wave touches 64 distinct banks
-  __shared__ float E[D][D + 4];
-  __shared__ float U[D][D + 4];
-  __shared__ float rc[NP], rs[NP];
-  __shared__ int32_t pr_p[NP], pr_q[NP];
-  __shared__ int32_t order[D];
-  __shared__ float red[NT / 64];
-  __shared__ float s_scale;
-  __shared__ int32_t sh_rot;
+__global__ __launch_bounds__(kEigThreads) void eig_tri_kernel(const float* __restrict__ m, int r,
+                                                              int rp, float* __restrict__ f,
+                                                              float* __restrict__ basis) {
+  constexpr int NT = kEigThreads, RT = NT / D, CW = D / RT, NV = D * (D - 1) / 2;
+  constexpr int EPL = D / 64;   // vector elements per lane in one-wave steps
+  constexpr int TB = 32;        // targets per batch of the twisted factorisation
+  constexpr int GV = 16, RPV = D / GV;   // back-transformation: lanes and rows per vector
+  static_assert(NT == 1024 && (D == 64 || D == 128), "layout assumes 1024 threads");
+  const int h = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  __shared__ double colb[2][D], pbf[2][D];
+  __shared__ double td[D], te[D], tb[D], tdn[D], ten[D];
+  __shared__ double2 st2[D];
+  __shared__ double lamn[64];
+  __shared__ double red[NT / 64];
+  __shared__ double tbuf[D];
+  __shared__ float V[NV];
+  __shared__ double Z[64][D];
+  __shared__ double W[TB][D];
+  constexpr int n = D;
+  const int rr = tid / RT, qq = tid % RT, c0 = CW * qq;
   const float* mh = m + (long long)h * D * D;
-  for (int e = tid; e < D * D; e += NT) {
-    const int i = e / D, j = e % D;
-    E[i][j] = mh[e];
-    U[i][j] = i == j ? 1.f : 0.f;
+  double er[CW];
+#pragma unroll
+  for (int i = 0; i < CW; ++i) {
+    const int j = c0 + i;
+    er[i] = 0.5 * (double(mh[rr * D + j]) + double(mh[j * D + rr]));
+  }
+  auto voff = [](int k) { return k * (2 * D - k - 1) / 2; };
+  // a. Householder steps k = 0 .. n - 3 (register index KI compile-time)
+  auto hh_step = [&](auto ki_c, int kb) __attribute__((always_inline)) {
+    constexpr int KI = decltype(ki_c)::value;
+    const int k = CW * kb + KI;
+    const int par = KI & 1;
+    if (qq == kb) colb[par][rr] = er[KI];
+    __syncthreads();
+    double xs[EPL];
+    double ss = 0.0;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) {
+      const int idx = k + 1 + lane + 64 * e;
+      xs[e] = idx < n ? colb[par][idx] : 0.0;
+      ss = fma(xs[e], xs[e], ss);
+    }
+    const double nx2 = wave_sum_f64(ss);
+    const double x0 = colb[par][k + 1];
+    double alpha = 0.0, beta = 0.0;
+    if (nx2 > 0.0) {
+      const double nx = sqrt(nx2);
+      alpha = x0 > 0.0 ? -nx : nx;
+      beta = rcp64(nx2 - alpha * x0);   // 2 / |v|^2, |v|^2 = 2 (|x|^2 - alpha x0)
+    }
+    if (wid == 0) {
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) {
+        const int idx = k + 1 + lane + 64 * e;
+        if (idx < n) V[voff(k) + idx - k - 1] = float(idx == k + 1 ? xs[e] - alpha : xs[e]);
+      }
+      if (lane == 0) {
+        td[k] = colb[par][k];
+        te[k] = alpha;
+        tb[k] = beta;
+      }
+    }
+    double vj[CW];
+#pragma unroll
+    for (int i = 0; i < CW; ++i) {
+      const int j = c0 + i;
+      const double cj = colb[par][j];
+      vj[i] = j > k ? (j == k + 1 ? cj - alpha : cj) : 0.0;
+    }
+    if (beta != 0.0) {
+      double s2 = 0.0;
+#pragma unroll
+      for (int i = 0; i < CW; ++i) s2 = fma(er[i], vj[i], s2);
+      s2 = group_sum_f64<RT>(s2);
+      if (qq == 0 && rr > k) pbf[par][rr] = beta * s2;
+    }
+    __syncthreads();
+    if (beta != 0.0) {
+      double ps = 0.0;
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) {
+        const int idx = k + 1 + lane + 64 * e;
+        if (idx < n) ps = fma(pbf[par][idx], idx == k + 1 ? xs[e] - alpha : xs[e], ps);
+      }
+      const double K = 0.5 * beta * wave_sum_f64(ps);
+      if (rr > k) {
+        const double cr = colb[par][rr];
+        const double vr = rr == k + 1 ? cr - alpha : cr;
+        const double wr = pbf[par][rr] - K * vr;
+#pragma unroll
+        for (int i = 0; i < CW; ++i) {
+          const int j = c0 + i;
+          if (j > k) {
+            const double wj = pbf[par][j] - K * vj[i];
+            er[i] -= fma(vr, wj, wr * vj[i]);
+          }
+        }
+      }
+    }
+  };
+  for (int kb = 0; kb * CW < n - 2; ++kb) {
+    [&]<int... KI>(std::integer_sequence<int, KI...>) {
+      ((CW * kb + KI < n - 2 ? hh_step(std::integral_constant<int, KI>{}, kb) : void()), ...);
+    }(std::make_integer_sequence<int, CW>{});
+  }
+  // the last 2 x 2 block of T
+#pragma unroll
+  for (int i = 0; i < CW; ++i) {
+    const int j = c0 + i;
+    if (rr == n - 2 && j == n - 2) td[n - 2] = er[i];
+    if (rr == n - 1 && j == n - 2) te[n - 2] = er[i];
+    if (rr == n - 1 && j == n - 1) td[n - 1] = er[i];
+  }
+  if (tid == 0) {
+    te[n - 1] = 0.0;
+    tb[n - 2] = 0.0;
+    tb[n - 1] = 0.0;
   }
   __syncthreads();
-  float trp = 0.f;
-  for (int i = tid; i < D; i += NT) trp += fabsf(E[i][i]);
-  const float tr = block_sum(trp, red);
-  const float abs_floor = 1e-30f + 4e-7f * tr;   // above the fp32 rounding noise of the trace
-  const int pi = tid / PER, cj = tid % PER;
-  for (int sweep = 0; sweep < 40; ++sweep) {
-    if (tid == 0) sh_rot = 0;
-    for (int rnd = 0; rnd < D - 1; ++rnd) {
-      if (tid < NP) {
-        int pp, qq;
-        if (tid == 0) {
-          pp = D - 1;
-          qq = rnd;
-        } else {
-          pp = rnd + tid;
-          pp -= pp >= D - 1 ? D - 1 : 0;
-          qq = rnd - tid;
-          qq += qq < 0 ? D - 1 : 0;
+  const int cap = r < 64 ? (r < n ? r : n) : 64;
+  // b. Gershgorin bounds; T normalised by tn = max |bound|
+  double glo = __builtin_huge_val(), ghi = -__builtin_huge_val();
+  if (tid < n) {
+    const double rad = (tid > 0 ? fabs(te[tid - 1]) : 0.0) + (tid + 1 < n ? fabs(te[tid]) : 0.0);
+    glo = td[tid] - rad;
+    ghi = td[tid] + rad;
+  }
+  glo = block_min(glo, red);
+  ghi = block_max(ghi, red);
+  const double tn = fmax(fabs(glo), fabs(ghi));
+  if (tid < 64) lamn[tid] = 0.0;
+  if (!(tn > 0.0)) {
+    // zero metric: every eigenvalue 0, unit vectors
+    for (int e = tid; e < 64 * n; e += NT) Z[e / n][e % n] = (e / n) == (e % n) ? 1.0 : 0.0;
+    __syncthreads();
+  } else {
+    if (tid < n) {
+      const double inv = 1.0 / tn;
+      tdn[tid] = td[tid] * inv;
+      const double en = te[tid] * inv;
+      ten[tid] = en;
+      if (tid + 1 < n) st2[tid] = double2{td[tid + 1] * inv, en * en};
+    }
+    __syncthreads();
+    const double lo0 = glo / tn - 4.0 * kEps64, hi0 = ghi / tn + 4.0 * kEps64;
+    int P = 64;
+    while (P > 1 && P * cap > 256) P >>= 1;   // waves 0..3: one per SIMD
+    const int j = tid / P, s = tid % P;
+    const bool act = j < cap;
+    const int target = n - 1 - j;       // ascending index of the j-th largest
+    const double d0 = tdn[0];
+    double a = lo0, b = hi0;
+    for (int round = 0; round < 40; ++round) {
+      const bool done = !act || (b - a) <= 2.0 * kEps64 * fmax(fabs(a), fabs(b)) + 4.0 * kEps64;
+      if (__all(done)) break;
+      const double x1 = a + (b - a) * (double(2 * s + 1) / double(2 * P + 1));
+      const double x2 = a + (b - a) * (double(2 * s + 2) / double(2 * P + 1));
+      int c1 = 0, c2 = 0;
+      if (act) sturm_count2(d0, st2, n, x1, x2, c1, c2);
+      double na = c2 <= target ? x2 : (c1 <= target ? x1 : a);
+      double nb = c1 > target ? x1 : (c2 > target ? x2 : b);
+      for (int o = 1; o < P; o <<= 1) {
+        na = fmax(na, __shfl_xor(na, o));
+        nb = fmin(nb, __shfl_xor(nb, o));
+      }
+      a = na;
+      b = nb;
+    }
+    if (act && s == 0) lamn[j] = 0.5 * (a + b);
+    __syncthreads();
+    // c. twisted factorisation, one thread per target, TB targets at a time:
+    // forward pivots Dp (in W), ratios e_i / Dp_i (in Z); backward pivots Dm
+    // with gamma_i = Dp_i + Dm_i - (d_i - mu), ratios e_(i-1) / Dm_i (in W)
+    for (int b0 = 0; b0 < cap; b0 += TB) {
+      if (tid < TB && b0 + tid < cap) {
+        const int c = b0 + tid;
+        const double mu = lamn[c];
+        double* zr = Z[c];
+        double* wr = W[tid];
+        double dp = tdn[0] - mu;
+        wr[0] = dp;
+        for (int i = 1; i < n; ++i) {
+          const double2 s2 = st2[i - 1];
+          const double ri = rcp64(fabs(dp) < kTiny ? -kTiny : dp);
+          zr[i - 1] = ten[i - 1] * ri;
+          dp = (s2.x - mu) - s2.y * ri;
+          wr[i] = dp;
         }
-        float c = 1.f, sn = 0.f;
-        const float apq = E[pp][qq], app = E[pp][pp], aqq = E[qq][qq];
-        if (fabsf(apq) > 2e-7f * sqrtf(fabsf(app * aqq)) && fabsf(apq) > abs_floor) {
-          const float tau = (aqq - app) / (2.f * apq);
-          const float t = (tau >= 0.f ? 1.f : -1.f) / (fabsf(tau) + sqrtf(1.f + tau * tau));
-          c = 1.f / sqrtf(1.f + t * t);
-          sn = t * c;
-          sh_rot = 1;
+        double dm = tdn[n - 1] - mu;
+        double gbest = fabs(wr[n - 1]);
+        int rt = n - 1;
+        for (int i = n - 2; i >= 0; --i) {
+          const double ri = rcp64(fabs(dm) < kTiny ? -kTiny : dm);
+          const double dpi = wr[i];
+          const double ei = ten[i];
+          wr[i + 1] = ei * ri;
+          const double ai = tdn[i] - mu;
+          dm = ai - ei * ei * ri;
+          const double g = fabs(dpi + dm - ai);
+          if (g < gbest) {
+            gbest = g;
+            rt = i;
+          }
         }
-        rc[tid] = c;
-        rs[tid] = sn;
-        pr_p[tid] = pp;
-        pr_q[tid] = qq;
+        double z = 1.0, nrm = 1.0;
+        for (int i = rt - 1; i >= 0; --i) {
+          z = -zr[i] * z;
+          zr[i] = z;
+          nrm = fma(z, z, nrm);
+        }
+        zr[rt] = 1.0;
+        z = 1.0;
+        for (int i = rt + 1; i < n; ++i) {
+          z = -wr[i] * z;
+          zr[i] = z;
+          nrm = fma(z, z, nrm);
+        }
+        const double sc_n = 1.0 / sqrt(nrm);
+        for (int i = 0; i < n; ++i) zr[i] *= sc_n;
       }
       __syncthreads();
-      const bool act = rs[pi] != 0.f;
-      const float ci = rc[pi], si = rs[pi];
-      const int p2 = pr_p[pi], q2 = pr_q[pi];
-      // loads of 8 columns are issued before their stores (the compiler
-      // cannot tell the addresses apart and would serialise each pair)
-      constexpr int CH = NCOL < 8 ? NCOL : 8;
-      if (act)
-        for (int l0 = 0; l0 < NCOL; l0 += CH) {   // rows: E <- J^T E
-          float x1[CH], x2[CH];
-#pragma unroll
-          for (int u = 0; u < CH; ++u) {
-            const int j = cj + PER * (l0 + u);
-            x1[u] = E[p2][j];
-            x2[u] = E[q2][j];
-          }
-#pragma unroll
-          for (int u = 0; u < CH; ++u) {
-            const int j = cj + PER * (l0 + u);
-            E[p2][j] = ci * x1[u] - si * x2[u];
-            E[q2][j] = si * x1[u] + ci * x2[u];
-          }
-        }
-      __syncthreads();
-      if (act)
-        for (int l0 = 0; l0 < NCOL; l0 += CH) {   // columns: E <- E J, U <- U J
-          float x1[CH], x2[CH], u1[CH], u2[CH];
-#pragma unroll
-          for (int u = 0; u < CH; ++u) {
-            const int j = cj + PER * (l0 + u);
-            x1[u] = E[j][p2];
-            x2[u] = E[j][q2];
-            u1[u] = U[j][p2];
-            u2[u] = U[j][q2];
-          }
-#pragma unroll
-          for (int u = 0; u < CH; ++u) {
-            const int j = cj + PER * (l0 + u);
-            E[j][p2] = ci * x1[u] - si * x2[u];
-            E[j][q2] = si * x1[u] + ci * x2[u];
-            U[j][p2] = ci * u1[u] - si * u2[u];
-            U[j][q2] = si * u1[u] + ci * u2[u];
-          }
-        }
-      __syncthreads();
     }
-    if (!sh_rot) break;
+    // orthogonality of the computed vectors
+    double worst = 0.0;
+    for (int e = tid; e < cap * cap; e += NT) {
+      const int c1 = e / cap, c2 = e - c1 * cap;
+      if (c2 <= c1) {
+        double dot = 0.0;
+        for (int i = 0; i < n; ++i) dot = fma(Z[c1][i], Z[c2][i], dot);
+        const double dev = c2 == c1 ? fabs(dot - 1.0) : fabs(dot);
+        worst = dev == dev ? fmax(worst, dev) : 1.0;   // NaN counts as lost
+      }
+    }
+    worst = block_max(worst, red);
+    if (!(worst <= 1e-10) && wid == 0) {
+      // rare: classical Gram-Schmidt twice in descending order; a vector that
+      // loses more than half its norm is recomputed by inverse iteration
+      // (LU of T - mu I without pivoting, tiny pivots raised) kept orthogonal
+      // to the earlier ones.  Lanes hold EPL elements each.
+      for (int c = 0; c < cap; ++c) {
+        double zi[EPL];
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) {
+          zi[e] = Z[c][lane + 64 * e];
+          if (!(zi[e] == zi[e])) zi[e] = 0.0;
+        }
+        auto orth = [&]() {
+          for (int pass = 0; pass < 2; ++pass)
+            for (int c2 = 0; c2 < c; ++c2) {
+              double dd = 0.0;
+#pragma unroll
+              for (int e = 0; e < EPL; ++e) dd = fma(Z[c2][lane + 64 * e], zi[e], dd);
+              dd = wave_sum_f64(dd);
+#pragma unroll
+              for (int e = 0; e < EPL; ++e) zi[e] -= dd * Z[c2][lane + 64 * e];
+            }
+        };
+        auto norm = [&]() {
+          double q = 0.0;
+#pragma unroll
+          for (int e = 0; e < EPL; ++e) q = fma(zi[e], zi[e], q);
+          return sqrt(wave_sum_f64(q));
+        };
+        orth();
+        double nz = norm();
+        if (!(nz >= 0.5)) {
+          const double mu = lamn[c];
+#pragma unroll
+          for (int e = 0; e < EPL; ++e) {
+            uint32_t hsh = uint32_t((lane + 64 * e) * 2654435761u) ^ uint32_t((c + 1) * 40503u);
+            hsh ^= hsh >> 13;
+            hsh *= 0x5bd1e995u;
+            hsh ^= hsh >> 15;
+            zi[e] = double(int32_t(hsh & 0xffff) - 32768);
+          }
+          for (int it = 0; it < 4; ++it) {
+            orth();
+#pragma unroll
+            for (int e = 0; e < EPL; ++e) W[0][lane + 64 * e] = zi[e];
+            if (lane == 0) {
+              double* y = W[0];
+              double u_prev = tdn[0] - mu;
+              if (fabs(u_prev) < kEps64) u_prev = kEps64;
+              tbuf[0] = u_prev;
+              for (int i = 1; i < n; ++i) {
+                const double l = ten[i - 1] / u_prev;
+                double u = (tdn[i] - mu) - l * ten[i - 1];
+                if (fabs(u) < kEps64) u = kEps64;
+                y[i] -= l * y[i - 1];
+                tbuf[i] = u;
+                u_prev = u;
+              }
+              y[n - 1] /= tbuf[n - 1];
+              for (int i = n - 2; i >= 0; --i) y[i] = (y[i] - ten[i] * y[i + 1]) / tbuf[i];
+            }
+#pragma unroll
+            for (int e = 0; e < EPL; ++e) zi[e] = W[0][lane + 64 * e];
+            const double nn = norm();
+#pragma unroll
+            for (int e = 0; e < EPL; ++e) zi[e] = nn > 0.0 ? zi[e] / nn : 0.0;
+          }
+          orth();
+          nz = norm();
+        }
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) Z[c][lane + 64 * e] = nz > 0.0 ? zi[e] / nz : 0.0;
+      }
+    }
     __syncthreads();
   }
-  // rank of each eigenvalue: descending, ties to the smaller index
-  if (tid < D) {
-    const float li = E[tid][tid];
-    int rk = 0;
-    for (int j = 0; j < D; ++j) {
-      const float lj = E[j][j];
-      rk += (lj > li || (lj == li && j < tid)) ? 1 : 0;
+  // d. U = H_0 ... H_(n-3) Z: vector c on lanes GV c .. + GV - 1, rows g + GV u
+  const int c = tid / GV, g = tid % GV;
+  double z[RPV];
+#pragma unroll
+  for (int u = 0; u < RPV; ++u) z[u] = c < cap ? Z[c][g + GV * u] : 0.0;
+  if (tn > 0.0) {
+    for (int k = n - 3; k >= 0; --k) {
+      const double beta = tb[k];
+      if (beta == 0.0) continue;
+      const float* vk = V + voff(k) - (k + 1);   // vk[i] = v_i, i > k
+      double dot = 0.0;
+#pragma unroll
+      for (int u = 0; u < RPV; ++u) {
+        const int i = g + GV * u;
+        if (i > k) dot = fma(double(vk[i]), z[u], dot);
+      }
+      dot = beta * group_sum_f64<GV>(dot);
+#pragma unroll
+      for (int u = 0; u < RPV; ++u) {
+        const int i = g + GV * u;
+        if (i > k) z[u] = fma(-dot, double(vk[i]), z[u]);
+      }
     }
-    order[rk] = tid;
   }
-  __syncthreads();
-  if (tid == 0) {
-    float s = 0.f;
-    for (int c = 0; c < r; ++c) s += fmaxf(E[order[c]][order[c]], 0.f);
-    s_scale = s / float(r);
-  }
-  __syncthreads();
-  const float mean = s_scale;
+  // scale: mean of the r retained eigenvalues (clamped at 0)
+  double mean = 0.0;
+  for (int i = 0; i < cap; ++i) mean += fmax(lamn[i] * tn, 0.0);
+  mean /= double(r > 0 ? r : 1);
   float* fh = f + (long long)h * D * rp;
-  for (int e = tid; e < D * rp; e += NT) {
-    const int j = e / rp, c = e % rp;
-    float v = 0.f;
-    if (c < r && mean > 0.f) {
-      const int ii = order[c];
-      v = U[j][ii] * sqrtf(fmaxf(E[ii][ii], 0.f) / mean);
+  if (c < cap) {
+    const double sc = mean > 0.0 ? sqrt(fmax(lamn[c] * tn, 0.0) / mean) : 0.0;
+#pragma unroll
+    for (int u = 0; u < RPV; ++u) {
+      const int i = g + GV * u;
+      fh[i * rp + c] = float(z[u] * sc);
+      if (basis) basis[(long long)h * D * r + i * r + c] = float(z[u]);
     }
-    fh[e] = v;
   }
-  // the leading r eigenvectors themselves (basis[h] is D x r, row-major)
-  if (basis) {
-    float* bh = basis + (long long)h * D * r;
-    for (int e = tid; e < D * r; e += NT) bh[e] = U[e / r][order[e % r]];
+  for (int e = tid; e < D * rp; e += NT) {
+    const int cc = e % rp;
+    if (cc >= cap) fh[e] = 0.f;
   }
 }
 
@@ -955,7 +1189,7 @@ int32_t rcp_run(const sparsepr_dims* d, int m_s, int r_k, int r_q, int iters, co
     subspace_factor_kernel<D><<<H, 256, 0, stream>>>(w.metric, s.basis_k, r_k, rpk, 2, w.factor,
                                                      s.basis_k);
   else
-    eig_factor_kernel<D><<<H, kEigThreads, 0, stream>>>(w.metric, r_k, rpk, w.factor, s.basis_k);
+    eig_tri_kernel<D><<<H, kEigThreads, 0, stream>>>(w.metric, r_k, rpk, w.factor, s.basis_k);
   SPR_LAUNCH_CHECK();
   project_kernel<D><<<dim3((d->n_k + 128 * kProjTiles - 1) / (128 * kProjTiles), H), 256, 0, stream>>>(
       k, d->dtype, d->kv_stride_head, d->kv_stride_tok, d->n_k, w.factor, r_k, rpk, 0, w.xh, w.xl,
@@ -983,7 +1217,7 @@ int32_t rcp_run(const sparsepr_dims* d, int m_s, int r_k, int r_q, int iters, co
     subspace_factor_kernel<D><<<H, 256, 0, stream>>>(w.metric, s.basis_q, r_q, rpq, 2, w.factor,
                                                      s.basis_q);
   else
-    eig_factor_kernel<D><<<H, kEigThreads, 0, stream>>>(w.metric, r_q, rpq, w.factor, s.basis_q);
+    eig_tri_kernel<D><<<H, kEigThreads, 0, stream>>>(w.metric, r_q, rpq, w.factor, s.basis_q);
   SPR_LAUNCH_CHECK();
   project_kernel<D><<<dim3((d->n_q + 128 * kProjTiles - 1) / (128 * kProjTiles), H), 256, 0, stream>>>(
       q, d->dtype, d->q_stride_head, d->q_stride_tok, d->n_q, w.factor, r_q, rpq, 1, w.xh, w.xl,
