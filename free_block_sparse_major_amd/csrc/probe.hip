@@ -22,8 +22,9 @@
 // review's step (4)), unit-sum weights for the means and the feature scale
 // sqrt(var + 1e-6), unit-mean weights for the ridge; the ridge is solved in
 // its dual (M x M) form B = Xw^T (Xw Xw^T + lam I)^-1 Rw with Xw = W~^1/2
-// Xbar, Rw = W~^1/2 Rbar; the right singular vectors of Rw come from a
-// cyclic Jacobi eigensolve of Rw Rw^T; finally B is folded with the
+// Xbar, Rw = W~^1/2 Rbar; the right singular vectors of Rw come from an
+// fp64 symmetric eigensolve of Rw Rw^T (Householder reduction to tridiagonal
+// form, bisection, twisted factorisations); finally B is folded with the
 // projection into A = diag(1/s) B Psi and c = mu_R - (mu_x A) Psi^T.
 
 #include <type_traits>

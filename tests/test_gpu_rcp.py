@@ -81,7 +81,9 @@ def check_head(w, params, hd, h, part, ik, iq, full_oracle=True):
 
 
 def assert_stage_bounds(e):
-    # coordinates: fp32 metric, Jacobi factor and projection against fp64
+    # coordinates: fp32 metric, fp64 eigensolve of it, projection with F as a
+    # bf16 pair, against the fp64 oracle
+    print("stage errors", {k: v for k, v in e.items() if isinstance(v, float)})
     assert e["phi_k_gram"] < 2e-3, e
     assert e["phi_q_gram"] < 2e-3, e
     assert e["phi_q_rms"] < 1e-4, e
