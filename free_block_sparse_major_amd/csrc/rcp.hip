@@ -917,58 +917,68 @@ __global__ __launch_bounds__(256) void kmeans_update_kernel(
 }
 
 // Assignment: label = argmin_c |c|^2 - 2 x.c = argmax_c x.c - |c|^2 / 2, ties
-// to the smaller c.  Block = kAssignWaves waves x 32 rows; centres pass
-// through LDS 128 at a time (rows padded by 16 bytes, so the 16 rows read by
-// one 16-lane group hit distinct banks), so each centre tile read from L2
-// serves 32 kAssignWaves rows.  S^T tile = C_tile X^T on
-// v_mfma_f32_32x32x16_bf16: lane l owns row l % 32 and 16 centres of each
-// 32-centre block.  The accumulator starts at -|c|^2 / 2 (-inf past the last
-// centre), so the products land on the score itself and the argmax needs
-// one compare per centre.
+// to the smaller c.  Block = kAssignWaves waves, each wave two sets of 32
+// rows that share every centre fragment read from LDS (one LDS read feeds two
+// products).  Centres pass through LDS 128 at a time (rows padded by 16
+// bytes, so the 16 rows read by one 16-lane group hit distinct banks).
+// S^T tile = C_tile X^T on v_mfma_f32_32x32x16_bf16: lane l owns row l % 32
+// of each set and 16 centres of each 32-centre block.  The accumulator
+// starts at -|c|^2 / 2 (-inf past the last centre), so the products land on
+// the score itself and the argmax needs one compare per centre.
 constexpr int kCenterTile = 128;
 constexpr int kAssignWaves = 8;
+constexpr int kRowSets = 2;
+constexpr int kAssignRows = 32 * kRowSets * kAssignWaves;   // rows per block
 template <int RP>
-__global__ __launch_bounds__(64 * kAssignWaves) void kmeans_assign_kernel(
+__global__ __launch_bounds__(64 * kAssignWaves, 4) void kmeans_assign_kernel(
     const uint16_t* __restrict__ xh, const uint16_t* __restrict__ xl, int n,
     const uint16_t* __restrict__ chi, const uint16_t* __restrict__ clo,
     const float* __restrict__ cnorm, int C, int32_t* __restrict__ labels) {
   constexpr int NS = RP / 16, LD = RP + 8;   // k-steps, LDS row length (bf16)
+  constexpr int NT = 64 * kAssignWaves;
+  constexpr int CH = kCenterTile * (RP / 8);  // 16-byte chunks of one tile (hi or lo)
   const int h = blockIdx.y, tid = threadIdx.x, wid = tid >> 6, lane = tid & 63;
   const int nl = lane & 31, g = lane >> 5;
   __shared__ __attribute__((aligned(16))) uint16_t sh[kCenterTile * LD];
   __shared__ __attribute__((aligned(16))) uint16_t sl[kCenterTile * LD];
   __shared__ __attribute__((aligned(16))) float sn[kCenterTile];
-  constexpr int NT = 64 * kAssignWaves;
-  const int row = blockIdx.x * (32 * kAssignWaves) + wid * 32 + nl;
-  bf16x8_t bh[NS], bl[NS];
-  {
-    const long long o = ((long long)h * n + (row < n ? row : 0)) * RP;
+  int row[kRowSets];
+  bf16x8_t bh[kRowSets][NS], bl[kRowSets][NS];
+#pragma unroll
+  for (int u = 0; u < kRowSets; ++u) {
+    row[u] = blockIdx.x * kAssignRows + (wid * kRowSets + u) * 32 + nl;
+    const long long o = ((long long)h * n + (row[u] < n ? row[u] : 0)) * RP;
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
-      const uint4 a = row < n ? *reinterpret_cast<const uint4*>(xh + o + 16 * s + 8 * g)
-                              : make_uint4(0, 0, 0, 0);
-      const uint4 b = row < n ? *reinterpret_cast<const uint4*>(xl + o + 16 * s + 8 * g)
-                              : make_uint4(0, 0, 0, 0);
-      bh[s] = __builtin_bit_cast(bf16x8_t, a);
-      bl[s] = __builtin_bit_cast(bf16x8_t, b);
+      const uint4 a = row[u] < n ? *reinterpret_cast<const uint4*>(xh + o + 16 * s + 8 * g)
+                                 : make_uint4(0, 0, 0, 0);
+      const uint4 b = row[u] < n ? *reinterpret_cast<const uint4*>(xl + o + 16 * s + 8 * g)
+                                 : make_uint4(0, 0, 0, 0);
+      bh[u][s] = __builtin_bit_cast(bf16x8_t, a);
+      bl[u][s] = __builtin_bit_cast(bf16x8_t, b);
     }
   }
-  float best = -__builtin_huge_valf();
-  int bi = 0;   // a valid label even if no candidate compares above -inf (NaN input)
+  float best[kRowSets];
+  int bi[kRowSets];
+#pragma unroll
+  for (int u = 0; u < kRowSets; ++u) {
+    best[u] = -__builtin_huge_valf();
+    bi[u] = 0;   // a valid label even if no candidate compares above -inf (NaN input)
+  }
   const uint16_t* ch = chi + (long long)h * C * RP;
   const uint16_t* cl = clo + (long long)h * C * RP;
   const float* cn = cnorm + (long long)h * C;
   for (int t0 = 0; t0 < C; t0 += kCenterTile) {
-    __syncthreads();
-    for (int e = tid; e < kCenterTile * (RP / 8); e += NT) {
-      const int cc = e / (RP / 8), ch8 = e % (RP / 8), c = t0 + cc;
+    __syncthreads();   // every wave is done with the previous tile
+    for (int e = tid; e < CH; e += NT) {
+      const int cc = e / (RP / 8), c8 = e % (RP / 8), c = t0 + cc;
       uint4 a = make_uint4(0, 0, 0, 0), b = make_uint4(0, 0, 0, 0);
       if (c < C) {
-        a = *reinterpret_cast<const uint4*>(ch + (long long)c * RP + 8 * ch8);
-        b = *reinterpret_cast<const uint4*>(cl + (long long)c * RP + 8 * ch8);
+        a = *reinterpret_cast<const uint4*>(ch + (long long)c * RP + 8 * c8);
+        b = *reinterpret_cast<const uint4*>(cl + (long long)c * RP + 8 * c8);
       }
-      *reinterpret_cast<uint4*>(sh + cc * LD + 8 * ch8) = a;
-      *reinterpret_cast<uint4*>(sl + cc * LD + 8 * ch8) = b;
+      *reinterpret_cast<uint4*>(sh + cc * LD + 8 * c8) = a;
+      *reinterpret_cast<uint4*>(sl + cc * LD + 8 * c8) = b;
     }
     for (int e = tid; e < kCenterTile; e += NT)
       sn[e] = t0 + e < C ? -0.5f * cn[t0 + e] : -__builtin_huge_valf();
@@ -976,16 +986,19 @@ __global__ __launch_bounds__(64 * kAssignWaves) void kmeans_assign_kernel(
 #pragma unroll 1
     for (int j = 0; j < kCenterTile / 32; ++j) {
       if (t0 + 32 * j >= C) break;
-      // accumulator in the C layout: register 4 q + r holds centre
+      // accumulators in the C layout: register 4 q + r holds centre
       // 32 j + 8 q + 4 g + r, i.e. four consecutive scores per q
-      f32x16_t acc;
+      f32x16_t acc[kRowSets];
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const float4 v4 = *reinterpret_cast<const float4*>(sn + 32 * j + 8 * q + 4 * g);
-        acc[4 * q] = v4.x;
-        acc[4 * q + 1] = v4.y;
-        acc[4 * q + 2] = v4.z;
-        acc[4 * q + 3] = v4.w;
+#pragma unroll
+        for (int u = 0; u < kRowSets; ++u) {
+          acc[u][4 * q] = v4.x;
+          acc[u][4 * q + 1] = v4.y;
+          acc[u][4 * q + 2] = v4.z;
+          acc[u][4 * q + 3] = v4.w;
+        }
       }
       const int crow = 32 * j + nl;
 #pragma unroll
@@ -994,27 +1007,40 @@ __global__ __launch_bounds__(64 * kAssignWaves) void kmeans_assign_kernel(
             *reinterpret_cast<const bf16x8_t*>(sh + crow * LD + 16 * s + 8 * g);
         const bf16x8_t al =
             *reinterpret_cast<const bf16x8_t*>(sl + crow * LD + 16 * s + 8 * g);
-        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, bh[s], acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, bl[s], acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al, bh[s], acc, 0, 0, 0);
+        // per accumulator the same three products in the same order
+#pragma unroll
+        for (int u = 0; u < kRowSets; ++u)
+          acc[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, bh[u][s], acc[u], 0, 0, 0);
+#pragma unroll
+        for (int u = 0; u < kRowSets; ++u)
+          acc[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, bl[u][s], acc[u], 0, 0, 0);
+#pragma unroll
+        for (int u = 0; u < kRowSets; ++u)
+          acc[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al, bh[u][s], acc[u], 0, 0, 0);
       }
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        if (acc[i] > best) {
-          best = acc[i];
-          bi = t0 + 32 * j + 8 * (i >> 2) + 4 * g + (i & 3);
+      for (int u = 0; u < kRowSets; ++u) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          if (acc[u][i] > best[u]) {
+            best[u] = acc[u][i];
+            bi[u] = t0 + 32 * j + 8 * (i >> 2) + 4 * g + (i & 3);
+          }
         }
       }
     }
   }
-  // the two lanes of a row hold interleaved centre subsets
-  const float ob = __shfl_xor(best, 32);
-  const int oi = __shfl_xor(bi, 32);
-  if (ob > best || (ob == best && oi < bi)) {
-    best = ob;
-    bi = oi;
+#pragma unroll
+  for (int u = 0; u < kRowSets; ++u) {
+    // the two lanes of a row hold interleaved centre subsets
+    const float ob = __shfl_xor(best[u], 32);
+    const int oi = __shfl_xor(bi[u], 32);
+    if (ob > best[u] || (ob == best[u] && oi < bi[u])) {
+      best[u] = ob;
+      bi[u] = oi;
+    }
+    if (g == 0 && row[u] < n) labels[(long long)h * n + row[u]] = bi[u];
   }
-  if (g == 0 && row < n) labels[(long long)h * n + row] = bi;
 }
 
 // Mean of each group's rows in the original space (fp32).  One block per
@@ -1130,8 +1156,8 @@ int32_t run_kmeans(const RcpWs& w, int H, int n, int C, const int32_t* init, int
     SPR_LAUNCH_CHECK();
   }
   for (int it = 0; it < iters; ++it) {
-    kmeans_assign_kernel<RP><<<dim3((n + 32 * kAssignWaves - 1) / (32 * kAssignWaves), H),
-                               64 * kAssignWaves, 0, stream>>>(
+    kmeans_assign_kernel<RP><<<dim3((n + kAssignRows - 1) / kAssignRows, H), 64 * kAssignWaves,
+                               0, stream>>>(
         w.xh, w.xl, n, w.chi, w.clo, w.cnorm, C, labels);
     SPR_LAUNCH_CHECK();
     if (it + 1 == iters) break;   // the partition is the last assignment
