@@ -35,7 +35,7 @@ EXPORTED = (
     "sparsepr_status_string", "sparsepr_version", "sparsepr_rcp_partition",
     "sparsepr_probe_fit_ex", "sparsepr_correct_ex", "sparsepr_route_cells_ex",
     "sparsepr_rcp_partition_ex", "sparsepr_debug_check", "sparsepr_sparse_attn_noalloc",
-    "sparsepr_sparse_attn_correct",
+    "sparsepr_sparse_attn_correct", "sparsepr_probe_select", "sparsepr_probe_fit_selected",
 )
 
 
@@ -98,6 +98,11 @@ def load_library(path: str = LIB_PATH):
     lib.sparsepr_probe_fit_ex.argtypes = ([DP, I32, I32, D, I32] + [P] * 7 + [I32] + [P] * 4
                                           + [ctypes.c_float] + [P] * 8 + [P, SZ, P])
     lib.sparsepr_probe_fit_ex.restype = I32
+    lib.sparsepr_probe_select.argtypes = [DP, I32] + [P] * 4 + [I32] + [P] * 3 + [P, SZ, P]
+    lib.sparsepr_probe_select.restype = I32
+    lib.sparsepr_probe_fit_selected.argtypes = ([DP, I32, I32, D, I32] + [P] * 8
+                                                + [ctypes.c_float] + [P] * 7 + [P, SZ, P])
+    lib.sparsepr_probe_fit_selected.restype = I32
     lib.sparsepr_correct_ex.argtypes = [DP, I32, I32] + [P] * 9 + [I32, I64, I64, P, SZ, P]
     lib.sparsepr_correct_ex.restype = I32
     lib.sparsepr_route_cells_ex.argtypes = [DP, I32, P, P, P, P, I64, P, P, P, P, SZ, P]
@@ -263,6 +268,28 @@ def sparsepr_probe_fit_ex(dims, m, rank, lam, estimator, offsets_q, offsets_kv, 
         _ptr(o_probe_sparse), _ptr(corr_a), _ptr(corr_psi_t), _ptr(corr_c), _ptr(corr_g),
         _ptr(ws), ws.numel() * ws.element_size() if ws is not None else 0, _stream(stream))
     _check(st, "sparsepr_probe_fit_ex")
+
+
+def sparsepr_probe_select(dims, m, offsets_q, perm_q, centroid_q, probe_feat, feat_dim, q_g,
+                          probe_rows, probe_tokens, ws, stream=None):
+    st = load_library().sparsepr_probe_select(
+        ctypes.byref(dims), int(m), _ptr(offsets_q), _ptr(perm_q), _ptr(centroid_q),
+        _ptr(probe_feat), int(feat_dim), _ptr(q_g), _ptr(probe_rows), _ptr(probe_tokens),
+        _ptr(ws), ws.numel() * ws.element_size() if ws is not None else 0, _stream(stream))
+    _check(st, "sparsepr_probe_select")
+
+
+def sparsepr_probe_fit_selected(dims, m, rank, lam, estimator, offsets_q, offsets_kv,
+                                cell_rowptr, cell_col, q_g, k_g, v_g, v_shift, softmax_scale,
+                                probe_rows, o_probe_dense, o_probe_sparse, corr_a, corr_psi_t,
+                                corr_c, corr_g, ws, stream=None):
+    st = load_library().sparsepr_probe_fit_selected(
+        ctypes.byref(dims), int(m), int(rank), float(lam), int(estimator), _ptr(offsets_q),
+        _ptr(offsets_kv), _ptr(cell_rowptr), _ptr(cell_col), _ptr(q_g), _ptr(k_g), _ptr(v_g),
+        _ptr(v_shift), ctypes.c_float(softmax_scale), _ptr(probe_rows), _ptr(o_probe_dense),
+        _ptr(o_probe_sparse), _ptr(corr_a), _ptr(corr_psi_t), _ptr(corr_c), _ptr(corr_g),
+        _ptr(ws), ws.numel() * ws.element_size() if ws is not None else 0, _stream(stream))
+    _check(st, "sparsepr_probe_fit_selected")
 
 
 def sparsepr_correct_ex(dims, m, rank, perm_q, o_sp, probe_tokens, o_probe_dense, corr_a,
@@ -480,6 +507,7 @@ class SparsePRCall:
         self.ws_layout, self.ws_route, self.ws_attn, self.ws_probe = (
             self._whole.ws_layout, self._whole.ws_route, self._whole.ws_attn, self._whole.ws_probe)
         self.side = torch.cuda.Stream(device=dev) if overlap else None
+        self.ev_laid = torch.cuda.Event()
         self.ev_routed = torch.cuda.Event()
         self.ev_fit = torch.cuda.Event()
         # head ranges of a chunked call: two workspace sets, used alternately
@@ -505,6 +533,7 @@ class SparsePRCall:
             self.stream_b = torch.cuda.Stream(device=dev)
             self.ev_start = torch.cuda.Event()
             self.ev_b_done = torch.cuda.Event()
+            self.ev_laid_c = [torch.cuda.Event() for _ in self.chunks]
             self.ev_routed_c = [torch.cuda.Event() for _ in self.chunks]
             self.ev_fit_c = [torch.cuda.Event() for _ in self.chunks]
 
@@ -562,6 +591,26 @@ class SparsePRCall:
                            p.o_probe_sparse, p.corr_a, p.corr_psi_t, p.corr_c,
                            p.ws_probe, stream)
 
+    def probe_select(self, stream=None, part=None):
+        """The probe selection alone (reads only the layout's outputs)."""
+        p = part or self._whole
+        if self.feat_dim and self.probe_feat is None:
+            raise SparsePRError("probe_feat is not set")
+        feat = self.probe_feat[p.h0:p.h1] if self.feat_dim else None
+        sparsepr_probe_select(p.dims, self.m, p.offsets_q, p.perm_q, p.centroid_q, feat,
+                              self.feat_dim, p.q_g, p.probe_rows, p.probe_tokens, p.ws_probe,
+                              stream)
+
+    def probe_fit_selected(self, stream=None, part=None):
+        """Exact probe rows, merge and fit for the probes probe_select chose."""
+        p = part or self._whole
+        sparsepr_probe_fit_selected(p.dims, self.m, self.rank, self.lam, self.estimator,
+                                    p.offsets_q, p.offsets_kv, p.cell_rowptr, p.cell_col,
+                                    p.q_g, p.k_g, p.v_g, p.v_shift, self.scale, p.probe_rows,
+                                    p.o_probe_dense, p.o_probe_sparse, p.corr_a, p.corr_psi_t,
+                                    p.corr_c, p.corr_g if self.estimator != EST_FULL else None,
+                                    p.ws_probe, stream)
+
     def correct(self, stream=None, part=None):
         p = part or self._whole
         if self.estimator != EST_FULL:
@@ -586,31 +635,42 @@ class SparsePRCall:
                                      p.ws_attn_correct, stream)
 
     def __call__(self, labels_q, labels_kv, q, k, v):
-        """One whole attention call on the current stream (probe fit on the
-        side stream when overlap is on).  Returns the output tensor."""
+        """One whole attention call on the current stream.  With overlap on,
+        the probe selection runs on the side stream while the cells are
+        routed, and the rest of the probe fit beside the attention (usual
+        order) or before it (fused order).  Returns the output tensor."""
         if self.chunks is not None:
             if self.fused:
                 return self._chunked_fused(labels_q, labels_kv, q, k, v)
             return self._chunked(labels_q, labels_kv, q, k, v)
-        if self.fused:
-            self.layout(labels_q, labels_kv, q, k, v)
-            self.route()
-            self.probe_fit()
-            self.attend_correct()
-            return self.out
         main = torch.cuda.current_stream()
         self.layout(labels_q, labels_kv, q, k, v)
-        self.route()
-        if self.side is not None:
-            self.ev_routed.record(main)
-            self.side.wait_event(self.ev_routed)
-            self.probe_fit(self.side)
-            self.ev_fit.record(self.side)
-            self.attend()
-            main.wait_event(self.ev_fit)
-        else:
+        if self.side is None:
+            self.route()
+            if self.fused:
+                self.probe_fit()
+                self.attend_correct()
+                return self.out
             self.attend()
             self.probe_fit()
+            self.correct()
+            return self.out
+        # the probe selection runs on the side stream while the cells are
+        # routed; the rest of the fit once the routing is done
+        self.ev_laid.record(main)
+        self.side.wait_event(self.ev_laid)
+        self.probe_select(self.side)
+        self.route()
+        self.ev_routed.record(main)
+        self.side.wait_event(self.ev_routed)
+        self.probe_fit_selected(self.side)
+        self.ev_fit.record(self.side)
+        if self.fused:
+            main.wait_event(self.ev_fit)
+            self.attend_correct()
+            return self.out
+        self.attend()
+        main.wait_event(self.ev_fit)
         self.correct()
         return self.out
 
@@ -635,8 +695,9 @@ class SparsePRCall:
 
     def _chunked_fused(self, labels_q, labels_kv, q, k, v):
         """Fused order over head ranges: layout and routing of every range on
-        the current stream, the probe fit of each range on the side stream as
-        soon as its routing is done, and the attention with the correction of
+        the current stream, the probe selection of each range on the side
+        stream once it is laid out and the rest of its fit once it is routed,
+        and the attention with the correction of
         range i on stream_b (even i) or the current stream (odd i) once its
         fit is done.  The fit of range i runs while later ranges are laid out
         and routed or while earlier ranges are attended, and two attention
@@ -649,10 +710,18 @@ class SparsePRCall:
         side.wait_event(self.ev_start)
         for i, p in enumerate(self.chunks):
             self.layout(labels_q, labels_kv, q, k, v, stream=main, part=p)
-            self.route(stream=main, part=p)
-            self.ev_routed_c[i].record(main)
-            side.wait_event(self.ev_routed_c[i])
-            self.probe_fit(stream=side, part=p)
+            if side is main:
+                self.route(stream=main, part=p)
+                self.probe_fit(stream=main, part=p)
+            else:
+                # selection beside the routing, the rest of the fit after it
+                self.ev_laid_c[i].record(main)
+                side.wait_event(self.ev_laid_c[i])
+                self.probe_select(stream=side, part=p)
+                self.route(stream=main, part=p)
+                self.ev_routed_c[i].record(main)
+                side.wait_event(self.ev_routed_c[i])
+                self.probe_fit_selected(stream=side, part=p)
             self.ev_fit_c[i].record(side)
         for i, p in enumerate(self.chunks):
             s = self.stream_b if i % 2 == 0 else main
@@ -675,15 +744,19 @@ class SparsePRCall:
         for i, p in enumerate(self.chunks):
             s = main if i % 2 == 0 else self.stream_b
             self.layout(labels_q, labels_kv, q, k, v, stream=s, part=p)
-            self.route(stream=s, part=p)
             if self.side is not None:
+                self.ev_laid_c[i].record(s)
+                self.side.wait_event(self.ev_laid_c[i])
+                self.probe_select(stream=self.side, part=p)
+                self.route(stream=s, part=p)
                 self.ev_routed_c[i].record(s)
                 self.side.wait_event(self.ev_routed_c[i])
-                self.probe_fit(stream=self.side, part=p)
+                self.probe_fit_selected(stream=self.side, part=p)
                 self.ev_fit_c[i].record(self.side)
                 self.attend(stream=s, part=p)
                 s.wait_event(self.ev_fit_c[i])
             else:
+                self.route(stream=s, part=p)
                 self.attend(stream=s, part=p)
                 self.probe_fit(stream=s, part=p)
             self.correct(stream=s, part=p)

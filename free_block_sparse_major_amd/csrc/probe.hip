@@ -1552,41 +1552,20 @@ size_t probe_feat_ws_bytes(const sparsepr_dims* d, int32_t m, int32_t rank) {
 using namespace spr;
 
 namespace {
-int32_t probe_fit_impl(const sparsepr_dims* dims, int32_t m, int32_t rank, double lambda,
-                       int32_t estimator, float* corr_g,
-                       const int32_t* offsets_q, const int32_t* offsets_kv, const int32_t* perm_q,
-                       const int32_t* cell_rowptr, const int32_t* cell_col,
-                       const double* centroid_q, const float* feat, int32_t fd, const void* q_g,
-                       const void* k_g, const void* v_g, const int32_t* v_shift,
-                       float softmax_scale, int32_t* probe_rows, int32_t* probe_tokens,
-                       float* o_probe_dense, float* o_probe_sparse, float* corr_a,
-                       float* corr_psi_t, float* corr_c, void* ws, size_t ws_bytes,
-                       hipStream_t stream) {
-  int32_t st = check_dims(dims);
-  if (st != SPARSEPR_OK) return st;
-  if (m < 1 || m > SPARSEPR_MAX_PROBES || rank < 0 || rank > SPARSEPR_MAX_RANK || !(lambda >= 0.0))
-    return SPARSEPR_ERR_INVALID;
-  if (feat ? (fd < 1 || fd > SPARSEPR_MAX_RANK) : !centroid_q) return SPARSEPR_ERR_INVALID;
-  if (estimator < SPARSEPR_EST_FULL || estimator > SPARSEPR_EST_DIAGONAL) return SPARSEPR_ERR_INVALID;
-  if (estimator != SPARSEPR_EST_FULL && !corr_g) return SPARSEPR_ERR_INVALID;
-  if (!offsets_q || !offsets_kv || !perm_q || !cell_rowptr || !cell_col || !q_g ||
-      !k_g || !v_g || !v_shift || !probe_rows || !probe_tokens || !o_probe_dense || !corr_a || !corr_psi_t ||
-      !corr_c)
-    return SPARSEPR_ERR_INVALID;
-  if (estimator == SPARSEPR_EST_FULL && rank > 0 && lambda == 0.0)
-    return SPARSEPR_ERR_INVALID;  // dual solve needs lam > 0
-  const size_t need = feat ? probe_feat_ws_bytes(dims, m, rank) : probe_ws_bytes(dims, m, rank);
-  if (!ws || ws_bytes < need) return SPARSEPR_ERR_WORKSPACE;
-  ProbeWs w = carve_probe(ws, dims, m);
+// S6: the probe plan and the probe rows of every group (Algorithm A.1); the
+// per-group probe counts and each probe's group stay in the workspace for
+// the fit stage.
+int32_t select_stage(const sparsepr_dims* dims, int32_t m, const int32_t* offsets_q,
+                     const int32_t* perm_q, const double* centroid_q, const float* feat,
+                     int32_t fd, const void* q_g, int32_t* probe_rows, int32_t* probe_tokens,
+                     const ProbeWs& w, void* ws, hipStream_t stream) {
   const int H = dims->heads, d = dims->head_dim;
-  const int me = m < dims->n_q ? m : dims->n_q;
   plan_kernel<<<H, 1024, 0, stream>>>(offsets_q, dims->c_q, dims->n_q, m, w.m_a, w.rank, w.s_tab,
                                       probe_rows, probe_tokens, w.group);
   SPR_LAUNCH_CHECK();
-  const float sl2 = softmax_scale * kLog2e;
   if (feat) {
     // feature rows and centroids after the standard workspace
-    Carver cv(static_cast<char*>(ws) + probe_ws_bytes(dims, m, rank));
+    Carver cv(static_cast<char*>(ws) + probe_ws_bytes(dims, m, 0));
     float* feat_g = cv.take<float>(size_t(H) * dims->n_q * fd);
     double* feat_cen = cv.take<double>(size_t(H) * dims->c_q * fd);
     // 16-byte chunks when rows are whole chunks and both arrays start on 16 bytes
@@ -1599,15 +1578,33 @@ int32_t probe_fit_impl(const sparsepr_dims* dims, int32_t m, int32_t rank, doubl
     select_kernel<float><<<dim3(dims->c_q, H), 256, 0, stream>>>(
         feat_g, feat_cen, offsets_q, perm_q, w.m_a, w.rank, w.s_tab, dims->n_q, dims->c_q, fd, m,
         w.dist, probe_rows, probe_tokens, w.group);
-    SPR_LAUNCH_CHECK();
+  } else if (dims->dtype == SPARSEPR_BF16) {
+    select_kernel<uint16_t><<<dim3(dims->c_q, H), 256, 0, stream>>>(
+        static_cast<const uint16_t*>(q_g), centroid_q, offsets_q, perm_q, w.m_a, w.rank,
+        w.s_tab, dims->n_q, dims->c_q, d, m, w.dist, probe_rows, probe_tokens, w.group);
+  } else {
+    select_kernel<float><<<dim3(dims->c_q, H), 256, 0, stream>>>(
+        static_cast<const float*>(q_g), centroid_q, offsets_q, perm_q, w.m_a, w.rank, w.s_tab,
+        dims->n_q, dims->c_q, d, m, w.dist, probe_rows, probe_tokens, w.group);
   }
+  SPR_LAUNCH_CHECK();
+  return SPARSEPR_OK;
+}
+
+// S7-S8: exact probe rows (retained / omitted sums over the routed cells),
+// their merge, and the fit, for the probes the select stage left in the
+// workspace.
+int32_t fit_stage(const sparsepr_dims* dims, int32_t m, int32_t rank, double lambda,
+                  int32_t estimator, float* corr_g, const int32_t* offsets_q,
+                  const int32_t* offsets_kv, const int32_t* cell_rowptr, const int32_t* cell_col,
+                  const void* q_g, const void* k_g, const void* v_g, const int32_t* v_shift,
+                  float softmax_scale, const int32_t* probe_rows, float* o_probe_dense,
+                  float* o_probe_sparse, float* corr_a, float* corr_psi_t, float* corr_c,
+                  const ProbeWs& w, hipStream_t stream) {
+  const int H = dims->heads, d = dims->head_dim;
+  const int me = m < dims->n_q ? m : dims->n_q;
+  const float sl2 = softmax_scale * kLog2e;
   if (dims->dtype == SPARSEPR_BF16) {
-    if (!feat) {
-      select_kernel<uint16_t><<<dim3(dims->c_q, H), 256, 0, stream>>>(
-          static_cast<const uint16_t*>(q_g), centroid_q, offsets_q, perm_q, w.m_a, w.rank,
-          w.s_tab, dims->n_q, dims->c_q, d, m, w.dist, probe_rows, probe_tokens, w.group);
-      SPR_LAUNCH_CHECK();
-    }
     auto* qq = static_cast<const uint16_t*>(q_g);
     auto* kk = static_cast<const uint16_t*>(k_g);
     auto* vv = static_cast<const uint16_t*>(v_g);
@@ -1620,12 +1617,6 @@ int32_t probe_fit_impl(const sparsepr_dims* dims, int32_t m, int32_t rank, doubl
           qq, kk, vv, v_shift, offsets_kv, cell_rowptr, cell_col, probe_rows, w.group, dims->n_q,
           dims->n_k, dims->c_q, dims->c_k, m, sl2, w.part_s, w.part_n);
   } else {
-    if (!feat) {
-      select_kernel<float><<<dim3(dims->c_q, H), 256, 0, stream>>>(
-          static_cast<const float*>(q_g), centroid_q, offsets_q, perm_q, w.m_a, w.rank, w.s_tab,
-          dims->n_q, dims->c_q, d, m, w.dist, probe_rows, probe_tokens, w.group);
-      SPR_LAUNCH_CHECK();
-    }
     auto* qq = static_cast<const float*>(q_g);
     auto* kk = static_cast<const float*>(k_g);
     auto* vv = static_cast<const float*>(v_g);
@@ -1668,6 +1659,63 @@ int32_t probe_fit_impl(const sparsepr_dims* dims, int32_t m, int32_t rank, doubl
   SPR_LAUNCH_CHECK();
   return SPARSEPR_OK;
 }
+
+// argument checks of the select stage (dims already checked)
+int32_t check_select(int32_t m, const int32_t* offsets_q, const int32_t* perm_q,
+                     const double* centroid_q, const float* feat, int32_t fd, const void* q_g,
+                     const int32_t* probe_rows, const int32_t* probe_tokens) {
+  if (m < 1 || m > SPARSEPR_MAX_PROBES) return SPARSEPR_ERR_INVALID;
+  if (feat ? (fd < 1 || fd > SPARSEPR_MAX_RANK) : (!centroid_q || !q_g)) return SPARSEPR_ERR_INVALID;
+  if (!offsets_q || !perm_q || !probe_rows || !probe_tokens) return SPARSEPR_ERR_INVALID;
+  return SPARSEPR_OK;
+}
+
+// argument checks of the fit stage (dims already checked)
+int32_t check_fit(int32_t m, int32_t rank, double lambda, int32_t estimator, const float* corr_g,
+                  const int32_t* offsets_q, const int32_t* offsets_kv, const int32_t* cell_rowptr,
+                  const int32_t* cell_col, const void* q_g, const void* k_g, const void* v_g,
+                  const int32_t* v_shift, const int32_t* probe_rows, const float* o_probe_dense,
+                  const float* corr_a, const float* corr_psi_t, const float* corr_c) {
+  if (m < 1 || m > SPARSEPR_MAX_PROBES || rank < 0 || rank > SPARSEPR_MAX_RANK || !(lambda >= 0.0))
+    return SPARSEPR_ERR_INVALID;
+  if (estimator < SPARSEPR_EST_FULL || estimator > SPARSEPR_EST_DIAGONAL) return SPARSEPR_ERR_INVALID;
+  if (estimator != SPARSEPR_EST_FULL && !corr_g) return SPARSEPR_ERR_INVALID;
+  if (!offsets_q || !offsets_kv || !cell_rowptr || !cell_col || !q_g || !k_g || !v_g ||
+      !v_shift || !probe_rows || !o_probe_dense || !corr_a || !corr_psi_t || !corr_c)
+    return SPARSEPR_ERR_INVALID;
+  if (estimator == SPARSEPR_EST_FULL && rank > 0 && lambda == 0.0)
+    return SPARSEPR_ERR_INVALID;  // dual solve needs lam > 0
+  return SPARSEPR_OK;
+}
+
+int32_t probe_fit_impl(const sparsepr_dims* dims, int32_t m, int32_t rank, double lambda,
+                       int32_t estimator, float* corr_g,
+                       const int32_t* offsets_q, const int32_t* offsets_kv, const int32_t* perm_q,
+                       const int32_t* cell_rowptr, const int32_t* cell_col,
+                       const double* centroid_q, const float* feat, int32_t fd, const void* q_g,
+                       const void* k_g, const void* v_g, const int32_t* v_shift,
+                       float softmax_scale, int32_t* probe_rows, int32_t* probe_tokens,
+                       float* o_probe_dense, float* o_probe_sparse, float* corr_a,
+                       float* corr_psi_t, float* corr_c, void* ws, size_t ws_bytes,
+                       hipStream_t stream) {
+  int32_t st = check_dims(dims);
+  if (st != SPARSEPR_OK) return st;
+  st = check_select(m, offsets_q, perm_q, centroid_q, feat, fd, q_g, probe_rows, probe_tokens);
+  if (st != SPARSEPR_OK) return st;
+  st = check_fit(m, rank, lambda, estimator, corr_g, offsets_q, offsets_kv, cell_rowptr,
+                 cell_col, q_g, k_g, v_g, v_shift, probe_rows, o_probe_dense, corr_a, corr_psi_t,
+                 corr_c);
+  if (st != SPARSEPR_OK) return st;
+  const size_t need = feat ? probe_feat_ws_bytes(dims, m, rank) : probe_ws_bytes(dims, m, rank);
+  if (!ws || ws_bytes < need) return SPARSEPR_ERR_WORKSPACE;
+  ProbeWs w = carve_probe(ws, dims, m);
+  st = select_stage(dims, m, offsets_q, perm_q, centroid_q, feat, fd, q_g, probe_rows,
+                    probe_tokens, w, ws, stream);
+  if (st != SPARSEPR_OK) return st;
+  return fit_stage(dims, m, rank, lambda, estimator, corr_g, offsets_q, offsets_kv, cell_rowptr,
+                   cell_col, q_g, k_g, v_g, v_shift, softmax_scale, probe_rows, o_probe_dense,
+                   o_probe_sparse, corr_a, corr_psi_t, corr_c, w, stream);
+}
 }  // namespace
 
 extern "C" int32_t sparsepr_probe_fit(const sparsepr_dims* dims, int32_t m, int32_t rank,
@@ -1701,4 +1749,41 @@ extern "C" int32_t sparsepr_probe_fit_ex(
                         feat_dim, q_g, k_g, v_g, v_shift, softmax_scale, probe_rows, probe_tokens,
                         o_probe_dense, o_probe_sparse, corr_a, corr_psi_t, corr_c, ws, ws_bytes,
                         stream);
+}
+
+extern "C" int32_t sparsepr_probe_select(const sparsepr_dims* dims, int32_t m,
+                                         const int32_t* offsets_q, const int32_t* perm_q,
+                                         const double* centroid_q, const float* probe_feat,
+                                         int32_t feat_dim, const void* q_g, int32_t* probe_rows,
+                                         int32_t* probe_tokens, void* ws, size_t ws_bytes,
+                                         hipStream_t stream) {
+  int32_t st = check_dims(dims);
+  if (st != SPARSEPR_OK) return st;
+  st = check_select(m, offsets_q, perm_q, probe_feat ? nullptr : centroid_q, probe_feat,
+                    feat_dim, q_g, probe_rows, probe_tokens);
+  if (st != SPARSEPR_OK) return st;
+  const size_t need = probe_feat ? probe_feat_ws_bytes(dims, m, 0) : probe_ws_bytes(dims, m, 0);
+  if (!ws || ws_bytes < need) return SPARSEPR_ERR_WORKSPACE;
+  const ProbeWs w = carve_probe(ws, dims, m);
+  return select_stage(dims, m, offsets_q, perm_q, probe_feat ? nullptr : centroid_q, probe_feat,
+                      feat_dim, q_g, probe_rows, probe_tokens, w, ws, stream);
+}
+
+extern "C" int32_t sparsepr_probe_fit_selected(
+    const sparsepr_dims* dims, int32_t m, int32_t rank, double lambda, int32_t estimator,
+    const int32_t* offsets_q, const int32_t* offsets_kv, const int32_t* cell_rowptr,
+    const int32_t* cell_col, const void* q_g, const void* k_g, const void* v_g,
+    const int32_t* v_shift, float softmax_scale, const int32_t* probe_rows, float* o_probe_dense,
+    float* o_probe_sparse, float* corr_a, float* corr_psi_t, float* corr_c, float* corr_g,
+    void* ws, size_t ws_bytes, hipStream_t stream) {
+  int32_t st = check_dims(dims);
+  if (st != SPARSEPR_OK) return st;
+  st = check_fit(m, rank, lambda, estimator, corr_g, offsets_q, offsets_kv, cell_rowptr, cell_col,
+                 q_g, k_g, v_g, v_shift, probe_rows, o_probe_dense, corr_a, corr_psi_t, corr_c);
+  if (st != SPARSEPR_OK) return st;
+  if (!ws || ws_bytes < probe_ws_bytes(dims, m, rank)) return SPARSEPR_ERR_WORKSPACE;
+  const ProbeWs w = carve_probe(ws, dims, m);
+  return fit_stage(dims, m, rank, lambda, estimator, corr_g, offsets_q, offsets_kv, cell_rowptr,
+                   cell_col, q_g, k_g, v_g, v_shift, softmax_scale, probe_rows, o_probe_dense,
+                   o_probe_sparse, corr_a, corr_psi_t, corr_c, w, stream);
 }

@@ -32,7 +32,9 @@
  * sparsepr_rcp_partition_ex does so across the calls of a layer;
  * sparsepr_route_cells_ex, sparsepr_probe_fit_ex and sparsepr_correct_ex
  * add the per-group routing rule, probe features and the restricted
- * residual estimators.
+ * residual estimators; sparsepr_probe_select with sparsepr_probe_fit_selected
+ * split probe_fit in two, so that the probe selection (which reads only the
+ * layout) can run while the cells are routed.
  *
  * Conventions shared by every call
  *   - Every pointer argument is a DEVICE pointer unless marked (host).
@@ -461,6 +463,44 @@ int32_t sparsepr_probe_fit_ex(const sparsepr_dims* dims /* host */, int32_t m, i
                               float* o_probe_dense, float* o_probe_sparse,
                               float* corr_a, float* corr_psi_t, float* corr_c, float* corr_g,
                               void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * S6-S8 in two calls.  (SparsePR paper App. A.2, Algorithm A.1: the probe
+ * rows are chosen from the query partition alone, so the selection can run
+ * before the routing is known; the exact probe rows and the fit of App. A.1,
+ * A.2 and D.3 need the routed cells.)  sparsepr_probe_select followed by
+ * sparsepr_probe_fit_selected on the same stream order, with the same dims,
+ * m and ws, computes exactly what one sparsepr_probe_fit_ex call computes.
+ *
+ * sparsepr_probe_select: the probe plan and probe rows.  Arguments as in
+ *   sparsepr_probe_fit_ex (probe_feat / feat_dim or centroid_q and q_g);
+ *   writes probe_rows, probe_tokens and, in ws, the per-group probe counts
+ *   and each probe's group.
+ * sparsepr_probe_fit_selected: exact probe rows, merge and fit for the
+ *   probes in probe_rows (read) and in ws, which must hold what the select
+ *   call wrote (the caller orders the two calls and keeps ws untouched in
+ *   between).  Other arguments as in sparsepr_probe_fit_ex.
+ * Workspace: one buffer of sparsepr_workspace_bytes(SPARSEPR_CALL_PROBE_FIT_EX,
+ * dims, m, rank) bytes for both calls (the fit call needs only the
+ * SPARSEPR_CALL_PROBE_FIT size).
+ */
+int32_t sparsepr_probe_select(const sparsepr_dims* dims /* host */, int32_t m,
+                              const int32_t* offsets_q, const int32_t* perm_q,
+                              const double* centroid_q, const float* probe_feat,
+                              int32_t feat_dim, const void* q_g, int32_t* probe_rows,
+                              int32_t* probe_tokens, void* ws, size_t ws_bytes,
+                              hipStream_t stream);
+
+int32_t sparsepr_probe_fit_selected(const sparsepr_dims* dims /* host */, int32_t m,
+                                    int32_t rank, double lambda, int32_t estimator,
+                                    const int32_t* offsets_q, const int32_t* offsets_kv,
+                                    const int32_t* cell_rowptr, const int32_t* cell_col,
+                                    const void* q_g, const void* k_g, const void* v_g,
+                                    const int32_t* v_shift, float softmax_scale,
+                                    const int32_t* probe_rows, float* o_probe_dense,
+                                    float* o_probe_sparse, float* corr_a, float* corr_psi_t,
+                                    float* corr_c, float* corr_g, void* ws, size_t ws_bytes,
+                                    hipStream_t stream);
 
 /*
  * S9 with a diagonal gain: as sparsepr_correct with

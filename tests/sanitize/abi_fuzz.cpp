@@ -167,7 +167,14 @@ int main(int argc, char** argv) {
                                   p<int32_t>(), p<int32_t>(), p<int32_t>(), p<int32_t>(),
                                   p<int64_t>(), p<int32_t>(), p<int32_t>(), p<uint32_t>(),
                                   nullptr);
-    for (int i = 0; i < 13; ++i) ++counts[checked(st[i])];
+    st[13] = sparsepr_probe_select(dp, m, p<int32_t>(), p<int32_t>(), p<double>(), p<float>(),
+                                   feat, ptr(), p<int32_t>(), p<int32_t>(), ptr(), ws, nullptr);
+    st[14] = sparsepr_probe_fit_selected(dp, m, rank, lam, int32_t(next() % 6) - 1,
+                                         p<int32_t>(), p<int32_t>(), p<int32_t>(), p<int32_t>(),
+                                         ptr(), ptr(), ptr(), p<int32_t>(), scale, p<int32_t>(),
+                                         p<float>(), p<float>(), p<float>(), p<float>(),
+                                         p<float>(), p<float>(), ptr(), ws, nullptr);
+    for (int i = 0; i < 15; ++i) ++counts[checked(st[i])];
   }
   for (int32_t s = -1; s <= 5; ++s) (void)sparsepr_status_string(s);
   std::printf("calls by status: ok %lld invalid %lld unsupported %lld workspace %lld hip %lld\n",

@@ -114,6 +114,25 @@ def test_argument_validation_before_launch(lib):
     assert part_ex(warm=1, state=None) == fb.ERR_INVALID
     assert part_ex(r_k=65) == fb.ERR_INVALID
     assert part_ex(ws_bytes=16) == fb.ERR_WORKSPACE
+    # split probe fit: m out of range, a missing centroid (no features), a
+    # feature width out of range, a small workspace; the fit half as probe_fit
+    def select(m=64, cen=P, feat=None, fd=0, ws_bytes=1 << 30):
+        return lib.sparsepr_probe_select(ctypes.byref(good), m, P, P, cen, feat, fd, P, P, P, P,
+                                         ws_bytes, None)
+    assert select(m=0) == fb.ERR_INVALID
+    assert select(m=65) == fb.ERR_INVALID
+    assert select(cen=None) == fb.ERR_INVALID
+    assert select(cen=None, feat=P, fd=65) == fb.ERR_INVALID
+    assert select(ws_bytes=16) == fb.ERR_WORKSPACE
+    def fit_sel(m=64, rank=16, lam=0.1, est=fb.EST_FULL, corr_g=None, ws_bytes=1 << 30):
+        return lib.sparsepr_probe_fit_selected(ctypes.byref(good), m, rank, lam, est, *([P] * 8),
+                                               ctypes.c_float(0.125), *([P] * 6), corr_g, P,
+                                               ws_bytes, None)
+    for m, rank, lam in [(0, 16, 0.1), (65, 16, 0.1), (64, -1, 0.1), (64, 65, 0.1), (64, 16, 0.0)]:
+        assert fit_sel(m, rank, lam) == fb.ERR_INVALID, (m, rank, lam)
+    assert fit_sel(est=fb.EST_MEAN) == fb.ERR_INVALID   # corr_g required
+    assert fit_sel(est=7) == fb.ERR_INVALID
+    assert fit_sel(ws_bytes=16) == fb.ERR_WORKSPACE
 
 
 def test_debug_check_and_size_limits(lib):
