@@ -695,8 +695,9 @@ __global__ __launch_bounds__(256) void project_kernel(const void* x, int dtype, 
   __shared__ __attribute__((aligned(16))) uint16_t fth[kMaxR * LD];
   __shared__ __attribute__((aligned(16))) uint16_t ftl[kMaxR * LD];
   const float* fh = f + (long long)h * D * rp;
+  // F is read row by row (consecutive threads, consecutive columns)
   for (int e = tid; e < kMaxR * D; e += 256) {
-    const int col = e / D, j = e % D;
+    const int j = e / kMaxR, col = e % kMaxR;
     const float v = col < rp ? fh[j * rp + col] : 0.f;
     const uint16_t b = f32_to_bf16_rne(v);
     fth[col * LD + j] = b;
