@@ -507,30 +507,25 @@ __global__ __launch_bounds__(256, 2) void probe_rows_mfma_kernel(
         mb1 |= ((hi >> (8 * q4)) & 0xfu) << (4 * q4);
       }
     }
+    // keys at or past the chunk end take no part: their scores become -inf,
+    // so they raise no maximum and their exponentials are 0 in both classes
+    // (this and the passes below are branch-free: selects, no conditional
+    // exponentials)
     const int tail = k1 - t0;
-    // keys at or past the chunk end take no part: clear them from both classes
-    uint32_t va = 0xffffu, vb_ = 0xffffu;
     if (tail < 64) {
-      va = 0;
-      vb_ = 0;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        va |= uint32_t(c_key(0, r, g) < tail) << r;
-        vb_ |= uint32_t(c_key(1, r, g) < tail) << r;
+        if (c_key(0, r, g) >= tail) s0[r] = NEG;
+        if (c_key(1, r, g) >= tail) s1[r] = NEG;
       }
     }
     float tS = NEG, tU = NEG;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
+      const bool ia = (mb0 >> r) & 1u, ib = (mb1 >> r) & 1u;
       const float xa = s0[r], xb = s1[r];
-      if ((va >> r) & 1u) {
-        if ((mb0 >> r) & 1u) tS = fmaxf(tS, xa);
-        else tU = fmaxf(tU, xa);
-      }
-      if ((vb_ >> r) & 1u) {
-        if ((mb1 >> r) & 1u) tS = fmaxf(tS, xb);
-        else tU = fmaxf(tU, xb);
-      }
+      tS = fmaxf(tS, fmaxf(ia ? xa : NEG, ib ? xb : NEG));
+      tU = fmaxf(tU, fmaxf(ia ? NEG : xa, ib ? NEG : xb));
     }
     tS = fmaxf(tS, __shfl_xor(tS, 32));
     tU = fmaxf(tU, __shfl_xor(tU, 32));
@@ -550,46 +545,57 @@ __global__ __launch_bounds__(256, 2) void probe_rows_mfma_kernel(
 #pragma unroll
       for (int db = 0; db < NDH; ++db) oU[db] *= al;
     }
-    const float mcS = mS * c2, mcU = mU * c2;
+    // a class not seen yet has no keys in this tile: any finite offset gives
+    // its (-inf) entries exp 0
+    const float offS = mS == NEG ? 0.f : -mS * c2, offU = mU == NEG ? 0.f : -mU * c2;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const bool ia = (mb0 >> r) & 1u, ib = (mb1 >> r) & 1u;
-      const float ea = ((va >> r) & 1u)
-                           ? __builtin_amdgcn_exp2f(__builtin_fmaf(s0[r], c2, ia ? -mcS : -mcU))
-                           : 0.f;
-      const float eb = ((vb_ >> r) & 1u)
-                           ? __builtin_amdgcn_exp2f(__builtin_fmaf(s1[r], c2, ib ? -mcS : -mcU))
-                           : 0.f;
+      const float ea = __builtin_amdgcn_exp2f(__builtin_fmaf(s0[r], c2, ia ? offS : offU));
+      const float eb = __builtin_amdgcn_exp2f(__builtin_fmaf(s1[r], c2, ib ? offS : offU));
       s0[r] = ea;
       s1[r] = eb;
-      zS += ia ? ea : 0.f;
-      zU += ia ? 0.f : ea;
-      zS += ib ? eb : 0.f;
-      zU += ib ? 0.f : eb;
     }
+    // P as hi + lo fp16 halves, two keys per 32-bit word; the class of each
+    // half is a 16-bit mask (sign-extended key bit), so one AND moves a word
+    // into the retained or the omitted operand, and the class sums are taken
+    // from the same halves the products use
+    const f16x2_t one2 = {static_cast<_Float16>(1.f), static_cast<_Float16>(1.f)};
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-      f16x8_t sh, sl, uh, ul;
+      uint32_t sh[4], sl[4], uh[4], ul[4];
+      const uint32_t mu = (u >> 1) ? mb1 : mb0;
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int r = 8 * (u & 1) + j;
-        const float e = (u >> 1) ? s1[r] : s0[r];
-        const _Float16 eh = static_cast<_Float16>(e);
-        const _Float16 el = static_cast<_Float16>(e - float(eh));
-        const bool in = ((u >> 1) ? (mb1 >> r) : (mb0 >> r)) & 1u;
-        const _Float16 z16 = static_cast<_Float16>(0.f);
-        sh[j] = in ? eh : z16;
-        sl[j] = in ? el : z16;
-        uh[j] = in ? z16 : eh;
-        ul[j] = in ? z16 : el;
+      for (int jj = 0; jj < 4; ++jj) {
+        const int r0 = 8 * (u & 1) + 2 * jj;
+        const float e0 = (u >> 1) ? s1[r0] : s0[r0];
+        const float e1 = (u >> 1) ? s1[r0 + 1] : s0[r0 + 1];
+        const _Float16 h0 = static_cast<_Float16>(e0), h1 = static_cast<_Float16>(e1);
+        const _Float16 l0 = static_cast<_Float16>(e0 - float(h0));
+        const _Float16 l1 = static_cast<_Float16>(e1 - float(h1));
+        const uint32_t hw = __builtin_bit_cast(uint32_t, f16x2_t{h0, h1});
+        const uint32_t lw = __builtin_bit_cast(uint32_t, f16x2_t{l0, l1});
+        const uint32_t m0 = uint32_t(int32_t(mu << (31 - r0)) >> 31);
+        const uint32_t m1 = uint32_t(int32_t(mu << (30 - r0)) >> 31);
+        const uint32_t mw = (m0 & 0x0000ffffu) | (m1 & 0xffff0000u);
+        sh[jj] = hw & mw;
+        sl[jj] = lw & mw;
+        uh[jj] = hw & ~mw;
+        ul[jj] = lw & ~mw;
+        zS = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, sh[jj]), one2, zS, false);
+        zS = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, sl[jj]), one2, zS, false);
+        zU = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, uh[jj]), one2, zU, false);
+        zU = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, ul[jj]), one2, zU, false);
       }
+      const f16x8_t fsh = __builtin_bit_cast(f16x8_t, sh), fsl = __builtin_bit_cast(f16x8_t, sl);
+      const f16x8_t fuh = __builtin_bit_cast(f16x8_t, uh), ful = __builtin_bit_cast(f16x8_t, ul);
 #pragma unroll
       for (int db = 0; db < NDH; ++db) {
         const f16x8_t vf = v_frag<D>(vt, lane, u, dh * NDH + db);
-        oS[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf, sh, oS[db], 0, 0, 0);
-        oS[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf, sl, oS[db], 0, 0, 0);
-        oU[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf, uh, oU[db], 0, 0, 0);
-        oU[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf, ul, oU[db], 0, 0, 0);
+        oS[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf, fsh, oS[db], 0, 0, 0);
+        oS[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf, fsl, oS[db], 0, 0, 0);
+        oU[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf, fuh, oU[db], 0, 0, 0);
+        oU[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf, ful, oU[db], 0, 0, 0);
       }
     }
   };
