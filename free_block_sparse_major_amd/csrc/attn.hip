@@ -101,6 +101,10 @@ __global__ __launch_bounds__(1024) void tile_table_kernel(const int32_t* __restr
 // order) and heads keep their order, so the items in flight still cover
 // about one head's K/V, and the list ends with the shortest items of the last
 // two heads (largest-first list scheduling evens out the finishing times).
+// Launches with few items per compute unit (all_heads = 1, one block) order
+// the groups of all heads together instead: there every unit runs only one
+// or two items, and a per-head order would still pair long items with long
+// ones (key streams at the CogVideoX-like shape range over 1.4k-9.6k keys).
 // The list is indexed by block id.  Blocks are dealt to the 8 XCDs round-robin,
 // so XCD x runs positions x, x + 8, ...; positions 8..15 of every complete
 // 16-position window are reversed, so that no XCD always takes the larger
@@ -109,13 +113,13 @@ constexpr int kOrderMax = 2 * SPARSEPR_MAX_GROUPS;
 __global__ __launch_bounds__(1024) void item_order_kernel(
     const int32_t* __restrict__ off_q, const int32_t* __restrict__ off_k,
     const int32_t* __restrict__ rowptr, const int32_t* __restrict__ col, int H, int c_q, int c_k,
-    int tq, const int32_t* __restrict__ tiles, int2* __restrict__ items) {
+    int tq, const int32_t* __restrict__ tiles, int2* __restrict__ items, int all_heads) {
   __shared__ unsigned long long key[kOrderMax];
   __shared__ int32_t len_g[kOrderMax];
   __shared__ int32_t okl[SPARSEPR_MAX_GROUPS + 1], rpl[SPARSEPR_MAX_GROUPS + 1];
   __shared__ long long red[16];
-  const int h0 = blockIdx.x;
-  const int nh = (H >= 2 && h0 == H - 2) ? 2 : 1;
+  const int h0 = all_heads ? 0 : int(blockIdx.x);
+  const int nh = all_heads ? H : ((H >= 2 && h0 == H - 2) ? 2 : 1);   // nh * c_q <= kOrderMax
   const int nent = nh * c_q;
   for (int e = threadIdx.x; e < kOrderMax; e += blockDim.x) len_g[e] = 0;
   // key-stream length of every group: 16 lanes per group sum the K/V group
@@ -1259,15 +1263,25 @@ int32_t launch_attn(const sparsepr_dims* dims, const int32_t* offsets_q,
   const int tq = rows_per_item(dims);
   tile_table_kernel<<<1, 1024, 0, stream>>>(offsets_q, dims->heads, dims->c_q, tq, tiles);
   SPR_LAUNCH_CHECK();
-  // the ordered list pays where compute units take many items each; with a
-  // few per unit (under 8 on average, by the bound) the natural order ran faster
-  if (item_bound(dims) < 8LL * 256) items = nullptr;
+  // With many items per compute unit (8 or more on average, by the bound) the
+  // list is ordered per head (L2 reuse within a head); with fewer, all heads
+  // are ordered together in one block when their groups fit its sort, and the
+  // items otherwise go in their natural order.
   if (items) {
-    const unsigned nblk = unsigned(dims->heads >= 2 ? dims->heads - 1 : 1);
-    item_order_kernel<<<nblk, 1024, 0, stream>>>(offsets_q, offsets_kv, cell_rowptr, cell_col,
-                                                 dims->heads, dims->c_q, dims->c_k, tq, tiles,
-                                                 items);
-    SPR_LAUNCH_CHECK();
+    const bool many = item_bound(dims) >= 8LL * 256;
+    if (many) {
+      const unsigned nblk = unsigned(dims->heads >= 2 ? dims->heads - 1 : 1);
+      item_order_kernel<<<nblk, 1024, 0, stream>>>(offsets_q, offsets_kv, cell_rowptr, cell_col,
+                                                   dims->heads, dims->c_q, dims->c_k, tq, tiles,
+                                                   items, 0);
+    } else if ((long long)dims->heads * dims->c_q <= kOrderMax) {
+      item_order_kernel<<<1, 1024, 0, stream>>>(offsets_q, offsets_kv, cell_rowptr, cell_col,
+                                                dims->heads, dims->c_q, dims->c_k, tq, tiles,
+                                                items, 1);
+    } else {
+      items = nullptr;
+    }
+    if (items) SPR_LAUNCH_CHECK();
   }
   long long bound = item_bound(dims);
   bound = (bound + 8 * kXcdRun - 1) / (8 * kXcdRun) * (8 * kXcdRun);

@@ -1,12 +1,12 @@
 """GPU check of the longest-first order of the attention's work items.
 
 The entry points with a workspace launch the items from an ordered list
-(sorted by cost per head, the last two heads together, dealt to the XCDs);
-the entry point without a workspace launches them in (head, group, tile)
-order.  On shapes with enough items for the list to be used (at least 8 per
-compute unit by the bound), both must write every row, bit-identically (the
-order changes which block computes an item, not how).  O_sp is filled with
-NaN first, so a row no item covers shows."""
+(sorted by cost per head, the last two heads together, when there are at
+least 8 items per compute unit by the bound; sorted over all heads in one
+block when there are fewer), dealt to the XCDs; the entry point without a
+workspace launches them in (head, group, tile) order.  Both must write every
+row, bit-identically (the order changes which block computes an item, not
+how).  O_sp is filled with NaN first, so a row no item covers shows."""
 import numpy as np
 import pytest
 
@@ -22,7 +22,14 @@ CASES = {
                             rho="0.22", seed=122),
     "h5": sg.small_workload(name="ord5", heads=5, n=20000, head_dim=64, components=512,
                             kv_split=2, rho="0.26", seed=123),
+    # few items per compute unit: one list over all heads
+    "few6": sg.small_workload(name="ordfew6", heads=6, n=17550, head_dim=64, components=64,
+                              rho="0.26", seed=124),
+    "few3": sg.small_workload(name="ordfew3", heads=3, n=9000, head_dim=128, components=256,
+                              kv_split=4, rho="0.22", seed=125),
 }
+# cases whose list is ordered over all heads (fewer than 8 items per unit)
+FEW = {"few6", "few3"}
 
 
 @pytest.mark.parametrize("name", list(CASES))
@@ -35,10 +42,14 @@ def test_ordered_items_match_natural_order(name):
     q, k, v, lq, lk = upload(w, data)
     call = fb.SparsePRCall(w.heads, w.n, w.n, w.head_dim, fb.BF16, w.c_q, w.c_k, m=w.m,
                            rank=w.r, rho=w.rho)
-    # the ordered list is used at this shape
+    # the list of the intended kind is used at this shape
     from test_gpu_large import item_waves, sample_rows
     tq = 32 * item_waves(w.heads, w.n, w.c_q)
-    assert w.heads * (-(-w.n // tq) + w.c_q) >= 8 * 256
+    bound = w.heads * (-(-w.n // tq) + w.c_q)
+    if name in FEW:
+        assert bound < 8 * 256 and w.heads * w.c_q <= 2048
+    else:
+        assert bound >= 8 * 256
     call.o_sp.fill_(float("nan"))
     call(lq, lk, q, k, v)
     o2 = torch.full_like(call.o_sp, float("nan"))
