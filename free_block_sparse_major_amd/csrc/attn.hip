@@ -125,7 +125,34 @@ __global__ __launch_bounds__(1024) void item_order_kernel(
   // key-stream length of every group: 16 lanes per group sum the K/V group
   // sizes of its cells (contiguous in the cell table) and reduce
   const int lane = threadIdx.x & 15, wv = threadIdx.x >> 4, nwv = blockDim.x >> 4;
-  for (int hh = 0; hh < nh; ++hh) {
+  if (all_heads) {
+    // every group of every head at once, reading the tables in global memory
+    // (a per-head pass would wait for its loads once per head): LPE lanes per
+    // group, as many as the block holds, at most 16
+    __syncthreads();
+    int lpe = 16;
+    while (lpe > 1 && lpe * nent > int(blockDim.x)) lpe >>= 1;
+    const int sub = threadIdx.x % lpe, grp = threadIdx.x / lpe, ngrp = blockDim.x / lpe;
+    for (int e = grp; e < nent; e += ngrp) {
+      const int h = e / c_q, a = e - (e / c_q) * c_q;
+      const int32_t* rp = rowptr + (long long)h * (c_q + 1);
+      const int32_t* cl = col + (long long)h * c_q * c_k;
+      const int32_t* ok = off_k + (long long)h * (c_k + 1);
+      const int c0 = rp[a], c1 = rp[a + 1];
+      int sum = 0;
+      for (int i = c0 + sub; i < c1; i += 4 * lpe) {
+        int b[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) b[u] = i + lpe * u < c1 ? cl[i + lpe * u] : -1;
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+          if (b[u] >= 0) sum += ok[b[u] + 1] - ok[b[u]];
+      }
+      for (int o = lpe >> 1; o > 0; o >>= 1) sum += __shfl_xor(sum, o);
+      if (sub == 0) len_g[e] = sum;
+    }
+  }
+  for (int hh = 0; hh < (all_heads ? 0 : nh); ++hh) {
     const int h = h0 + hh;
     __syncthreads();
     for (int i = threadIdx.x; i <= c_k; i += blockDim.x) okl[i] = off_k[(long long)h * (c_k + 1) + i];

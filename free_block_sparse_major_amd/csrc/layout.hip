@@ -201,12 +201,25 @@ __global__ __launch_bounds__(kThreads) void vmax_kernel(const uint16_t* __restri
   const int chunks = d / 8;
   __shared__ uint32_t red[kThreads / 64];
   uint32_t mx = 0;
-  for (int i = threadIdx.x; i < rows * chunks; i += kThreads) {
-    const int r = i / chunks, c = i - r * chunks;
-    const uint4 w = *reinterpret_cast<const uint4*>(v + h * stride_head + (r0 + r) * stride_tok + c * 8);
-    const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+  // eight 16-byte loads in flight per thread before their values are used
+  constexpr int U = 8;
+  const int total = rows * chunks;
+  for (int i0 = threadIdx.x; i0 < total; i0 += U * kThreads) {
+    uint4 w[U];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) mx = max(mx, max(ws[j] & 0x7fffu, (ws[j] >> 16) & 0x7fffu));
+    for (int u = 0; u < U; ++u) {
+      const int i = i0 + u * kThreads;
+      const int r = i / chunks, c = i - r * chunks;
+      w[u] = i < total ? *reinterpret_cast<const uint4*>(v + h * stride_head +
+                                                         (r0 + r) * stride_tok + c * 8)
+                       : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const uint32_t ws[4] = {w[u].x, w[u].y, w[u].z, w[u].w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) mx = max(mx, max(ws[j] & 0x7fffu, (ws[j] >> 16) & 0x7fffu));
+    }
   }
   mx = block_max(mx, red);
   if (threadIdx.x == 0) atomicMax(&vmax[h], mx);
