@@ -488,13 +488,30 @@ __global__ __launch_bounds__(256, 2) void probe_rows_mfma_kernel(
     }
     const uint4* kt = stg == 0 ? kt0 : kt1;
     const uint4* vt = stg == 0 ? vt0 : vt1;
-    f32x16_t s0 = f32x16_t{}, s1 = f32x16_t{};
+    f32x16_t s0, s1;
+    const int tail = k1 - t0;
+    // scores of the tile; keys at or past the chunk end take no part: their
+    // scores become -inf, so they raise no maximum and their exponentials are
+    // 0 in both classes (this and the passes below are branch-free: selects,
+    // no conditional exponentials)
+    auto scores = [&]() __attribute__((always_inline)) {
+      s0 = f32x16_t{};
+      s1 = f32x16_t{};
 #pragma unroll
-    for (int s2 = 0; s2 < NS; ++s2) {
-      s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k_frag<D>(kt, n, s2, g), qf[s2], s0, 0, 0, 0);
-      s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k_frag<D>(kt, 32 + n, s2, g), qf[s2], s1, 0, 0,
-                                                   0);
-    }
+      for (int s2 = 0; s2 < NS; ++s2) {
+        s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k_frag<D>(kt, n, s2, g), qf[s2], s0, 0, 0, 0);
+        s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k_frag<D>(kt, 32 + n, s2, g), qf[s2], s1, 0,
+                                                     0, 0);
+      }
+      if (tail < 64) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          if (c_key(0, r, g) >= tail) s0[r] = NEG;
+          if (c_key(1, r, g) >= tail) s1[r] = NEG;
+        }
+      }
+    };
+    scores();
     // this lane's 16 keys of each 32-key block as a 16-bit retained mask:
     // keys 8 (r / 4) + 4 g + r % 4 of block 0 and 32 + the same of block 1
     const unsigned long long bits64 = tmask[stg][p];
@@ -507,54 +524,68 @@ __global__ __launch_bounds__(256, 2) void probe_rows_mfma_kernel(
         mb1 |= ((hi >> (8 * q4)) & 0xfu) << (4 * q4);
       }
     }
-    // keys at or past the chunk end take no part: their scores become -inf,
-    // so they raise no maximum and their exponentials are 0 in both classes
-    // (this and the passes below are branch-free: selects, no conditional
-    // exponentials)
-    const int tail = k1 - t0;
-    if (tail < 64) {
+    // Class references are lazy: a tile's exponents x = s c2 - reference
+    // (log2 units) are formed against the running references as they stand,
+    // and the class maxima of x are taken only on a tile where a class
+    // appears for the first time in the chunk or some x exceeds 8 (a score
+    // past its reference by more than the slack).  There a class with a
+    // reference raises it by d = max(class max of x, 0) and a new class takes
+    // its maximum as the reference; the running sums and numerators scale by
+    // 2^-d and the exponents drop by d.  Any reference gives the same sums; a
+    // reference is always a score seen (at most the class's running maximum)
+    // and never more than the slack below it, so every exponential stays at
+    // or below 2^8 and the class's largest at or above 1.
+    {
+      const float offS = mS == NEG ? 0.f : -mS * c2, offU = mU == NEG ? 0.f : -mU * c2;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        if (c_key(0, r, g) >= tail) s0[r] = NEG;
-        if (c_key(1, r, g) >= tail) s1[r] = NEG;
+        const bool ia = (mb0 >> r) & 1u, ib = (mb1 >> r) & 1u;
+        s0[r] = __builtin_fmaf(s0[r], c2, ia ? offS : offU);
+        s1[r] = __builtin_fmaf(s1[r], c2, ib ? offS : offU);
       }
     }
-    float tS = NEG, tU = NEG;
+    float xmax = NEG;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) xmax = fmaxf(xmax, fmaxf(s0[r], s1[r]));
+    // a class with keys in this lane's part of the tile and no reference yet
+    // (keys past the chunk end count as omitted here: harmless, they only
+    // send the tile down the branch below)
+    const bool first = (mS == NEG && (mb0 | mb1) != 0u) || (mU == NEG && (mb0 & mb1) != 0xffffu);
+    if (__ballot(first || !(xmax <= 8.f))) {
+      float tS = NEG, tU = NEG;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const bool ia = (mb0 >> r) & 1u, ib = (mb1 >> r) & 1u;
+        tS = fmaxf(tS, fmaxf(ia ? s0[r] : NEG, ib ? s1[r] : NEG));
+        tU = fmaxf(tU, fmaxf(ia ? NEG : s0[r], ib ? NEG : s1[r]));
+      }
+      tS = fmaxf(tS, __shfl_xor(tS, 32));
+      tU = fmaxf(tU, __shfl_xor(tU, 32));
+      // no key of the class here: no change (d = 0)
+      const float dS = tS == NEG ? 0.f : (mS == NEG ? tS : fmaxf(tS, 0.f));
+      const float dU = tU == NEG ? 0.f : (mU == NEG ? tU : fmaxf(tU, 0.f));
+      const float aS = mS == NEG ? 1.f : __builtin_amdgcn_exp2f(-dS);
+      const float aU = mU == NEG ? 1.f : __builtin_amdgcn_exp2f(-dU);
+      if (tS != NEG) mS = mS == NEG ? tS / c2 : mS + dS / c2;
+      if (tU != NEG) mU = mU == NEG ? tU / c2 : mU + dU / c2;
+      zS *= aS;
+      zU *= aU;
+#pragma unroll
+      for (int db = 0; db < NDH; ++db) {
+        oS[db] *= aS;
+        oU[db] *= aU;
+      }
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const bool ia = (mb0 >> r) & 1u, ib = (mb1 >> r) & 1u;
+        s0[r] -= ia ? dS : dU;
+        s1[r] -= ib ? dS : dU;
+      }
+    }
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const bool ia = (mb0 >> r) & 1u, ib = (mb1 >> r) & 1u;
-      const float xa = s0[r], xb = s1[r];
-      tS = fmaxf(tS, fmaxf(ia ? xa : NEG, ib ? xb : NEG));
-      tU = fmaxf(tU, fmaxf(ia ? NEG : xa, ib ? NEG : xb));
-    }
-    tS = fmaxf(tS, __shfl_xor(tS, 32));
-    tU = fmaxf(tU, __shfl_xor(tU, 32));
-    if (__ballot(tS > mS + slack)) {
-      const float nm = fmaxf(mS, tS);
-      const float al = nm == NEG ? 1.f : __builtin_amdgcn_exp2f((mS - nm) * c2);
-      mS = nm;
-      zS *= al;
-#pragma unroll
-      for (int db = 0; db < NDH; ++db) oS[db] *= al;
-    }
-    if (__ballot(tU > mU + slack)) {
-      const float nm = fmaxf(mU, tU);
-      const float al = nm == NEG ? 1.f : __builtin_amdgcn_exp2f((mU - nm) * c2);
-      mU = nm;
-      zU *= al;
-#pragma unroll
-      for (int db = 0; db < NDH; ++db) oU[db] *= al;
-    }
-    // a class not seen yet has no keys in this tile: any finite offset gives
-    // its (-inf) entries exp 0
-    const float offS = mS == NEG ? 0.f : -mS * c2, offU = mU == NEG ? 0.f : -mU * c2;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const bool ia = (mb0 >> r) & 1u, ib = (mb1 >> r) & 1u;
-      const float ea = __builtin_amdgcn_exp2f(__builtin_fmaf(s0[r], c2, ia ? offS : offU));
-      const float eb = __builtin_amdgcn_exp2f(__builtin_fmaf(s1[r], c2, ib ? offS : offU));
-      s0[r] = ea;
-      s1[r] = eb;
+      s0[r] = __builtin_amdgcn_exp2f(s0[r]);
+      s1[r] = __builtin_amdgcn_exp2f(s1[r]);
     }
     // P as hi + lo fp16 halves, two keys per 32-bit word; the class of each
     // half is a 16-bit mask (sign-extended key bit), so one AND moves a word
