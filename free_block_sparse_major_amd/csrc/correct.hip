@@ -306,22 +306,21 @@ __global__ __launch_bounds__(256) void correct_mfma_kernel(const int32_t* __rest
   }
 }
 
-// probe rows take their dense output (after the correction pass on the stream)
-__global__ __launch_bounds__(256) void probe_overwrite_kernel(const int32_t* __restrict__ tokens,
+// probe rows take their dense output (after the correction pass on the
+// stream): one block of d threads per (probe, head), one row each
+__global__ __launch_bounds__(128) void probe_overwrite_kernel(const int32_t* __restrict__ tokens,
                                                               const float* __restrict__ dense,
                                                               int m, int d, void* out,
                                                               int64_t sh, int64_t st,
                                                               int out_bf16) {
-  const int h = blockIdx.x;
-  for (int e = threadIdx.x; e < m * d; e += 256) {
-    const int p = e / d, j = e % d;
-    const int tok = tokens[(long long)h * m + p];
-    if (tok < 0) continue;
-    const float v = dense[((long long)h * m + p) * d + j];
-    const long long o = (long long)h * sh + (long long)tok * st + j;
-    if (out_bf16) static_cast<uint16_t*>(out)[o] = f32_to_bf16_rne(v);
-    else static_cast<float*>(out)[o] = v;
-  }
+  const int p = blockIdx.x, h = blockIdx.y, j = threadIdx.x;
+  if (p >= m || j >= d) return;
+  const int tok = tokens[(long long)h * m + p];
+  if (tok < 0) return;
+  const float v = dense[((long long)h * m + p) * d + j];
+  const long long o = (long long)h * sh + (long long)tok * st + j;
+  if (out_bf16) static_cast<uint16_t*>(out)[o] = f32_to_bf16_rne(v);
+  else static_cast<float*>(out)[o] = v;
 }
 
 template <int D>
@@ -343,8 +342,8 @@ namespace spr {
 int32_t launch_probe_overwrite(const sparsepr_dims* d, int m, const int32_t* tokens,
                                const float* dense, void* out, int out_bf16, int64_t sh,
                                int64_t st, hipStream_t stream) {
-  probe_overwrite_kernel<<<d->heads, 256, 0, stream>>>(tokens, dense, m, d->head_dim, out, sh, st,
-                                                       out_bf16);
+  probe_overwrite_kernel<<<dim3(m, d->heads), 128, 0, stream>>>(tokens, dense, m, d->head_dim,
+                                                                out, sh, st, out_bf16);
   SPR_LAUNCH_CHECK();
   return SPARSEPR_OK;
 }
@@ -385,14 +384,19 @@ int32_t correct_impl(const sparsepr_dims* dims, int32_t m, int32_t rank, const i
   a.out_bf16 = out_dtype == SPARSEPR_BF16;
   if (rank <= 16 && dims->dtype == SPARSEPR_BF16) {
     // bf16 inputs (tolerance of the bf16 path): 16-row tiles on MFMA, 4 waves
-    // per block, a few tiles per wave; fp32 inputs keep the fp32 VALU kernel
-    constexpr int kTilesPerWave = 8;
+    // per block, up to 8 tiles per wave (the operand setup is paid once per
+    // wave); calls with few rows take fewer tiles per wave, so the grid still
+    // holds about four blocks per compute unit; fp32 inputs keep the fp32
+    // VALU kernel
     const int ntile = (dims->n_q + 15) / 16;
-    dim3 grid((ntile + 4 * kTilesPerWave - 1) / (4 * kTilesPerWave), dims->heads);
+    const long long waves = (long long)ntile * dims->heads;
+    int tpw = int(waves / (4LL * 4 * 256));
+    tpw = tpw < 1 ? 1 : (tpw > 8 ? 8 : tpw);
+    dim3 grid((ntile + 4 * tpw - 1) / (4 * tpw), dims->heads);
     auto launch = [&](auto kern) {
       kern<<<grid, 256, 0, stream>>>(perm_q, o_sp, corr_a, corr_psi_t, corr_c, corr_g, out,
                                      out_stride_head, out_stride_tok, dims->n_q, rank, a.out_bf16,
-                                     kTilesPerWave);
+                                     tpw);
     };
     if (dims->head_dim == 128) {
       if (corr_g) launch(correct_mfma_kernel<128, true>);
@@ -407,11 +411,8 @@ int32_t correct_impl(const sparsepr_dims* dims, int32_t m, int32_t rank, const i
     else launch_correct<64>(a, grid, stream);
   }
   SPR_LAUNCH_CHECK();
-  probe_overwrite_kernel<<<dims->heads, 256, 0, stream>>>(probe_tokens, o_probe_dense, m,
-                                                          dims->head_dim, out, out_stride_head,
-                                                          out_stride_tok, a.out_bf16);
-  SPR_LAUNCH_CHECK();
-  return SPARSEPR_OK;
+  return launch_probe_overwrite(dims, m, probe_tokens, o_probe_dense, out, a.out_bf16,
+                                out_stride_head, out_stride_tok, stream);
 }
 }  // namespace
 
