@@ -95,74 +95,68 @@ __global__ __launch_bounds__(1024) void scan_kernel(KindArgs qa, KindArgs ka) {
   if (threadIdx.x == 0) off[A.c] = A.n;
 }
 
-// Per tile: sort the tile's (label, local index) keys with a bitonic network,
-// then the sorted position minus the tile-local start of the label is the
-// token's rank among earlier same-label tokens of the tile.
+// Per tile: the stable rank of every token among the tile's earlier tokens of
+// its label, added to the scanned base of (label, tile).  The tile's 1024
+// tokens are 16 rows of 64 in token order and wave w takes rows 4w .. 4w+3.
+// Within a row the lanes holding the same label are found with one ballot per
+// label bit (multi-split), and a lane's rank in the row is the number of them
+// below it; earlier rows of the wave count through the wave's running label
+// histogram, earlier waves through a prefix of the waves' histograms.
 __global__ __launch_bounds__(kThreads) void scatter_kernel(KindArgs qa, KindArgs ka) {
   const KindArgs& A = blockIdx.z == 0 ? qa : ka;
   const int tile = blockIdx.x, h = blockIdx.y;
   if (tile >= A.ntiles) return;
-  __shared__ uint32_t keys[kTile];
-  __shared__ int32_t hist[SPARSEPR_MAX_GROUPS];
-  __shared__ long long red[kThreads / 64];
+  constexpr int NW = kThreads / 64;           // waves
+  constexpr int RPW = kTile / 64 / NW;        // rows of 64 tokens per wave
+  static_assert(RPW * 64 * NW == kTile, "rows cover the tile");
+  __shared__ int32_t whist[NW][SPARSEPR_MAX_GROUPS];
+  const int wid = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int32_t* lab = A.labels + int64_t(h) * A.n;
   const int t0 = tile * kTile;
-  for (int i = threadIdx.x; i < A.c; i += kThreads) hist[i] = 0;
-  __syncthreads();
-  for (int i = threadIdx.x; i < kTile; i += kThreads) {
-    int t = t0 + i;
-    uint32_t key = 0xffffffffu;  // padding sorts last
-    if (t < A.n) {
-      int l = clamp_label(lab[t], A.c);
-      key = (uint32_t(l) << 10) | uint32_t(i);
-      atomicAdd(&hist[l], 1);
-    }
-    keys[i] = key;
+  for (int i = threadIdx.x; i < NW * A.c; i += kThreads) whist[i / A.c][i % A.c] = 0;
+  int l[RPW];
+#pragma unroll
+  for (int r = 0; r < RPW; ++r) {
+    const int t = t0 + (wid * RPW + r) * 64 + lane;
+    l[r] = t < A.n ? clamp_label(lab[t], A.c) : -1;
   }
   __syncthreads();
-  // exclusive scan of the tile histogram (C <= 1024 entries, 4 per thread)
-  {
-    int base = threadIdx.x * 4;
-    long long s = 0;
-    int v[4];
-    for (int j = 0; j < 4; ++j) {
-      v[j] = base + j < A.c ? hist[base + j] : 0;
-      s += v[j];
-    }
-    long long tot;
-    long long run = block_exclusive_scan(s, red, &tot);
-    __syncthreads();
-    for (int j = 0; j < 4; ++j) {
-      if (base + j < A.c) hist[base + j] = int32_t(run);
-      run += v[j];
+#pragma unroll
+  for (int r = 0; r < RPW; ++r)
+    if (l[r] >= 0) atomicAdd(&whist[wid][l[r]], 1);
+  __syncthreads();
+  // per label, exclusive prefix over the waves (in place)
+  for (int c = threadIdx.x; c < A.c; c += kThreads) {
+    int run = 0;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      const int v = whist[w][c];
+      whist[w][c] = run;
+      run += v;
     }
   }
   __syncthreads();
-  // bitonic sort, ascending, 1024 keys, 2 compare-exchanges per thread per stage
-  for (int size = 2; size <= kTile; size <<= 1) {
-    for (int stride = size >> 1; stride > 0; stride >>= 1) {
-      for (int p = threadIdx.x; p < kTile / 2; p += kThreads) {
-        int i = 2 * p - (p & (stride - 1));
-        int j = i + stride;
-        bool up = (i & size) == 0;
-        uint32_t a = keys[i], b = keys[j];
-        if ((a > b) == up) {
-          keys[i] = b;
-          keys[j] = a;
-        }
-      }
-      __syncthreads();
-    }
-  }
+  const int nbits = A.c > 1 ? 32 - __clz(A.c - 1) : 0;   // label bits
+  const uint64_t below = (1ull << lane) - 1ull;
   const int32_t* cnt = A.counts + int64_t(h) * A.c * A.ntiles;
   int32_t* perm = A.perm + int64_t(h) * A.n;
-  for (int s = threadIdx.x; s < kTile; s += kThreads) {
-    uint32_t key = keys[s];
-    if (key == 0xffffffffu) continue;
-    int l = int(key >> 10), i = int(key & 1023u);
-    int rank = s - hist[l];
-    int dest = cnt[int64_t(l) * A.ntiles + tile] + rank;
-    perm[dest] = t0 + i;
+#pragma unroll
+  for (int r = 0; r < RPW; ++r) {
+    const int lr = l[r];
+    const bool valid = lr >= 0;
+    uint64_t same = __ballot(valid);
+    for (int bt = 0; bt < nbits; ++bt) {
+      const bool bit = (lr >> bt) & 1;
+      const uint64_t ones = __ballot(valid && bit);
+      same &= bit ? ones : ~ones;
+    }
+    if (valid) {
+      const int rank = whist[wid][lr] + __popcll(same & below);
+      perm[cnt[int64_t(lr) * A.ntiles + tile] + rank] = t0 + (wid * RPW + r) * 64 + lane;
+      // the highest lane of each label adds the row's count (one writer per
+      // label, after every lane of the row has read the running count)
+      if ((same >> lane) == 1ull) whist[wid][lr] += __popcll(same);
+    }
   }
 }
 
