@@ -38,6 +38,9 @@ typedef double f64x4_t __attribute__((ext_vector_type(4)));
 // column (B) l % 16 at k = l / 16; result lane l holds column l % 16 of rows
 // l / 16 + 4 i, i < 4.  Products accumulate in fp64, in a different order
 // than a sequential dot product (within fp64 rounding).
+// VEC: both centroid arrays 16-byte aligned (chosen on the host), so rows
+// move in 16-byte pairs; otherwise one double at a time.
+template <bool VEC>
 __global__ __launch_bounds__(256) void score_mfma_kernel(const double* __restrict__ cq,
                                                          const double* __restrict__ ck,
                                                          double* __restrict__ scores, int c_q,
@@ -52,13 +55,39 @@ __global__ __launch_bounds__(256) void score_mfma_kernel(const double* __restric
 #pragma unroll
   for (int j = 0; j < 4; ++j) acc[j] = f64x4_t{0.0, 0.0, 0.0, 0.0};
   for (int d0 = 0; d0 < d; d0 += 32) {
-    __syncthreads();
-    for (int i = tid; i < 64 * 32; i += 256) {
-      const int rr = i >> 5, c = i & 31;
-      As[rr][c] = a0 + rr < c_q ? Q[int64_t(a0 + rr) * d + d0 + c] : 0.0;
-      Bs[rr][c] = b0 + rr < c_k ? K[int64_t(b0 + rr) * d + d0 + c] : 0.0;
+    if constexpr (!VEC) {
+      __syncthreads();
+      for (int i = tid; i < 64 * 32; i += 256) {
+        const int rr = i >> 5, c = i & 31;
+        As[rr][c] = a0 + rr < c_q ? Q[int64_t(a0 + rr) * d + d0 + c] : 0.0;
+        Bs[rr][c] = b0 + rr < c_k ? K[int64_t(b0 + rr) * d + d0 + c] : 0.0;
+      }
+      __syncthreads();
+    } else {
+    // 16-byte loads, all eight of a thread in flight before the first store
+    // (rows are d = 64 or 128 doubles, so with an aligned base every pair is)
+    double2 qa[4], kb[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int i = tid + 256 * u, rr = i >> 4, c = 2 * (i & 15);
+      qa[u] = a0 + rr < c_q
+                  ? *reinterpret_cast<const double2*>(Q + int64_t(a0 + rr) * d + d0 + c)
+                  : double2{0.0, 0.0};
+      kb[u] = b0 + rr < c_k
+                  ? *reinterpret_cast<const double2*>(K + int64_t(b0 + rr) * d + d0 + c)
+                  : double2{0.0, 0.0};
     }
     __syncthreads();
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int i = tid + 256 * u, rr = i >> 4, c = 2 * (i & 15);
+      As[rr][c] = qa[u].x;
+      As[rr][c + 1] = qa[u].y;
+      Bs[rr][c] = kb[u].x;
+      Bs[rr][c + 1] = kb[u].y;
+    }
+    __syncthreads();
+    }
 #pragma unroll
     for (int kk = 0; kk < 32; kk += 4) {
       const double av = As[16 * wid + r][kk + kq];
@@ -684,8 +713,12 @@ extern "C" int32_t sparsepr_route_cells_ex(const sparsepr_dims* dims, int32_t ru
   int32_t* counts = cv.take<int32_t>(size_t(H) * dims->c_q);
   long long* pairs = cv.take<long long>(size_t(H) * dims->c_q);
   dim3 g1((dims->c_q + 63) / 64, (dims->c_k + 63) / 64, H);
-  score_mfma_kernel<<<g1, 256, 0, stream>>>(centroid_q, centroid_k, scores, dims->c_q, dims->c_k,
-                                            d, __builtin_sqrt(double(d)));
+  if (aligned16(centroid_q) && aligned16(centroid_k))
+    score_mfma_kernel<true><<<g1, 256, 0, stream>>>(centroid_q, centroid_k, scores, dims->c_q,
+                                                    dims->c_k, d, __builtin_sqrt(double(d)));
+  else
+    score_mfma_kernel<false><<<g1, 256, 0, stream>>>(centroid_q, centroid_k, scores, dims->c_q,
+                                                     dims->c_k, d, __builtin_sqrt(double(d)));
   SPR_LAUNCH_CHECK();
   group_route_kernel<<<dim3(dims->c_q, H), 256, 0, stream>>>(scores, offsets_q, offsets_kv,
                                                              dims->c_q, dims->c_k,
@@ -717,8 +750,12 @@ extern "C" int32_t sparsepr_route_cells(const sparsepr_dims* dims, const int32_t
   const SelWs w = carve_sel(ws, dims, nullptr);
   const int H = dims->heads, d = dims->head_dim, c_q = dims->c_q, c_k = dims->c_k;
   dim3 g1((c_q + 63) / 64, (c_k + 63) / 64, H);
-  score_mfma_kernel<<<g1, 256, 0, stream>>>(centroid_q, centroid_k, w.scores, c_q, c_k, d,
-                                            __builtin_sqrt(double(d)));
+  if (aligned16(centroid_q) && aligned16(centroid_k))
+    score_mfma_kernel<true><<<g1, 256, 0, stream>>>(centroid_q, centroid_k, w.scores, c_q, c_k,
+                                                    d, __builtin_sqrt(double(d)));
+  else
+    score_mfma_kernel<false><<<g1, 256, 0, stream>>>(centroid_q, centroid_k, w.scores, c_q, c_k,
+                                                     d, __builtin_sqrt(double(d)));
   SPR_LAUNCH_CHECK();
   const dim3 gr((c_q + 3) / 4, H);
   row_stats_kernel<<<gr, 256, 0, stream>>>(w.scores, offsets_q, offsets_kv, c_q, c_k, w.forced,

@@ -118,3 +118,40 @@ def test_repeat_calls_are_deterministic():
     o2 = call(lq, lk, q, k, v).clone()
     torch.cuda.synchronize()
     assert torch.equal(o1, o2)
+
+
+@pytest.mark.parametrize("rule", ["global", "per_group"])
+def test_routing_with_unaligned_centroids(rule):
+    # the score kernel moves centroid rows in 16-byte pairs only when both
+    # arrays are 16-byte aligned; centroids at an 8-byte offset take the
+    # one-double path and give the same cells
+    import torch
+    import free_block_sparse_major_amd as fb
+    w = sg.small_workload(name="unal", heads=2, n=2000, head_dim=64, components=12, kv_split=2,
+                          rho="0.3", seed=141)
+    g = run_gpu(w, sg.make_call(w), route_rule=rule)
+    call = g["call"]
+
+    def shifted(t):
+        buf = torch.empty(t.numel() + 1, dtype=t.dtype, device=t.device)
+        v = buf[1:].view(t.shape)
+        v.copy_(t)
+        assert v.data_ptr() % 16 == 8
+        return v
+    cq, ck = shifted(call.centroid_q), shifted(call.centroid_k)
+    rowptr = torch.empty_like(call.cell_rowptr)
+    col = torch.full_like(call.cell_col, -1)
+    pairs = torch.empty_like(call.routed_pairs)
+    if rule == "global":
+        fb.sparsepr_route_cells(call.dims, call.offsets_q, call.offsets_kv, cq, ck, call.budget,
+                                rowptr, col, pairs, call.ws_route)
+    else:
+        fb.sparsepr_route_cells_ex(call.dims, fb.ROUTE_RULES[rule], call.offsets_q,
+                                   call.offsets_kv, cq, ck, call.budget, rowptr, col, pairs,
+                                   call.ws_route)
+    torch.cuda.synchronize()
+    assert torch.equal(rowptr, call.cell_rowptr)
+    assert torch.equal(pairs, call.routed_pairs)
+    for h in range(w.heads):
+        used = int(rowptr[h][-1])
+        assert torch.equal(col[h][:used], call.cell_col[h][:used])
