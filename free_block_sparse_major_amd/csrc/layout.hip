@@ -70,24 +70,43 @@ __global__ __launch_bounds__(1024) void scan_kernel(KindArgs qa, KindArgs ka) {
   const long long seg = (len + kWaves - 1) / kWaves;
   const long long lo = seg * wid < len ? seg * wid : len;
   const long long hi = lo + seg < len ? lo + seg : len;
+  // both passes load U chunks of 64 entries before using any of them
+  constexpr int U = 8;
   long long s = 0;
-  for (long long i = lo + lane; i < hi; i += 64) s += cnt[i];
+  for (long long b0 = lo; b0 < hi; b0 += 64 * U) {
+    int v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const long long i = b0 + 64 * u + lane;
+      v[u] = i < hi ? cnt[i] : 0;
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) s += v[u];
+  }
   s = wave_sum(s);
   if (lane == 0) wt[wid] = s;
   __syncthreads();
   long long carry = 0;
   for (int w = 0; w < wid; ++w) carry += wt[w];
-  for (long long base = lo; base < hi; base += 64) {
-    const long long i = base + lane;
-    const int v = i < hi ? cnt[i] : 0;
-    int x = v;   // inclusive scan of the 64 entries
+  for (long long b0 = lo; b0 < hi; b0 += 64 * U) {
+    int v[U];
 #pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const int y = __shfl_up(x, o);
-      if (lane >= o) x += y;
+    for (int u = 0; u < U; ++u) {
+      const long long i = b0 + 64 * u + lane;
+      v[u] = i < hi ? cnt[i] : 0;
     }
-    if (i < hi) cnt[i] = int32_t(carry + x - v);
-    carry += __shfl(x, 63);
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const long long i = b0 + 64 * u + lane;
+      int x = v[u];   // inclusive scan of the 64 entries
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const int y = __shfl_up(x, o);
+        if (lane >= o) x += y;
+      }
+      if (i < hi) cnt[i] = int32_t(carry + x - v[u]);
+      carry += __shfl(x, 63);
+    }
   }
   __syncthreads();
   int32_t* off = A.offsets + int64_t(h) * (A.c + 1);
