@@ -1389,7 +1389,7 @@ __global__ __launch_bounds__(kFitThreads) void fit_kernel(FitArgs f) {
   __syncthreads();
   // A[:, c] = diag(1/s) Xw^T y_c,  Psi[:, c] = Rw^T u_c / sigma_c: Xw and Rw
   // staged again into the free G and E areas; thread (column j, c-phase)
-  // runs over the probes, 8 c at a time
+  // runs over the probes, CB c at a time
   double* Ab = f.abuf + (long long)h * d * kMaxM;
   double* Pb = f.pbuf + (long long)h * d * kMaxM;
   for (int pass = 0; pass < 2; ++pass) {
@@ -1412,20 +1412,23 @@ __global__ __launch_bounds__(kFitThreads) void fit_kernel(FitArgs f) {
     }
     __syncthreads();
     const double* vecs = pass == 0 ? Ws : Zs;
-    for (int cb = (tid / d) * 8; cb < k; cb += (kFitThreads / d) * 8) {
-      double acc[8];
+    // CB directions per thread: 4 keeps every thread busy for k = 16 at
+    // d = 128 (8 left half of them idle)
+    constexpr int CB = 4;
+    for (int cb = (tid / d) * CB; cb < k; cb += (kFitThreads / d) * CB) {
+      double acc[CB];
 #pragma unroll
-      for (int c = 0; c < 8; ++c) acc[c] = 0.0;
+      for (int c = 0; c < CB; ++c) acc[c] = 0.0;
       for (int p = 0; p < me; ++p) {
         const double xv = st[p * d + jc];
 #pragma unroll
-        for (int c = 0; c < 8; ++c) {
+        for (int c = 0; c < CB; ++c) {
           const int cc = cb + c < k ? cb + c : k - 1;
           acc[c] = fma(xv, vecs[cc * kLd + p], acc[c]);
         }
       }
 #pragma unroll
-      for (int c = 0; c < 8; ++c)
+      for (int c = 0; c < CB; ++c)
         if (cb + c < k) {
           if (pass == 0) Ab[jc * kMaxM + cb + c] = acc[c] * isc[jc];
           else Pb[jc * kMaxM + cb + c] = acc[c] / sqrt(lamn[cb + c] * tn);
