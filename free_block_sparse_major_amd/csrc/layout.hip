@@ -7,7 +7,7 @@
 // ascending token order, so the layout is a stable counting sort of the labels.
 //
 // Kernels (per tensor kind, per head):
-//   hist     per 1024-token tile: label histogram            -> counts[c][tile]
+//   hist     per 1024-token tile: label histogram            -> counts[tile][c]
 //   scan     exclusive scan of counts in (label, tile) order  -> bases, offsets
 //   scatter  per tile: bitonic sort of (label, index), rank   -> perm
 //   gather   row copy q_g[j] = q[perm[j]] with 16-byte accesses (HBM bound)
@@ -25,7 +25,7 @@ struct KindArgs {
   const int32_t* labels;  // [H][N]
   int32_t* perm;          // [H][N]
   int32_t* offsets;       // [H][C+1]
-  int32_t* counts;        // [H][C][ntiles] (workspace)
+  int32_t* counts;        // [H][ntiles][C] (workspace)
   int n, c, ntiles;
 };
 
@@ -52,66 +52,49 @@ __global__ __launch_bounds__(kThreads) void hist_kernel(KindArgs qa, KindArgs ka
   }
   __syncthreads();
   int32_t* cnt = A.counts + int64_t(h) * A.c * A.ntiles;
-  for (int c = threadIdx.x; c < A.c; c += kThreads) cnt[int64_t(c) * A.ntiles + tile] = hist[c];
+  for (int c = threadIdx.x; c < A.c; c += kThreads) cnt[int64_t(tile) * A.c + c] = hist[c];
 }
 
-// One block per (head, kind): exclusive scan of counts[c][tile] in (c, tile)
-// order, in place.  offsets[c] = base of (c, tile 0), offsets[C] = N.  Each
-// wave scans a contiguous segment 64 entries at a time (coalesced loads, a
-// shuffle scan per 64), after the segment totals are scanned across waves.
+// One block per (head, kind): exclusive scan of counts[tile][c] in (c, tile)
+// order, in place.  Thread c sums its label over the tiles (each tile's row
+// of counts is read by consecutive threads), a block scan over the labels
+// gives each label's base, and thread c walks its tiles again writing the
+// running bases.  offsets[c] = base of (c, tile 0), offsets[C] = N.
 __global__ __launch_bounds__(1024) void scan_kernel(KindArgs qa, KindArgs ka) {
   const KindArgs& A = blockIdx.y == 0 ? qa : ka;
   const int h = blockIdx.x;
-  constexpr int kWaves = 1024 / 64;
-  __shared__ long long wt[kWaves];
-  const int wid = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  __shared__ long long red[1024 / 64];
   int32_t* cnt = A.counts + int64_t(h) * A.c * A.ntiles;
-  const long long len = int64_t(A.c) * A.ntiles;
-  const long long seg = (len + kWaves - 1) / kWaves;
-  const long long lo = seg * wid < len ? seg * wid : len;
-  const long long hi = lo + seg < len ? lo + seg : len;
-  // both passes load U chunks of 64 entries before using any of them
-  constexpr int U = 8;
-  long long s = 0;
-  for (long long b0 = lo; b0 < hi; b0 += 64 * U) {
-    int v[U];
+  const int c = threadIdx.x;   // C <= SPARSEPR_MAX_GROUPS = 1024 = blockDim.x
+  constexpr int U = 8;         // tiles loaded before their counts are used
+  long long tot = 0;
+  if (c < A.c) {
+    for (int t0 = 0; t0 < A.ntiles; t0 += U) {
+      int v[U];
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const long long i = b0 + 64 * u + lane;
-      v[u] = i < hi ? cnt[i] : 0;
-    }
+      for (int u = 0; u < U; ++u) v[u] = t0 + u < A.ntiles ? cnt[int64_t(t0 + u) * A.c + c] : 0;
 #pragma unroll
-    for (int u = 0; u < U; ++u) s += v[u];
-  }
-  s = wave_sum(s);
-  if (lane == 0) wt[wid] = s;
-  __syncthreads();
-  long long carry = 0;
-  for (int w = 0; w < wid; ++w) carry += wt[w];
-  for (long long b0 = lo; b0 < hi; b0 += 64 * U) {
-    int v[U];
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const long long i = b0 + 64 * u + lane;
-      v[u] = i < hi ? cnt[i] : 0;
-    }
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const long long i = b0 + 64 * u + lane;
-      int x = v[u];   // inclusive scan of the 64 entries
-#pragma unroll
-      for (int o = 1; o < 64; o <<= 1) {
-        const int y = __shfl_up(x, o);
-        if (lane >= o) x += y;
-      }
-      if (i < hi) cnt[i] = int32_t(carry + x - v[u]);
-      carry += __shfl(x, 63);
+      for (int u = 0; u < U; ++u) tot += v[u];
     }
   }
-  __syncthreads();
-  int32_t* off = A.offsets + int64_t(h) * (A.c + 1);
-  for (int c = threadIdx.x; c < A.c; c += blockDim.x) off[c] = cnt[int64_t(c) * A.ntiles];
-  if (threadIdx.x == 0) off[A.c] = A.n;
+  long long all;
+  const long long base = block_exclusive_scan(tot, red, &all);
+  if (c < A.c) {
+    long long run = base;
+    for (int t0 = 0; t0 < A.ntiles; t0 += U) {
+      int v[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) v[u] = t0 + u < A.ntiles ? cnt[int64_t(t0 + u) * A.c + c] : 0;
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+        if (t0 + u < A.ntiles) {
+          cnt[int64_t(t0 + u) * A.c + c] = int32_t(run);
+          run += v[u];
+        }
+    }
+    A.offsets[int64_t(h) * (A.c + 1) + c] = int32_t(base);
+  }
+  if (threadIdx.x == 0) A.offsets[int64_t(h) * (A.c + 1) + A.c] = A.n;
 }
 
 // Per tile: the stable rank of every token among the tile's earlier tokens of
@@ -171,7 +154,7 @@ __global__ __launch_bounds__(kThreads) void scatter_kernel(KindArgs qa, KindArgs
     }
     if (valid) {
       const int rank = whist[wid][lr] + __popcll(same & below);
-      perm[cnt[int64_t(lr) * A.ntiles + tile] + rank] = t0 + (wid * RPW + r) * 64 + lane;
+      perm[cnt[int64_t(tile) * A.c + lr] + rank] = t0 + (wid * RPW + r) * 64 + lane;
       // the highest lane of each label adds the row's count (one writer per
       // label, after every lane of the row has read the running count)
       if ((same >> lane) == 1ull) whist[wid][lr] += __popcll(same);
