@@ -240,11 +240,16 @@ def main():
                     else int(x), default=1,
                     help="split each call into this many head ranges on alternating streams "
                          "(layout and routing of one range overlap the attention of the last)")
+    ap.add_argument("--lead", default="auto", choices=("auto", "fused", "unfused"),
+                    help="fused order over head ranges: unfused lets the first range attend as "
+                         "soon as it is routed and take the correction kernel after its fit; "
+                         "auto: unfused where --order auto picks the fused order")
     ap.add_argument("--order", default="auto", choices=("auto", "usual", "fused"),
                     help="usual: attention, probe fit on a side stream, then the correction "
                          "kernel; fused: probe fit first, correction in the attention epilogue; "
                          "auto: fused over two head ranges (a quarter of the heads, then the "
-                         "rest) for bf16 calls of 16 heads or more (measured faster there), "
+                         "rest, the first range unfused) for bf16 calls of 16 heads or more "
+                         "(measured faster there), "
                          "usual otherwise")
     ap.add_argument("--rcp-warm", action="store_true",
                     help="with a response-coupled workload: after a first call in the warm-up, "
@@ -299,6 +304,10 @@ def main():
             # a quarter of the heads first: its probe fit is short and its
             # attention starts early; the rest are fitted meanwhile
             args.head_chunks = [w.heads // 4, w.heads - w.heads // 4]
+        if big and args.lead == "auto":
+            # the first range's fit then runs beside its attention instead of
+            # in front of it
+            args.lead = "unfused"
     t0 = time.time()
     arr = sg.make_call_arrays(w)
     gen_s = time.time() - t0
@@ -317,7 +326,8 @@ def main():
                            lam=w.lam, rho=w.rho, out_dtype=fb.BF16 if w.dtype == "bf16" else fb.F32,
                            feat_dim=rp["r_q"] if rcp else 0, estimator=args.estimator,
                            route_rule=args.route_rule, head_chunks=args.head_chunks,
-                           overlap=not args.serial, fused=args.order == "fused")
+                           overlap=not args.serial, fused=args.order == "fused",
+                           lead_unfused=args.lead == "unfused")
     part = None
     if rcp:
         part = fb.RcpPartition(w.heads, w.n, w.n, w.head_dim, dtype, w.c_q, w.c_k, **rp,
@@ -444,8 +454,12 @@ def main():
             "estimator": args.estimator,
             "route_rule": args.route_rule,
             "head_chunks": args.head_chunks,
-            "order": args.order,
-            "probe_fit": ("before the attention, correction in its epilogue"
+            "order": args.order + (" (first range unfused)"
+                                   if args.order == "fused" and args.lead == "unfused" else ""),
+            "probe_fit": ("first range: beside its attention, then the correction kernel; "
+                          "later ranges: before the attention, correction in its epilogue"
+                          if args.order == "fused" and args.lead == "unfused" else
+                          "before the attention, correction in its epilogue"
                           if args.order == "fused" else
                           "main stream after the attention" if args.serial else "side stream"),
             "parallelism": "single GPU",

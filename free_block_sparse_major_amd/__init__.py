@@ -431,12 +431,16 @@ class SparsePRCall:
 
     fused=True runs the probe-first order: the probe fit before the attention,
     and the attention writes the corrected output in token order
-    (sparsepr_sparse_attn_correct), so O_sp is neither stored nor read."""
+    (sparsepr_sparse_attn_correct), so O_sp is neither stored nor read.
+    lead_unfused=True (fused order over head ranges, overlap on) lets the
+    first range attend as soon as it is routed, storing O_sp, and take the
+    correction kernel once its fit is done, so that fit runs beside the
+    attention instead of in front of it."""
 
     def __init__(self, heads, n_q, n_k, head_dim, dtype, c_q, c_k, m=64, rank=16, lam=0.1,
                  rho="0.26", budget=None, out_dtype=F32, device="cuda", q_strides=None,
                  kv_strides=None, overlap=True, feat_dim=0, estimator="full",
-                 route_rule="global", head_chunks=1, fused=False):
+                 route_rule="global", head_chunks=1, fused=False, lead_unfused=False):
         load_library()
         self.dims = make_dims(heads, n_q, n_k, head_dim, dtype, c_q, c_k, q_strides, kv_strides)
         self.m, self.rank, self.lam = m, rank, lam
@@ -489,6 +493,9 @@ class SparsePRCall:
         self._ex = bool(feat_dim) or self.estimator != EST_FULL
 
         self.fused = bool(fused)
+        # fused order over head ranges: the first range instead attends as soon
+        # as it is routed and takes the correction kernel once its fit is done
+        self.lead_unfused = bool(lead_unfused) and self.fused and overlap
 
         def ws_set(dims):
             def ws(which):
@@ -701,8 +708,9 @@ class SparsePRCall:
         range i on stream_b (even i) or the current stream (odd i) once its
         fit is done.  The fit of range i runs while later ranges are laid out
         and routed or while earlier ranges are attended, and two attention
-        launches overlap each other's tails.  Attention launches on one
-        stream share a workspace set; the two streams use different sets."""
+        launches overlap each other's tails (with lead_unfused, range 0 attends
+        once it is routed and is corrected after its fit).  Attention launches
+        on one stream share a workspace set; the two streams use different sets."""
         main = torch.cuda.current_stream()
         side = self.side if self.side is not None else main
         self.ev_start.record(main)
@@ -725,6 +733,12 @@ class SparsePRCall:
             self.ev_fit_c[i].record(side)
         for i, p in enumerate(self.chunks):
             s = self.stream_b if i % 2 == 0 else main
+            if i == 0 and self.lead_unfused and side is not main:
+                s.wait_event(self.ev_routed_c[i])
+                self.attend(stream=s, part=p)
+                s.wait_event(self.ev_fit_c[i])
+                self.correct(stream=s, part=p)
+                continue
             s.wait_event(self.ev_fit_c[i])
             self.attend_correct(stream=s, part=p)
         self.ev_b_done.record(self.stream_b)

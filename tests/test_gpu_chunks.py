@@ -64,3 +64,28 @@ def test_chunked_call_with_options_and_strided_inputs():
         split = _run(w, tensors, 4, layout="nhd", feat=feat, **kw)
         _same(whole, split)
         say(f"[chunks] options {kw}: identical")
+
+
+def test_fused_ranges_with_unfused_first_range():
+    # lead_unfused: the first range attends as soon as it is routed and takes
+    # the correction kernel after its fit (the usual order on those heads); the
+    # later ranges keep the correction in the attention epilogue
+    w = sg.small_workload(name="chunks_lead", heads=5, n=3200, head_dim=128, components=16,
+                          kv_split=2, grid=(4, 20, 40), rho="0.26", seed=63)
+    tensors = upload(w, sg.make_call(w))
+    usual = _run(w, tensors, 1)
+    fused = _run(w, tensors, 1, fused=True)
+    mixed = _run(w, tensors, [2, 3], fused=True, lead_unfused=True)
+    shared = [n for n in OUTPUTS if n not in ("o_sp", "out", "lse")]
+    for name in shared:
+        assert torch_equal(usual[name], mixed[name]), name
+    assert torch_equal(usual["lse"][:2], mixed["lse"][:2])
+    assert torch_equal(usual["o_sp"][:2], mixed["o_sp"][:2])
+    assert torch_equal(usual["out"][:2], mixed["out"][:2]), "first range: usual order"
+    assert torch_equal(fused["out"][2:], mixed["out"][2:]), "later ranges: fused order"
+    say("[chunks] unfused first range: heads 0-1 as the usual order, 2-4 as the fused order")
+
+
+def torch_equal(a, b):
+    import torch
+    return torch.equal(a, b)
